@@ -1,0 +1,483 @@
+"""Pins of the float64 oracle to things other than itself.
+
+Each check is chosen so that a plausible slip in the oracle (a swapped gate
+chunk, the GRU reset gate outside or inside the wrong term, a dropped bias, a
+wrong reverse start, a transposed weight) fails at least one of them:
+closed forms, invariants, brute force on tiny inputs, and library special
+cases (PyTorch's CPU modules in float64, which implement the gate
+conventions the oracle follows).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+torch.set_default_dtype(torch.float64)
+
+TIGHT = dict(rtol=1e-11, atol=1e-12)
+
+
+def _rand_case(mode, T=7, B=5, F=6, H=4, P=0, L=1, bidir=False, bias=True, lengths=None,
+               seed=0, h0=True):
+    d = synth.make_rnn_inputs(mode, T, B, F, H, proj_size=P, num_layers=L, bidirectional=bidir,
+                              lengths=lengths, w_scale=0.6, bias=bias, seed=seed,
+                              h0_std=0.5 if h0 else 0.0, c0_std=0.5 if h0 else 0.0)
+    return d
+
+
+def _torch_rnn(mode, d):
+    D = 2 if d["bidirectional"] else 1
+    H = d["hidden_size"]
+    bias = d["params"][0]["b_ih"] is not None
+    if mode == "gru":
+        m = torch.nn.GRU(d["input_size"], H, num_layers=d["num_layers"], bias=bias,
+                         bidirectional=d["bidirectional"])
+    else:
+        m = torch.nn.LSTM(d["input_size"], H, num_layers=d["num_layers"], bias=bias,
+                          bidirectional=d["bidirectional"], proj_size=d["proj_size"])
+    sd = {}
+    for layer in range(d["num_layers"]):
+        for di in range(D):
+            p = d["params"][layer * D + di]
+            sfx = f"_l{layer}" + ("_reverse" if di == 1 else "")
+            sd["weight_ih" + sfx] = torch.tensor(p["w_ih"], dtype=torch.float64)
+            sd["weight_hh" + sfx] = torch.tensor(p["w_hh"], dtype=torch.float64)
+            if bias:
+                sd["bias_ih" + sfx] = torch.tensor(p["b_ih"], dtype=torch.float64)
+                sd["bias_hh" + sfx] = torch.tensor(p["b_hh"], dtype=torch.float64)
+            if mode == "lstmp":
+                sd["weight_hr" + sfx] = torch.tensor(p["w_hr"], dtype=torch.float64)
+    m.load_state_dict(sd)
+    return m.double()
+
+
+def _torch_run(mode, d):
+    m = _torch_rnn(mode, d)
+    K = d["proj_size"] if mode == "lstmp" else d["hidden_size"]
+    D = 2 if d["bidirectional"] else 1
+    LD = d["num_layers"] * D
+    B = d["B"]
+    h0 = torch.zeros(LD, B, K) if d["h0"] is None else torch.tensor(d["h0"], dtype=torch.float64)
+    x = torch.tensor(np.nan_to_num(d["x_padded"]), dtype=torch.float64)
+    lengths = d["lengths"]
+    if lengths is not None:
+        x = torch.nn.utils.rnn.pack_padded_sequence(x, torch.tensor(lengths, dtype=torch.int64),
+                                                    enforce_sorted=False)
+    with torch.no_grad():
+        if mode == "gru":
+            y, hn = m(x, h0)
+            cn = None
+        else:
+            c0 = (torch.zeros(LD, B, d["hidden_size"]) if d["c0"] is None
+                  else torch.tensor(d["c0"], dtype=torch.float64))
+            y, (hn, cn) = m(x, (h0, c0))
+    if lengths is not None:
+        y, _ = torch.nn.utils.rnn.pad_packed_sequence(y, total_length=d["T"])
+    return y.numpy(), hn.numpy(), None if cn is None else cn.numpy()
+
+
+def _oracle_run(mode, d, **kw):
+    return oracle.rnn_forward(mode, d["x"], d["params"], lengths=d["lengths"], h0=d["h0"],
+                              c0=d["c0"], num_layers=d["num_layers"],
+                              bidirectional=d["bidirectional"], proj_size=d["proj_size"],
+                              layout=d["layout"], **kw)
+
+
+def _compare_padded(y_or, y_t, lengths):
+    """Oracle leaves unwritten positions NaN; torch's unpack writes zeros there."""
+    if lengths is None:
+        np.testing.assert_allclose(y_or, y_t, **TIGHT)
+        return
+    T = y_or.shape[0]
+    for b, Lb in enumerate(lengths):
+        np.testing.assert_allclose(y_or[:Lb, b], y_t[:Lb, b], **TIGHT)
+        assert np.isnan(y_or[Lb:T, b]).all()
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+def test_lstm_zero_weights_closed_form():
+    # All weights and biases zero: i = f = o = 1/2 and g = 0, so c_t = 2^-t c0
+    # and h_t = tanh(c_t) / 2 whatever h0 and x are.
+    T, B, F, H = 6, 3, 5, 4
+    d = _rand_case("lstm", T=T, B=B, F=F, H=H, seed=1)
+    for p in d["params"]:
+        for k in p:
+            p[k] = np.zeros_like(p[k])
+    y, hn, cn = _oracle_run("lstm", d)
+    c0 = d["c0"][0].astype(np.float64)
+    for t in range(T):
+        ct = c0 * 2.0 ** -(t + 1)
+        np.testing.assert_allclose(y[t], 0.5 * np.tanh(ct), **TIGHT)
+    np.testing.assert_allclose(cn[0], c0 * 2.0 ** -T, **TIGHT)
+
+
+def test_gru_zero_weights_closed_form():
+    # r = z = 1/2 and n = tanh(0) = 0, so h_t = 2^-t h0.
+    T = 9
+    d = _rand_case("gru", T=T, seed=2)
+    for p in d["params"]:
+        for k in p:
+            p[k] = np.zeros_like(p[k])
+    y, hn, _ = _oracle_run("gru", d)
+    h0 = d["h0"][0].astype(np.float64)
+    for t in range(T):
+        np.testing.assert_allclose(y[t], h0 * 2.0 ** -(t + 1), **TIGHT)
+
+
+@pytest.mark.parametrize("beta", [0.375, -1.75, 2.5])
+def test_gru_reset_gate_wraps_hidden_bias(beta):
+    # W = 0, every bias 0 except b_hn = beta, h0 = 0: r = z = 1/2, so
+    # h_1 = (1 - 1/2) tanh(r * beta) = tanh(beta / 2) / 2. Were b_hn outside
+    # the reset product the value would be tanh(beta) / 2.
+    H = 3
+    d = _rand_case("gru", T=1, B=2, H=H, seed=3, h0=False)
+    p = d["params"][0]
+    for k in p:
+        p[k] = np.zeros_like(p[k])
+    p["b_hh"][2 * H:] = beta
+    y, _, _ = _oracle_run("gru", d)
+    np.testing.assert_allclose(y[0], np.full((2, H), 0.5 * math.tanh(beta / 2)), **TIGHT)
+
+
+def test_lstm_scalar_brute_force():
+    # H = 1, F = 1 with distinct hand-set gate weights: one step by hand.
+    wi = np.array([[0.5], [-0.25], [1.5], [0.75]])
+    wh = np.array([[0.1], [0.2], [-0.3], [0.4]])
+    bi = np.array([0.01, 0.02, 0.03, 0.04])
+    bh = np.array([-0.05, 0.06, -0.07, 0.08])
+    x, h, c = 0.8, -0.6, 0.9
+    pre = wi[:, 0] * x + wh[:, 0] * h + bi + bh
+    s = lambda v: 1.0 / (1.0 + math.exp(-v))
+    c1 = s(pre[1]) * c + s(pre[0]) * math.tanh(pre[2])
+    h1 = s(pre[3]) * math.tanh(c1)
+    hh, cc = oracle.lstm_cell(np.array([[x]]), np.array([[h]]), np.array([[c]]), wi, wh, bi, bh)
+    assert abs(hh[0, 0] - h1) < 1e-14 and abs(cc[0, 0] - c1) < 1e-14
+
+
+def test_gru_scalar_brute_force():
+    wi = np.array([[0.5], [-0.25], [1.5]])
+    wh = np.array([[0.1], [0.2], [-0.3]])
+    bi = np.array([0.01, 0.02, 0.03])
+    bh = np.array([-0.05, 0.06, -0.07])
+    x, h = 0.8, -0.6
+    s = lambda v: 1.0 / (1.0 + math.exp(-v))
+    r = s(wi[0, 0] * x + bi[0] + wh[0, 0] * h + bh[0])
+    z = s(wi[1, 0] * x + bi[1] + wh[1, 0] * h + bh[1])
+    n = math.tanh(wi[2, 0] * x + bi[2] + r * (wh[2, 0] * h + bh[2]))
+    h1 = (1 - z) * n + z * h
+    got = oracle.gru_cell(np.array([[x]]), np.array([[h]]), wi, wh, bi, bh)
+    assert abs(got[0, 0] - h1) < 1e-14
+
+
+def test_activation_functions_against_library():
+    x = np.linspace(-40, 40, 2001)
+    tx = torch.tensor(x)
+    np.testing.assert_allclose(oracle.sigmoid(x), torch.sigmoid(tx).numpy(), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(oracle.elu(x), torch.nn.functional.elu(tx).numpy(), rtol=1e-14, atol=1e-300)
+    # PyTorch's softplus switches to the identity above 20; the exact value
+    # differs there by log1p(exp(-x)) < 2.1e-9.
+    np.testing.assert_allclose(oracle.softplus(x), torch.nn.functional.softplus(tx).numpy(),
+                               rtol=0, atol=2.1e-9)
+    np.testing.assert_allclose(oracle.softplus(x[x < 20]), np.log1p(np.exp(x[x < 20])), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Library special cases: PyTorch CPU modules in float64
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bias", [True, False])
+def test_lstm_cell_matches_torch_lstmcell(bias):
+    d = _rand_case("lstm", T=1, B=5, F=7, H=6, bias=bias, seed=4)
+    p = d["params"][0]
+    cell = torch.nn.LSTMCell(7, 6, bias=bias).double()
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.tensor(p["w_ih"]))
+        cell.weight_hh.copy_(torch.tensor(p["w_hh"]))
+        if bias:
+            cell.bias_ih.copy_(torch.tensor(p["b_ih"]))
+            cell.bias_hh.copy_(torch.tensor(p["b_hh"]))
+        ht, ct = cell(torch.tensor(d["x"][0], dtype=torch.float64),
+                      (torch.tensor(d["h0"][0], dtype=torch.float64),
+                       torch.tensor(d["c0"][0], dtype=torch.float64)))
+    h, c = oracle.lstm_cell(d["x"][0], d["h0"][0], d["c0"][0], p["w_ih"], p["w_hh"],
+                            p["b_ih"], p["b_hh"])
+    np.testing.assert_allclose(h, ht.numpy(), **TIGHT)
+    np.testing.assert_allclose(c, ct.numpy(), **TIGHT)
+    # T = 1 through the sequence entry point equals one cell call.
+    y, hn, cn = _oracle_run("lstm", d)
+    np.testing.assert_allclose(y[0], ht.numpy(), **TIGHT)
+    np.testing.assert_allclose(cn[0], ct.numpy(), **TIGHT)
+
+
+@pytest.mark.parametrize("bias", [True, False])
+def test_gru_cell_matches_torch_grucell(bias):
+    d = _rand_case("gru", T=1, B=5, F=7, H=6, bias=bias, seed=5)
+    p = d["params"][0]
+    cell = torch.nn.GRUCell(7, 6, bias=bias).double()
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.tensor(p["w_ih"]))
+        cell.weight_hh.copy_(torch.tensor(p["w_hh"]))
+        if bias:
+            cell.bias_ih.copy_(torch.tensor(p["b_ih"]))
+            cell.bias_hh.copy_(torch.tensor(p["b_hh"]))
+        ht = cell(torch.tensor(d["x"][0], dtype=torch.float64),
+                  torch.tensor(d["h0"][0], dtype=torch.float64))
+    y, hn, _ = _oracle_run("gru", d)
+    np.testing.assert_allclose(y[0], ht.numpy(), **TIGHT)
+    np.testing.assert_allclose(hn[0], ht.numpy(), **TIGHT)
+
+
+CASES = [
+    # mode, L, bidir, P, bias, varlen
+    ("lstm", 1, False, 0, True, False),
+    ("lstm", 2, True, 0, True, False),
+    ("lstm", 2, True, 0, False, True),
+    ("lstm", 1, True, 0, True, True),
+    ("gru", 1, False, 0, True, False),
+    ("gru", 2, True, 0, True, True),
+    ("gru", 1, False, 0, False, False),
+    ("lstmp", 1, False, 3, True, False),
+    ("lstmp", 2, False, 3, True, False),
+    ("lstmp", 2, True, 2, False, True),
+]
+
+
+@pytest.mark.parametrize("mode,L,bidir,P,bias,varlen", CASES)
+def test_sequence_matches_torch_modules(mode, L, bidir, P, bias, varlen):
+    B, T = 5, 8
+    lengths = np.array([8, 3, 6, 1, 5], dtype=np.int32) if varlen else None
+    d = _rand_case(mode, T=T, B=B, F=6, H=4, P=P, L=L, bidir=bidir, bias=bias,
+                   lengths=lengths, seed=10 + L + 3 * bidir + P)
+    y_t, hn_t, cn_t = _torch_run(mode, d)
+    y, hn, cn = _oracle_run(mode, d)
+    _compare_padded(y, y_t, lengths)
+    np.testing.assert_allclose(hn, hn_t, **TIGHT)
+    if cn_t is not None:
+        np.testing.assert_allclose(cn, cn_t, **TIGHT)
+
+
+def test_packed_layout_matches_torch_packing():
+    lengths = np.array([7, 7, 5, 2, 1], dtype=np.int32)
+    d = synth.make_rnn_inputs("lstm", 7, 5, 3, 4, layout="packed", lengths=lengths, seed=6)
+    packed_t = torch.nn.utils.rnn.pack_padded_sequence(
+        torch.tensor(np.nan_to_num(d["x_padded"])), torch.tensor(lengths, dtype=torch.int64))
+    np.testing.assert_array_equal(oracle.pack_sequence(d["x_padded"], lengths), packed_t.data.numpy())
+    np.testing.assert_array_equal(d["x"], packed_t.data.numpy())
+    bs, off = oracle.packed_offsets(lengths)
+    np.testing.assert_array_equal(bs, packed_t.batch_sizes.numpy())
+    back = oracle.unpack_sequence(d["x"], lengths, 7)
+    np.testing.assert_array_equal(np.isnan(back), np.isnan(d["x_padded"]))
+    np.testing.assert_array_equal(np.nan_to_num(back), np.nan_to_num(d["x_padded"]))
+
+
+def test_oracle_rejects_projection_outside_lstm():
+    d = _rand_case("gru", T=2, seed=7)
+    with pytest.raises(ValueError):
+        oracle.rnn_forward("gru", d["x"], d["params"], proj_size=3)
+    with pytest.raises(ValueError):
+        oracle.rnn_forward("lstmp", d["x"], d["params"], proj_size=0)
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+def test_lstmp_identity_projection_reduces_to_lstm():
+    d = _rand_case("lstmp", T=6, B=3, F=5, H=4, P=4, seed=8)
+    d["params"][0]["w_hr"] = np.eye(4, dtype=np.float32)
+    y_p, hn_p, cn_p = _oracle_run("lstmp", d)
+    d2 = dict(d, proj_size=0)
+    d2["params"] = [{k: v for k, v in d["params"][0].items() if k != "w_hr"}]
+    y, hn, cn = _oracle_run("lstm", d2)
+    np.testing.assert_allclose(y_p, y, **TIGHT)
+    np.testing.assert_allclose(cn_p, cn, **TIGHT)
+
+
+def test_lstmp_zero_projection_gives_zero_output():
+    d = _rand_case("lstmp", T=5, B=3, F=5, H=4, P=2, seed=9, h0=False)
+    d["params"][0]["w_hr"] = np.zeros_like(d["params"][0]["w_hr"])
+    y, hn, cn = _oracle_run("lstmp", d)
+    assert np.all(y == 0) and np.all(hn == 0)
+    # Gates then depend on x only: c follows the zero-state recursion on x.
+    p = d["params"][0]
+    c = np.zeros((3, 4))
+    for t in range(5):
+        _, c = oracle.lstm_cell(d["x"][t], np.zeros((3, 2)), c, p["w_ih"], p["w_hh"], p["b_ih"], p["b_hh"])
+    np.testing.assert_allclose(cn[0], c, **TIGHT)
+
+
+@pytest.mark.parametrize("mode,P", [("lstm", 0), ("gru", 0), ("lstmp", 3)])
+def test_time_chunking_equals_one_run(mode, P):
+    d = _rand_case(mode, T=9, B=4, F=5, H=4, P=P, L=2, seed=11)
+    y, hn, cn = _oracle_run(mode, d)
+    d1 = dict(d, x=d["x"][:4], x_padded=d["x"][:4], T=4)
+    y1, hn1, cn1 = _oracle_run(mode, d1)
+    d2 = dict(d, x=d["x"][4:], x_padded=d["x"][4:], T=5, h0=hn1, c0=cn1)
+    y2, hn2, cn2 = _oracle_run(mode, d2)
+    np.testing.assert_allclose(np.concatenate([y1, y2]), y, **TIGHT)
+    np.testing.assert_allclose(hn2, hn, **TIGHT)
+    if cn is not None:
+        np.testing.assert_allclose(cn2, cn, **TIGHT)
+
+
+@pytest.mark.parametrize("mode,P", [("lstm", 0), ("gru", 0), ("lstmp", 2)])
+def test_varlen_rows_equal_single_sequence_runs(mode, P):
+    lengths = np.array([6, 6, 4, 2, 1], dtype=np.int32)
+    d = synth.make_rnn_inputs(mode, 6, 5, 3, 4, proj_size=P, num_layers=2, bidirectional=True,
+                              layout="packed", lengths=lengths, w_scale=0.6, h0_std=0.3,
+                              c0_std=0.3, seed=12)
+    y, hn, cn = _oracle_run(mode, d)
+    y_pad = oracle.unpack_sequence(y, lengths, 6)
+    for b, Lb in enumerate(lengths):
+        xb = d["x_padded"][:Lb, b:b + 1]
+        yb, hb, cb = oracle.rnn_forward(mode, xb, d["params"], h0=d["h0"][:, b:b + 1],
+                                        c0=None if cn is None else d["c0"][:, b:b + 1],
+                                        num_layers=2, bidirectional=True, proj_size=P)
+        np.testing.assert_allclose(y_pad[:Lb, b], yb[:, 0], **TIGHT)
+        np.testing.assert_allclose(hn[:, b], hb[:, 0], **TIGHT)
+        if cn is not None:
+            np.testing.assert_allclose(cn[:, b], cb[:, 0], **TIGHT)
+
+
+def test_packed_equals_padded():
+    lengths = np.array([9, 7, 7, 3, 1, 1], dtype=np.int32)
+    d = synth.make_rnn_inputs("lstm", 9, 6, 4, 5, num_layers=2, bidirectional=True,
+                              layout="packed", lengths=lengths, w_scale=0.5, seed=13)
+    y_pk, hn_pk, cn_pk = _oracle_run("lstm", d)
+    dp = dict(d, layout="padded", x=d["x_padded"])
+    y_pd, hn_pd, cn_pd = _oracle_run("lstm", dp)
+    np.testing.assert_allclose(oracle.pack_sequence(y_pd, lengths), y_pk, **TIGHT)
+    np.testing.assert_allclose(hn_pk, hn_pd, **TIGHT)
+    np.testing.assert_allclose(cn_pk, cn_pd, **TIGHT)
+
+
+def test_bidirectional_is_forward_plus_reversed_forward():
+    lengths = np.array([7, 5, 2], dtype=np.int32)
+    d = synth.make_rnn_inputs("lstm", 7, 3, 4, 3, bidirectional=True, lengths=lengths,
+                              w_scale=0.5, h0_std=0.4, c0_std=0.4, seed=14)
+    y, hn, cn = _oracle_run("lstm", d)
+    H = 3
+    for b, Lb in enumerate(lengths):
+        xb = d["x_padded"][:Lb, b:b + 1]
+        yf, hf, cf = oracle.rnn_forward("lstm", xb, [d["params"][0]], h0=d["h0"][0:1, b:b + 1],
+                                        c0=d["c0"][0:1, b:b + 1])
+        yr, hr, cr = oracle.rnn_forward("lstm", xb[::-1], [d["params"][1]], h0=d["h0"][1:2, b:b + 1],
+                                        c0=d["c0"][1:2, b:b + 1])
+        np.testing.assert_allclose(y[:Lb, b, :H], yf[:, 0], **TIGHT)
+        np.testing.assert_allclose(y[:Lb, b, H:], yr[::-1, 0], **TIGHT)
+        np.testing.assert_allclose(hn[1, b], hr[0, 0], **TIGHT)
+        np.testing.assert_allclose(cn[1, b], cr[0, 0], **TIGHT)
+
+
+# ---------------------------------------------------------------------------
+# RSSM prior
+# ---------------------------------------------------------------------------
+
+def _torch_rssm(w, actions, eps, s0=None, h0=None):
+    """PyTorch modules assembled from the RSSMPrior description (float64)."""
+    E, SA = w["w_as"].shape
+    Hb = w["w_hh"].shape[1]
+    S2 = w["w_2"].shape[0]
+    lin_as = torch.nn.Linear(SA, E)
+    gru = torch.nn.GRUCell(E, Hb)
+    lin1 = torch.nn.Linear(Hb, w["w_1"].shape[0])
+    lin2 = torch.nn.Linear(w["w_1"].shape[0], S2)
+    with torch.no_grad():
+        for mod, wk, bk in ((lin_as, "w_as", "b_as"), (lin1, "w_1", "b_1"), (lin2, "w_2", "b_2")):
+            mod.weight.copy_(torch.tensor(w[wk]))
+            mod.bias.copy_(torch.tensor(w[bk]))
+        gru.weight_ih.copy_(torch.tensor(w["w_ih"]))
+        gru.weight_hh.copy_(torch.tensor(w["w_hh"]))
+        gru.bias_ih.copy_(torch.tensor(w["b_ih"]))
+        gru.bias_hh.copy_(torch.tensor(w["b_hh"]))
+        B, T = actions.shape[:2]
+        S = S2 // 2
+        state = torch.zeros(B, S) if s0 is None else torch.tensor(s0, dtype=torch.float64)
+        belief = torch.zeros(B, Hb) if h0 is None else torch.tensor(h0, dtype=torch.float64)
+        outs = [[], [], [], []]
+        for t in range(T):
+            a = torch.tensor(actions[:, t], dtype=torch.float64)
+            e = torch.nn.functional.elu(lin_as(torch.cat([state, a], dim=-1)))
+            belief = gru(e, belief)
+            v = lin2(torch.nn.functional.elu(lin1(belief)))
+            mean, raw = v[:, :S], v[:, S:]
+            std = torch.nn.functional.softplus(raw) + 0.1
+            state = mean + torch.tensor(eps[:, t], dtype=torch.float64) * std
+            for lst, val in zip(outs, (mean, std, state, belief)):
+                lst.append(val)
+        return [torch.stack(o, 1).numpy() for o in outs]
+
+
+def test_rssm_matches_torch_modules():
+    d = synth.make_rssm_inputs(6, 9, state_dim=5, action_dim=3, embed_dim=7, belief_dim=8,
+                               seed=15, s0_std=0.5, h0_std=0.5)
+    got = oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"], d["s0"], d["h0"])
+    ref = _torch_rssm(d["weights"], d["actions"], d["eps"], d["s0"], d["h0"])
+    for g, r in zip(got, ref):
+        # softplus arguments here stay far below PyTorch's threshold of 20.
+        np.testing.assert_allclose(g, r, rtol=1e-11, atol=1e-12)
+
+
+def test_rssm_zero_weights_closed_form():
+    # beliefs = 0, means = 0, stds = softplus(0) + 0.1 = ln 2 + 0.1 and
+    # states = (ln 2 + 0.1) * eps at every step.
+    d = synth.make_rssm_inputs(4, 5, seed=16, zero_weights=True)
+    means, stds, states, beliefs = oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"])
+    k = math.log(2.0) + 0.1
+    assert np.all(beliefs == 0) and np.all(means == 0)
+    np.testing.assert_allclose(stds, np.full_like(stds, 0.7931471805599453), rtol=1e-15)
+    assert abs(k - 0.7931471805599453) < 1e-15
+    np.testing.assert_allclose(states, k * d["eps"].astype(np.float64), rtol=1e-15)
+
+
+def test_rssm_time_chunking_and_single_step():
+    d = synth.make_rssm_inputs(3, 8, state_dim=4, action_dim=2, embed_dim=6, belief_dim=5, seed=17)
+    full = oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"])
+    a = oracle.rssm_prior_unroll(d["actions"][:, :3], d["eps"][:, :3], d["weights"])
+    b = oracle.rssm_prior_unroll(d["actions"][:, 3:], d["eps"][:, 3:], d["weights"],
+                                 a[2][:, -1], a[3][:, -1])
+    for f, x, y in zip(full, a, b):
+        np.testing.assert_allclose(np.concatenate([x, y], axis=1), f, **TIGHT)
+    one = oracle.rssm_prior_step(np.zeros((3, 4)), np.zeros((3, 5)), d["actions"][:, 0],
+                                 d["eps"][:, 0], d["weights"])
+    for o, f in zip(one, full):
+        np.testing.assert_allclose(o, f[:, 0], **TIGHT)
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding and the bf16 tolerance headroom
+# ---------------------------------------------------------------------------
+
+def test_bf16_rounding_three_ways_agree():
+    rng = np.random.default_rng(18)
+    v = np.concatenate([rng.normal(0, 1, 5000), rng.normal(0, 1e4, 500),
+                        [0.0, -0.0, 1.0, 1.00390625, 1.005859375, 1.0078125, -2.5, 3.0e38]]).astype(np.float32)
+    a = oracle.round_to_bf16(v)
+    b = synth.bf16_round(v).astype(np.float64)
+    c = torch.tensor(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(a, c)
+    # Ties go to even: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7.
+    assert oracle.round_to_bf16(np.float32(1.00390625)) == 1.0
+    assert oracle.round_to_bf16(np.float32(1.005859375)) == 1.0078125
+
+
+@pytest.mark.parametrize("mode,H,P,T,L", [("gru", 64, 0, 48, 1), ("lstmp", 128, 32, 64, 2)])
+def test_bf16_state_rounding_stays_inside_tolerance(mode, H, P, T, L):
+    # Rounding the recurrent operand (h, and LSTMP's m) and the layer output to
+    # bf16 every step must stay well inside the 2e-2 absolute bound.
+    d = synth.make_rnn_inputs(mode, T, 16, 48, H, proj_size=P, num_layers=L, dtype="bf16",
+                              w_scale=1.0 / np.sqrt(H), h0_std=0.1 if mode == "gru" else 0.0,
+                              seed=19)
+    y, hn, cn = _oracle_run(mode, d)
+    ye, hne, cne = _oracle_run(mode, d, emulate_bf16=True)
+    assert np.max(np.abs(ye - y)) < 5e-3
+    assert np.max(np.abs(hne - hn)) < 5e-3
