@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the recurrence forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|1..5]
+
+A step is one rnn_forward of the whole hot path for the workload (every
+kernel it enqueues: input-projection GEMMs, scans, or the RSSM kernel) on
+seeded synthetic inputs already resident in HBM. Prints ONE JSON line with
+the throughput in timestep*batch/s, the roofline of the dominant kernel
+(timed with HIP events around its launches inside the timed region) and the
+float64 CPU oracle timed on the host on a bounded sample of the same work.
+
+Default workload: the RSSM-prior unroll, B=50, T=50 (state 20, action 6,
+hidden 200, GRU hidden 200, fp32).
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "f32_mfma": 157.3, "f32_vector": 157.3}
+
+KIND_NAMES = {1: "gemm_xw", 2: "scan", 3: "rssm"}
+
+# The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
+# apache/tvm PR "[TOPI] TE implementation of LSTM using scan", benchmark
+# thread): timestep*batch per second for the TE-scan and Relay-unrolled LSTM.
+PAGES_CONTEXT = {
+    "lstm_t80_b1": {"tvm_te_scan": 80 / 48.967991919999996e-3, "tvm_relay_unrolled": 80 / 14.4790252e-3},
+    "lstm_t256_b1_small": {"tvm_te_scan": 256 / 0.14541639e-3, "tvm_relay_unrolled": 256 / 2.62690786e-3},
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="rssm_b50_t50")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--tile-batch", type=int, default=0)
+    ap.add_argument("--tile-hidden", type=int, default=0)
+    return ap.parse_args()
+
+
+def _hip():
+    """The HIP runtime already loaded in this process (torch's)."""
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+    h = ctypes.CDLL(path or "libamdhip64.so.7")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def algorithmic(spec, d):
+    """Algorithmic flops and HBM bytes per launch, by kernel kind and layer."""
+    import synth  # noqa: F401
+    out = {}
+    if spec.mode == "rssm":
+        B, T, S, A, E, Hb = d["B"], d["T"], d["state_dim"], d["action_dim"], d["embed_dim"], d["belief_dim"]
+        per_tok = 2 * (E * (S + A) + 3 * Hb * (E + Hb) + E * Hb + 2 * S * E)
+        weights = 4 * (E * (S + A) + E + 6 * Hb * (E + Hb) / 2 + 6 * Hb + E * Hb + E + 2 * S * E + 2 * S)
+        io = 4 * B * T * (A + S + 3 * S + Hb)
+        out[3] = [{"flops": per_tok * B * T, "bytes": weights + io, "tokens": B * T}]
+        return out
+    D = 2 if spec.bidirectional else 1
+    gates = 3 if spec.mode == "gru" else 4
+    H = spec.hidden_size
+    G = gates * H
+    K = spec.proj_size if spec.mode == "lstmp" else H
+    es = 2 if spec.dtype == "bf16" else 4
+    L = d["lengths"]
+    tokens = int(L.sum()) if L is not None else spec.T * spec.B
+    rows = tokens if spec.layout == "packed" else spec.T * spec.B
+    gemms, scans = [], []
+    for layer in range(spec.num_layers):
+        in_l = spec.input_size if layer == 0 else D * K
+        gemms.append({"flops": 2 * rows * D * G * in_l,
+                      "bytes": rows * in_l * es + D * G * in_l * es + rows * D * G * 4, "tokens": tokens})
+        fl = 2 * tokens * D * G * K
+        if spec.mode == "lstmp":
+            fl += 2 * tokens * D * spec.proj_size * H
+        scans.append({"flops": fl, "bytes": tokens * D * (G * 4 + K * es), "tokens": tokens})
+    out[1] = gemms
+    out[2] = scans
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the recurrence shards by batch with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import gru_sequence_scan_amd as gss
+    import synth
+
+    name = synth.ORDER[int(args.workload) - 1] if args.workload.isdigit() else args.workload
+    spec = synth.spec(name)
+    d = synth.make_inputs(name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+
+    def T(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(dt)
+
+    # Build the C structs once (inputs resident in HBM before timing).
+    keep = []
+    if spec.mode == "rssm":
+        w = {k: T(v) for k, v in d["weights"].items()}
+        (out, ws) = gss.rssm_prior_unroll(T(d["actions"]), T(d["eps"]), w, tile_batch=args.tile_batch,
+                                          tile_hidden=args.tile_hidden, return_workspace=True)
+        B, Tn = d["B"], d["T"]
+        desc = gss.RnnDesc()
+        desc.mode, desc.dtype, desc.layout = 3, 0, 2
+        desc.T, desc.B, desc.num_layers, desc.has_bias = Tn, B, 1, 1
+        desc.state_dim, desc.action_dim = d["state_dim"], d["action_dim"]
+        desc.embed_dim, desc.belief_dim, desc.scale_lb = d["embed_dim"], d["belief_dim"], 0.1
+        desc.tile_batch, desc.tile_hidden = args.tile_batch, args.tile_hidden
+        wt = gss.RnnWeights()
+        wt.w_as, wt.b_as, wt.w_1, wt.b_1, wt.w_2, wt.b_2 = (w[k].data_ptr() for k in
+                                                            ("w_as", "b_as", "w_1", "b_1", "w_2", "b_2"))
+        wt.w_ih[0], wt.w_hh[0], wt.b_ih[0], wt.b_hh[0] = (w[k].data_ptr() for k in ("w_ih", "w_hh", "b_ih", "b_hh"))
+        acts, eps = T(d["actions"]), T(d["eps"])
+        io = gss.RnnIO()
+        io.x, io.noise = acts.data_ptr(), eps.data_ptr()
+        io.means, io.stds, io.states, io.beliefs = (o.data_ptr() for o in out)
+        keep += [w, acts, eps, out]
+        tokens = B * Tn
+        config = {"workload": name, "B": B, "T": Tn, "state": d["state_dim"], "action": d["action_dim"],
+                  "hidden": d["embed_dim"], "gru_hidden": d["belief_dim"]}
+        lengths = None
+    else:
+        params = [{k: T(v) for k, v in p.items() if v is not None} for p in d["params"]]
+        x = T(d["x"])
+        (out, ws) = gss.rnn_forward(spec.mode, x, params, lengths=d["lengths"], layout=spec.layout,
+                                    num_layers=spec.num_layers, bidirectional=spec.bidirectional,
+                                    proj_size=spec.proj_size, tile_batch=args.tile_batch,
+                                    tile_hidden=args.tile_hidden, return_workspace=True)
+        y, hn, cn = out
+        D = 2 if spec.bidirectional else 1
+        desc = gss.RnnDesc()
+        desc.mode = gss.MODES[spec.mode]
+        desc.dtype = 1 if spec.dtype == "bf16" else 0
+        desc.layout = 1 if spec.layout == "packed" else 0
+        desc.T, desc.B = spec.T, spec.B
+        desc.input_size, desc.hidden_size, desc.proj_size = spec.input_size, spec.hidden_size, spec.proj_size
+        desc.num_layers, desc.bidirectional, desc.has_bias = spec.num_layers, int(spec.bidirectional), 1
+        desc.tile_batch, desc.tile_hidden = args.tile_batch, args.tile_hidden
+        wt = gss.RnnWeights()
+        for i, p in enumerate(params):
+            for k, v in p.items():
+                getattr(wt, k)[i] = v.data_ptr()
+        io = gss.RnnIO()
+        io.x, io.y, io.h_n = x.data_ptr(), y.data_ptr(), hn.data_ptr()
+        io.c_n = cn.data_ptr() if cn is not None else None
+        lengths = d["lengths"]
+        keep_len, io.lengths_host = gss.binding._len_ptr(lengths)
+        keep += [params, x, out, keep_len]
+        tokens = int(lengths.sum()) if lengths is not None else spec.T * spec.B
+        config = {"workload": name, "mode": spec.mode, "T": spec.T, "B": spec.B, "input": spec.input_size,
+                  "hidden": spec.hidden_size, "proj": spec.proj_size, "layers": spec.num_layers,
+                  "bidirectional": spec.bidirectional, "layout": spec.layout, "tokens": tokens}
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    hip = _hip()
+    lib = gss.lib()
+    lib.rnn_forward_profiled.restype = ctypes.c_int
+    lib.rnn_forward_profiled.argtypes = [ctypes.POINTER(gss.RnnDesc), ctypes.POINTER(gss.RnnWeights),
+                                         ctypes.POINTER(gss.RnnIO), ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    max_k = 8
+    ws_ptr, ws_n = ws.data_ptr(), ws.numel()
+
+    def step(evs=None, kinds=None, nk=None):
+        if evs is None:
+            st = lib.rnn_forward(ctypes.byref(desc), ctypes.byref(wt), ctypes.byref(io), ws_ptr, ws_n, stream)
+        else:
+            st = lib.rnn_forward_profiled(ctypes.byref(desc), ctypes.byref(wt), ctypes.byref(io), ws_ptr, ws_n,
+                                          stream, evs, 2 * max_k, kinds, ctypes.byref(nk))
+        if st != 0:
+            raise gss.RnnError(st, "rnn_forward")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if gss.rnn_read_status(ws_ptr, stream) != 0:
+        raise RuntimeError("device status error after warmup")
+
+    K = args.steps
+    ev_arrays = []
+    for _ in range(K):
+        arr = (ctypes.c_void_p * (2 * max_k))()
+        for j in range(2 * max_k):
+            h = ctypes.c_void_p()
+            hip.hipEventCreate(ctypes.byref(h))
+            arr[j] = h.value
+        ev_arrays.append(arr)
+    kinds = (ctypes.c_int * max_k)()
+    nk = ctypes.c_int(0)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(ev_arrays[i], kinds, nk)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    status = gss.rnn_read_status(ws_ptr, stream)
+    if status != 0:
+        raise RuntimeError(f"device status {status} after timed steps")
+
+    n_k = nk.value
+    per_kernel = [[] for _ in range(n_k)]
+    for arr in ev_arrays:
+        for j in range(min(n_k, max_k)):
+            ms = ctypes.c_float(0)
+            hip.hipEventElapsedTime(ctypes.byref(ms), arr[2 * j], arr[2 * j + 1])
+            per_kernel[j].append(ms.value)
+    for arr in ev_arrays:
+        for j in range(2 * max_k):
+            hip.hipEventDestroy(arr[j])
+    kind_list = [kinds[j] for j in range(min(n_k, max_k))]
+    algo = algorithmic(spec, d)
+    kernels = []
+    seen = {}
+    for j, kd in enumerate(kind_list):
+        idx = seen.get(kd, 0)
+        seen[kd] = idx + 1
+        a = algo[kd][idx]
+        avg_ms = float(np.mean(per_kernel[j]))
+        kernels.append({"kernel": KIND_NAMES[kd], "index": idx, "avg_us": avg_ms * 1e3,
+                        "min_us": float(np.min(per_kernel[j])) * 1e3, "flops": a["flops"], "bytes": a["bytes"]})
+    dom = max(kernels, key=lambda k: k["avg_us"])
+    if dom["kernel"] == "rssm":
+        bound, peak, unit = "alu", PEAK_TFLOPS["f32_vector"], "TFLOP/s"
+        achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
+        traffic = None
+    elif dom["kernel"] == "scan" and spec.B < 16:
+        bound, peak, unit = "alu", PEAK_TFLOPS["f32_vector"], "TFLOP/s"
+        achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
+        traffic = None
+    else:
+        bound, unit = "mfma", "TFLOP/s"
+        peak = PEAK_TFLOPS["bf16"] if spec.dtype == "bf16" else PEAK_TFLOPS["f32_mfma"]
+        achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
+        traffic = None
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+                "traffic": traffic, "kernel": f"{dom['kernel']}[{dom['index']}]", "avg_us": dom["avg_us"]}
+
+    ms_per_step = elapsed / K * 1e3
+    value = tokens / (elapsed / K)
+    ctx = PAGES_CONTEXT.get(name)
+    vs = (value / max(ctx.values())) if ctx else None
+    rec = {
+        "metric": "timestep·batch/s per RNN config", "value": value, "unit": "timestep·batch/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": vs,
+        "dtype": spec.dtype, "data": "synthetic", "config": config,
+        "roofline": roofline, "kernels": kernels,
+    }
+    if ctx:
+        rec["pages_context"] = {k: v for k, v in ctx.items()}
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline_any(spec, d, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_any(spec, d, seconds):
+    """The float64 oracle on the host, on a bounded sample of the workload:
+    the RSSM unroll is repeated whole; for the recurrent stacks the sample is
+    a subset of batch rows over all their timesteps (rows are independent),
+    sized from a one-row probe to take about `seconds`."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    if spec.mode == "rssm":
+        t0 = time.perf_counter()
+        tokens, runs = 0, 0
+        while True:
+            oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"])
+            tokens += d["B"] * d["T"]
+            runs += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        el = time.perf_counter() - t0
+        sample = f"whole unroll (B={d['B']}, T={d['T']}) x{runs}, {el:.1f} s"
+    else:
+        L = d["lengths"]
+        order = np.random.default_rng(0).permutation(spec.B)
+
+        def run(rows):
+            sub = np.sort(order[:rows])
+            lengths = None if L is None else L[sub]
+            if spec.layout == "packed":
+                x = oracle.pack_sequence(np.nan_to_num(d["x_padded"][:, sub]), lengths)
+            else:
+                x = d["x"][:, sub]
+            t0 = time.perf_counter()
+            oracle.rnn_forward(spec.mode, x, d["params"], lengths=lengths, num_layers=spec.num_layers,
+                               bidirectional=spec.bidirectional, proj_size=spec.proj_size,
+                               layout=spec.layout)
+            el = time.perf_counter() - t0
+            return (int(lengths.sum()) if lengths is not None else spec.T * rows), el
+
+        _, t1 = run(1)
+        rows = int(min(spec.B, max(1, seconds / max(t1, 1e-6))))
+        tokens, el = run(rows)
+        sample = f"{rows} of {spec.B} batch rows over all timesteps, {el:.1f} s"
+    return {"value": tokens / el, "unit": "timestep·batch/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample}
+
+
+if __name__ == "__main__":
+    main()

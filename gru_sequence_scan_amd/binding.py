@@ -1,0 +1,344 @@
+"""ctypes binding of include/rnn.h plus tensor marshalling.
+
+Only argument marshalling happens here: shape and dtype checks, re-layout of
+tensors whose memory is not C-dense (pytorch/rl PR "LSTM/GRU scan: canonical
+strides + ...": a tensor can pass is_contiguous() yet carry strides that a
+pointer-based kernel cannot honour), allocation of outputs and workspace
+with torch, and the call on torch's current HIP stream.
+"""
+
+import ctypes
+import os
+
+import torch
+
+RNN_ABI_VERSION = 1
+RNN_MAX_LAYERS = 8
+RNN_MAX_LD = 2 * RNN_MAX_LAYERS
+
+MODES = {"lstm": 0, "gru": 1, "lstmp": 2, "rssm": 3}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+LAYOUTS = {"padded": 0, "packed": 1, "batch_major": 2}
+STATUS = {
+    0: "RNN_OK", -1: "RNN_E_NULL", -2: "RNN_E_SHAPE", -3: "RNN_E_UNSUPPORTED",
+    -4: "RNN_E_LENGTHS", -5: "RNN_E_WORKSPACE", -6: "RNN_E_ALIGN", -7: "RNN_E_DEVICE",
+    -8: "RNN_E_HIP", -9: "RNN_E_TIMEOUT", -10: "RNN_E_PLAN",
+}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path():
+    return os.path.join(_PKG, "_lib", "librnn_gfx950.so")
+
+
+class RnnDesc(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int32), ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("T", ctypes.c_int32), ("B", ctypes.c_int32), ("input_size", ctypes.c_int32),
+        ("hidden_size", ctypes.c_int32), ("proj_size", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32), ("bidirectional", ctypes.c_int32),
+        ("has_bias", ctypes.c_int32), ("state_dim", ctypes.c_int32),
+        ("action_dim", ctypes.c_int32), ("embed_dim", ctypes.c_int32),
+        ("belief_dim", ctypes.c_int32), ("scale_lb", ctypes.c_float),
+        ("tile_batch", ctypes.c_int32), ("tile_hidden", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 6),
+    ]
+
+
+_PtrArr = ctypes.c_void_p * RNN_MAX_LD
+
+
+class RnnWeights(ctypes.Structure):
+    _fields_ = [
+        ("w_ih", _PtrArr), ("w_hh", _PtrArr), ("b_ih", _PtrArr), ("b_hh", _PtrArr),
+        ("w_hr", _PtrArr), ("w_as", ctypes.c_void_p), ("b_as", ctypes.c_void_p),
+        ("w_1", ctypes.c_void_p), ("b_1", ctypes.c_void_p), ("w_2", ctypes.c_void_p),
+        ("b_2", ctypes.c_void_p),
+    ]
+
+
+class RnnIO(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p), ("lengths_host", ctypes.POINTER(ctypes.c_int32)),
+        ("h0", ctypes.c_void_p), ("c0", ctypes.c_void_p), ("s0", ctypes.c_void_p),
+        ("noise", ctypes.c_void_p), ("y", ctypes.c_void_p), ("h_n", ctypes.c_void_p),
+        ("c_n", ctypes.c_void_p), ("means", ctypes.c_void_p), ("stds", ctypes.c_void_p),
+        ("states", ctypes.c_void_p), ("beliefs", ctypes.c_void_p),
+    ]
+
+
+class RnnError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({rnn_strerror(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """Load the native library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"native library {path} is missing; build it with "
+                               "`python -m gru_sequence_scan_amd.build`")
+        L = ctypes.CDLL(path)
+        L.rnn_abi_version.restype = ctypes.c_int
+        L.rnn_abi_version.argtypes = []
+        L.rnn_strerror.restype = ctypes.c_char_p
+        L.rnn_strerror.argtypes = [ctypes.c_int]
+        L.rnn_workspace_bytes.restype = ctypes.c_int
+        L.rnn_workspace_bytes.argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.rnn_forward.restype = ctypes.c_int
+        L.rnn_forward.argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(RnnWeights),
+                                  ctypes.POINTER(RnnIO), ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]
+        L.rnn_read_status.restype = ctypes.c_int
+        L.rnn_read_status.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
+        L.rnn_device_check.restype = ctypes.c_int
+        L.rnn_device_check.argtypes = []
+        if L.rnn_abi_version() != RNN_ABI_VERSION:
+            raise RuntimeError("native library ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# Raw C entry points
+# ---------------------------------------------------------------------------
+
+def rnn_abi_version():
+    return lib().rnn_abi_version()
+
+
+def rnn_strerror(status):
+    return lib().rnn_strerror(int(status)).decode()
+
+
+def _len_ptr(lengths):
+    if lengths is None:
+        return None, None
+    arr = (ctypes.c_int32 * len(lengths))(*[int(v) for v in lengths])
+    return arr, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+
+
+def rnn_workspace_bytes(desc, lengths=None):
+    keep, lp = _len_ptr(lengths)
+    n = ctypes.c_size_t(0)
+    st = lib().rnn_workspace_bytes(ctypes.byref(desc), lp, ctypes.byref(n))
+    if st != 0:
+        raise RnnError(st, "rnn_workspace_bytes")
+    return n.value
+
+
+def rnn_forward_raw(desc, weights, io, workspace_ptr, ws_bytes, stream_ptr):
+    """Direct call of the C rnn_forward; returns the status code."""
+    return lib().rnn_forward(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(io),
+                             ctypes.c_void_p(workspace_ptr), ctypes.c_size_t(ws_bytes),
+                             ctypes.c_void_p(stream_ptr))
+
+
+def rnn_read_status(workspace_ptr, stream_ptr):
+    v = ctypes.c_int(0)
+    st = lib().rnn_read_status(ctypes.c_void_p(workspace_ptr), ctypes.c_void_p(stream_ptr), ctypes.byref(v))
+    if st != 0:
+        raise RnnError(st, "rnn_read_status")
+    return v.value
+
+
+def rnn_device_check():
+    return lib().rnn_device_check()
+
+
+# ---------------------------------------------------------------------------
+# Tensor marshalling
+# ---------------------------------------------------------------------------
+
+def _c_dense(t):
+    """True when the memory of t is laid out in C order (strides of size-1
+    dimensions do not matter to a pointer-based kernel)."""
+    expect = 1
+    for size, stride in zip(reversed(t.shape), reversed(t.stride())):
+        if size != 1 and stride != expect:
+            return False
+        expect *= size
+    return True
+
+
+def _dense(t):
+    if t is None:
+        return None
+    if _c_dense(t):
+        return t
+    out = torch.empty(t.shape, dtype=t.dtype, device=t.device)
+    out.copy_(t)
+    return out
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_ptr(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return None
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype} != {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: device {t.device} != {device}")
+    return _dense(t)
+
+
+def _call(desc, w, io, lengths, device, keep):
+    ws_bytes = rnn_workspace_bytes(desc, lengths)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device)
+    keep.append(ws)
+    st = rnn_forward_raw(desc, w, io, ws.data_ptr(), ws.numel(), _stream_ptr(device))
+    if st != 0:
+        raise RnnError(st, "rnn_forward")
+    return ws
+
+
+def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padded",
+                num_layers=1, bidirectional=False, proj_size=0, hidden_size=None, y_out=None,
+                tile_batch=0, tile_hidden=0, return_workspace=False):
+    """Forward of an LSTM / GRU / LSTMP stack on the current HIP stream.
+
+    x: padded [T, B, F] or packed [N_tok, F] (float32 or bfloat16, on a GPU).
+    params: list over layer * D + direction of dicts with 'w_ih' [G, in_l],
+    'w_hh' [G, K], optional 'b_ih', 'b_hh' [G] and, for LSTMP, 'w_hr' [P, H].
+    lengths: host sequence of B ints (required for packed; for padded it
+    masks rows, which are then never written past their length).
+    Returns (y, h_n, c_n) with c_n None for GRU.
+    """
+    mode = mode.lower()
+    if mode not in ("lstm", "gru", "lstmp"):
+        raise ValueError(f"mode {mode!r}")
+    dtype, device = x.dtype, x.device
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype {dtype} not supported (float32, bfloat16)")
+    if device.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    D = 2 if bidirectional else 1
+    LD = num_layers * D
+    if len(params) != LD:
+        raise ValueError(f"expected {LD} parameter sets, got {len(params)}")
+    gates = 3 if mode == "gru" else 4
+    H = params[0]["w_hh"].shape[0] // gates if hidden_size is None else hidden_size
+    K = proj_size if mode == "lstmp" else H
+    F = x.shape[-1]
+    if lengths is not None:
+        lengths = [int(v) for v in (lengths.tolist() if hasattr(lengths, "tolist") else lengths)]
+    if layout == "packed":
+        if lengths is None:
+            raise ValueError("packed layout needs lengths")
+        B = len(lengths)
+        T = max(lengths)
+        n_tok = sum(lengths)
+        x = _check(x, "x", (n_tok, F), dtype, device)
+        y_shape = (n_tok, D * K)
+    else:
+        T, B = x.shape[0], x.shape[1]
+        x = _check(x, "x", (T, B, F), dtype, device)
+        y_shape = (T, B, D * K)
+    has_bias = params[0].get("b_ih") is not None
+    keep = [x]
+    w = RnnWeights()
+    for i, p in enumerate(params):
+        in_l = F if i < D else D * K
+        pw = {"w_ih": (gates * H, in_l), "w_hh": (gates * H, K)}
+        if has_bias:
+            pw.update({"b_ih": (gates * H,), "b_hh": (gates * H,)})
+        if mode == "lstmp":
+            pw["w_hr"] = (proj_size, H)
+        for name, shp in pw.items():
+            t = _check(p[name], f"params[{i}].{name}", shp, dtype, device)
+            keep.append(t)
+            getattr(w, name)[i] = _ptr(t)
+    h0 = _check(h0, "h0", (LD, B, K), dtype, device)
+    c0 = _check(c0, "c0", (LD, B, H), dtype, device) if mode != "gru" else None
+    keep += [h0, c0]
+    if y_out is None:
+        y = torch.empty(y_shape, dtype=dtype, device=device)
+    else:
+        if tuple(y_out.shape) != y_shape or y_out.dtype != dtype or not _c_dense(y_out):
+            raise ValueError("y_out must be a C-dense tensor of the output shape and dtype")
+        y = y_out
+    h_n = torch.empty((LD, B, K), dtype=dtype, device=device)
+    c_n = torch.empty((LD, B, H), dtype=dtype, device=device) if mode != "gru" else None
+
+    desc = RnnDesc()
+    desc.mode = MODES[mode]
+    desc.dtype = DTYPES[dtype]
+    desc.layout = LAYOUTS[layout]
+    desc.T, desc.B = T, B
+    desc.input_size, desc.hidden_size, desc.proj_size = F, H, proj_size if mode == "lstmp" else 0
+    desc.num_layers, desc.bidirectional, desc.has_bias = num_layers, int(bidirectional), int(has_bias)
+    desc.tile_batch, desc.tile_hidden = tile_batch, tile_hidden
+    io = RnnIO()
+    io.x = _ptr(x)
+    keep_len, io.lengths_host = _len_ptr(lengths)
+    io.h0, io.c0 = _ptr(h0), _ptr(c0)
+    io.y, io.h_n, io.c_n = _ptr(y), _ptr(h_n), _ptr(c_n)
+    ws = _call(desc, w, io, lengths, device, keep)
+    out = (y, h_n, c_n)
+    return (out, ws) if return_workspace else out
+
+
+def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale_lb=0.1,
+                      tile_batch=0, tile_hidden=0, return_workspace=False):
+    """RSSM prior unrolled over actions [B, T, A] with injected eps [B, T, S].
+
+    weights: dict with w_as [E, S + A], b_as, w_ih [3Hb, E], w_hh [3Hb, Hb],
+    b_ih, b_hh, w_1 [E, Hb], b_1, w_2 [2S, E], b_2 (float32, on the GPU).
+    Returns (means, stds, states, beliefs) stacked on dim 1.
+    """
+    dtype, device = actions.dtype, actions.device
+    if dtype != torch.float32:
+        raise ValueError("the RSSM prior runs in float32")
+    B, T, A = actions.shape
+    S = eps.shape[2]
+    E, SA = weights["w_as"].shape
+    Hb = weights["w_hh"].shape[1]
+    if SA != S + A:
+        raise ValueError("w_as must have S + A columns")
+    shapes = {"w_as": (E, S + A), "b_as": (E,), "w_ih": (3 * Hb, E), "w_hh": (3 * Hb, Hb),
+              "b_ih": (3 * Hb,), "b_hh": (3 * Hb,), "w_1": (E, Hb), "b_1": (E,),
+              "w_2": (2 * S, E), "b_2": (2 * S,)}
+    wt = {k: _check(weights[k], k, s, dtype, device) for k, s in shapes.items()}
+    actions = _check(actions, "actions", (B, T, A), dtype, device)
+    eps = _check(eps, "eps", (B, T, S), dtype, device)
+    state0 = _check(state0, "state0", (B, S), dtype, device)
+    belief0 = _check(belief0, "belief0", (B, Hb), dtype, device)
+    keep = [actions, eps, state0, belief0] + list(wt.values())
+    w = RnnWeights()
+    w.w_as, w.b_as = _ptr(wt["w_as"]), _ptr(wt["b_as"])
+    w.w_ih[0], w.w_hh[0], w.b_ih[0], w.b_hh[0] = (_ptr(wt[k]) for k in ("w_ih", "w_hh", "b_ih", "b_hh"))
+    w.w_1, w.b_1, w.w_2, w.b_2 = (_ptr(wt[k]) for k in ("w_1", "b_1", "w_2", "b_2"))
+    means = torch.empty((B, T, S), dtype=dtype, device=device)
+    stds = torch.empty_like(means)
+    states = torch.empty_like(means)
+    beliefs = torch.empty((B, T, Hb), dtype=dtype, device=device)
+    desc = RnnDesc()
+    desc.mode, desc.dtype, desc.layout = MODES["rssm"], 0, LAYOUTS["batch_major"]
+    desc.T, desc.B = T, B
+    desc.num_layers, desc.bidirectional, desc.has_bias = 1, 0, 1
+    desc.state_dim, desc.action_dim, desc.embed_dim, desc.belief_dim = S, A, E, Hb
+    desc.scale_lb = scale_lb
+    desc.tile_batch, desc.tile_hidden = tile_batch, tile_hidden
+    io = RnnIO()
+    io.x, io.noise, io.s0, io.h0 = _ptr(actions), _ptr(eps), _ptr(state0), _ptr(belief0)
+    io.means, io.stds, io.states, io.beliefs = _ptr(means), _ptr(stds), _ptr(states), _ptr(beliefs)
+    ws = _call(desc, w, io, None, device, keep)
+    out = (means, stds, states, beliefs)
+    return (out, ws) if return_workspace else out

@@ -1,0 +1,198 @@
+// Kernel 1: the input-hidden dense op hoisted out of the time loop.
+//
+//   Gx[m, n] = sum_k X[m, k] * W_dir(n)[n mod G, k] + bias(n)
+//
+// for every token row m at once (apache/tvm PR "[TOPI] TE implementation of
+// LSTM using scan", description: the initial input-hidden dense is one of the
+// three dense ops of an LSTM). Both directions of a bidirectional layer share
+// one launch (N = D * G). bias(n) folds b_ih and, except for the GRU n gate
+// whose b_hn sits inside the reset product, b_hh.
+//
+// gfx950 design: 128x128 output tile per 256-thread workgroup, 4 waves in a
+// 2x2 arrangement, each wave a 64x64 block of 32x32 MFMA tiles
+// (v_mfma_f32_32x32x16_bf16 for bf16 operands, v_mfma_f32_32x32x2_f32 for
+// fp32). K advances 64 bytes per stage through double-buffered LDS; global
+// loads of the next stage are in flight while the current one is multiplied.
+// Every lane reads whole 16-byte chunks from LDS: the k index a lane supplies
+// to each MFMA step is permuted identically for both operands, which leaves
+// each dot product unchanged. Output tiles are dealt to XCDs in contiguous
+// runs so that tiles sharing X rows share an L2.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace rnnk {
+
+namespace {
+
+constexpr int kBM = 128;
+constexpr int kBN = 128;
+constexpr int kRowBytes = 64;        // one K stage of one row
+constexpr int kLdsRow = 80;          // padded LDS row stride (bytes)
+constexpr int kTileBytes = kBM * kLdsRow;
+
+template <typename DT>
+struct Mfma;
+
+template <>
+struct Mfma<bf16> {
+  static constexpr int kSteps = 2;  // 16 k per step, 32 k per stage
+  __device__ static void run(const char* a_row, const char* b_row, int half, f32x16& acc) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(a_row + (2 * s + half) * 16);
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(b_row + (2 * s + half) * 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    }
+  }
+};
+
+template <>
+struct Mfma<float> {
+  static constexpr int kSteps = 8;  // 2 k per step, 16 k per stage
+  __device__ static void run(const char* a_row, const char* b_row, int half, f32x16& acc) {
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(a_row + (2 * half) * 16);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(a_row + (2 * half + 1) * 16);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(b_row + (2 * half) * 16);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(b_row + (2 * half + 1) * 16);
+    const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s], bv[s], acc, 0, 0, 0);
+  }
+};
+
+// Load the 16-byte chunk `cc` (of four) of row `row` for the K stage at k0.
+template <typename DT>
+__device__ __forceinline__ u32x4 load_chunk(const DT* base, int rows, int K, int row, int k0, int cc,
+                                            bool vec_ok) {
+  constexpr int kEpc = 16 / sizeof(DT);
+  const int k = k0 + cc * kEpc;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row >= rows) return v;
+  const DT* p = base + (size_t)row * K + k;
+  if (vec_ok && k + kEpc <= K) return *reinterpret_cast<const u32x4*>(p);
+  DT tmp[kEpc];
+#pragma unroll
+  for (int e = 0; e < kEpc; ++e) tmp[e] = (k + e < K) ? p[e] : (DT)0.0f;
+  __builtin_memcpy(&v, tmp, 16);
+  return v;
+}
+
+template <typename DT>
+__global__ void __launch_bounds__(256) gemm_xw_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
+  constexpr int kBK = kRowBytes / sizeof(DT);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ntn = (a.N + kBN - 1) / kBN;
+  const int ntm = (a.M + kBM - 1) / kBM;
+  const int ntiles = ntn * ntm;
+
+  // XCD-aware order: workgroup ids are dealt round-robin over the 8 XCDs;
+  // give each XCD a contiguous run of tiles (row-major, N fastest).
+  int bid = blockIdx.x;
+  const int per_xcd = ntiles / 8;
+  if (bid < per_xcd * 8) bid = (bid & 7) * per_xcd + (bid >> 3);
+  const int tile_m = bid / ntn, tile_n = bid - tile_m * ntn;
+  const int m0 = tile_m * kBM, n0 = tile_n * kBN;
+
+  const DT* A = reinterpret_cast<const DT*>(a.A);
+  // Rows of this thread's two chunks (A and B use the same mapping).
+  const int c0 = tid, c1 = tid + 256;
+  const int r0 = c0 >> 2, cc0 = c0 & 3, r1 = c1 >> 2, cc1 = c1 & 3;
+  // B rows: output column n -> direction and weight row.
+  auto wrow = [&](int r, const DT*& base) -> int {
+    const int n = n0 + r;
+    if (n >= a.N) { base = nullptr; return 0; }
+    const int dir = n / a.G;
+    base = reinterpret_cast<const DT*>(a.W[dir]);
+    return n - dir * a.G;
+  };
+  const DT* wb0; const DT* wb1;
+  const int wr0 = wrow(r0, wb0), wr1 = wrow(r1, wb1);
+
+  const int nk = (a.K + kBK - 1) / kBK;
+  u32x4 ra0, ra1, rb0, rb1;
+  auto gload = [&](int k0) {
+    ra0 = load_chunk<DT>(A, a.M, a.K, m0 + r0, k0, cc0, a.vec_ok);
+    ra1 = load_chunk<DT>(A, a.M, a.K, m0 + r1, k0, cc1, a.vec_ok);
+    rb0 = wb0 ? load_chunk<DT>(wb0, a.G, a.K, wr0, k0, cc0, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
+    rb1 = wb1 ? load_chunk<DT>(wb1, a.G, a.K, wr1, k0, cc1, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto lstore = [&](int buf) {
+    *reinterpret_cast<u32x4*>(&smem[buf][0][r0 * kLdsRow + cc0 * 16]) = ra0;
+    *reinterpret_cast<u32x4*>(&smem[buf][0][r1 * kLdsRow + cc1 * 16]) = ra1;
+    *reinterpret_cast<u32x4*>(&smem[buf][1][r0 * kLdsRow + cc0 * 16]) = rb0;
+    *reinterpret_cast<u32x4*>(&smem[buf][1][r1 * kLdsRow + cc1 * 16]) = rb1;
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    const char* As = smem[buf][0];
+    const char* Bs = smem[buf][1];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const char* arow = As + (wm * 64 + i * 32 + l32) * kLdsRow;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const char* brow = Bs + (wn * 64 + j * 32 + l32) * kLdsRow;
+        Mfma<DT>::run(arow, brow, half, acc[i][j]);
+      }
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: bias fold and fp32 store. 32x32 accumulator layout: lane holds
+  // column l32 and rows 8*(v/4) + 4*half + (v%4).
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + l32;
+    if (n >= a.N) continue;
+    float bias = 0.0f;
+    if (a.has_bias) {
+      const int dir = n / a.G, nr = n - dir * a.G;
+      bias = to_f32<DT>(reinterpret_cast<const DT*>(a.b_ih[dir])[nr]);
+      if (nr < a.hh_fold_rows) bias += to_f32<DT>(reinterpret_cast<const DT*>(a.b_hh[dir])[nr]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (m < a.M) a.C[(size_t)m * a.N + n] = acc[i][j][v] + bias;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream) {
+  const int ntn = (a.N + kBN - 1) / kBN;
+  const int ntm = (a.M + kBM - 1) / kBM;
+  const dim3 grid(ntn * ntm), block(256);
+  if (dtype_bf16)
+    hipLaunchKernelGGL(gemm_xw_kernel<bf16>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(gemm_xw_kernel<float>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rnnk

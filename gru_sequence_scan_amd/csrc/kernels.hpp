@@ -1,0 +1,96 @@
+// Launch interface between the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rnnk {
+
+// Kernel 1: Gx = X W^T + folded bias, both directions in one launch.
+struct GemmArgs {
+  const void* A;        // [M, K] storage dtype
+  const void* W[2];     // per direction [G, K]
+  const void* b_ih[2];  // per direction [G] (has_bias)
+  const void* b_hh[2];  // per direction [G] (has_bias)
+  float* C;             // [M, N] fp32, N = D * G
+  int M, N, K, G;
+  int hh_fold_rows;     // b_hh folded for gate rows < this (G, or 2H for GRU)
+  int has_bias;
+  int vec_ok;           // A and W rows 16-byte aligned (K * esize % 16 == 0)
+};
+hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream);
+
+// Kernel 2: persistent scan over time for one layer, all directions.
+enum ScanMode { kLSTM = 0, kGRU = 1, kLSTMP = 2 };
+
+struct ScanArgs {
+  int mode;          // ScanMode
+  int T;             // number of time steps looped over (T_max)
+  int B, H, K, P;    // K = recurrent width (H, or P for LSTMP)
+  int D;             // directions
+  int G;             // gate rows per direction
+  int packed;        // 1: rows of step t start at offsets[t]
+  int has_bias;
+  // tiling
+  int bb;            // batch rows per workgroup
+  int hs;            // hidden units per workgroup
+  int ns;            // workgroups per group (one group = one direction x batch block)
+  int ps;            // projection outputs per workgroup (LSTMP)
+  int nbb;           // batch blocks
+  int Kp, Hp;        // padded widths of the exchange rows (multiples of 32)
+  // per direction tensors (already offset to this layer)
+  const void* w_hh[2];
+  const void* w_hr[2];
+  const void* b_hh[2];
+  const void* h0[2];   // [B, K] or null
+  const void* c0[2];   // [B, H] or null
+  void* h_n[2];        // [B, K] or null
+  void* c_n[2];        // [B, H] or null
+  const float* gx;     // [rows, D * G]
+  void* y;             // [rows, D * K]
+  const int* lengths;  // device [B] or null (all T)
+  const int* offsets;  // device [T + 1] (packed)
+  // exchange and synchronisation (workspace)
+  void* hx;            // [2][D][B][Kp]
+  void* mx;            // [D][B][Hp] (LSTMP)
+  unsigned* counters;  // [D * nbb] counters, 64 bytes apart
+  int* status;
+};
+hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
+
+// Kernel 3: persistent RSSM-prior unroll.
+struct RssmArgs {
+  int B, T, S, A, E, Hb;
+  float scale_lb;
+  // tiling
+  int rows;          // batch rows per group
+  int ngroups;
+  int nw;            // workgroups per group
+  int h_per;         // GRU hidden units per workgroup
+  const float* w_as; const float* b_as;
+  const float* w_ih; const float* w_hh; const float* b_ih; const float* b_hh;
+  const float* w_1; const float* b_1; const float* w_2; const float* b_2;
+  const float* actions; const float* eps; const float* s0; const float* h0;
+  float* means; float* stds; float* states; float* beliefs;
+  // exchange (workspace)
+  float* ex_h;   // [2][B][Hbp]   whole h_t, ping-pong on t
+  float* ex_p;   // [2][B][nw][Ep] per-member partial sums of W_1 h_t
+  int Ep, Hbp;
+  unsigned* counters;  // [ngroups], 64 bytes apart
+  int* status;
+};
+hipError_t launch_rssm(const RssmArgs& a, hipStream_t stream);
+int rssm_lds_bytes(const RssmArgs& a);
+int rssm_max_rows();
+constexpr int kRssmMaxMembers = 64;
+int scan_lds_bytes(const ScanArgs& a, int esize);
+
+// Copy up to kIntsPerLaunch host ints into device memory through kernel
+// arguments (stream-ordered, no host staging buffer to keep alive).
+constexpr int kIntsPerLaunch = 480;
+hipError_t launch_write_ints(int* dst, const int* src, int n, hipStream_t stream);
+
+// Zero-fill of small workspace regions (counters, status word).
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace rnnk

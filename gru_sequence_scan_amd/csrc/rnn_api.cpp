@@ -1,0 +1,567 @@
+// Host side of the C ABI declared in include/rnn.h: argument validation,
+// workspace layout, launch planning and the enqueue of the kernels.
+//
+// Everything a call needs is derived from its arguments; the only state kept
+// between calls is a per-device cache of immutable facts (architecture name,
+// compute-unit count), filled once under a lock.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/rnn.h"
+#include "kernels.hpp"
+
+using namespace rnnk;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxLds = 160 * 1024;
+constexpr int kCounterBytes = 64;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int rup(int x, int m) { return (x + m - 1) / m * m; }
+int cdiv(int x, int m) { return (x + m - 1) / m; }
+
+// ---------------------------------------------------------------------------
+// Device facts
+// ---------------------------------------------------------------------------
+struct DeviceInfo {
+  bool ok = false;
+  int cus = 0;
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+bool g_dev_init[kMaxDevices] = {};
+
+int current_device_info(DeviceInfo* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RNN_E_DEVICE;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev_init[dev]) {
+    hipDeviceProp_t p;
+    DeviceInfo info;
+    if (hipGetDeviceProperties(&p, dev) == hipSuccess) {
+      info.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+      info.cus = p.multiProcessorCount;
+    }
+    g_dev[dev] = info;
+    g_dev_init[dev] = true;
+  }
+  *out = g_dev[dev];
+  return out->ok ? RNN_OK : RNN_E_DEVICE;
+}
+
+// ---------------------------------------------------------------------------
+// Validation
+// ---------------------------------------------------------------------------
+bool is_rnn_mode(int m) { return m == RNN_MODE_LSTM || m == RNN_MODE_GRU || m == RNN_MODE_LSTMP; }
+
+int validate_desc(const RnnDesc* d) {
+  if (!d) return RNN_E_NULL;
+  for (int r : d->reserved)
+    if (r != 0) return RNN_E_SHAPE;
+  if (d->dtype != RNN_DTYPE_F32 && d->dtype != RNN_DTYPE_BF16) return RNN_E_UNSUPPORTED;
+  if (d->T < 1 || d->B < 1) return RNN_E_SHAPE;
+  if (d->tile_batch < 0 || d->tile_hidden < 0) return RNN_E_SHAPE;
+  if (d->mode == RNN_MODE_RSSM_PRIOR) {
+    if (d->layout != RNN_LAYOUT_BATCH_MAJOR) return RNN_E_UNSUPPORTED;
+    if (d->dtype != RNN_DTYPE_F32) return RNN_E_UNSUPPORTED;
+    if (d->num_layers != 1 || d->bidirectional != 0 || d->proj_size != 0) return RNN_E_UNSUPPORTED;
+    if (!d->has_bias) return RNN_E_UNSUPPORTED;
+    if (d->state_dim < 1 || d->action_dim < 1 || d->embed_dim < 1 || d->belief_dim < 1) return RNN_E_SHAPE;
+    if (!std::isfinite(d->scale_lb)) return RNN_E_SHAPE;
+    const double big = (double)d->B * d->T * std::max({d->state_dim, d->belief_dim, d->action_dim});
+    if (big > 2e9) return RNN_E_SHAPE;
+    return RNN_OK;
+  }
+  if (!is_rnn_mode(d->mode)) return RNN_E_UNSUPPORTED;
+  if (d->layout != RNN_LAYOUT_PADDED && d->layout != RNN_LAYOUT_PACKED) return RNN_E_UNSUPPORTED;
+  if ((d->mode == RNN_MODE_LSTMP) != (d->proj_size > 0)) return RNN_E_UNSUPPORTED;
+  if (d->proj_size < 0) return RNN_E_SHAPE;
+  if (d->num_layers < 1 || d->num_layers > RNN_MAX_LAYERS) return RNN_E_SHAPE;
+  if (d->bidirectional != 0 && d->bidirectional != 1) return RNN_E_SHAPE;
+  if (d->input_size < 1 || d->hidden_size < 1) return RNN_E_SHAPE;
+  const int D = d->bidirectional ? 2 : 1;
+  const int G = (d->mode == RNN_MODE_GRU ? 3 : 4) * d->hidden_size;
+  const int K = d->mode == RNN_MODE_LSTMP ? d->proj_size : d->hidden_size;
+  const double rows = (double)d->T * d->B;
+  if (rows * D * G > 2e9 || rows * std::max(d->input_size, D * K) > 2e9) return RNN_E_SHAPE;
+  if ((double)d->hidden_size * std::max(d->input_size, D * K) > 2e9) return RNN_E_SHAPE;
+  return RNN_OK;
+}
+
+int validate_lengths(const RnnDesc* d, const int32_t* len, long long* n_tok, int* t_max) {
+  if (d->mode == RNN_MODE_RSSM_PRIOR) {
+    *n_tok = (long long)d->T * d->B;
+    *t_max = d->T;
+    return RNN_OK;
+  }
+  if (!len) {
+    if (d->layout == RNN_LAYOUT_PACKED) return RNN_E_LENGTHS;
+    *n_tok = (long long)d->T * d->B;
+    *t_max = d->T;
+    return RNN_OK;
+  }
+  long long s = 0;
+  int mx = 0;
+  for (int b = 0; b < d->B; ++b) {
+    if (len[b] < 1 || len[b] > d->T) return RNN_E_LENGTHS;
+    if (d->layout == RNN_LAYOUT_PACKED && b > 0 && len[b] > len[b - 1]) return RNN_E_LENGTHS;
+    s += len[b];
+    mx = std::max(mx, (int)len[b]);
+  }
+  *n_tok = s;
+  *t_max = mx;
+  return RNN_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ---------------------------------------------------------------------------
+// Workspace layout (independent of the launch plan, so rnn_workspace_bytes
+// needs no device)
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  size_t status, counters, ints, gx, inter0, inter1, hx, mx, ex_h, ex_p, total;
+  size_t counters_bytes;
+  int n_ints;
+};
+
+struct Dims {
+  int D, G, K, Kp, Hp, gates, esize;
+  long long rows;  // Gx / y rows per layer
+};
+
+Dims dims_of(const RnnDesc* d, long long n_tok) {
+  Dims m{};
+  m.D = d->bidirectional ? 2 : 1;
+  m.gates = d->mode == RNN_MODE_GRU ? 3 : 4;
+  m.G = m.gates * d->hidden_size;
+  m.K = d->mode == RNN_MODE_LSTMP ? d->proj_size : d->hidden_size;
+  m.Kp = rup(m.K, 32);
+  m.Hp = rup(d->hidden_size, 32);
+  m.esize = d->dtype == RNN_DTYPE_BF16 ? 2 : 4;
+  m.rows = d->layout == RNN_LAYOUT_PACKED ? n_tok : (long long)d->T * d->B;
+  return m;
+}
+
+WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
+  WsLayout w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, kAlign);
+    return at;
+  };
+  w.status = take(kAlign);
+  if (d->mode == RNN_MODE_RSSM_PRIOR) {
+    w.counters_bytes = (size_t)d->B * kCounterBytes;
+    w.counters = take(w.counters_bytes);
+    const int Hbp = rup(d->belief_dim, 4), Ep = rup(d->embed_dim, 4);
+    w.ex_h = take((size_t)2 * d->B * Hbp * 4);
+    w.ex_p = take((size_t)2 * d->B * kRssmMaxMembers * Ep * 4);
+    w.total = o;
+    return w;
+  }
+  const Dims m = dims_of(d, n_tok);
+  w.counters_bytes = (size_t)d->num_layers * m.D * d->B * kCounterBytes;
+  w.counters = take(w.counters_bytes);
+  w.n_ints = has_lengths ? d->B + d->T + 1 : 0;
+  w.ints = take((size_t)std::max(w.n_ints, 1) * 4);
+  w.gx = take((size_t)m.rows * m.D * m.G * 4);
+  const size_t inter = (size_t)m.rows * m.D * m.K * m.esize;
+  w.inter0 = d->num_layers > 1 ? take(inter) : 0;
+  w.inter1 = d->num_layers > 2 ? take(inter) : 0;
+  w.hx = take((size_t)2 * m.D * d->B * m.Kp * m.esize);
+  w.mx = d->mode == RNN_MODE_LSTMP ? take((size_t)m.D * d->B * m.Hp * m.esize) : 0;
+  w.total = o;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Launch planning
+// ---------------------------------------------------------------------------
+// Per-step time model (microseconds) from measurements on MI355X: a group
+// barrier with device-coherent exchange costs ~0.65 us plus ~9 ns per member;
+// the exchange read streams at roughly 100 GB/s per workgroup; MFMA and LDS
+// rates are those of one compute unit at 2.4 GHz.
+double barrier_us(int members) { return 0.65 + 0.009 * members; }
+
+double mm_us(bool mfma, int esize, int rows, int cols, int kp) {
+  if (mfma) {
+    const double tiles = (double)(rows / 16) * cdiv(cols, 16);
+    double mf_cycles, lds_bytes;
+    if (esize == 2) {
+      mf_cycles = tiles * (kp / 32) * 16.0 / 4.0;
+      lds_bytes = tiles * (kp / 32) * 2048.0;
+    } else {
+      mf_cycles = tiles * (kp / 4) * 32.0 / 4.0;
+      lds_bytes = tiles * (kp / 16) * 2048.0;
+    }
+    return std::max(mf_cycles, lds_bytes / 128.0) / 2400.0;
+  }
+  return (double)rows * cols * kp / 32.0 / 2400.0;
+}
+
+struct ScanPlan {
+  int bb, hs, ns, ps, nbb, lds;
+};
+
+int plan_scan(const RnnDesc* d, const Dims& m, int cus, ScanPlan* out) {
+  const int B = d->B, H = d->hidden_size, P = d->proj_size;
+  const bool lstmp = d->mode == RNN_MODE_LSTMP;
+  std::vector<int> bbs;
+  if (d->tile_batch > 0) {
+    bbs.push_back(d->tile_batch);
+  } else if (B >= 16) {
+    for (int bb = 16; bb <= std::min(64, rup(B, 16)); bb += 16) bbs.push_back(bb);
+  } else {
+    bbs.push_back(B);
+  }
+  std::vector<int> hss;
+  if (d->tile_hidden > 0) {
+    hss.push_back(d->tile_hidden);
+  } else {
+    for (int hs = 1; hs <= std::min(H, 256); hs *= 2) hss.push_back(hs);
+    if (std::find(hss.begin(), hss.end(), H) == hss.end() && H <= 256) hss.push_back(H);
+  }
+  double best = 1e30;
+  bool found = false;
+  for (int bb : bbs) {
+    if (bb < 1) continue;
+    const bool mfma = bb % 16 == 0;
+    for (int hs : hss) {
+      if (hs < 1 || bb * hs > 2048) continue;
+      const int ns = cdiv(H, hs);
+      const int nbb = cdiv(B, bb);
+      if ((long long)m.D * nbb * ns > cus) continue;
+      const int ps = lstmp ? cdiv(P, ns) : 0;
+      ScanArgs a{};
+      a.mode = d->mode == RNN_MODE_GRU ? kGRU : (lstmp ? kLSTMP : kLSTM);
+      a.bb = bb; a.hs = hs; a.ps = ps; a.Kp = m.Kp; a.Hp = m.Hp;
+      const int lds = scan_lds_bytes(a, m.esize);
+      if (lds > kMaxLds) continue;
+      const int rows = mfma ? bb : bb;
+      double t = barrier_us(ns) + 0.3 + (double)bb * m.Kp * m.esize / 100e3 +
+                 mm_us(mfma, m.esize, rows, m.gates * hs, mfma ? m.Kp : m.K) + bb * hs / 256.0 * 0.05;
+      if (lstmp)
+        t += barrier_us(ns) + 0.3 + (double)bb * m.Hp * m.esize / 100e3 +
+             mm_us(mfma, m.esize, rows, ps, mfma ? m.Hp : H);
+      t *= nbb > 0 ? 1.0 : 1.0;
+      if (t < best) {
+        best = t;
+        *out = ScanPlan{bb, hs, ns, ps, nbb, lds};
+        found = true;
+      }
+    }
+  }
+  return found ? RNN_OK : RNN_E_PLAN;
+}
+
+struct RssmPlan {
+  int rows, ngroups, nw, h_per, u_per, lds;
+};
+
+int plan_rssm(const RnnDesc* d, int cus, RssmPlan* out) {
+  const int B = d->B, S = d->state_dim, A = d->action_dim, E = d->embed_dim, Hb = d->belief_dim;
+  double best = 1e30;
+  bool found = false;
+  for (int rows = 1; rows <= rssm_max_rows(); ++rows) {
+    if (d->tile_batch > 0 && rows != d->tile_batch) continue;
+    const int ngroups = cdiv(B, rows);
+    for (int nw = 1; nw <= kRssmMaxMembers; ++nw) {
+      const int h_per = cdiv(Hb, nw);
+      if (d->tile_hidden > 0 && h_per != d->tile_hidden) continue;
+      if (nw > 1 && cdiv(Hb, nw - 1) == h_per) continue;  // same slices with fewer members
+      if ((long long)ngroups * nw > cus) continue;
+      if (rows * h_per > 256) continue;
+      RssmArgs a{};
+      a.S = S; a.A = A; a.E = E; a.Hb = Hb; a.rows = rows; a.nw = nw; a.h_per = h_per;
+      const int lds = rssm_lds_bytes(a);
+      if (lds > kMaxLds) continue;
+      // GRU slice + partial of W_1 + (redundant) partial sums, W_2 and W_as
+      const double macs = (double)rows * (3.0 * h_per * (E + Hb) + (double)E * h_per + (double)E * nw +
+                                          2.0 * S * E + (double)E * (S + A));
+      const double bytes = (double)rows * (Hb + (double)nw * E) * 4.0;
+      const double t = barrier_us(nw) + 0.3 + bytes / 100e3 + macs / 32.0 / 2400.0;
+      if (t < best) {
+        best = t;
+        *out = RssmPlan{rows, ngroups, nw, h_per, 0, lds};
+        found = true;
+      }
+    }
+  }
+  return found ? RNN_OK : RNN_E_PLAN;
+}
+
+// ---------------------------------------------------------------------------
+// Forward paths
+// ---------------------------------------------------------------------------
+int hip_status(hipError_t e) { return e == hipSuccess ? RNN_OK : RNN_E_HIP; }
+
+// Optional per-kernel event brackets (rnn_forward_profiled).
+struct Prof {
+  void* const* events = nullptr;
+  int n_events = 0;
+  int* kinds = nullptr;
+  int n = 0;
+  hipStream_t st = nullptr;
+  int begin(int kind) {
+    if (kinds && n < n_events / 2) kinds[n] = kind;
+    if (events && n < n_events / 2)
+      return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[2 * n]), st));
+    return RNN_OK;
+  }
+  int end() {
+    int rc = RNN_OK;
+    if (events && n < n_events / 2)
+      rc = hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[2 * n + 1]), st));
+    ++n;
+    return rc;
+  }
+};
+
+int check_ptr(const void* p, size_t elem) {
+  if (!p) return RNN_E_NULL;
+  return aligned(p, elem) ? RNN_OK : RNN_E_ALIGN;
+}
+
+int check_opt(const void* p, size_t elem) { return (!p || aligned(p, elem)) ? RNN_OK : RNN_E_ALIGN; }
+
+int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws, size_t ws_bytes,
+                 hipStream_t st, int cus, Prof& prof) {
+  int rc;
+  const void* req[] = {w->w_as, w->b_as, w->w_ih[0], w->w_hh[0], w->b_ih[0], w->b_hh[0], w->w_1, w->b_1,
+                       w->w_2, w->b_2, io->x, io->noise, io->means, io->stds, io->states, io->beliefs};
+  for (const void* p : req)
+    if ((rc = check_ptr(p, 4)) != RNN_OK) return rc;
+  if ((rc = check_opt(io->s0, 4)) != RNN_OK || (rc = check_opt(io->h0, 4)) != RNN_OK) return rc;
+  const WsLayout L = layout_of(d, 0, false);
+  if (!ws) return RNN_E_WORKSPACE;
+  if (ws_bytes < L.total) return RNN_E_WORKSPACE;
+  if (!aligned(ws, 16)) return RNN_E_ALIGN;
+  RssmPlan p;
+  if ((rc = plan_rssm(d, cus, &p)) != RNN_OK) return rc;
+
+  RssmArgs a{};
+  a.B = d->B; a.T = d->T; a.S = d->state_dim; a.A = d->action_dim; a.E = d->embed_dim; a.Hb = d->belief_dim;
+  a.scale_lb = d->scale_lb;
+  a.rows = p.rows; a.ngroups = p.ngroups; a.nw = p.nw; a.h_per = p.h_per;
+  a.w_as = (const float*)w->w_as; a.b_as = (const float*)w->b_as;
+  a.w_ih = (const float*)w->w_ih[0]; a.w_hh = (const float*)w->w_hh[0];
+  a.b_ih = (const float*)w->b_ih[0]; a.b_hh = (const float*)w->b_hh[0];
+  a.w_1 = (const float*)w->w_1; a.b_1 = (const float*)w->b_1;
+  a.w_2 = (const float*)w->w_2; a.b_2 = (const float*)w->b_2;
+  a.actions = (const float*)io->x; a.eps = (const float*)io->noise;
+  a.s0 = (const float*)io->s0; a.h0 = (const float*)io->h0;
+  a.means = (float*)io->means; a.stds = (float*)io->stds; a.states = (float*)io->states;
+  a.beliefs = (float*)io->beliefs;
+  a.ex_h = (float*)(ws + L.ex_h); a.ex_p = (float*)(ws + L.ex_p);
+  a.Ep = rup(d->embed_dim, 4); a.Hbp = rup(d->belief_dim, 4);
+  a.counters = (unsigned*)(ws + L.counters);
+  a.status = (int*)(ws + L.status);
+  // status word and counters are contiguous at the start of the workspace
+  if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
+  if ((rc = prof.begin(3)) != RNN_OK) return rc;
+  if ((rc = hip_status(launch_rssm(a, st))) != RNN_OK) return rc;
+  return prof.end();
+}
+
+int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws, size_t ws_bytes,
+                hipStream_t st, int cus, Prof& prof) {
+  int rc;
+  long long n_tok = 0;
+  int t_max = 0;
+  if ((rc = validate_lengths(d, io->lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
+  const Dims m = dims_of(d, n_tok);
+  const size_t es = m.esize;
+  const int LD = d->num_layers * m.D;
+  for (int i = 0; i < LD; ++i) {
+    if ((rc = check_ptr(w->w_ih[i], es)) != RNN_OK || (rc = check_ptr(w->w_hh[i], es)) != RNN_OK) return rc;
+    if (d->has_bias) {
+      if ((rc = check_ptr(w->b_ih[i], es)) != RNN_OK || (rc = check_ptr(w->b_hh[i], es)) != RNN_OK) return rc;
+    }
+    if (d->mode == RNN_MODE_LSTMP && (rc = check_ptr(w->w_hr[i], es)) != RNN_OK) return rc;
+  }
+  if ((rc = check_ptr(io->x, es)) != RNN_OK || (rc = check_ptr(io->y, es)) != RNN_OK) return rc;
+  if ((rc = check_opt(io->h0, es)) != RNN_OK || (rc = check_opt(io->h_n, es)) != RNN_OK) return rc;
+  if (d->mode != RNN_MODE_GRU &&
+      ((rc = check_opt(io->c0, es)) != RNN_OK || (rc = check_opt(io->c_n, es)) != RNN_OK))
+    return rc;
+  const bool has_len = io->lengths_host != nullptr;
+  const WsLayout L = layout_of(d, n_tok, has_len);
+  if (!ws || ws_bytes < L.total) return RNN_E_WORKSPACE;
+  if (!aligned(ws, 16)) return RNN_E_ALIGN;
+  ScanPlan p;
+  if ((rc = plan_scan(d, m, cus, &p)) != RNN_OK) return rc;
+
+  // ---- enqueue ----
+  if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
+  int* dev_len = nullptr;
+  int* dev_off = nullptr;
+  if (has_len) {
+    std::vector<int> ints((size_t)d->B + d->T + 1, 0);
+    for (int b = 0; b < d->B; ++b) ints[b] = io->lengths_host[b];
+    if (d->layout == RNN_LAYOUT_PACKED) {
+      // offsets[t] = sum_b min(L_b, t): first packed row of step t
+      long long acc = 0;
+      for (int t = 0; t <= d->T; ++t) {
+        ints[d->B + t] = (int)acc;
+        for (int b = 0; b < d->B; ++b)
+          if (io->lengths_host[b] > t) ++acc;
+      }
+    }
+    dev_len = (int*)(ws + L.ints);
+    dev_off = dev_len + d->B;
+    if ((rc = hip_status(launch_write_ints(dev_len, ints.data(), (int)ints.size(), st))) != RNN_OK) return rc;
+  }
+
+  const bool bf16 = d->dtype == RNN_DTYPE_BF16;
+  float* gx = (float*)(ws + L.gx);
+  const void* layer_in = io->x;
+  for (int l = 0; l < d->num_layers; ++l) {
+    const int in_l = l == 0 ? d->input_size : m.D * m.K;
+    void* layer_out = l == d->num_layers - 1 ? io->y : (void*)(ws + ((l % 2 == 0) ? L.inter0 : L.inter1));
+    // Kernel 1: Gx for every row of this layer, both directions.
+    GemmArgs g{};
+    g.A = layer_in;
+    g.M = (int)m.rows; g.N = m.D * m.G; g.K = in_l; g.G = m.G;
+    g.hh_fold_rows = d->mode == RNN_MODE_GRU ? 2 * d->hidden_size : m.G;
+    g.has_bias = d->has_bias;
+    g.C = gx;
+    bool vec = (size_t)in_l * es % 16 == 0 && aligned(layer_in, 16);
+    for (int di = 0; di < m.D; ++di) {
+      const int i = l * m.D + di;
+      g.W[di] = w->w_ih[i];
+      g.b_ih[di] = w->b_ih[i];
+      g.b_hh[di] = w->b_hh[i];
+      vec = vec && aligned(w->w_ih[i], 16);
+    }
+    g.vec_ok = vec;
+    if ((rc = prof.begin(1)) != RNN_OK) return rc;
+    if ((rc = hip_status(launch_gemm_xw(g, bf16, st))) != RNN_OK) return rc;
+    if ((rc = prof.end()) != RNN_OK) return rc;
+
+    // Kernel 2: the scan.
+    ScanArgs a{};
+    a.mode = d->mode == RNN_MODE_GRU ? kGRU : (d->mode == RNN_MODE_LSTMP ? kLSTMP : kLSTM);
+    a.T = t_max; a.B = d->B; a.H = d->hidden_size; a.K = m.K; a.P = d->proj_size; a.D = m.D; a.G = m.G;
+    a.packed = d->layout == RNN_LAYOUT_PACKED;
+    a.has_bias = d->has_bias;
+    a.bb = p.bb; a.hs = p.hs; a.ns = p.ns; a.ps = p.ps; a.nbb = p.nbb; a.Kp = m.Kp; a.Hp = m.Hp;
+    for (int di = 0; di < m.D; ++di) {
+      const int i = l * m.D + di;
+      a.w_hh[di] = w->w_hh[i];
+      a.w_hr[di] = d->mode == RNN_MODE_LSTMP ? w->w_hr[i] : nullptr;
+      a.b_hh[di] = d->has_bias ? w->b_hh[i] : nullptr;
+      a.h0[di] = io->h0 ? (const char*)io->h0 + (size_t)i * d->B * m.K * es : nullptr;
+      a.c0[di] = (d->mode != RNN_MODE_GRU && io->c0) ? (const char*)io->c0 + (size_t)i * d->B * d->hidden_size * es : nullptr;
+      a.h_n[di] = io->h_n ? (char*)io->h_n + (size_t)i * d->B * m.K * es : nullptr;
+      a.c_n[di] = (d->mode != RNN_MODE_GRU && io->c_n) ? (char*)io->c_n + (size_t)i * d->B * d->hidden_size * es : nullptr;
+    }
+    a.gx = gx;
+    a.y = layer_out;
+    a.lengths = dev_len;
+    a.offsets = dev_off;
+    a.hx = ws + L.hx;
+    a.mx = d->mode == RNN_MODE_LSTMP ? ws + L.mx : nullptr;
+    a.counters = (unsigned*)(ws + L.counters + (size_t)l * m.D * d->B * kCounterBytes);
+    a.status = (int*)(ws + L.status);
+    if ((rc = prof.begin(2)) != RNN_OK) return rc;
+    if ((rc = hip_status(launch_scan(a, bf16, st))) != RNN_OK) return rc;
+    if ((rc = prof.end()) != RNN_OK) return rc;
+    layer_in = layer_out;
+  }
+  return RNN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rnn_abi_version(void) { return RNN_ABI_VERSION; }
+
+const char* rnn_strerror(int status) {
+  switch (status) {
+    case RNN_OK: return "ok";
+    case RNN_E_NULL: return "a required pointer is NULL";
+    case RNN_E_SHAPE: return "a size is out of range or inconsistent";
+    case RNN_E_UNSUPPORTED: return "unsupported combination of mode, dtype, layout or options";
+    case RNN_E_LENGTHS: return "sequence lengths out of range, missing, or not sorted non-increasing for the packed layout";
+    case RNN_E_WORKSPACE: return "workspace missing or too small";
+    case RNN_E_ALIGN: return "a pointer is not aligned to its element size (workspace: 16 bytes)";
+    case RNN_E_DEVICE: return "no gfx950 device is current";
+    case RNN_E_HIP: return "a HIP runtime call or kernel launch failed";
+    case RNN_E_TIMEOUT: return "a step barrier timed out on the device (workgroups not co-resident)";
+    case RNN_E_PLAN: return "the problem does not fit the persistent kernels' on-chip residency limits";
+    default: return "unknown status";
+  }
+}
+
+int rnn_workspace_bytes(const RnnDesc* desc, const int32_t* lengths_host, size_t* bytes) {
+  int rc = validate_desc(desc);
+  if (rc != RNN_OK) return rc;
+  if (!bytes) return RNN_E_NULL;
+  long long n_tok = 0;
+  int t_max = 0;
+  if ((rc = validate_lengths(desc, lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
+  *bytes = layout_of(desc, n_tok, lengths_host != nullptr).total;
+  return RNN_OK;
+}
+
+int rnn_device_check(void) {
+  DeviceInfo info;
+  return current_device_info(&info);
+}
+
+int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* workspace,
+                         size_t ws_bytes, void* stream, void* const* events, int n_events, int* kinds,
+                         int* n_kernels) {
+  int rc = validate_desc(desc);
+  if (rc != RNN_OK) return rc;
+  if (!weights || !io) return RNN_E_NULL;
+  if (desc->mode != RNN_MODE_RSSM_PRIOR) {
+    long long n_tok = 0;
+    int t_max = 0;
+    if ((rc = validate_lengths(desc, io->lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
+  }
+  DeviceInfo info;
+  if ((rc = current_device_info(&info)) != RNN_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (n_events < 0) return RNN_E_SHAPE;
+  if (n_events > 0 && !events) return RNN_E_NULL;
+  Prof prof;
+  prof.events = events;
+  prof.n_events = n_events;
+  prof.kinds = kinds;
+  prof.st = st;
+  rc = desc->mode == RNN_MODE_RSSM_PRIOR
+           ? forward_rssm(desc, weights, io, (char*)workspace, ws_bytes, st, info.cus, prof)
+           : forward_rnn(desc, weights, io, (char*)workspace, ws_bytes, st, info.cus, prof);
+  if (n_kernels) *n_kernels = prof.n;
+  return rc;
+}
+
+int rnn_forward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* workspace,
+                size_t ws_bytes, void* stream) {
+  return rnn_forward_profiled(desc, weights, io, workspace, ws_bytes, stream, nullptr, 0, nullptr, nullptr);
+}
+
+int rnn_read_status(const void* workspace, void* stream, int* device_status) {
+  if (!workspace || !device_status) return RNN_E_NULL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return RNN_E_HIP;
+  int v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return RNN_E_HIP;
+  *device_status = v;
+  return RNN_OK;
+}
+
+}  // extern "C"

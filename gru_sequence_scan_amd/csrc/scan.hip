@@ -1,0 +1,400 @@
+// Kernel 2: the persistent scan over time of one layer (all directions).
+//
+// The recurrence is a true sequential loop over t that runs inside one
+// launch (apache/tvm PR "[TOPI] TE implementation of LSTM using scan",
+// description: te.scan keeps the time loop sequential instead of unrolling
+// it, with a symbolic length). Each step does the hidden-hidden dense op
+// h_{t-1} W_hh^T, the gate math with the hoisted Gx added (gates and
+// activations fused into the step, as in the same PR's benchmark notes),
+// and for LSTMP the hidden-projection dense op h_t = W_hr m_t.
+//
+// Work split. The batch is cut into blocks of `bb` rows and the hidden units
+// into slices of `hs`. A group (one direction x one batch block) is `ns`
+// workgroups, one per hidden slice; each keeps its slice of W_hh (all gates
+// of its units) and, for LSTMP, a slice of `ps` rows of W_hr resident in
+// LDS for the whole launch. Groups never talk to each other. Inside a group
+// the state h_t is exchanged through a device-coherent ping-pong buffer and
+// one barrier per step (two for LSTMP: after m_t, after h_t).
+//
+// Variable length (apache/mxnet issue "RNN Op Changes", RFC): row b is
+// active at step t iff t < L_b. Inactive rows read nothing, write nothing
+// and keep their state, so a reverse-direction row starts at its own
+// t = L_b - 1 from h0. A group stops once none of its rows is active.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace rnnk {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxEpt = 8;  // owned gate elements per thread: bb * hs <= 2048
+
+struct ScanLds {
+  int ws, wr, as, acc, flag, total;  // byte offsets
+  int ws_ld, wr_ld, as_ld, acc_ld;    // row strides in elements
+  int ncw, ncp;                       // W rows (padded to 16), acc columns
+};
+
+__host__ __device__ inline int rup(int x, int m) { return (x + m - 1) / m * m; }
+
+__host__ __device__ inline ScanLds scan_lds(const ScanArgs& a, int esize) {
+  ScanLds L;
+  const int gates = a.mode == kGRU ? 3 : 4;
+  const int pad = 16 / esize;
+  const int nc = gates * a.hs;
+  L.ncw = rup(nc, 16);
+  const int ps16 = a.mode == kLSTMP ? rup(a.ps, 16) : 0;
+  L.ncp = L.ncw > ps16 ? L.ncw : ps16;
+  L.ws_ld = a.Kp + pad;
+  L.wr_ld = a.Hp + pad;
+  const int aw = a.mode == kLSTMP ? (a.Kp > a.Hp ? a.Kp : a.Hp) : a.Kp;
+  L.as_ld = aw + pad;
+  L.acc_ld = L.ncp + 1;
+  const int bb16 = rup(a.bb, 16);
+  int off = 0;
+  L.ws = off; off += rup(L.ncw * L.ws_ld * esize, 16);
+  L.wr = off; off += a.mode == kLSTMP ? rup(ps16 * L.wr_ld * esize, 16) : 0;
+  L.as = off; off += rup(bb16 * L.as_ld * esize, 16);
+  L.acc = off; off += rup(bb16 * L.acc_ld * 4, 16);
+  L.flag = off; off += 16;
+  L.total = off;
+  return L;
+}
+
+// acc[r][c] = sum_k A[r][k] * W[c][k] on 16x16 MFMA tiles (bb a multiple of
+// 16). Tiles are dealt over the 4 waves.
+template <typename DT>
+__device__ void mm_mfma(const char* lds, int as_off, int as_ld, int w_off, int w_ld, float* acc,
+                        int acc_ld, int mtiles, int ntiles, int kp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const DT* As = reinterpret_cast<const DT*>(lds + as_off);
+  const DT* Ws = reinterpret_cast<const DT*>(lds + w_off);
+  for (int ti = wave; ti < mtiles * ntiles; ti += 4) {
+    const int mt = ti / ntiles, nt = ti - mt * ntiles;
+    const DT* arow = As + (mt * 16 + lr) * as_ld;
+    const DT* brow = Ws + (nt * 16 + lr) * w_ld;
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (sizeof(DT) == 2) {
+      for (int k0 = 0; k0 < kp; k0 += 32) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(arow + k0 + 8 * lq);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(brow + k0 + 8 * lq);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+      }
+    } else {
+      for (int k0 = 0; k0 < kp; k0 += 16) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(arow + k0 + 4 * lq);
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(brow + k0 + 4 * lq);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], bv[3], c, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[(mt * 16 + 4 * lq + v) * acc_ld + nt * 16 + lr] = c[v];
+  }
+}
+
+// Same product on the vector ALUs for small batch blocks (bb < 16).
+template <typename DT>
+__device__ __forceinline__ void mm_valu(const char* lds, int as_off, int as_ld, int w_off, int w_ld, float* acc,
+                                        int acc_ld, int rows, int cols, int kp) {
+  lds_gemv_rows<DT, 4, 2>(reinterpret_cast<const DT*>(lds + as_off), as_ld,
+                          reinterpret_cast<const DT*>(lds + w_off), w_ld, acc, acc_ld, rows, cols,
+                          kp * (int)sizeof(DT) / 16);
+}
+
+// Copy `rows` rows of `width_el` elements from a coherent exchange buffer
+// (row stride `src_ld` elements) into LDS (row stride `dst_ld`). Rows whose
+// batch index is outside [0, B) are zero-filled.
+template <typename DT>
+__device__ void load_tile_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t src_base_el, int src_ld, int b0,
+                                   int B, int rows, int width_el, char* lds, int dst_off, int dst_ld) {
+  constexpr int kEpc = 16 / sizeof(DT);
+  const int cpr = width_el / kEpc;
+  const int total = rows * cpr;
+  DT* dst = reinterpret_cast<DT*>(lds + dst_off);
+  for (int base = 0; base < total; base += kThreads * 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = base + i * kThreads + threadIdx.x;
+      const int r = idx / cpr, cc = idx - r * cpr;
+      if (idx < total && b0 + r < B)
+        v[i] = coh_load16(rs, (src_base_el + (uint32_t)(r * src_ld + cc * kEpc)) * sizeof(DT));
+      else
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = base + i * kThreads + threadIdx.x;
+      if (idx < total) {
+        const int r = idx / cpr, cc = idx - r * cpr;
+        *reinterpret_cast<u32x4*>(dst + r * dst_ld + cc * kEpc) = v[i];
+      }
+    }
+  }
+}
+
+// Load `nrows` weight rows into LDS as [nrows][ld], zero-padding k >= klen
+// and rows for which row_of() returns -1.
+template <typename DT, typename RowFn>
+__device__ void load_weights(const DT* w, int klen, int kpad, int nrows, RowFn row_of, char* lds,
+                             int off, int ld) {
+  DT* dst = reinterpret_cast<DT*>(lds + off);
+  const int total = nrows * kpad;
+  for (int idx = threadIdx.x; idx < total; idx += kThreads) {
+    const int r = idx / kpad, k = idx - r * kpad;
+    const int gr = row_of(r);
+    dst[r * ld + k] = (gr >= 0 && k < klen) ? w[(size_t)gr * klen + k] : (DT)0.0f;
+  }
+}
+
+template <typename DT>
+__global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const ScanLds L = scan_lds(a, (int)sizeof(DT));
+  const int tid = threadIdx.x;
+  const int gates = a.mode == kGRU ? 3 : 4;
+
+  // Workgroup -> (direction, batch block, hidden slice).
+  const int s = blockIdx.x % a.ns;
+  const int grp = blockIdx.x / a.ns;
+  const int nb = grp % a.nbb;
+  const int d = grp / a.nbb;
+  const int b0 = nb * a.bb;
+  const int j0 = s * a.hs;
+  const int hs_act = min(a.hs, a.H - j0);  // may be <= 0 for a trailing slice
+  const int p0 = s * a.ps;
+  const int ps_act = a.mode == kLSTMP ? min(a.ps, a.P - p0) : 0;
+  const bool rev = d == 1;
+  const int DK = a.D * a.K;
+  const int DG = a.D * a.G;
+  unsigned* counter = a.counters + (size_t)grp * 16;
+  int* abort_flag = reinterpret_cast<int*>(lds + L.flag);
+
+  const uint32_t hx_bytes = (uint32_t)(2 * a.D * a.B * a.Kp) * sizeof(DT);
+  const __amdgpu_buffer_rsrc_t hx_rs = make_rsrc(a.hx, hx_bytes);
+  const uint32_t mx_bytes = a.mode == kLSTMP ? (uint32_t)(a.D * a.B * a.Hp) * sizeof(DT) : 16u;
+  const __amdgpu_buffer_rsrc_t mx_rs = make_rsrc(a.mode == kLSTMP ? a.mx : a.hx, mx_bytes);
+  auto hx_el = [&](int par, int b, int k) -> uint32_t {
+    return (uint32_t)(((par * a.D + d) * a.B + b) * a.Kp + k);
+  };
+  auto mx_el = [&](int b, int j) -> uint32_t { return (uint32_t)((d * a.B + b) * a.Hp + j); };
+  auto len_of = [&](int b) -> int { return a.lengths ? a.lengths[b] : a.T; };
+
+  if (tid == 0) *abort_flag = 0;
+
+  // --- resident weights -----------------------------------------------------
+  const DT* whh = reinterpret_cast<const DT*>(a.w_hh[d]);
+  load_weights<DT>(whh, a.K, a.Kp, L.ncw, [&](int r) -> int {
+    const int q = r / a.hs, u = r - q * a.hs;
+    return (q < gates && u < hs_act) ? q * a.H + j0 + u : -1;
+  }, lds, L.ws, L.ws_ld);
+  if (a.mode == kLSTMP) {
+    const DT* whr = reinterpret_cast<const DT*>(a.w_hr[d]);
+    load_weights<DT>(whr, a.H, a.Hp, rup(a.ps, 16), [&](int r) -> int {
+      return r < ps_act ? p0 + r : -1;
+    }, lds, L.wr, L.wr_ld);
+  }
+
+  // --- owned state: gate elements e = tid + i * 256 -> (row r, unit u) -------
+  const int n_el = a.bb * a.hs;
+  float hreg[kMaxEpt], creg[kMaxEpt];
+  float bhn[kMaxEpt];
+  const DT* h0 = reinterpret_cast<const DT*>(a.h0[d]);
+  const DT* c0 = reinterpret_cast<const DT*>(a.c0[d]);
+  const DT* bhh = reinterpret_cast<const DT*>(a.b_hh[d]);
+#pragma unroll
+  for (int i = 0; i < kMaxEpt; ++i) {
+    const int e = tid + i * kThreads;
+    const int r = e / a.hs, u = e - r * a.hs;
+    const int b = b0 + r;
+    hreg[i] = 0.f; creg[i] = 0.f; bhn[i] = 0.f;
+    if (e < n_el && u < hs_act && b < a.B) {
+      const int j = j0 + u;
+      if (a.mode != kLSTMP && h0) hreg[i] = to_f32<DT>(h0[(size_t)b * a.K + j]);
+      if (a.mode != kGRU && c0) creg[i] = to_f32<DT>(c0[(size_t)b * a.H + j]);
+      if (a.mode == kGRU && a.has_bias) bhn[i] = to_f32<DT>(bhh[2 * a.H + j]);
+      if (a.mode != kLSTMP) {
+        coh_store_elem<DT>(hx_rs, hx_el(0, b, j), hreg[i]);
+        coh_store_elem<DT>(hx_rs, hx_el(1, b, j), hreg[i]);
+      }
+    }
+  }
+  if (a.mode == kLSTMP) {
+    // projection owners publish h0 for their outputs
+    for (int e = tid; e < a.bb * a.ps; e += kThreads) {
+      const int r = e / a.ps, p = e - r * a.ps;
+      const int b = b0 + r;
+      if (p < ps_act && b < a.B) {
+        const float v = h0 ? to_f32<DT>(h0[(size_t)b * a.K + p0 + p]) : 0.f;
+        coh_store_elem<DT>(hx_rs, hx_el(0, b, p0 + p), v);
+        coh_store_elem<DT>(hx_rs, hx_el(1, b, p0 + p), v);
+      }
+    }
+  }
+  if (s == 0) {  // zero the padding columns of this block's exchange rows
+    for (int e = tid; e < a.bb * (a.Kp - a.K); e += kThreads) {
+      const int r = e / (a.Kp - a.K), k = a.K + (e - r * (a.Kp - a.K));
+      if (b0 + r < a.B) {
+        coh_store_elem<DT>(hx_rs, hx_el(0, b0 + r, k), 0.f);
+        coh_store_elem<DT>(hx_rs, hx_el(1, b0 + r, k), 0.f);
+      }
+    }
+    if (a.mode == kLSTMP) {
+      for (int e = tid; e < a.bb * (a.Hp - a.H); e += kThreads) {
+        const int r = e / (a.Hp - a.H), k = a.H + (e - r * (a.Hp - a.H));
+        if (b0 + r < a.B) coh_store_elem<DT>(mx_rs, mx_el(b0 + r, k), 0.f);
+      }
+    }
+  }
+
+  // Longest sequence of this block bounds the steps it takes part in.
+  int maxlen = 0;
+  for (int r = 0; r < a.bb && b0 + r < a.B; ++r) maxlen = max(maxlen, len_of(b0 + r));
+
+  unsigned nbar = 1;
+  if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+
+  const bool use_mfma = (a.bb % 16) == 0;
+  float* acc = reinterpret_cast<float*>(lds + L.acc);
+  const int mtiles = rup(a.bb, 16) / 16;
+  DT* yout = reinterpret_cast<DT*>(a.y);
+  DT* hn = reinterpret_cast<DT*>(a.h_n[d]);
+  DT* cn = reinterpret_cast<DT*>(a.c_n[d]);
+  int par = 0;  // exchange buffer holding h_{t-1}
+
+  for (int step = 0; step < a.T; ++step) {
+    const int t = rev ? a.T - 1 - step : step;
+    if (t >= maxlen) {
+      if (rev) continue;  // reverse rows have not started yet
+      break;              // forward rows are all finished
+    }
+    const int rowbase = a.packed ? a.offsets[t] : t * a.B;
+
+    // Prefetch this step's Gx for the owned elements.
+    float gxv[kMaxEpt][4];
+#pragma unroll
+    for (int i = 0; i < kMaxEpt; ++i) {
+      const int e = tid + i * kThreads;
+      const int r = e / a.hs, u = e - r * a.hs;
+      const int b = b0 + r;
+      const bool act = e < n_el && u < hs_act && b < a.B && t < len_of(b);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) gxv[i][q] = 0.f;
+      if (act) {
+        const float* g = a.gx + (size_t)(rowbase + b) * DG + d * a.G + j0 + u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q < gates) gxv[i][q] = g[q * a.H];
+      }
+    }
+
+    // h_{t-1} of the block -> LDS, then the hidden-hidden product.
+    load_tile_coherent<DT>(hx_rs, hx_el(par, b0, 0), a.Kp, b0, a.B, use_mfma ? rup(a.bb, 16) : a.bb,
+                           a.Kp, lds, L.as, L.as_ld);
+    __syncthreads();
+    if (use_mfma)
+      mm_mfma<DT>(lds, L.as, L.as_ld, L.ws, L.ws_ld, acc, L.acc_ld, mtiles, L.ncw / 16, a.Kp);
+    else
+      mm_valu<DT>(lds, L.as, L.as_ld, L.ws, L.ws_ld, acc, L.acc_ld, a.bb, gates * a.hs, a.Kp);
+    __syncthreads();
+
+    // Gate math on the owned elements.
+#pragma unroll
+    for (int i = 0; i < kMaxEpt; ++i) {
+      const int e = tid + i * kThreads;
+      const int r = e / a.hs, u = e - r * a.hs;
+      const int b = b0 + r;
+      if (!(e < n_el && u < hs_act && b < a.B)) continue;
+      const int lb = len_of(b);
+      if (t >= lb) continue;
+      const bool last = rev ? (t == 0) : (t == lb - 1);
+      const int j = j0 + u;
+      const float* ar = acc + r * L.acc_ld;
+      const size_t yrow = (size_t)(rowbase + b) * DK + d * a.K;
+      if (a.mode == kGRU) {
+        const float rg = fsigmoid(gxv[i][0] + ar[u]);
+        const float zg = fsigmoid(gxv[i][1] + ar[a.hs + u]);
+        const float ng = ftanh(gxv[i][2] + rg * (ar[2 * a.hs + u] + bhn[i]));
+        const float h = (1.f - zg) * ng + zg * hreg[i];
+        hreg[i] = h;
+        coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), h);
+        yout[yrow + j] = from_f32<DT>(h);
+        if (last && hn) hn[(size_t)b * a.K + j] = from_f32<DT>(h);
+      } else {
+        const float ig = fsigmoid(gxv[i][0] + ar[u]);
+        const float fg = fsigmoid(gxv[i][1] + ar[a.hs + u]);
+        const float gg = ftanh(gxv[i][2] + ar[2 * a.hs + u]);
+        const float og = fsigmoid(gxv[i][3] + ar[3 * a.hs + u]);
+        const float c = fg * creg[i] + ig * gg;
+        const float m = og * ftanh(c);
+        creg[i] = c;
+        if (last && cn) cn[(size_t)b * a.H + j] = from_f32<DT>(c);
+        if (a.mode == kLSTM) {
+          coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), m);
+          yout[yrow + j] = from_f32<DT>(m);
+          if (last && hn) hn[(size_t)b * a.K + j] = from_f32<DT>(m);
+        } else {
+          coh_store_elem<DT>(mx_rs, mx_el(b, j), m);
+        }
+      }
+    }
+    ++nbar;
+    if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+
+    if (a.mode == kLSTMP) {
+      // hidden-projection dense: h_t = m_t W_hr^T for this slice of P
+      load_tile_coherent<DT>(mx_rs, mx_el(b0, 0), a.Hp, b0, a.B, use_mfma ? rup(a.bb, 16) : a.bb,
+                             a.Hp, lds, L.as, L.as_ld);
+      __syncthreads();
+      if (use_mfma)
+        mm_mfma<DT>(lds, L.as, L.as_ld, L.wr, L.wr_ld, acc, L.acc_ld, mtiles, rup(a.ps, 16) / 16, a.Hp);
+      else
+        mm_valu<DT>(lds, L.as, L.as_ld, L.wr, L.wr_ld, acc, L.acc_ld, a.bb, a.ps, a.Hp);
+      __syncthreads();
+      for (int e = tid; e < a.bb * a.ps; e += kThreads) {
+        const int r = e / a.ps, p = e - r * a.ps;
+        const int b = b0 + r;
+        if (p >= ps_act || b >= a.B) continue;
+        const int lb = len_of(b);
+        if (t >= lb) continue;
+        const bool last = rev ? (t == 0) : (t == lb - 1);
+        const float h = acc[r * L.acc_ld + p];
+        coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, p0 + p), h);
+        yout[(size_t)(rowbase + b) * DK + d * a.K + p0 + p] = from_f32<DT>(h);
+        if (last && hn) hn[(size_t)b * a.K + p0 + p] = from_f32<DT>(h);
+      }
+      ++nbar;
+      if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+    }
+    par ^= 1;
+  }
+}
+
+}  // namespace
+
+int scan_lds_bytes(const ScanArgs& a, int esize) { return scan_lds(a, esize).total; }
+
+hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream) {
+  const int esize = dtype_bf16 ? 2 : 4;
+  const int lds = scan_lds(a, esize).total;
+  const dim3 grid(a.D * a.nbb * a.ns), block(kThreads);
+  if (dtype_bf16) {
+    hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<bf16>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scan_kernel<bf16>, grid, block, lds, stream, a);
+  } else {
+    hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<float>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scan_kernel<float>, grid, block, lds, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rnnk

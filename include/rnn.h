@@ -1,0 +1,231 @@
+/*
+ * rnn.h -- C ABI of the gfx950 (MI355X) multi-timestep recurrence library.
+ *
+ * One call, rnn_forward, runs the whole forward of a recurrent stack on the
+ * caller's HIP stream:
+ *   mode LSTM         nn.LSTM forward (pytorch/pytorch issue "Integrating
+ *                     CuDNN API for LSTMs with projections", Motivation and
+ *                     design discussion), PyTorch gate order [i | f | g | o].
+ *   mode LSTMP        LSTM with a recurrent projection h = W_hr (o * tanh c),
+ *                     fed back as the recurrent input: "LSTMCell plus one
+ *                     matmul" (same issue, design discussion; arXiv 1402.1128
+ *                     cited in its Feature section).
+ *   mode GRU          GRU with PyTorch's r/z/n convention (pytorch/rl issue
+ *                     "[Feature Request] CUDNN version of RSSM", RSSMPrior uses
+ *                     nn.GRUCell); the reset gate multiplies W_hn h + b_hn.
+ *   mode RSSM_PRIOR   the RSSM prior unrolled over given actions (same rl
+ *                     issue, Solution: RSSMPrior.forward and the first unroll),
+ *                     with the Gaussian draw injected as a noise tensor.
+ * Variable-length batches (per-sequence lengths as an extra argument, the
+ * pack/unpack handled inside the op) and bidirectional stacks follow apache/
+ * mxnet issue "RNN Op Changes (was: Variable Length Support for cuDNN RNN)",
+ * RFC. The three dense ops are those named in apache/tvm PR "[TOPI] TE
+ * implementation of LSTM using scan", description: input-hidden (hoisted
+ * over all timesteps), hidden-hidden and hidden-projection (inside the
+ * sequential time loop, which runs on the device).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device allocations owned by the caller; the
+ *     library allocates no device memory, keeps no pointer after returning
+ *     and reads host arrays (lengths) only during the call.
+ *   - Tensors are dense with C-canonical strides (pytorch/rl PR "LSTM/GRU
+ *     scan: canonical strides + ...", description: a tensor can pass
+ *     is_contiguous() and still carry non-canonical strides; callers must
+ *     re-materialise). Device pointers must be 16-byte aligned.
+ *   - Weight pointers are read-only and may alias one flat storage (same PR:
+ *     per-layer views of a single flat parameter storage).
+ *   - All validation happens once, before anything is enqueued (same PR,
+ *     review: do the layout work before the loop). Nothing is enqueued when
+ *     a call returns an error.
+ *   - The library keeps no mutable global state and reads no environment
+ *     variables (same PR: a module-global mode flag leaked across threads);
+ *     concurrent calls on different streams with different workspaces are
+ *     safe. Two calls that share a workspace must be stream-ordered.
+ *   - Floating-point results are deterministic: the same inputs give the
+ *     same bits (no floating-point atomics).
+ */
+#ifndef GRU_SEQUENCE_SCAN_RNN_H
+#define GRU_SEQUENCE_SCAN_RNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RNN_ABI_VERSION 1
+#define RNN_MAX_LAYERS 8
+#define RNN_MAX_LD (2 * RNN_MAX_LAYERS) /* layers x directions */
+
+typedef enum RnnMode {
+  RNN_MODE_LSTM = 0,
+  RNN_MODE_GRU = 1,
+  RNN_MODE_LSTMP = 2,
+  RNN_MODE_RSSM_PRIOR = 3
+} RnnMode;
+
+/* Storage type of weights, inputs, initial states and outputs. Arithmetic
+ * always accumulates in fp32; the LSTM cell state is always carried in fp32
+ * inside the kernels. */
+typedef enum RnnDtype { RNN_DTYPE_F32 = 0, RNN_DTYPE_BF16 = 1 } RnnDtype;
+
+typedef enum RnnLayout {
+  RNN_LAYOUT_PADDED = 0,      /* x [T, B, F], y [T, B, D*K]                    */
+  RNN_LAYOUT_PACKED = 1,      /* x [N_tok, F], y [N_tok, D*K]: step-major rows
+                                 of the sequences still active at each step,
+                                 lengths sorted non-increasing (PackedSequence) */
+  RNN_LAYOUT_BATCH_MAJOR = 2  /* RSSM only: [B, T, .] like the unroll's stack
+                                 on dim 1                                      */
+} RnnLayout;
+
+typedef enum RnnStatus {
+  RNN_OK = 0,
+  RNN_E_NULL = -1,        /* a required pointer is NULL                        */
+  RNN_E_SHAPE = -2,       /* a size is out of range or inconsistent            */
+  RNN_E_UNSUPPORTED = -3, /* combination not defined: projection outside LSTMP,
+                             LSTMP without projection, bidirectional or
+                             multi-layer RSSM, RSSM in bf16, ...               */
+  RNN_E_LENGTHS = -4,     /* a length outside [1, T], or packed lengths not
+                             sorted non-increasing                             */
+  RNN_E_WORKSPACE = -5,   /* workspace NULL or smaller than required           */
+  RNN_E_ALIGN = -6,       /* a device pointer is not 16-byte aligned           */
+  RNN_E_DEVICE = -7,      /* no usable gfx950 device is current                */
+  RNN_E_HIP = -8,         /* a HIP runtime call or launch failed               */
+  RNN_E_TIMEOUT = -9,     /* device status only: a step barrier waited too long
+                             (workgroups were not co-resident); outputs are
+                             invalid                                           */
+  RNN_E_PLAN = -10        /* the problem does not fit the device's persistent
+                             residency limits (e.g. weights exceed on-chip
+                             capacity of the available compute units)          */
+} RnnStatus;
+
+/* Problem description (all sizes in elements). */
+typedef struct RnnDesc {
+  int32_t mode;          /* RnnMode                                            */
+  int32_t dtype;         /* RnnDtype                                           */
+  int32_t layout;        /* RnnLayout                                          */
+  int32_t T;             /* time extent: padded buffers' T; for PACKED an upper
+                            bound on the lengths; RSSM: unroll length         */
+  int32_t B;             /* batch size                                         */
+  int32_t input_size;    /* F of layer 0                                       */
+  int32_t hidden_size;   /* H                                                  */
+  int32_t proj_size;     /* P (> 0 exactly for LSTMP)                          */
+  int32_t num_layers;    /* 1 .. RNN_MAX_LAYERS                                */
+  int32_t bidirectional; /* 0 or 1                                             */
+  int32_t has_bias;      /* 0: bias pointers ignored (treated as zero)         */
+  /* RSSM prior dimensions (mode RSSM_PRIOR only) */
+  int32_t state_dim;     /* S: stochastic state size                          */
+  int32_t action_dim;    /* A                                                  */
+  int32_t embed_dim;     /* E: width of the action-state and prior projector
+                            hidden layers                                      */
+  int32_t belief_dim;    /* Hb: GRU hidden size                               */
+  float scale_lb;        /* lower bound added to softplus(raw scale)          */
+  /* Launch-shape hints (0 = choose automatically). They change only how the
+   * work is tiled, never which arithmetic is done per output element. */
+  int32_t tile_batch;    /* batch rows per workgroup in the scan               */
+  int32_t tile_hidden;   /* hidden units per workgroup in the scan             */
+  int32_t reserved[6];   /* must be zero                                       */
+} RnnDesc;
+
+/* Weights, PyTorch shapes and meaning. Index i = layer * D + direction
+ * (direction 0 forward, 1 reverse). G = 4H (LSTM, LSTMP) or 3H (GRU);
+ * K = P for LSTMP, else H; in_l = input_size for layer 0, else D*K.
+ *   w_ih[i]  [G, in_l]   w_hh[i] [G, K]   b_ih[i] [G]   b_hh[i] [G]
+ *   w_hr[i]  [P, H]      (LSTMP only; no projection bias)
+ * RSSM_PRIOR (single layer, forward): GRU cell in w_ih[0] [3Hb, E],
+ * w_hh[0] [3Hb, Hb], b_ih[0], b_hh[0] [3Hb]; plus
+ *   w_as [E, S + A] (columns: state first, then action), b_as [E]
+ *   w_1  [E, Hb], b_1 [E]   (first prior-projector layer, reads the belief)
+ *   w_2  [2S, E], b_2 [2S]  (rows 0..S-1 mean, S..2S-1 raw scale)
+ * All in the RnnDesc dtype. */
+typedef struct RnnWeights {
+  const void* w_ih[RNN_MAX_LD];
+  const void* w_hh[RNN_MAX_LD];
+  const void* b_ih[RNN_MAX_LD];
+  const void* b_hh[RNN_MAX_LD];
+  const void* w_hr[RNN_MAX_LD];
+  const void* w_as;
+  const void* b_as;
+  const void* w_1;
+  const void* b_1;
+  const void* w_2;
+  const void* b_2;
+} RnnWeights;
+
+/* Inputs and outputs (device pointers unless noted), all in the RnnDesc dtype.
+ *   x             PADDED [T, B, F] | PACKED [N_tok, F] | RSSM actions [B, T, A]
+ *   lengths_host  HOST int32 [B]; NULL means every sequence has length T.
+ *                 1 <= L_b <= T; PACKED requires L_0 >= L_1 >= ... and
+ *                 N_tok = sum L_b. Row b is active at step t iff t < L_b; the
+ *                 reverse direction of row b starts at t = L_b - 1 from h0.
+ *   h0 [L*D, B, K], c0 [L*D, B, H]   NULL = zeros (RSSM: h0 = belief0 [B, Hb])
+ *   s0            RSSM initial state [B, S], NULL = zeros
+ *   noise         RSSM eps [B, T, S] (the unroll's Gaussian draw, injected)
+ *   y             PADDED [T, B, D*K] (positions t >= L_b are never written)
+ *                 | PACKED [N_tok, D*K]; forward half first on the last axis
+ *   h_n [L*D, B, K], c_n [L*D, B, H]  each row's final state; NULL = skip
+ *   means, stds, states [B, T, S], beliefs [B, T, Hb]  RSSM outputs
+ * Outputs must not overlap inputs or the workspace. */
+typedef struct RnnIO {
+  const void* x;
+  const int32_t* lengths_host;
+  const void* h0;
+  const void* c0;
+  const void* s0;
+  const void* noise;
+  void* y;
+  void* h_n;
+  void* c_n;
+  void* means;
+  void* stds;
+  void* states;
+  void* beliefs;
+} RnnIO;
+
+/* Version of this ABI (RNN_ABI_VERSION). */
+int rnn_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* rnn_strerror(int status);
+
+/* Validates desc (and lengths_host when given) and writes the workspace size
+ * rnn_forward needs into *bytes. Host-only, touches no device. Returns
+ * RNN_OK or a negative RnnStatus. */
+int rnn_workspace_bytes(const RnnDesc* desc, const int32_t* lengths_host, size_t* bytes);
+
+/* Enqueues the whole forward on `stream` (a hipStream_t; NULL = the null
+ * stream of the current device) and returns once everything is enqueued,
+ * without synchronising. `workspace` is caller-owned device memory of at
+ * least rnn_workspace_bytes() bytes; its prior contents do not matter.
+ * Returns RNN_OK, or a negative RnnStatus with nothing enqueued (RNN_E_HIP
+ * when a launch fails after validation). Device-side failures (RNN_E_TIMEOUT)
+ * are reported through rnn_read_status after the stream completes. */
+int rnn_forward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io,
+                void* workspace, size_t ws_bytes, void* stream);
+
+/* Same as rnn_forward, and additionally brackets each compute kernel it
+ * enqueues with caller-created hipEvent_t handles: events[2i] is recorded on
+ * `stream` right before the i-th kernel and events[2i + 1] right after it,
+ * for i < n_events / 2; kinds[i] (when kinds is non-NULL, room for
+ * n_events / 2 entries) receives 1 for the input-projection GEMM, 2 for a
+ * layer's scan and 3 for the RSSM kernel; *n_kernels (nullable) receives the
+ * number of compute kernels enqueued. For timing the kernels inside a
+ * measured region. Errors as rnn_forward. */
+int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io,
+                         void* workspace, size_t ws_bytes, void* stream, void* const* events,
+                         int n_events, int* kinds, int* n_kernels);
+
+/* Synchronises `stream`, then reads the device status word of the last
+ * rnn_forward that used `workspace` into *device_status (RNN_OK or
+ * RNN_E_TIMEOUT). Returns RNN_OK or RNN_E_HIP / RNN_E_NULL. */
+int rnn_read_status(const void* workspace, void* stream, int* device_status);
+
+/* RNN_OK when the current device is a gfx950 GPU; RNN_E_DEVICE otherwise. */
+int rnn_device_check(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRU_SEQUENCE_SCAN_RNN_H */

@@ -1,0 +1,78 @@
+"""Helpers shared by the GPU tests: run the library on synth inputs."""
+
+import sys
+
+import numpy as np
+import torch
+
+import gru_sequence_scan_amd as gss
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype, device="cuda:0"):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.float32)))
+    return t.to(device=device).to(dtype)
+
+
+def tdtype(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def run_rnn(d, y_fill=None, **kw):
+    """Run the GPU path on a synth RNN problem; returns numpy float64 outputs."""
+    dt = tdtype(d["dtype"])
+    params = []
+    for p in d["params"]:
+        params.append({k: to_dev(v, dt) for k, v in p.items() if v is not None})
+    x = to_dev(d["x"], dt)
+    h0 = to_dev(d["h0"], dt)
+    c0 = to_dev(d.get("c0"), dt)
+    D = 2 if d["bidirectional"] else 1
+    K = d["proj_size"] if d["mode"] == "lstmp" else d["hidden_size"]
+    y_out = None
+    if y_fill is not None:
+        shape = (x.shape[0], D * K) if d["layout"] == "packed" else (d["T"], d["B"], D * K)
+        y_out = torch.full(shape, y_fill, dtype=dt, device=x.device)
+    y, hn, cn = gss.rnn_forward(d["mode"], x, params, h0=h0, c0=c0, lengths=d["lengths"],
+                                layout=d["layout"], num_layers=d["num_layers"],
+                                bidirectional=d["bidirectional"], proj_size=d["proj_size"],
+                                y_out=y_out, **kw)
+    torch.cuda.synchronize()
+    f = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
+    return f(y), f(hn), f(cn)
+
+
+def run_rssm(d, **kw):
+    w = {k: to_dev(v, torch.float32) for k, v in d["weights"].items()}
+    out = gss.rssm_prior_unroll(to_dev(d["actions"], torch.float32), to_dev(d["eps"], torch.float32), w,
+                                to_dev(d["s0"], torch.float32), to_dev(d["h0"], torch.float32), **kw)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy().astype(np.float64) for t in out]
+
+
+def subset_rows(d, rows):
+    """The same problem restricted to batch rows `rows` (rows are independent)."""
+    rows = np.asarray(rows)
+    e = dict(d)
+    e["B"] = len(rows)
+    L = d["lengths"]
+    e["lengths"] = None if L is None else np.ascontiguousarray(L[rows])
+    if d["layout"] == "packed":
+        import synth
+        xp = d["x_padded"][:, rows]
+        e["x_padded"] = xp
+        T = int(np.max(e["lengths"]))
+        bs, off = synth.packed_layout(e["lengths"])
+        e["x"] = np.concatenate([xp[t, :bs[t]] for t in range(T)], axis=0)
+    else:
+        e["x"] = d["x"][:, rows]
+        e["x_padded"] = e["x"]
+    e["h0"] = None if d["h0"] is None else d["h0"][:, rows]
+    e["c0"] = None if d.get("c0") is None else d["c0"][:, rows]
+    return e

@@ -1,0 +1,223 @@
+"""Parity of the HIP path (called through the C ABI) with the float64 oracle.
+
+Tolerances: fp32 elementwise |g - r| <= 1e-4 |r| + 1e-5 plus a 1e-4 relative
+L2 bound; bf16 storage (fp32 accumulation) |g - r| <= 2e-2.
+Small cases span several workgroup tiles and ragged tails; the five
+workloads run at full size in the launch shape the bench times, and are
+compared on sampled batch rows (rows are independent, so the oracle on the
+sampled sub-batch is the exact reference for them).
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import log, run_rnn, run_rssm, subset_rows
+from helpers import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gru_sequence_scan_amd as gss
+    assert gss.rnn_device_check() == 0, "current device is not gfx950"
+    torch.cuda.set_device(0)
+
+
+def _oracle(d, **kw):
+    return oracle.rnn_forward(d["mode"], d["x"], d["params"], lengths=d["lengths"], h0=d["h0"],
+                              c0=d.get("c0"), num_layers=d["num_layers"],
+                              bidirectional=d["bidirectional"], proj_size=d["proj_size"],
+                              layout=d["layout"], **kw)
+
+
+def _compare(d, got, ref, what):
+    y, hn, cn = got
+    yr, hnr, cnr = ref
+    assert_close(y, yr, d["dtype"], what + " y")
+    assert_close(hn, hnr, d["dtype"], what + " h_n")
+    if cnr is not None:
+        assert_close(cn, cnr, d["dtype"], what + " c_n")
+
+
+SMALL = [
+    # name, mode, dtype, T, B, F, H, P, L, bidir, layout, varlen, bias, state
+    ("lstm_b1_valu", "lstm", "f32", 9, 1, 13, 20, 0, 1, False, "padded", None, True, True),
+    ("lstm_b5_valu", "lstm", "f32", 7, 5, 24, 40, 0, 1, False, "padded", None, True, False),
+    ("lstm_b37_mfma", "lstm", "f32", 11, 37, 40, 72, 0, 1, False, "padded", None, True, True),
+    ("lstm_nobias", "lstm", "f32", 6, 18, 16, 33, 0, 1, False, "padded", None, False, True),
+    ("gru_f32", "gru", "f32", 10, 33, 20, 48, 0, 1, False, "padded", None, True, True),
+    ("gru_bf16", "gru", "bf16", 12, 40, 64, 96, 0, 1, False, "padded", None, True, True),
+    ("gru_b3", "gru", "f32", 8, 3, 10, 17, 0, 2, True, "padded", None, True, True),
+    ("lstmp_f32", "lstmp", "f32", 9, 20, 24, 64, 24, 2, False, "padded", None, True, True),
+    ("lstmp_bf16", "lstmp", "bf16", 10, 33, 40, 128, 40, 2, False, "padded", None, True, False),
+    ("bilstm_packed", "lstm", "f32", 15, 21, 19, 40, 0, 2, True, "packed", (1, 15), True, True),
+    ("bigru_packed_bf16", "gru", "bf16", 13, 34, 32, 64, 0, 2, True, "packed", (2, 13), True, False),
+    ("bilstmp_packed", "lstmp", "f32", 12, 17, 16, 48, 16, 2, True, "packed", (1, 12), True, True),
+    ("lstm_padded_varlen", "lstm", "f32", 14, 19, 12, 36, 0, 1, True, "padded", "unsorted", True, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases(case):
+    name, mode, dt, T, B, F, H, P, L, bidir, layout, varlen, bias, state = case
+    log(f"[gpu] small case {name}")
+    lengths = None
+    vl = None
+    if varlen == "unsorted":
+        lengths = np.random.default_rng(7).integers(1, T + 1, size=B).astype(np.int32)
+        lengths[3] = T
+    elif varlen is not None:
+        vl = varlen
+    d = synth.make_rnn_inputs(mode, T, B, F, H, proj_size=P, num_layers=L, bidirectional=bidir,
+                              dtype=dt, layout=layout, lengths=lengths, varlen=vl,
+                              w_scale=1.0 / np.sqrt(H), bias=bias, seed=zlib.crc32(name.encode()) % 1000,
+                              h0_std=0.3 if state else 0.0, c0_std=0.3 if state else 0.0)
+    got = run_rnn(d, y_fill=float("nan"))
+    ref = _oracle(d)
+    _compare(d, got, ref, name)
+
+
+def test_padding_sentinel_untouched():
+    log("[gpu] padding sentinel")
+    lengths = np.array([5, 9, 2, 9, 1, 7, 3, 8], dtype=np.int32)
+    d = synth.make_rnn_inputs("lstm", 9, 8, 12, 24, num_layers=2, bidirectional=True,
+                              lengths=lengths, w_scale=0.2, seed=3)
+    y, hn, cn = run_rnn(d, y_fill=1234.5)
+    for b, lb in enumerate(lengths):
+        assert np.all(y[lb:, b] == 1234.5), f"row {b}: padding overwritten"
+        assert np.all(np.isfinite(y[:lb, b]))
+
+
+def test_determinism_bitwise():
+    log("[gpu] determinism")
+    d = synth.make_rnn_inputs("gru", 16, 48, 32, 64, dtype="bf16", w_scale=0.125, seed=4, h0_std=0.1)
+    a = run_rnn(d)
+    b = run_rnn(d)
+    for x, y in zip(a, b):
+        if x is not None:
+            assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("mode,P", [("lstm", 0), ("gru", 0), ("lstmp", 16)])
+def test_time_chunking_matches_one_call(mode, P):
+    log(f"[gpu] chunking {mode}")
+    d = synth.make_rnn_inputs(mode, 12, 20, 16, 48, proj_size=P, num_layers=2, w_scale=0.15, seed=5)
+    y, hn, cn = run_rnn(d)
+    d1 = dict(d, x=d["x"][:5], x_padded=d["x"][:5], T=5)
+    y1, hn1, cn1 = run_rnn(d1)
+    d2 = dict(d, x=d["x"][5:], x_padded=d["x"][5:], T=7, h0=hn1.astype(np.float32),
+              c0=None if cn1 is None else cn1.astype(np.float32))
+    y2, hn2, cn2 = run_rnn(d2)
+    assert_close(np.concatenate([y1, y2]), y, "f32", "chunked y")
+    assert_close(hn2, hn, "f32", "chunked h_n")
+
+
+def test_t1_equals_one_cell_step():
+    log("[gpu] T=1")
+    d = synth.make_rnn_inputs("lstm", 1, 16, 24, 32, w_scale=0.2, seed=6, h0_std=0.5, c0_std=0.5)
+    y, hn, cn = run_rnn(d)
+    p = d["params"][0]
+    h1, c1 = oracle.lstm_cell(d["x"][0], d["h0"][0], d["c0"][0], p["w_ih"], p["w_hh"], p["b_ih"], p["b_hh"])
+    assert_close(y[0], h1, "f32", "T=1 y")
+    assert_close(cn[0], c1, "f32", "T=1 c")
+
+
+def test_packed_equals_padded_on_gpu():
+    log("[gpu] packed == padded")
+    lengths = np.array([10, 9, 9, 6, 4, 4, 2, 1], dtype=np.int32)
+    d = synth.make_rnn_inputs("lstm", 10, 8, 16, 40, num_layers=2, bidirectional=True,
+                              layout="packed", lengths=lengths, w_scale=0.2, seed=8)
+    yk, hk, ck = run_rnn(d)
+    dp = dict(d, layout="padded", x=np.nan_to_num(d["x_padded"]))
+    yp, hp, cp = run_rnn(dp, y_fill=float("nan"))
+    np.testing.assert_array_equal(oracle.pack_sequence(yp, lengths), yk)
+    np.testing.assert_array_equal(hk, hp)
+    np.testing.assert_array_equal(ck, cp)
+
+
+# ---------------------------------------------------------------------------
+# RSSM prior
+# ---------------------------------------------------------------------------
+
+def test_rssm_small():
+    log("[gpu] rssm small")
+    d = synth.make_rssm_inputs(7, 9, state_dim=5, action_dim=3, embed_dim=24, belief_dim=20, seed=9,
+                               s0_std=0.5, h0_std=0.5)
+    got = run_rssm(d)
+    ref = oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"], d["s0"], d["h0"])
+    for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs")):
+        assert_close(g, r, "f32", "rssm " + nm)
+
+
+def test_rssm_zero_weights_closed_form():
+    log("[gpu] rssm closed form")
+    d = synth.make_rssm_inputs(6, 4, seed=10, zero_weights=True)
+    means, stds, states, beliefs = run_rssm(d)
+    assert np.all(beliefs == 0) and np.all(means == 0)
+    k = np.log(2.0) + 0.1
+    assert_close(stds, np.full_like(stds, k), "f32", "stds")
+    assert_close(states, k * d["eps"].astype(np.float64), "f32", "states")
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size
+# ---------------------------------------------------------------------------
+
+def _sampled_full(name, rows):
+    d = synth.make_inputs(name)
+    log(f"[gpu] full-size {name} (sampled rows {list(rows)})")
+    got = run_rnn(d, y_fill=float("nan"))
+    sub = subset_rows(d, rows)
+    ref = _oracle(sub)
+    y, hn, cn = got
+    if d["layout"] == "packed":
+        yp = oracle.unpack_sequence(y, d["lengths"], int(d["lengths"].max()))[:, rows]
+        yr = oracle.unpack_sequence(ref[0], sub["lengths"], int(sub["lengths"].max()))
+        yp = yp[:yr.shape[0]]
+    else:
+        yp, yr = y[:, rows], ref[0]
+    assert_close(yp, yr, d["dtype"], name + " y")
+    assert_close(hn[:, rows], ref[1], d["dtype"], name + " h_n")
+    if ref[2] is not None:
+        assert_close(cn[:, rows], ref[2], d["dtype"], name + " c_n")
+    return got
+
+
+def test_full_lstm_t80_b1():
+    d = synth.make_inputs("lstm_t80_b1")
+    log("[gpu] full-size lstm_t80_b1")
+    _compare(d, run_rnn(d), _oracle(d), "lstm_t80_b1")
+
+
+def test_full_rssm_b50_t50():
+    d = synth.make_inputs("rssm_b50_t50")
+    log("[gpu] full-size rssm_b50_t50")
+    got = run_rssm(d)
+    ref = oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"])
+    for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs")):
+        assert_close(g, r, "f32", "rssm_b50_t50 " + nm)
+
+
+def test_full_gru_t256_b256():
+    _sampled_full("gru_t256_b256", [0, 1, 77, 128, 200, 255])
+
+
+def test_full_lstmp_t1000_b32():
+    _sampled_full("lstmp_t1000_b32", [0, 13, 31])
+
+
+def test_full_bilstm_varlen_b64():
+    _sampled_full("bilstm_varlen_b64", [0, 5, 31, 47, 63])
+
+
+def test_full_lstm_t256_b1_small():
+    d = synth.make_inputs("lstm_t256_b1_small")
+    log("[gpu] full-size lstm_t256_b1_small")
+    _compare(d, run_rnn(d), _oracle(d), "lstm_t256_b1_small")
