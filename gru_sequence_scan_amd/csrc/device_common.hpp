@@ -83,12 +83,21 @@ __device__ __forceinline__ void wait_all_mem() {
 // ---------------------------------------------------------------------------
 constexpr uint64_t kWatchdogTicks = 200000000ull;  // 2 s at 100 MHz
 
-__device__ __forceinline__ bool group_barrier(unsigned* counter, unsigned target, int* status,
-                                              int* abort_flag_lds) {
+// Arrive at the group barrier: wait for this wave's memory operations
+// (in particular the coherent stores of the exchanged state), join the
+// workgroup, then thread 0 adds 1 to the counter. Work that does not feed
+// the exchange (output stores, prefetches) can be issued between
+// group_arrive and group_wait so that it overlaps the wait.
+__device__ __forceinline__ void group_arrive(unsigned* counter) {
   wait_all_mem();
   __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until the counter reaches `target` (barrier n of a group of m
+// members completes at n * m). Returns false if the watchdog fired.
+__device__ __forceinline__ bool group_wait(unsigned* counter, unsigned target, int* status, int* abort_flag_lds) {
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint64_t t0 = 0;
     unsigned polls = 0;
     while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -108,6 +117,12 @@ __device__ __forceinline__ bool group_barrier(unsigned* counter, unsigned target
   return *abort_flag_lds == 0;
 }
 
+__device__ __forceinline__ bool group_barrier(unsigned* counter, unsigned target, int* status,
+                                              int* abort_flag_lds) {
+  group_arrive(counter);
+  return group_wait(counter, target, status, abort_flag_lds);
+}
+
 // ---------------------------------------------------------------------------
 // Activations in fp32 from the hardware exp2 / log2. Near zero, where
 // exp(x) - 1 and log(1 + y) cancel, short Taylor polynomials keep the
@@ -118,21 +133,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-__device__ __forceinline__ float fsigmoid(float x) { return 1.0f / (1.0f + fexp(-x)); }
+// Logistic function with the hardware reciprocal (about 1 ulp): exp2 of a
+// large argument gives +inf and rcp(inf) = 0, so both tails are exact.
+__device__ __forceinline__ float fsigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + fexp(-x)); }
 
+// tanh(x) = sign(x) (1 - e) / (1 + e) with e = exp(-2|x|) in (0, 1]; near
+// zero the absolute error stays at the fp32 rounding level of 1.
 __device__ __forceinline__ float ftanh(float x) {
-  const float ax = __builtin_fabsf(x);
-  float r;
-  if (ax < 0.0625f) {
-    const float x2 = x * x;
-    // x - x^3/3 + 2x^5/15 - 17x^7/315
-    r = x * (1.0f + x2 * (-0.333333333333f + x2 * (0.133333333333f + x2 * (-0.053968253968f))));
-  } else {
-    const float e = fexp(-2.0f * ax);
-    r = (1.0f - e) / (1.0f + e);
-    r = x < 0.0f ? -r : r;
-  }
-  return r;
+  const float e = fexp(-2.0f * __builtin_fabsf(x));
+  const float r = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+  return __builtin_copysignf(r, x);
 }
 
 __device__ __forceinline__ float fexpm1(float x) {

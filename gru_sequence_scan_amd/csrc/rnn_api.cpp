@@ -238,7 +238,7 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, ScanPlan* out) {
     if (bb < 1) continue;
     const bool mfma = bb % 16 == 0;
     for (int hs : hss) {
-      if (hs < 1 || bb * hs > 2048) continue;
+      if (hs < 1 || bb * hs > 1024) continue;
       const int ns = cdiv(H, hs);
       const int nbb = cdiv(B, bb);
       if ((long long)m.D * nbb * ns > cus) continue;
@@ -281,7 +281,7 @@ int plan_rssm(const RnnDesc* d, int cus, RssmPlan* out) {
       if (d->tile_hidden > 0 && h_per != d->tile_hidden) continue;
       if (nw > 1 && cdiv(Hb, nw - 1) == h_per) continue;  // same slices with fewer members
       if ((long long)ngroups * nw > cus) continue;
-      if (rows * h_per > 256) continue;
+      if (rows * h_per > 256 || rows * S > 256 || rows * A > 256) continue;
       RssmArgs a{};
       a.S = S; a.A = A; a.E = E; a.Hb = Hb; a.rows = rows; a.nw = nw; a.h_per = h_per;
       const int lds = rssm_lds_bytes(a);
@@ -513,6 +513,30 @@ int rnn_workspace_bytes(const RnnDesc* desc, const int32_t* lengths_host, size_t
   int t_max = 0;
   if ((rc = validate_lengths(desc, lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
   *bytes = layout_of(desc, n_tok, lengths_host != nullptr).total;
+  return RNN_OK;
+}
+
+int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int* info, int n_info) {
+  int rc = validate_desc(desc);
+  if (rc != RNN_OK) return rc;
+  if (!info || n_info < 8) return RNN_E_NULL;
+  if (cus < 1) return RNN_E_SHAPE;
+  for (int i = 0; i < n_info; ++i) info[i] = 0;
+  if (desc->mode == RNN_MODE_RSSM_PRIOR) {
+    RssmPlan p;
+    if ((rc = plan_rssm(desc, cus, &p)) != RNN_OK) return rc;
+    info[0] = 3; info[1] = p.ngroups * p.nw; info[2] = p.lds; info[3] = p.rows; info[4] = p.h_per;
+    info[5] = p.nw; info[6] = 0; info[7] = p.ngroups;
+    return RNN_OK;
+  }
+  long long n_tok = 0;
+  int t_max = 0;
+  if ((rc = validate_lengths(desc, lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
+  const Dims m = dims_of(desc, n_tok);
+  ScanPlan p;
+  if ((rc = plan_scan(desc, m, cus, &p)) != RNN_OK) return rc;
+  info[0] = 2; info[1] = m.D * p.nbb * p.ns; info[2] = p.lds; info[3] = p.bb; info[4] = p.hs;
+  info[5] = p.ns; info[6] = p.ps; info[7] = p.nbb;
   return RNN_OK;
 }
 

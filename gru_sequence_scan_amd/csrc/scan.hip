@@ -28,10 +28,10 @@ namespace rnnk {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxEpt = 8;  // owned gate elements per thread: bb * hs <= 2048
+constexpr int kMaxEpt = 4;  // owned gate elements per thread: bb * hs <= 1024
 
 struct ScanLds {
-  int ws, wr, as, acc, flag, total;  // byte offsets
+  int ws, wr, as, acc, lens, flag, total;  // byte offsets
   int ws_ld, wr_ld, as_ld, acc_ld;    // row strides in elements
   int ncw, ncp;                       // W rows (padded to 16), acc columns
 };
@@ -57,43 +57,118 @@ __host__ __device__ inline ScanLds scan_lds(const ScanArgs& a, int esize) {
   L.wr = off; off += a.mode == kLSTMP ? rup(ps16 * L.wr_ld * esize, 16) : 0;
   L.as = off; off += rup(bb16 * L.as_ld * esize, 16);
   L.acc = off; off += rup(bb16 * L.acc_ld * 4, 16);
+  L.lens = off; off += rup(a.bb * 4, 16);
   L.flag = off; off += 16;
   L.total = off;
   return L;
 }
 
-// acc[r][c] = sum_k A[r][k] * W[c][k] on 16x16 MFMA tiles (bb a multiple of
-// 16). Tiles are dealt over the 4 waves.
+// One 16-byte chunk per lane of each operand feeds one 16x16 MFMA step:
+// bf16 16x16x32 takes 8 values of k per lane directly; fp32 16x16x4 takes
+// one value per lane per instruction, so the chunk's 4 values go to 4
+// instructions. Lane l supplies k-group l / 16 of every step for both
+// operands, which keeps each dot product intact.
+template <typename DT>
+struct Chunk;
+template <>
+struct Chunk<bf16> {
+  typedef bf16x8 T;
+  static constexpr int kK = 32;  // k covered by one chunk across the 4 lane quads
+  __device__ static f32x4 mfma(const T& a, const T& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Chunk<float> {
+  typedef f32x4 T;
+  static constexpr int kK = 16;
+  __device__ static f32x4 mfma(const T& a, const T& b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+  }
+};
+
+// NT output tiles of one wave over the whole K, two chunks of loads in flight.
+template <typename DT, int NT>
+__device__ __forceinline__ void mm_tiles(const DT* As, int as_ld, const DT* Ws, int w_ld, float* acc, int acc_ld,
+                                         const int* tm, const int* tn, int kp) {
+  typedef typename Chunk<DT>::T V;
+  constexpr int kEpc = 16 / sizeof(DT);
+  constexpr int kK = Chunk<DT>::kK;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  const DT* ap[NT];
+  const DT* bp[NT];
+  f32x4 c[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    ap[j] = As + (tm[j] * 16 + lr) * as_ld + lq * kEpc;
+    bp[j] = Ws + (tn[j] * 16 + lr) * w_ld + lq * kEpc;
+    c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int nch = kp / kK;
+  int ch = 0;
+  for (; ch + 1 < nch; ch += 2) {
+    V a0[NT], b0[NT], a1[NT], b1[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      a0[j] = *reinterpret_cast<const V*>(ap[j] + ch * kK);
+      b0[j] = *reinterpret_cast<const V*>(bp[j] + ch * kK);
+      a1[j] = *reinterpret_cast<const V*>(ap[j] + (ch + 1) * kK);
+      b1[j] = *reinterpret_cast<const V*>(bp[j] + (ch + 1) * kK);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) c[j] = Chunk<DT>::mfma(a0[j], b0[j], c[j]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) c[j] = Chunk<DT>::mfma(a1[j], b1[j], c[j]);
+  }
+  if (ch < nch) {
+    V a0[NT], b0[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      a0[j] = *reinterpret_cast<const V*>(ap[j] + ch * kK);
+      b0[j] = *reinterpret_cast<const V*>(bp[j] + ch * kK);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) c[j] = Chunk<DT>::mfma(a0[j], b0[j], c[j]);
+  }
+  // 16x16 accumulator layout: lane holds column l % 16, rows 4 * (l / 16) + v.
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[(tm[j] * 16 + 4 * lq + v) * acc_ld + tn[j] * 16 + lr] = c[j][v];
+}
+
+// acc[r][c] = sum_k A[r][k] * W[c][k] on 16x16 MFMA tiles (rows a multiple
+// of 16), A and W in LDS. Each wave takes a contiguous run of tiles and
+// computes up to four of them together.
 template <typename DT>
 __device__ void mm_mfma(const char* lds, int as_off, int as_ld, int w_off, int w_ld, float* acc,
                         int acc_ld, int mtiles, int ntiles, int kp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, lq = lane >> 4;
   const DT* As = reinterpret_cast<const DT*>(lds + as_off);
   const DT* Ws = reinterpret_cast<const DT*>(lds + w_off);
-  for (int ti = wave; ti < mtiles * ntiles; ti += 4) {
-    const int mt = ti / ntiles, nt = ti - mt * ntiles;
-    const DT* arow = As + (mt * 16 + lr) * as_ld;
-    const DT* brow = Ws + (nt * 16 + lr) * w_ld;
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (sizeof(DT) == 2) {
-      for (int k0 = 0; k0 < kp; k0 += 32) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(arow + k0 + 8 * lq);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(brow + k0 + 8 * lq);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
-      }
-    } else {
-      for (int k0 = 0; k0 < kp; k0 += 16) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(arow + k0 + 4 * lq);
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(brow + k0 + 4 * lq);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], bv[3], c, 0, 0, 0);
-      }
-    }
+  const int wave = threadIdx.x >> 6;
+  const int total = mtiles * ntiles;
+  const int per = (total + 3) / 4;
+  int t0 = wave * per;
+  const int t1 = min(total, t0 + per);
+  while (t0 < t1) {
+    const int n = min(4, t1 - t0);
+    int tm[4], tn[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[(mt * 16 + 4 * lq + v) * acc_ld + nt * 16 + lr] = c[v];
+    for (int j = 0; j < 4; ++j) {
+      const int tt = t0 + min(j, n - 1);
+      tm[j] = tt / ntiles;
+      tn[j] = tt - tm[j] * ntiles;
+    }
+    switch (n) {
+      case 1: mm_tiles<DT, 1>(As, as_ld, Ws, w_ld, acc, acc_ld, tm, tn, kp); break;
+      case 2: mm_tiles<DT, 2>(As, as_ld, Ws, w_ld, acc, acc_ld, tm, tn, kp); break;
+      case 3: mm_tiles<DT, 3>(As, as_ld, Ws, w_ld, acc, acc_ld, tm, tn, kp); break;
+      default: mm_tiles<DT, 4>(As, as_ld, Ws, w_ld, acc, acc_ld, tm, tn, kp); break;
+    }
+    t0 += n;
   }
 }
 
@@ -183,9 +258,15 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     return (uint32_t)(((par * a.D + d) * a.B + b) * a.Kp + k);
   };
   auto mx_el = [&](int b, int j) -> uint32_t { return (uint32_t)((d * a.B + b) * a.Hp + j); };
-  auto len_of = [&](int b) -> int { return a.lengths ? a.lengths[b] : a.T; };
-
+  // Lengths of the block's rows, staged once: reading them from global
+  // memory inside the step loop would make every use wait for all of the
+  // wave's outstanding memory operations.
+  int* lens = reinterpret_cast<int*>(lds + L.lens);
+  for (int r = tid; r < a.bb; r += kThreads)
+    lens[r] = b0 + r < a.B ? (a.lengths ? a.lengths[b0 + r] : a.T) : 0;
   if (tid == 0) *abort_flag = 0;
+  __syncthreads();
+  auto len_of = [&](int b) -> int { return lens[b - b0]; };
 
   // --- resident weights -----------------------------------------------------
   const DT* whh = reinterpret_cast<const DT*>(a.w_hh[d]);
@@ -207,12 +288,18 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   const DT* h0 = reinterpret_cast<const DT*>(a.h0[d]);
   const DT* c0 = reinterpret_cast<const DT*>(a.c0[d]);
   const DT* bhh = reinterpret_cast<const DT*>(a.b_hh[d]);
+  // Owned element i: row er[i] of the block, unit eu[i] of the slice, and the
+  // row's length (0 when the element is not owned), computed once.
+  int lenreg[kMaxEpt], er[kMaxEpt], eu[kMaxEpt];
 #pragma unroll
   for (int i = 0; i < kMaxEpt; ++i) {
     const int e = tid + i * kThreads;
     const int r = e / a.hs, u = e - r * a.hs;
     const int b = b0 + r;
+    er[i] = r;
+    eu[i] = u;
     hreg[i] = 0.f; creg[i] = 0.f; bhn[i] = 0.f;
+    lenreg[i] = (e < n_el && u < hs_act && b < a.B) ? len_of(b) : 0;
     if (e < n_el && u < hs_act && b < a.B) {
       const int j = j0 + u;
       if (a.mode != kLSTMP && h0) hreg[i] = to_f32<DT>(h0[(size_t)b * a.K + j]);
@@ -252,12 +339,11 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     }
   }
 
-  // Longest sequence of this block bounds the steps it takes part in.
+  // Longest sequence of this block bounds the steps it takes part in
+  // (wave-uniform, so per-step indices stay in scalar registers).
   int maxlen = 0;
   for (int r = 0; r < a.bb && b0 + r < a.B; ++r) maxlen = max(maxlen, len_of(b0 + r));
-
-  unsigned nbar = 1;
-  if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+  maxlen = __builtin_amdgcn_readfirstlane(maxlen);
 
   const bool use_mfma = (a.bb % 16) == 0;
   float* acc = reinterpret_cast<float*>(lds + L.acc);
@@ -265,24 +351,15 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   DT* yout = reinterpret_cast<DT*>(a.y);
   DT* hn = reinterpret_cast<DT*>(a.h_n[d]);
   DT* cn = reinterpret_cast<DT*>(a.c_n[d]);
-  int par = 0;  // exchange buffer holding h_{t-1}
 
-  for (int step = 0; step < a.T; ++step) {
-    const int t = rev ? a.T - 1 - step : step;
-    if (t >= maxlen) {
-      if (rev) continue;  // reverse rows have not started yet
-      break;              // forward rows are all finished
-    }
+  // Gx of the owned elements for step t (zero for inactive ones).
+  float gxv[kMaxEpt][4];
+  auto prefetch = [&](int t) {
     const int rowbase = a.packed ? a.offsets[t] : t * a.B;
-
-    // Prefetch this step's Gx for the owned elements.
-    float gxv[kMaxEpt][4];
 #pragma unroll
     for (int i = 0; i < kMaxEpt; ++i) {
-      const int e = tid + i * kThreads;
-      const int r = e / a.hs, u = e - r * a.hs;
-      const int b = b0 + r;
-      const bool act = e < n_el && u < hs_act && b < a.B && t < len_of(b);
+      const int b = b0 + er[i], u = eu[i];
+      const bool act = t < lenreg[i];
 #pragma unroll
       for (int q = 0; q < 4; ++q) gxv[i][q] = 0.f;
       if (act) {
@@ -292,6 +369,22 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
           if (q < gates) gxv[i][q] = g[q * a.H];
       }
     }
+  };
+  // The block takes part in steps t < maxlen: forward t = 0 .. maxlen-1,
+  // reverse t = maxlen-1 .. 0 (earlier reverse steps have no active row).
+  const int nsteps = maxlen;
+  auto t_of = [&](int k) { return rev ? maxlen - 1 - k : k; };
+
+  // h0 is published: arrive, prefetch the first step's Gx, then wait.
+  unsigned nbar = 1;
+  group_arrive(counter);
+  if (nsteps > 0) prefetch(t_of(0));
+  if (!group_wait(counter, nbar * a.ns, a.status, abort_flag)) return;
+  int par = 0;  // exchange buffer holding h_{t-1}
+
+  for (int k = 0; k < nsteps; ++k) {
+    const int t = t_of(k);
+    const int rowbase = a.packed ? a.offsets[t] : t * a.B;
 
     // h_{t-1} of the block -> LDS, then the hidden-hidden product.
     load_tile_coherent<DT>(hx_rs, hx_el(par, b0, 0), a.Kp, b0, a.B, use_mfma ? rup(a.bb, 16) : a.bb,
@@ -303,19 +396,15 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
       mm_valu<DT>(lds, L.as, L.as_ld, L.ws, L.ws_ld, acc, L.acc_ld, a.bb, gates * a.hs, a.Kp);
     __syncthreads();
 
-    // Gate math on the owned elements.
+    // Gate math on the owned elements; only the exchanged state is stored
+    // before the barrier arrival.
 #pragma unroll
     for (int i = 0; i < kMaxEpt; ++i) {
-      const int e = tid + i * kThreads;
-      const int r = e / a.hs, u = e - r * a.hs;
+      const int r = er[i], u = eu[i];
       const int b = b0 + r;
-      if (!(e < n_el && u < hs_act && b < a.B)) continue;
-      const int lb = len_of(b);
-      if (t >= lb) continue;
-      const bool last = rev ? (t == 0) : (t == lb - 1);
+      if (t >= lenreg[i]) continue;
       const int j = j0 + u;
       const float* ar = acc + r * L.acc_ld;
-      const size_t yrow = (size_t)(rowbase + b) * DK + d * a.K;
       if (a.mode == kGRU) {
         const float rg = fsigmoid(gxv[i][0] + ar[u]);
         const float zg = fsigmoid(gxv[i][1] + ar[a.hs + u]);
@@ -323,8 +412,6 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const float h = (1.f - zg) * ng + zg * hreg[i];
         hreg[i] = h;
         coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), h);
-        yout[yrow + j] = from_f32<DT>(h);
-        if (last && hn) hn[(size_t)b * a.K + j] = from_f32<DT>(h);
       } else {
         const float ig = fsigmoid(gxv[i][0] + ar[u]);
         const float fg = fsigmoid(gxv[i][1] + ar[a.hs + u]);
@@ -333,18 +420,29 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const float c = fg * creg[i] + ig * gg;
         const float m = og * ftanh(c);
         creg[i] = c;
-        if (last && cn) cn[(size_t)b * a.H + j] = from_f32<DT>(c);
-        if (a.mode == kLSTM) {
+        hreg[i] = m;
+        if (a.mode == kLSTM)
           coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), m);
-          yout[yrow + j] = from_f32<DT>(m);
-          if (last && hn) hn[(size_t)b * a.K + j] = from_f32<DT>(m);
-        } else {
+        else
           coh_store_elem<DT>(mx_rs, mx_el(b, j), m);
-        }
       }
     }
     ++nbar;
-    if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+    group_arrive(counter);
+    // While the other members arrive: outputs of this step, Gx of the next.
+#pragma unroll
+    for (int i = 0; i < kMaxEpt; ++i) {
+      const int b = b0 + er[i], u = eu[i];
+      const int lb = lenreg[i];
+      if (t >= lb) continue;
+      const bool last = rev ? (t == 0) : (t == lb - 1);
+      const int j = j0 + u;
+      if (a.mode != kLSTMP) yout[(size_t)(rowbase + b) * DK + d * a.K + j] = from_f32<DT>(hreg[i]);
+      if (last && hn && a.mode != kLSTMP) hn[(size_t)b * a.K + j] = from_f32<DT>(hreg[i]);
+      if (last && cn && a.mode != kGRU) cn[(size_t)b * a.H + j] = from_f32<DT>(creg[i]);
+    }
+    if (k + 1 < nsteps) prefetch(t_of(k + 1));
+    if (!group_wait(counter, nbar * a.ns, a.status, abort_flag)) return;
 
     if (a.mode == kLSTMP) {
       // hidden-projection dense: h_t = m_t W_hr^T for this slice of P
@@ -360,16 +458,25 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const int r = e / a.ps, p = e - r * a.ps;
         const int b = b0 + r;
         if (p >= ps_act || b >= a.B) continue;
+        if (t >= len_of(b)) continue;
+        coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, p0 + p), acc[r * L.acc_ld + p]);
+      }
+      ++nbar;
+      group_arrive(counter);
+      // acc stays untouched until the next product, so the outputs are
+      // written from it while the other members arrive.
+      for (int e = tid; e < a.bb * a.ps; e += kThreads) {
+        const int r = e / a.ps, p = e - r * a.ps;
+        const int b = b0 + r;
+        if (p >= ps_act || b >= a.B) continue;
         const int lb = len_of(b);
         if (t >= lb) continue;
         const bool last = rev ? (t == 0) : (t == lb - 1);
-        const float h = acc[r * L.acc_ld + p];
-        coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, p0 + p), h);
-        yout[(size_t)(rowbase + b) * DK + d * a.K + p0 + p] = from_f32<DT>(h);
-        if (last && hn) hn[(size_t)b * a.K + p0 + p] = from_f32<DT>(h);
+        const DT h = from_f32<DT>(acc[r * L.acc_ld + p]);
+        yout[(size_t)(rowbase + b) * DK + d * a.K + p0 + p] = h;
+        if (last && hn) hn[(size_t)b * a.K + p0 + p] = h;
       }
-      ++nbar;
-      if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+      if (!group_wait(counter, nbar * a.ns, a.status, abort_flag)) return;
     }
     par ^= 1;
   }

@@ -221,6 +221,14 @@ int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const R
  * RNN_E_TIMEOUT). Returns RNN_OK or RNN_E_HIP / RNN_E_NULL. */
 int rnn_read_status(const void* workspace, void* stream, int* device_status);
 
+/* Host-only: the launch shape rnn_forward would use for this problem on a
+ * device with `cus` compute units. info[0..7] = {kernel (2 scan, 3 RSSM),
+ * workgroups, LDS bytes per workgroup, batch rows per workgroup, hidden
+ * units per workgroup, workgroups per group, projection outputs per
+ * workgroup (LSTMP), number of groups per direction}; n_info >= 8. For
+ * inspection and tests; touches no device. */
+int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int* info, int n_info);
+
 /* RNN_OK when the current device is a gfx950 GPU; RNN_E_DEVICE otherwise. */
 int rnn_device_check(void);
 
