@@ -48,11 +48,18 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K4 = (K + 3) >> 2;
   const float* xr = X + (lane & 3) * ldx;
+  // One accumulator: an MFMA whose accumulator input is exactly the
+  // previous MFMA's output issues back to back, so a single chain runs at
+  // full rate and needs no register shuffling. Two chunks per iteration let
+  // the second chunk's LDS reads overlap the first chunk's products. Bounds
+  // are wave-uniform.
   auto run = [&](int c, int k4a, int k4b) -> f32x4 {
+    k4a = __builtin_amdgcn_readfirstlane(k4a);
+    k4b = __builtin_amdgcn_readfirstlane(k4b);
     const float* wr = W + (c < N ? c : N - 1) * ldw;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     int k4 = k4a;
-    for (; k4 + 1 < k4b; k4 += 2) {
+    for (; k4 + 2 <= k4b; k4 += 2) {
       const f32x4 a0 = *reinterpret_cast<const f32x4*>(xr + 4 * k4);
       const f32x4 b0 = *reinterpret_cast<const f32x4*>(wr + 4 * k4);
       const f32x4 a1 = *reinterpret_cast<const f32x4*>(xr + 4 * k4 + 4);
@@ -63,15 +70,15 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
       for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(a1[e], b1[e], acc, 0, 0, 0);
     }
     if (k4 < k4b) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(xr + 4 * k4);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(wr + 4 * k4);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(xr + 4 * k4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(wr + 4 * k4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(a0[e], b0[e], acc, 0, 0, 0);
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(a[e], b[e], acc, 0, 0, 0);
     }
     return acc;
   };
   if (N > 64) {
-    for (int cg = wave; cg * 64 < N; cg += 4) {
+    for (int cg = __builtin_amdgcn_readfirstlane(wave); cg * 64 < N; cg += 4) {
       const int c = cg * 64 + lane;
       const f32x4 acc = run(c, 0, K4);
       if (c < N) {
@@ -275,9 +282,18 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     }
     for (int i = tid; i < nrows * (L.ld_e / 4); i += kThreads) {
       const int r = i / (L.ld_e / 4), c4 = i - r * (L.ld_e / 4);
+      // all members' partials in a fixed order, eight loads in flight
       f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
-      for (int m = 0; m < a.nw; ++m)
-        s4 += __builtin_bit_cast(f32x4, coh_load16(px_rs, px_el(par, b0 + r, m, 4 * c4) * 4u));
+      for (int m0 = 0; m0 < a.nw; m0 += 8) {
+        u32x4 pv[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) pv[m] = coh_load16(px_rs, px_el(par, b0 + r, min(m0 + m, a.nw - 1), 4 * c4) * 4u);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const f32x4 v = __builtin_bit_cast(f32x4, pv[m]);
+          s4 += (m0 + m < a.nw) ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
       *reinterpret_cast<f32x4*>(sm + L.u + r * L.ld_e + 4 * c4) = s4;
     }
     __syncthreads();
