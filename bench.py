@@ -31,6 +31,25 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32_mfma": 157.3, "f32_vector": 157.3}
 
 KIND_NAMES = {1: "gemm_xw", 2: "scan", 3: "rssm"}
+METRIC = "timestep\u00b7batch/s per RNN config; % of MFMA / on-chip BW roofline"
+UNIT = "timestep\u00b7batch/s"
+
+# Sources whose change invalidates a kernel's measured traffic.
+CSRC = os.path.join(ROOT, "gru_sequence_scan_amd", "csrc")
+KERNEL_SOURCES = {
+    "gemm_xw": ["gemm_xw.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
+    "scan": ["scan.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
+    "rssm": ["rssm.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
+}
+
+# HBM bytes per launch of a workload's dominant kernel, from two rocprofv3
+# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE), each divided by
+# the ratio the same counter reads for a plain copy of known size
+# (--calibrate-copy). Valid only for the kernel sources they were taken on.
+MEASURED_TRAFFIC = {
+    "rssm_b50_t50": {"kernel": "rssm", "fetch_bytes": 269825151, "write_bytes": 36772013,
+                     "sources": "11867ec4abdf93c6"},
+}
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
 # apache/tvm PR "[TOPI] TE implementation of LSTM using scan", benchmark
@@ -51,7 +70,32 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--tile-batch", type=int, default=0)
     ap.add_argument("--tile-hidden", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
     return ap.parse_args()
+
+
+def sources_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def calibrate_copy():
+    """A plain elementwise copy (negation) of 256 MiB fp32, launched 5 times:
+    each launch reads and writes exactly 256 MiB of HBM."""
+    import torch
+    n = 64 << 20
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "kernel": "neg fp32", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                      "launches": 5}), flush=True)
 
 
 def _hip():
@@ -110,6 +154,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the recurrence shards by batch with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
 
     import gru_sequence_scan_amd as gss
@@ -253,28 +300,34 @@ def main():
         kernels.append({"kernel": KIND_NAMES[kd], "index": idx, "avg_us": avg_ms * 1e3,
                         "min_us": float(np.min(per_kernel[j])) * 1e3, "flops": a["flops"], "bytes": a["bytes"]})
     dom = max(kernels, key=lambda k: k["avg_us"])
-    if dom["kernel"] == "rssm":
-        bound, peak, unit = "alu", PEAK_TFLOPS["f32_vector"], "TFLOP/s"
-        achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
-        traffic = None
-    elif dom["kernel"] == "scan" and spec.B < 16:
-        bound, peak, unit = "alu", PEAK_TFLOPS["f32_vector"], "TFLOP/s"
-        achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
-        traffic = None
+    achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
+    unit = "TFLOP/s"
+    if dom["kernel"] == "scan" and spec.B < 16:
+        # the B=1 scans run their products on the vector ALUs
+        bound, peak = "alu", PEAK_TFLOPS["f32_vector"]
     else:
-        bound, unit = "mfma", "TFLOP/s"
+        bound = "mfma"
         peak = PEAK_TFLOPS["bf16"] if spec.dtype == "bf16" else PEAK_TFLOPS["f32_mfma"]
-        achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
-        traffic = None
+    traffic = None
+    meas = MEASURED_TRAFFIC.get(name)
+    digest = sources_digest(dom["kernel"])
+    if meas and meas["kernel"] == dom["kernel"] and meas["sources"] == digest:
+        traffic = meas["fetch_bytes"] + meas["write_bytes"]
     roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
-                "traffic": traffic, "kernel": f"{dom['kernel']}[{dom['index']}]", "avg_us": dom["avg_us"]}
+                "traffic": traffic, "kernel": f"{dom['kernel']}[{dom['index']}]", "avg_us": dom["avg_us"],
+                "algorithmic_flops": dom["flops"], "algorithmic_hbm_bytes": dom["bytes"],
+                "hbm_frac": dom["bytes"] / (dom["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                "sources": digest}
+    if meas and traffic is not None:
+        roofline["traffic_fetch"] = meas["fetch_bytes"]
+        roofline["traffic_write"] = meas["write_bytes"]
 
     ms_per_step = elapsed / K * 1e3
     value = tokens / (elapsed / K)
     ctx = PAGES_CONTEXT.get(name)
     vs = (value / max(ctx.values())) if ctx else None
     rec = {
-        "metric": "timestep·batch/s per RNN config", "value": value, "unit": "timestep·batch/s",
+        "metric": METRIC, "value": value, "unit": UNIT,
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": vs,
         "dtype": spec.dtype, "data": "synthetic", "config": config,
@@ -331,7 +384,7 @@ def cpu_baseline_any(spec, d, seconds):
         rows = int(min(spec.B, max(1, seconds / max(t1, 1e-6))))
         tokens, el = run(rows)
         sample = f"{rows} of {spec.B} batch rows over all timesteps, {el:.1f} s"
-    return {"value": tokens / el, "unit": "timestep·batch/s", "cores": int(threads), "kind": "oracle",
+    return {"value": tokens / el, "unit": UNIT, "cores": int(threads), "kind": "oracle",
             "sample": sample}
 
 
