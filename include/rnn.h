@@ -7,9 +7,10 @@
  *                     CuDNN API for LSTMs with projections", Motivation and
  *                     design discussion), PyTorch gate order [i | f | g | o].
  *   mode LSTMP        LSTM with a recurrent projection h = W_hr (o * tanh c),
- *                     fed back as the recurrent input: "LSTMCell plus one
- *                     matmul" (same issue, design discussion; arXiv 1402.1128
- *                     cited in its Feature section).
+ *                     fed back as the recurrent input: an LSTM cell followed
+ *                     by one more matrix product (same issue, design
+ *                     discussion; arXiv 1402.1128 cited in its Feature
+ *                     section).
  *   mode GRU          GRU with PyTorch's r/z/n convention (pytorch/rl issue
  *                     "[Feature Request] CUDNN version of RSSM", RSSMPrior uses
  *                     nn.GRUCell); the reset gate multiplies W_hn h + b_hn.
@@ -31,7 +32,9 @@
  *   - Tensors are dense with C-canonical strides (pytorch/rl PR "LSTM/GRU
  *     scan: canonical strides + ...", description: a tensor can pass
  *     is_contiguous() and still carry non-canonical strides; callers must
- *     re-materialise). Device pointers must be 16-byte aligned.
+ *     re-materialise). Every device pointer must be aligned to its
+ *     element size and the workspace to 16 bytes; 16-byte aligned inputs
+ *     and weights with rows of a multiple of 16 bytes take vector loads.
  *   - Weight pointers are read-only and may alias one flat storage (same PR:
  *     per-layer views of a single flat parameter storage).
  *   - All validation happens once, before anything is enqueued (same PR,
@@ -89,7 +92,8 @@ typedef enum RnnStatus {
   RNN_E_LENGTHS = -4,     /* a length outside [1, T], or packed lengths not
                              sorted non-increasing                             */
   RNN_E_WORKSPACE = -5,   /* workspace NULL or smaller than required           */
-  RNN_E_ALIGN = -6,       /* a device pointer is not 16-byte aligned           */
+  RNN_E_ALIGN = -6,       /* a device pointer is not aligned to its element
+                             size, or the workspace not to 16 bytes            */
   RNN_E_DEVICE = -7,      /* no usable gfx950 device is current                */
   RNN_E_HIP = -8,         /* a HIP runtime call or launch failed               */
   RNN_E_TIMEOUT = -9,     /* device status only: a step barrier waited too long
