@@ -35,6 +35,51 @@ constexpr int kMaxRows = 4;  // batch rows per group: one 4x4 MFMA block row set
 
 __host__ __device__ inline int r4(int x) { return (x + 3) & ~3; }
 
+// acc += sum over 16-byte chunks k4 in [k4a, k4b) of the 4x4x1 MFMA products
+// of X chunk (lane's batch row) and W chunk (lane's output column). One
+// accumulator: an MFMA whose accumulator input is exactly the previous MFMA's
+// output issues back to back, so a single chain runs at full rate and needs
+// no register shuffling. Four chunks per iteration keep their eight LDS reads
+// in flight together. Bounds must be wave-uniform.
+__device__ __forceinline__ f32x4 dot_chain(const float* xr, const float* wr, int k4a, int k4b, f32x4 acc) {
+  k4a = __builtin_amdgcn_readfirstlane(k4a);
+  k4b = __builtin_amdgcn_readfirstlane(k4b);
+  int k4 = k4a;
+  for (; k4 + 4 <= k4b; k4 += 4) {
+    f32x4 x[4], y[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x[q] = *reinterpret_cast<const f32x4*>(xr + 4 * (k4 + q));
+      y[q] = *reinterpret_cast<const f32x4*>(wr + 4 * (k4 + q));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(x[q][e], y[q][e], acc, 0, 0, 0);
+  }
+  for (; k4 < k4b; ++k4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(xr + 4 * k4);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(wr + 4 * k4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(x[e], y[e], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Sum the four waves' K-split partial products (lane = column) held in `red`
+// into out[v * ldo + c], c < N, for the four rows v.
+__device__ __forceinline__ void reduce_waves(const f32x4& acc, float* red, float* out, int ldo, int N) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[(wave * 4 + v) * 64 + lane] = acc[v];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 4 * N; i += kThreads) {
+    const int v = i / N, c = i - v * N;
+    out[v * ldo + c] = red[(0 * 4 + v) * 64 + c] + red[(1 * 4 + v) * 64 + c] + red[(2 * 4 + v) * 64 + c] +
+                       red[(3 * 4 + v) * 64 + c];
+  }
+}
+
 // out[v * ldo + c] = sum_{k < K} X[v * ldx + k] * W[c * ldw + k] for all four
 // rows v of X (rows past the group's batch rows hold zeros and are ignored
 // by the callers) and c < N, on v_mfma_f32_4x4x1f32: 16 blocks of 4x4 per
@@ -48,39 +93,11 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K4 = (K + 3) >> 2;
   const float* xr = X + (lane & 3) * ldx;
-  // One accumulator: an MFMA whose accumulator input is exactly the
-  // previous MFMA's output issues back to back, so a single chain runs at
-  // full rate and needs no register shuffling. Two chunks per iteration let
-  // the second chunk's LDS reads overlap the first chunk's products. Bounds
-  // are wave-uniform.
-  auto run = [&](int c, int k4a, int k4b) -> f32x4 {
-    k4a = __builtin_amdgcn_readfirstlane(k4a);
-    k4b = __builtin_amdgcn_readfirstlane(k4b);
-    const float* wr = W + (c < N ? c : N - 1) * ldw;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int k4 = k4a;
-    for (; k4 + 2 <= k4b; k4 += 2) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(xr + 4 * k4);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(wr + 4 * k4);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(xr + 4 * k4 + 4);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(wr + 4 * k4 + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(a0[e], b0[e], acc, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(a1[e], b1[e], acc, 0, 0, 0);
-    }
-    if (k4 < k4b) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(xr + 4 * k4);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(wr + 4 * k4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(a[e], b[e], acc, 0, 0, 0);
-    }
-    return acc;
-  };
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   if (N > 64) {
     for (int cg = __builtin_amdgcn_readfirstlane(wave); cg * 64 < N; cg += 4) {
       const int c = cg * 64 + lane;
-      const f32x4 acc = run(c, 0, K4);
+      const f32x4 acc = dot_chain(xr, W + (c < N ? c : N - 1) * ldw, 0, K4, zero4);
       if (c < N) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) out[v * ldo + c] = acc[v];
@@ -90,21 +107,56 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
   }
   const int per = (K4 + 3) >> 2;
   const int ka = min(K4, wave * per), kb = min(K4, ka + per);
-  const f32x4 acc = run(lane, ka, kb);
+  reduce_waves(dot_chain(xr, W + (lane < N ? lane : N - 1) * ldw, ka, kb, zero4), red, out, ldo, N);
+}
+
+// The GRU products of the owned slice of hp units in one K-split pass:
+// output columns [r | z | n_x | n_h], hp each, where
+//   r, z : W_ih e + W_hh h   (the sum both gates need),
+//   n_x  : W_ih e            (input part of the candidate),
+//   n_h  : W_hh h            (hidden part; the reset gate scales it).
+// The reduction runs over the concatenated chunks [e | h]; a column that takes
+// no part in a segment reads the shared zero row. Slices of up to 16 units
+// split K over the waves; wider ones give the waves whole column passes.
+__device__ void gru_product(const float* e, int lde, const float* h, int ldh, const float* wih, const float* whh,
+                            const float* zero, float* out, int ldo, int hp, int E, int Hb, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int E4 = (E + 3) >> 2, H4 = (Hb + 3) >> 2, N = 4 * hp;
+  const float* xe = e + (lane & 3) * lde;
+  const float* xh = h + (lane & 3) * ldh;
+  // W rows of output column c in the e and h segments
+  auto rows_of = [&](int c, const float*& we, const float*& wh) {
+    const int q = c / hp, j = c - q * hp;  // gate block and unit
+    we = (c < N && q < 3) ? wih + (q * hp + j) * lde : zero;
+    wh = (c < N && q != 2) ? whh + ((q == 3 ? 2 : q) * hp + j) * ldh : zero;
+  };
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  if (N > 64) {  // wide slices: whole 64-column passes per wave, no K split
+    for (int cg = __builtin_amdgcn_readfirstlane(wave); cg * 64 < N; cg += 4) {
+      const int c = cg * 64 + lane;
+      const float *we, *wh;
+      rows_of(c, we, wh);
+      const f32x4 acc = dot_chain(xh, wh, 0, H4, dot_chain(xe, we, 0, E4, zero4));
+      if (c < N) {
 #pragma unroll
-  for (int v = 0; v < 4; ++v) red[(wave * 4 + v) * 64 + lane] = acc[v];
-  __syncthreads();
-  for (int i = threadIdx.x; i < 4 * N; i += kThreads) {
-    const int v = i / N, c = i - v * N;
-    out[v * ldo + c] = red[(0 * 4 + v) * 64 + c] + red[(1 * 4 + v) * 64 + c] + red[(2 * 4 + v) * 64 + c] +
-                       red[(3 * 4 + v) * 64 + c];
+        for (int v = 0; v < 4; ++v) out[v * ldo + c] = acc[v];
+      }
+    }
+    return;
   }
+  const float *we, *wh;
+  rows_of(lane, we, wh);
+  const int Q = E4 + H4, per = (Q + 3) >> 2;
+  const int qa = min(Q, wave * per), qb = min(Q, qa + per);
+  f32x4 acc = dot_chain(xe, we, min(qa, E4), min(qb, E4), zero4);
+  acc = dot_chain(xh, wh, max(qa, E4) - E4, max(qb, E4) - E4, acc);
+  reduce_waves(acc, red, out, ldo, N);
 }
 
 struct RssmLds {
   // float offsets (all multiples of 4)
-  int was, bas, w2, b2, wih, whh, bih, bhh, w1s, b1;
-  int sa, e, h, hs, u, v, gi, gh, pu, red, flag, total;
+  int was, bas, w2, b2, wih, whh, w1s, b1;
+  int sa, e, h, hs, u, v, gi, zero, red, flag, total;
   int ld_sa, ld_e, ld_h, ld_hs, ld_v, ld_g;
 };
 
@@ -116,7 +168,7 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   L.ld_h = r4(a.Hb);
   L.ld_hs = r4(a.h_per);
   L.ld_v = r4(2 * a.S);
-  L.ld_g = r4(3 * a.h_per);
+  L.ld_g = r4(4 * a.h_per);
   const int R = kMaxRows;
   int o = 0;
   auto take = [&](int n) { const int at = o; o += r4(n); return at; };
@@ -126,8 +178,6 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   L.b2 = take(2 * a.S);
   L.wih = take(3 * a.h_per * L.ld_e);
   L.whh = take(3 * a.h_per * L.ld_h);
-  L.bih = take(3 * a.h_per);
-  L.bhh = take(3 * a.h_per);
   L.w1s = take(a.E * L.ld_hs);
   L.b1 = take(a.E);
   L.sa = take(R * L.ld_sa);
@@ -137,8 +187,7 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   L.u = take(R * L.ld_e);
   L.v = take(R * L.ld_v);
   L.gi = take(R * L.ld_g);
-  L.gh = take(R * L.ld_g);
-  L.pu = take(R * L.ld_e);
+  L.zero = take(L.ld_e > L.ld_h ? L.ld_e : L.ld_h);
   L.red = take(4 * 4 * 64);
   L.flag = take(4);
   L.total = o * 4;
@@ -197,13 +246,6 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     const int q = r / hp, jj = r - q * hp;
     if (jj < hn) sm[L.whh + r * L.ld_h + c] = a.w_hh[(size_t)(q * Hb + j0 + jj) * Hb + c];
   }
-  for (int i = tid; i < 3 * hp; i += kThreads) {
-    const int q = i / hp, jj = i - q * hp;
-    if (jj < hn) {
-      sm[L.bih + i] = a.b_ih[q * Hb + j0 + jj];
-      sm[L.bhh + i] = a.b_hh[q * Hb + j0 + jj];
-    }
-  }
   // W_1 columns of the slice: w1s[k][jj] = W_1[k][j0 + jj]
   for (int i = tid; i < E * hp; i += kThreads) {
     const int k = i / hp, jj = i - k * hp;
@@ -224,6 +266,17 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
   const int own_r = tid / hp, own_j = tid - own_r * hp;
   const bool owner = tid < a.rows * hp && own_r < nrows && own_j < hn;
   float hreg = (owner && a.h0) ? a.h0[(size_t)(b0 + own_r) * Hb + j0 + own_j] : 0.f;
+  // the owner's gate biases: r and z take b_ih + b_hh, the candidate keeps
+  // b_hn inside the reset product
+  float bias_r = 0.f, bias_z = 0.f, bias_nx = 0.f, bias_nh = 0.f;
+  if (owner) {
+    const float* bi = a.b_ih;
+    const float* bh = a.b_hh;
+    bias_r = bi[j0 + own_j] + bh[j0 + own_j];
+    bias_z = bi[Hb + j0 + own_j] + bh[Hb + j0 + own_j];
+    bias_nx = bi[2 * Hb + j0 + own_j];
+    bias_nh = bh[2 * Hb + j0 + own_j];
+  }
   // per-thread (row, state unit) of the tail, fixed for the launch
   const int tr = tid / S, tc = tid - tr * S;
   const bool tail_owner = tid < nrows * S;
@@ -241,31 +294,36 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
   unsigned nbar = 0;
   for (int t = 0; t < a.T; ++t) {
     const int par = t & 1;
-    // ---- GRU phase on the owned slice: gi = W_ih e_t, gh = W_hh h_{t-1} ----
-    mv4(sm + L.e, L.ld_e, sm + L.wih, L.ld_e, sm + L.gi, L.ld_g, 3 * hp, E, red);
-    __syncthreads();
-    mv4(sm + L.h, L.ld_h, sm + L.whh, L.ld_h, sm + L.gh, L.ld_g, 3 * hp, Hb, red);
+    // ---- GRU phase on the owned slice ----
+    gru_product(sm + L.e, L.ld_e, sm + L.h, L.ld_h, sm + L.wih, sm + L.whh, sm + L.zero, sm + L.gi, L.ld_g, hp, E,
+                Hb, red);
     __syncthreads();
     if (owner) {
-      const float* gi = sm + L.gi + own_r * L.ld_g;
-      const float* gh = sm + L.gh + own_r * L.ld_g;
-      const int jr = own_j, jz = hp + own_j, jn = 2 * hp + own_j;
-      const float rg = fsigmoid(gi[jr] + sm[L.bih + jr] + gh[jr] + sm[L.bhh + jr]);
-      const float zg = fsigmoid(gi[jz] + sm[L.bih + jz] + gh[jz] + sm[L.bhh + jz]);
-      const float ng = ftanh(gi[jn] + sm[L.bih + jn] + rg * (gh[jn] + sm[L.bhh + jn]));
+      const float* gg = sm + L.gi + own_r * L.ld_g;
+      const float rg = fsigmoid(gg[own_j] + bias_r);
+      const float zg = fsigmoid(gg[hp + own_j] + bias_z);
+      const float ng = ftanh(gg[2 * hp + own_j] + bias_nx + rg * (gg[3 * hp + own_j] + bias_nh));
       const float h = (1.f - zg) * ng + zg * hreg;
       hreg = h;
       sm[L.hs + own_r * L.ld_hs + own_j] = h;
       coh_store_elem<float>(hx_rs, hx_el(par, b0 + own_r, j0 + own_j), h);
     }
     __syncthreads();
-    // ---- this slice's share of the projector's first layer ----
-    mv4(sm + L.hs, L.ld_hs, sm + L.w1s, L.ld_hs, sm + L.pu, L.ld_e, E, hp, red);
-    __syncthreads();
-    for (int i = tid; i < nrows * (L.ld_e / 4); i += kThreads) {
-      const int r = i / (L.ld_e / 4), c4 = i - r * (L.ld_e / 4);
-      coh_store16(px_rs, px_el(par, b0 + r, w, 4 * c4) * 4u,
-                  *reinterpret_cast<const u32x4*>(sm + L.pu + r * L.ld_e + 4 * c4));
+    // ---- this slice's share of the projector's first layer, stored to the
+    //      exchange straight from the MFMA lanes (lane = output column) ----
+    {
+      const int lane = tid & 63;
+      const float* xr = sm + L.hs + (lane & 3) * L.ld_hs;
+      for (int cg = __builtin_amdgcn_readfirstlane(tid >> 6); cg * 64 < E; cg += 4) {
+        const int c = cg * 64 + lane;
+        const f32x4 acc = dot_chain(xr, sm + L.w1s + (c < E ? c : E - 1) * L.ld_hs, 0, L.ld_hs / 4,
+                                    f32x4{0.f, 0.f, 0.f, 0.f});
+        if (c < E) {
+#pragma unroll
+          for (int v = 0; v < kMaxRows; ++v)
+            if (v < nrows) coh_store_elem<float>(px_rs, px_el(par, b0 + v, w, c), acc[v]);
+        }
+      }
     }
     ++nbar;
     group_arrive(counter);
@@ -275,26 +333,46 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     const float act_v = (act_owner && t + 1 < a.T) ? a.actions[((size_t)(b0 + ar) * a.T + t + 1) * A + ac] : 0.f;
     if (!group_wait(counter, nbar * a.nw, a.status, abort_flag)) return;
 
-    // ---- whole h_t for the next GRU phase; u_t from the summed partials ----
-    for (int i = tid; i < nrows * (a.Hbp / 4); i += kThreads) {
-      const int r = i / (a.Hbp / 4), c4 = i - r * (a.Hbp / 4);
-      *reinterpret_cast<u32x4*>(sm + L.h + r * L.ld_h + 4 * c4) = coh_load16(hx_rs, hx_el(par, b0 + r, 4 * c4) * 4u);
-    }
-    for (int i = tid; i < nrows * (L.ld_e / 4); i += kThreads) {
-      const int r = i / (L.ld_e / 4), c4 = i - r * (L.ld_e / 4);
-      // all members' partials in a fixed order, eight loads in flight
-      f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
-      for (int m0 = 0; m0 < a.nw; m0 += 8) {
-        u32x4 pv[8];
+    // ---- whole h_t for the next GRU phase; u_t from the summed partials.
+    //      Thread i < nrows * EC owns chunk i of h (when it exists) and of the
+    //      partial sums; all its loads are issued before the first is used.
+    //      Elements past Hb or E (exchange padding nobody writes) read as 0.
+    {
+      const int EC = L.ld_e / 4, HC = a.Hbp / 4;
+      const int i = tid;
+      if (i < nrows * EC || i < nrows * HC) {
+        const bool has_h = i < nrows * HC, has_p = i < nrows * EC;
+        const int rh = has_h ? i / HC : 0, ch = i - rh * HC;
+        const int rp = has_p ? i / EC : 0, cp = i - rp * EC;
+        u32x4 hv = {0u, 0u, 0u, 0u};
+        if (has_h) hv = coh_load16(hx_rs, hx_el(par, b0 + rh, 4 * ch) * 4u);
+        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+        if (has_p) {
+          // all members' partials in a fixed order, sixteen loads in flight
+          for (int m0 = 0; m0 < a.nw; m0 += 16) {
+            u32x4 pv[16];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) pv[m] = coh_load16(px_rs, px_el(par, b0 + r, min(m0 + m, a.nw - 1), 4 * c4) * 4u);
+            for (int m = 0; m < 16; ++m)
+              pv[m] = coh_load16(px_rs, px_el(par, b0 + rp, min(m0 + m, a.nw - 1), 4 * cp) * 4u);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const f32x4 v = __builtin_bit_cast(f32x4, pv[m]);
-          s4 += (m0 + m < a.nw) ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < 16; ++m) {
+              const f32x4 v = __builtin_bit_cast(f32x4, pv[m]);
+              s4 += (m0 + m < a.nw) ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (4 * cp + k >= E) s4[k] = 0.f;
+          *reinterpret_cast<f32x4*>(sm + L.u + rp * L.ld_e + 4 * cp) = s4;
+        }
+        if (has_h) {
+          f32x4 hf = __builtin_bit_cast(f32x4, hv);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (4 * ch + k >= Hb) hf[k] = 0.f;
+          *reinterpret_cast<f32x4*>(sm + L.h + rh * L.ld_h + 4 * ch) = hf;
         }
       }
-      *reinterpret_cast<f32x4*>(sm + L.u + r * L.ld_e + 4 * c4) = s4;
     }
     __syncthreads();
     for (int i = tid; i < nrows * E; i += kThreads) {
