@@ -70,6 +70,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--tile-batch", type=int, default=0)
     ap.add_argument("--tile-hidden", type=int, default=0)
+    ap.add_argument("--placement", type=int, default=0, help="0 auto, 1 flat, 2 XCD-aligned groups")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -177,14 +178,15 @@ def main():
     if spec.mode == "rssm":
         w = {k: T(v) for k, v in d["weights"].items()}
         (out, ws) = gss.rssm_prior_unroll(T(d["actions"]), T(d["eps"]), w, tile_batch=args.tile_batch,
-                                          tile_hidden=args.tile_hidden, return_workspace=True)
+                                          tile_hidden=args.tile_hidden, placement=args.placement,
+                                          return_workspace=True)
         B, Tn = d["B"], d["T"]
         desc = gss.RnnDesc()
         desc.mode, desc.dtype, desc.layout = 3, 0, 2
         desc.T, desc.B, desc.num_layers, desc.has_bias = Tn, B, 1, 1
         desc.state_dim, desc.action_dim = d["state_dim"], d["action_dim"]
         desc.embed_dim, desc.belief_dim, desc.scale_lb = d["embed_dim"], d["belief_dim"], 0.1
-        desc.tile_batch, desc.tile_hidden = args.tile_batch, args.tile_hidden
+        desc.tile_batch, desc.tile_hidden, desc.placement = args.tile_batch, args.tile_hidden, args.placement
         wt = gss.RnnWeights()
         wt.w_as, wt.b_as, wt.w_1, wt.b_1, wt.w_2, wt.b_2 = (w[k].data_ptr() for k in
                                                             ("w_as", "b_as", "w_1", "b_1", "w_2", "b_2"))
@@ -204,7 +206,8 @@ def main():
         (out, ws) = gss.rnn_forward(spec.mode, x, params, lengths=d["lengths"], layout=spec.layout,
                                     num_layers=spec.num_layers, bidirectional=spec.bidirectional,
                                     proj_size=spec.proj_size, tile_batch=args.tile_batch,
-                                    tile_hidden=args.tile_hidden, return_workspace=True)
+                                    tile_hidden=args.tile_hidden, placement=args.placement,
+                                    return_workspace=True)
         y, hn, cn = out
         D = 2 if spec.bidirectional else 1
         desc = gss.RnnDesc()
@@ -214,7 +217,7 @@ def main():
         desc.T, desc.B = spec.T, spec.B
         desc.input_size, desc.hidden_size, desc.proj_size = spec.input_size, spec.hidden_size, spec.proj_size
         desc.num_layers, desc.bidirectional, desc.has_bias = spec.num_layers, int(spec.bidirectional), 1
-        desc.tile_batch, desc.tile_hidden = args.tile_batch, args.tile_hidden
+        desc.tile_batch, desc.tile_hidden, desc.placement = args.tile_batch, args.tile_hidden, args.placement
         wt = gss.RnnWeights()
         for i, p in enumerate(params):
             for k, v in p.items():

@@ -42,7 +42,7 @@ class RnnDesc(ctypes.Structure):
         ("action_dim", ctypes.c_int32), ("embed_dim", ctypes.c_int32),
         ("belief_dim", ctypes.c_int32), ("scale_lb", ctypes.c_float),
         ("tile_batch", ctypes.c_int32), ("tile_hidden", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 6),
+        ("placement", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5),
     ]
 
 
@@ -101,6 +101,9 @@ def lib():
         L.rnn_read_status.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
         L.rnn_device_check.restype = ctypes.c_int
         L.rnn_device_check.argtypes = []
+        L.rnn_plan_info.restype = ctypes.c_int
+        L.rnn_plan_info.argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
+                                    ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.c_int]
         if L.rnn_abi_version() != RNN_ABI_VERSION:
             raise RuntimeError("native library ABI version mismatch")
         _lib = L
@@ -140,6 +143,21 @@ def rnn_forward_raw(desc, weights, io, workspace_ptr, ws_bytes, stream_ptr):
     return lib().rnn_forward(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(io),
                              ctypes.c_void_p(workspace_ptr), ctypes.c_size_t(ws_bytes),
                              ctypes.c_void_p(stream_ptr))
+
+
+PLAN_FIELDS = ("kernel", "workgroups", "lds_bytes", "rows", "hidden_per_wg", "members", "proj_per_wg",
+               "groups", "groups_per_xcd")
+
+
+def rnn_plan_info(desc, lengths=None, cus=256, xcds=8):
+    """The launch shape the library would choose on a device with `cus`
+    compute units in `xcds` XCDs (host only), as a dict of PLAN_FIELDS."""
+    keep, lp = _len_ptr(lengths)
+    info = (ctypes.c_int * len(PLAN_FIELDS))()
+    st = lib().rnn_plan_info(ctypes.byref(desc), lp, int(cus), int(xcds), info, len(PLAN_FIELDS))
+    if st != 0:
+        raise RnnError(st, "rnn_plan_info")
+    return dict(zip(PLAN_FIELDS, list(info)))
 
 
 def rnn_read_status(workspace_ptr, stream_ptr):
@@ -211,7 +229,7 @@ def _call(desc, w, io, lengths, device, keep):
 
 def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padded",
                 num_layers=1, bidirectional=False, proj_size=0, hidden_size=None, y_out=None,
-                tile_batch=0, tile_hidden=0, return_workspace=False):
+                tile_batch=0, tile_hidden=0, placement=0, return_workspace=False):
     """Forward of an LSTM / GRU / LSTMP stack on the current HIP stream.
 
     x: padded [T, B, F] or packed [N_tok, F] (float32 or bfloat16, on a GPU).
@@ -284,7 +302,7 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     desc.T, desc.B = T, B
     desc.input_size, desc.hidden_size, desc.proj_size = F, H, proj_size if mode == "lstmp" else 0
     desc.num_layers, desc.bidirectional, desc.has_bias = num_layers, int(bidirectional), int(has_bias)
-    desc.tile_batch, desc.tile_hidden = tile_batch, tile_hidden
+    desc.tile_batch, desc.tile_hidden, desc.placement = tile_batch, tile_hidden, placement
     io = RnnIO()
     io.x = _ptr(x)
     keep_len, io.lengths_host = _len_ptr(lengths)
@@ -296,7 +314,7 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
 
 
 def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale_lb=0.1,
-                      tile_batch=0, tile_hidden=0, return_workspace=False):
+                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False):
     """RSSM prior unrolled over actions [B, T, A] with injected eps [B, T, S].
 
     weights: dict with w_as [E, S + A], b_as, w_ih [3Hb, E], w_hh [3Hb, Hb],
@@ -335,7 +353,7 @@ def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale
     desc.num_layers, desc.bidirectional, desc.has_bias = 1, 0, 1
     desc.state_dim, desc.action_dim, desc.embed_dim, desc.belief_dim = S, A, E, Hb
     desc.scale_lb = scale_lb
-    desc.tile_batch, desc.tile_hidden = tile_batch, tile_hidden
+    desc.tile_batch, desc.tile_hidden, desc.placement = tile_batch, tile_hidden, placement
     io = RnnIO()
     io.x, io.noise, io.s0, io.h0 = _ptr(actions), _ptr(eps), _ptr(state0), _ptr(belief0)
     io.means, io.stds, io.states, io.beliefs = _ptr(means), _ptr(stds), _ptr(states), _ptr(beliefs)

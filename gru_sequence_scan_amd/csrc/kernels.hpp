@@ -37,6 +37,9 @@ struct ScanArgs {
   int ns;            // workgroups per group (one group = one direction x batch block)
   int ps;            // projection outputs per workgroup (LSTMP)
   int nbb;           // batch blocks
+  int nxcd;          // XCDs the launch is dealt over (round-robin by workgroup id)
+  int gpx;           // > 0: groups per XCD, members of a group share one XCD;
+                     // 0: consecutive workgroup ids form a group
   int Kp, Hp;        // padded widths of the exchange rows (multiples of 32)
   // per direction tensors (already offset to this layer)
   const void* w_hh[2];
@@ -67,6 +70,9 @@ struct RssmArgs {
   int ngroups;
   int nw;            // workgroups per group
   int h_per;         // GRU hidden units per workgroup
+  int nxcd;          // XCDs the launch is dealt over (round-robin by workgroup id)
+  int gpx;           // > 0: groups per XCD, members of a group share one XCD;
+                     // 0: consecutive workgroup ids form a group
   const float* w_as; const float* b_as;
   const float* w_ih; const float* w_hh; const float* b_ih; const float* b_hh;
   const float* w_1; const float* b_1; const float* w_2; const float* b_2;

@@ -33,6 +33,7 @@ int cdiv(int x, int m) { return (x + m - 1) / m; }
 struct DeviceInfo {
   bool ok = false;
   int cus = 0;
+  int xcds = 1;
 };
 
 constexpr int kMaxDevices = 64;
@@ -50,6 +51,8 @@ int current_device_info(DeviceInfo* out) {
     if (hipGetDeviceProperties(&p, dev) == hipSuccess) {
       info.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
       info.cus = p.multiProcessorCount;
+      int x = 0;
+      if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && x > 0) info.xcds = x;
     }
     g_dev[dev] = info;
     g_dev_init[dev] = true;
@@ -67,6 +70,7 @@ int validate_desc(const RnnDesc* d) {
   if (!d) return RNN_E_NULL;
   for (int r : d->reserved)
     if (r != 0) return RNN_E_SHAPE;
+  if (d->placement < 0 || d->placement > 2) return RNN_E_SHAPE;
   if (d->dtype != RNN_DTYPE_F32 && d->dtype != RNN_DTYPE_BF16) return RNN_E_UNSUPPORTED;
   if (d->T < 1 || d->B < 1) return RNN_E_SHAPE;
   if (d->tile_batch < 0 || d->tile_hidden < 0) return RNN_E_SHAPE;
@@ -211,10 +215,12 @@ double mm_us(bool mfma, int esize, int rows, int cols, int kp) {
 }
 
 struct ScanPlan {
-  int bb, hs, ns, ps, nbb, lds;
+  int bb, hs, ns, ps, nbb, gpx, lds;
 };
 
-int plan_scan(const RnnDesc* d, const Dims& m, int cus, ScanPlan* out) {
+int scan_grid(const ScanPlan& p, int D, int xcds) { return p.gpx > 0 ? xcds * p.gpx * p.ns : D * p.nbb * p.ns; }
+
+int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, ScanPlan* out) {
   const int B = d->B, H = d->hidden_size, P = d->proj_size;
   const bool lstmp = d->mode == RNN_MODE_LSTMP;
   std::vector<int> bbs;
@@ -232,6 +238,7 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, ScanPlan* out) {
     for (int hs = 1; hs <= std::min(H, 256); hs *= 2) hss.push_back(hs);
     if (std::find(hss.begin(), hss.end(), H) == hss.end() && H <= 256) hss.push_back(H);
   }
+  const int per_xcd = xcds > 1 ? cus / xcds : 0;
   double best = 1e30;
   bool found = false;
   for (int bb : bbs) {
@@ -248,16 +255,23 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, ScanPlan* out) {
       a.bb = bb; a.hs = hs; a.ps = ps; a.Kp = m.Kp; a.Hp = m.Hp;
       const int lds = scan_lds_bytes(a, m.esize);
       if (lds > kMaxLds) continue;
-      const int rows = mfma ? bb : bb;
-      double t = barrier_us(ns) + 0.3 + (double)bb * m.Kp * m.esize / 100e3 +
+      const int rows = bb;
+      const int groups = m.D * nbb;
+      const int gpx = per_xcd > 0 && d->placement != 1 ? cdiv(groups, xcds) : 0;
+      const bool xcd_aligned = gpx > 0 && gpx * ns <= per_xcd;
+      // a group whose members share one XCD exchanges ~15% faster (measured)
+      const double xf = xcd_aligned && ns > 1 ? 0.85 : 1.0;
+      // a one-member group keeps h in LDS: no exchange and no barrier
+      const double ex = ns == 1 && !lstmp ? 0.1 : (barrier_us(ns) + 0.3 + (double)bb * m.Kp * m.esize / 100e3) * xf;
+      double t = ex +
                  mm_us(mfma, m.esize, rows, m.gates * hs, mfma ? m.Kp : m.K) + bb * hs / 256.0 * 0.05;
       if (lstmp)
-        t += barrier_us(ns) + 0.3 + (double)bb * m.Hp * m.esize / 100e3 +
+        t += (barrier_us(ns) + 0.3 + (double)bb * m.Hp * m.esize / 100e3) * xf +
              mm_us(mfma, m.esize, rows, ps, mfma ? m.Hp : H);
-      t *= nbb > 0 ? 1.0 : 1.0;
+      if (d->placement == 2 && !xcd_aligned) t += 1e3;  // requested: aligned plans first
       if (t < best) {
         best = t;
-        *out = ScanPlan{bb, hs, ns, ps, nbb, lds};
+        *out = ScanPlan{bb, hs, ns, ps, nbb, xcd_aligned ? gpx : 0, lds};
         found = true;
       }
     }
@@ -266,11 +280,16 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, ScanPlan* out) {
 }
 
 struct RssmPlan {
-  int rows, ngroups, nw, h_per, u_per, lds;
+  int rows, ngroups, nw, h_per, gpx, lds;
 };
 
-int plan_rssm(const RnnDesc* d, int cus, RssmPlan* out) {
+// Grid of an RSSM plan: with XCD-aligned groups every XCD gets gpx whole
+// groups (the last XCDs may hold padding slots).
+int rssm_grid(const RssmPlan& p, int xcds) { return p.gpx > 0 ? xcds * p.gpx * p.nw : p.ngroups * p.nw; }
+
+int plan_rssm(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
   const int B = d->B, S = d->state_dim, A = d->action_dim, E = d->embed_dim, Hb = d->belief_dim;
+  const int per_xcd = xcds > 1 ? cus / xcds : 0;
   double best = 1e30;
   bool found = false;
   for (int rows = 1; rows <= rssm_max_rows(); ++rows) {
@@ -286,14 +305,20 @@ int plan_rssm(const RnnDesc* d, int cus, RssmPlan* out) {
       a.S = S; a.A = A; a.E = E; a.Hb = Hb; a.rows = rows; a.nw = nw; a.h_per = h_per;
       const int lds = rssm_lds_bytes(a);
       if (lds > kMaxLds) continue;
-      // GRU slice + partial of W_1 + (redundant) partial sums, W_2 and W_as
-      const double macs = (double)rows * (3.0 * h_per * (E + Hb) + (double)E * h_per + (double)E * nw +
-                                          2.0 * S * E + (double)E * (S + A));
+      // XCD-aligned groups only on request: for this kernel they measured no
+      // faster, and the planner would trade rows for them
+      const int gpx = per_xcd > 0 && d->placement == 2 ? cdiv(ngroups, xcds) : 0;
+      const bool xcd_aligned = gpx > 0 && gpx * nw <= per_xcd;
+      // GRU slice + partial of W_1 + (redundant) partial sums, W_2 and W_as;
+      // the 4x4 MFMA blocks cost the same for any 1..4 batch rows
+      const double macs = 4.0 * (3.0 * h_per * (E + Hb) + (double)E * h_per + (double)E * nw +
+                                 2.0 * S * E + (double)E * (S + A));
       const double bytes = (double)rows * (Hb + (double)nw * E) * 4.0;
-      const double t = barrier_us(nw) + 0.3 + bytes / 100e3 + macs / 32.0 / 2400.0;
+      double t = barrier_us(nw) + 0.3 + bytes / 100e3 + macs / 32.0 / 2400.0;
+      if (d->placement == 2 && !xcd_aligned) t += 1e3;  // requested: aligned plans first
       if (t < best) {
         best = t;
-        *out = RssmPlan{rows, ngroups, nw, h_per, 0, lds};
+        *out = RssmPlan{rows, ngroups, nw, h_per, xcd_aligned ? gpx : 0, lds};
         found = true;
       }
     }
@@ -336,7 +361,7 @@ int check_ptr(const void* p, size_t elem) {
 int check_opt(const void* p, size_t elem) { return (!p || aligned(p, elem)) ? RNN_OK : RNN_E_ALIGN; }
 
 int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws, size_t ws_bytes,
-                 hipStream_t st, int cus, Prof& prof) {
+                 hipStream_t st, int cus, int xcds, Prof& prof) {
   int rc;
   const void* req[] = {w->w_as, w->b_as, w->w_ih[0], w->w_hh[0], w->b_ih[0], w->b_hh[0], w->w_1, w->b_1,
                        w->w_2, w->b_2, io->x, io->noise, io->means, io->stds, io->states, io->beliefs};
@@ -348,12 +373,13 @@ int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* w
   if (ws_bytes < L.total) return RNN_E_WORKSPACE;
   if (!aligned(ws, 16)) return RNN_E_ALIGN;
   RssmPlan p;
-  if ((rc = plan_rssm(d, cus, &p)) != RNN_OK) return rc;
+  if ((rc = plan_rssm(d, cus, xcds, &p)) != RNN_OK) return rc;
 
   RssmArgs a{};
   a.B = d->B; a.T = d->T; a.S = d->state_dim; a.A = d->action_dim; a.E = d->embed_dim; a.Hb = d->belief_dim;
   a.scale_lb = d->scale_lb;
   a.rows = p.rows; a.ngroups = p.ngroups; a.nw = p.nw; a.h_per = p.h_per;
+  a.nxcd = xcds; a.gpx = p.gpx;
   a.w_as = (const float*)w->w_as; a.b_as = (const float*)w->b_as;
   a.w_ih = (const float*)w->w_ih[0]; a.w_hh = (const float*)w->w_hh[0];
   a.b_ih = (const float*)w->b_ih[0]; a.b_hh = (const float*)w->b_hh[0];
@@ -375,7 +401,7 @@ int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* w
 }
 
 int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws, size_t ws_bytes,
-                hipStream_t st, int cus, Prof& prof) {
+                hipStream_t st, int cus, int xcds, Prof& prof) {
   int rc;
   long long n_tok = 0;
   int t_max = 0;
@@ -400,7 +426,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   if (!ws || ws_bytes < L.total) return RNN_E_WORKSPACE;
   if (!aligned(ws, 16)) return RNN_E_ALIGN;
   ScanPlan p;
-  if ((rc = plan_scan(d, m, cus, &p)) != RNN_OK) return rc;
+  if ((rc = plan_scan(d, m, cus, xcds, &p)) != RNN_OK) return rc;
 
   // ---- enqueue ----
   if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
@@ -456,6 +482,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     a.packed = d->layout == RNN_LAYOUT_PACKED;
     a.has_bias = d->has_bias;
     a.bb = p.bb; a.hs = p.hs; a.ns = p.ns; a.ps = p.ps; a.nbb = p.nbb; a.Kp = m.Kp; a.Hp = m.Hp;
+    a.nxcd = xcds; a.gpx = p.gpx;
     for (int di = 0; di < m.D; ++di) {
       const int i = l * m.D + di;
       a.w_hh[di] = w->w_hh[i];
@@ -516,17 +543,17 @@ int rnn_workspace_bytes(const RnnDesc* desc, const int32_t* lengths_host, size_t
   return RNN_OK;
 }
 
-int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int* info, int n_info) {
+int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int xcds, int* info, int n_info) {
   int rc = validate_desc(desc);
   if (rc != RNN_OK) return rc;
-  if (!info || n_info < 8) return RNN_E_NULL;
-  if (cus < 1) return RNN_E_SHAPE;
+  if (!info || n_info < 9) return RNN_E_NULL;
+  if (cus < 1 || xcds < 1 || cus % xcds != 0) return RNN_E_SHAPE;
   for (int i = 0; i < n_info; ++i) info[i] = 0;
   if (desc->mode == RNN_MODE_RSSM_PRIOR) {
     RssmPlan p;
-    if ((rc = plan_rssm(desc, cus, &p)) != RNN_OK) return rc;
-    info[0] = 3; info[1] = p.ngroups * p.nw; info[2] = p.lds; info[3] = p.rows; info[4] = p.h_per;
-    info[5] = p.nw; info[6] = 0; info[7] = p.ngroups;
+    if ((rc = plan_rssm(desc, cus, xcds, &p)) != RNN_OK) return rc;
+    info[0] = 3; info[1] = rssm_grid(p, xcds); info[2] = p.lds; info[3] = p.rows; info[4] = p.h_per;
+    info[5] = p.nw; info[6] = 0; info[7] = p.ngroups; info[8] = p.gpx;
     return RNN_OK;
   }
   long long n_tok = 0;
@@ -534,9 +561,9 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
   if ((rc = validate_lengths(desc, lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
   const Dims m = dims_of(desc, n_tok);
   ScanPlan p;
-  if ((rc = plan_scan(desc, m, cus, &p)) != RNN_OK) return rc;
-  info[0] = 2; info[1] = m.D * p.nbb * p.ns; info[2] = p.lds; info[3] = p.bb; info[4] = p.hs;
-  info[5] = p.ns; info[6] = p.ps; info[7] = p.nbb;
+  if ((rc = plan_scan(desc, m, cus, xcds, &p)) != RNN_OK) return rc;
+  info[0] = 2; info[1] = scan_grid(p, m.D, xcds); info[2] = p.lds; info[3] = p.bb; info[4] = p.hs;
+  info[5] = p.ns; info[6] = p.ps; info[7] = p.nbb; info[8] = p.gpx;
   return RNN_OK;
 }
 
@@ -567,8 +594,8 @@ int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const R
   prof.kinds = kinds;
   prof.st = st;
   rc = desc->mode == RNN_MODE_RSSM_PRIOR
-           ? forward_rssm(desc, weights, io, (char*)workspace, ws_bytes, st, info.cus, prof)
-           : forward_rnn(desc, weights, io, (char*)workspace, ws_bytes, st, info.cus, prof);
+           ? forward_rssm(desc, weights, io, (char*)workspace, ws_bytes, st, info.cus, info.xcds, prof)
+           : forward_rnn(desc, weights, io, (char*)workspace, ws_bytes, st, info.cus, info.xcds, prof);
   if (n_kernels) *n_kernels = prof.n;
   return rc;
 }

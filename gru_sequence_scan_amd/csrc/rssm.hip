@@ -198,8 +198,20 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   const RssmLds L = rssm_lds(a);
   const int tid = threadIdx.x;
-  const int w = blockIdx.x % a.nw;
-  const int g = blockIdx.x / a.nw;
+  // Group and member of this workgroup. Workgroups are dealt to the XCDs
+  // round-robin by id, so with gpx > 0 the ids xcd, xcd + nxcd, ... form the
+  // groups of one XCD: the members' coherent exchange then stays between
+  // the CUs of one chiplet (placement only; correctness never depends on it).
+  int g, w;
+  if (a.gpx > 0) {
+    const int xcd = blockIdx.x % a.nxcd, slot = blockIdx.x / a.nxcd;
+    g = xcd * a.gpx + slot / a.nw;
+    w = slot % a.nw;
+  } else {
+    g = blockIdx.x / a.nw;
+    w = blockIdx.x % a.nw;
+  }
+  if (g >= a.ngroups) return;  // padding slots of the XCD-aligned layout
   const int b0 = g * a.rows;
   const int nrows = min(a.rows, a.B - b0);
   const int S = a.S, A = a.A, E = a.E, Hb = a.Hb, SA = a.S + a.A;
@@ -419,7 +431,8 @@ hipError_t launch_rssm(const RssmArgs& a, hipStream_t stream) {
   const int lds = rssm_lds(a).total;
   hipError_t e = hipFuncSetAttribute((const void*)rssm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rssm_kernel, dim3(a.ngroups * a.nw), dim3(kThreads), lds, stream, a);
+  const int grid = a.gpx > 0 ? a.nxcd * a.gpx * a.nw : a.ngroups * a.nw;
+  hipLaunchKernelGGL(rssm_kernel, dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -234,9 +234,20 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   const int tid = threadIdx.x;
   const int gates = a.mode == kGRU ? 3 : 4;
 
-  // Workgroup -> (direction, batch block, hidden slice).
-  const int s = blockIdx.x % a.ns;
-  const int grp = blockIdx.x / a.ns;
+  // Workgroup -> (direction, batch block, hidden slice). Workgroups are dealt
+  // to the XCDs round-robin by id, so with gpx > 0 the ids xcd, xcd + nxcd,
+  // ... form the groups of one XCD and a group's exchange stays between the
+  // CUs of one chiplet (placement only; correctness never depends on it).
+  int s, grp;
+  if (a.gpx > 0) {
+    const int xcd = blockIdx.x % a.nxcd, slot = blockIdx.x / a.nxcd;
+    grp = xcd * a.gpx + slot / a.ns;
+    s = slot % a.ns;
+  } else {
+    s = blockIdx.x % a.ns;
+    grp = blockIdx.x / a.ns;
+  }
+  if (grp >= a.D * a.nbb) return;  // padding slots of the XCD-aligned layout
   const int nb = grp % a.nbb;
   const int d = grp / a.nbb;
   const int b0 = nb * a.bb;
@@ -281,6 +292,22 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     }, lds, L.wr, L.wr_ld);
   }
 
+  // A group of one workgroup owns every hidden unit of its rows: h_t then
+  // never leaves the workgroup and is written straight into the LDS operand
+  // tile of the next step (no exchange buffer, no group barrier).
+  const bool solo = a.ns == 1 && a.mode != kLSTMP;
+  const bool use_mfma = (a.bb % 16) == 0;
+  const int tile_rows = use_mfma ? rup(a.bb, 16) : a.bb;
+  DT* tile = reinterpret_cast<DT*>(lds + L.as);
+  if (solo) {
+    const DT* h0s = reinterpret_cast<const DT*>(a.h0[d]);
+    for (int e = tid; e < tile_rows * a.Kp; e += kThreads) {
+      const int r = e / a.Kp, k = e - r * a.Kp;
+      const int b = b0 + r;
+      tile[r * L.as_ld + k] = (h0s && b < a.B && k < a.K) ? h0s[(size_t)b * a.K + k] : (DT)0.0f;
+    }
+  }
+
   // --- owned state: gate elements e = tid + i * 256 -> (row r, unit u) -------
   const int n_el = a.bb * a.hs;
   float hreg[kMaxEpt], creg[kMaxEpt];
@@ -305,7 +332,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
       if (a.mode != kLSTMP && h0) hreg[i] = to_f32<DT>(h0[(size_t)b * a.K + j]);
       if (a.mode != kGRU && c0) creg[i] = to_f32<DT>(c0[(size_t)b * a.H + j]);
       if (a.mode == kGRU && a.has_bias) bhn[i] = to_f32<DT>(bhh[2 * a.H + j]);
-      if (a.mode != kLSTMP) {
+      if (a.mode != kLSTMP && !solo) {
         coh_store_elem<DT>(hx_rs, hx_el(0, b, j), hreg[i]);
         coh_store_elem<DT>(hx_rs, hx_el(1, b, j), hreg[i]);
       }
@@ -323,7 +350,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
       }
     }
   }
-  if (s == 0) {  // zero the padding columns of this block's exchange rows
+  if (s == 0 && !solo) {  // zero the padding columns of this block's exchange rows
     for (int e = tid; e < a.bb * (a.Kp - a.K); e += kThreads) {
       const int r = e / (a.Kp - a.K), k = a.K + (e - r * (a.Kp - a.K));
       if (b0 + r < a.B) {
@@ -345,7 +372,6 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   for (int r = 0; r < a.bb && b0 + r < a.B; ++r) maxlen = max(maxlen, len_of(b0 + r));
   maxlen = __builtin_amdgcn_readfirstlane(maxlen);
 
-  const bool use_mfma = (a.bb % 16) == 0;
   float* acc = reinterpret_cast<float*>(lds + L.acc);
   const int mtiles = rup(a.bb, 16) / 16;
   DT* yout = reinterpret_cast<DT*>(a.y);
@@ -377,9 +403,12 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
 
   // h0 is published: arrive, prefetch the first step's Gx, then wait.
   unsigned nbar = 1;
-  group_arrive(counter);
+  if (!solo) group_arrive(counter);
   if (nsteps > 0) prefetch(t_of(0));
-  if (!group_wait(counter, nbar * a.ns, a.status, abort_flag)) return;
+  if (solo)
+    __syncthreads();
+  else if (!group_wait(counter, nbar * a.ns, a.status, abort_flag))
+    return;
   int par = 0;  // exchange buffer holding h_{t-1}
 
   for (int k = 0; k < nsteps; ++k) {
@@ -387,9 +416,10 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     const int rowbase = a.packed ? a.offsets[t] : t * a.B;
 
     // h_{t-1} of the block -> LDS, then the hidden-hidden product.
-    load_tile_coherent<DT>(hx_rs, hx_el(par, b0, 0), a.Kp, b0, a.B, use_mfma ? rup(a.bb, 16) : a.bb,
-                           a.Kp, lds, L.as, L.as_ld);
-    __syncthreads();
+    if (!solo) {
+      load_tile_coherent<DT>(hx_rs, hx_el(par, b0, 0), a.Kp, b0, a.B, tile_rows, a.Kp, lds, L.as, L.as_ld);
+      __syncthreads();
+    }
     if (use_mfma)
       mm_mfma<DT>(lds, L.as, L.as_ld, L.ws, L.ws_ld, acc, L.acc_ld, mtiles, L.ncw / 16, a.Kp);
     else
@@ -411,7 +441,10 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const float ng = ftanh(gxv[i][2] + rg * (ar[2 * a.hs + u] + bhn[i]));
         const float h = (1.f - zg) * ng + zg * hreg[i];
         hreg[i] = h;
-        coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), h);
+        if (solo)
+          tile[r * L.as_ld + j] = from_f32<DT>(h);
+        else
+          coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), h);
       } else {
         const float ig = fsigmoid(gxv[i][0] + ar[u]);
         const float fg = fsigmoid(gxv[i][1] + ar[a.hs + u]);
@@ -421,14 +454,16 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const float m = og * ftanh(c);
         creg[i] = c;
         hreg[i] = m;
-        if (a.mode == kLSTM)
+        if (solo)
+          tile[r * L.as_ld + j] = from_f32<DT>(m);
+        else if (a.mode == kLSTM)
           coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), m);
         else
           coh_store_elem<DT>(mx_rs, mx_el(b, j), m);
       }
     }
     ++nbar;
-    group_arrive(counter);
+    if (!solo) group_arrive(counter);
     // While the other members arrive: outputs of this step, Gx of the next.
 #pragma unroll
     for (int i = 0; i < kMaxEpt; ++i) {
@@ -442,7 +477,10 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
       if (last && cn && a.mode != kGRU) cn[(size_t)b * a.H + j] = from_f32<DT>(creg[i]);
     }
     if (k + 1 < nsteps) prefetch(t_of(k + 1));
-    if (!group_wait(counter, nbar * a.ns, a.status, abort_flag)) return;
+    if (solo)
+      __syncthreads();
+    else if (!group_wait(counter, nbar * a.ns, a.status, abort_flag))
+      return;
 
     if (a.mode == kLSTMP) {
       // hidden-projection dense: h_t = m_t W_hr^T for this slice of P
@@ -489,7 +527,7 @@ int scan_lds_bytes(const ScanArgs& a, int esize) { return scan_lds(a, esize).tot
 hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream) {
   const int esize = dtype_bf16 ? 2 : 4;
   const int lds = scan_lds(a, esize).total;
-  const dim3 grid(a.D * a.nbb * a.ns), block(kThreads);
+  const dim3 grid(a.gpx > 0 ? a.nxcd * a.gpx * a.ns : a.D * a.nbb * a.ns), block(kThreads);
   if (dtype_bf16) {
     hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<bf16>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);

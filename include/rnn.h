@@ -129,7 +129,11 @@ typedef struct RnnDesc {
    * work is tiled, never which arithmetic is done per output element. */
   int32_t tile_batch;    /* batch rows per workgroup in the scan               */
   int32_t tile_hidden;   /* hidden units per workgroup in the scan             */
-  int32_t reserved[6];   /* must be zero                                       */
+  int32_t placement;     /* 0: automatic (scan: XCD-aligned groups when they
+                            fit; RSSM: consecutive ids); 1: consecutive
+                            workgroup ids form a group; 2: every group on one
+                            XCD when it fits                                  */
+  int32_t reserved[5];   /* must be zero                                       */
 } RnnDesc;
 
 /* Weights, PyTorch shapes and meaning. Index i = layer * D + direction
@@ -226,12 +230,14 @@ int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const R
 int rnn_read_status(const void* workspace, void* stream, int* device_status);
 
 /* Host-only: the launch shape rnn_forward would use for this problem on a
- * device with `cus` compute units. info[0..7] = {kernel (2 scan, 3 RSSM),
- * workgroups, LDS bytes per workgroup, batch rows per workgroup, hidden
- * units per workgroup, workgroups per group, projection outputs per
- * workgroup (LSTMP), number of groups per direction}; n_info >= 8. For
+ * device with `cus` compute units in `xcds` chiplets (XCDs; workgroups are
+ * dealt to them round-robin). info[0..8] = {kernel (2 scan, 3 RSSM),
+ * workgroups launched, LDS bytes per workgroup, batch rows per workgroup,
+ * hidden units per workgroup, workgroups per group, projection outputs per
+ * workgroup (LSTMP), number of groups (per direction for the scan), groups
+ * per XCD when every group sits on one XCD (else 0)}; n_info >= 9. For
  * inspection and tests; touches no device. */
-int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int* info, int n_info);
+int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int xcds, int* info, int n_info);
 
 /* RNN_OK when the current device is a gfx950 GPU; RNN_E_DEVICE otherwise. */
 int rnn_device_check(void);

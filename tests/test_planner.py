@@ -1,0 +1,106 @@
+"""Launch planning on the CPU (rnn_plan_info): every workload gets a plan
+whose workgroups are all co-resident (the per-step group barriers need
+that), whose LDS fits a CU, whose slices cover the problem, and whose
+XCD-aligned layout keeps each group on one XCD."""
+
+import math
+
+import pytest
+
+import synth
+
+gss = pytest.importorskip("gru_sequence_scan_amd")
+
+LDS_MAX = 160 * 1024
+CODE = {v: k for k, v in gss.STATUS.items()}
+
+
+def desc_for(name, **hints):
+    s = synth.spec(name)
+    d = gss.RnnDesc()
+    if s.mode == "rssm":
+        d.mode, d.layout, d.T, d.B, d.num_layers, d.has_bias = 3, 2, s.T, s.B, 1, 1
+        d.state_dim, d.action_dim, d.embed_dim, d.belief_dim, d.scale_lb = (
+            s.state_dim, s.action_dim, s.embed_dim, s.belief_dim, 0.1)
+    else:
+        d.mode = gss.MODES[s.mode]
+        d.dtype = 1 if s.dtype == "bf16" else 0
+        d.layout = 1 if s.layout == "packed" else 0
+        d.T, d.B = s.T, s.B
+        d.input_size, d.hidden_size, d.proj_size = s.input_size, s.hidden_size, s.proj_size
+        d.num_layers, d.bidirectional, d.has_bias = s.num_layers, int(s.bidirectional), 1
+    for k, v in hints.items():
+        setattr(d, k, v)
+    lengths = synth.make_inputs(name)["lengths"] if s.varlen else None
+    return s, d, lengths
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+@pytest.mark.parametrize("cus,xcds", [(256, 8), (256, 1), (32, 1), (80, 1)])
+def test_plan_is_coresident_and_covers(name, cus, xcds):
+    s, d, lengths = desc_for(name)
+    try:
+        p = gss.rnn_plan_info(d, lengths, cus=cus, xcds=xcds)
+    except gss.RnnError as e:
+        # a device too small for the persistent layout must say so, never
+        # return a plan that would deadlock
+        assert e.status == CODE["RNN_E_PLAN"]
+        assert cus < 256
+        return
+    assert p["workgroups"] <= cus
+    assert 0 < p["lds_bytes"] <= LDS_MAX
+    if p["kernel"] == 3:
+        assert p["groups"] == math.ceil(s.B / p["rows"])
+        assert p["hidden_per_wg"] * p["members"] >= s.belief_dim
+        assert p["hidden_per_wg"] * (p["members"] - 1) < s.belief_dim
+        assert 1 <= p["rows"] <= 4
+    else:
+        D = 2 if s.bidirectional else 1
+        assert p["groups"] * p["rows"] >= s.B
+        assert p["hidden_per_wg"] * p["members"] >= s.hidden_size
+        assert p["rows"] * p["hidden_per_wg"] <= 1024
+        if s.mode == "lstmp":
+            assert p["proj_per_wg"] * p["members"] >= s.proj_size
+        groups = D * p["groups"]
+        if p["groups_per_xcd"]:
+            assert p["groups_per_xcd"] * xcds >= groups
+            assert p["groups_per_xcd"] * p["members"] <= cus // xcds
+            assert p["workgroups"] == xcds * p["groups_per_xcd"] * p["members"]
+        else:
+            assert p["workgroups"] == groups * p["members"]
+
+
+@pytest.mark.parametrize("name", ["gru_t256_b256", "lstm_t80_b1", "rssm_b50_t50"])
+def test_placement_hint(name):
+    _, d, lengths = desc_for(name, placement=1)
+    assert gss.rnn_plan_info(d, lengths)["groups_per_xcd"] == 0
+    _, d, lengths = desc_for(name, placement=2)
+    p = gss.rnn_plan_info(d, lengths)
+    assert p["groups_per_xcd"] > 0
+    assert p["groups_per_xcd"] * p["members"] <= 256 // 8
+
+
+def test_single_xcd_device_never_aligns():
+    _, d, lengths = desc_for("gru_t256_b256")
+    assert gss.rnn_plan_info(d, lengths, cus=256, xcds=1)["groups_per_xcd"] == 0
+
+
+def test_hints_are_honoured():
+    _, d, lengths = desc_for("rssm_b50_t50", tile_batch=3, tile_hidden=14)
+    p = gss.rnn_plan_info(d, lengths)
+    assert (p["rows"], p["hidden_per_wg"], p["members"]) == (3, 14, 15)
+    _, d, lengths = desc_for("gru_t256_b256", tile_batch=16, tile_hidden=32)
+    p = gss.rnn_plan_info(d, lengths)
+    assert (p["rows"], p["hidden_per_wg"]) == (16, 32)
+
+
+def test_invalid_arguments():
+    _, d, lengths = desc_for("gru_t256_b256")
+    for cus, xcds in [(0, 1), (256, 0), (250, 8)]:
+        with pytest.raises(gss.RnnError) as e:
+            gss.rnn_plan_info(d, lengths, cus=cus, xcds=xcds)
+        assert e.value.status == CODE["RNN_E_SHAPE"]
+    _, d, lengths = desc_for("gru_t256_b256", placement=3)
+    with pytest.raises(gss.RnnError) as e:
+        gss.rnn_plan_info(d, lengths)
+    assert e.value.status == CODE["RNN_E_SHAPE"]
