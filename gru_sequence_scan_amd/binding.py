@@ -42,7 +42,7 @@ class RnnDesc(ctypes.Structure):
         ("action_dim", ctypes.c_int32), ("embed_dim", ctypes.c_int32),
         ("belief_dim", ctypes.c_int32), ("scale_lb", ctypes.c_float),
         ("tile_batch", ctypes.c_int32), ("tile_hidden", ctypes.c_int32),
-        ("placement", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5),
+        ("placement", ctypes.c_int32), ("weights", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4),
     ]
 
 
@@ -146,7 +146,7 @@ def rnn_forward_raw(desc, weights, io, workspace_ptr, ws_bytes, stream_ptr):
 
 
 PLAN_FIELDS = ("kernel", "workgroups", "lds_bytes", "rows", "hidden_per_wg", "members", "proj_per_wg",
-               "groups", "groups_per_xcd")
+               "groups", "groups_per_xcd", "wreg", "reg_tiles", "reg_ksplit", "reg_chunks")
 
 
 def rnn_plan_info(desc, lengths=None, cus=256, xcds=8):
@@ -229,7 +229,7 @@ def _call(desc, w, io, lengths, device, keep):
 
 def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padded",
                 num_layers=1, bidirectional=False, proj_size=0, hidden_size=None, y_out=None,
-                tile_batch=0, tile_hidden=0, placement=0, return_workspace=False):
+                tile_batch=0, tile_hidden=0, placement=0, weights=0, return_workspace=False):
     """Forward of an LSTM / GRU / LSTMP stack on the current HIP stream.
 
     x: padded [T, B, F] or packed [N_tok, F] (float32 or bfloat16, on a GPU).
@@ -303,6 +303,7 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     desc.input_size, desc.hidden_size, desc.proj_size = F, H, proj_size if mode == "lstmp" else 0
     desc.num_layers, desc.bidirectional, desc.has_bias = num_layers, int(bidirectional), int(has_bias)
     desc.tile_batch, desc.tile_hidden, desc.placement = tile_batch, tile_hidden, placement
+    desc.weights = weights
     io = RnnIO()
     io.x = _ptr(x)
     keep_len, io.lengths_host = _len_ptr(lengths)

@@ -41,6 +41,12 @@ struct ScanArgs {
   int gpx;           // > 0: groups per XCD, members of a group share one XCD;
                      // 0: consecutive workgroup ids form a group
   int Kp, Hp;        // padded widths of the exchange rows (multiples of 32)
+  // Where each workgroup keeps its W_hh slice: wreg = 0 in LDS; wreg = 1 in
+  // registers (kScanRegChunks 16-byte chunks per lane). MFMA register path
+  // (rnt = 1, 2, 4): each wave holds rnt 16-column tiles over 1/rks of K,
+  // rcpt chunks per tile. VALU register path (rnt = 0): thread t holds
+  // output column t % (256 / rks) over K slice t / (256 / rks), rcpt chunks.
+  int wreg, rnt, rks, rcpt;
   // per direction tensors (already offset to this layer)
   const void* w_hh[2];
   const void* w_hr[2];
@@ -60,6 +66,7 @@ struct ScanArgs {
   int* status;
 };
 hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
+constexpr int kScanRegChunks = 32;
 
 // Kernel 3: persistent RSSM-prior unroll.
 struct RssmArgs {

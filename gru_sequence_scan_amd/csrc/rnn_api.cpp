@@ -71,6 +71,7 @@ int validate_desc(const RnnDesc* d) {
   for (int r : d->reserved)
     if (r != 0) return RNN_E_SHAPE;
   if (d->placement < 0 || d->placement > 2) return RNN_E_SHAPE;
+  if (d->weights < 0 || d->weights > 2) return RNN_E_SHAPE;
   if (d->dtype != RNN_DTYPE_F32 && d->dtype != RNN_DTYPE_BF16) return RNN_E_UNSUPPORTED;
   if (d->T < 1 || d->B < 1) return RNN_E_SHAPE;
   if (d->tile_batch < 0 || d->tile_hidden < 0) return RNN_E_SHAPE;
@@ -199,6 +200,8 @@ WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
 double barrier_us(int members) { return 0.65 + 0.009 * members; }
 
 double mm_us(bool mfma, int esize, int rows, int cols, int kp) {
+  // (LDS-resident weights; the VALU form is bound by LDS latency, measured
+  // at ~1 us plus ~8 MAC/clk)
   if (mfma) {
     const double tiles = (double)(rows / 16) * cdiv(cols, 16);
     double mf_cycles, lds_bytes;
@@ -209,18 +212,56 @@ double mm_us(bool mfma, int esize, int rows, int cols, int kp) {
       mf_cycles = tiles * (kp / 4) * 32.0 / 4.0;
       lds_bytes = tiles * (kp / 16) * 2048.0;
     }
-    return std::max(mf_cycles, lds_bytes / 128.0) / 2400.0;
+    // measured about twice this bound (LDS latency between dependent steps)
+    return 2.0 * std::max(mf_cycles, lds_bytes / 128.0) / 2400.0;
   }
-  return (double)rows * cols * kp / 32.0 / 2400.0;
+  return 1.0 + (double)rows * cols * kp / 8.0 / 2400.0;
 }
 
 struct ScanPlan {
   int bb, hs, ns, ps, nbb, gpx, lds;
+  int wreg, rnt, rks, rcpt;  // register-resident W_hh layout (ScanArgs)
 };
 
 int scan_grid(const ScanPlan& p, int D, int xcds) { return p.gpx > 0 ? xcds * p.gpx * p.ns : D * p.nbb * p.ns; }
 
-int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, ScanPlan* out) {
+// Register layout of a slice of ncw W_hh rows (padded to 16) for a batch
+// block of bb rows, or false when none fits kScanRegChunks 16-byte chunks
+// per lane. MFMA (bb a multiple of 16): rnt column tiles per wave, rks waves
+// per tile set splitting K, rcpt chunks per tile (a multiple of 4). VALU:
+// one output column per thread over one of rks K slices of rcpt chunks.
+bool reg_layout(int bb, int ncw, int Kp, int esize, int* rnt, int* rks, int* rcpt) {
+  if (bb % 16 == 0) {
+    // the four waves cover 4 * nt / ks column tiles (>= the slice's, the
+    // extra ones are zero rows); fewest padded tiles first, then least K split
+    const int ct = ncw / 16, nch = Kp / (esize == 2 ? 32 : 16);
+    int best_cols = 1 << 30;
+    bool ok = false;
+    for (int ks = 1; ks <= 4; ks *= 2) {
+      for (int nt = 1; nt <= 4; nt *= 2) {
+        const int cover = 4 * nt / ks;
+        if (4 * nt % ks != 0 || cover < ct) continue;
+        if (nch % ks != 0) continue;
+        const int cpt = nch / ks;
+        if (cpt % 4 != 0 || cpt * nt > kScanRegChunks) continue;
+        if (cover < best_cols) {
+          best_cols = cover;
+          *rnt = nt; *rks = ks; *rcpt = cpt;
+          ok = true;
+        }
+      }
+    }
+    return ok;
+  }
+  if (ncw > 256) return false;
+  const int c = ncw <= 64 ? 64 : (ncw <= 128 ? 128 : 256);
+  const int q = 256 / c, nch = Kp * esize / 16;
+  if (nch % q != 0 || nch / q > kScanRegChunks) return false;
+  *rnt = 0; *rks = q; *rcpt = nch / q;
+  return true;
+}
+
+int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wreg, ScanPlan* out) {
   const int B = d->B, H = d->hidden_size, P = d->proj_size;
   const bool lstmp = d->mode == RNN_MODE_LSTMP;
   std::vector<int> bbs;
@@ -250,29 +291,45 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, ScanPlan* out)
       const int nbb = cdiv(B, bb);
       if ((long long)m.D * nbb * ns > cus) continue;
       const int ps = lstmp ? cdiv(P, ns) : 0;
-      ScanArgs a{};
-      a.mode = d->mode == RNN_MODE_GRU ? kGRU : (lstmp ? kLSTMP : kLSTM);
-      a.bb = bb; a.hs = hs; a.ps = ps; a.Kp = m.Kp; a.Hp = m.Hp;
-      const int lds = scan_lds_bytes(a, m.esize);
-      if (lds > kMaxLds) continue;
-      const int rows = bb;
-      const int groups = m.D * nbb;
-      const int gpx = per_xcd > 0 && d->placement != 1 ? cdiv(groups, xcds) : 0;
-      const bool xcd_aligned = gpx > 0 && gpx * ns <= per_xcd;
-      // a group whose members share one XCD exchanges ~15% faster (measured)
-      const double xf = xcd_aligned && ns > 1 ? 0.85 : 1.0;
-      // a one-member group keeps h in LDS: no exchange and no barrier
-      const double ex = ns == 1 && !lstmp ? 0.1 : (barrier_us(ns) + 0.3 + (double)bb * m.Kp * m.esize / 100e3) * xf;
-      double t = ex +
-                 mm_us(mfma, m.esize, rows, m.gates * hs, mfma ? m.Kp : m.K) + bb * hs / 256.0 * 0.05;
-      if (lstmp)
-        t += (barrier_us(ns) + 0.3 + (double)bb * m.Hp * m.esize / 100e3) * xf +
-             mm_us(mfma, m.esize, rows, ps, mfma ? m.Hp : H);
-      if (d->placement == 2 && !xcd_aligned) t += 1e3;  // requested: aligned plans first
-      if (t < best) {
-        best = t;
-        *out = ScanPlan{bb, hs, ns, ps, nbb, xcd_aligned ? gpx : 0, lds};
-        found = true;
+      const int ncw = rup(m.gates * hs, 16);
+      for (int wreg = allow_wreg && d->weights != 1 ? 1 : 0; wreg >= 0; --wreg) {
+        ScanArgs a{};
+        a.mode = d->mode == RNN_MODE_GRU ? kGRU : (lstmp ? kLSTMP : kLSTM);
+        a.bb = bb; a.hs = hs; a.ps = ps; a.Kp = m.Kp; a.Hp = m.Hp;
+        a.wreg = wreg;
+        if (wreg && !reg_layout(bb, ncw, m.Kp, m.esize, &a.rnt, &a.rks, &a.rcpt)) continue;
+        const int lds = scan_lds_bytes(a, m.esize);
+        if (lds > kMaxLds) continue;
+        const int groups = m.D * nbb;
+        const int gpx = per_xcd > 0 && d->placement != 1 ? cdiv(groups, xcds) : 0;
+        const bool xcd_aligned = gpx > 0 && gpx * ns <= per_xcd;
+        // a group whose members share one XCD exchanges ~15% faster (measured)
+        const double xf = xcd_aligned && ns > 1 ? 0.85 : 1.0;
+        // a one-member group keeps h in LDS: no exchange and no barrier
+        const double ex =
+            ns == 1 && !lstmp ? 0.1 : (barrier_us(ns) + 0.3 + (double)bb * m.Kp * m.esize / 100e3) * xf;
+        double mm;
+        if (wreg && mfma) {
+          // per wave: rtiles * rcpt chunks, rnt MFMA tiles each; the h tile
+          // is the only LDS operand
+          const double rt = bb / 16, per_chunk = m.esize == 2 ? 16.0 : 32.0;
+          mm = std::max(rt * a.rcpt * a.rnt * per_chunk, rt * a.rcpt * 32.0) / 2400.0 + (a.rks > 1 ? 0.2 : 0.0);
+        } else if (wreg) {
+          mm = (double)bb * a.rcpt * 10.0 / 2400.0 + 0.1 + (a.rks > 1 ? 0.2 : 0.0);
+        } else {
+          mm = mm_us(mfma, m.esize, bb, m.gates * hs, mfma ? m.Kp : m.K);
+        }
+        double t = ex + mm + bb * hs / 256.0 * 0.05;
+        if (lstmp)
+          t += (barrier_us(ns) + 0.3 + (double)bb * m.Hp * m.esize / 100e3) * xf +
+               mm_us(mfma, m.esize, bb, ps, mfma ? m.Hp : H);
+        if (d->placement == 2 && !xcd_aligned) t += 1e3;  // requested: aligned plans first
+        if (d->weights == 2 && !wreg) t += 1e3;            // requested: registers first
+        if (t < best) {
+          best = t;
+          *out = ScanPlan{bb, hs, ns, ps, nbb, xcd_aligned ? gpx : 0, lds, wreg, a.rnt, a.rks, a.rcpt};
+          found = true;
+        }
       }
     }
   }
@@ -425,8 +482,11 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   const WsLayout L = layout_of(d, n_tok, has_len);
   if (!ws || ws_bytes < L.total) return RNN_E_WORKSPACE;
   if (!aligned(ws, 16)) return RNN_E_ALIGN;
+  // W_hh slices go to registers only as whole aligned 16-byte chunks
+  bool wreg_ok = (size_t)m.K * es % 16 == 0;
+  for (int i = 0; i < LD; ++i) wreg_ok = wreg_ok && aligned(w->w_hh[i], 16);
   ScanPlan p;
-  if ((rc = plan_scan(d, m, cus, xcds, &p)) != RNN_OK) return rc;
+  if ((rc = plan_scan(d, m, cus, xcds, wreg_ok, &p)) != RNN_OK) return rc;
 
   // ---- enqueue ----
   if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
@@ -483,6 +543,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     a.has_bias = d->has_bias;
     a.bb = p.bb; a.hs = p.hs; a.ns = p.ns; a.ps = p.ps; a.nbb = p.nbb; a.Kp = m.Kp; a.Hp = m.Hp;
     a.nxcd = xcds; a.gpx = p.gpx;
+    a.wreg = p.wreg; a.rnt = p.rnt; a.rks = p.rks; a.rcpt = p.rcpt;
     for (int di = 0; di < m.D; ++di) {
       const int i = l * m.D + di;
       a.w_hh[di] = w->w_hh[i];
@@ -561,9 +622,12 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
   if ((rc = validate_lengths(desc, lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
   const Dims m = dims_of(desc, n_tok);
   ScanPlan p;
-  if ((rc = plan_scan(desc, m, cus, xcds, &p)) != RNN_OK) return rc;
+  if ((rc = plan_scan(desc, m, cus, xcds, (size_t)m.K * m.esize % 16 == 0, &p)) != RNN_OK) return rc;
   info[0] = 2; info[1] = scan_grid(p, m.D, xcds); info[2] = p.lds; info[3] = p.bb; info[4] = p.hs;
   info[5] = p.ns; info[6] = p.ps; info[7] = p.nbb; info[8] = p.gpx;
+  if (n_info >= 13) {
+    info[9] = p.wreg; info[10] = p.rnt; info[11] = p.rks; info[12] = p.rcpt;
+  }
   return RNN_OK;
 }
 

@@ -31,7 +31,7 @@ constexpr int kThreads = 256;
 constexpr int kMaxEpt = 4;  // owned gate elements per thread: bb * hs <= 1024
 
 struct ScanLds {
-  int ws, wr, as, acc, lens, flag, total;  // byte offsets
+  int ws, wr, as, acc, red, lens, flag, total;  // byte offsets
   int ws_ld, wr_ld, as_ld, acc_ld;    // row strides in elements
   int ncw, ncp;                       // W rows (padded to 16), acc columns
 };
@@ -44,6 +44,9 @@ __host__ __device__ inline ScanLds scan_lds(const ScanArgs& a, int esize) {
   const int pad = 16 / esize;
   const int nc = gates * a.hs;
   L.ncw = rup(nc, 16);
+  // register MFMA layouts cover 4 * rnt / rks column tiles (the last ones
+  // may be zero padding), all of which the product writes
+  if (a.wreg && a.rnt > 0 && 64 * a.rnt / a.rks > L.ncw) L.ncw = 64 * a.rnt / a.rks;
   const int ps16 = a.mode == kLSTMP ? rup(a.ps, 16) : 0;
   L.ncp = L.ncw > ps16 ? L.ncw : ps16;
   L.ws_ld = a.Kp + pad;
@@ -53,10 +56,12 @@ __host__ __device__ inline ScanLds scan_lds(const ScanArgs& a, int esize) {
   L.acc_ld = L.ncp + 1;
   const int bb16 = rup(a.bb, 16);
   int off = 0;
-  L.ws = off; off += rup(L.ncw * L.ws_ld * esize, 16);
+  L.ws = off; off += a.wreg ? 0 : rup(L.ncw * L.ws_ld * esize, 16);
   L.wr = off; off += a.mode == kLSTMP ? rup(ps16 * L.wr_ld * esize, 16) : 0;
   L.as = off; off += rup(bb16 * L.as_ld * esize, 16);
   L.acc = off; off += rup(bb16 * L.acc_ld * 4, 16);
+  // K-split partial sums of the register-weight product
+  L.red = off; off += (a.wreg && a.rks > 1) ? rup(a.rks * bb16 * L.acc_ld * 4, 16) : 0;
   L.lens = off; off += rup(a.bb * 4, 16);
   L.flag = off; off += 16;
   L.total = off;
@@ -181,6 +186,167 @@ __device__ __forceinline__ void mm_valu(const char* lds, int as_off, int as_ld, 
                           kp * (int)sizeof(DT) / 16);
 }
 
+// ---------------------------------------------------------------------------
+// W_hh slice resident in registers. Each lane keeps kScanRegChunks 16-byte
+// chunks of the slice for the whole launch, so a step's product reads only
+// the h tile from LDS.
+// ---------------------------------------------------------------------------
+// Global W_hh row of row r of the slice (gate q, owned unit u), -1 for padding.
+__device__ __forceinline__ int slice_row(int r, int hs, int hs_act, int gates, int H, int j0) {
+  const int q = r / hs, u = r - q * hs;
+  return (q < gates && u < hs_act) ? q * H + j0 + u : -1;
+}
+
+// Chunk of global row gr of W (row length K) starting at column k0; zero
+// for padding rows and columns. The register path is only planned when W is
+// 16-byte aligned and K is a multiple of a chunk, so a chunk is one aligned
+// 16-byte load that lies wholly inside or wholly outside the row.
+template <typename DT>
+__device__ __forceinline__ typename Chunk<DT>::T load_chunk(const DT* w, int gr, int K, int k0) {
+  typedef typename Chunk<DT>::T V;
+  V v = {};
+  if (gr >= 0 && k0 < K) v = *reinterpret_cast<const V*>(w + (size_t)gr * K + k0);
+  return v;
+}
+
+// MFMA layout: wave w holds column tiles (w / rks) * NTC + j, j < NTC, over
+// K chunks [(w % rks) * rcpt, + rcpt); lane l holds, for each, row
+// 16 * tile + l % 16 at k-group l / 16 (the B operand of Chunk<DT>::mfma).
+template <typename DT, int NTC>
+__device__ __forceinline__ void load_wreg_mfma(typename Chunk<DT>::T (&wr)[kScanRegChunks], const DT* w,
+                                               const ScanArgs& a, int gates, int j0, int hs_act) {
+  constexpr int CPT = kScanRegChunks / NTC;
+  constexpr int kEpc = 16 / sizeof(DT), kK = Chunk<DT>::kK;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4, wave = threadIdx.x >> 6;
+  const int tg = wave / a.rks, ks = wave - tg * a.rks;
+#pragma unroll
+  for (int j = 0; j < NTC; ++j) {
+    const int gr = slice_row((tg * NTC + j) * 16 + lr, a.hs, hs_act, gates, a.H, j0);
+#pragma unroll
+    for (int ch = 0; ch < CPT; ++ch)
+      wr[j * CPT + ch] = load_chunk<DT>(w, ch < a.rcpt ? gr : -1, a.K, (ks * a.rcpt + ch) * kK + lq * kEpc);
+  }
+}
+
+// out[r][c] (row stride out_ld) = sum_k A[r][k] W[c][k] for the wave's tiles,
+// rows 16 * rtiles; with rks > 1 each K share writes its own partial block
+// (16 * rtiles rows apart) for reduce_ksplit.
+template <typename DT, int NTC>
+__device__ __forceinline__ void mm_wreg(const typename Chunk<DT>::T (&wr)[kScanRegChunks], const DT* As, int as_ld,
+                                        int rtiles, const ScanArgs& a, float* out, int out_ld) {
+  typedef typename Chunk<DT>::T V;
+  constexpr int CPT = kScanRegChunks / NTC;
+  constexpr int kEpc = 16 / sizeof(DT), kK = Chunk<DT>::kK;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4, wave = threadIdx.x >> 6;
+  const int tg = wave / a.rks, ks = wave - tg * a.rks;
+  float* o = out + ks * rtiles * 16 * out_ld;
+  for (int rt = 0; rt < rtiles; ++rt) {
+    f32x4 c[NTC];
+#pragma unroll
+    for (int j = 0; j < NTC; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const DT* ap = As + (rt * 16 + lr) * as_ld + lq * kEpc + ks * a.rcpt * kK;
+#pragma unroll
+    for (int g = 0; g < CPT; g += 4) {
+      if (g < a.rcpt) {  // rcpt is a multiple of 4
+        V x[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = *reinterpret_cast<const V*>(ap + (g + q) * kK);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < NTC; ++j) c[j] = Chunk<DT>::mfma(x[q], wr[j * CPT + g + q], c[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NTC; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[(rt * 16 + 4 * lq + v) * out_ld + (tg * NTC + j) * 16 + lr] = c[j][v];
+  }
+}
+
+// VALU layout (batch blocks below 16 rows): thread t owns column
+// t % (256 / rks) of the slice over K chunks [(t / (256 / rks)) * rcpt, + rcpt).
+template <typename DT>
+__device__ __forceinline__ void load_wreg_valu(typename Chunk<DT>::T (&wr)[kScanRegChunks], const DT* w,
+                                               const ScanArgs& a, int gates, int j0, int hs_act) {
+  constexpr int kEpc = 16 / sizeof(DT);
+  const int C = kThreads / a.rks;
+  const int c = threadIdx.x % C, q = threadIdx.x / C;
+  const int gr = slice_row(c, a.hs, hs_act, gates, a.H, j0);
+#pragma unroll
+  for (int s = 0; s < kScanRegChunks; ++s)
+    wr[s] = load_chunk<DT>(w, s < a.rcpt ? gr : -1, a.K, (q * a.rcpt + s) * kEpc);
+}
+
+// One chunk of a VALU dot product into two accumulators. bf16 pairs go
+// through the packed dot instruction, so the resident weights are never
+// widened (widened copies would be hoisted out of the loop and double the
+// registers they occupy).
+template <typename DT>
+__device__ __forceinline__ void valu_chunk(const typename Chunk<DT>::T& wv, const DT* xp, float& s0, float& s1);
+template <>
+__device__ __forceinline__ void valu_chunk<float>(const f32x4& wv, const float* xp, float& s0, float& s1) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(xp);
+  s0 = __builtin_fmaf(x[0], wv[0], s0);
+  s1 = __builtin_fmaf(x[1], wv[1], s1);
+  s0 = __builtin_fmaf(x[2], wv[2], s0);
+  s1 = __builtin_fmaf(x[3], wv[3], s1);
+}
+template <>
+__device__ __forceinline__ void valu_chunk<bf16>(const bf16x8& wv, const bf16* xp, float& s0, float& s1) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(xp);
+  s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), __builtin_shufflevector(wv, wv, 0, 1),
+                                       s0, false);
+  s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), __builtin_shufflevector(wv, wv, 2, 3),
+                                       s1, false);
+  s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), __builtin_shufflevector(wv, wv, 4, 5),
+                                       s0, false);
+  s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), __builtin_shufflevector(wv, wv, 6, 7),
+                                       s1, false);
+}
+
+// out[r][c] = sum_k A[r][k] W[c][k], r < rows, for the thread's column and
+// K share; with rks > 1 each share writes its own partial block (rows apart
+// by `rows`) for reduce_ksplit. All lanes of a wave read the same A chunk.
+template <typename DT>
+__device__ __forceinline__ void mm_wreg_valu(const typename Chunk<DT>::T (&wr)[kScanRegChunks], const DT* As,
+                                             int as_ld, int rows, int ncols, const ScanArgs& a, float* out,
+                                             int out_ld) {
+  constexpr int kEpc = 16 / sizeof(DT);
+  const int C = kThreads / a.rks;
+  const int c = threadIdx.x % C, q = threadIdx.x / C;
+  float* o = out + q * rows * out_ld;
+  for (int r = 0; r < rows; ++r) {
+    const DT* xr = As + r * as_ld + q * a.rcpt * kEpc;
+    float s0 = 0.f, s1 = 0.f;
+    if ((a.rcpt & 3) == 0) {
+#pragma unroll
+      for (int g = 0; g < kScanRegChunks; g += 4) {
+        if (g < a.rcpt) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) valu_chunk<DT>(wr[g + u], xr + (g + u) * kEpc, s0, s1);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < kScanRegChunks; ++g)
+        if (g < a.rcpt) valu_chunk<DT>(wr[g], xr + g * kEpc, s0, s1);
+    }
+    if (c < ncols) o[r * out_ld + c] = s0 + s1;
+  }
+}
+
+// acc[r][c] = sum over the rks K shares of their partial blocks (fixed order).
+__device__ __forceinline__ void reduce_ksplit(const float* red, int rks, int rows, int ncols, float* acc,
+                                              int acc_ld) {
+  for (int i = threadIdx.x; i < rows * ncols; i += kThreads) {
+    const int r = i / ncols, c = i - r * ncols;
+    float v = red[r * acc_ld + c];
+    for (int k = 1; k < rks; ++k) v += red[(k * rows + r) * acc_ld + c];
+    acc[r * acc_ld + c] = v;
+  }
+}
+
 // Copy `rows` rows of `width_el` elements from a coherent exchange buffer
 // (row stride `src_ld` elements) into LDS (row stride `dst_ld`). Rows whose
 // batch index is outside [0, B) are zero-filled.
@@ -227,7 +393,7 @@ __device__ void load_weights(const DT* w, int klen, int kpad, int nrows, RowFn r
   }
 }
 
-template <typename DT>
+template <typename DT, bool WREG>
 __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const ScanLds L = scan_lds(a, (int)sizeof(DT));
@@ -281,10 +447,19 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
 
   // --- resident weights -----------------------------------------------------
   const DT* whh = reinterpret_cast<const DT*>(a.w_hh[d]);
-  load_weights<DT>(whh, a.K, a.Kp, L.ncw, [&](int r) -> int {
-    const int q = r / a.hs, u = r - q * a.hs;
-    return (q < gates && u < hs_act) ? q * a.H + j0 + u : -1;
-  }, lds, L.ws, L.ws_ld);
+  typename Chunk<DT>::T wreg[WREG ? kScanRegChunks : 1];
+  if constexpr (WREG) {
+    switch (a.rnt) {
+      case 1: load_wreg_mfma<DT, 1>(wreg, whh, a, gates, j0, hs_act); break;
+      case 2: load_wreg_mfma<DT, 2>(wreg, whh, a, gates, j0, hs_act); break;
+      case 4: load_wreg_mfma<DT, 4>(wreg, whh, a, gates, j0, hs_act); break;
+      default: load_wreg_valu<DT>(wreg, whh, a, gates, j0, hs_act); break;
+    }
+  } else {
+    load_weights<DT>(whh, a.K, a.Kp, L.ncw, [&](int r) -> int {
+      return slice_row(r, a.hs, hs_act, gates, a.H, j0);
+    }, lds, L.ws, L.ws_ld);
+  }
   if (a.mode == kLSTMP) {
     const DT* whr = reinterpret_cast<const DT*>(a.w_hr[d]);
     load_weights<DT>(whr, a.H, a.Hp, rup(a.ps, 16), [&](int r) -> int {
@@ -420,10 +595,24 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
       load_tile_coherent<DT>(hx_rs, hx_el(par, b0, 0), a.Kp, b0, a.B, tile_rows, a.Kp, lds, L.as, L.as_ld);
       __syncthreads();
     }
-    if (use_mfma)
+    if constexpr (WREG) {
+      const DT* As = reinterpret_cast<const DT*>(lds + L.as);
+      float* part = a.rks > 1 ? reinterpret_cast<float*>(lds + L.red) : acc;
+      switch (a.rnt) {
+        case 1: mm_wreg<DT, 1>(wreg, As, L.as_ld, mtiles, a, part, L.acc_ld); break;
+        case 2: mm_wreg<DT, 2>(wreg, As, L.as_ld, mtiles, a, part, L.acc_ld); break;
+        case 4: mm_wreg<DT, 4>(wreg, As, L.as_ld, mtiles, a, part, L.acc_ld); break;
+        default: mm_wreg_valu<DT>(wreg, As, L.as_ld, a.bb, L.ncw, a, part, L.acc_ld); break;
+      }
+      if (a.rks > 1) {
+        __syncthreads();
+        reduce_ksplit(part, a.rks, a.rnt ? tile_rows : a.bb, L.ncw, acc, L.acc_ld);
+      }
+    } else if (use_mfma) {
       mm_mfma<DT>(lds, L.as, L.as_ld, L.ws, L.ws_ld, acc, L.acc_ld, mtiles, L.ncw / 16, a.Kp);
-    else
+    } else {
       mm_valu<DT>(lds, L.as, L.as_ld, L.ws, L.ws_ld, acc, L.acc_ld, a.bb, gates * a.hs, a.Kp);
+    }
     __syncthreads();
 
     // Gate math on the owned elements; only the exchanged state is stored
@@ -524,22 +713,22 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
 
 int scan_lds_bytes(const ScanArgs& a, int esize) { return scan_lds(a, esize).total; }
 
+template <typename DT, bool WREG>
+hipError_t launch_scan_as(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<DT, WREG>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((scan_kernel<DT, WREG>), grid, dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream) {
   const int esize = dtype_bf16 ? 2 : 4;
   const int lds = scan_lds(a, esize).total;
-  const dim3 grid(a.gpx > 0 ? a.nxcd * a.gpx * a.ns : a.D * a.nbb * a.ns), block(kThreads);
-  if (dtype_bf16) {
-    hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<bf16>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(scan_kernel<bf16>, grid, block, lds, stream, a);
-  } else {
-    hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<float>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(scan_kernel<float>, grid, block, lds, stream, a);
-  }
-  return hipGetLastError();
+  const dim3 grid(a.gpx > 0 ? a.nxcd * a.gpx * a.ns : a.D * a.nbb * a.ns);
+  if (dtype_bf16)
+    return a.wreg ? launch_scan_as<bf16, true>(a, lds, grid, stream) : launch_scan_as<bf16, false>(a, lds, grid, stream);
+  return a.wreg ? launch_scan_as<float, true>(a, lds, grid, stream) : launch_scan_as<float, false>(a, lds, grid, stream);
 }
 
 }  // namespace rnnk

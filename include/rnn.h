@@ -133,7 +133,9 @@ typedef struct RnnDesc {
                             fit; RSSM: consecutive ids); 1: consecutive
                             workgroup ids form a group; 2: every group on one
                             XCD when it fits                                  */
-  int32_t reserved[5];   /* must be zero                                       */
+  int32_t weights;       /* scan W_hh slice: 0 automatic; 1 in LDS; 2 in
+                            registers when a layout fits (else LDS)           */
+  int32_t reserved[4];   /* must be zero                                       */
 } RnnDesc;
 
 /* Weights, PyTorch shapes and meaning. Index i = layer * D + direction
@@ -235,8 +237,11 @@ int rnn_read_status(const void* workspace, void* stream, int* device_status);
  * workgroups launched, LDS bytes per workgroup, batch rows per workgroup,
  * hidden units per workgroup, workgroups per group, projection outputs per
  * workgroup (LSTMP), number of groups (per direction for the scan), groups
- * per XCD when every group sits on one XCD (else 0)}; n_info >= 9. For
- * inspection and tests; touches no device. */
+ * per XCD when every group sits on one XCD (else 0)}; n_info >= 9. With
+ * n_info >= 13, info[9..12] = {scan W_hh slice in registers (1) or LDS (0),
+ * MFMA column tiles per wave (0: VALU), waves splitting K (VALU: K slices),
+ * 16-byte chunks per tile per lane}; the plan assumes 16-byte aligned
+ * weights. For inspection and tests; touches no device. */
 int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int xcds, int* info, int n_info);
 
 /* RNN_OK when the current device is a gfx950 GPU; RNN_E_DEVICE otherwise. */

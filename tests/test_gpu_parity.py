@@ -84,6 +84,19 @@ def test_small_cases(case):
     _compare(d, got, ref, name)
 
 
+@pytest.mark.parametrize("case", __import__("layout_cases").REG_CASES, ids=lambda c: c[0])
+def test_register_layouts(case):
+    """Each register-resident W_hh layout (and the LDS fallback) against the
+    oracle; the planner side of each case is checked on the CPU."""
+    name, mode, dt, T, B, F, H, P, bb, hs, bidir, layout, varlen, expect = case
+    log(f"[gpu] register layout case {name}")
+    d = synth.make_rnn_inputs(mode, T, B, F, H, proj_size=P, num_layers=1, bidirectional=bidir, dtype=dt,
+                              layout=layout, varlen=varlen, w_scale=1.0 / np.sqrt(H),
+                              seed=zlib.crc32(name.encode()) % 1000, h0_std=0.3, c0_std=0.3)
+    got = run_rnn(d, y_fill=float("nan"), tile_batch=bb, tile_hidden=hs, weights=2 if expect[0] else 1)
+    _compare(d, got, _oracle(d), name)
+
+
 def test_padding_sentinel_untouched():
     log("[gpu] padding sentinel")
     lengths = np.array([5, 9, 2, 9, 1, 7, 3, 8], dtype=np.int32)

@@ -104,3 +104,24 @@ def test_invalid_arguments():
     with pytest.raises(gss.RnnError) as e:
         gss.rnn_plan_info(d, lengths)
     assert e.value.status == CODE["RNN_E_SHAPE"]
+
+
+@pytest.mark.parametrize("case", __import__("layout_cases").REG_CASES, ids=lambda c: c[0])
+def test_forced_register_layouts(case):
+    import numpy as np
+    name, mode, dt, T, B, F, H, P, bb, hs, bidir, layout, varlen, expect = case
+    d = gss.RnnDesc()
+    d.mode = gss.MODES[mode]
+    d.dtype = 1 if dt == "bf16" else 0
+    d.layout = 1 if layout == "packed" else 0
+    d.T, d.B, d.input_size, d.hidden_size, d.proj_size = T, B, F, H, P
+    d.num_layers, d.bidirectional, d.has_bias = 1, int(bidir), 1
+    d.tile_batch, d.tile_hidden = bb, hs
+    d.weights = 2 if expect[0] else 1
+    lengths = None
+    if varlen:
+        lengths = np.sort(np.random.default_rng(0).integers(varlen[0], varlen[1] + 1, size=B))[::-1]
+        lengths = lengths.astype(np.int32)
+    p = gss.rnn_plan_info(d, lengths)
+    assert (p["rows"], p["hidden_per_wg"]) == (bb, hs)
+    assert (p["wreg"], p["reg_tiles"], p["reg_ksplit"], p["reg_chunks"]) == expect
