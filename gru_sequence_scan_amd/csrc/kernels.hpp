@@ -47,6 +47,10 @@ struct ScanArgs {
   // rcpt chunks per tile. VALU register path (rnt = 0): thread t holds
   // output column t % (256 / rks) over K slice t / (256 / rks), rcpt chunks.
   int wreg, rnt, rks, rcpt;
+  // LSTMP projection product (W_hr slice in LDS) on MFMA: pnt column tiles
+  // per wave, pks waves splitting K, pcpt chunks each; pnt = 0: whole tiles
+  // per wave without a K split.
+  int pnt, pks, pcpt;
   // per direction tensors (already offset to this layer)
   const void* w_hh[2];
   const void* w_hr[2];

@@ -221,6 +221,7 @@ double mm_us(bool mfma, int esize, int rows, int cols, int kp) {
 struct ScanPlan {
   int bb, hs, ns, ps, nbb, gpx, lds;
   int wreg, rnt, rks, rcpt;  // register-resident W_hh layout (ScanArgs)
+  int pnt, pks, pcpt;        // LSTMP projection product layout (ScanArgs)
 };
 
 int scan_grid(const ScanPlan& p, int D, int xcds) { return p.gpx > 0 ? xcds * p.gpx * p.ns : D * p.nbb * p.ns; }
@@ -230,35 +231,49 @@ int scan_grid(const ScanPlan& p, int D, int xcds) { return p.gpx > 0 ? xcds * p.
 // per lane. MFMA (bb a multiple of 16): rnt column tiles per wave, rks waves
 // per tile set splitting K, rcpt chunks per tile (a multiple of 4). VALU:
 // one output column per thread over one of rks K slices of rcpt chunks.
-bool reg_layout(int bb, int ncw, int Kp, int esize, int* rnt, int* rks, int* rcpt) {
-  if (bb % 16 == 0) {
-    // the four waves cover 4 * nt / ks column tiles (>= the slice's, the
-    // extra ones are zero rows); fewest padded tiles first, then least K split
-    const int ct = ncw / 16, nch = Kp / (esize == 2 ? 32 : 16);
-    int best_cols = 1 << 30;
-    bool ok = false;
-    for (int ks = 1; ks <= 4; ks *= 2) {
-      for (int nt = 1; nt <= 4; nt *= 2) {
-        const int cover = 4 * nt / ks;
-        if (4 * nt % ks != 0 || cover < ct) continue;
-        if (nch % ks != 0) continue;
-        const int cpt = nch / ks;
-        if (cpt % 4 != 0 || cpt * nt > kScanRegChunks) continue;
-        if (cover < best_cols) {
-          best_cols = cover;
-          *rnt = nt; *rks = ks; *rcpt = cpt;
-          ok = true;
-        }
+// MFMA wave layout of an ncw-row product over Kp: the four waves cover
+// 4 * nt / ks column tiles (>= the ncw / 16 needed; extra ones are zero
+// rows), ks waves splitting K into cpt chunks each (a multiple of 4), at most
+// max_chunks chunks (nt * cpt) per lane. Fewest padded tiles first, then the
+// least K split.
+bool mfma_split(int ncw, int Kp, int esize, int max_chunks, int* rnt, int* rks, int* rcpt) {
+  const int ct = ncw / 16, nch = Kp / (esize == 2 ? 32 : 16);
+  int best_cols = 1 << 30;
+  bool ok = false;
+  for (int ks = 1; ks <= 4; ks *= 2) {
+    for (int nt = 1; nt <= 4; nt *= 2) {
+      const int cover = 4 * nt / ks;
+      if (4 * nt % ks != 0 || cover < ct) continue;
+      if (nch % ks != 0) continue;
+      const int cpt = nch / ks;
+      if (cpt % 4 != 0 || cpt * nt > max_chunks) continue;
+      if (cover < best_cols) {
+        best_cols = cover;
+        *rnt = nt; *rks = ks; *rcpt = cpt;
+        ok = true;
       }
     }
-    return ok;
   }
-  if (ncw > 256) return false;
-  const int c = ncw <= 64 ? 64 : (ncw <= 128 ? 128 : 256);
-  const int q = 256 / c, nch = Kp * esize / 16;
-  if (nch % q != 0 || nch / q > kScanRegChunks) return false;
-  *rnt = 0; *rks = q; *rcpt = nch / q;
-  return true;
+  return ok;
+}
+
+bool reg_layout(int bb, int ncw, int Kp, int esize, int* rnt, int* rks, int* rcpt) {
+  if (bb % 16 == 0) return mfma_split(ncw, Kp, esize, kScanRegChunks, rnt, rks, rcpt);
+  // VALU: 256 / q columns, q K slices; a slice's chunks cost ~12 cycles each
+  // in sequence, the K-split reduction ~300 cycles (barrier + LDS round trip)
+  const int nch = Kp * esize / 16;
+  double best = 1e30;
+  bool ok = false;
+  for (int q = 1; q <= 4; q *= 2) {
+    if (256 / q < ncw || nch % q != 0 || nch / q > kScanRegChunks) continue;
+    const double cyc = 12.0 * (nch / q) + (q > 1 ? 300.0 : 0.0);
+    if (cyc < best) {
+      best = cyc;
+      *rnt = 0; *rks = q; *rcpt = nch / q;
+      ok = true;
+    }
+  }
+  return ok;
 }
 
 int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wreg, ScanPlan* out) {
@@ -298,6 +313,8 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wre
         a.bb = bb; a.hs = hs; a.ps = ps; a.Kp = m.Kp; a.Hp = m.Hp;
         a.wreg = wreg;
         if (wreg && !reg_layout(bb, ncw, m.Kp, m.esize, &a.rnt, &a.rks, &a.rcpt)) continue;
+        if (lstmp && mfma && !mfma_split(rup(ps, 16), m.Hp, m.esize, 1 << 20, &a.pnt, &a.pks, &a.pcpt))
+          a.pnt = a.pks = a.pcpt = 0;
         const int lds = scan_lds_bytes(a, m.esize);
         if (lds > kMaxLds) continue;
         const int groups = m.D * nbb;
@@ -315,19 +332,23 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wre
           const double rt = bb / 16, per_chunk = m.esize == 2 ? 16.0 : 32.0;
           mm = std::max(rt * a.rcpt * a.rnt * per_chunk, rt * a.rcpt * 32.0) / 2400.0 + (a.rks > 1 ? 0.2 : 0.0);
         } else if (wreg) {
-          mm = (double)bb * a.rcpt * 10.0 / 2400.0 + 0.1 + (a.rks > 1 ? 0.2 : 0.0);
+          mm = (double)bb * a.rcpt * 12.0 / 2400.0 + 0.1 + (a.rks > 1 ? 0.125 : 0.0);
         } else {
           mm = mm_us(mfma, m.esize, bb, m.gates * hs, mfma ? m.Kp : m.K);
         }
         double t = ex + mm + bb * hs / 256.0 * 0.05;
-        if (lstmp)
-          t += (barrier_us(ns) + 0.3 + (double)bb * m.Hp * m.esize / 100e3) * xf +
-               mm_us(mfma, m.esize, bb, ps, mfma ? m.Hp : H);
+        if (lstmp) {
+          double mp = mm_us(mfma, m.esize, bb, ps, mfma ? m.Hp : H);
+          if (a.pnt > 0)  // K split over the waves
+            mp = mp * a.pnt * a.pks / 4.0 + (a.pks > 1 ? 0.125 : 0.0);
+          t += (barrier_us(ns) + 0.3 + (double)bb * m.Hp * m.esize / 100e3) * xf + mp;
+        }
         if (d->placement == 2 && !xcd_aligned) t += 1e3;  // requested: aligned plans first
         if (d->weights == 2 && !wreg) t += 1e3;            // requested: registers first
         if (t < best) {
           best = t;
-          *out = ScanPlan{bb, hs, ns, ps, nbb, xcd_aligned ? gpx : 0, lds, wreg, a.rnt, a.rks, a.rcpt};
+          *out = ScanPlan{bb, hs, ns, ps, nbb, xcd_aligned ? gpx : 0, lds, wreg, a.rnt, a.rks, a.rcpt,
+                          a.pnt, a.pks, a.pcpt};
           found = true;
         }
       }
@@ -544,6 +565,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     a.bb = p.bb; a.hs = p.hs; a.ns = p.ns; a.ps = p.ps; a.nbb = p.nbb; a.Kp = m.Kp; a.Hp = m.Hp;
     a.nxcd = xcds; a.gpx = p.gpx;
     a.wreg = p.wreg; a.rnt = p.rnt; a.rks = p.rks; a.rcpt = p.rcpt;
+    a.pnt = p.pnt; a.pks = p.pks; a.pcpt = p.pcpt;
     for (int di = 0; di < m.D; ++di) {
       const int i = l * m.D + di;
       a.w_hh[di] = w->w_hh[i];

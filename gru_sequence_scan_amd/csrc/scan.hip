@@ -34,6 +34,7 @@ struct ScanLds {
   int ws, wr, as, acc, red, lens, flag, total;  // byte offsets
   int ws_ld, wr_ld, as_ld, acc_ld;    // row strides in elements
   int ncw, ncp;                       // W rows (padded to 16), acc columns
+  int ncp_wr;                         // W_hr rows held in LDS (LSTMP)
 };
 
 __host__ __device__ inline int rup(int x, int m) { return (x + m - 1) / m * m; }
@@ -47,7 +48,8 @@ __host__ __device__ inline ScanLds scan_lds(const ScanArgs& a, int esize) {
   // register MFMA layouts cover 4 * rnt / rks column tiles (the last ones
   // may be zero padding), all of which the product writes
   if (a.wreg && a.rnt > 0 && 64 * a.rnt / a.rks > L.ncw) L.ncw = 64 * a.rnt / a.rks;
-  const int ps16 = a.mode == kLSTMP ? rup(a.ps, 16) : 0;
+  int ps16 = a.mode == kLSTMP ? rup(a.ps, 16) : 0;
+  if (a.mode == kLSTMP && a.pnt > 0 && 64 * a.pnt / a.pks > ps16) ps16 = 64 * a.pnt / a.pks;
   L.ncp = L.ncw > ps16 ? L.ncw : ps16;
   L.ws_ld = a.Kp + pad;
   L.wr_ld = a.Hp + pad;
@@ -57,11 +59,14 @@ __host__ __device__ inline ScanLds scan_lds(const ScanArgs& a, int esize) {
   const int bb16 = rup(a.bb, 16);
   int off = 0;
   L.ws = off; off += a.wreg ? 0 : rup(L.ncw * L.ws_ld * esize, 16);
+  L.ncp_wr = ps16;
   L.wr = off; off += a.mode == kLSTMP ? rup(ps16 * L.wr_ld * esize, 16) : 0;
   L.as = off; off += rup(bb16 * L.as_ld * esize, 16);
   L.acc = off; off += rup(bb16 * L.acc_ld * 4, 16);
-  // K-split partial sums of the register-weight product
-  L.red = off; off += (a.wreg && a.rks > 1) ? rup(a.rks * bb16 * L.acc_ld * 4, 16) : 0;
+  // K-split partial sums of the register-weight and projection products
+  int ks_max = a.wreg ? a.rks : 1;
+  if (a.mode == kLSTMP && a.pnt > 0 && a.pks > ks_max) ks_max = a.pks;
+  L.red = off; off += ks_max > 1 ? rup(ks_max * bb16 * L.acc_ld * 4, 16) : 0;
   L.lens = off; off += rup(a.bb * 4, 16);
   L.flag = off; off += 16;
   L.total = off;
@@ -256,6 +261,46 @@ __device__ __forceinline__ void mm_wreg(const typename Chunk<DT>::T (&wr)[kScanR
 #pragma unroll
           for (int j = 0; j < NTC; ++j) c[j] = Chunk<DT>::mfma(x[q], wr[j * CPT + g + q], c[j]);
       }
+    }
+#pragma unroll
+    for (int j = 0; j < NTC; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[(rt * 16 + 4 * lq + v) * out_ld + (tg * NTC + j) * 16 + lr] = c[j][v];
+  }
+}
+
+// The same wave layout with the B operand read from LDS (W rows of stride
+// w_ld): wave w takes column tiles (w / ks) * NTC + j over K chunks
+// [(w % ks) * cpt, + cpt); with ks > 1 each K share writes its own partial
+// block for reduce_ksplit.
+template <typename DT, int NTC>
+__device__ __forceinline__ void mm_lds_split(const DT* As, int as_ld, const DT* Ws, int w_ld, int rtiles, int ks_n,
+                                             int cpt, float* out, int out_ld) {
+  typedef typename Chunk<DT>::T V;
+  constexpr int kEpc = 16 / sizeof(DT), kK = Chunk<DT>::kK;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4, wave = threadIdx.x >> 6;
+  const int tg = wave / ks_n, ks = wave - tg * ks_n;
+  float* o = out + ks * rtiles * 16 * out_ld;
+  const DT* wp[NTC];
+#pragma unroll
+  for (int j = 0; j < NTC; ++j) wp[j] = Ws + ((tg * NTC + j) * 16 + lr) * w_ld + lq * kEpc + ks * cpt * kK;
+  for (int rt = 0; rt < rtiles; ++rt) {
+    f32x4 c[NTC];
+#pragma unroll
+    for (int j = 0; j < NTC; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const DT* ap = As + (rt * 16 + lr) * as_ld + lq * kEpc + ks * cpt * kK;
+    for (int g = 0; g < cpt; g += 4) {  // cpt is a multiple of 4
+      V x[4], y[4][NTC];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[q] = *reinterpret_cast<const V*>(ap + (g + q) * kK);
+#pragma unroll
+        for (int j = 0; j < NTC; ++j) y[q][j] = *reinterpret_cast<const V*>(wp[j] + (g + q) * kK);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NTC; ++j) c[j] = Chunk<DT>::mfma(x[q], y[q][j], c[j]);
     }
 #pragma unroll
     for (int j = 0; j < NTC; ++j)
@@ -462,7 +507,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   }
   if (a.mode == kLSTMP) {
     const DT* whr = reinterpret_cast<const DT*>(a.w_hr[d]);
-    load_weights<DT>(whr, a.H, a.Hp, rup(a.ps, 16), [&](int r) -> int {
+    load_weights<DT>(whr, a.H, a.Hp, L.ncp_wr, [&](int r) -> int {
       return r < ps_act ? p0 + r : -1;
     }, lds, L.wr, L.wr_ld);
   }
@@ -676,10 +721,24 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
       load_tile_coherent<DT>(mx_rs, mx_el(b0, 0), a.Hp, b0, a.B, use_mfma ? rup(a.bb, 16) : a.bb,
                              a.Hp, lds, L.as, L.as_ld);
       __syncthreads();
-      if (use_mfma)
+      if (use_mfma && a.pnt > 0) {
+        const DT* As = reinterpret_cast<const DT*>(lds + L.as);
+        const DT* Wr = reinterpret_cast<const DT*>(lds + L.wr);
+        float* part = a.pks > 1 ? reinterpret_cast<float*>(lds + L.red) : acc;
+        switch (a.pnt) {
+          case 1: mm_lds_split<DT, 1>(As, L.as_ld, Wr, L.wr_ld, mtiles, a.pks, a.pcpt, part, L.acc_ld); break;
+          case 2: mm_lds_split<DT, 2>(As, L.as_ld, Wr, L.wr_ld, mtiles, a.pks, a.pcpt, part, L.acc_ld); break;
+          default: mm_lds_split<DT, 4>(As, L.as_ld, Wr, L.wr_ld, mtiles, a.pks, a.pcpt, part, L.acc_ld); break;
+        }
+        if (a.pks > 1) {
+          __syncthreads();
+          reduce_ksplit(part, a.pks, tile_rows, 64 * a.pnt / a.pks, acc, L.acc_ld);
+        }
+      } else if (use_mfma) {
         mm_mfma<DT>(lds, L.as, L.as_ld, L.wr, L.wr_ld, acc, L.acc_ld, mtiles, rup(a.ps, 16) / 16, a.Hp);
-      else
+      } else {
         mm_valu<DT>(lds, L.as, L.as_ld, L.wr, L.wr_ld, acc, L.acc_ld, a.bb, a.ps, a.Hp);
+      }
       __syncthreads();
       for (int e = tid; e < a.bb * a.ps; e += kThreads) {
         const int r = e / a.ps, p = e - r * a.ps;
