@@ -80,16 +80,21 @@ __device__ __forceinline__ void reduce_waves(const f32x4& acc, float* red, float
   }
 }
 
-// out[v * ldo + c] = sum_{k < K} X[v * ldx + k] * W[c * ldw + k] for all four
-// rows v of X (rows past the group's batch rows hold zeros and are ignored
-// by the callers) and c < N, on v_mfma_f32_4x4x1f32: 16 blocks of 4x4 per
-// instruction, lane l of a pass owning output column 64 * pass + l. X and W
-// rows are 16-byte aligned and zero-padded to a multiple of 4. Narrow
-// products (N <= 64) split K over the four waves and reduce through `red`
-// (4 waves x 4 rows x 64 floats); wider ones give the waves whole 64-column
-// passes.
+struct Plain {
+  __device__ float operator()(int, float x) const { return x; }
+};
+
+// out[v * ldo + c] = epi(c, sum_{k < K} X[v * ldx + k] * W[c * ldw + k]) for
+// all four rows v of X (rows past the group's batch rows hold zeros and are
+// ignored by the callers) and c < N, on v_mfma_f32_4x4x1f32: 16 blocks of
+// 4x4 per instruction, lane l of a pass owning output column 64 * pass + l.
+// X and W rows are 16-byte aligned and zero-padded to a multiple of 4.
+// Narrow products (N <= 64) split K over the four waves and reduce through
+// `red` (4 waves x 4 rows x 64 floats); wider ones give the waves whole
+// 64-column passes.
+template <typename Epi = Plain>
 __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out, int ldo, int N, int K,
-                    float* red) {
+                    float* red, Epi epi = Epi()) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K4 = (K + 3) >> 2;
   const float* xr = X + (lane & 3) * ldx;
@@ -100,63 +105,80 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
       const f32x4 acc = dot_chain(xr, W + (c < N ? c : N - 1) * ldw, 0, K4, zero4);
       if (c < N) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) out[v * ldo + c] = acc[v];
+        for (int v = 0; v < 4; ++v) out[v * ldo + c] = epi(c, acc[v]);
       }
     }
     return;
   }
   const int per = (K4 + 3) >> 2;
   const int ka = min(K4, wave * per), kb = min(K4, ka + per);
-  reduce_waves(dot_chain(xr, W + (lane < N ? lane : N - 1) * ldw, ka, kb, zero4), red, out, ldo, N);
+  const f32x4 acc = dot_chain(xr, W + (lane < N ? lane : N - 1) * ldw, ka, kb, zero4);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[(wave * 4 + v) * 64 + lane] = acc[v];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 4 * N; i += kThreads) {
+    const int v = i / N, c = i - v * N;
+    out[v * ldo + c] = epi(c, red[(0 * 4 + v) * 64 + c] + red[(1 * 4 + v) * 64 + c] +
+                                  red[(2 * 4 + v) * 64 + c] + red[(3 * 4 + v) * 64 + c]);
+  }
 }
 
-// The GRU products of the owned slice of hp units in one K-split pass:
-// output columns [r | z | n_x | n_h], hp each, where
-//   r, z : W_ih e + W_hh h   (the sum both gates need),
-//   n_x  : W_ih e            (input part of the candidate),
-//   n_h  : W_hh h            (hidden part; the reset gate scales it).
-// The reduction runs over the concatenated chunks [e | h]; a column that takes
-// no part in a segment reads the shared zero row. Slices of up to 16 units
-// split K over the waves; wider ones give the waves whole column passes.
-__device__ void gru_product(const float* e, int lde, const float* h, int ldh, const float* wih, const float* whh,
-                            const float* zero, float* out, int ldo, int hp, int E, int Hb, float* red) {
+// Two independent narrow products (N1, N2 <= 64) in one K-split pass: their
+// chains interleave, so the second costs little extra latency. The four
+// waves' partial sums are left in red1 / red2 (4 waves x 4 rows x 64 floats)
+// for the caller to reduce after a barrier.
+__device__ void mv4_pair(const float* X1, int ldx1, const float* W1, int ldw1, int N1, int K1, float* red1,
+                         const float* X2, int ldx2, const float* W2, int ldw2, int N2, int K2, float* red2) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int E4 = (E + 3) >> 2, H4 = (Hb + 3) >> 2, N = 4 * hp;
-  const float* xe = e + (lane & 3) * lde;
-  const float* xh = h + (lane & 3) * ldh;
-  // W rows of output column c in the e and h segments
-  auto rows_of = [&](int c, const float*& we, const float*& wh) {
-    const int q = c / hp, j = c - q * hp;  // gate block and unit
-    we = (c < N && q < 3) ? wih + (q * hp + j) * lde : zero;
-    wh = (c < N && q != 2) ? whh + ((q == 3 ? 2 : q) * hp + j) * ldh : zero;
-  };
+  const int A4 = (K1 + 3) >> 2, B4 = (K2 + 3) >> 2;
+  const int pa = (A4 + 3) >> 2, pb = (B4 + 3) >> 2;
+  const int a0 = min(A4, wave * pa), a1 = min(A4, a0 + pa);
+  const int b0 = min(B4, wave * pb), b1 = min(B4, b0 + pb);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  if (N > 64) {  // wide slices: whole 64-column passes per wave, no K split
-    for (int cg = __builtin_amdgcn_readfirstlane(wave); cg * 64 < N; cg += 4) {
-      const int c = cg * 64 + lane;
-      const float *we, *wh;
-      rows_of(c, we, wh);
-      const f32x4 acc = dot_chain(xh, wh, 0, H4, dot_chain(xe, we, 0, E4, zero4));
-      if (c < N) {
+  const float* x1 = X1 + (lane & 3) * ldx1;
+  const float* x2 = X2 + (lane & 3) * ldx2;
+  const float* w1 = W1 + (lane < N1 ? lane : N1 - 1) * ldw1;
+  const float* w2 = W2 + (lane < N2 ? lane : N2 - 1) * ldw2;
+  f32x4 c1 = zero4, c2 = zero4;
+  // common part: both chains advance together, four chunks per iteration
+  const int n1 = a1 - a0, n2 = b1 - b0, nc = __builtin_amdgcn_readfirstlane(min(n1, n2));
+  int q = 0;
+  for (; q + 4 <= nc; q += 4) {
+    f32x4 xa[4], wa[4], xb[4], wb[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) out[v * ldo + c] = acc[v];
-      }
+    for (int u = 0; u < 4; ++u) {
+      xa[u] = *reinterpret_cast<const f32x4*>(x1 + 4 * (a0 + q + u));
+      wa[u] = *reinterpret_cast<const f32x4*>(w1 + 4 * (a0 + q + u));
+      xb[u] = *reinterpret_cast<const f32x4*>(x2 + 4 * (b0 + q + u));
+      wb[u] = *reinterpret_cast<const f32x4*>(w2 + 4 * (b0 + q + u));
     }
-    return;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[u][e], wa[u][e], c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_4x4x1f32(xb[u][e], wb[u][e], c2, 0, 0, 0);
+      }
   }
-  const float *we, *wh;
-  rows_of(lane, we, wh);
-  const int Q = E4 + H4, per = (Q + 3) >> 2;
-  const int qa = min(Q, wave * per), qb = min(Q, qa + per);
-  f32x4 acc = dot_chain(xe, we, min(qa, E4), min(qb, E4), zero4);
-  acc = dot_chain(xh, wh, max(qa, E4) - E4, max(qb, E4) - E4, acc);
-  reduce_waves(acc, red, out, ldo, N);
+  c1 = dot_chain(x1, w1, a0 + q, a1, c1);
+  c2 = dot_chain(x2, w2, b0 + q, b1, c2);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    red1[(wave * 4 + v) * 64 + lane] = c1[v];
+    red2[(wave * 4 + v) * 64 + lane] = c2[v];
+  }
+}
+
+// Fixed-order sum of the four waves' partials of output (row v, column c).
+__device__ __forceinline__ float red_sum(const float* red, int v, int c) {
+  return red[(0 * 4 + v) * 64 + c] + red[(1 * 4 + v) * 64 + c] + red[(2 * 4 + v) * 64 + c] +
+         red[(3 * 4 + v) * 64 + c];
 }
 
 struct RssmLds {
   // float offsets (all multiples of 4)
   int was, bas, w2, b2, wih, whh, w1s, b1;
-  int sa, e, h, hs, u, v, gi, zero, red, flag, total;
+  int sa, e, h, hs, u, v, gi, gh, red, red2, flag, total;
   int ld_sa, ld_e, ld_h, ld_hs, ld_v, ld_g;
 };
 
@@ -168,7 +190,7 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   L.ld_h = r4(a.Hb);
   L.ld_hs = r4(a.h_per);
   L.ld_v = r4(2 * a.S);
-  L.ld_g = r4(4 * a.h_per);
+  L.ld_g = r4(3 * a.h_per);
   const int R = kMaxRows;
   int o = 0;
   auto take = [&](int n) { const int at = o; o += r4(n); return at; };
@@ -187,8 +209,9 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   L.u = take(R * L.ld_e);
   L.v = take(R * L.ld_v);
   L.gi = take(R * L.ld_g);
-  L.zero = take(L.ld_e > L.ld_h ? L.ld_e : L.ld_h);
+  L.gh = take(R * L.ld_g);
   L.red = take(4 * 4 * 64);
+  L.red2 = take(4 * 4 * 64);
   L.flag = take(4);
   L.total = o * 4;
   return L;
@@ -295,26 +318,28 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
   const int ar = tid / A, ac = tid - ar * A;
   const bool act_owner = tid < nrows * A;
   __syncthreads();
-  mv4(sm + L.sa, L.ld_sa, sm + L.was, L.ld_sa, sm + L.e, L.ld_e, E, SA, red);
+  // e_0 = ELU(W_as [s_0; a_0] + b_as) and the hidden part of the first GRU
+  // step, W_hh h_0 on the owned slice
+  const float* bas = sm + L.bas;
+  auto elu_bias = [bas](int c, float x) { return felu(x + bas[c]); };
+  mv4(sm + L.sa, L.ld_sa, sm + L.was, L.ld_sa, sm + L.e, L.ld_e, E, SA, red, elu_bias);
   __syncthreads();
-  for (int i = tid; i < nrows * E; i += kThreads) {
-    const int r = i / E, c = i - r * E;
-    sm[L.e + r * L.ld_e + c] = felu(sm[L.e + r * L.ld_e + c] + sm[L.bas + c]);
-  }
+  mv4(sm + L.h, L.ld_h, sm + L.whh, L.ld_h, sm + L.gh, L.ld_g, 3 * hp, Hb, red);
   __syncthreads();
 
   unsigned nbar = 0;
   for (int t = 0; t < a.T; ++t) {
     const int par = t & 1;
-    // ---- GRU phase on the owned slice ----
-    gru_product(sm + L.e, L.ld_e, sm + L.h, L.ld_h, sm + L.wih, sm + L.whh, sm + L.zero, sm + L.gi, L.ld_g, hp, E,
-                Hb, red);
+    // ---- GRU phase on the owned slice: W_ih e_t here, W_hh h_{t-1} was
+    //      computed alongside the previous step's projector ----
+    mv4(sm + L.e, L.ld_e, sm + L.wih, L.ld_e, sm + L.gi, L.ld_g, 3 * hp, E, red);
     __syncthreads();
     if (owner) {
-      const float* gg = sm + L.gi + own_r * L.ld_g;
-      const float rg = fsigmoid(gg[own_j] + bias_r);
-      const float zg = fsigmoid(gg[hp + own_j] + bias_z);
-      const float ng = ftanh(gg[2 * hp + own_j] + bias_nx + rg * (gg[3 * hp + own_j] + bias_nh));
+      const float* gi = sm + L.gi + own_r * L.ld_g;
+      const float* gh = sm + L.gh + own_r * L.ld_g;
+      const float rg = fsigmoid(gi[own_j] + gh[own_j] + bias_r);
+      const float zg = fsigmoid(gi[hp + own_j] + gh[hp + own_j] + bias_z);
+      const float ng = ftanh(gi[2 * hp + own_j] + bias_nx + rg * (gh[2 * hp + own_j] + bias_nh));
       const float h = (1.f - zg) * ng + zg * hreg;
       hreg = h;
       sm[L.hs + own_r * L.ld_hs + own_j] = h;
@@ -372,9 +397,9 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
               s4 += (m0 + m < a.nw) ? v : f32x4{0.f, 0.f, 0.f, 0.f};
             }
           }
+          // u_t = ELU(W_1 h_t + b_1); padding columns stay 0
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            if (4 * cp + k >= E) s4[k] = 0.f;
+          for (int k = 0; k < 4; ++k) s4[k] = 4 * cp + k < E ? felu(s4[k] + sm[L.b1 + 4 * cp + k]) : 0.f;
           *reinterpret_cast<f32x4*>(sm + L.u + rp * L.ld_e + 4 * cp) = s4;
         }
         if (has_h) {
@@ -387,18 +412,24 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
       }
     }
     __syncthreads();
-    for (int i = tid; i < nrows * E; i += kThreads) {
-      const int r = i / E, k = i - r * E;
-      sm[L.u + r * L.ld_e + k] = felu(sm[L.u + r * L.ld_e + k] + sm[L.b1 + k]);
+    // ---- v_t = W_2 u_t and, for the next GRU step, W_hh h_t on the owned
+    //      slice, in one K-split pass ----
+    const bool pair = 2 * S <= 64 && 3 * hp <= 64;
+    if (pair) {
+      mv4_pair(sm + L.u, L.ld_e, sm + L.w2, L.ld_e, 2 * S, E, red, sm + L.h, L.ld_h, sm + L.whh, L.ld_h, 3 * hp, Hb,
+               sm + L.red2);
+    } else {
+      mv4(sm + L.u, L.ld_e, sm + L.w2, L.ld_e, sm + L.v, L.ld_v, 2 * S, E, red);
+      __syncthreads();
+      mv4(sm + L.h, L.ld_h, sm + L.whh, L.ld_h, sm + L.gh, L.ld_g, 3 * hp, Hb, sm + L.red2);
     }
     __syncthreads();
-    // ---- v_t, (mean, std, s_t), then e_{t+1} (every member, whole) ----
-    mv4(sm + L.u, L.ld_e, sm + L.w2, L.ld_e, sm + L.v, L.ld_v, 2 * S, E, red);
-    __syncthreads();
+    // (mean, std, s_t) straight from the reduction of v_t
     if (tail_owner) {
-      const float* vr = sm + L.v + tr * L.ld_v;
-      const float mean = vr[tc] + sm[L.b2 + tc];
-      const float sd = fsoftplus(vr[S + tc] + sm[L.b2 + S + tc]) + a.scale_lb;
+      const float vm = pair ? red_sum(red, tr, tc) : sm[L.v + tr * L.ld_v + tc];
+      const float vs = pair ? red_sum(red, tr, S + tc) : sm[L.v + tr * L.ld_v + S + tc];
+      const float mean = vm + sm[L.b2 + tc];
+      const float sd = fsoftplus(vs + sm[L.b2 + S + tc]) + a.scale_lb;
       const float st = mean + eps_v * sd;
       sm[L.sa + tr * L.ld_sa + tc] = st;
       if (w == 0) {
@@ -408,15 +439,18 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
         a.states[o] = st;
       }
     }
+    if (pair) {
+      const float* red2 = sm + L.red2;
+      for (int i = tid; i < 4 * 3 * hp; i += kThreads) {
+        const int v = i / (3 * hp), c = i - v * (3 * hp);
+        sm[L.gh + v * L.ld_g + c] = red_sum(red2, v, c);
+      }
+    }
     if (t + 1 < a.T) {
       if (act_owner) sm[L.sa + ar * L.ld_sa + S + ac] = act_v;
       __syncthreads();
-      mv4(sm + L.sa, L.ld_sa, sm + L.was, L.ld_sa, sm + L.e, L.ld_e, E, SA, red);
-      __syncthreads();
-      for (int i = tid; i < nrows * E; i += kThreads) {
-        const int r = i / E, c = i - r * E;
-        sm[L.e + r * L.ld_e + c] = felu(sm[L.e + r * L.ld_e + c] + sm[L.bas + c]);
-      }
+      // e_{t+1} = ELU(W_as [s_t; a_{t+1}] + b_as), every member, whole
+      mv4(sm + L.sa, L.ld_sa, sm + L.was, L.ld_sa, sm + L.e, L.ld_e, E, SA, red, elu_bias);
     }
     __syncthreads();
   }

@@ -169,6 +169,27 @@ def test_rssm_small():
         assert_close(g, r, "f32", "rssm " + nm)
 
 
+RSSM_SHAPES = [
+    # name, B, T, S, A, E, Hb, tile_batch, tile_hidden
+    ("rssm_wide_state", 6, 5, 40, 4, 36, 30, 0, 0),      # 2S > 64: products in two passes
+    ("rssm_wide_slice", 5, 6, 6, 2, 70, 75, 0, 25),      # 3 * slice > 64, E > 64
+    ("rssm_rows4_odd", 10, 7, 8, 3, 33, 26, 4, 0),       # widths not multiples of 4
+    ("rssm_rows1", 3, 4, 5, 2, 16, 12, 1, 0),
+]
+
+
+@pytest.mark.parametrize("case", RSSM_SHAPES, ids=[c[0] for c in RSSM_SHAPES])
+def test_rssm_shapes(case):
+    name, B, T, S, A, E, Hb, tb, th = case
+    log(f"[gpu] rssm shape {name}")
+    d = synth.make_rssm_inputs(B, T, state_dim=S, action_dim=A, embed_dim=E, belief_dim=Hb,
+                               seed=zlib.crc32(name.encode()) % 1000, s0_std=0.5, h0_std=0.5)
+    got = run_rssm(d, tile_batch=tb, tile_hidden=th)
+    ref = oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"], d["s0"], d["h0"])
+    for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs")):
+        assert_close(g, r, "f32", f"{name} {nm}")
+
+
 def test_rssm_zero_weights_closed_form():
     log("[gpu] rssm closed form")
     d = synth.make_rssm_inputs(6, 4, seed=10, zero_weights=True)
