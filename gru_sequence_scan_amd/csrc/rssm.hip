@@ -34,6 +34,10 @@ constexpr int kThreads = 256;
 constexpr int kMaxRows = 4;  // batch rows per group: one 4x4 MFMA block row set
 
 __host__ __device__ inline int r4(int x) { return (x + 3) & ~3; }
+// Row stride (floats) of an LDS matrix whose rows are read one per lane in
+// 16-byte chunks: an odd number of chunks keeps the 64 lanes of a read on
+// distinct banks.
+__host__ __device__ inline int ld_rows(int x) { return (r4(x) / 4) % 2 == 1 ? r4(x) : r4(x) + 4; }
 
 // acc += sum over 16-byte chunks k4 in [k4a, k4b) of the 4x4x1 MFMA products
 // of X chunk (lane's batch row) and W chunk (lane's output column). One
@@ -185,10 +189,10 @@ struct RssmLds {
 __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   RssmLds L;
   const int SA = a.S + a.A;
-  L.ld_sa = r4(SA);
-  L.ld_e = r4(a.E);
-  L.ld_h = r4(a.Hb);
-  L.ld_hs = r4(a.h_per);
+  L.ld_sa = ld_rows(SA);
+  L.ld_e = ld_rows(a.E);
+  L.ld_h = ld_rows(a.Hb);
+  L.ld_hs = ld_rows(a.h_per);
   L.ld_v = r4(2 * a.S);
   L.ld_g = r4(3 * a.h_per);
   const int R = kMaxRows;
@@ -353,7 +357,7 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
       const float* xr = sm + L.hs + (lane & 3) * L.ld_hs;
       for (int cg = __builtin_amdgcn_readfirstlane(tid >> 6); cg * 64 < E; cg += 4) {
         const int c = cg * 64 + lane;
-        const f32x4 acc = dot_chain(xr, sm + L.w1s + (c < E ? c : E - 1) * L.ld_hs, 0, L.ld_hs / 4,
+        const f32x4 acc = dot_chain(xr, sm + L.w1s + (c < E ? c : E - 1) * L.ld_hs, 0, (hp + 3) / 4,
                                     f32x4{0.f, 0.f, 0.f, 0.f});
         if (c < E) {
 #pragma unroll
@@ -375,7 +379,7 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     //      partial sums; all its loads are issued before the first is used.
     //      Elements past Hb or E (exchange padding nobody writes) read as 0.
     {
-      const int EC = L.ld_e / 4, HC = a.Hbp / 4;
+      const int EC = (E + 3) / 4, HC = a.Hbp / 4;
       const int i = tid;
       if (i < nrows * EC || i < nrows * HC) {
         const bool has_h = i < nrows * HC, has_p = i < nrows * EC;
