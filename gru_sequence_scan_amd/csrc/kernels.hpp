@@ -17,6 +17,7 @@ struct GemmArgs {
   int hh_fold_rows;     // b_hh folded for gate rows < this (G, or 2H for GRU)
   int has_bias;
   int vec_ok;           // A and W rows 16-byte aligned (K * esize % 16 == 0)
+  const void* zero16;   // 16 zero bytes in device memory (stand-in for rows past M or N)
 };
 hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream);
 

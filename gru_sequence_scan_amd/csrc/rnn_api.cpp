@@ -20,6 +20,10 @@ using namespace rnnk;
 namespace {
 
 constexpr size_t kAlign = 256;
+// 16 zero bytes inside the status block of the workspace (cleared at the
+// start of every call, never written afterwards): the GEMM's stand-in for
+// rows past the matrix.
+constexpr size_t kZeroChunk = 128;
 constexpr int kMaxLds = 160 * 1024;
 constexpr int kCounterBytes = 64;
 
@@ -552,6 +556,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
       vec = vec && aligned(w->w_ih[i], 16);
     }
     g.vec_ok = vec;
+    g.zero16 = ws + L.status + kZeroChunk;
     if ((rc = prof.begin(1)) != RNN_OK) return rc;
     if ((rc = hip_status(launch_gemm_xw(g, bf16, st))) != RNN_OK) return rc;
     if ((rc = prof.end()) != RNN_OK) return rc;
