@@ -47,8 +47,18 @@ KERNEL_SOURCES = {
 # the ratio the same counter reads for a plain copy of known size
 # (--calibrate-copy). Valid only for the kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "rssm_b50_t50": {"kernel": "rssm", "fetch_bytes": 269825151, "write_bytes": 36772013,
-                     "sources": "11867ec4abdf93c6"},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 269883029, "write_bytes": 36772025,
+                   "sources": "dc6528ed077676bd"},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1591847, "write_bytes": 209408,
+                  "sources": "34cd963edd4ff325"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484768956, "write_bytes": 137109504,
+                    "sources": "34cd963edd4ff325"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": 1, "fetch_bytes": 612354682, "write_bytes": 100467712,
+                      "sources": "34cd963edd4ff325"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430765179, "write_bytes": 162342912,
+                        "sources": "34cd963edd4ff325"},
+    "lstm_t256_b1_small": {"kernel": "scan", "index": 0, "fetch_bytes": 190530, "write_bytes": 16512,
+                         "sources": "34cd963edd4ff325"},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
@@ -314,7 +324,7 @@ def main():
     traffic = None
     meas = MEASURED_TRAFFIC.get(name)
     digest = sources_digest(dom["kernel"])
-    if meas and meas["kernel"] == dom["kernel"] and meas["sources"] == digest:
+    if meas and (meas["kernel"], meas["index"]) == (dom["kernel"], dom["index"]) and meas["sources"] == digest:
         traffic = meas["fetch_bytes"] + meas["write_bytes"]
     roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
                 "traffic": traffic, "kernel": f"{dom['kernel']}[{dom['index']}]", "avg_us": dom["avg_us"],
