@@ -396,7 +396,8 @@ int plan_rssm(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
       const double macs = 4.0 * (3.0 * h_per * (E + Hb) + (double)E * h_per + (double)E * nw +
                                  2.0 * S * E + (double)E * (S + A));
       const double bytes = (double)rows * (Hb + (double)nw * E) * 4.0;
-      double t = barrier_us(nw) + 0.3 + bytes / 100e3 + macs / 32.0 / 2400.0;
+      // products run on 8 waves: ~64 MAC/clk of the 4x4 MFMA chains (measured)
+      double t = barrier_us(nw) + 0.3 + bytes / 100e3 + macs / 64.0 / 2400.0;
       if (d->placement == 2 && !xcd_aligned) t += 1e3;  // requested: aligned plans first
       if (t < best) {
         best = t;

@@ -30,7 +30,8 @@ namespace rnnk {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kMaxRows = 4;  // batch rows per group: one 4x4 MFMA block row set
 
 __host__ __device__ inline int r4(int x) { return (x + 3) & ~3; }
@@ -70,32 +71,28 @@ __device__ __forceinline__ f32x4 dot_chain(const float* xr, const float* wr, int
   return acc;
 }
 
-// Sum the four waves' K-split partial products (lane = column) held in `red`
-// into out[v * ldo + c], c < N, for the four rows v.
-__device__ __forceinline__ void reduce_waves(const f32x4& acc, float* red, float* out, int ldo, int N) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) red[(wave * 4 + v) * 64 + lane] = acc[v];
-  __syncthreads();
-  for (int i = threadIdx.x; i < 4 * N; i += kThreads) {
-    const int v = i / N, c = i - v * N;
-    out[v * ldo + c] = red[(0 * 4 + v) * 64 + c] + red[(1 * 4 + v) * 64 + c] + red[(2 * 4 + v) * 64 + c] +
-                       red[(3 * 4 + v) * 64 + c];
-  }
-}
-
 struct Plain {
   __device__ float operator()(int, float x) const { return x; }
 };
+
+// Fixed-order sum over the waves of the partials of (row v, column c) that
+// the K-split products leave in `red` (kWaves waves x 4 rows x 64 floats).
+__device__ __forceinline__ float red_sum(const float* red, int v, int c) {
+  float s = red[v * 64 + c];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) s += red[(w * 4 + v) * 64 + c];
+  return s;
+}
 
 // out[v * ldo + c] = epi(c, sum_{k < K} X[v * ldx + k] * W[c * ldw + k]) for
 // all four rows v of X (rows past the group's batch rows hold zeros and are
 // ignored by the callers) and c < N, on v_mfma_f32_4x4x1f32: 16 blocks of
 // 4x4 per instruction, lane l of a pass owning output column 64 * pass + l.
 // X and W rows are 16-byte aligned and zero-padded to a multiple of 4.
-// Narrow products (N <= 64) split K over the four waves and reduce through
-// `red` (4 waves x 4 rows x 64 floats); wider ones give the waves whole
-// 64-column passes.
+// Narrow products (N <= 64) split K over all waves; wider ones give each
+// 64-column pass two waves that split K in halves (or whole passes per wave
+// when there are more passes than wave pairs); partials meet in `red`
+// (kWaves x 4 x 64 floats) and are summed in a fixed order.
 template <typename Epi = Plain>
 __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out, int ldo, int N, int K,
                     float* red, Epi epi = Epi()) {
@@ -104,17 +101,34 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
   const float* xr = X + (lane & 3) * ldx;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   if (N > 64) {
-    for (int cg = __builtin_amdgcn_readfirstlane(wave); cg * 64 < N; cg += 4) {
-      const int c = cg * 64 + lane;
-      const f32x4 acc = dot_chain(xr, W + (c < N ? c : N - 1) * ldw, 0, K4, zero4);
-      if (c < N) {
+    const int npass = (N + 63) >> 6;
+    if (2 * npass > kWaves) {
+      for (int cg = __builtin_amdgcn_readfirstlane(wave); cg < npass; cg += kWaves) {
+        const int c = cg * 64 + lane;
+        const f32x4 acc = dot_chain(xr, W + (c < N ? c : N - 1) * ldw, 0, K4, zero4);
+        if (c < N) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) out[v * ldo + c] = epi(c, acc[v]);
+          for (int v = 0; v < 4; ++v) out[v * ldo + c] = epi(c, acc[v]);
+        }
       }
+      return;
+    }
+    // pass wave / 2, K half wave % 2
+    const int pass = wave >> 1, half = wave & 1, kh = (K4 + 1) >> 1;
+    if (pass < npass) {
+      const int c = pass * 64 + lane;
+      const f32x4 acc = dot_chain(xr, W + (c < N ? c : N - 1) * ldw, half ? kh : 0, half ? K4 : kh, zero4);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[((pass * 2 + half) * 4 + v) * 64 + lane] = acc[v];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 4 * N; i += kThreads) {
+      const int v = i / N, c = i - v * N, p = c >> 6, l = c & 63;
+      out[v * ldo + c] = epi(c, red[((p * 2) * 4 + v) * 64 + l] + red[((p * 2 + 1) * 4 + v) * 64 + l]);
     }
     return;
   }
-  const int per = (K4 + 3) >> 2;
+  const int per = (K4 + kWaves - 1) / kWaves;
   const int ka = min(K4, wave * per), kb = min(K4, ka + per);
   const f32x4 acc = dot_chain(xr, W + (lane < N ? lane : N - 1) * ldw, ka, kb, zero4);
 #pragma unroll
@@ -122,20 +136,19 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
   __syncthreads();
   for (int i = threadIdx.x; i < 4 * N; i += kThreads) {
     const int v = i / N, c = i - v * N;
-    out[v * ldo + c] = epi(c, red[(0 * 4 + v) * 64 + c] + red[(1 * 4 + v) * 64 + c] +
-                                  red[(2 * 4 + v) * 64 + c] + red[(3 * 4 + v) * 64 + c]);
+    out[v * ldo + c] = epi(c, red_sum(red, v, c));
   }
 }
 
 // Two independent narrow products (N1, N2 <= 64) in one K-split pass: their
-// chains interleave, so the second costs little extra latency. The four
-// waves' partial sums are left in red1 / red2 (4 waves x 4 rows x 64 floats)
-// for the caller to reduce after a barrier.
+// chains interleave, so the second costs little extra latency. The waves'
+// partial sums are left in red1 / red2 (kWaves x 4 rows x 64 floats) for the
+// caller to reduce after a barrier.
 __device__ void mv4_pair(const float* X1, int ldx1, const float* W1, int ldw1, int N1, int K1, float* red1,
                          const float* X2, int ldx2, const float* W2, int ldw2, int N2, int K2, float* red2) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int A4 = (K1 + 3) >> 2, B4 = (K2 + 3) >> 2;
-  const int pa = (A4 + 3) >> 2, pb = (B4 + 3) >> 2;
+  const int pa = (A4 + kWaves - 1) / kWaves, pb = (B4 + kWaves - 1) / kWaves;
   const int a0 = min(A4, wave * pa), a1 = min(A4, a0 + pa);
   const int b0 = min(B4, wave * pb), b1 = min(B4, b0 + pb);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -173,10 +186,45 @@ __device__ void mv4_pair(const float* X1, int ldx1, const float* W1, int ldw1, i
   }
 }
 
-// Fixed-order sum of the four waves' partials of output (row v, column c).
-__device__ __forceinline__ float red_sum(const float* red, int v, int c) {
-  return red[(0 * 4 + v) * 64 + c] + red[(1 * 4 + v) * 64 + c] + red[(2 * 4 + v) * 64 + c] +
-         red[(3 * 4 + v) * 64 + c];
+
+// W_hh (owned slice) and W_2 can live in registers when both products are
+// narrow (one 64-column pass) and each wave's share of K fits kRegChunks
+// 16-byte chunks.
+constexpr int kRegChunks = 8;
+__host__ __device__ inline bool rssm_regw(const RssmArgs& a) {
+  const int e4 = (a.E + 3) / 4, h4 = (a.Hb + 3) / 4;
+  return 2 * a.S <= 64 && 3 * a.h_per <= 64 && e4 <= kRegChunks * kWaves && h4 <= kRegChunks * kWaves;
+}
+
+// acc += sum over this wave's chunks [k0, k0 + n) of X chunk (LDS, lane's
+// batch row) times the resident W chunks wr[0 .. n) (lane's column).
+__device__ __forceinline__ f32x4 dot_chain_reg(const float* xr, const f32x4 (&wr)[kRegChunks], int k0, int n,
+                                               f32x4 acc) {
+  n = __builtin_amdgcn_readfirstlane(n);
+  f32x4 x[kRegChunks];
+#pragma unroll
+  for (int q = 0; q < kRegChunks; ++q)
+    if (q < n) x[q] = *reinterpret_cast<const f32x4*>(xr + 4 * (k0 + q));
+#pragma unroll
+  for (int q = 0; q < kRegChunks; ++q)
+    if (q < n) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(x[q][e], wr[q][e], acc, 0, 0, 0);
+    }
+  return acc;
+}
+
+// Resident chunks of W row `row` (or zeros when row < 0) for this wave's
+// share of K4 chunks: wr[q] = W[row][4 (k0 + q) .. + 3], k < K.
+__device__ __forceinline__ void load_wreg(f32x4 (&wr)[kRegChunks], const float* W, int row, int K, int k0, int n) {
+#pragma unroll
+  for (int q = 0; q < kRegChunks; ++q) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 4 * (k0 + q) + e;
+      wr[q][e] = (row >= 0 && q < n && k < K) ? W[(size_t)row * K + k] : 0.f;
+    }
+  }
 }
 
 struct RssmLds {
@@ -200,10 +248,11 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   auto take = [&](int n) { const int at = o; o += r4(n); return at; };
   L.was = take(a.E * L.ld_sa);
   L.bas = take(a.E);
-  L.w2 = take(2 * a.S * L.ld_e);
+  const bool regw = rssm_regw(a);
+  L.w2 = take(regw ? 0 : 2 * a.S * L.ld_e);
   L.b2 = take(2 * a.S);
   L.wih = take(3 * a.h_per * L.ld_e);
-  L.whh = take(3 * a.h_per * L.ld_h);
+  L.whh = take(regw ? 0 : 3 * a.h_per * L.ld_h);
   L.w1s = take(a.E * L.ld_hs);
   L.b1 = take(a.E);
   L.sa = take(R * L.ld_sa);
@@ -214,13 +263,14 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   L.v = take(R * L.ld_v);
   L.gi = take(R * L.ld_g);
   L.gh = take(R * L.ld_g);
-  L.red = take(4 * 4 * 64);
-  L.red2 = take(4 * 4 * 64);
+  L.red = take(kWaves * 4 * 64);
+  L.red2 = take(kWaves * 4 * 64);
   L.flag = take(4);
   L.total = o * 4;
   return L;
 }
 
+template <bool REGW>
 __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   const RssmLds L = rssm_lds(a);
@@ -269,9 +319,11 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     sm[L.bas + i] = a.b_as[i];
     sm[L.b1 + i] = a.b_1[i];
   }
-  for (int i = tid; i < 2 * S * E; i += kThreads) {
-    const int r = i / E, c = i - r * E;
-    sm[L.w2 + r * L.ld_e + c] = a.w_2[i];
+  if (!REGW) {
+    for (int i = tid; i < 2 * S * E; i += kThreads) {
+      const int r = i / E, c = i - r * E;
+      sm[L.w2 + r * L.ld_e + c] = a.w_2[i];
+    }
   }
   for (int i = tid; i < 2 * S; i += kThreads) sm[L.b2 + i] = a.b_2[i];
   // GRU slice: local row q * hp + jj <-> global row q * Hb + j0 + jj
@@ -280,10 +332,25 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     const int q = r / hp, jj = r - q * hp;
     if (jj < hn) sm[L.wih + r * L.ld_e + c] = a.w_ih[(size_t)(q * Hb + j0 + jj) * E + c];
   }
-  for (int i = tid; i < 3 * hp * Hb; i += kThreads) {
-    const int r = i / Hb, c = i - r * Hb;
-    const int q = r / hp, jj = r - q * hp;
-    if (jj < hn) sm[L.whh + r * L.ld_h + c] = a.w_hh[(size_t)(q * Hb + j0 + jj) * Hb + c];
+  if (!REGW) {
+    for (int i = tid; i < 3 * hp * Hb; i += kThreads) {
+      const int r = i / Hb, c = i - r * Hb;
+      const int q = r / hp, jj = r - q * hp;
+      if (jj < hn) sm[L.whh + r * L.ld_h + c] = a.w_hh[(size_t)(q * Hb + j0 + jj) * Hb + c];
+    }
+  }
+  // Resident W_2 and W_hh chunks (REGW): lane c holds row c of each (W_hh:
+  // slice row c = gate q, unit jj) over this wave's share of K.
+  const int wave = tid >> 6, lane = tid & 63;
+  const int E4 = (E + 3) / 4, H4 = (Hb + 3) / 4;
+  const int per_e = (E4 + kWaves - 1) / kWaves, per_h = (H4 + kWaves - 1) / kWaves;
+  const int ke0 = min(E4, wave * per_e), ne = min(E4, ke0 + per_e) - ke0;
+  const int kh0 = min(H4, wave * per_h), nh = min(H4, kh0 + per_h) - kh0;
+  f32x4 w2r[REGW ? kRegChunks : 1], whr[REGW ? kRegChunks : 1];
+  if constexpr (REGW) {
+    load_wreg(w2r, a.w_2, lane < 2 * S ? lane : -1, E, ke0, ne);
+    const int q = lane / hp, jj = lane - q * hp;
+    load_wreg(whr, a.w_hh, (lane < 3 * hp && jj < hn) ? q * Hb + j0 + jj : -1, Hb, kh0, nh);
   }
   // W_1 columns of the slice: w1s[k][jj] = W_1[k][j0 + jj]
   for (int i = tid; i < E * hp; i += kThreads) {
@@ -328,7 +395,18 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
   auto elu_bias = [bas](int c, float x) { return felu(x + bas[c]); };
   mv4(sm + L.sa, L.ld_sa, sm + L.was, L.ld_sa, sm + L.e, L.ld_e, E, SA, red, elu_bias);
   __syncthreads();
-  mv4(sm + L.h, L.ld_h, sm + L.whh, L.ld_h, sm + L.gh, L.ld_g, 3 * hp, Hb, red);
+  if constexpr (REGW) {
+    const f32x4 acc = dot_chain_reg(sm + L.h + (lane & 3) * L.ld_h, whr, kh0, nh, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(wave * 4 + v) * 64 + lane] = acc[v];
+    __syncthreads();
+    for (int i = tid; i < 4 * 3 * hp; i += kThreads) {
+      const int v = i / (3 * hp), c = i - v * (3 * hp);
+      sm[L.gh + v * L.ld_g + c] = red_sum(red, v, c);
+    }
+  } else {
+    mv4(sm + L.h, L.ld_h, sm + L.whh, L.ld_h, sm + L.gh, L.ld_g, 3 * hp, Hb, red);
+  }
   __syncthreads();
 
   unsigned nbar = 0;
@@ -355,7 +433,7 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     {
       const int lane = tid & 63;
       const float* xr = sm + L.hs + (lane & 3) * L.ld_hs;
-      for (int cg = __builtin_amdgcn_readfirstlane(tid >> 6); cg * 64 < E; cg += 4) {
+      for (int cg = __builtin_amdgcn_readfirstlane(tid >> 6); cg * 64 < E; cg += kWaves) {
         const int c = cg * 64 + lane;
         const f32x4 acc = dot_chain(xr, sm + L.w1s + (c < E ? c : E - 1) * L.ld_hs, 0, (hp + 3) / 4,
                                     f32x4{0.f, 0.f, 0.f, 0.f});
@@ -419,7 +497,16 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     // ---- v_t = W_2 u_t and, for the next GRU step, W_hh h_t on the owned
     //      slice, in one K-split pass ----
     const bool pair = 2 * S <= 64 && 3 * hp <= 64;
-    if (pair) {
+    if constexpr (REGW) {
+      // both chains from resident weights, interleaved by the scheduler
+      const f32x4 c1 = dot_chain_reg(sm + L.u + (lane & 3) * L.ld_e, w2r, ke0, ne, f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 c2 = dot_chain_reg(sm + L.h + (lane & 3) * L.ld_h, whr, kh0, nh, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        red[(wave * 4 + v) * 64 + lane] = c1[v];
+        sm[L.red2 + (wave * 4 + v) * 64 + lane] = c2[v];
+      }
+    } else if (pair) {
       mv4_pair(sm + L.u, L.ld_e, sm + L.w2, L.ld_e, 2 * S, E, red, sm + L.h, L.ld_h, sm + L.whh, L.ld_h, 3 * hp, Hb,
                sm + L.red2);
     } else {
@@ -467,10 +554,15 @@ int rssm_max_rows() { return kMaxRows; }
 
 hipError_t launch_rssm(const RssmArgs& a, hipStream_t stream) {
   const int lds = rssm_lds(a).total;
-  hipError_t e = hipFuncSetAttribute((const void*)rssm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const bool regw = rssm_regw(a);
+  const void* fn = regw ? (const void*)rssm_kernel<true> : (const void*)rssm_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int grid = a.gpx > 0 ? a.nxcd * a.gpx * a.nw : a.ngroups * a.nw;
-  hipLaunchKernelGGL(rssm_kernel, dim3(grid), dim3(kThreads), lds, stream, a);
+  if (regw)
+    hipLaunchKernelGGL(rssm_kernel<true>, dim3(grid), dim3(kThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL(rssm_kernel<false>, dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
