@@ -21,7 +21,9 @@ Sources (web pages; cited by title and section):
     projection is an LSTM-only option; with- and without-bias cases).
   * apache/mxnet issue "RNN Op Changes (was: Variable Length Support for cuDNN
     RNN)", opening RFC (per-sequence lengths, sorted packed layout,
-    bidirectional runs that masking cannot fake).
+    bidirectional runs that masking cannot fake) and the later discussion
+    (cell clipping in cuDNN v7.2; requests for state and projection
+    clipping).
   * apache/tvm PR "[TOPI] TE implementation of LSTM using scan", description
     (input-hidden, hidden-hidden and hidden-projection dense ops; the
     recurrence is a true sequential loop).
@@ -37,7 +39,7 @@ tests/test_oracle_pins.py.
 """
 
 from .rnn import (  # noqa: F401
-    sigmoid, elu, softplus, lstm_cell, gru_cell, run_direction, rnn_forward,
+    sigmoid, elu, softplus, clip, lstm_cell, gru_cell, run_direction, rnn_forward,
     pack_sequence, unpack_sequence, packed_offsets, round_to_bf16,
 )
 from .rssm import rssm_prior_step, rssm_prior_unroll  # noqa: F401

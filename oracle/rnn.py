@@ -14,6 +14,12 @@ documented ones:
         m  = sigmoid(o) * tanh(c')
         h' = m                     (plain LSTM)
         h' = W_hr m                (LSTMP; no projection bias)
+  Optional clipping (LSTM, LSTMP), named but not defined by the apache/mxnet
+  issue "RNN Op Changes" (cuDNN's cell clipping; the requests for state and
+  projection clipping). Read as clamps that keep NaN:
+        c' <- clip(c', lo, hi)     after the cell update, before tanh(c');
+                                   the clipped c' is the carried state
+        h' <- clip(W_hr m, -p, p)  (LSTMP, on the projected output)
   GRU   ax = W_ih x + b_ih, ah = W_hh h + b_hh, chunks [r | z | n]
         r = sigmoid(ax_r + ah_r), z = sigmoid(ax_z + ah_z)
         n = tanh(ax_n + r * ah_n)  (reset gate multiplies ah_n incl. b_hn)
@@ -23,7 +29,7 @@ documented ones:
 import numpy as np
 
 __all__ = [
-    "sigmoid", "elu", "softplus", "lstm_cell", "gru_cell", "run_direction",
+    "sigmoid", "elu", "softplus", "clip", "lstm_cell", "gru_cell", "run_direction",
     "rnn_forward", "pack_sequence", "unpack_sequence", "packed_offsets",
     "round_to_bf16",
 ]
@@ -72,11 +78,20 @@ def round_to_bf16(a):
     return out.reshape(np.shape(a))
 
 
-def lstm_cell(x, h, c, w_ih, w_hh, b_ih=None, b_hh=None, w_hr=None, round_m=None):
+def clip(a, lo, hi):
+    """Clamp to [lo, hi] elementwise; NaN stays NaN (np.clip semantics)."""
+    a = np.asarray(a, dtype=np.float64)
+    return np.where(a < lo, lo, np.where(a > hi, hi, a))
+
+
+def lstm_cell(x, h, c, w_ih, w_hh, b_ih=None, b_hh=None, w_hr=None, round_m=None,
+              cell_clip=None, proj_clip=None):
     """One LSTM (or LSTMP when ``w_hr`` is given) step for a batch of rows.
 
     x [B, F], h [B, K], c [B, H]; w_ih [4H, F], w_hh [4H, K], b_* [4H],
     w_hr [P, H]. K = H for LSTM, K = P for LSTMP. Returns (h', c').
+    cell_clip (lo, hi) clamps the updated cell state; proj_clip p clamps
+    the projected output to [-p, p] (LSTMP only).
     LSTMP is "LSTMCell plus one more matmul on the resulting hidden state"
     (pytorch/pytorch issue "Integrating CuDNN API for LSTMs with
     projections", design discussion).
@@ -92,12 +107,19 @@ def lstm_cell(x, h, c, w_ih, w_hh, b_ih=None, b_hh=None, w_hr=None, round_m=None
     g = np.tanh(a[:, 2 * H:3 * H])
     o = sigmoid(a[:, 3 * H:4 * H])
     c_new = f * _f64(c) + i * g
+    if cell_clip is not None:
+        c_new = clip(c_new, cell_clip[0], cell_clip[1])
     m = o * np.tanh(c_new)
     if w_hr is None:
+        if proj_clip is not None:
+            raise ValueError("projection clipping needs a projection")
         return m, c_new
     if round_m is not None:
         m = round_m(m)
-    return m @ _f64(w_hr).T, c_new
+    h_new = m @ _f64(w_hr).T
+    if proj_clip is not None:
+        h_new = clip(h_new, -proj_clip, proj_clip)
+    return h_new, c_new
 
 
 def gru_cell(x, h, w_ih, w_hh, b_ih=None, b_hh=None):
@@ -167,7 +189,8 @@ def unpack_sequence(packed, lengths, T, fill=np.nan):
     return out
 
 
-def run_direction(mode, x, lengths, h0, c0, p, reverse=False, emulate_bf16=False):
+def run_direction(mode, x, lengths, h0, c0, p, reverse=False, emulate_bf16=False,
+                  cell_clip=None, proj_clip=None):
     """Run one layer in one direction over a padded batch.
 
     mode 'lstm' | 'lstmp' | 'gru'; x [T, B, F]; lengths [B] (1 <= L_b <= T);
@@ -175,9 +198,12 @@ def run_direction(mode, x, lengths, h0, c0, p, reverse=False, emulate_bf16=False
     inactive rows neither update nor write (apache/mxnet issue "RNN Op
     Changes", RFC: variable-length sequences that masking cannot fake). In
     reverse, each row starts at its own t = L_b - 1 from h0, c0 (PackedSequence
-    semantics). Returns (out [T, B, K] with NaN where nothing is written,
-    h_last [B, K], c_last [B, H] or None).
+    semantics). cell_clip / proj_clip as in lstm_cell (LSTM and LSTMP only).
+    Returns (out [T, B, K] with NaN where nothing is written, h_last [B, K],
+    c_last [B, H] or None).
     """
+    if mode == "gru" and (cell_clip is not None or proj_clip is not None):
+        raise ValueError("clipping is an LSTM / LSTMP option")
     x = _f64(x)
     T, B = x.shape[0], x.shape[1]
     L = np.full(B, T, dtype=np.int64) if lengths is None else np.asarray(lengths, dtype=np.int64)
@@ -198,7 +224,8 @@ def run_direction(mode, x, lengths, h0, c0, p, reverse=False, emulate_bf16=False
         elif mode in ("lstm", "lstmp"):
             hn, cn = lstm_cell(xt, h[rows], c[rows], p["w_ih"], p["w_hh"], p.get("b_ih"),
                                p.get("b_hh"), p.get("w_hr") if mode == "lstmp" else None,
-                               round_m=round_to_bf16 if emulate_bf16 else None)
+                               round_m=round_to_bf16 if emulate_bf16 else None,
+                               cell_clip=cell_clip, proj_clip=proj_clip)
             c[rows] = cn
         else:
             raise ValueError(f"unknown mode {mode!r}")
@@ -209,7 +236,8 @@ def run_direction(mode, x, lengths, h0, c0, p, reverse=False, emulate_bf16=False
 
 
 def rnn_forward(mode, x, params, *, lengths=None, h0=None, c0=None, num_layers=1,
-                bidirectional=False, proj_size=0, layout="padded", emulate_bf16=False):
+                bidirectional=False, proj_size=0, layout="padded", emulate_bf16=False,
+                cell_clip=None, proj_clip=None):
     """Multi-layer, optionally bidirectional, optionally variable-length forward.
 
     params: list indexed l * D + d of dicts with 'w_ih', 'w_hh', 'b_ih', 'b_hh'
@@ -217,7 +245,8 @@ def rnn_forward(mode, x, params, *, lengths=None, h0=None, c0=None, num_layers=1
     concatenation [forward output ; reverse output] of layer l. h_n and c_n
     are stacked at index l * D + d. layout 'padded': x [T, B, F], y [T, B,
     D * K] with NaN at unwritten positions; layout 'packed': x [N_tok, F],
-    y [N_tok, D * K], lengths sorted non-increasing.
+    y [N_tok, D * K], lengths sorted non-increasing. cell_clip (lo, hi) and
+    proj_clip p as in lstm_cell, applied in every layer and direction.
     Returns (y, h_n [L * D, B, K], c_n [L * D, B, H] or None).
     """
     if mode not in ("lstm", "lstmp", "gru"):
@@ -247,7 +276,8 @@ def rnn_forward(mode, x, params, *, lengths=None, h0=None, c0=None, num_layers=1
             h_init = np.zeros((B, K)) if h0 is None else _f64(h0)[idx]
             c_init = None if mode == "gru" else (np.zeros((B, H)) if c0 is None else _f64(c0)[idx])
             out, h_last, c_last = run_direction(mode, inp, lengths, h_init, c_init, params[idx],
-                                                reverse=(d == 1), emulate_bf16=emulate_bf16)
+                                                reverse=(d == 1), emulate_bf16=emulate_bf16,
+                                                cell_clip=cell_clip, proj_clip=proj_clip)
             outs.append(out)
             hn[idx] = h_last
             if cn is not None:

@@ -481,3 +481,119 @@ def test_bf16_state_rounding_stays_inside_tolerance(mode, H, P, T, L):
     ye, hne, cne = _oracle_run(mode, d, emulate_bf16=True)
     assert np.max(np.abs(ye - y)) < 5e-3
     assert np.max(np.abs(hne - hn)) < 5e-3
+
+
+# ---------------------------------------------------------------------------
+# Cell and projection clipping (LSTM, LSTMP). The apache/mxnet issue "RNN Op
+# Changes" names cuDNN's cell clipping and asks for state and projection
+# clipping without defining them; the oracle reads them as clamps of the
+# updated cell state (carried forward) and of the projected output.
+# ---------------------------------------------------------------------------
+
+def _gate_bias_case(mode, H, P=0, F=None, T=5, B=1, seed=40):
+    F = F or H
+    d = _rand_case(mode, T=T, B=B, F=F, H=H, P=P, seed=seed, h0=False)
+    p = d["params"][0]
+    for k in p:
+        p[k] = np.zeros(np.shape(p[k]), dtype=np.float64)  # exact float64 gate values
+    return d, p
+
+
+def test_cell_clip_recursion_closed_form():
+    # i = sigmoid(40) = 1 (to double precision), f = sigmoid(0) = 1/2,
+    # g = tanh(atanh(-1/2)) = -1/2, o = 1/2, c0 = 4: the carried state obeys
+    # c_t = clip(c_{t-1} / 2 - 1/2, lo, hi) and h_t = tanh(c_t) / 2. Clipping
+    # only the output (not the carried state) would give c_2 = 1/4 here.
+    H, T, lo, hi = 1, 6, -0.7, 1.0
+    d, p = _gate_bias_case("lstm", H, T=T)
+    p["b_ih"][0] = 40.0
+    p["b_ih"][2] = math.atanh(-0.5)
+    d["c0"] = np.full((1, 1, H), 4.0)
+    y, hn, cn = _oracle_run("lstm", d, cell_clip=(lo, hi))
+    c = 4.0
+    for t in range(T):
+        c = min(max(c / 2.0 - 0.5, lo), hi)
+        np.testing.assert_allclose(y[t, 0, 0], 0.5 * math.tanh(c), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(cn[0, 0, 0], c, rtol=1e-14, atol=1e-15)
+    assert c == lo  # the lower bound is reached and held
+
+
+def test_cell_clip_per_unit_bounds():
+    # f = 0, i = 1: c_t = g = tanh(b_g) per unit each step; clip bounds cut
+    # the units above hi and below lo, the others pass through.
+    gs = np.array([0.9, -0.9, 0.1, -0.2])
+    H = gs.size
+    d, p = _gate_bias_case("lstm", H, T=3)
+    p["b_ih"][0:H] = 40.0
+    p["b_ih"][H:2 * H] = -40.0
+    p["b_ih"][2 * H:3 * H] = np.arctanh(gs)
+    y, hn, cn = _oracle_run("lstm", d, cell_clip=(-0.5, 0.25))
+    want_c = np.array([0.25, -0.5, 0.1, -0.2])
+    np.testing.assert_allclose(cn[0, 0], want_c, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(y[2, 0], 0.5 * np.tanh(want_c), rtol=1e-14, atol=1e-15)
+
+
+def test_projection_clip_scalar_brute_force():
+    # P = H = F = 1. i = 1, f = 0, o = 1/2; W_ih(g) = 1 reads x, W_hh(g) = 1
+    # reads the previous projected output, W_hr = 10. Then per step
+    #   u_t = x_t + h_{t-1},  c_t = tanh(u_t),  h_t = clip(5 tanh(c_t), -p, p),
+    # so a clipped output that is not fed back would change u_{t+1}.
+    T, pc = 5, 1.5
+    d, p = _gate_bias_case("lstmp", 1, P=1, F=1, T=T)
+    p["b_ih"][0], p["b_ih"][1] = 40.0, -40.0
+    p["w_ih"][2, 0] = 1.0
+    p["w_hh"][2, 0] = 1.0
+    p["w_hr"][0, 0] = 10.0
+    xs = [0.8, -0.05, -3.0, 0.0, 0.3]
+    d["x"] = np.array(xs, dtype=np.float64).reshape(T, 1, 1)
+    y, hn, cn = _oracle_run("lstmp", d, proj_clip=pc)
+    h, hits = 0.0, 0
+    for t in range(T):
+        v = 5.0 * math.tanh(math.tanh(xs[t] + h))
+        hits += abs(v) > pc
+        h = min(max(v, -pc), pc)
+        np.testing.assert_allclose(y[t, 0, 0], h, rtol=1e-14, atol=1e-15)
+    assert hits >= 2
+
+
+def test_projection_clip_per_unit_closed_form():
+    # W_hr = 10 I, W_hh = 0, i = 1, f = 0, o = 1/2, c = g: h = clip(5 tanh(g)).
+    gs = np.array([0.9, -0.9, 0.1, -0.2])
+    H = gs.size
+    d, p = _gate_bias_case("lstmp", H, P=H, T=2)
+    p["b_ih"][0:H] = 40.0
+    p["b_ih"][H:2 * H] = -40.0
+    p["b_ih"][2 * H:3 * H] = np.arctanh(gs)
+    p["w_hr"] = 10.0 * np.eye(H)
+    y, hn, cn = _oracle_run("lstmp", d, proj_clip=2.0)
+    raw = 5.0 * np.tanh(gs)
+    np.testing.assert_allclose(hn[0, 0], np.minimum(np.maximum(raw, -2.0), 2.0), rtol=1e-14, atol=1e-15)
+    assert np.abs(raw).max() > 2.0 and np.abs(raw).min() < 2.0
+
+
+@pytest.mark.parametrize("mode,P", [("lstm", 0), ("lstmp", 3)])
+def test_infinite_clip_bounds_change_nothing(mode, P):
+    d = _rand_case(mode, T=6, B=3, F=5, H=4, P=P, L=2, bidir=True, lengths=[6, 4, 2], seed=41)
+    ref = _oracle_run(mode, d)
+    kw = dict(cell_clip=(-np.inf, np.inf))
+    if P:
+        kw["proj_clip"] = np.inf
+    got = _oracle_run(mode, d, **kw)
+    for a, b in zip(ref, got):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_clip_keeps_nan_like_numpy():
+    rng = np.random.default_rng(42)
+    a = rng.normal(size=200) * 3
+    a[::17] = np.nan
+    np.testing.assert_array_equal(oracle.clip(a, -1.25, 0.5), np.clip(a, -1.25, 0.5))
+
+
+def test_clipping_outside_lstm_is_rejected():
+    d = _rand_case("gru", T=3, B=2, F=3, H=2, seed=43)
+    with pytest.raises(ValueError):
+        _oracle_run("gru", d, cell_clip=(-1.0, 1.0))
+    d = _rand_case("lstm", T=3, B=2, F=3, H=2, seed=43)
+    with pytest.raises(ValueError):
+        _oracle_run("lstm", d, proj_clip=1.0)
