@@ -16,4 +16,5 @@ from .binding import (  # noqa: F401
     RNN_ABI_VERSION, RnnDesc, RnnWeights, RnnIO, RnnError, lib, lib_path,
     rnn_abi_version, rnn_strerror, rnn_workspace_bytes, rnn_forward_raw, rnn_read_status,
     rnn_device_check, rnn_forward, rssm_prior_unroll, rnn_plan_info, MODES, STATUS,
+    CLIP_CELL, CLIP_PROJ,
 )

@@ -12,7 +12,7 @@ import os
 
 import torch
 
-RNN_ABI_VERSION = 1
+RNN_ABI_VERSION = 2
 RNN_MAX_LAYERS = 8
 RNN_MAX_LD = 2 * RNN_MAX_LAYERS
 
@@ -24,6 +24,8 @@ STATUS = {
     -4: "RNN_E_LENGTHS", -5: "RNN_E_WORKSPACE", -6: "RNN_E_ALIGN", -7: "RNN_E_DEVICE",
     -8: "RNN_E_HIP", -9: "RNN_E_TIMEOUT", -10: "RNN_E_PLAN",
 }
+
+CLIP_CELL, CLIP_PROJ = 1, 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 
@@ -42,7 +44,9 @@ class RnnDesc(ctypes.Structure):
         ("action_dim", ctypes.c_int32), ("embed_dim", ctypes.c_int32),
         ("belief_dim", ctypes.c_int32), ("scale_lb", ctypes.c_float),
         ("tile_batch", ctypes.c_int32), ("tile_hidden", ctypes.c_int32),
-        ("placement", ctypes.c_int32), ("weights", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4),
+        ("placement", ctypes.c_int32), ("weights", ctypes.c_int32),
+        ("clip", ctypes.c_int32), ("cell_clip_lo", ctypes.c_float), ("cell_clip_hi", ctypes.c_float),
+        ("proj_clip", ctypes.c_float), ("reserved", ctypes.c_int32 * 4),
     ]
 
 
@@ -229,7 +233,8 @@ def _call(desc, w, io, lengths, device, keep):
 
 def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padded",
                 num_layers=1, bidirectional=False, proj_size=0, hidden_size=None, y_out=None,
-                tile_batch=0, tile_hidden=0, placement=0, weights=0, return_workspace=False):
+                tile_batch=0, tile_hidden=0, placement=0, weights=0, cell_clip=None, proj_clip=None,
+                return_workspace=False):
     """Forward of an LSTM / GRU / LSTMP stack on the current HIP stream.
 
     x: padded [T, B, F] or packed [N_tok, F] (float32 or bfloat16, on a GPU).
@@ -237,6 +242,8 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     'w_hh' [G, K], optional 'b_ih', 'b_hh' [G] and, for LSTMP, 'w_hr' [P, H].
     lengths: host sequence of B ints (required for packed; for padded it
     masks rows, which are then never written past their length).
+    cell_clip: c (clamp to [-c, c]) or (lo, hi), clamps the updated LSTM cell
+    state; proj_clip: p, clamps the LSTMP projected output to [-p, p].
     Returns (y, h_n, c_n) with c_n None for GRU.
     """
     mode = mode.lower()
@@ -304,6 +311,13 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     desc.num_layers, desc.bidirectional, desc.has_bias = num_layers, int(bidirectional), int(has_bias)
     desc.tile_batch, desc.tile_hidden, desc.placement = tile_batch, tile_hidden, placement
     desc.weights = weights
+    if cell_clip is not None:
+        lo, hi = (-cell_clip, cell_clip) if isinstance(cell_clip, (int, float)) else cell_clip
+        desc.clip |= CLIP_CELL
+        desc.cell_clip_lo, desc.cell_clip_hi = float(lo), float(hi)
+    if proj_clip is not None:
+        desc.clip |= CLIP_PROJ
+        desc.proj_clip = float(proj_clip)
     io = RnnIO()
     io.x = _ptr(x)
     keep_len, io.lengths_host = _len_ptr(lengths)

@@ -133,6 +133,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
+// Clamp to [lo, hi] by comparisons, so NaN passes through (a min/max pair
+// would replace it by a bound). Infinite bounds make it the identity.
+__device__ __forceinline__ float clampf(float x, float lo, float hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
 // Logistic function with the hardware reciprocal (about 1 ulp): exp2 of a
 // large argument gives +inf and rcp(inf) = 0, so both tails are exact.
 __device__ __forceinline__ float fsigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + fexp(-x)); }

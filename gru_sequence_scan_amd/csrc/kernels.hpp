@@ -52,6 +52,9 @@ struct ScanArgs {
   // per wave, pks waves splitting K, pcpt chunks each; pnt = 0: whole tiles
   // per wave without a K split.
   int pnt, pks, pcpt;
+  // Clamp bounds of the updated cell state and of the projected output
+  // (infinite when that clipping is off); NaN passes through.
+  float c_lo, c_hi, p_lo, p_hi;
   // per direction tensors (already offset to this layer)
   const void* w_hh[2];
   const void* w_hr[2];

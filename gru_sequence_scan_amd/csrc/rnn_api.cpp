@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <limits>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -86,11 +87,19 @@ int validate_desc(const RnnDesc* d) {
     if (!d->has_bias) return RNN_E_UNSUPPORTED;
     if (d->state_dim < 1 || d->action_dim < 1 || d->embed_dim < 1 || d->belief_dim < 1) return RNN_E_SHAPE;
     if (!std::isfinite(d->scale_lb)) return RNN_E_SHAPE;
+    if (d->clip != 0) return RNN_E_UNSUPPORTED;
     const double big = (double)d->B * d->T * std::max({d->state_dim, d->belief_dim, d->action_dim});
     if (big > 2e9) return RNN_E_SHAPE;
     return RNN_OK;
   }
   if (!is_rnn_mode(d->mode)) return RNN_E_UNSUPPORTED;
+  if (d->clip & ~(RNN_CLIP_CELL | RNN_CLIP_PROJ)) return RNN_E_UNSUPPORTED;
+  if ((d->clip & RNN_CLIP_CELL) && d->mode == RNN_MODE_GRU) return RNN_E_UNSUPPORTED;
+  if ((d->clip & RNN_CLIP_PROJ) && d->mode != RNN_MODE_LSTMP) return RNN_E_UNSUPPORTED;
+  if ((d->clip & RNN_CLIP_CELL) &&
+      (std::isnan(d->cell_clip_lo) || std::isnan(d->cell_clip_hi) || !(d->cell_clip_lo <= d->cell_clip_hi)))
+    return RNN_E_SHAPE;
+  if ((d->clip & RNN_CLIP_PROJ) && !(d->proj_clip >= 0.f)) return RNN_E_SHAPE;
   if (d->layout != RNN_LAYOUT_PADDED && d->layout != RNN_LAYOUT_PACKED) return RNN_E_UNSUPPORTED;
   if ((d->mode == RNN_MODE_LSTMP) != (d->proj_size > 0)) return RNN_E_UNSUPPORTED;
   if (d->proj_size < 0) return RNN_E_SHAPE;
@@ -572,6 +581,12 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     a.nxcd = xcds; a.gpx = p.gpx;
     a.wreg = p.wreg; a.rnt = p.rnt; a.rks = p.rks; a.rcpt = p.rcpt;
     a.pnt = p.pnt; a.pks = p.pks; a.pcpt = p.pcpt;
+    const float inf = std::numeric_limits<float>::infinity();
+    const bool cclip = d->clip & RNN_CLIP_CELL, pclip = d->clip & RNN_CLIP_PROJ;
+    a.c_lo = cclip ? d->cell_clip_lo : -inf;
+    a.c_hi = cclip ? d->cell_clip_hi : inf;
+    a.p_lo = pclip ? -d->proj_clip : -inf;
+    a.p_hi = pclip ? d->proj_clip : inf;
     for (int di = 0; di < m.D; ++di) {
       const int i = l * m.D + di;
       a.w_hh[di] = w->w_hh[i];

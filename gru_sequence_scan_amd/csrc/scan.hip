@@ -684,7 +684,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const float fg = fsigmoid(gxv[i][1] + ar[a.hs + u]);
         const float gg = ftanh(gxv[i][2] + ar[2 * a.hs + u]);
         const float og = fsigmoid(gxv[i][3] + ar[3 * a.hs + u]);
-        const float c = fg * creg[i] + ig * gg;
+        const float c = clampf(fg * creg[i] + ig * gg, a.c_lo, a.c_hi);
         const float m = og * ftanh(c);
         creg[i] = c;
         hreg[i] = m;
@@ -745,7 +745,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const int b = b0 + r;
         if (p >= ps_act || b >= a.B) continue;
         if (t >= len_of(b)) continue;
-        coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, p0 + p), acc[r * L.acc_ld + p]);
+        coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, p0 + p), clampf(acc[r * L.acc_ld + p], a.p_lo, a.p_hi));
       }
       ++nbar;
       group_arrive(counter);
@@ -758,7 +758,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         const int lb = len_of(b);
         if (t >= lb) continue;
         const bool last = rev ? (t == 0) : (t == lb - 1);
-        const DT h = from_f32<DT>(acc[r * L.acc_ld + p]);
+        const DT h = from_f32<DT>(clampf(acc[r * L.acc_ld + p], a.p_lo, a.p_hi));
         yout[(size_t)(rowbase + b) * DK + d * a.K + p0 + p] = h;
         if (last && hn) hn[(size_t)b * a.K + p0 + p] = h;
       }

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define RNN_ABI_VERSION 1
+#define RNN_ABI_VERSION 2
 #define RNN_MAX_LAYERS 8
 #define RNN_MAX_LD (2 * RNN_MAX_LAYERS) /* layers x directions */
 
@@ -88,7 +88,8 @@ typedef enum RnnStatus {
   RNN_E_SHAPE = -2,       /* a size is out of range or inconsistent            */
   RNN_E_UNSUPPORTED = -3, /* combination not defined: projection outside LSTMP,
                              LSTMP without projection, bidirectional or
-                             multi-layer RSSM, RSSM in bf16, ...               */
+                             multi-layer RSSM, RSSM in bf16, clipping outside
+                             LSTM / LSTMP, ...                                 */
   RNN_E_LENGTHS = -4,     /* a length outside [1, T], or packed lengths not
                              sorted non-increasing                             */
   RNN_E_WORKSPACE = -5,   /* workspace NULL or smaller than required           */
@@ -135,8 +136,30 @@ typedef struct RnnDesc {
                             XCD when it fits                                  */
   int32_t weights;       /* scan W_hh slice: 0 automatic; 1 in LDS; 2 in
                             registers when a layout fits (else LDS)           */
+  /* Clipping, LSTM and LSTMP only (apache/mxnet issue "RNN Op Changes",
+   * discussion: cuDNN's cell clipping and the requests for state and
+   * projection clipping; the pages name these without a formula, read here
+   * as clamps). Bits of `clip`:
+   *   RNN_CLIP_CELL  each updated cell state c_t is clamped to
+   *                  [cell_clip_lo, cell_clip_hi] before tanh(c_t); the
+   *                  clamped value is carried to the next step and is what
+   *                  c_n reports.
+   *   RNN_CLIP_PROJ  (LSTMP) each projected output h_t = W_hr m_t is clamped
+   *                  to [-proj_clip, proj_clip]; the clamped value is the
+   *                  output and the next step's recurrent input.
+   * NaN passes through both clamps. Requirements: cell_clip_lo <=
+   * cell_clip_hi, proj_clip >= 0, none NaN (infinite bounds are allowed);
+   * otherwise RNN_E_SHAPE. A bit set for a mode without the quantity is
+   * RNN_E_UNSUPPORTED; the float fields are ignored when their bit is clear. */
+  int32_t clip;
+  float cell_clip_lo;
+  float cell_clip_hi;
+  float proj_clip;
   int32_t reserved[4];   /* must be zero                                       */
 } RnnDesc;
+
+#define RNN_CLIP_CELL 1
+#define RNN_CLIP_PROJ 2
 
 /* Weights, PyTorch shapes and meaning. Index i = layer * D + direction
  * (direction 0 forward, 1 reverse). G = 4H (LSTM, LSTMP) or 3H (GRU);

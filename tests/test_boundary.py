@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert gss.rnn_abi_version() == gss.RNN_ABI_VERSION == 1
+    assert gss.rnn_abi_version() == gss.RNN_ABI_VERSION == 2
     for code in range(-10, 1):
         s = gss.rnn_strerror(code)
         assert isinstance(s, str) and s
@@ -59,6 +59,8 @@ int main(void) {
   printf("%zu %zu %zu\n", sizeof(RnnDesc), sizeof(RnnWeights), sizeof(RnnIO));
   printf("%zu %zu %zu %zu\n", offsetof(RnnDesc, scale_lb), offsetof(RnnDesc, tile_batch),
          offsetof(RnnWeights, w_as), offsetof(RnnIO, beliefs));
+  printf("%zu %zu %zu %d %d\n", offsetof(RnnDesc, clip), offsetof(RnnDesc, proj_clip),
+         offsetof(RnnDesc, reserved), RNN_CLIP_CELL, RNN_CLIP_PROJ);
   return 0;
 }
 ''')
@@ -73,6 +75,10 @@ int main(void) {
     assert sizes[4] == gss.RnnDesc.tile_batch.offset
     assert sizes[5] == gss.RnnWeights.w_as.offset
     assert sizes[6] == gss.RnnIO.beliefs.offset
+    assert sizes[7] == gss.RnnDesc.clip.offset
+    assert sizes[8] == gss.RnnDesc.proj_clip.offset
+    assert sizes[9] == gss.RnnDesc.reserved.offset
+    assert (sizes[10], sizes[11]) == (gss.CLIP_CELL, gss.CLIP_PROJ)
 
 
 def _desc(**kw):
@@ -126,6 +132,31 @@ def test_workspace_validation(lib, kw, lengths, expect):
     assert st == expect, gss.rnn_strerror(st)
     if st == OK:
         assert n > 0
+
+
+INF, NAN = float("inf"), float("nan")
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({"clip": 1, "cell_clip_lo": -1.0, "cell_clip_hi": 1.0}, OK),
+    ({"clip": 1, "cell_clip_lo": -INF, "cell_clip_hi": 0.5}, OK),
+    ({"clip": 1, "cell_clip_lo": 0.25, "cell_clip_hi": 0.25}, OK),
+    ({"mode": 2, "proj_size": 8, "clip": 3, "cell_clip_lo": -2.0, "cell_clip_hi": 2.0, "proj_clip": 0.5}, OK),
+    ({"mode": 2, "proj_size": 8, "clip": 2, "proj_clip": INF}, OK),
+    ({"clip": 1, "cell_clip_lo": 1.0, "cell_clip_hi": -1.0}, E_SHAPE),    # lo > hi
+    ({"clip": 1, "cell_clip_lo": NAN, "cell_clip_hi": 1.0}, E_SHAPE),
+    ({"mode": 2, "proj_size": 8, "clip": 2, "proj_clip": -0.5}, E_SHAPE),
+    ({"mode": 2, "proj_size": 8, "clip": 2, "proj_clip": NAN}, E_SHAPE),
+    ({"mode": 1, "clip": 1, "cell_clip_lo": -1.0, "cell_clip_hi": 1.0}, E_UNSUPPORTED),  # GRU has no cell
+    ({"clip": 2, "proj_clip": 1.0}, E_UNSUPPORTED),                                     # LSTM has no projection
+    ({"clip": 4}, E_UNSUPPORTED),
+    ({"mode": 3, "layout": 2, "state_dim": 20, "action_dim": 6, "embed_dim": 200, "belief_dim": 200,
+      "clip": 1, "cell_clip_lo": -1.0, "cell_clip_hi": 1.0}, E_UNSUPPORTED),
+    ({"clip": 0, "cell_clip_lo": NAN, "proj_clip": NAN}, OK),                          # ignored when off
+])
+def test_clip_validation(lib, kw, expect):
+    st, _ = _ws(_desc(**kw))
+    assert st == expect, gss.rnn_strerror(st)
 
 
 def test_reserved_fields_must_be_zero(lib):

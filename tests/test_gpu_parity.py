@@ -97,6 +97,38 @@ def test_register_layouts(case):
     _compare(d, got, _oracle(d), name)
 
 
+CLIP_CASES = [
+    # name, mode, dtype, T, B, F, H, P, L, bidir, layout, varlen, cell_clip, proj_clip
+    ("clip_lstm_mfma", "lstm", "f32", 11, 37, 40, 72, 0, 1, False, "padded", None, (-0.3, 0.45), None),
+    ("clip_lstm_valu", "lstm", "f32", 9, 5, 24, 40, 0, 2, False, "padded", None, 0.35, None),
+    ("clip_lstm_solo", "lstm", "f32", 20, 1, 8, 16, 0, 1, False, "padded", None, (-0.5, 0.2), None),
+    ("clip_lstmp_bf16", "lstmp", "bf16", 10, 33, 40, 128, 40, 2, False, "padded", None, 0.4, 0.1),
+    ("clip_bilstmp_packed", "lstmp", "f32", 12, 17, 16, 48, 16, 2, True, "packed", (1, 12), (-0.25, 0.6), 0.15),
+    ("clip_lstmp_proj_only", "lstmp", "f32", 9, 20, 24, 64, 24, 1, False, "padded", None, None, 0.12),
+]
+
+
+@pytest.mark.parametrize("case", CLIP_CASES, ids=[c[0] for c in CLIP_CASES])
+def test_clipping(case):
+    """Cell-state and projection clipping against the oracle, with weights
+    large enough that the clamps bind on many elements."""
+    name, mode, dt, T, B, F, H, P, L, bidir, layout, varlen, cc, pc = case
+    log(f"[gpu] clipping case {name}")
+    d = synth.make_rnn_inputs(mode, T, B, F, H, proj_size=P, num_layers=L, bidirectional=bidir,
+                              dtype=dt, layout=layout, varlen=varlen, w_scale=2.0 / np.sqrt(H),
+                              seed=zlib.crc32(name.encode()) % 1000, h0_std=0.3, c0_std=0.3)
+    lohi = None if cc is None else ((-cc, cc) if isinstance(cc, float) else cc)
+    ref = _oracle(d, cell_clip=lohi, proj_clip=pc)
+    # the clamps must actually bind somewhere, else the case tests nothing
+    if lohi is not None:
+        assert np.isin(ref[2], lohi).mean() > 0.02
+    if pc is not None:
+        y = ref[0][~np.isnan(ref[0])]
+        assert (np.abs(y) == pc).mean() > 0.02
+    got = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc)
+    _compare(d, got, ref, name)
+
+
 def test_padding_sentinel_untouched():
     log("[gpu] padding sentinel")
     lengths = np.array([5, 9, 2, 9, 1, 7, 3, 8], dtype=np.int32)
