@@ -15,7 +15,8 @@ one timestep at a time, with the input projection computed inside the step
 
 Sources (web pages; cited by title and section):
   * pytorch/rl issue "[Feature Request] CUDNN version of RSSM", Solution
-    (the RSSMPrior module and the first unroll loop, actions given).
+    (the RSSMPrior module, the first unroll loop with actions given, and the
+    second with an actor computing each action on the fly).
   * pytorch/pytorch issue "Integrating CuDNN API for LSTMs with projections"
     (LSTM with projections = LSTMCell plus one matmul on the hidden output;
     projection is an LSTM-only option; with- and without-bias cases).
@@ -42,4 +43,4 @@ from .rnn import (  # noqa: F401
     sigmoid, elu, softplus, clip, lstm_cell, gru_cell, run_direction, rnn_forward,
     pack_sequence, unpack_sequence, packed_offsets, round_to_bf16,
 )
-from .rssm import rssm_prior_step, rssm_prior_unroll  # noqa: F401
+from .rssm import rssm_prior_step, rssm_prior_unroll, actor_mlp, rssm_actor_unroll  # noqa: F401

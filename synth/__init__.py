@@ -20,6 +20,9 @@ Workloads (named by what they are):
                    fp32, B=64, L_b ~ U{50..500} sorted descending, in 256,
                    hidden 512 per direction
   lstm_t256_b1_small  the TVM thread's second shape: T=256, B=1, in 16, h 16
+  rssm_actor_b50_h50  the same issue's second unroll: the RSSM prior with a
+                   synthetic actor (hidden 200) choosing each action from
+                   the previous state and belief, B=50, horizon 50
 
 Draw order per workload (one ``np.random.default_rng(seed)``): lengths (var-len
 only); weights in parameter order (layer-major, forward before reverse; w_ih,
@@ -62,6 +65,7 @@ class Spec:
     action_dim: int = 0
     embed_dim: int = 0
     belief_dim: int = 0
+    actor_dim: int = 0
     extra: dict = field(default_factory=dict)
 
     @property
@@ -84,6 +88,9 @@ WORKLOADS = {
                               varlen=(50, 500), w_scale=1.0 / np.sqrt(512.0), seed=1005),
     "lstm_t256_b1_small": Spec("lstm_t256_b1_small", "lstm", "f32", T=256, B=1, input_size=16,
                                hidden_size=16, w_scale=0.25, seed=1006),
+    "rssm_actor_b50_h50": Spec("rssm_actor_b50_h50", "rssm_actor", "f32", T=50, B=50, layout="batch_major",
+                               state_dim=20, action_dim=6, embed_dim=200, belief_dim=200, actor_dim=200,
+                               seed=1007),
 }
 
 # The five headline workloads in their conventional order (1-based index).
@@ -200,13 +207,17 @@ def make_rnn_inputs(mode, T, B, input_size, hidden_size, *, proj_size=0, num_lay
 
 
 def make_rssm_inputs(B, T, *, state_dim=20, action_dim=6, embed_dim=200, belief_dim=200,
-                     seed=0, s0_std=0.0, h0_std=0.0, zero_weights=False):
+                     seed=0, s0_std=0.0, h0_std=0.0, zero_weights=False, actor_dim=0):
     """Draw one RSSM-prior unroll problem (float32).
 
     Every Linear and GRUCell parameter is U(-1/sqrt(fan_in), 1/sqrt(fan_in))
     as PyTorch initialises them (GRUCell uses 1/sqrt(hidden)). Order: w_as,
     b_as, w_ih, w_hh, b_ih, b_hh, w_1, b_1, w_2, b_2, then actions ~ U(-1, 1)
     [B, T, A], eps ~ N(0, 1) [B, T, S].
+    actor_dim > 0: the unroll with an actor in the loop (horizon T). The
+    actor's w_a1 [actor_dim, S + Hb], b_a1, w_a2 [A, actor_dim], b_a2 are
+    drawn after the prior's parameters (same init rule), then eps; no
+    actions are drawn ("actions" is None).
     """
     rng = np.random.default_rng(seed)
     S, A, E, Hb = state_dim, action_dim, embed_dim, belief_dim
@@ -224,6 +235,16 @@ def make_rssm_inputs(B, T, *, state_dim=20, action_dim=6, embed_dim=200, belief_
     }
     if zero_weights:
         w = {k: np.zeros_like(v) for k, v in w.items()}
+    if actor_dim > 0:
+        Ea = actor_dim
+        aw = {"w_a1": u((Ea, S + Hb), S + Hb), "b_a1": u((Ea,), S + Hb),
+              "w_a2": u((A, Ea), Ea), "b_a2": u((A,), Ea)}
+        eps = rng.normal(0.0, 1.0, (B, T, S)).astype(np.float32)
+        s0 = rng.normal(0.0, s0_std, (B, S)).astype(np.float32) if s0_std > 0 else None
+        h0 = rng.normal(0.0, h0_std, (B, Hb)).astype(np.float32) if h0_std > 0 else None
+        return {"mode": "rssm_actor", "B": B, "T": T, "state_dim": S, "action_dim": A, "embed_dim": E,
+                "belief_dim": Hb, "actor_dim": Ea, "weights": w, "actor": aw, "actions": None,
+                "eps": eps, "s0": s0, "h0": h0, "dtype": "f32"}
     actions = rng.uniform(-1.0, 1.0, (B, T, A)).astype(np.float32)
     eps = rng.normal(0.0, 1.0, (B, T, S)).astype(np.float32)
     s0 = rng.normal(0.0, s0_std, (B, S)).astype(np.float32) if s0_std > 0 else None
@@ -237,9 +258,10 @@ def make_inputs(name_or_index, seed=None):
     """Inputs of a named workload (see the module docstring)."""
     s = spec(name_or_index)
     sd = s.seed if seed is None else seed
-    if s.mode == "rssm":
+    if s.mode in ("rssm", "rssm_actor"):
         return make_rssm_inputs(s.B, s.T, state_dim=s.state_dim, action_dim=s.action_dim,
-                                embed_dim=s.embed_dim, belief_dim=s.belief_dim, seed=sd)
+                                embed_dim=s.embed_dim, belief_dim=s.belief_dim, seed=sd,
+                                actor_dim=s.actor_dim)
     return make_rnn_inputs(s.mode, s.T, s.B, s.input_size, s.hidden_size, proj_size=s.proj_size,
                            num_layers=s.num_layers, bidirectional=s.bidirectional, dtype=s.dtype,
                            layout=s.layout, varlen=s.varlen, w_scale=s.w_scale,

@@ -453,6 +453,95 @@ def test_rssm_time_chunking_and_single_step():
 
 
 # ---------------------------------------------------------------------------
+# RSSM prior with an actor in the loop (the issue's second unroll; the actor
+# is the synthetic MLP tanh(W_a2 ELU(W_a1 [s; h] + b_a1) + b_a2))
+# ---------------------------------------------------------------------------
+
+def _torch_rssm_actor(w, aw, eps, s0=None, h0=None):
+    """The second unroll written with PyTorch modules in float64."""
+    E, SA = w["w_as"].shape
+    Hb = w["w_hh"].shape[1]
+    S2 = w["w_2"].shape[0]
+    Ea, SH = aw["w_a1"].shape
+    A = aw["w_a2"].shape[0]
+    lin_as = torch.nn.Linear(SA, E)
+    gru = torch.nn.GRUCell(E, Hb)
+    lin1 = torch.nn.Linear(Hb, w["w_1"].shape[0])
+    lin2 = torch.nn.Linear(w["w_1"].shape[0], S2)
+    actor = torch.nn.Sequential(torch.nn.Linear(SH, Ea), torch.nn.ELU(), torch.nn.Linear(Ea, A), torch.nn.Tanh())
+    with torch.no_grad():
+        for mod, wk, bk in ((lin_as, "w_as", "b_as"), (lin1, "w_1", "b_1"), (lin2, "w_2", "b_2")):
+            mod.weight.copy_(torch.tensor(w[wk]))
+            mod.bias.copy_(torch.tensor(w[bk]))
+        actor[0].weight.copy_(torch.tensor(aw["w_a1"]))
+        actor[0].bias.copy_(torch.tensor(aw["b_a1"]))
+        actor[2].weight.copy_(torch.tensor(aw["w_a2"]))
+        actor[2].bias.copy_(torch.tensor(aw["b_a2"]))
+        gru.weight_ih.copy_(torch.tensor(w["w_ih"]))
+        gru.weight_hh.copy_(torch.tensor(w["w_hh"]))
+        gru.bias_ih.copy_(torch.tensor(w["b_ih"]))
+        gru.bias_hh.copy_(torch.tensor(w["b_hh"]))
+        B, H = eps.shape[:2]
+        S = S2 // 2
+        state = torch.zeros(B, S) if s0 is None else torch.tensor(s0, dtype=torch.float64)
+        belief = torch.zeros(B, Hb) if h0 is None else torch.tensor(h0, dtype=torch.float64)
+        outs = [[], [], [], [], []]
+        for t in range(H):
+            action = actor(torch.cat([state, belief], dim=-1))
+            e = torch.nn.functional.elu(lin_as(torch.cat([state, action], dim=-1)))
+            belief = gru(e, belief)
+            v = lin2(torch.nn.functional.elu(lin1(belief)))
+            mean, raw = v[:, :S], v[:, S:]
+            std = torch.nn.functional.softplus(raw) + 0.1
+            state = mean + torch.tensor(eps[:, t], dtype=torch.float64) * std
+            for lst, val in zip(outs, (mean, std, state, belief, action)):
+                lst.append(val)
+        return [torch.stack(o, 1).numpy() for o in outs]
+
+
+def test_rssm_actor_matches_torch_modules():
+    d = synth.make_rssm_inputs(5, 8, state_dim=4, action_dim=3, embed_dim=7, belief_dim=6, actor_dim=9,
+                               seed=19, s0_std=0.5, h0_std=0.5)
+    got = oracle.rssm_actor_unroll(d["eps"], d["weights"], d["actor"], d["s0"], d["h0"])
+    ref = _torch_rssm_actor(d["weights"], d["actor"], d["eps"], d["s0"], d["h0"])
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-11, atol=1e-12)
+
+
+def test_rssm_actor_constant_policy_equals_given_actions():
+    # W_a1 = W_a2 = 0 and b_a2 = atanh(c): the actor returns c every step,
+    # so the unroll is the first one over constant actions c.
+    d = synth.make_rssm_inputs(4, 7, state_dim=3, action_dim=2, embed_dim=5, belief_dim=6, actor_dim=4,
+                               seed=20, s0_std=0.3, h0_std=0.3)
+    c = np.array([0.4, -0.7])
+    aw = {"w_a1": np.zeros((4, 9)), "b_a1": np.ones(4), "w_a2": np.zeros((2, 4)), "b_a2": np.arctanh(c)}
+    got = oracle.rssm_actor_unroll(d["eps"], d["weights"], aw, d["s0"], d["h0"])
+    acts = np.broadcast_to(c, (4, 7, 2))
+    ref = oracle.rssm_prior_unroll(acts, d["eps"], d["weights"], d["s0"], d["h0"])
+    for g, r in zip(got[:4], ref):
+        np.testing.assert_allclose(g, r, **TIGHT)
+    np.testing.assert_allclose(got[4], acts, rtol=1e-15)
+
+
+def test_rssm_actor_zero_weights_closed_form():
+    d = synth.make_rssm_inputs(3, 4, seed=21, zero_weights=True, actor_dim=8)
+    aw = {k: np.zeros_like(v) for k, v in d["actor"].items()}
+    means, stds, states, beliefs, actions = oracle.rssm_actor_unroll(d["eps"], d["weights"], aw)
+    assert np.all(actions == 0) and np.all(beliefs == 0) and np.all(means == 0)
+    np.testing.assert_allclose(stds, np.full_like(stds, 0.7931471805599453), rtol=1e-15)
+    np.testing.assert_allclose(states, 0.7931471805599453 * d["eps"].astype(np.float64), rtol=1e-15)
+
+
+def test_rssm_actor_time_chunking():
+    d = synth.make_rssm_inputs(3, 9, state_dim=4, action_dim=2, embed_dim=6, belief_dim=5, actor_dim=7, seed=22)
+    full = oracle.rssm_actor_unroll(d["eps"], d["weights"], d["actor"])
+    a = oracle.rssm_actor_unroll(d["eps"][:, :4], d["weights"], d["actor"])
+    b = oracle.rssm_actor_unroll(d["eps"][:, 4:], d["weights"], d["actor"], a[2][:, -1], a[3][:, -1])
+    for f, x, y in zip(full, a, b):
+        np.testing.assert_allclose(np.concatenate([x, y], axis=1), f, **TIGHT)
+
+
+# ---------------------------------------------------------------------------
 # bf16 rounding and the bf16 tolerance headroom
 # ---------------------------------------------------------------------------
 
