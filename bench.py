@@ -129,11 +129,13 @@ def algorithmic(spec, d):
     """Algorithmic flops and HBM bytes per launch, by kernel kind and layer."""
     import synth  # noqa: F401
     out = {}
-    if spec.mode == "rssm":
+    if spec.mode in ("rssm", "rssm_actor"):
         B, T, S, A, E, Hb = d["B"], d["T"], d["state_dim"], d["action_dim"], d["embed_dim"], d["belief_dim"]
-        per_tok = 2 * (E * (S + A) + 3 * Hb * (E + Hb) + E * Hb + 2 * S * E)
-        weights = 4 * (E * (S + A) + E + 6 * Hb * (E + Hb) / 2 + 6 * Hb + E * Hb + E + 2 * S * E + 2 * S)
-        io = 4 * B * T * (A + S + 3 * S + Hb)
+        Ea = d.get("actor_dim", 0)
+        per_tok = 2 * (E * (S + A) + 3 * Hb * (E + Hb) + E * Hb + 2 * S * E + Ea * (S + Hb) + A * Ea)
+        weights = 4 * (E * (S + A) + E + 6 * Hb * (E + Hb) / 2 + 6 * Hb + E * Hb + E + 2 * S * E + 2 * S
+                       + (Ea * (S + Hb) + Ea + A * Ea + A if Ea else 0))
+        io = 4 * B * T * (A + S + 3 * S + Hb)  # actions read (or, with the actor, written)
         out[3] = [{"flops": per_tok * B * T, "bytes": weights + io, "tokens": B * T}]
         return out
     D = 2 if spec.bidirectional else 1
@@ -185,14 +187,21 @@ def main():
 
     # Build the C structs once (inputs resident in HBM before timing).
     keep = []
-    if spec.mode == "rssm":
+    if spec.mode in ("rssm", "rssm_actor"):
+        actor = spec.mode == "rssm_actor"
         w = {k: T(v) for k, v in d["weights"].items()}
-        (out, ws) = gss.rssm_prior_unroll(T(d["actions"]), T(d["eps"]), w, tile_batch=args.tile_batch,
-                                          tile_hidden=args.tile_hidden, placement=args.placement,
-                                          return_workspace=True)
+        aw = {k: T(v) for k, v in d["actor"].items()} if actor else None
+        acts, eps = T(d["actions"]), T(d["eps"])
+        hints = dict(tile_batch=args.tile_batch, tile_hidden=args.tile_hidden, placement=args.placement,
+                     return_workspace=True)
+        if actor:
+            (out, ws) = gss.rssm_actor_unroll(eps, w, aw, **hints)
+        else:
+            (out, ws) = gss.rssm_prior_unroll(acts, eps, w, **hints)
         B, Tn = d["B"], d["T"]
         desc = gss.RnnDesc()
-        desc.mode, desc.dtype, desc.layout = 3, 0, 2
+        desc.mode, desc.dtype, desc.layout = gss.MODES[spec.mode], 0, 2
+        desc.actor_dim = d.get("actor_dim", 0)
         desc.T, desc.B, desc.num_layers, desc.has_bias = Tn, B, 1, 1
         desc.state_dim, desc.action_dim = d["state_dim"], d["action_dim"]
         desc.embed_dim, desc.belief_dim, desc.scale_lb = d["embed_dim"], d["belief_dim"], 0.1
@@ -201,14 +210,19 @@ def main():
         wt.w_as, wt.b_as, wt.w_1, wt.b_1, wt.w_2, wt.b_2 = (w[k].data_ptr() for k in
                                                             ("w_as", "b_as", "w_1", "b_1", "w_2", "b_2"))
         wt.w_ih[0], wt.w_hh[0], wt.b_ih[0], wt.b_hh[0] = (w[k].data_ptr() for k in ("w_ih", "w_hh", "b_ih", "b_hh"))
-        acts, eps = T(d["actions"]), T(d["eps"])
+        if actor:
+            wt.w_a1, wt.b_a1, wt.w_a2, wt.b_a2 = (aw[k].data_ptr() for k in ("w_a1", "b_a1", "w_a2", "b_a2"))
         io = gss.RnnIO()
-        io.x, io.noise = acts.data_ptr(), eps.data_ptr()
-        io.means, io.stds, io.states, io.beliefs = (o.data_ptr() for o in out)
-        keep += [w, acts, eps, out]
+        io.x, io.noise = (acts.data_ptr() if acts is not None else None), eps.data_ptr()
+        io.means, io.stds, io.states, io.beliefs = (o.data_ptr() for o in out[:4])
+        if actor:
+            io.actions = out[4].data_ptr()
+        keep += [w, aw, acts, eps, out]
         tokens = B * Tn
         config = {"workload": name, "B": B, "T": Tn, "state": d["state_dim"], "action": d["action_dim"],
                   "hidden": d["embed_dim"], "gru_hidden": d["belief_dim"]}
+        if actor:
+            config["actor_hidden"] = d["actor_dim"]
         lengths = None
     else:
         params = [{k: T(v) for k, v in p.items() if v is not None} for p in d["params"]]
@@ -364,11 +378,14 @@ def cpu_baseline_any(spec, d, seconds):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    if spec.mode == "rssm":
+    if spec.mode in ("rssm", "rssm_actor"):
         t0 = time.perf_counter()
         tokens, runs = 0, 0
         while True:
-            oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"])
+            if spec.mode == "rssm_actor":
+                oracle.rssm_actor_unroll(d["eps"], d["weights"], d["actor"])
+            else:
+                oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"])
             tokens += d["B"] * d["T"]
             runs += 1
             if time.perf_counter() - t0 > seconds:

@@ -16,7 +16,7 @@ RNN_ABI_VERSION = 2
 RNN_MAX_LAYERS = 8
 RNN_MAX_LD = 2 * RNN_MAX_LAYERS
 
-MODES = {"lstm": 0, "gru": 1, "lstmp": 2, "rssm": 3}
+MODES = {"lstm": 0, "gru": 1, "lstmp": 2, "rssm": 3, "rssm_actor": 4}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 LAYOUTS = {"padded": 0, "packed": 1, "batch_major": 2}
 STATUS = {
@@ -46,7 +46,7 @@ class RnnDesc(ctypes.Structure):
         ("tile_batch", ctypes.c_int32), ("tile_hidden", ctypes.c_int32),
         ("placement", ctypes.c_int32), ("weights", ctypes.c_int32),
         ("clip", ctypes.c_int32), ("cell_clip_lo", ctypes.c_float), ("cell_clip_hi", ctypes.c_float),
-        ("proj_clip", ctypes.c_float), ("reserved", ctypes.c_int32 * 4),
+        ("proj_clip", ctypes.c_float), ("actor_dim", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -58,7 +58,8 @@ class RnnWeights(ctypes.Structure):
         ("w_ih", _PtrArr), ("w_hh", _PtrArr), ("b_ih", _PtrArr), ("b_hh", _PtrArr),
         ("w_hr", _PtrArr), ("w_as", ctypes.c_void_p), ("b_as", ctypes.c_void_p),
         ("w_1", ctypes.c_void_p), ("b_1", ctypes.c_void_p), ("w_2", ctypes.c_void_p),
-        ("b_2", ctypes.c_void_p),
+        ("b_2", ctypes.c_void_p), ("w_a1", ctypes.c_void_p), ("b_a1", ctypes.c_void_p),
+        ("w_a2", ctypes.c_void_p), ("b_a2", ctypes.c_void_p),
     ]
 
 
@@ -68,7 +69,7 @@ class RnnIO(ctypes.Structure):
         ("h0", ctypes.c_void_p), ("c0", ctypes.c_void_p), ("s0", ctypes.c_void_p),
         ("noise", ctypes.c_void_p), ("y", ctypes.c_void_p), ("h_n", ctypes.c_void_p),
         ("c_n", ctypes.c_void_p), ("means", ctypes.c_void_p), ("stds", ctypes.c_void_p),
-        ("states", ctypes.c_void_p), ("beliefs", ctypes.c_void_p),
+        ("states", ctypes.c_void_p), ("beliefs", ctypes.c_void_p), ("actions", ctypes.c_void_p),
     ]
 
 
@@ -328,19 +329,13 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     return (out, ws) if return_workspace else out
 
 
-def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale_lb=0.1,
-                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False):
-    """RSSM prior unrolled over actions [B, T, A] with injected eps [B, T, S].
-
-    weights: dict with w_as [E, S + A], b_as, w_ih [3Hb, E], w_hh [3Hb, Hb],
-    b_ih, b_hh, w_1 [E, Hb], b_1, w_2 [2S, E], b_2 (float32, on the GPU).
-    Returns (means, stds, states, beliefs) stacked on dim 1.
-    """
-    dtype, device = actions.dtype, actions.device
+def _rssm(mode, actions, eps, weights, actor, A, state0, belief0, scale_lb, tile_batch, tile_hidden,
+          placement):
+    """Marshal one RSSM unroll (given actions, or an actor) into the C ABI."""
+    dtype, device = eps.dtype, eps.device
     if dtype != torch.float32:
         raise ValueError("the RSSM prior runs in float32")
-    B, T, A = actions.shape
-    S = eps.shape[2]
+    B, T, S = eps.shape
     E, SA = weights["w_as"].shape
     Hb = weights["w_hh"].shape[1]
     if SA != S + A:
@@ -349,7 +344,13 @@ def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale
               "b_ih": (3 * Hb,), "b_hh": (3 * Hb,), "w_1": (E, Hb), "b_1": (E,),
               "w_2": (2 * S, E), "b_2": (2 * S,)}
     wt = {k: _check(weights[k], k, s, dtype, device) for k, s in shapes.items()}
-    actions = _check(actions, "actions", (B, T, A), dtype, device)
+    Ea = 0
+    if actor is not None:
+        Ea = actor["w_a1"].shape[0]
+        ashapes = {"w_a1": (Ea, S + Hb), "b_a1": (Ea,), "w_a2": (A, Ea), "b_a2": (A,)}
+        wt.update({k: _check(actor[k], k, s, dtype, device) for k, s in ashapes.items()})
+    if actions is not None:
+        actions = _check(actions, "actions", (B, T, A), dtype, device)
     eps = _check(eps, "eps", (B, T, S), dtype, device)
     state0 = _check(state0, "state0", (B, S), dtype, device)
     belief0 = _check(belief0, "belief0", (B, Hb), dtype, device)
@@ -358,20 +359,52 @@ def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale
     w.w_as, w.b_as = _ptr(wt["w_as"]), _ptr(wt["b_as"])
     w.w_ih[0], w.w_hh[0], w.b_ih[0], w.b_hh[0] = (_ptr(wt[k]) for k in ("w_ih", "w_hh", "b_ih", "b_hh"))
     w.w_1, w.b_1, w.w_2, w.b_2 = (_ptr(wt[k]) for k in ("w_1", "b_1", "w_2", "b_2"))
+    if actor is not None:
+        w.w_a1, w.b_a1, w.w_a2, w.b_a2 = (_ptr(wt[k]) for k in ("w_a1", "b_a1", "w_a2", "b_a2"))
     means = torch.empty((B, T, S), dtype=dtype, device=device)
     stds = torch.empty_like(means)
     states = torch.empty_like(means)
     beliefs = torch.empty((B, T, Hb), dtype=dtype, device=device)
+    acts = torch.empty((B, T, A), dtype=dtype, device=device) if actor is not None else None
     desc = RnnDesc()
-    desc.mode, desc.dtype, desc.layout = MODES["rssm"], 0, LAYOUTS["batch_major"]
+    desc.mode, desc.dtype, desc.layout = MODES[mode], 0, LAYOUTS["batch_major"]
     desc.T, desc.B = T, B
     desc.num_layers, desc.bidirectional, desc.has_bias = 1, 0, 1
     desc.state_dim, desc.action_dim, desc.embed_dim, desc.belief_dim = S, A, E, Hb
+    desc.actor_dim = Ea
     desc.scale_lb = scale_lb
     desc.tile_batch, desc.tile_hidden, desc.placement = tile_batch, tile_hidden, placement
     io = RnnIO()
     io.x, io.noise, io.s0, io.h0 = _ptr(actions), _ptr(eps), _ptr(state0), _ptr(belief0)
     io.means, io.stds, io.states, io.beliefs = _ptr(means), _ptr(stds), _ptr(states), _ptr(beliefs)
+    io.actions = _ptr(acts)
     ws = _call(desc, w, io, None, device, keep)
-    out = (means, stds, states, beliefs)
+    out = (means, stds, states, beliefs) + ((acts,) if actor is not None else ())
+    return out, ws
+
+
+def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale_lb=0.1,
+                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False):
+    """RSSM prior unrolled over actions [B, T, A] with injected eps [B, T, S].
+
+    weights: dict with w_as [E, S + A], b_as, w_ih [3Hb, E], w_hh [3Hb, Hb],
+    b_ih, b_hh, w_1 [E, Hb], b_1, w_2 [2S, E], b_2 (float32, on the GPU).
+    Returns (means, stds, states, beliefs) stacked on dim 1.
+    """
+    out, ws = _rssm("rssm", actions, eps, weights, None, actions.shape[2], state0, belief0, scale_lb,
+                    tile_batch, tile_hidden, placement)
+    return (out, ws) if return_workspace else out
+
+
+def rssm_actor_unroll(eps, weights, actor, state0=None, belief0=None, *, scale_lb=0.1,
+                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False):
+    """RSSM prior unrolled for H = eps.shape[1] steps with the actor choosing
+    each action from the previous state and belief.
+
+    weights as for rssm_prior_unroll; actor: dict with w_a1 [Ea, S + Hb],
+    b_a1 [Ea], w_a2 [A, Ea], b_a2 [A] (float32, on the GPU).
+    Returns (means, stds, states, beliefs, actions) stacked on dim 1.
+    """
+    out, ws = _rssm("rssm_actor", None, eps, weights, actor, actor["w_a2"].shape[0], state0, belief0,
+                    scale_lb, tile_batch, tile_hidden, placement)
     return (out, ws) if return_workspace else out

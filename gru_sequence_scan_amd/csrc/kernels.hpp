@@ -93,9 +93,15 @@ struct RssmArgs {
   const float* w_1; const float* b_1; const float* w_2; const float* b_2;
   const float* actions; const float* eps; const float* s0; const float* h0;
   float* means; float* stds; float* states; float* beliefs;
+  // Actor in the loop (Ea > 0): a_t = tanh(W_a2 ELU(W_a1 [s_{t-1}; h_{t-1}]
+  // + b_a1) + b_a2) replaces the given actions; act_out [B, T, A] or null.
+  int Ea;
+  const float* w_a1; const float* b_a1; const float* w_a2; const float* b_a2;
+  float* act_out;
   // exchange (workspace)
   float* ex_h;   // [2][B][Hbp]   whole h_t, ping-pong on t
-  float* ex_p;   // [2][B][nw][Ep] per-member partial sums of W_1 h_t
+  float* ex_p;   // [2][B][nw][Ep] per-member partial sums of W_1 h_t (columns
+                 // 0..E-1) and, with an actor, of W_a1[:, S:] h_t (from r4(E))
   int Ep, Hbp;
   unsigned* counters;  // [ngroups], 64 bytes apart
   int* status;

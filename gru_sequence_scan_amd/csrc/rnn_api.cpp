@@ -70,6 +70,7 @@ int current_device_info(DeviceInfo* out) {
 // Validation
 // ---------------------------------------------------------------------------
 bool is_rnn_mode(int m) { return m == RNN_MODE_LSTM || m == RNN_MODE_GRU || m == RNN_MODE_LSTMP; }
+bool is_rssm(int m) { return m == RNN_MODE_RSSM_PRIOR || m == RNN_MODE_RSSM_ACTOR; }
 
 int validate_desc(const RnnDesc* d) {
   if (!d) return RNN_E_NULL;
@@ -80,7 +81,8 @@ int validate_desc(const RnnDesc* d) {
   if (d->dtype != RNN_DTYPE_F32 && d->dtype != RNN_DTYPE_BF16) return RNN_E_UNSUPPORTED;
   if (d->T < 1 || d->B < 1) return RNN_E_SHAPE;
   if (d->tile_batch < 0 || d->tile_hidden < 0) return RNN_E_SHAPE;
-  if (d->mode == RNN_MODE_RSSM_PRIOR) {
+  if (d->mode == RNN_MODE_RSSM_ACTOR ? d->actor_dim < 1 : d->actor_dim != 0) return RNN_E_SHAPE;
+  if (is_rssm(d->mode)) {
     if (d->layout != RNN_LAYOUT_BATCH_MAJOR) return RNN_E_UNSUPPORTED;
     if (d->dtype != RNN_DTYPE_F32) return RNN_E_UNSUPPORTED;
     if (d->num_layers != 1 || d->bidirectional != 0 || d->proj_size != 0) return RNN_E_UNSUPPORTED;
@@ -90,6 +92,8 @@ int validate_desc(const RnnDesc* d) {
     if (d->clip != 0) return RNN_E_UNSUPPORTED;
     const double big = (double)d->B * d->T * std::max({d->state_dim, d->belief_dim, d->action_dim});
     if (big > 2e9) return RNN_E_SHAPE;
+    const double wa1 = (double)d->actor_dim * (d->state_dim + d->belief_dim);
+    if (wa1 > 2e9) return RNN_E_SHAPE;
     return RNN_OK;
   }
   if (!is_rnn_mode(d->mode)) return RNN_E_UNSUPPORTED;
@@ -116,7 +120,7 @@ int validate_desc(const RnnDesc* d) {
 }
 
 int validate_lengths(const RnnDesc* d, const int32_t* len, long long* n_tok, int* t_max) {
-  if (d->mode == RNN_MODE_RSSM_PRIOR) {
+  if (is_rssm(d->mode)) {
     *n_tok = (long long)d->T * d->B;
     *t_max = d->T;
     return RNN_OK;
@@ -170,6 +174,10 @@ Dims dims_of(const RnnDesc* d, long long n_tok) {
   return m;
 }
 
+// Columns of one member's partial-sum row in the RSSM exchange: W_1 h
+// (E, padded to 4), then the actor's W_a1[:, S:] h (Ea, padded to 4).
+int rssm_ex_cols(const RnnDesc* d) { return rup(d->embed_dim, 4) + rup(d->actor_dim, 4); }
+
 WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
   WsLayout w{};
   size_t o = 0;
@@ -179,10 +187,10 @@ WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
     return at;
   };
   w.status = take(kAlign);
-  if (d->mode == RNN_MODE_RSSM_PRIOR) {
+  if (is_rssm(d->mode)) {
     w.counters_bytes = (size_t)d->B * kCounterBytes;
     w.counters = take(w.counters_bytes);
-    const int Hbp = rup(d->belief_dim, 4), Ep = rup(d->embed_dim, 4);
+    const int Hbp = rup(d->belief_dim, 4), Ep = rssm_ex_cols(d);
     w.ex_h = take((size_t)2 * d->B * Hbp * 4);
     w.ex_p = take((size_t)2 * d->B * kRssmMaxMembers * Ep * 4);
     w.total = o;
@@ -380,6 +388,7 @@ int rssm_grid(const RssmPlan& p, int xcds) { return p.gpx > 0 ? xcds * p.gpx * p
 
 int plan_rssm(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
   const int B = d->B, S = d->state_dim, A = d->action_dim, E = d->embed_dim, Hb = d->belief_dim;
+  const int Ea = d->actor_dim;
   const int per_xcd = xcds > 1 ? cus / xcds : 0;
   double best = 1e30;
   bool found = false;
@@ -393,7 +402,7 @@ int plan_rssm(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
       if ((long long)ngroups * nw > cus) continue;
       if (rows * h_per > 256 || rows * S > 256 || rows * A > 256) continue;
       RssmArgs a{};
-      a.S = S; a.A = A; a.E = E; a.Hb = Hb; a.rows = rows; a.nw = nw; a.h_per = h_per;
+      a.S = S; a.A = A; a.E = E; a.Hb = Hb; a.rows = rows; a.nw = nw; a.h_per = h_per; a.Ea = Ea;
       const int lds = rssm_lds_bytes(a);
       if (lds > kMaxLds) continue;
       // XCD-aligned groups only on request: for this kernel they measured no
@@ -402,11 +411,12 @@ int plan_rssm(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
       const bool xcd_aligned = gpx > 0 && gpx * nw <= per_xcd;
       // GRU slice + partial of W_1 + (redundant) partial sums, W_2 and W_as;
       // the 4x4 MFMA blocks cost the same for any 1..4 batch rows
-      const double macs = 4.0 * (3.0 * h_per * (E + Hb) + (double)E * h_per + (double)E * nw +
-                                 2.0 * S * E + (double)E * (S + A));
-      const double bytes = (double)rows * (Hb + (double)nw * E) * 4.0;
+      // (+ the actor: belief-column partials, their sum, state part, W_a2)
+      const double macs = 4.0 * (3.0 * h_per * (E + Hb) + (double)(E + Ea) * h_per + (double)(E + Ea) * nw +
+                                 2.0 * S * E + (double)E * (S + A) + (double)Ea * (S + A));
+      const double bytes = (double)rows * (Hb + (double)nw * (E + Ea)) * 4.0;
       // products run on 8 waves: ~64 MAC/clk of the 4x4 MFMA chains (measured)
-      double t = barrier_us(nw) + 0.3 + bytes / 100e3 + macs / 64.0 / 2400.0;
+      double t = barrier_us(nw) + 0.3 + (Ea > 0 ? 0.6 : 0.0) + bytes / 100e3 + macs / 64.0 / 2400.0;
       if (d->placement == 2 && !xcd_aligned) t += 1e3;  // requested: aligned plans first
       if (t < best) {
         best = t;
@@ -455,10 +465,18 @@ int check_opt(const void* p, size_t elem) { return (!p || aligned(p, elem)) ? RN
 int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws, size_t ws_bytes,
                  hipStream_t st, int cus, int xcds, Prof& prof) {
   int rc;
+  const bool actor = d->mode == RNN_MODE_RSSM_ACTOR;
   const void* req[] = {w->w_as, w->b_as, w->w_ih[0], w->w_hh[0], w->b_ih[0], w->b_hh[0], w->w_1, w->b_1,
-                       w->w_2, w->b_2, io->x, io->noise, io->means, io->stds, io->states, io->beliefs};
+                       w->w_2, w->b_2, io->noise, io->means, io->stds, io->states, io->beliefs};
   for (const void* p : req)
     if ((rc = check_ptr(p, 4)) != RNN_OK) return rc;
+  if (actor) {
+    for (const void* p : {w->w_a1, w->b_a1, w->w_a2, w->b_a2})
+      if ((rc = check_ptr(p, 4)) != RNN_OK) return rc;
+    if ((rc = check_opt(io->actions, 4)) != RNN_OK) return rc;
+  } else if ((rc = check_ptr(io->x, 4)) != RNN_OK) {
+    return rc;
+  }
   if ((rc = check_opt(io->s0, 4)) != RNN_OK || (rc = check_opt(io->h0, 4)) != RNN_OK) return rc;
   const WsLayout L = layout_of(d, 0, false);
   if (!ws) return RNN_E_WORKSPACE;
@@ -477,12 +495,16 @@ int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* w
   a.b_ih = (const float*)w->b_ih[0]; a.b_hh = (const float*)w->b_hh[0];
   a.w_1 = (const float*)w->w_1; a.b_1 = (const float*)w->b_1;
   a.w_2 = (const float*)w->w_2; a.b_2 = (const float*)w->b_2;
-  a.actions = (const float*)io->x; a.eps = (const float*)io->noise;
+  a.actions = actor ? nullptr : (const float*)io->x; a.eps = (const float*)io->noise;
+  a.Ea = actor ? d->actor_dim : 0;
+  a.w_a1 = actor ? (const float*)w->w_a1 : nullptr; a.b_a1 = actor ? (const float*)w->b_a1 : nullptr;
+  a.w_a2 = actor ? (const float*)w->w_a2 : nullptr; a.b_a2 = actor ? (const float*)w->b_a2 : nullptr;
+  a.act_out = actor ? (float*)io->actions : nullptr;
   a.s0 = (const float*)io->s0; a.h0 = (const float*)io->h0;
   a.means = (float*)io->means; a.stds = (float*)io->stds; a.states = (float*)io->states;
   a.beliefs = (float*)io->beliefs;
   a.ex_h = (float*)(ws + L.ex_h); a.ex_p = (float*)(ws + L.ex_p);
-  a.Ep = rup(d->embed_dim, 4); a.Hbp = rup(d->belief_dim, 4);
+  a.Ep = rssm_ex_cols(d); a.Hbp = rup(d->belief_dim, 4);
   a.counters = (unsigned*)(ws + L.counters);
   a.status = (int*)(ws + L.status);
   // status word and counters are contiguous at the start of the workspace
@@ -653,7 +675,7 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
   if (!info || n_info < 9) return RNN_E_NULL;
   if (cus < 1 || xcds < 1 || cus % xcds != 0) return RNN_E_SHAPE;
   for (int i = 0; i < n_info; ++i) info[i] = 0;
-  if (desc->mode == RNN_MODE_RSSM_PRIOR) {
+  if (is_rssm(desc->mode)) {
     RssmPlan p;
     if ((rc = plan_rssm(desc, cus, xcds, &p)) != RNN_OK) return rc;
     info[0] = 3; info[1] = rssm_grid(p, xcds); info[2] = p.lds; info[3] = p.rows; info[4] = p.h_per;
@@ -685,7 +707,7 @@ int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const R
   int rc = validate_desc(desc);
   if (rc != RNN_OK) return rc;
   if (!weights || !io) return RNN_E_NULL;
-  if (desc->mode != RNN_MODE_RSSM_PRIOR) {
+  if (!is_rssm(desc->mode)) {
     long long n_tok = 0;
     int t_max = 0;
     if ((rc = validate_lengths(desc, io->lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
@@ -700,7 +722,7 @@ int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const R
   prof.n_events = n_events;
   prof.kinds = kinds;
   prof.st = st;
-  rc = desc->mode == RNN_MODE_RSSM_PRIOR
+  rc = is_rssm(desc->mode)
            ? forward_rssm(desc, weights, io, (char*)workspace, ws_bytes, st, info.cus, info.xcds, prof)
            : forward_rnn(desc, weights, io, (char*)workspace, ws_bytes, st, info.cus, info.xcds, prof);
   if (n_kernels) *n_kernels = prof.n;

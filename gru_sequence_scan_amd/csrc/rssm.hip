@@ -23,6 +23,13 @@
 //     the next GRU phase) and all members' partials, sums the partials in a
 //     fixed order (deterministic), and computes u_t, v_t, s_t and e_{t+1}
 //     itself (W_2 and W_as are small enough to keep whole in every member).
+//
+// With an actor in the loop (the issue's second unroll, the actor being the
+// synthetic MLP a = tanh(W_a2 ELU(W_a1 [s; h] + b_a1) + b_a2)), the action
+// of step t + 1 is computed from s_t and h_t at the end of step t: the
+// belief part W_a1[:, S:] h_t is split over the members like W_1 and rides
+// the same exchange (extra partial-sum columns); the state part, the ELU,
+// W_a2 and the tanh are small products every member does whole.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -72,7 +79,7 @@ __device__ __forceinline__ f32x4 dot_chain(const float* xr, const float* wr, int
 }
 
 struct Plain {
-  __device__ float operator()(int, float x) const { return x; }
+  __device__ float operator()(int, int, float x) const { return x; }
 };
 
 // Fixed-order sum over the waves of the partials of (row v, column c) that
@@ -84,7 +91,7 @@ __device__ __forceinline__ float red_sum(const float* red, int v, int c) {
   return s;
 }
 
-// out[v * ldo + c] = epi(c, sum_{k < K} X[v * ldx + k] * W[c * ldw + k]) for
+// out[v * ldo + c] = epi(v, c, sum_{k < K} X[v * ldx + k] * W[c * ldw + k]) for
 // all four rows v of X (rows past the group's batch rows hold zeros and are
 // ignored by the callers) and c < N, on v_mfma_f32_4x4x1f32: 16 blocks of
 // 4x4 per instruction, lane l of a pass owning output column 64 * pass + l.
@@ -108,7 +115,7 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
         const f32x4 acc = dot_chain(xr, W + (c < N ? c : N - 1) * ldw, 0, K4, zero4);
         if (c < N) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) out[v * ldo + c] = epi(c, acc[v]);
+          for (int v = 0; v < 4; ++v) out[v * ldo + c] = epi(v, c, acc[v]);
         }
       }
       return;
@@ -124,7 +131,7 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
     __syncthreads();
     for (int i = threadIdx.x; i < 4 * N; i += kThreads) {
       const int v = i / N, c = i - v * N, p = c >> 6, l = c & 63;
-      out[v * ldo + c] = epi(c, red[((p * 2) * 4 + v) * 64 + l] + red[((p * 2 + 1) * 4 + v) * 64 + l]);
+      out[v * ldo + c] = epi(v, c, red[((p * 2) * 4 + v) * 64 + l] + red[((p * 2 + 1) * 4 + v) * 64 + l]);
     }
     return;
   }
@@ -136,7 +143,7 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
   __syncthreads();
   for (int i = threadIdx.x; i < 4 * N; i += kThreads) {
     const int v = i / N, c = i - v * N;
-    out[v * ldo + c] = epi(c, red_sum(red, v, c));
+    out[v * ldo + c] = epi(v, c, red_sum(red, v, c));
   }
 }
 
@@ -230,8 +237,9 @@ __device__ __forceinline__ void load_wreg(f32x4 (&wr)[kRegChunks], const float* 
 struct RssmLds {
   // float offsets (all multiples of 4)
   int was, bas, w2, b2, wih, whh, w1s, b1;
+  int wa1s, ba1, wa2, ba2, q, qa;  // actor (empty without one)
   int sa, e, h, hs, u, v, gi, gh, red, red2, flag, total;
-  int ld_sa, ld_e, ld_h, ld_hs, ld_v, ld_g;
+  int ld_sa, ld_e, ld_h, ld_hs, ld_v, ld_g, ld_s, ld_q;
 };
 
 __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
@@ -243,6 +251,9 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   L.ld_hs = ld_rows(a.h_per);
   L.ld_v = r4(2 * a.S);
   L.ld_g = r4(3 * a.h_per);
+  L.ld_s = ld_rows(a.S);
+  L.ld_q = ld_rows(a.Ea);
+  const int Ea = a.Ea;
   const int R = kMaxRows;
   int o = 0;
   auto take = [&](int n) { const int at = o; o += r4(n); return at; };
@@ -253,8 +264,14 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   L.b2 = take(2 * a.S);
   L.wih = take(3 * a.h_per * L.ld_e);
   L.whh = take(regw ? 0 : 3 * a.h_per * L.ld_h);
-  L.w1s = take(a.E * L.ld_hs);
+  L.w1s = take((a.E + Ea) * L.ld_hs);  // W_1 columns, then W_a1 belief columns
   L.b1 = take(a.E);
+  L.wa1s = take(Ea * L.ld_s);
+  L.ba1 = take(Ea);
+  L.wa2 = take(Ea > 0 ? a.A * L.ld_q : 0);
+  L.ba2 = take(Ea > 0 ? a.A : 0);
+  L.q = take(Ea > 0 ? R * L.ld_q : 0);
+  L.qa = take(Ea > 0 ? R * L.ld_q : 0);
   L.sa = take(R * L.ld_sa);
   L.e = take(R * L.ld_e);
   L.h = take(R * L.ld_h);
@@ -270,7 +287,7 @@ __host__ __device__ inline RssmLds rssm_lds(const RssmArgs& a) {
   return L;
 }
 
-template <bool REGW>
+template <bool REGW, bool ACTOR>
 __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   const RssmLds L = rssm_lds(a);
@@ -292,6 +309,9 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
   const int b0 = g * a.rows;
   const int nrows = min(a.rows, a.B - b0);
   const int S = a.S, A = a.A, E = a.E, Hb = a.Hb, SA = a.S + a.A;
+  const int Ea = ACTOR ? a.Ea : 0;
+  const int SH = S + Hb;        // W_a1 row length
+  const int ea0 = r4(E);        // first actor column of an exchange row
   const int hp = a.h_per;
   const int j0 = w * hp, hn = max(0, min(hp, Hb - j0));  // owned hidden slice
   unsigned* counter = a.counters + (size_t)g * 16;
@@ -357,13 +377,33 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     const int k = i / hp, jj = i - k * hp;
     if (jj < hn) sm[L.w1s + k * L.ld_hs + jj] = a.w_1[(size_t)k * Hb + j0 + jj];
   }
+  if constexpr (ACTOR) {
+    // belief columns of W_a1 for the slice (rows E .. E + Ea - 1 of w1s),
+    // its state columns whole, W_a2 whole, and both biases
+    for (int i = tid; i < Ea * hp; i += kThreads) {
+      const int k = i / hp, jj = i - k * hp;
+      if (jj < hn) sm[L.w1s + (E + k) * L.ld_hs + jj] = a.w_a1[(size_t)k * SH + S + j0 + jj];
+    }
+    for (int i = tid; i < Ea * S; i += kThreads) {
+      const int r = i / S, c = i - r * S;
+      sm[L.wa1s + r * L.ld_s + c] = a.w_a1[(size_t)r * SH + c];
+    }
+    for (int i = tid; i < A * Ea; i += kThreads) {
+      const int r = i / Ea, c = i - r * Ea;
+      sm[L.wa2 + r * L.ld_q + c] = a.w_a2[i];
+    }
+    for (int i = tid; i < Ea; i += kThreads) sm[L.ba1 + i] = a.b_a1[i];
+    for (int i = tid; i < A; i += kThreads) sm[L.ba2 + i] = a.b_a2[i];
+  }
 
   // --- initial state: [s_0; a_0], whole h_0, own h copy ----------------------
   for (int i = tid; i < nrows * SA; i += kThreads) {
     const int r = i / SA, c = i - r * SA;
     const int b = b0 + r;
-    sm[L.sa + r * L.ld_sa + c] = c < S ? (a.s0 ? a.s0[(size_t)b * S + c] : 0.f)
-                                       : a.actions[((size_t)b * a.T + 0) * A + (c - S)];
+    if (c < S)
+      sm[L.sa + r * L.ld_sa + c] = a.s0 ? a.s0[(size_t)b * S + c] : 0.f;
+    else if (!ACTOR)
+      sm[L.sa + r * L.ld_sa + c] = a.actions[((size_t)b * a.T + 0) * A + (c - S)];
   }
   for (int i = tid; i < nrows * Hb; i += kThreads) {
     const int r = i / Hb, c = i - r * Hb;
@@ -389,10 +429,31 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
   const int ar = tid / A, ac = tid - ar * A;
   const bool act_owner = tid < nrows * A;
   __syncthreads();
+  if constexpr (ACTOR) {
+    // a_0 = actor(s_0, h_0), once, straight from global W_a1 (not resident)
+    for (int i = tid; i < nrows * Ea; i += kThreads) {
+      const int r = i / Ea, c = i - r * Ea;
+      const float* wr = a.w_a1 + (size_t)c * SH;
+      float acc = 0.f;
+      for (int k = 0; k < S; ++k) acc += wr[k] * sm[L.sa + r * L.ld_sa + k];
+      for (int k = 0; k < Hb; ++k) acc += wr[S + k] * sm[L.h + r * L.ld_h + k];
+      sm[L.q + r * L.ld_q + c] = felu(acc + sm[L.ba1 + c]);
+    }
+    __syncthreads();
+    for (int i = tid; i < nrows * A; i += kThreads) {
+      const int r = i / A, c = i - r * A;
+      float acc = 0.f;
+      for (int k = 0; k < Ea; ++k) acc += sm[L.wa2 + c * L.ld_q + k] * sm[L.q + r * L.ld_q + k];
+      const float act = ftanh(acc + sm[L.ba2 + c]);
+      sm[L.sa + r * L.ld_sa + S + c] = act;
+      if (w == 0 && a.act_out) a.act_out[((size_t)(b0 + r) * a.T + 0) * A + c] = act;
+    }
+    __syncthreads();
+  }
   // e_0 = ELU(W_as [s_0; a_0] + b_as) and the hidden part of the first GRU
   // step, W_hh h_0 on the owned slice
   const float* bas = sm + L.bas;
-  auto elu_bias = [bas](int c, float x) { return felu(x + bas[c]); };
+  auto elu_bias = [bas](int, int c, float x) { return felu(x + bas[c]); };
   mv4(sm + L.sa, L.ld_sa, sm + L.was, L.ld_sa, sm + L.e, L.ld_e, E, SA, red, elu_bias);
   __syncthreads();
   if constexpr (REGW) {
@@ -433,14 +494,16 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     {
       const int lane = tid & 63;
       const float* xr = sm + L.hs + (lane & 3) * L.ld_hs;
-      for (int cg = __builtin_amdgcn_readfirstlane(tid >> 6); cg * 64 < E; cg += kWaves) {
+      const int N1 = E + Ea;
+      for (int cg = __builtin_amdgcn_readfirstlane(tid >> 6); cg * 64 < N1; cg += kWaves) {
         const int c = cg * 64 + lane;
-        const f32x4 acc = dot_chain(xr, sm + L.w1s + (c < E ? c : E - 1) * L.ld_hs, 0, (hp + 3) / 4,
+        const f32x4 acc = dot_chain(xr, sm + L.w1s + (c < N1 ? c : N1 - 1) * L.ld_hs, 0, (hp + 3) / 4,
                                     f32x4{0.f, 0.f, 0.f, 0.f});
-        if (c < E) {
+        if (c < N1) {
+          const int col = c < E ? c : ea0 + (c - E);
 #pragma unroll
           for (int v = 0; v < kMaxRows; ++v)
-            if (v < nrows) coh_store_elem<float>(px_rs, px_el(par, b0 + v, w, c), acc[v]);
+            if (v < nrows) coh_store_elem<float>(px_rs, px_el(par, b0 + v, w, col), acc[v]);
         }
       }
     }
@@ -449,7 +512,8 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
     // while the other members arrive: this step's belief, next inputs
     if (owner) a.beliefs[((size_t)(b0 + own_r) * a.T + t) * Hb + j0 + own_j] = hreg;
     const float eps_v = tail_owner ? a.eps[((size_t)(b0 + tr) * a.T + t) * S + tc] : 0.f;
-    const float act_v = (act_owner && t + 1 < a.T) ? a.actions[((size_t)(b0 + ar) * a.T + t + 1) * A + ac] : 0.f;
+    const float act_v =
+        (!ACTOR && act_owner && t + 1 < a.T) ? a.actions[((size_t)(b0 + ar) * a.T + t + 1) * A + ac] : 0.f;
     if (!group_wait(counter, nbar * a.nw, a.status, abort_flag)) return;
 
     // ---- whole h_t for the next GRU phase; u_t from the summed partials.
@@ -490,6 +554,32 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
           for (int k = 0; k < 4; ++k)
             if (4 * ch + k >= Hb) hf[k] = 0.f;
           *reinterpret_cast<f32x4*>(sm + L.h + rh * L.ld_h + 4 * ch) = hf;
+        }
+      }
+      if constexpr (ACTOR) {
+        // belief part of the actor's pre-activation for step t + 1: all
+        // members' partials of W_a1[:, S:] h_t in the same fixed order, on
+        // the threads after those busy above (rotated thread index)
+        const int EA = (Ea + 3) / 4;
+        const int busy = max(nrows * EC, nrows * HC) % kThreads;
+        for (int j = (tid - busy + kThreads) % kThreads; j < nrows * EA; j += kThreads) {
+          const int rq = j / EA, cq = j - rq * EA;
+          f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+          for (int m0 = 0; m0 < a.nw; m0 += 16) {
+            u32x4 pv[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+              pv[m] = coh_load16(px_rs, px_el(par, b0 + rq, min(m0 + m, a.nw - 1), ea0 + 4 * cq) * 4u);
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+              const f32x4 v = __builtin_bit_cast(f32x4, pv[m]);
+              s4 += (m0 + m < a.nw) ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (4 * cq + k >= Ea) s4[k] = 0.f;
+          *reinterpret_cast<f32x4*>(sm + L.qa + rq * L.ld_q + 4 * cq) = s4;
         }
       }
     }
@@ -538,8 +628,26 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
       }
     }
     if (t + 1 < a.T) {
-      if (act_owner) sm[L.sa + ar * L.ld_sa + S + ac] = act_v;
-      __syncthreads();
+      if constexpr (ACTOR) {
+        __syncthreads();
+        // a_{t+1} = tanh(W_a2 ELU(W_a1[:, :S] s_t + (W_a1[:, S:] h_t) + b_a1) + b_a2),
+        // written into the action slot that e_{t+1} reads
+        const float* qa = sm + L.qa;
+        const float* ba1 = sm + L.ba1;
+        const int ldq = L.ld_q;
+        mv4(sm + L.sa, L.ld_sa, sm + L.wa1s, L.ld_s, sm + L.q, L.ld_q, Ea, S, red,
+            [qa, ba1, ldq](int v, int c, float x) { return felu(x + qa[v * ldq + c] + ba1[c]); });
+        __syncthreads();
+        const float* ba2 = sm + L.ba2;
+        mv4(sm + L.q, L.ld_q, sm + L.wa2, L.ld_q, sm + L.sa + S, L.ld_sa, A, Ea, red,
+            [ba2](int, int c, float x) { return ftanh(x + ba2[c]); });
+        __syncthreads();
+        if (w == 0 && a.act_out && act_owner)
+          a.act_out[((size_t)(b0 + ar) * a.T + t + 1) * A + ac] = sm[L.sa + ar * L.ld_sa + S + ac];
+      } else {
+        if (act_owner) sm[L.sa + ar * L.ld_sa + S + ac] = act_v;
+        __syncthreads();
+      }
       // e_{t+1} = ELU(W_as [s_t; a_{t+1}] + b_as), every member, whole
       mv4(sm + L.sa, L.ld_sa, sm + L.was, L.ld_sa, sm + L.e, L.ld_e, E, SA, red, elu_bias);
     }
@@ -552,18 +660,21 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
 int rssm_lds_bytes(const RssmArgs& a) { return rssm_lds(a).total; }
 int rssm_max_rows() { return kMaxRows; }
 
-hipError_t launch_rssm(const RssmArgs& a, hipStream_t stream) {
-  const int lds = rssm_lds(a).total;
-  const bool regw = rssm_regw(a);
-  const void* fn = regw ? (const void*)rssm_kernel<true> : (const void*)rssm_kernel<false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+template <bool REGW, bool ACTOR>
+hipError_t launch_rssm_as(const RssmArgs& a, int lds, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute((const void*)rssm_kernel<REGW, ACTOR>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int grid = a.gpx > 0 ? a.nxcd * a.gpx * a.nw : a.ngroups * a.nw;
-  if (regw)
-    hipLaunchKernelGGL(rssm_kernel<true>, dim3(grid), dim3(kThreads), lds, stream, a);
-  else
-    hipLaunchKernelGGL(rssm_kernel<false>, dim3(grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((rssm_kernel<REGW, ACTOR>), dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_rssm(const RssmArgs& a, hipStream_t stream) {
+  const int lds = rssm_lds(a).total;
+  const bool regw = rssm_regw(a), actor = a.Ea > 0;
+  if (regw) return actor ? launch_rssm_as<true, true>(a, lds, stream) : launch_rssm_as<true, false>(a, lds, stream);
+  return actor ? launch_rssm_as<false, true>(a, lds, stream) : launch_rssm_as<false, false>(a, lds, stream);
 }
 
 }  // namespace rnnk

@@ -65,7 +65,13 @@ typedef enum RnnMode {
   RNN_MODE_LSTM = 0,
   RNN_MODE_GRU = 1,
   RNN_MODE_LSTMP = 2,
-  RNN_MODE_RSSM_PRIOR = 3
+  RNN_MODE_RSSM_PRIOR = 3,
+  RNN_MODE_RSSM_ACTOR = 4  /* the RSSM prior with an actor choosing each action
+                              (pytorch/rl issue "[Feature Request] CUDNN
+                              version of RSSM", Solution, second unroll);
+                              the pages leave the actor undefined, here it is
+                              a_t = tanh(W_a2 ELU(W_a1 [s_{t-1}; h_{t-1}]
+                              + b_a1) + b_a2)                                  */
 } RnnMode;
 
 /* Storage type of weights, inputs, initial states and outputs. Arithmetic
@@ -111,7 +117,8 @@ typedef struct RnnDesc {
   int32_t dtype;         /* RnnDtype                                           */
   int32_t layout;        /* RnnLayout                                          */
   int32_t T;             /* time extent: padded buffers' T; for PACKED an upper
-                            bound on the lengths; RSSM: unroll length         */
+                            bound on the lengths; RSSM: unroll length (the
+                            actor unroll's horizon)                           */
   int32_t B;             /* batch size                                         */
   int32_t input_size;    /* F of layer 0                                       */
   int32_t hidden_size;   /* H                                                  */
@@ -155,7 +162,9 @@ typedef struct RnnDesc {
   float cell_clip_lo;
   float cell_clip_hi;
   float proj_clip;
-  int32_t reserved[4];   /* must be zero                                       */
+  int32_t actor_dim;     /* RSSM_ACTOR: hidden width Ea of the actor MLP (>= 1);
+                            must be 0 in every other mode                     */
+  int32_t reserved[3];   /* must be zero                                       */
 } RnnDesc;
 
 #define RNN_CLIP_CELL 1
@@ -171,6 +180,9 @@ typedef struct RnnDesc {
  *   w_as [E, S + A] (columns: state first, then action), b_as [E]
  *   w_1  [E, Hb], b_1 [E]   (first prior-projector layer, reads the belief)
  *   w_2  [2S, E], b_2 [2S]  (rows 0..S-1 mean, S..2S-1 raw scale)
+ * RSSM_ACTOR additionally (NULL otherwise):
+ *   w_a1 [Ea, S + Hb] (columns: state first, then belief), b_a1 [Ea]
+ *   w_a2 [A, Ea], b_a2 [A]
  * All in the RnnDesc dtype. */
 typedef struct RnnWeights {
   const void* w_ih[RNN_MAX_LD];
@@ -184,10 +196,15 @@ typedef struct RnnWeights {
   const void* b_1;
   const void* w_2;
   const void* b_2;
+  const void* w_a1;
+  const void* b_a1;
+  const void* w_a2;
+  const void* b_a2;
 } RnnWeights;
 
 /* Inputs and outputs (device pointers unless noted), all in the RnnDesc dtype.
  *   x             PADDED [T, B, F] | PACKED [N_tok, F] | RSSM actions [B, T, A]
+ *                 (ignored by RSSM_ACTOR, which computes its actions)
  *   lengths_host  HOST int32 [B]; NULL means every sequence has length T.
  *                 1 <= L_b <= T; PACKED requires L_0 >= L_1 >= ... and
  *                 N_tok = sum L_b. Row b is active at step t iff t < L_b; the
@@ -199,6 +216,8 @@ typedef struct RnnWeights {
  *                 | PACKED [N_tok, D*K]; forward half first on the last axis
  *   h_n [L*D, B, K], c_n [L*D, B, H]  each row's final state; NULL = skip
  *   means, stds, states [B, T, S], beliefs [B, T, Hb]  RSSM outputs
+ *   actions       RSSM_ACTOR output [B, T, A]: the action each step used;
+ *                 NULL = skip (ignored by the other modes)
  * Outputs must not overlap inputs or the workspace. */
 typedef struct RnnIO {
   const void* x;
@@ -214,6 +233,7 @@ typedef struct RnnIO {
   void* stds;
   void* states;
   void* beliefs;
+  void* actions;
 } RnnIO;
 
 /* Version of this ABI (RNN_ABI_VERSION). */

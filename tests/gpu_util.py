@@ -56,6 +56,15 @@ def run_rssm(d, **kw):
     return [t.cpu().numpy().astype(np.float64) for t in out]
 
 
+def run_rssm_actor(d, **kw):
+    w = {k: to_dev(v, torch.float32) for k, v in d["weights"].items()}
+    aw = {k: to_dev(v, torch.float32) for k, v in d["actor"].items()}
+    out = gss.rssm_actor_unroll(to_dev(d["eps"], torch.float32), w, aw, to_dev(d["s0"], torch.float32),
+                                to_dev(d["h0"], torch.float32), **kw)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy().astype(np.float64) for t in out]
+
+
 def subset_rows(d, rows):
     """The same problem restricted to batch rows `rows` (rows are independent)."""
     rows = np.asarray(rows)

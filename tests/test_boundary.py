@@ -61,6 +61,8 @@ int main(void) {
          offsetof(RnnWeights, w_as), offsetof(RnnIO, beliefs));
   printf("%zu %zu %zu %d %d\n", offsetof(RnnDesc, clip), offsetof(RnnDesc, proj_clip),
          offsetof(RnnDesc, reserved), RNN_CLIP_CELL, RNN_CLIP_PROJ);
+  printf("%zu %zu %zu %d\n", offsetof(RnnDesc, actor_dim), offsetof(RnnWeights, w_a1),
+         offsetof(RnnIO, actions), (int)RNN_MODE_RSSM_ACTOR);
   return 0;
 }
 ''')
@@ -79,6 +81,10 @@ int main(void) {
     assert sizes[8] == gss.RnnDesc.proj_clip.offset
     assert sizes[9] == gss.RnnDesc.reserved.offset
     assert (sizes[10], sizes[11]) == (gss.CLIP_CELL, gss.CLIP_PROJ)
+    assert sizes[12] == gss.RnnDesc.actor_dim.offset
+    assert sizes[13] == gss.RnnWeights.w_a1.offset
+    assert sizes[14] == gss.RnnIO.actions.offset
+    assert sizes[15] == gss.MODES["rssm_actor"]
 
 
 def _desc(**kw):
@@ -157,6 +163,33 @@ INF, NAN = float("inf"), float("nan")
 def test_clip_validation(lib, kw, expect):
     st, _ = _ws(_desc(**kw))
     assert st == expect, gss.rnn_strerror(st)
+
+
+RSSM_KW = {"layout": 2, "state_dim": 20, "action_dim": 6, "embed_dim": 200, "belief_dim": 200}
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({"mode": 4, "actor_dim": 200}, OK),
+    ({"mode": 4, "actor_dim": 1}, OK),
+    ({"mode": 4, "actor_dim": 0}, E_SHAPE),             # the actor needs a width
+    ({"mode": 4, "actor_dim": -3}, E_SHAPE),
+    ({"mode": 3, "actor_dim": 16}, E_SHAPE),            # only the actor mode has one
+    ({"mode": 0, "actor_dim": 16, "layout": 0}, E_SHAPE),
+    ({"mode": 4, "actor_dim": 8, "bidirectional": 1}, E_UNSUPPORTED),
+    ({"mode": 4, "actor_dim": 8, "dtype": 1}, E_UNSUPPORTED),
+    ({"mode": 4, "actor_dim": 8, "layout": 0}, E_UNSUPPORTED),
+])
+def test_actor_mode_validation(lib, kw, expect):
+    base = dict(RSSM_KW)
+    base.update(kw)
+    st, n = _ws(_desc(**base))
+    assert st == expect, gss.rnn_strerror(st)
+
+
+def test_actor_exchange_is_larger(lib):
+    st0, n0 = _ws(_desc(mode=3, **RSSM_KW))
+    st1, n1 = _ws(_desc(mode=4, actor_dim=200, **RSSM_KW))
+    assert st0 == st1 == OK and n1 > n0
 
 
 def test_reserved_fields_must_be_zero(lib):

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import log, run_rnn, run_rssm, subset_rows
+from gpu_util import log, run_rnn, run_rssm, run_rssm_actor, subset_rows
 from helpers import assert_close
 
 pytestmark = pytest.mark.gpu
@@ -232,6 +232,39 @@ def test_rssm_zero_weights_closed_form():
     assert_close(states, k * d["eps"].astype(np.float64), "f32", "states")
 
 
+RSSM_ACTOR_SHAPES = [
+    # name, B, T, S, A, E, Hb, Ea, tile_batch, tile_hidden
+    ("actor_small", 7, 6, 5, 3, 24, 40, 17, 0, 0),         # widths not multiples of 4
+    ("actor_wide", 6, 5, 8, 4, 36, 30, 90, 0, 0),          # actor wider than one 64-column pass
+    ("actor_rows4", 9, 7, 4, 2, 20, 26, 33, 4, 0),
+    ("actor_rows1_slices", 3, 5, 6, 5, 18, 50, 12, 1, 7),
+    ("actor_lds_weights", 4, 4, 36, 3, 30, 24, 20, 0, 0),  # 2S > 64: weights stay in LDS
+]
+
+
+@pytest.mark.parametrize("case", RSSM_ACTOR_SHAPES, ids=[c[0] for c in RSSM_ACTOR_SHAPES])
+def test_rssm_actor_shapes(case):
+    name, B, T, S, A, E, Hb, Ea, tb, th = case
+    log(f"[gpu] rssm actor shape {name}")
+    d = synth.make_rssm_inputs(B, T, state_dim=S, action_dim=A, embed_dim=E, belief_dim=Hb, actor_dim=Ea,
+                               seed=zlib.crc32(name.encode()) % 1000, s0_std=0.5, h0_std=0.5)
+    got = run_rssm_actor(d, tile_batch=tb, tile_hidden=th)
+    ref = oracle.rssm_actor_unroll(d["eps"], d["weights"], d["actor"], d["s0"], d["h0"])
+    for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs", "actions")):
+        assert_close(g, r, "f32", f"{name} {nm}")
+
+
+def test_rssm_actor_zero_weights_closed_form():
+    log("[gpu] rssm actor closed form")
+    d = synth.make_rssm_inputs(5, 4, seed=11, zero_weights=True, actor_dim=24)
+    d["actor"] = {k: np.zeros_like(v) for k, v in d["actor"].items()}
+    means, stds, states, beliefs, actions = run_rssm_actor(d)
+    assert np.all(beliefs == 0) and np.all(means == 0) and np.all(actions == 0)
+    k = np.log(2.0) + 0.1
+    assert_close(stds, np.full_like(stds, k), "f32", "stds")
+    assert_close(states, k * d["eps"].astype(np.float64), "f32", "states")
+
+
 # ---------------------------------------------------------------------------
 # The five workloads at full size
 # ---------------------------------------------------------------------------
@@ -287,3 +320,12 @@ def test_full_lstm_t256_b1_small():
     d = synth.make_inputs("lstm_t256_b1_small")
     log("[gpu] full-size lstm_t256_b1_small")
     _compare(d, run_rnn(d), _oracle(d), "lstm_t256_b1_small")
+
+
+def test_full_rssm_actor_b50_h50():
+    d = synth.make_inputs("rssm_actor_b50_h50")
+    log("[gpu] full-size rssm_actor_b50_h50")
+    got = run_rssm_actor(d)
+    ref = oracle.rssm_actor_unroll(d["eps"], d["weights"], d["actor"])
+    for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs", "actions")):
+        assert_close(g, r, "f32", "rssm_actor_b50_h50 " + nm)

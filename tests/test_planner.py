@@ -18,10 +18,11 @@ CODE = {v: k for k, v in gss.STATUS.items()}
 def desc_for(name, **hints):
     s = synth.spec(name)
     d = gss.RnnDesc()
-    if s.mode == "rssm":
-        d.mode, d.layout, d.T, d.B, d.num_layers, d.has_bias = 3, 2, s.T, s.B, 1, 1
+    if s.mode in ("rssm", "rssm_actor"):
+        d.mode, d.layout, d.T, d.B, d.num_layers, d.has_bias = gss.MODES[s.mode], 2, s.T, s.B, 1, 1
         d.state_dim, d.action_dim, d.embed_dim, d.belief_dim, d.scale_lb = (
             s.state_dim, s.action_dim, s.embed_dim, s.belief_dim, 0.1)
+        d.actor_dim = s.actor_dim
     else:
         d.mode = gss.MODES[s.mode]
         d.dtype = 1 if s.dtype == "bf16" else 0
@@ -35,7 +36,7 @@ def desc_for(name, **hints):
     return s, d, lengths
 
 
-@pytest.mark.parametrize("name", [n for n in synth.WORKLOADS if synth.spec(n).mode != "rssm_actor"])
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
 @pytest.mark.parametrize("cus,xcds", [(256, 8), (256, 1), (32, 1), (80, 1)])
 def test_plan_is_coresident_and_covers(name, cus, xcds):
     s, d, lengths = desc_for(name)
