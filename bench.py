@@ -47,18 +47,20 @@ KERNEL_SOURCES = {
 # the ratio the same counter reads for a plain copy of known size
 # (--calibrate-copy). Valid only for the kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 269883029, "write_bytes": 36772025,
-                   "sources": "dc6528ed077676bd"},
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1591847, "write_bytes": 209408,
-                  "sources": "34cd963edd4ff325"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484768956, "write_bytes": 137109504,
-                    "sources": "34cd963edd4ff325"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": 1, "fetch_bytes": 612354682, "write_bytes": 100467712,
-                      "sources": "34cd963edd4ff325"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430765179, "write_bytes": 162342912,
-                        "sources": "34cd963edd4ff325"},
-    "lstm_t256_b1_small": {"kernel": "scan", "index": 0, "fetch_bytes": 190530, "write_bytes": 16512,
-                         "sources": "34cd963edd4ff325"},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1584806, "write_bytes": 209408,
+                  "sources": "d3d3c303c7192ed7"},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186348324, "write_bytes": 25801363,
+                   "sources": "daf4657f46f4da58"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484773337, "write_bytes": 137109504,
+                    "sources": "d3d3c303c7192ed7"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": 0, "fetch_bytes": 612258183, "write_bytes": 100467712,
+                      "sources": "d3d3c303c7192ed7"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430796854, "write_bytes": 162342912,
+                        "sources": "d3d3c303c7192ed7"},
+    "lstm_t256_b1_small": {"kernel": "scan", "index": 0, "fetch_bytes": 183746, "write_bytes": 16512,
+                         "sources": "d3d3c303c7192ed7"},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 348807202, "write_bytes": 47403686,
+                         "sources": "daf4657f46f4da58"},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
