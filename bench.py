@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32_mfma": 157.3, "f32_vector": 157.3}
 
-KIND_NAMES = {1: "gemm_xw", 2: "scan", 3: "rssm"}
+KIND_NAMES = {1: "gemm_xw", 2: "scan", 3: "rssm", 4: "scan_wave"}
 METRIC = "timestep\u00b7batch/s per RNN config; % of MFMA / on-chip BW roofline"
 UNIT = "timestep\u00b7batch/s"
 
@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "gemm_xw": ["gemm_xw.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
     "scan": ["scan.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
     "rssm": ["rssm.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
+    "scan_wave": ["scan_wave.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
 }
 
 # HBM bytes per launch of a workload's dominant kernel, from two rocprofv3
@@ -160,6 +161,7 @@ def algorithmic(spec, d):
         scans.append({"flops": fl, "bytes": tokens * D * (G * 4 + K * es), "tokens": tokens})
     out[1] = gemms
     out[2] = scans
+    out[4] = scans  # the one-wave-per-row scan does the same work
     return out
 
 
@@ -331,8 +333,8 @@ def main():
     dom = max(kernels, key=lambda k: k["avg_us"])
     achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
     unit = "TFLOP/s"
-    if dom["kernel"] == "scan" and spec.B < 16:
-        # the B=1 scans run their products on the vector ALUs
+    if dom["kernel"] == "scan_wave" or (dom["kernel"] == "scan" and spec.B < 16):
+        # the small-batch scans run their products on the vector ALUs
         bound, peak = "alu", PEAK_TFLOPS["f32_vector"]
     else:
         bound = "mfma"

@@ -76,6 +76,14 @@ struct ScanArgs {
 hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
 constexpr int kScanRegChunks = 32;
 
+// Kernel 2b: one wavefront per (direction, batch row) when all gate rows of
+// a unit set fit one wave (LSTM H <= 16, GRU H <= 21; not LSTMP). Uses the
+// ScanArgs problem fields, the per-direction tensors, gx, y, lengths,
+// offsets and the clip bounds; no tiling, exchange or counters.
+bool scan_wave_fits(int mode, int H, int K);
+int scan_wave_grid(int D, int B);
+hipError_t launch_scan_wave(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
+
 // Kernel 3: persistent RSSM-prior unroll.
 struct RssmArgs {
   int B, T, S, A, E, Hb;

@@ -514,6 +514,14 @@ int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* w
   return prof.end();
 }
 
+// The one-wave-per-row scan runs when every gate row of the layer fits one
+// wavefront and no tiling hint asks for the tiled scan.
+bool use_wave_scan(const RnnDesc* d, const Dims& m) {
+  if (d->tile_batch || d->tile_hidden || d->weights) return false;
+  const int mk = d->mode == RNN_MODE_GRU ? kGRU : (d->mode == RNN_MODE_LSTMP ? kLSTMP : kLSTM);
+  return scan_wave_fits(mk, d->hidden_size, m.K);
+}
+
 int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws, size_t ws_bytes,
                 hipStream_t st, int cus, int xcds, Prof& prof) {
   int rc;
@@ -542,8 +550,9 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   // W_hh slices go to registers only as whole aligned 16-byte chunks
   bool wreg_ok = (size_t)m.K * es % 16 == 0;
   for (int i = 0; i < LD; ++i) wreg_ok = wreg_ok && aligned(w->w_hh[i], 16);
-  ScanPlan p;
-  if ((rc = plan_scan(d, m, cus, xcds, wreg_ok, &p)) != RNN_OK) return rc;
+  const bool wave = use_wave_scan(d, m);
+  ScanPlan p{};
+  if (!wave && (rc = plan_scan(d, m, cus, xcds, wreg_ok, &p)) != RNN_OK) return rc;
 
   // ---- enqueue ----
   if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
@@ -627,8 +636,8 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     a.mx = d->mode == RNN_MODE_LSTMP ? ws + L.mx : nullptr;
     a.counters = (unsigned*)(ws + L.counters + (size_t)l * m.D * d->B * kCounterBytes);
     a.status = (int*)(ws + L.status);
-    if ((rc = prof.begin(2)) != RNN_OK) return rc;
-    if ((rc = hip_status(launch_scan(a, bf16, st))) != RNN_OK) return rc;
+    if ((rc = prof.begin(wave ? 4 : 2)) != RNN_OK) return rc;
+    if ((rc = hip_status(wave ? launch_scan_wave(a, bf16, st) : launch_scan(a, bf16, st))) != RNN_OK) return rc;
     if ((rc = prof.end()) != RNN_OK) return rc;
     layer_in = layer_out;
   }
@@ -686,6 +695,12 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
   int t_max = 0;
   if ((rc = validate_lengths(desc, lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
   const Dims m = dims_of(desc, n_tok);
+  if (use_wave_scan(desc, m)) {
+    // one wave per (direction, row): no co-residency needed, no LDS
+    info[0] = 4; info[1] = scan_wave_grid(m.D, desc->B); info[2] = 0; info[3] = 1; info[4] = desc->hidden_size;
+    info[5] = 1; info[6] = 0; info[7] = desc->B; info[8] = 0;
+    return RNN_OK;
+  }
   ScanPlan p;
   if ((rc = plan_scan(desc, m, cus, xcds, (size_t)m.K * m.esize % 16 == 0, &p)) != RNN_OK) return rc;
   info[0] = 2; info[1] = scan_grid(p, m.D, xcds); info[2] = p.lds; info[3] = p.bb; info[4] = p.hs;

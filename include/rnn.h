@@ -262,7 +262,8 @@ int rnn_forward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io,
  * `stream` right before the i-th kernel and events[2i + 1] right after it,
  * for i < n_events / 2; kinds[i] (when kinds is non-NULL, room for
  * n_events / 2 entries) receives 1 for the input-projection GEMM, 2 for a
- * layer's scan and 3 for the RSSM kernel; *n_kernels (nullable) receives the
+ * layer's tiled scan, 3 for the RSSM kernel and 4 for a layer's
+ * one-wave-per-row scan; *n_kernels (nullable) receives the
  * number of compute kernels enqueued. For timing the kernels inside a
  * measured region. Errors as rnn_forward. */
 int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io,
@@ -276,7 +277,10 @@ int rnn_read_status(const void* workspace, void* stream, int* device_status);
 
 /* Host-only: the launch shape rnn_forward would use for this problem on a
  * device with `cus` compute units in `xcds` chiplets (XCDs; workgroups are
- * dealt to them round-robin). info[0..8] = {kernel (2 scan, 3 RSSM),
+ * dealt to them round-robin). info[0..8] = {kernel (2 tiled scan, 3 RSSM,
+ * 4 one-wave-per-row scan: LSTM with H <= 16 or GRU with H <= 21 when no
+ * tiling hint is set; its waves are independent, so it needs no
+ * co-residency),
  * workgroups launched, LDS bytes per workgroup, batch rows per workgroup,
  * hidden units per workgroup, workgroups per group, projection outputs per
  * workgroup (LSTMP), number of groups (per direction for the scan), groups

@@ -129,6 +129,42 @@ def test_clipping(case):
     _compare(d, got, ref, name)
 
 
+WAVE_CASES = [
+    # one wave per (direction, row): gates * H <= 64
+    # name, mode, dtype, T, B, F, H, L, bidir, layout, varlen, bias, cell_clip
+    ("wave_lstm_h16_b1", "lstm", "f32", 40, 1, 16, 16, 1, False, "padded", None, True, None),
+    ("wave_bilstm_packed", "lstm", "f32", 17, 9, 12, 16, 2, True, "packed", (1, 17), True, None),
+    ("wave_gru_h21_bf16", "gru", "bf16", 23, 6, 20, 21, 2, False, "padded", None, True, None),
+    ("wave_gru_h1", "gru", "f32", 9, 3, 4, 1, 1, False, "padded", None, True, None),
+    ("wave_lstm_h5_varlen", "lstm", "f32", 15, 7, 6, 5, 1, True, "padded", "unsorted", True, None),
+    ("wave_lstm_clip", "lstm", "f32", 12, 4, 8, 12, 1, False, "padded", None, True, (-0.3, 0.25)),
+    ("wave_lstm_nobias_bf16", "lstm", "bf16", 10, 5, 16, 16, 1, False, "padded", None, False, None),
+    ("wave_gru_b300", "gru", "f32", 6, 300, 8, 8, 1, True, "padded", None, True, None),
+]
+
+
+@pytest.mark.parametrize("case", WAVE_CASES, ids=[c[0] for c in WAVE_CASES])
+def test_wave_scan(case):
+    name, mode, dt, T, B, F, H, L, bidir, layout, varlen, bias, cc = case
+    log(f"[gpu] wave scan case {name}")
+    lengths, vl = None, None
+    if varlen == "unsorted":
+        lengths = np.random.default_rng(8).integers(1, T + 1, size=B).astype(np.int32)
+    elif varlen is not None:
+        vl = varlen
+    d = synth.make_rnn_inputs(mode, T, B, F, H, num_layers=L, bidirectional=bidir, dtype=dt, layout=layout,
+                              lengths=lengths, varlen=vl, w_scale=1.5 / np.sqrt(H), bias=bias,
+                              seed=zlib.crc32(name.encode()) % 1000, h0_std=0.3, c0_std=0.3)
+    ref = _oracle(d, cell_clip=cc)
+    got = run_rnn(d, y_fill=float("nan"), cell_clip=cc)
+    _compare(d, got, ref, name)
+    # the tiled scan (forced by a tiling hint) agrees with the oracle too,
+    # where its persistent groups fit the device
+    if B <= 32:
+        got_tiled = run_rnn(d, y_fill=float("nan"), cell_clip=cc, tile_batch=1)
+        _compare(d, got_tiled, ref, name + " tiled")
+
+
 def test_padding_sentinel_untouched():
     log("[gpu] padding sentinel")
     lengths = np.array([5, 9, 2, 9, 1, 7, 3, 8], dtype=np.int32)

@@ -48,6 +48,12 @@ def test_plan_is_coresident_and_covers(name, cus, xcds):
         assert e.status == CODE["RNN_E_PLAN"]
         assert cus < 256
         return
+    if p["kernel"] == 4:
+        # one independent wave per (direction, row): any grid size works
+        D = 2 if s.bidirectional else 1
+        assert s.mode in ("lstm", "gru") and (3 if s.mode == "gru" else 4) * s.hidden_size <= 64
+        assert p["workgroups"] * 4 >= D * s.B and p["lds_bytes"] == 0
+        return
     assert p["workgroups"] <= cus
     assert 0 < p["lds_bytes"] <= LDS_MAX
     if p["kernel"] == 3:
@@ -126,3 +132,17 @@ def test_forced_register_layouts(case):
     p = gss.rnn_plan_info(d, lengths)
     assert (p["rows"], p["hidden_per_wg"]) == (bb, hs)
     assert (p["wreg"], p["reg_tiles"], p["reg_ksplit"], p["reg_chunks"]) == expect
+
+
+@pytest.mark.parametrize("mode,H,expect", [("lstm", 16, 4), ("lstm", 17, 2), ("gru", 21, 4), ("gru", 22, 2),
+                                           ("lstm", 1, 4), ("lstmp", 8, 2)])
+def test_wave_scan_choice(mode, H, expect):
+    d = gss.RnnDesc()
+    d.mode, d.T, d.B, d.input_size, d.hidden_size, d.num_layers, d.has_bias = gss.MODES[mode], 8, 5, 7, H, 1, 1
+    if mode == "lstmp":
+        d.proj_size = 4
+    assert gss.rnn_plan_info(d)["kernel"] == expect
+    if expect == 4:
+        # a tiling hint asks for the tiled scan
+        d.tile_batch = 1
+        assert gss.rnn_plan_info(d)["kernel"] == 2
