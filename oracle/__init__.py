@@ -40,7 +40,8 @@ tests/test_oracle_pins.py.
 """
 
 from .rnn import (  # noqa: F401
-    sigmoid, elu, softplus, clip, lstm_cell, gru_cell, run_direction, rnn_forward,
+    sigmoid, elu, softplus, clip, lstm_cell, gru_cell, run_direction, rnn_forward, rnn_backward,
+    run_direction_backward,
     pack_sequence, unpack_sequence, packed_offsets, round_to_bf16,
 )
 from .rssm import rssm_prior_step, rssm_prior_unroll, actor_mlp, rssm_actor_unroll  # noqa: F401

@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "sigmoid", "elu", "softplus", "clip", "lstm_cell", "gru_cell", "run_direction",
-    "rnn_forward", "pack_sequence", "unpack_sequence", "packed_offsets",
+    "rnn_forward", "rnn_backward", "run_direction_backward", "pack_sequence", "unpack_sequence", "packed_offsets",
     "round_to_bf16",
 ]
 
@@ -287,3 +287,192 @@ def rnn_forward(mode, x, params, *, lengths=None, h0=None, c0=None, num_layers=1
     if layout == "packed":
         y = pack_sequence(y, lengths)
     return y, hn, cn
+
+
+# ---------------------------------------------------------------------------
+# Backward through time (training). The pages' AMP / TorchScript discussion
+# (pytorch/pytorch issue "Integrating CuDNN API for LSTMs with projections",
+# thread) is about the backward of these cells; its definition is the chain
+# rule through the cell equations above, step by step in reverse time.
+# ---------------------------------------------------------------------------
+
+def _lstm_cell_backward(x, h, c, p, dh, dc, grads, w_hr=None):
+    """One LSTM / LSTMP step backward for a batch of rows.
+
+    Recomputes the step from its inputs (x, h_{t-1}, c_{t-1}), then takes
+    dh (gradient of the loss w.r.t. the step's output h_t) and dc (w.r.t.
+    c_t from later steps). Accumulates the weight gradients into `grads`;
+    returns (dx, dh_prev, dc_prev).
+    """
+    H = c.shape[-1]
+    a = x @ _f64(p["w_ih"]).T + h @ _f64(p["w_hh"]).T
+    if p.get("b_ih") is not None:
+        a = a + _f64(p["b_ih"])
+    if p.get("b_hh") is not None:
+        a = a + _f64(p["b_hh"])
+    i = sigmoid(a[:, 0:H])
+    f = sigmoid(a[:, H:2 * H])
+    g = np.tanh(a[:, 2 * H:3 * H])
+    o = sigmoid(a[:, 3 * H:4 * H])
+    c_new = f * c + i * g
+    tc = np.tanh(c_new)
+    if w_hr is not None:
+        m = o * tc
+        grads["w_hr"] += dh.T @ m
+        dh = dh @ _f64(w_hr)          # gradient w.r.t. m
+    do = dh * tc
+    dct = dc + dh * o * (1.0 - tc * tc)
+    di, df, dg = dct * g, dct * c, dct * i
+    da = np.concatenate([di * i * (1 - i), df * f * (1 - f), dg * (1 - g * g), do * o * (1 - o)], axis=1)
+    grads["w_ih"] += da.T @ x
+    grads["w_hh"] += da.T @ h
+    grads["b_ih"] += da.sum(0)
+    grads["b_hh"] += da.sum(0)
+    return da @ _f64(p["w_ih"]), da @ _f64(p["w_hh"]), dct * f
+
+
+def _gru_cell_backward(x, h, p, dh, grads):
+    """One GRU step backward (PyTorch r/z/n convention); returns (dx, dh_prev)."""
+    H = h.shape[-1]
+    ax = x @ _f64(p["w_ih"]).T
+    ah = h @ _f64(p["w_hh"]).T
+    if p.get("b_ih") is not None:
+        ax = ax + _f64(p["b_ih"])
+    if p.get("b_hh") is not None:
+        ah = ah + _f64(p["b_hh"])
+    r = sigmoid(ax[:, 0:H] + ah[:, 0:H])
+    z = sigmoid(ax[:, H:2 * H] + ah[:, H:2 * H])
+    n = np.tanh(ax[:, 2 * H:3 * H] + r * ah[:, 2 * H:3 * H])
+    dn = dh * (1 - z)
+    dz = dh * (h - n)
+    dan = dn * (1 - n * n)
+    dr = dan * ah[:, 2 * H:3 * H]
+    dar = dr * r * (1 - r)
+    daz = dz * z * (1 - z)
+    dax = np.concatenate([dar, daz, dan], axis=1)
+    dah = np.concatenate([dar, daz, dan * r], axis=1)
+    grads["w_ih"] += dax.T @ x
+    grads["w_hh"] += dah.T @ h
+    grads["b_ih"] += dax.sum(0)
+    grads["b_hh"] += dah.sum(0)
+    return dax @ _f64(p["w_ih"]), dah @ _f64(p["w_hh"]) + dh * z
+
+
+def run_direction_backward(mode, x, lengths, h0, c0, p, dy, dh_n, dc_n, reverse=False):
+    """Backward of run_direction for one layer and direction (padded layout).
+
+    x [T, B, F]; dy [T, B, K] (ignored where t >= L_b); dh_n [B, K], dc_n
+    [B, H] (LSTM / LSTMP) or None: gradients w.r.t. the final states.
+    Replays the forward to recover each step's inputs, then walks the steps
+    in the opposite order. Returns (dx [T, B, F] (zero where t >= L_b),
+    dh0 [B, K], dc0 [B, H] or None, grads dict of w_ih, w_hh, b_ih, b_hh
+    (and w_hr for LSTMP)).
+    """
+    x = _f64(x)
+    T, B = x.shape[0], x.shape[1]
+    L = np.full(B, T, dtype=np.int64) if lengths is None else np.asarray(lengths, dtype=np.int64)
+    h = _f64(h0).copy()
+    c = None if c0 is None else _f64(c0).copy()
+    steps = list(range(T - 1, -1, -1)) if reverse else list(range(T))
+    w_hr = p.get("w_hr") if mode == "lstmp" else None
+    # forward replay: the state entering each step
+    saved = []
+    for t in steps:
+        rows = np.nonzero(L > t)[0]
+        if rows.size == 0:
+            saved.append(None)
+            continue
+        saved.append((rows, h[rows].copy(), None if c is None else c[rows].copy()))
+        if mode == "gru":
+            h[rows] = gru_cell(x[t, rows], h[rows], p["w_ih"], p["w_hh"], p.get("b_ih"), p.get("b_hh"))
+        else:
+            hn, cn = lstm_cell(x[t, rows], h[rows], c[rows], p["w_ih"], p["w_hh"], p.get("b_ih"),
+                               p.get("b_hh"), w_hr)
+            h[rows], c[rows] = hn, cn
+    grads = {k: np.zeros(np.shape(p[k])) for k in ("w_ih", "w_hh")}
+    G = np.shape(p["w_ih"])[0]
+    grads["b_ih"] = np.zeros(G)
+    grads["b_hh"] = np.zeros(G)
+    if w_hr is not None:
+        grads["w_hr"] = np.zeros(np.shape(w_hr))
+    dx = np.zeros_like(x)
+    dh = _f64(dh_n).copy()
+    dc = None if c is None else (np.zeros_like(c) if dc_n is None else _f64(dc_n).copy())
+    dy = _f64(dy)
+    for t, sv in zip(reversed(steps), reversed(saved)):
+        if sv is None:
+            continue
+        rows, hp, cp = sv
+        g_h = dh[rows] + dy[t, rows]
+        if mode == "gru":
+            dxt, dhp = _gru_cell_backward(x[t, rows], hp, p, g_h, grads)
+        else:
+            dxt, dhp, dcp = _lstm_cell_backward(x[t, rows], hp, cp, p, g_h, dc[rows], grads, w_hr)
+            dc[rows] = dcp
+        dx[t, rows] = dxt
+        dh[rows] = dhp
+    return dx, dh, dc, grads
+
+
+def rnn_backward(mode, x, params, dy, *, dh_n=None, dc_n=None, lengths=None, h0=None, c0=None,
+                 num_layers=1, bidirectional=False, proj_size=0, layout="padded"):
+    """Gradients of a loss through rnn_forward (same arguments), given
+    dy (shape of y), dh_n [L * D, B, K] and dc_n [L * D, B, H] (None = 0).
+
+    Layer l + 1 reads [forward output ; reverse output] of layer l, so the
+    gradient w.r.t. layer l's output is the matching half of layer l + 1's
+    input gradient. Returns (dx like x, dh0 [L * D, B, K], dc0 [L * D, B, H]
+    or None, grads: list over l * D + d of dicts w_ih, w_hh, b_ih, b_hh
+    (+ w_hr)).
+    """
+    if mode not in ("lstm", "lstmp", "gru"):
+        raise ValueError(mode)
+    D = 2 if bidirectional else 1
+    x = _f64(x)
+    dy = _f64(dy)
+    if layout == "packed":
+        T = int(np.max(lengths))
+        xp = unpack_sequence(x, lengths, T, fill=0.0)
+        dyp = unpack_sequence(dy, lengths, T, fill=0.0)
+    else:
+        xp, dyp = x, np.nan_to_num(dy)
+        T = xp.shape[0]
+    B = xp.shape[1]
+    H = params[0]["w_hh"].shape[0] // (3 if mode == "gru" else 4)
+    K = proj_size if mode == "lstmp" else H
+    h0 = np.zeros((num_layers * D, B, K)) if h0 is None else _f64(h0)
+    c0 = None if mode == "gru" else (np.zeros((num_layers * D, B, H)) if c0 is None else _f64(c0))
+    dh_n = np.zeros((num_layers * D, B, K)) if dh_n is None else _f64(dh_n)
+    dc_n = None if mode == "gru" else (np.zeros((num_layers * D, B, H)) if dc_n is None else _f64(dc_n))
+    # layer inputs from a forward pass (unwritten positions as zeros)
+    inputs = [xp]
+    for layer in range(num_layers - 1):
+        outs = []
+        for d in range(D):
+            idx = layer * D + d
+            out, _, _ = run_direction(mode, inputs[-1], lengths, h0[idx], None if c0 is None else c0[idx],
+                                      params[idx], reverse=(d == 1))
+            outs.append(np.nan_to_num(out))
+        inputs.append(np.concatenate(outs, axis=2))
+    grads = [None] * (num_layers * D)
+    dh0 = np.zeros_like(h0)
+    dc0 = None if c0 is None else np.zeros_like(c0)
+    d_out = dyp
+    for layer in range(num_layers - 1, -1, -1):
+        d_in = np.zeros_like(inputs[layer])
+        for d in range(D):
+            idx = layer * D + d
+            dx, dh, dc, g = run_direction_backward(
+                mode, inputs[layer], lengths, h0[idx], None if c0 is None else c0[idx], params[idx],
+                d_out[:, :, d * K:(d + 1) * K], dh_n[idx], None if dc_n is None else dc_n[idx],
+                reverse=(d == 1))
+            d_in += dx
+            dh0[idx] = dh
+            if dc0 is not None:
+                dc0[idx] = dc
+            grads[idx] = g
+        d_out = d_in
+    dx = d_out
+    if layout == "packed":
+        dx = pack_sequence(dx, lengths)
+    return dx, dh0, dc0, grads

@@ -686,3 +686,150 @@ def test_clipping_outside_lstm_is_rejected():
     d = _rand_case("lstm", T=3, B=2, F=3, H=2, seed=43)
     with pytest.raises(ValueError):
         _oracle_run("lstm", d, proj_clip=1.0)
+
+
+# ---------------------------------------------------------------------------
+# Backward through time: torch autograd on the float64 modules, and central
+# finite differences of the (pinned) forward oracle.
+# ---------------------------------------------------------------------------
+
+def _torch_grads(mode, d, dy, dh_n, dc_n):
+    """Gradients of sum(dy * y) + sum(dh_n * h_n) + sum(dc_n * c_n) by autograd."""
+    m = _torch_rnn(mode, d)
+    K = d["proj_size"] if mode == "lstmp" else d["hidden_size"]
+    D = 2 if d["bidirectional"] else 1
+    LD, B = d["num_layers"] * D, d["B"]
+    h0 = torch.tensor(d["h0"] if d["h0"] is not None else np.zeros((LD, B, K)), dtype=torch.float64,
+                      requires_grad=True)
+    x = torch.tensor(np.nan_to_num(d["x_padded"]), dtype=torch.float64, requires_grad=True)
+    lengths = d["lengths"]
+    xin = x if lengths is None else torch.nn.utils.rnn.pack_padded_sequence(
+        x, torch.tensor(lengths, dtype=torch.int64), enforce_sorted=False)
+    if mode == "gru":
+        y, hn = m(xin, h0)
+        cn, c0 = None, None
+    else:
+        c0 = torch.tensor(d["c0"] if d["c0"] is not None else np.zeros((LD, B, d["hidden_size"])),
+                          dtype=torch.float64, requires_grad=True)
+        y, (hn, cn) = m(xin, (h0, c0))
+    if lengths is not None:
+        y, _ = torch.nn.utils.rnn.pad_packed_sequence(y, total_length=d["T"])
+    loss = (y * torch.tensor(dy)).sum() + (hn * torch.tensor(dh_n)).sum()
+    if cn is not None:
+        loss = loss + (cn * torch.tensor(dc_n)).sum()
+    loss.backward()
+    grads = []
+    for layer in range(d["num_layers"]):
+        for di in range(D):
+            sfx = f"_l{layer}" + ("_reverse" if di == 1 else "")
+            g = {"w_ih": getattr(m, "weight_ih" + sfx).grad.numpy(), "w_hh": getattr(m, "weight_hh" + sfx).grad.numpy()}
+            if d["params"][0]["b_ih"] is not None:
+                g["b_ih"] = getattr(m, "bias_ih" + sfx).grad.numpy()
+                g["b_hh"] = getattr(m, "bias_hh" + sfx).grad.numpy()
+            if mode == "lstmp":
+                g["w_hr"] = getattr(m, "weight_hr" + sfx).grad.numpy()
+            grads.append(g)
+    return x.grad.numpy(), h0.grad.numpy(), None if c0 is None else c0.grad.numpy(), grads
+
+
+def _bwd_case(mode, L, bidir, P, bias, varlen, seed):
+    B, T = 5, 7
+    lengths = np.array([7, 3, 6, 1, 5], dtype=np.int32) if varlen else None
+    d = _rand_case(mode, T=T, B=B, F=4, H=3, P=P, L=L, bidir=bidir, bias=bias, lengths=lengths, seed=seed)
+    rng = np.random.default_rng(seed + 100)
+    D = 2 if bidir else 1
+    K = P if mode == "lstmp" else 3
+    dy = rng.normal(size=(T, B, D * K))
+    if lengths is not None:
+        for b, Lb in enumerate(lengths):
+            dy[Lb:, b] = 0.0
+    dh_n = rng.normal(size=(L * D, B, K))
+    dc_n = rng.normal(size=(L * D, B, 3)) if mode != "gru" else None
+    return d, dy, dh_n, dc_n
+
+
+BWD_CASES = [
+    # mode, L, bidir, P, bias, varlen
+    ("lstm", 1, False, 0, True, False),
+    ("lstm", 2, True, 0, True, True),
+    ("lstm", 1, False, 0, False, True),
+    ("gru", 1, False, 0, True, False),
+    ("gru", 2, True, 0, True, True),
+    ("gru", 1, True, 0, False, False),
+    ("lstmp", 1, False, 2, True, False),
+    ("lstmp", 2, True, 2, True, True),
+]
+
+
+@pytest.mark.parametrize("mode,L,bidir,P,bias,varlen", BWD_CASES)
+def test_backward_matches_torch_autograd(mode, L, bidir, P, bias, varlen):
+    d, dy, dh_n, dc_n = _bwd_case(mode, L, bidir, P, bias, varlen, seed=50 + L + 2 * bidir + P)
+    ref = _torch_grads(mode, d, dy, dh_n, dc_n)
+    got = oracle.rnn_backward(mode, d["x"], d["params"], dy, dh_n=dh_n, dc_n=dc_n, lengths=d["lengths"],
+                              h0=d["h0"], c0=d["c0"], num_layers=L, bidirectional=bidir, proj_size=P)
+    dx, dh0, dc0, grads = got
+    np.testing.assert_allclose(dx, ref[0], **TIGHT)
+    np.testing.assert_allclose(dh0, ref[1], **TIGHT)
+    if ref[2] is not None:
+        np.testing.assert_allclose(dc0, ref[2], **TIGHT)
+    for g, r in zip(grads, ref[3]):
+        for k, v in r.items():
+            np.testing.assert_allclose(g[k], v, err_msg=k, **TIGHT)
+
+
+@pytest.mark.parametrize("mode,P", [("lstm", 0), ("gru", 0), ("lstmp", 2)])
+def test_backward_finite_differences(mode, P):
+    # central differences of L = sum(dy * y) + sum(dh_n * h_n) + sum(dc_n * c_n)
+    d, dy, dh_n, dc_n = _bwd_case(mode, 1, True, P, True, True, seed=60 + P)
+
+    def loss(params=d["params"], x=d["x"], h0=d["h0"], c0=d["c0"]):
+        y, hn, cn = oracle.rnn_forward(mode, x, params, lengths=d["lengths"], h0=h0, c0=c0,
+                                       bidirectional=True, proj_size=P)
+        s = float((np.nan_to_num(y) * dy).sum() + (hn * dh_n).sum())
+        return s + (float((cn * dc_n).sum()) if cn is not None else 0.0)
+
+    dx, dh0, dc0, grads = oracle.rnn_backward(mode, d["x"], d["params"], dy, dh_n=dh_n, dc_n=dc_n,
+                                              lengths=d["lengths"], h0=d["h0"], c0=d["c0"],
+                                              bidirectional=True, proj_size=P)
+    eps = 1e-6
+    rng = np.random.default_rng(7)
+    for idx in (0, 1):
+        for k in grads[idx]:
+            arr = d["params"][idx][k]
+            for flat in rng.choice(arr.size, size=min(4, arr.size), replace=False):
+                pos = np.unravel_index(flat, arr.shape)
+                plus = [dict(p) for p in d["params"]]
+                minus = [dict(p) for p in d["params"]]
+                a = np.array(arr, dtype=np.float64)
+                a[pos] += eps
+                plus[idx][k] = a.copy()
+                a[pos] -= 2 * eps
+                minus[idx][k] = a
+                fd = (loss(params=plus) - loss(params=minus)) / (2 * eps)
+                assert abs(fd - grads[idx][k][pos]) < 1e-6 * max(1.0, abs(fd)), (idx, k, pos)
+    x = np.array(d["x"], dtype=np.float64)
+    for pos in [(0, 0, 0), (2, 1, 3), (4, 4, 1)]:
+        xp, xm = x.copy(), x.copy()
+        xp[pos] += eps
+        xm[pos] -= eps
+        fd = (loss(x=xp) - loss(x=xm)) / (2 * eps)
+        assert abs(fd - dx[pos]) < 1e-6 * max(1.0, abs(fd)), pos
+
+
+def test_backward_packed_equals_padded():
+    lengths = np.array([6, 6, 4, 2, 1], dtype=np.int32)
+    dp = synth.make_rnn_inputs("lstm", 6, 5, 3, 4, num_layers=2, bidirectional=True, layout="packed",
+                               lengths=lengths, seed=70, h0_std=0.5, c0_std=0.5)
+    rng = np.random.default_rng(71)
+    dy_p = rng.normal(size=(int(lengths.sum()), 8))
+    kw = dict(lengths=lengths, h0=dp["h0"], c0=dp["c0"], num_layers=2, bidirectional=True)
+    dxp, dh0p, dc0p, gp = oracle.rnn_backward("lstm", dp["x"], dp["params"], dy_p, layout="packed", **kw)
+    x_pad = np.nan_to_num(oracle.unpack_sequence(dp["x"], lengths, 6))
+    dy_pad = np.nan_to_num(oracle.unpack_sequence(dy_p, lengths, 6))
+    dx, dh0, dc0, g = oracle.rnn_backward("lstm", x_pad, dp["params"], dy_pad, **kw)
+    np.testing.assert_allclose(dxp, oracle.pack_sequence(dx, lengths), **TIGHT)
+    np.testing.assert_allclose(dh0p, dh0, **TIGHT)
+    np.testing.assert_allclose(dc0p, dc0, **TIGHT)
+    for a, b in zip(gp, g):
+        for k in a:
+            np.testing.assert_allclose(a[k], b[k], **TIGHT)
