@@ -73,6 +73,14 @@ class RnnIO(ctypes.Structure):
     ]
 
 
+class RnnGrads(ctypes.Structure):
+    _fields_ = [
+        ("dy", ctypes.c_void_p), ("dh_n", ctypes.c_void_p), ("dc_n", ctypes.c_void_p),
+        ("dx", ctypes.c_void_p), ("dh0", ctypes.c_void_p), ("dc0", ctypes.c_void_p),
+        ("dw_ih", _PtrArr), ("dw_hh", _PtrArr), ("db_ih", _PtrArr), ("db_hh", _PtrArr),
+    ]
+
+
 class RnnError(RuntimeError):
     def __init__(self, status, where=""):
         self.status = status
@@ -109,6 +117,18 @@ def lib():
         L.rnn_plan_info.restype = ctypes.c_int
         L.rnn_plan_info.argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
                                     ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.c_int]
+        for nm in ("rnn_reserve_bytes", "rnn_backward_workspace_bytes"):
+            getattr(L, nm).restype = ctypes.c_int
+            getattr(L, nm).argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_size_t)]
+        L.rnn_forward_train.restype = ctypes.c_int
+        L.rnn_forward_train.argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(RnnWeights), ctypes.POINTER(RnnIO),
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
+        L.rnn_backward.restype = ctypes.c_int
+        L.rnn_backward.argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(RnnWeights), ctypes.POINTER(RnnIO),
+                                   ctypes.POINTER(RnnGrads), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]
         if L.rnn_abi_version() != RNN_ABI_VERSION:
             raise RuntimeError("native library ABI version mismatch")
         _lib = L
@@ -235,7 +255,7 @@ def _call(desc, w, io, lengths, device, keep):
 def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padded",
                 num_layers=1, bidirectional=False, proj_size=0, hidden_size=None, y_out=None,
                 tile_batch=0, tile_hidden=0, placement=0, weights=0, cell_clip=None, proj_clip=None,
-                return_workspace=False):
+                return_workspace=False, _train=False):
     """Forward of an LSTM / GRU / LSTMP stack on the current HIP stream.
 
     x: padded [T, B, F] or packed [N_tok, F] (float32 or bfloat16, on a GPU).
@@ -324,9 +344,81 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     keep_len, io.lengths_host = _len_ptr(lengths)
     io.h0, io.c0 = _ptr(h0), _ptr(c0)
     io.y, io.h_n, io.c_n = _ptr(y), _ptr(h_n), _ptr(c_n)
-    ws = _call(desc, w, io, lengths, device, keep)
     out = (y, h_n, c_n)
+    if _train:
+        n = ctypes.c_size_t(0)
+        st = lib().rnn_reserve_bytes(ctypes.byref(desc), io.lengths_host, ctypes.byref(n))
+        if st != 0:
+            raise RnnError(st, "rnn_reserve_bytes")
+        reserve = torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+        ws_bytes = rnn_workspace_bytes(desc, lengths)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device)
+        st = lib().rnn_forward_train(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(io), reserve.data_ptr(),
+                                     reserve.numel(), ws.data_ptr(), ws.numel(), _stream_ptr(device))
+        if st != 0:
+            raise RnnError(st, "rnn_forward_train")
+        ctx = TrainContext(desc, w, io, keep + [keep_len, y, h_n, c_n], reserve, lengths, mode, params, D, H, K)
+        return out, ctx
+    ws = _call(desc, w, io, lengths, device, keep)
     return (out, ws) if return_workspace else out
+
+
+class TrainContext:
+    """What rnn_backward needs from rnn_forward_train: the C structs of that
+    call, the tensors they point to (kept alive here) and the reserve."""
+
+    def __init__(self, desc, w, io, keep, reserve, lengths, mode, params, D, H, K):
+        self.desc, self.w, self.io, self.keep, self.reserve = desc, w, io, keep, reserve
+        self.lengths, self.mode, self.params, self.D, self.H, self.K = lengths, mode, params, D, H, K
+
+
+def rnn_forward_train(mode, x, params, **kw):
+    """rnn_forward that also keeps what the backward needs (fp32 LSTM / GRU).
+    Returns ((y, h_n, c_n), ctx); pass ctx to rnn_backward."""
+    return rnn_forward(mode, x, params, _train=True, **kw)
+
+
+def rnn_backward(ctx, dy, dh_n=None, dc_n=None):
+    """Gradients through the forward recorded in ctx, given dy (shape of y)
+    and optionally dh_n, dc_n (shape of h_n, c_n). Returns (dx, dh0, dc0,
+    grads) with grads a list over layer * D + direction of dicts dw_ih,
+    dw_hh, db_ih, db_hh (bias entries only with biases); dc0 None for GRU."""
+    y = ctx.keep[-3]
+    device, dtype = y.device, y.dtype
+    desc, io = ctx.desc, ctx.io
+    LD = desc.num_layers * ctx.D
+    B, H = desc.B, ctx.H
+    dy = _check(dy, "dy", tuple(y.shape), dtype, device)
+    dh_n = _check(dh_n, "dh_n", (LD, B, H), dtype, device)
+    dc_n = _check(dc_n, "dc_n", (LD, B, H), dtype, device) if ctx.mode != "gru" else None
+    x = ctx.keep[0]
+    dx = torch.empty_like(x)
+    dh0 = torch.empty((LD, B, H), dtype=dtype, device=device)
+    dc0 = torch.empty((LD, B, H), dtype=dtype, device=device) if ctx.mode != "gru" else None
+    g = RnnGrads()
+    g.dy, g.dh_n, g.dc_n = _ptr(dy), _ptr(dh_n), _ptr(dc_n)
+    g.dx, g.dh0, g.dc0 = _ptr(dx), _ptr(dh0), _ptr(dc0)
+    grads = []
+    for i, p in enumerate(ctx.params):
+        gi = {"dw_ih": torch.empty_like(p["w_ih"]), "dw_hh": torch.empty_like(p["w_hh"])}
+        if desc.has_bias:
+            gi["db_ih"] = torch.empty_like(p["b_ih"])
+            gi["db_hh"] = torch.empty_like(p["b_hh"])
+        for k, t in gi.items():
+            getattr(g, k)[i] = t.data_ptr()
+        grads.append(gi)
+    n = ctypes.c_size_t(0)
+    st = lib().rnn_backward_workspace_bytes(ctypes.byref(desc), io.lengths_host, ctypes.byref(n))
+    if st != 0:
+        raise RnnError(st, "rnn_backward_workspace_bytes")
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+    st = lib().rnn_backward(ctypes.byref(desc), ctypes.byref(ctx.w), ctypes.byref(io), ctypes.byref(g),
+                            ctx.reserve.data_ptr(), ctx.reserve.numel(), ws.data_ptr(), ws.numel(),
+                            _stream_ptr(device))
+    if st != 0:
+        raise RnnError(st, "rnn_backward")
+    ctx.bwd_workspace = ws
+    return dx, dh0, dc0, grads
 
 
 def _rssm(mode, actions, eps, weights, actor, A, state0, belief0, scale_lb, tile_batch, tile_hidden,

@@ -55,6 +55,10 @@ struct ScanArgs {
   // Clamp bounds of the updated cell state and of the projected output
   // (infinite when that clipping is off); NaN passes through.
   float c_lo, c_hi, p_lo, p_hi;
+  // Training: per token and direction, the gate values the backward needs,
+  // [rows, D, R] fp32 with R = 5H for LSTM (i, f, g, o, c_t) and 4H for GRU
+  // (r, z, n, W_hn h_{t-1} + b_hn); null when not training.
+  float* rsv;
   // per direction tensors (already offset to this layer)
   const void* w_hh[2];
   const void* w_hr[2];
@@ -83,6 +87,64 @@ constexpr int kScanRegChunks = 32;
 bool scan_wave_fits(int mode, int H, int K);
 int scan_wave_grid(int D, int B);
 hipError_t launch_scan_wave(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
+
+// Backward of one layer's scan (all directions), persistent like the
+// forward: a group of ns workgroups per (direction, batch block), each
+// owning hs hidden units. Walks the forward's steps in the opposite order.
+struct ScanBwdArgs {
+  int mode;            // kLSTM or kGRU
+  int T, B, H, D, G;   // recurrent width K == H
+  int packed;
+  int bb, hs, ns, nbb, nxcd, gpx;
+  int Hp;              // exchange row width (H rounded up to 32)
+  int kp;              // product depth: gates * hs rounded up to 16
+  const float* w_hh[2];  // [G, H]
+  const float* rsv;      // [rows, D, R] this layer (see ScanArgs::rsv)
+  const float* y;        // [rows, D * H] this layer's forward output
+  const float* dy;       // [rows, D * H] gradient w.r.t. y
+  const float* h0[2];    // [B, H] or null
+  const float* c0[2];
+  const float* dh_n[2];  // [B, H] or null
+  const float* dc_n[2];
+  float* dh0[2];         // [B, H] or null
+  float* dc0[2];
+  float* dgx;            // [rows, D, G] input-side pre-activation gradients
+  float* dgh;            // [rows, D, G] hidden side (GRU; null for LSTM: same as dgx)
+  const int* lengths;    // device [B] or null
+  const int* offsets;    // device [T + 1] (packed)
+  float* ex;             // [2][D][ns][B][Hp] per-member partial sums of W_hh^T dG
+  unsigned* counters;
+  int* status;
+};
+int scan_bwd_lds_bytes(const ScanBwdArgs& a);
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t stream);
+
+// C[m, n] (+)= sum_k A(m, k) B(k, n), fp32, with A(m, k) = A[m * sam + k * sak]
+// and B(k, n) = B[k * sbk + n * sbn]: the backward's NN and TN products.
+struct GemmGenArgs {
+  const float* A; long long sam, sak;
+  const float* B; long long sbk, sbn;
+  float* C; long long ldc;
+  int M, N, K;
+  int accumulate;      // 1: C += product, 0: C = product
+};
+hipError_t launch_gemm_gen(const GemmGenArgs& a, hipStream_t stream);
+// out[n] = sum over m of A[m * lda + n] for n < N (fixed order), using
+// `partial` (nchunk * N floats) for a two-pass deterministic reduction.
+hipError_t launch_colsum(const float* A, long long lda, int M, int N, float* partial, int nchunk, float* out,
+                         hipStream_t stream);
+constexpr int kColsumChunks = 64;
+// hprev[row(t, b), :] = the state entering step t of direction d for rows
+// active at t (y of the previous step, or h0), zero for inactive rows.
+struct HprevArgs {
+  const float* y; int ldy, col0;   // y[row * ldy + col0 + j]
+  const float* h0;                 // [B, H] or null
+  float* out;                      // [rows, H]
+  int T, B, H, packed, rev;
+  const int* lengths;              // device [B] or null
+  const int* offsets;              // device [T + 1] (packed)
+};
+hipError_t launch_hprev(const HprevArgs& a, hipStream_t stream);
 
 // Kernel 3: persistent RSSM-prior unroll.
 struct RssmArgs {

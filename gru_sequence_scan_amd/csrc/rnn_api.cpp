@@ -522,8 +522,38 @@ bool use_wave_scan(const RnnDesc* d, const Dims& m) {
   return scan_wave_fits(mk, d->hidden_size, m.K);
 }
 
+// Training reserve: per layer, the gate values of every token and
+// direction ([rows, D, R] fp32, R = 5H LSTM / 4H GRU) and, below the last
+// layer, the layer's output ([rows, D * H] fp32), which is the next layer's
+// input and the source of h_{t-1}.
+struct ReserveLayout {
+  size_t gates[RNN_MAX_LAYERS], y[RNN_MAX_LAYERS], total;
+  int R;
+};
+
+ReserveLayout reserve_of(const RnnDesc* d, const Dims& m) {
+  ReserveLayout r{};
+  r.R = (d->mode == RNN_MODE_GRU ? 4 : 5) * d->hidden_size;
+  size_t o = 0;
+  for (int l = 0; l < d->num_layers; ++l) {
+    r.gates[l] = o;
+    o = align_up(o + (size_t)m.rows * m.D * r.R * 4, kAlign);
+    r.y[l] = o;
+    if (l + 1 < d->num_layers) o = align_up(o + (size_t)m.rows * m.D * d->hidden_size * 4, kAlign);
+  }
+  r.total = o;
+  return r;
+}
+
+// Training is built for fp32 LSTM and GRU stacks without clipping.
+int validate_train(const RnnDesc* d) {
+  if (d->mode != RNN_MODE_LSTM && d->mode != RNN_MODE_GRU) return RNN_E_UNSUPPORTED;
+  if (d->dtype != RNN_DTYPE_F32 || d->clip != 0) return RNN_E_UNSUPPORTED;
+  return RNN_OK;
+}
+
 int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws, size_t ws_bytes,
-                hipStream_t st, int cus, int xcds, Prof& prof) {
+                hipStream_t st, int cus, int xcds, Prof& prof, char* rsv = nullptr) {
   int rc;
   long long n_tok = 0;
   int t_max = 0;
@@ -550,9 +580,10 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   // W_hh slices go to registers only as whole aligned 16-byte chunks
   bool wreg_ok = (size_t)m.K * es % 16 == 0;
   for (int i = 0; i < LD; ++i) wreg_ok = wreg_ok && aligned(w->w_hh[i], 16);
-  const bool wave = use_wave_scan(d, m);
+  const bool wave = !rsv && use_wave_scan(d, m);
   ScanPlan p{};
   if (!wave && (rc = plan_scan(d, m, cus, xcds, wreg_ok, &p)) != RNN_OK) return rc;
+  const ReserveLayout RL = reserve_of(d, m);
 
   // ---- enqueue ----
   if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
@@ -576,11 +607,19 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   }
 
   const bool bf16 = d->dtype == RNN_DTYPE_BF16;
+  // padded var-len: the reserved layer outputs are read at every position
+  // by the backward's products, so the ones the scan never writes are zero
+  if (rsv && has_len && d->layout == RNN_LAYOUT_PADDED)
+    for (int l = 0; l + 1 < d->num_layers; ++l)
+      if ((rc = hip_status(launch_fill_zero(rsv + RL.y[l], (size_t)m.rows * m.D * d->hidden_size * 4, st))) != RNN_OK)
+        return rc;
   float* gx = (float*)(ws + L.gx);
   const void* layer_in = io->x;
   for (int l = 0; l < d->num_layers; ++l) {
     const int in_l = l == 0 ? d->input_size : m.D * m.K;
-    void* layer_out = l == d->num_layers - 1 ? io->y : (void*)(ws + ((l % 2 == 0) ? L.inter0 : L.inter1));
+    void* layer_out = l == d->num_layers - 1 ? io->y
+                      : rsv ? (void*)(rsv + RL.y[l])
+                            : (void*)(ws + ((l % 2 == 0) ? L.inter0 : L.inter1));
     // Kernel 1: Gx for every row of this layer, both directions.
     GemmArgs g{};
     g.A = layer_in;
@@ -630,6 +669,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     }
     a.gx = gx;
     a.y = layer_out;
+    a.rsv = rsv ? (float*)(rsv + RL.gates[l]) : nullptr;
     a.lengths = dev_len;
     a.offsets = dev_off;
     a.hx = ws + L.hx;
@@ -640,6 +680,227 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     if ((rc = hip_status(wave ? launch_scan_wave(a, bf16, st) : launch_scan(a, bf16, st))) != RNN_OK) return rc;
     if ((rc = prof.end()) != RNN_OK) return rc;
     layer_in = layer_out;
+  }
+  return RNN_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// Backward through time (training)
+// ---------------------------------------------------------------------------
+constexpr int kBwdMaxMembers = 64;
+
+struct BwdPlan {
+  int bb, hs, ns, nbb, kp, lds;
+};
+
+// Same shape of search as plan_scan: every group co-resident, LDS within a
+// CU, elements per thread bounded; the step model adds the partial-sum
+// exchange (write a row block of all H columns, read the owned columns of
+// every member).
+int plan_scan_bwd(const RnnDesc* d, const Dims& m, int cus, BwdPlan* out) {
+  const int H = d->hidden_size, B = d->B, Hp = m.Hp;
+  std::vector<int> bbs, hss;
+  if (d->tile_batch > 0) {
+    bbs.push_back(d->tile_batch);
+  } else {
+    for (int bb = 1; bb < B; bb *= 2) bbs.push_back(bb);
+    bbs.push_back(B);
+  }
+  if (d->tile_hidden > 0) {
+    hss.push_back(d->tile_hidden);
+  } else {
+    for (int hs = 4; hs <= std::max(4, rup(H, 4)); hs *= 2) hss.push_back(hs);
+  }
+  double best = 1e30;
+  bool found = false;
+  for (int bb : bbs) {
+    for (int hs : hss) {
+      if (bb < 1 || hs < 1 || hs % 4 != 0 || bb * hs > 1024) continue;
+      const int ns = cdiv(H, hs), nbb = cdiv(B, bb);
+      if (ns > kBwdMaxMembers || (long long)m.D * nbb * ns > cus) continue;
+      ScanBwdArgs a{};
+      a.mode = d->mode == RNN_MODE_GRU ? kGRU : kLSTM;
+      a.bb = bb; a.hs = hs; a.Hp = Hp; a.kp = rup(m.gates * hs, 16);
+      const int lds = scan_bwd_lds_bytes(a);
+      if (lds > kMaxLds) continue;
+      const double xbytes = (double)ns * std::min(bb, B) * hs * 4 + (double)bb * Hp * 4;
+      const double t = barrier_us(ns) + xbytes / 100e3 + mm_us(bb % 16 == 0, 4, bb, Hp, a.kp);
+      if (t < best) {
+        best = t;
+        *out = BwdPlan{bb, hs, ns, nbb, a.kp, lds};
+        found = true;
+      }
+    }
+  }
+  return found ? RNN_OK : RNN_E_PLAN;
+}
+
+struct BwdLayout {
+  size_t status, counters, ints, dgx, dgh, hprev, dx0, dx1, ex, part, total;
+  size_t counters_bytes;
+  int n_ints;
+};
+
+BwdLayout bwd_layout_of(const RnnDesc* d, const Dims& m, bool has_lengths) {
+  BwdLayout w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, kAlign);
+    return at;
+  };
+  const size_t rows = (size_t)m.rows;
+  w.status = take(kAlign);
+  w.counters_bytes = (size_t)d->num_layers * m.D * d->B * kCounterBytes;
+  w.counters = take(w.counters_bytes);
+  w.n_ints = has_lengths ? d->B + d->T + 1 : 0;
+  w.ints = take((size_t)std::max(w.n_ints, 1) * 4);
+  w.dgx = take(rows * m.D * m.G * 4);
+  w.dgh = d->mode == RNN_MODE_GRU ? take(rows * m.D * m.G * 4) : w.dgx;
+  w.hprev = take(rows * d->hidden_size * 4);
+  const size_t dxb = rows * m.D * d->hidden_size * 4;
+  w.dx0 = d->num_layers > 1 ? take(dxb) : 0;
+  w.dx1 = d->num_layers > 2 ? take(dxb) : 0;
+  w.ex = take((size_t)2 * m.D * kBwdMaxMembers * d->B * m.Hp * 4);
+  w.part = take((size_t)kColsumChunks * m.G * 4);
+  w.total = o;
+  return w;
+}
+
+int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const RnnGrads* gr, const char* rsv,
+                 size_t rsv_bytes, char* ws, size_t ws_bytes, hipStream_t st, int cus) {
+  int rc;
+  long long n_tok = 0;
+  int t_max = 0;
+  if ((rc = validate_lengths(d, io->lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
+  const Dims m = dims_of(d, n_tok);
+  const int LD = d->num_layers * m.D, H = d->hidden_size, G = m.G;
+  for (int i = 0; i < LD; ++i) {
+    if ((rc = check_ptr(w->w_ih[i], 4)) != RNN_OK || (rc = check_ptr(w->w_hh[i], 4)) != RNN_OK) return rc;
+    if ((rc = check_ptr(gr->dw_ih[i], 4)) != RNN_OK || (rc = check_ptr(gr->dw_hh[i], 4)) != RNN_OK) return rc;
+    if (d->has_bias &&
+        ((rc = check_ptr(gr->db_ih[i], 4)) != RNN_OK || (rc = check_ptr(gr->db_hh[i], 4)) != RNN_OK))
+      return rc;
+  }
+  if ((rc = check_ptr(io->x, 4)) != RNN_OK || (rc = check_ptr(io->y, 4)) != RNN_OK) return rc;
+  if ((rc = check_ptr(gr->dy, 4)) != RNN_OK || (rc = check_ptr(gr->dx, 4)) != RNN_OK) return rc;
+  for (const void* p : {io->h0, io->c0, gr->dh_n, gr->dc_n, (const void*)gr->dh0, (const void*)gr->dc0})
+    if ((rc = check_opt(p, 4)) != RNN_OK) return rc;
+  const ReserveLayout RL = reserve_of(d, m);
+  if (!rsv || rsv_bytes < RL.total) return RNN_E_WORKSPACE;
+  const bool has_len = io->lengths_host != nullptr;
+  const BwdLayout L = bwd_layout_of(d, m, has_len);
+  if (!ws || ws_bytes < L.total) return RNN_E_WORKSPACE;
+  if (!aligned(ws, 16) || !aligned(rsv, 16)) return RNN_E_ALIGN;
+  BwdPlan p;
+  if ((rc = plan_scan_bwd(d, m, cus, &p)) != RNN_OK) return rc;
+
+  // ---- enqueue ----
+  if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
+  int* dev_len = nullptr;
+  int* dev_off = nullptr;
+  if (has_len) {
+    std::vector<int> ints((size_t)d->B + d->T + 1, 0);
+    for (int b = 0; b < d->B; ++b) ints[b] = io->lengths_host[b];
+    if (d->layout == RNN_LAYOUT_PACKED) {
+      long long acc = 0;
+      for (int t = 0; t <= d->T; ++t) {
+        ints[d->B + t] = (int)acc;
+        for (int b = 0; b < d->B; ++b)
+          if (io->lengths_host[b] > t) ++acc;
+      }
+    }
+    dev_len = (int*)(ws + L.ints);
+    dev_off = dev_len + d->B;
+    if ((rc = hip_status(launch_write_ints(dev_len, ints.data(), (int)ints.size(), st))) != RNN_OK) return rc;
+  }
+  float* dgx = (float*)(ws + L.dgx);
+  float* dgh = (float*)(ws + L.dgh);
+  const size_t gbytes = (size_t)m.rows * m.D * G * 4;
+  // padded var-len: positions the scan never writes must read as zero
+  if (has_len && d->layout == RNN_LAYOUT_PADDED) {
+    if ((rc = hip_status(launch_fill_zero(dgx, gbytes, st))) != RNN_OK) return rc;
+    if (dgh != dgx && (rc = hip_status(launch_fill_zero(dgh, gbytes, st))) != RNN_OK) return rc;
+  }
+  float* hprev = (float*)(ws + L.hprev);
+  float* part = (float*)(ws + L.part);
+  const size_t sB = (size_t)d->B * H;
+  const int rows = (int)m.rows;
+  for (int l = d->num_layers - 1; l >= 0; --l) {
+    const float* y_l = l == d->num_layers - 1 ? (const float*)io->y : (const float*)(rsv + RL.y[l]);
+    const float* dy_l = l == d->num_layers - 1 ? (const float*)gr->dy
+                                               : (const float*)(ws + ((l % 2 == 0) ? L.dx0 : L.dx1));
+    ScanBwdArgs a{};
+    a.mode = d->mode == RNN_MODE_GRU ? kGRU : kLSTM;
+    a.T = t_max; a.B = d->B; a.H = H; a.D = m.D; a.G = G;
+    a.packed = d->layout == RNN_LAYOUT_PACKED;
+    a.bb = p.bb; a.hs = p.hs; a.ns = p.ns; a.nbb = p.nbb; a.nxcd = 1; a.gpx = 0;
+    a.Hp = m.Hp; a.kp = p.kp;
+    a.rsv = (const float*)(rsv + RL.gates[l]);
+    a.y = y_l;
+    a.dy = dy_l;
+    for (int di = 0; di < m.D; ++di) {
+      const int i = l * m.D + di;
+      a.w_hh[di] = (const float*)w->w_hh[i];
+      a.h0[di] = io->h0 ? (const float*)io->h0 + i * sB : nullptr;
+      a.c0[di] = (d->mode != RNN_MODE_GRU && io->c0) ? (const float*)io->c0 + i * sB : nullptr;
+      a.dh_n[di] = gr->dh_n ? (const float*)gr->dh_n + i * sB : nullptr;
+      a.dc_n[di] = (d->mode != RNN_MODE_GRU && gr->dc_n) ? (const float*)gr->dc_n + i * sB : nullptr;
+      a.dh0[di] = gr->dh0 ? (float*)gr->dh0 + i * sB : nullptr;
+      a.dc0[di] = (d->mode != RNN_MODE_GRU && gr->dc0) ? (float*)gr->dc0 + i * sB : nullptr;
+    }
+    a.dgx = dgx;
+    a.dgh = d->mode == RNN_MODE_GRU ? dgh : nullptr;
+    a.lengths = dev_len;
+    a.offsets = dev_off;
+    a.ex = (float*)(ws + L.ex);
+    a.counters = (unsigned*)(ws + L.counters + (size_t)l * m.D * d->B * kCounterBytes);
+    a.status = (int*)(ws + L.status);
+    if ((rc = hip_status(launch_scan_bwd(a, st))) != RNN_OK) return rc;
+
+    const int in_l = l == 0 ? d->input_size : m.D * H;
+    const float* x_l = l == 0 ? (const float*)io->x : (const float*)(rsv + RL.y[l - 1]);
+    float* dx_l = l == 0 ? (float*)gr->dx : (float*)(ws + (((l - 1) % 2 == 0) ? L.dx0 : L.dx1));
+    for (int di = 0; di < m.D; ++di) {
+      const int i = l * m.D + di;
+      // dW_ih = dG_x^T X_l
+      GemmGenArgs g{};
+      g.A = dgx + di * G; g.sam = 1; g.sak = (long long)m.D * G;
+      g.B = x_l; g.sbk = in_l; g.sbn = 1;
+      g.C = (float*)gr->dw_ih[i]; g.ldc = in_l;
+      g.M = G; g.N = in_l; g.K = rows; g.accumulate = 0;
+      if ((rc = hip_status(launch_gemm_gen(g, st))) != RNN_OK) return rc;
+      // dW_hh = dG_h^T H_prev
+      HprevArgs hp{};
+      hp.y = y_l; hp.ldy = m.D * H; hp.col0 = di * H;
+      hp.h0 = a.h0[di];
+      hp.out = hprev;
+      hp.T = t_max; hp.B = d->B; hp.H = H; hp.packed = a.packed; hp.rev = di == 1;
+      hp.lengths = dev_len; hp.offsets = dev_off;
+      if ((rc = hip_status(launch_hprev(hp, st))) != RNN_OK) return rc;
+      GemmGenArgs gh{};
+      gh.A = dgh + di * G; gh.sam = 1; gh.sak = (long long)m.D * G;
+      gh.B = hprev; gh.sbk = H; gh.sbn = 1;
+      gh.C = (float*)gr->dw_hh[i]; gh.ldc = H;
+      gh.M = G; gh.N = H; gh.K = rows; gh.accumulate = 0;
+      if ((rc = hip_status(launch_gemm_gen(gh, st))) != RNN_OK) return rc;
+      if (d->has_bias) {
+        if ((rc = hip_status(launch_colsum(dgx + di * G, (long long)m.D * G, rows, G, part, kColsumChunks,
+                                           (float*)gr->db_ih[i], st))) != RNN_OK)
+          return rc;
+        if ((rc = hip_status(launch_colsum(dgh + di * G, (long long)m.D * G, rows, G, part, kColsumChunks,
+                                           (float*)gr->db_hh[i], st))) != RNN_OK)
+          return rc;
+      }
+      // dX_l (+)= dG_x W_ih
+      GemmGenArgs gx{};
+      gx.A = dgx + di * G; gx.sam = (long long)m.D * G; gx.sak = 1;
+      gx.B = (const float*)w->w_ih[i]; gx.sbk = in_l; gx.sbn = 1;
+      gx.C = dx_l; gx.ldc = in_l;
+      gx.M = rows; gx.N = in_l; gx.K = G; gx.accumulate = di > 0;
+      if ((rc = hip_status(launch_gemm_gen(gx, st))) != RNN_OK) return rc;
+    }
   }
   return RNN_OK;
 }
@@ -709,6 +970,61 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
     info[9] = p.wreg; info[10] = p.rnt; info[11] = p.rks; info[12] = p.rcpt;
   }
   return RNN_OK;
+}
+
+
+int rnn_reserve_bytes(const RnnDesc* desc, const int32_t* lengths_host, size_t* bytes) {
+  int rc = validate_desc(desc);
+  if (rc != RNN_OK) return rc;
+  if ((rc = validate_train(desc)) != RNN_OK) return rc;
+  if (!bytes) return RNN_E_NULL;
+  long long n_tok = 0;
+  int t_max = 0;
+  if ((rc = validate_lengths(desc, lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
+  *bytes = reserve_of(desc, dims_of(desc, n_tok)).total;
+  return RNN_OK;
+}
+
+int rnn_backward_workspace_bytes(const RnnDesc* desc, const int32_t* lengths_host, size_t* bytes) {
+  int rc = validate_desc(desc);
+  if (rc != RNN_OK) return rc;
+  if ((rc = validate_train(desc)) != RNN_OK) return rc;
+  if (!bytes) return RNN_E_NULL;
+  long long n_tok = 0;
+  int t_max = 0;
+  if ((rc = validate_lengths(desc, lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
+  *bytes = bwd_layout_of(desc, dims_of(desc, n_tok), lengths_host != nullptr).total;
+  return RNN_OK;
+}
+
+int rnn_forward_train(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* reserve,
+                      size_t reserve_bytes, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = validate_desc(desc);
+  if (rc != RNN_OK) return rc;
+  if ((rc = validate_train(desc)) != RNN_OK) return rc;
+  if (!weights || !io) return RNN_E_NULL;
+  long long n_tok = 0;
+  int t_max = 0;
+  if ((rc = validate_lengths(desc, io->lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
+  if (!reserve || reserve_bytes < reserve_of(desc, dims_of(desc, n_tok)).total) return RNN_E_WORKSPACE;
+  if (!aligned(reserve, 16)) return RNN_E_ALIGN;
+  DeviceInfo info;
+  if ((rc = current_device_info(&info)) != RNN_OK) return rc;
+  Prof prof;
+  return forward_rnn(desc, weights, io, (char*)workspace, ws_bytes, reinterpret_cast<hipStream_t>(stream),
+                     info.cus, info.xcds, prof, (char*)reserve);
+}
+
+int rnn_backward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, const RnnGrads* grads,
+                 const void* reserve, size_t reserve_bytes, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = validate_desc(desc);
+  if (rc != RNN_OK) return rc;
+  if ((rc = validate_train(desc)) != RNN_OK) return rc;
+  if (!weights || !io || !grads) return RNN_E_NULL;
+  DeviceInfo info;
+  if ((rc = current_device_info(&info)) != RNN_OK) return rc;
+  return backward_rnn(desc, weights, io, grads, (const char*)reserve, reserve_bytes, (char*)workspace, ws_bytes,
+                      reinterpret_cast<hipStream_t>(stream), info.cus);
 }
 
 int rnn_device_check(void) {

@@ -1,0 +1,254 @@
+// Backward through time of one layer's scan (training), all directions in
+// one launch. It walks the forward's steps in the opposite order with the
+// chain rule through the cell equations (PyTorch conventions; the backward
+// of these cells is what the pytorch/pytorch issue "Integrating CuDNN API
+// for LSTMs with projections" discusses in its thread):
+//   LSTM  dct = dc + dh o (1 - tanh^2 c);  d(i, f, g, o) pre-activations
+//         = (dct g i(1-i), dct c_{t-1} f(1-f), dct i (1-g^2), dh tanh(c) o(1-o));
+//         dc_{t-1} = dct f
+//   GRU   dn = dh (1 - z), dz = dh (h_{t-1} - n), dan = dn (1 - n^2),
+//         dr = dan (W_hn h + b_hn); input side (dr r(1-r), dz z(1-z), dan),
+//         hidden side the same with dan r in the n slot; the direct term
+//         dh z joins dh_{t-1}
+//   dh_{t-1} = W_hh^T (hidden-side gradients) (+ dh z for GRU) + dy_{t-1}.
+//
+// Work split as in the forward: a group of ns workgroups per (direction,
+// batch block), each owning hs hidden units. A member computes the gate
+// gradients of its own units, multiplies them by its own W_hh rows (kept
+// transposed in LDS) into partial sums over all H columns of dh_{t-1},
+// and publishes them; after the group barrier every member sums its own
+// columns over all members in a fixed order (deterministic). The reserve
+// written by the training forward holds the gate values of every token.
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "scan_common.hpp"
+
+namespace rnnk {
+
+namespace {
+
+constexpr int kBT = kScanThreads;
+constexpr int kMaxEptB = 4;  // owned elements per thread: bb * hs <= 1024
+
+__host__ __device__ inline int rup_b(int x, int m) { return (x + m - 1) / m * m; }
+
+struct BwdLds {
+  int wt, wt_ld, as, as_ld, acc, acc_ld, lens, flag, total;  // byte offsets, lds in floats
+};
+
+__host__ __device__ inline BwdLds bwd_lds(const ScanBwdArgs& a) {
+  BwdLds L;
+  const int rows = rup_b(a.bb, 16);
+  // odd numbers of 16-byte chunks per row keep row-parallel reads on
+  // distinct banks
+  L.wt_ld = a.kp + 4;
+  L.as_ld = a.kp + 4;
+  L.acc_ld = a.Hp + 4;
+  int o = 0;
+  L.wt = o;
+  o += a.Hp * L.wt_ld * 4;  // wt[c][q * hs + u] = W_hh[q * H + j0 + u][c]
+  L.as = o;
+  o += rows * L.as_ld * 4;  // own hidden-side gate gradients [rows][gates * hs]
+  L.acc = o;
+  o += rows * L.acc_ld * 4;  // this member's partial sums [rows][Hp]
+  L.lens = o;
+  o += rup_b(a.bb, 4) * 4;
+  L.flag = o;
+  o += 16;
+  L.total = o;
+  return L;
+}
+
+__global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const BwdLds L = bwd_lds(a);
+  const int tid = threadIdx.x;
+  const bool gru = a.mode == kGRU;
+  const int gates = gru ? 3 : 4;
+  const int H = a.H, G = a.G, D = a.D;
+  const int R = gru ? 4 * H : 5 * H;
+  int grp, s;
+  if (a.gpx > 0) {
+    const int xcd = blockIdx.x % a.nxcd, slot = blockIdx.x / a.nxcd;
+    grp = xcd * a.gpx + slot / a.ns;
+    s = slot % a.ns;
+  } else {
+    grp = blockIdx.x / a.ns;
+    s = blockIdx.x % a.ns;
+  }
+  if (grp >= D * a.nbb) return;  // padding slots of the XCD-aligned layout
+  const int d = grp / a.nbb, blk = grp - d * a.nbb;
+  const bool rev = d == 1;
+  const int b0 = blk * a.bb;
+  const int j0 = s * a.hs, hs_act = max(0, min(a.hs, H - j0));
+  unsigned* counter = a.counters + (size_t)grp * 16;
+  int* abort_flag = reinterpret_cast<int*>(lds + L.flag);
+  int* lens = reinterpret_cast<int*>(lds + L.lens);
+  float* wt = reinterpret_cast<float*>(lds + L.wt);
+  float* As = reinterpret_cast<float*>(lds + L.as);
+  float* acc = reinterpret_cast<float*>(lds + L.acc);
+  const int tile_rows = rup_b(a.bb, 16);
+  const bool use_mfma = a.bb % 16 == 0;
+
+  if (tid == 0) *abort_flag = 0;
+  for (int r = tid; r < a.bb; r += kBT) lens[r] = b0 + r < a.B ? (a.lengths ? a.lengths[b0 + r] : a.T) : 0;
+  const float* W = a.w_hh[d];
+  for (int e = tid; e < a.Hp * a.kp; e += kBT) {
+    const int c = e / a.kp, kk = e - c * a.kp;
+    const int q = kk / a.hs, u = kk - q * a.hs;
+    float v = 0.f;
+    if (c < H && q < gates && u < hs_act) v = W[(size_t)(q * H + j0 + u) * H + c];
+    wt[c * L.wt_ld + kk] = v;
+  }
+  for (int e = tid; e < tile_rows * L.as_ld; e += kBT) As[e] = 0.f;
+  __syncthreads();
+  int maxlen = 0;
+  for (int r = 0; r < a.bb; ++r) maxlen = max(maxlen, lens[r]);
+  maxlen = __builtin_amdgcn_readfirstlane(maxlen);
+  const int nsteps = maxlen;
+  // the forward took t = 0 .. maxlen-1 (reverse: maxlen-1 .. 0); walk back
+  auto t_of = [&](int k) { return rev ? k : maxlen - 1 - k; };
+  const __attribute__((address_space(4))) int* offs = (const __attribute__((address_space(4))) int*)a.offsets;
+  auto row_of = [&](int t) -> int { return a.packed ? offs[t] : t * a.B; };
+
+  const uint32_t ex_bytes = (uint32_t)(2 * D * a.ns * a.B * a.Hp) * 4u;
+  const __amdgpu_buffer_rsrc_t ex_rs = make_rsrc(a.ex, ex_bytes);
+  auto ex_el = [&](int par, int m, int b, int c) -> uint32_t {
+    return (uint32_t)((((par * D + d) * a.ns + m) * a.B + b) * a.Hp + c);
+  };
+
+  // owned elements: e = tid + i * kBT -> (row r, unit u)
+  int er[kMaxEptB], eu[kMaxEptB], elen[kMaxEptB];
+  float dcr[kMaxEptB], dhd[kMaxEptB];
+#pragma unroll
+  for (int i = 0; i < kMaxEptB; ++i) {
+    const int e = tid + i * kBT;
+    const int r = e / a.hs, u = e - r * a.hs;
+    er[i] = r;
+    eu[i] = u;
+    elen[i] = (e < a.bb * a.hs && u < hs_act && b0 + r < a.B) ? lens[r] : 0;
+    dcr[i] = 0.f;
+    dhd[i] = 0.f;
+  }
+
+  unsigned nbar = 0;
+  for (int k = 0; k <= nsteps; ++k) {
+    const int t = k < nsteps ? t_of(k) : -1;
+    const int tpk = k > 0 ? t_of(k - 1) : -1;  // the step handled last
+    const int rowbase = t >= 0 ? row_of(t) : 0;
+#pragma unroll
+    for (int i = 0; i < kMaxEptB; ++i) {
+      const int r = er[i], u = eu[i], b = b0 + r, j = j0 + u;
+      const int len = elen[i];
+      const bool act = t >= 0 && t < len;
+      const bool was = tpk >= 0 && tpk < len;
+      // recurrent gradient from the previous step's partial sums, summed
+      // over the members in order
+      float dh_rec = 0.f;
+      if (was) {
+        for (int m0 = 0; m0 < a.ns; m0 += 8) {  // eight loads in flight
+          float pv[8];
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            pv[m] = __builtin_bit_cast(float, coh_load4(ex_rs, ex_el((k - 1) & 1, min(m0 + m, a.ns - 1), b, j) * 4u));
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            if (m0 + m < a.ns) dh_rec += pv[m];
+        }
+        dh_rec += dhd[i];
+      }
+      if (was && !act) {  // this row's walk is over: gradients of the initial state
+        if (a.dh0[d]) a.dh0[d][(size_t)b * H + j] = dh_rec;
+        if (!gru && a.dc0[d]) a.dc0[d][(size_t)b * H + j] = dcr[i];
+      }
+      if (len == 0 || u >= hs_act) continue;
+      if (!act) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q < gates) As[r * L.as_ld + q * a.hs + u] = 0.f;
+        continue;
+      }
+      const size_t row = (size_t)rowbase + b;
+      float dh = was ? dh_rec : (a.dh_n[d] ? a.dh_n[d][(size_t)b * H + j] : 0.f);
+      dh += a.dy[row * (D * H) + d * H + j];
+      const float* rv = a.rsv + (row * D + d) * R + j;
+      const bool has_prev = rev ? (t + 1 < len) : (t >= 1);
+      const int tp = rev ? t + 1 : t - 1;
+      const size_t prow = has_prev ? (size_t)row_of(tp) + b : 0;
+      float* gx = a.dgx + (row * D + d) * G + j;
+      if (gru) {
+        const float rg = rv[0], zg = rv[H], ng = rv[2 * H], ahn = rv[3 * H];
+        const float hp = has_prev ? a.y[prow * (D * H) + d * H + j] : (a.h0[d] ? a.h0[d][(size_t)b * H + j] : 0.f);
+        const float dn = dh * (1.f - zg);
+        const float dz = dh * (hp - ng);
+        const float dan = dn * (1.f - ng * ng);
+        const float dar = dan * ahn * rg * (1.f - rg);
+        const float daz = dz * zg * (1.f - zg);
+        gx[0] = dar;
+        gx[H] = daz;
+        gx[2 * H] = dan;
+        float* gh = a.dgh + (row * D + d) * G + j;
+        gh[0] = dar;
+        gh[H] = daz;
+        gh[2 * H] = dan * rg;
+        As[r * L.as_ld + u] = dar;
+        As[r * L.as_ld + a.hs + u] = daz;
+        As[r * L.as_ld + 2 * a.hs + u] = dan * rg;
+        dhd[i] = dh * zg;
+      } else {
+        const float ig = rv[0], fg = rv[H], gg = rv[2 * H], og = rv[3 * H], c = rv[4 * H];
+        const float dc_in = was ? dcr[i] : (a.dc_n[d] ? a.dc_n[d][(size_t)b * H + j] : 0.f);
+        const float cp = has_prev ? a.rsv[(prow * D + d) * R + 4 * H + j]
+                                  : (a.c0[d] ? a.c0[d][(size_t)b * H + j] : 0.f);
+        const float tc = ftanh(c);
+        const float dct = dc_in + dh * og * (1.f - tc * tc);
+        const float dai = dct * gg * ig * (1.f - ig);
+        const float daf = dct * cp * fg * (1.f - fg);
+        const float dag = dct * ig * (1.f - gg * gg);
+        const float dao = dh * tc * og * (1.f - og);
+        dcr[i] = dct * fg;
+        gx[0] = dai;
+        gx[H] = daf;
+        gx[2 * H] = dag;
+        gx[3 * H] = dao;
+        As[r * L.as_ld + u] = dai;
+        As[r * L.as_ld + a.hs + u] = daf;
+        As[r * L.as_ld + 2 * a.hs + u] = dag;
+        As[r * L.as_ld + 3 * a.hs + u] = dao;
+      }
+    }
+    if (k == nsteps) break;
+    __syncthreads();
+    // this member's share of W_hh^T (hidden-side gradients), all H columns
+    if (use_mfma)
+      mm_mfma<float>(lds, L.as, L.as_ld, L.wt, L.wt_ld, acc, L.acc_ld, tile_rows / 16, a.Hp / 16, a.kp);
+    else
+      mm_valu<float>(lds, L.as, L.as_ld, L.wt, L.wt_ld, acc, L.acc_ld, a.bb, a.Hp, a.kp);
+    __syncthreads();
+    const int cpr = a.Hp / 4;
+    for (int e = tid; e < a.bb * cpr; e += kBT) {
+      const int r = e / cpr, cc = e - r * cpr;
+      if (b0 + r < a.B)
+        coh_store16(ex_rs, ex_el(k & 1, s, b0 + r, 4 * cc) * 4u,
+                    *reinterpret_cast<const u32x4*>(acc + r * L.acc_ld + 4 * cc));
+    }
+    ++nbar;
+    if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+  }
+}
+
+}  // namespace
+
+int scan_bwd_lds_bytes(const ScanBwdArgs& a) { return bwd_lds(a).total; }
+
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t stream) {
+  const int lds = bwd_lds(a).total;
+  hipError_t e = hipFuncSetAttribute((const void*)scan_bwd_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  const int groups = a.D * a.nbb;
+  const int grid = a.gpx > 0 ? a.nxcd * a.gpx * a.ns : groups * a.ns;
+  hipLaunchKernelGGL(scan_bwd_kernel, dim3(grid), dim3(kBT), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rnnk

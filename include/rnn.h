@@ -236,6 +236,29 @@ typedef struct RnnIO {
   void* actions;
 } RnnIO;
 
+/* Gradients for rnn_backward (device pointers, fp32, C-dense, canonical
+ * shapes; the shapes of the tensors they are gradients of):
+ *   dy    like y (PADDED [T, B, D*H] | PACKED [N_tok, D*H]), required;
+ *         positions t >= L_b are never read
+ *   dh_n  [L*D, B, H], dc_n [L*D, B, H] (LSTM) or NULL (= zero)
+ *   dx    like x, required; written whole (zero at t >= L_b in PADDED)
+ *   dh0, dc0 [L*D, B, H] or NULL (= skip)
+ *   dw_ih[i] [G, in_l], dw_hh[i] [G, H], db_ih[i], db_hh[i] [G] for
+ *   i = l*D + d (bias gradients required when has_bias); written, not
+ *   accumulated. */
+typedef struct RnnGrads {
+  const void* dy;
+  const void* dh_n;
+  const void* dc_n;
+  void* dx;
+  void* dh0;
+  void* dc0;
+  void* dw_ih[RNN_MAX_LD];
+  void* dw_hh[RNN_MAX_LD];
+  void* db_ih[RNN_MAX_LD];
+  void* db_hh[RNN_MAX_LD];
+} RnnGrads;
+
 /* Version of this ABI (RNN_ABI_VERSION). */
 int rnn_abi_version(void);
 
@@ -290,6 +313,38 @@ int rnn_read_status(const void* workspace, void* stream, int* device_status);
  * 16-byte chunks per tile per lane}; the plan assumes 16-byte aligned
  * weights. For inspection and tests; touches no device. */
 int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int xcds, int* info, int n_info);
+
+/* Training (backward through time; pytorch/pytorch issue "Integrating CuDNN
+ * API for LSTMs with projections", thread: the backward of these cells).
+ * Built for fp32 LSTM and GRU stacks without clipping, every layout,
+ * length mix, layer count and direction the forward takes; other
+ * combinations return RNN_E_UNSUPPORTED.
+ *
+ * rnn_reserve_bytes: size of the caller-owned reserve that
+ * rnn_forward_train fills and rnn_backward reads (the gate values of every
+ * token, and the outputs of the layers below the last). Host-only. */
+int rnn_reserve_bytes(const RnnDesc* desc, const int32_t* lengths_host, size_t* bytes);
+
+/* Workspace bytes rnn_backward needs (gate-gradient buffers, the exchange of
+ * the backward scan, counters). Host-only. */
+int rnn_backward_workspace_bytes(const RnnDesc* desc, const int32_t* lengths_host, size_t* bytes);
+
+/* rnn_forward that also writes the reserve (16-byte aligned, at least
+ * rnn_reserve_bytes). Same outputs, same workspace as rnn_forward.
+ * Enqueued on `stream`; errors as rnn_forward plus RNN_E_WORKSPACE for a
+ * missing or small reserve. */
+int rnn_forward_train(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* reserve,
+                      size_t reserve_bytes, void* workspace, size_t ws_bytes, void* stream);
+
+/* Gradients of a loss through the forward that rnn_forward_train ran with
+ * the same desc, weights and io (x, h0, c0, lengths and the y it wrote are
+ * read again) and filled `reserve`. For PADDED input, x must be finite at
+ * positions t >= L_b (they enter the weight-gradient products with zero
+ * weight). Enqueued on `stream`; the workspace (16-byte aligned, at least
+ * rnn_backward_workspace_bytes) is independent of the forward's. Device
+ * status as rnn_forward (rnn_read_status on this workspace). */
+int rnn_backward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, const RnnGrads* grads,
+                 const void* reserve, size_t reserve_bytes, void* workspace, size_t ws_bytes, void* stream);
 
 /* RNN_OK when the current device is a gfx950 GPU; RNN_E_DEVICE otherwise. */
 int rnn_device_check(void);

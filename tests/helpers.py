@@ -32,3 +32,24 @@ def assert_close(got, ref, dtype="f32", what=""):
         if nr > 0:
             rel = float(np.linalg.norm(g - r)) / nr
             assert rel <= FP32_RTOL, f"{what}: relative L2 {rel:.3e} > {FP32_RTOL}"
+
+
+# Gradients (backward through time) are sums over every token of products
+# whose terms cancel, so an element can be small next to its neighbours.
+# Reading for fp32: |g - r| <= 1e-4 |r| + 1e-5 max|r| elementwise (the
+# absolute part scaled to the tensor), and relative L2 error <= 1e-4.
+def assert_grad_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} != {ref.shape}"
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    err = np.abs(got - ref)
+    lim = FP32_RTOL * np.abs(ref) + FP32_ATOL * max(scale, 1e-30)
+    bad = err > lim
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {ref.size} elements over tolerance "
+                           f"(worst abs {float(err.max()):.3e}, scale {scale:.3e})")
+    nr = float(np.linalg.norm(ref))
+    if nr > 0:
+        rel = float(np.linalg.norm(got - ref)) / nr
+        assert rel <= FP32_RTOL, f"{what}: relative L2 {rel:.3e} > {FP32_RTOL}"
