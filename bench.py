@@ -84,6 +84,8 @@ def parse():
     ap.add_argument("--tile-batch", type=int, default=0)
     ap.add_argument("--tile-hidden", type=int, default=0)
     ap.add_argument("--placement", type=int, default=0, help="0 auto, 1 flat, 2 XCD-aligned groups")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step (rnn_forward_train + rnn_backward) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -173,6 +175,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.train:
+        train_main(args)
         return
     import torch
 
@@ -369,6 +374,129 @@ def main():
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline_any(spec, d, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def train_flops(spec, d):
+    """Algorithmic flops of one training step: the forward (input GEMM and
+    recurrent product per layer) and the backward (recurrent product,
+    dW_ih, dW_hh and dX per layer)."""
+    D = 2 if spec.bidirectional else 1
+    G = (3 if spec.mode == "gru" else 4) * spec.hidden_size
+    H = spec.hidden_size
+    L = d["lengths"]
+    tokens = int(L.sum()) if L is not None else spec.T * spec.B
+    rows = tokens if spec.layout == "packed" else spec.T * spec.B
+    fl = 0
+    for layer in range(spec.num_layers):
+        in_l = spec.input_size if layer == 0 else D * H
+        fl += 2 * rows * D * G * in_l + 2 * tokens * D * G * H            # forward
+        fl += 2 * tokens * D * G * H                                      # backward recurrent product
+        fl += 2 * rows * D * G * in_l * 2 + 2 * rows * D * G * H          # dW_ih, dX, dW_hh
+    return fl, tokens
+
+
+def train_main(args):
+    """One training step = rnn_forward_train + rnn_backward over the
+    workload, inputs and upstream gradients resident on the GPU."""
+    import torch
+
+    import gru_sequence_scan_amd as gss
+    import synth
+
+    name = synth.ORDER[int(args.workload) - 1] if args.workload.isdigit() else args.workload
+    spec = synth.spec(name)
+    if spec.mode not in ("lstm", "gru") or spec.dtype != "f32":
+        print(f"training is built for fp32 LSTM / GRU stacks; {name} is {spec.dtype} {spec.mode}",
+              file=sys.stderr)
+        sys.exit(2)
+    d = synth.make_inputs(name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def T(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    params = [{k: T(v) for k, v in p.items() if v is not None} for p in d["params"]]
+    x = T(np.nan_to_num(d["x"]))
+    D = 2 if spec.bidirectional else 1
+    H = spec.hidden_size
+    rng = np.random.default_rng(spec.seed + 1)
+    yshape = (x.shape[0], D * H) if spec.layout == "packed" else (spec.T, spec.B, D * H)
+    dy = T(rng.normal(size=yshape))
+    kw = dict(lengths=d["lengths"], layout=spec.layout, num_layers=spec.num_layers,
+              bidirectional=spec.bidirectional, tile_batch=args.tile_batch, tile_hidden=args.tile_hidden)
+
+    def step():
+        _, ctx = gss.rnn_forward_train(spec.mode, x, params, **kw)
+        return gss.rnn_backward(ctx, dy)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1) / K
+    flops, tokens = train_flops(spec, d)
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["f32_mfma"]
+    line = {
+        "metric": METRIC, "value": tokens / (elapsed / K), "unit": UNIT, "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": elapsed / K * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "pass": "forward+backward", "mode": spec.mode, "T": spec.T, "B": spec.B,
+                   "input": spec.input_size, "hidden": H, "layers": spec.num_layers,
+                   "bidirectional": spec.bidirectional, "layout": spec.layout, "tokens": tokens},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None, "kernel": "training step (all kernels)",
+                     "avg_us": ev_ms * 1e3, "algorithmic_flops": flops},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_train(spec, d, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_train(spec, d, seconds):
+    """The float64 oracle's forward + BPTT on a sample of batch rows (all
+    timesteps), sized from a one-row probe."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    L = d["lengths"]
+    order = np.random.default_rng(0).permutation(spec.B)
+    D = 2 if spec.bidirectional else 1
+
+    def run(rows):
+        sub = np.sort(order[:rows])
+        lengths = None if L is None else L[sub]
+        if spec.layout == "packed":
+            x = oracle.pack_sequence(np.nan_to_num(d["x_padded"][:, sub]), lengths)
+            dy = np.ones((x.shape[0], D * spec.hidden_size))
+        else:
+            x = d["x"][:, sub]
+            dy = np.ones((spec.T, rows, D * spec.hidden_size))
+        kw = dict(lengths=lengths, num_layers=spec.num_layers, bidirectional=spec.bidirectional,
+                  layout=spec.layout)
+        t0 = time.perf_counter()
+        oracle.rnn_forward(spec.mode, x, d["params"], **kw)
+        oracle.rnn_backward(spec.mode, x, d["params"], dy, **kw)
+        el = time.perf_counter() - t0
+        return (int(lengths.sum()) if lengths is not None else spec.T * rows), el
+
+    _, t1 = run(1)
+    rows = int(min(spec.B, max(1, seconds / max(t1, 1e-6))))
+    tokens, el = run(rows)
+    return {"value": tokens / el, "unit": UNIT, "cores": int(threads), "kind": "oracle",
+            "sample": f"forward + backward of {rows} of {spec.B} batch rows over all timesteps, {el:.1f} s"}
 
 
 def cpu_baseline_any(spec, d, seconds):

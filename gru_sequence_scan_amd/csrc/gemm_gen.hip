@@ -14,8 +14,12 @@ namespace {
 
 constexpr int kGemmThreads = 256;
 constexpr int kTile = 64;   // 64 x 64 output tile, four waves of 32 x 32
-constexpr int kSlab = 16;   // k per LDS stage
+constexpr int kSlab = 32;   // k per LDS stage
+constexpr int kPer = kTile * kSlab / kGemmThreads;  // elements per thread per operand and stage
 
+// Each stage's operands are loaded into registers one stage ahead, so the
+// global-load latency overlaps the previous stage's MFMAs; consecutive
+// threads walk each operand's unit-stride dimension (coalesced).
 __global__ void __launch_bounds__(kGemmThreads) gemm_gen_kernel(GemmGenArgs a) {
   // k-major tiles: As[k][m], Bs[k][n]; one column of padding per row
   __shared__ float As[kSlab][kTile + 1];
@@ -27,20 +31,36 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_gen_kernel(GemmGenArgs a) {
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-  const bool a_kfast = a.sak == 1;  // consecutive threads walk the unit-stride dimension
+  const bool a_kfast = a.sak == 1;
   const bool b_nfast = a.sbn == 1;
+  int am[kPer], ak[kPer], bn[kPer], bk[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid + i * kGemmThreads;
+    am[i] = a_kfast ? e / kSlab : e % kTile;
+    ak[i] = a_kfast ? e % kSlab : e / kTile;
+    bn[i] = b_nfast ? e % kTile : e / kSlab;
+    bk[i] = b_nfast ? e / kTile : e % kSlab;
+  }
+  float ra[kPer], rb[kPer];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int gm = m0 + am[i], gk = k0 + ak[i];
+      ra[i] = (gm < a.M && gk < a.K) ? a.A[gm * a.sam + gk * a.sak] : 0.f;
+      const int gn = n0 + bn[i], gk2 = k0 + bk[i];
+      rb[i] = (gn < a.N && gk2 < a.K) ? a.B[gk2 * a.sbk + gn * a.sbn] : 0.f;
+    }
+  };
+  load(0);
   for (int k0 = 0; k0 < a.K; k0 += kSlab) {
 #pragma unroll
-    for (int i = 0; i < kTile * kSlab / kGemmThreads; ++i) {
-      const int e = tid + i * kGemmThreads;
-      const int am = a_kfast ? e / kSlab : e % kTile, ak = a_kfast ? e % kSlab : e / kTile;
-      const int bn = b_nfast ? e % kTile : e / kSlab, bk = b_nfast ? e / kTile : e % kSlab;
-      const int gm = m0 + am, gk = k0 + ak;
-      As[ak][am] = (gm < a.M && gk < a.K) ? a.A[gm * a.sam + gk * a.sak] : 0.f;
-      const int gn = n0 + bn, gk2 = k0 + bk;
-      Bs[bk][bn] = (gn < a.N && gk2 < a.K) ? a.B[gk2 * a.sbk + gn * a.sbn] : 0.f;
+    for (int i = 0; i < kPer; ++i) {
+      As[ak[i]][am[i]] = ra[i];
+      Bs[bk[i]][bn[i]] = rb[i];
     }
     __syncthreads();
+    if (k0 + kSlab < a.K) load(k0 + kSlab);
 #pragma unroll
     for (int kk = 0; kk < kSlab; kk += 2)
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + half][wm * 32 + l32], Bs[kk + half][wn * 32 + l32], acc,

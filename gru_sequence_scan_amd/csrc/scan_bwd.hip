@@ -146,13 +146,13 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
       // over the members in order
       float dh_rec = 0.f;
       if (was) {
-        for (int m0 = 0; m0 < a.ns; m0 += 8) {  // eight loads in flight
-          float pv[8];
+        for (int m0 = 0; m0 < a.ns; m0 += 32) {  // up to 32 loads in flight
+          float pv[32];
 #pragma unroll
-          for (int m = 0; m < 8; ++m)
+          for (int m = 0; m < 32; ++m)
             pv[m] = __builtin_bit_cast(float, coh_load4(ex_rs, ex_el((k - 1) & 1, min(m0 + m, a.ns - 1), b, j) * 4u));
 #pragma unroll
-          for (int m = 0; m < 8; ++m)
+          for (int m = 0; m < 32; ++m)
             if (m0 + m < a.ns) dh_rec += pv[m];
         }
         dh_rec += dhd[i];
