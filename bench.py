@@ -38,7 +38,7 @@ UNIT = "timestep\u00b7batch/s"
 CSRC = os.path.join(ROOT, "gru_sequence_scan_amd", "csrc")
 KERNEL_SOURCES = {
     "gemm_xw": ["gemm_xw.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
-    "scan": ["scan.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
+    "scan": ["scan.hip", "scan_common.hpp", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
     "rssm": ["rssm.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
     "scan_wave": ["scan_wave.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
 }

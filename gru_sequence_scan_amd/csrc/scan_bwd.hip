@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kBT = kScanThreads;
 constexpr int kMaxEptB = 4;  // owned elements per thread: bb * hs <= 1024
+constexpr int kBwdMaxMembersDev = 64;  // members per group (the planner's bound)
 
 __host__ __device__ inline int rup_b(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -142,19 +143,41 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
       const int len = elen[i];
       const bool act = t >= 0 && t < len;
       const bool was = tpk >= 0 && tpk < len;
+      // Every load this element needs is issued before the first is used, so
+      // their latencies overlap: this step's dy and reserved gate values, the
+      // previous state, then the previous step's partial sums of all members.
+      const size_t row = (size_t)rowbase + b;
+      const bool has_prev = act && (rev ? (t + 1 < len) : (t >= 1));
+      const int tp = rev ? t + 1 : t - 1;
+      const size_t prow = has_prev ? (size_t)row_of(tp) + b : 0;
+      float rvv[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+      float dyv = 0.f, prevv = 0.f, dhn = 0.f, dcn = 0.f;
+      if (act) {
+        const float* rv = a.rsv + (row * D + d) * R + j;
+#pragma unroll
+        for (int q = 0; q < 5; ++q)
+          if (q < (gru ? 4 : 5)) rvv[q] = rv[q * H];
+        dyv = a.dy[row * (D * H) + d * H + j];
+        if (gru)
+          prevv = has_prev ? a.y[prow * (D * H) + d * H + j] : (a.h0[d] ? a.h0[d][(size_t)b * H + j] : 0.f);
+        else
+          prevv = has_prev ? a.rsv[(prow * D + d) * R + 4 * H + j] : (a.c0[d] ? a.c0[d][(size_t)b * H + j] : 0.f);
+        if (!was) {
+          dhn = a.dh_n[d] ? a.dh_n[d][(size_t)b * H + j] : 0.f;
+          dcn = (!gru && a.dc_n[d]) ? a.dc_n[d][(size_t)b * H + j] : 0.f;
+        }
+      }
       // recurrent gradient from the previous step's partial sums, summed
-      // over the members in order
+      // over the members in order (up to 64 loads in flight)
       float dh_rec = 0.f;
       if (was) {
-        for (int m0 = 0; m0 < a.ns; m0 += 32) {  // up to 32 loads in flight
-          float pv[32];
+        float pv[kBwdMaxMembersDev];
 #pragma unroll
-          for (int m = 0; m < 32; ++m)
-            pv[m] = __builtin_bit_cast(float, coh_load4(ex_rs, ex_el((k - 1) & 1, min(m0 + m, a.ns - 1), b, j) * 4u));
+        for (int m = 0; m < kBwdMaxMembersDev; ++m)
+          if (m < a.ns) pv[m] = __builtin_bit_cast(float, coh_load4(ex_rs, ex_el((k - 1) & 1, m, b, j) * 4u));
 #pragma unroll
-          for (int m = 0; m < 32; ++m)
-            if (m0 + m < a.ns) dh_rec += pv[m];
-        }
+        for (int m = 0; m < kBwdMaxMembersDev; ++m)
+          if (m < a.ns) dh_rec += pv[m];
         dh_rec += dhd[i];
       }
       if (was && !act) {  // this row's walk is over: gradients of the initial state
@@ -168,17 +191,11 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
           if (q < gates) As[r * L.as_ld + q * a.hs + u] = 0.f;
         continue;
       }
-      const size_t row = (size_t)rowbase + b;
-      float dh = was ? dh_rec : (a.dh_n[d] ? a.dh_n[d][(size_t)b * H + j] : 0.f);
-      dh += a.dy[row * (D * H) + d * H + j];
-      const float* rv = a.rsv + (row * D + d) * R + j;
-      const bool has_prev = rev ? (t + 1 < len) : (t >= 1);
-      const int tp = rev ? t + 1 : t - 1;
-      const size_t prow = has_prev ? (size_t)row_of(tp) + b : 0;
+      const float dh = (was ? dh_rec : dhn) + dyv;
       float* gx = a.dgx + (row * D + d) * G + j;
       if (gru) {
-        const float rg = rv[0], zg = rv[H], ng = rv[2 * H], ahn = rv[3 * H];
-        const float hp = has_prev ? a.y[prow * (D * H) + d * H + j] : (a.h0[d] ? a.h0[d][(size_t)b * H + j] : 0.f);
+        const float rg = rvv[0], zg = rvv[1], ng = rvv[2], ahn = rvv[3];
+        const float hp = prevv;
         const float dn = dh * (1.f - zg);
         const float dz = dh * (hp - ng);
         const float dan = dn * (1.f - ng * ng);
@@ -196,10 +213,9 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
         As[r * L.as_ld + 2 * a.hs + u] = dan * rg;
         dhd[i] = dh * zg;
       } else {
-        const float ig = rv[0], fg = rv[H], gg = rv[2 * H], og = rv[3 * H], c = rv[4 * H];
-        const float dc_in = was ? dcr[i] : (a.dc_n[d] ? a.dc_n[d][(size_t)b * H + j] : 0.f);
-        const float cp = has_prev ? a.rsv[(prow * D + d) * R + 4 * H + j]
-                                  : (a.c0[d] ? a.c0[d][(size_t)b * H + j] : 0.f);
+        const float ig = rvv[0], fg = rvv[1], gg = rvv[2], og = rvv[3], c = rvv[4];
+        const float dc_in = was ? dcr[i] : dcn;
+        const float cp = prevv;
         const float tc = ftanh(c);
         const float dct = dc_in + dh * og * (1.f - tc * tc);
         const float dai = dct * gg * ig * (1.f - ig);
@@ -218,13 +234,13 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
       }
     }
     if (k == nsteps) break;
-    __syncthreads();
+    lds_barrier();
     // this member's share of W_hh^T (hidden-side gradients), all H columns
     if (use_mfma)
       mm_mfma<float>(lds, L.as, L.as_ld, L.wt, L.wt_ld, acc, L.acc_ld, tile_rows / 16, a.Hp / 16, a.kp);
     else
       mm_valu<float>(lds, L.as, L.as_ld, L.wt, L.wt_ld, acc, L.acc_ld, a.bb, a.Hp, a.kp);
-    __syncthreads();
+    lds_barrier();
     const int cpr = a.Hp / 4;
     for (int e = tid; e < a.bb * cpr; e += kBT) {
       const int r = e / cpr, cc = e - r * cpr;
