@@ -48,20 +48,20 @@ KERNEL_SOURCES = {
 # the ratio the same counter reads for a plain copy of known size
 # (--calibrate-copy). Valid only for the kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1584806, "write_bytes": 209408,
-                  "sources": "d3d3c303c7192ed7"},
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186348324, "write_bytes": 25801363,
-                   "sources": "daf4657f46f4da58"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484773337, "write_bytes": 137109504,
-                    "sources": "d3d3c303c7192ed7"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": 0, "fetch_bytes": 612258183, "write_bytes": 100467712,
-                      "sources": "d3d3c303c7192ed7"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430796854, "write_bytes": 162342912,
-                        "sources": "d3d3c303c7192ed7"},
-    "lstm_t256_b1_small": {"kernel": "scan", "index": 0, "fetch_bytes": 183746, "write_bytes": 16512,
-                         "sources": "d3d3c303c7192ed7"},
-    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 348807202, "write_bytes": 47403686,
-                         "sources": "daf4657f46f4da58"},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1578755, "write_bytes": 209408,
+                  "sources": "e7b0e248aab102ee"},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186349358, "write_bytes": 25801350,
+                   "sources": "f697425d4261139a"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484741994, "write_bytes": 137109504,
+                    "sources": "e7b0e248aab102ee"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": 1, "fetch_bytes": 612226732, "write_bytes": 100467712,
+                      "sources": "e7b0e248aab102ee"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430798996, "write_bytes": 162342912,
+                        "sources": "e7b0e248aab102ee"},
+    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 89031, "write_bytes": 16512,
+                         "sources": "8fa5d4c56ef316cf"},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 348819337, "write_bytes": 47403520,
+                         "sources": "f697425d4261139a"},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
