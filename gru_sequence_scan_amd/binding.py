@@ -78,6 +78,7 @@ class RnnGrads(ctypes.Structure):
         ("dy", ctypes.c_void_p), ("dh_n", ctypes.c_void_p), ("dc_n", ctypes.c_void_p),
         ("dx", ctypes.c_void_p), ("dh0", ctypes.c_void_p), ("dc0", ctypes.c_void_p),
         ("dw_ih", _PtrArr), ("dw_hh", _PtrArr), ("db_ih", _PtrArr), ("db_hh", _PtrArr),
+        ("dw_hr", _PtrArr),
     ]
 
 
@@ -373,7 +374,7 @@ class TrainContext:
 
 
 def rnn_forward_train(mode, x, params, **kw):
-    """rnn_forward that also keeps what the backward needs (fp32 LSTM / GRU).
+    """rnn_forward that also keeps what the backward needs (fp32 LSTM / LSTMP / GRU).
     Returns ((y, h_n, c_n), ctx); pass ctx to rnn_backward."""
     return rnn_forward(mode, x, params, _train=True, **kw)
 
@@ -382,18 +383,19 @@ def rnn_backward(ctx, dy, dh_n=None, dc_n=None):
     """Gradients through the forward recorded in ctx, given dy (shape of y)
     and optionally dh_n, dc_n (shape of h_n, c_n). Returns (dx, dh0, dc0,
     grads) with grads a list over layer * D + direction of dicts dw_ih,
-    dw_hh, db_ih, db_hh (bias entries only with biases); dc0 None for GRU."""
+    dw_hh, db_ih, db_hh (bias entries only with biases) and dw_hr (LSTMP);
+    dc0 None for GRU."""
     y = ctx.keep[-3]
     device, dtype = y.device, y.dtype
     desc, io = ctx.desc, ctx.io
     LD = desc.num_layers * ctx.D
-    B, H = desc.B, ctx.H
+    B, H, K = desc.B, ctx.H, ctx.K
     dy = _check(dy, "dy", tuple(y.shape), dtype, device)
-    dh_n = _check(dh_n, "dh_n", (LD, B, H), dtype, device)
+    dh_n = _check(dh_n, "dh_n", (LD, B, K), dtype, device)
     dc_n = _check(dc_n, "dc_n", (LD, B, H), dtype, device) if ctx.mode != "gru" else None
     x = ctx.keep[0]
     dx = torch.empty_like(x)
-    dh0 = torch.empty((LD, B, H), dtype=dtype, device=device)
+    dh0 = torch.empty((LD, B, K), dtype=dtype, device=device)
     dc0 = torch.empty((LD, B, H), dtype=dtype, device=device) if ctx.mode != "gru" else None
     g = RnnGrads()
     g.dy, g.dh_n, g.dc_n = _ptr(dy), _ptr(dh_n), _ptr(dc_n)
@@ -404,6 +406,8 @@ def rnn_backward(ctx, dy, dh_n=None, dc_n=None):
         if desc.has_bias:
             gi["db_ih"] = torch.empty_like(p["b_ih"])
             gi["db_hh"] = torch.empty_like(p["b_hh"])
+        if ctx.mode == "lstmp":
+            gi["dw_hr"] = torch.empty_like(p["w_hr"])
         for k, t in gi.items():
             getattr(g, k)[i] = t.data_ptr()
         grads.append(gi)

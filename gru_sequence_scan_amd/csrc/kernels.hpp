@@ -113,8 +113,15 @@ struct ScanBwdArgs {
   const int* lengths;    // device [B] or null
   const int* offsets;    // device [T + 1] (packed)
   float* ex;             // [2][D][ns][B][Hp] per-member partial sums of W_hh^T dG
+                         // (LSTMP: [2][D][ns][B][Pp], the partials over P)
   unsigned* counters;
   int* status;
+  // LSTMP (mode kLSTMP): recurrent width P, members also own ps projection
+  // outputs; dy, y, h0, dh_n, dh0 have width P.
+  int P, Pp, ps;
+  const float* w_hr[2];  // [P, H]
+  float* dh;             // [rows, D, P] the step gradients w.r.t. h_t (for dW_hr)
+  float* ex2;            // [D][B][Pp] the whole dh_t of the step, coherent
 };
 int scan_bwd_lds_bytes(const ScanBwdArgs& a);
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t stream);
@@ -145,6 +152,9 @@ struct HprevArgs {
   const int* offsets;              // device [T + 1] (packed)
 };
 hipError_t launch_hprev(const HprevArgs& a, hipStream_t stream);
+// out[row, j] = o * tanh(c) of direction d from an LSTM reserve ([rows, D,
+// 5H]: i, f, g, o, c), i.e. the cell output m_t that LSTMP projects.
+hipError_t launch_mgather(const float* rsv, int D, int d, int H, long long rows, float* out, hipStream_t stream);
 
 // Kernel 3: persistent RSSM-prior unroll.
 struct RssmArgs {

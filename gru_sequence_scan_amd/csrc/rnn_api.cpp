@@ -539,15 +539,15 @@ ReserveLayout reserve_of(const RnnDesc* d, const Dims& m) {
     r.gates[l] = o;
     o = align_up(o + (size_t)m.rows * m.D * r.R * 4, kAlign);
     r.y[l] = o;
-    if (l + 1 < d->num_layers) o = align_up(o + (size_t)m.rows * m.D * d->hidden_size * 4, kAlign);
+    if (l + 1 < d->num_layers) o = align_up(o + (size_t)m.rows * m.D * m.K * 4, kAlign);
   }
   r.total = o;
   return r;
 }
 
-// Training is built for fp32 LSTM and GRU stacks without clipping.
+// Training is built for fp32 LSTM, LSTMP and GRU stacks without clipping.
 int validate_train(const RnnDesc* d) {
-  if (d->mode != RNN_MODE_LSTM && d->mode != RNN_MODE_GRU) return RNN_E_UNSUPPORTED;
+  if (d->mode != RNN_MODE_LSTM && d->mode != RNN_MODE_GRU && d->mode != RNN_MODE_LSTMP) return RNN_E_UNSUPPORTED;
   if (d->dtype != RNN_DTYPE_F32 || d->clip != 0) return RNN_E_UNSUPPORTED;
   return RNN_OK;
 }
@@ -611,7 +611,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   // by the backward's products, so the ones the scan never writes are zero
   if (rsv && has_len && d->layout == RNN_LAYOUT_PADDED)
     for (int l = 0; l + 1 < d->num_layers; ++l)
-      if ((rc = hip_status(launch_fill_zero(rsv + RL.y[l], (size_t)m.rows * m.D * d->hidden_size * 4, st))) != RNN_OK)
+      if ((rc = hip_status(launch_fill_zero(rsv + RL.y[l], (size_t)m.rows * m.D * m.K * 4, st))) != RNN_OK)
         return rc;
   float* gx = (float*)(ws + L.gx);
   const void* layer_in = io->x;
@@ -691,7 +691,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
 constexpr int kBwdMaxMembers = 64;
 
 struct BwdPlan {
-  int bb, hs, ns, nbb, kp, lds;
+  int bb, hs, ns, nbb, kp, lds, ps;
 };
 
 // Same shape of search as plan_scan: every group co-resident, LDS within a
@@ -699,7 +699,8 @@ struct BwdPlan {
 // exchange (write a row block of all H columns, read the owned columns of
 // every member).
 int plan_scan_bwd(const RnnDesc* d, const Dims& m, int cus, BwdPlan* out) {
-  const int H = d->hidden_size, B = d->B, Hp = m.Hp;
+  const int H = d->hidden_size, B = d->B, Hp = m.Kp;  // partial-sum width: the recurrent width K, padded
+  const bool proj = d->mode == RNN_MODE_LSTMP;
   std::vector<int> bbs, hss;
   if (d->tile_batch > 0) {
     bbs.push_back(d->tile_batch);
@@ -719,16 +720,20 @@ int plan_scan_bwd(const RnnDesc* d, const Dims& m, int cus, BwdPlan* out) {
       if (bb < 1 || hs < 1 || hs % 4 != 0 || bb * hs > 1024) continue;
       const int ns = cdiv(H, hs), nbb = cdiv(B, bb);
       if (ns > kBwdMaxMembers || (long long)m.D * nbb * ns > cus) continue;
+      const int ps = proj ? cdiv(m.K, ns) : 0;
+      if (bb * ps > 1024) continue;
       ScanBwdArgs a{};
-      a.mode = d->mode == RNN_MODE_GRU ? kGRU : kLSTM;
+      a.mode = d->mode == RNN_MODE_GRU ? kGRU : (proj ? kLSTMP : kLSTM);
       a.bb = bb; a.hs = hs; a.Hp = Hp; a.kp = rup(m.gates * hs, 16);
+      a.P = m.K; a.Pp = Hp; a.ps = ps;
       const int lds = scan_bwd_lds_bytes(a);
       if (lds > kMaxLds) continue;
-      const double xbytes = (double)ns * std::min(bb, B) * hs * 4 + (double)bb * Hp * 4;
-      const double t = barrier_us(ns) + xbytes / 100e3 + mm_us(bb % 16 == 0, 4, bb, Hp, a.kp);
+      const double xbytes = (double)ns * std::min(bb, B) * (proj ? ps : hs) * 4 + (double)bb * Hp * 4;
+      double t = barrier_us(ns) + xbytes / 100e3 + mm_us(bb % 16 == 0, 4, bb, Hp, a.kp);
+      if (proj) t += barrier_us(ns) + (double)bb * Hp * 4 / 100e3 + mm_us(bb % 16 == 0, 4, bb, rup(hs, 16), Hp);
       if (t < best) {
         best = t;
-        *out = BwdPlan{bb, hs, ns, nbb, a.kp, lds};
+        *out = BwdPlan{bb, hs, ns, nbb, a.kp, lds, ps};
         found = true;
       }
     }
@@ -737,7 +742,7 @@ int plan_scan_bwd(const RnnDesc* d, const Dims& m, int cus, BwdPlan* out) {
 }
 
 struct BwdLayout {
-  size_t status, counters, ints, dgx, dgh, hprev, dx0, dx1, ex, part, total;
+  size_t status, counters, ints, dgx, dgh, hprev, dx0, dx1, ex, part, ex2, dh, mbuf, total;
   size_t counters_bytes;
   int n_ints;
 };
@@ -758,12 +763,17 @@ BwdLayout bwd_layout_of(const RnnDesc* d, const Dims& m, bool has_lengths) {
   w.ints = take((size_t)std::max(w.n_ints, 1) * 4);
   w.dgx = take(rows * m.D * m.G * 4);
   w.dgh = d->mode == RNN_MODE_GRU ? take(rows * m.D * m.G * 4) : w.dgx;
-  w.hprev = take(rows * d->hidden_size * 4);
-  const size_t dxb = rows * m.D * d->hidden_size * 4;
+  w.hprev = take(rows * m.K * 4);
+  const size_t dxb = rows * m.D * m.K * 4;
   w.dx0 = d->num_layers > 1 ? take(dxb) : 0;
   w.dx1 = d->num_layers > 2 ? take(dxb) : 0;
-  w.ex = take((size_t)2 * m.D * kBwdMaxMembers * d->B * m.Hp * 4);
-  w.part = take((size_t)kColsumChunks * m.G * 4);
+  w.ex = take((size_t)2 * m.D * kBwdMaxMembers * d->B * m.Kp * 4);
+  w.part = take((size_t)kColsumChunks * std::max(m.G, m.K) * 4);
+  if (d->mode == RNN_MODE_LSTMP) {
+    w.ex2 = take((size_t)m.D * d->B * m.Kp * 4);
+    w.dh = take(rows * m.D * m.K * 4);
+    w.mbuf = take(rows * d->hidden_size * 4);
+  }
   w.total = o;
   return w;
 }
@@ -775,10 +785,13 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
   int t_max = 0;
   if ((rc = validate_lengths(d, io->lengths_host, &n_tok, &t_max)) != RNN_OK) return rc;
   const Dims m = dims_of(d, n_tok);
-  const int LD = d->num_layers * m.D, H = d->hidden_size, G = m.G;
+  const int LD = d->num_layers * m.D, H = d->hidden_size, G = m.G, K = m.K;
+  const bool proj = d->mode == RNN_MODE_LSTMP;
   for (int i = 0; i < LD; ++i) {
     if ((rc = check_ptr(w->w_ih[i], 4)) != RNN_OK || (rc = check_ptr(w->w_hh[i], 4)) != RNN_OK) return rc;
     if ((rc = check_ptr(gr->dw_ih[i], 4)) != RNN_OK || (rc = check_ptr(gr->dw_hh[i], 4)) != RNN_OK) return rc;
+    if (proj && ((rc = check_ptr(w->w_hr[i], 4)) != RNN_OK || (rc = check_ptr(gr->dw_hr[i], 4)) != RNN_OK))
+      return rc;
     if (d->has_bias &&
         ((rc = check_ptr(gr->db_ih[i], 4)) != RNN_OK || (rc = check_ptr(gr->db_hh[i], 4)) != RNN_OK))
       return rc;
@@ -822,32 +835,38 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
   if (has_len && d->layout == RNN_LAYOUT_PADDED) {
     if ((rc = hip_status(launch_fill_zero(dgx, gbytes, st))) != RNN_OK) return rc;
     if (dgh != dgx && (rc = hip_status(launch_fill_zero(dgh, gbytes, st))) != RNN_OK) return rc;
+    if (proj && (rc = hip_status(launch_fill_zero(ws + L.dh, (size_t)m.rows * m.D * K * 4, st))) != RNN_OK)
+      return rc;
   }
   float* hprev = (float*)(ws + L.hprev);
   float* part = (float*)(ws + L.part);
-  const size_t sB = (size_t)d->B * H;
+  const size_t sB = (size_t)d->B * H, sK = (size_t)d->B * K;
   const int rows = (int)m.rows;
   for (int l = d->num_layers - 1; l >= 0; --l) {
     const float* y_l = l == d->num_layers - 1 ? (const float*)io->y : (const float*)(rsv + RL.y[l]);
     const float* dy_l = l == d->num_layers - 1 ? (const float*)gr->dy
                                                : (const float*)(ws + ((l % 2 == 0) ? L.dx0 : L.dx1));
     ScanBwdArgs a{};
-    a.mode = d->mode == RNN_MODE_GRU ? kGRU : kLSTM;
+    a.mode = d->mode == RNN_MODE_GRU ? kGRU : (proj ? kLSTMP : kLSTM);
     a.T = t_max; a.B = d->B; a.H = H; a.D = m.D; a.G = G;
     a.packed = d->layout == RNN_LAYOUT_PACKED;
     a.bb = p.bb; a.hs = p.hs; a.ns = p.ns; a.nbb = p.nbb; a.nxcd = 1; a.gpx = 0;
-    a.Hp = m.Hp; a.kp = p.kp;
+    a.Hp = m.Kp; a.kp = p.kp;
+    a.P = K; a.Pp = m.Kp; a.ps = p.ps;
+    a.dh = proj ? (float*)(ws + L.dh) : nullptr;
+    a.ex2 = proj ? (float*)(ws + L.ex2) : nullptr;
     a.rsv = (const float*)(rsv + RL.gates[l]);
     a.y = y_l;
     a.dy = dy_l;
     for (int di = 0; di < m.D; ++di) {
       const int i = l * m.D + di;
       a.w_hh[di] = (const float*)w->w_hh[i];
-      a.h0[di] = io->h0 ? (const float*)io->h0 + i * sB : nullptr;
+      a.w_hr[di] = proj ? (const float*)w->w_hr[i] : nullptr;
+      a.h0[di] = io->h0 ? (const float*)io->h0 + i * sK : nullptr;
       a.c0[di] = (d->mode != RNN_MODE_GRU && io->c0) ? (const float*)io->c0 + i * sB : nullptr;
-      a.dh_n[di] = gr->dh_n ? (const float*)gr->dh_n + i * sB : nullptr;
+      a.dh_n[di] = gr->dh_n ? (const float*)gr->dh_n + i * sK : nullptr;
       a.dc_n[di] = (d->mode != RNN_MODE_GRU && gr->dc_n) ? (const float*)gr->dc_n + i * sB : nullptr;
-      a.dh0[di] = gr->dh0 ? (float*)gr->dh0 + i * sB : nullptr;
+      a.dh0[di] = gr->dh0 ? (float*)gr->dh0 + i * sK : nullptr;
       a.dc0[di] = (d->mode != RNN_MODE_GRU && gr->dc0) ? (float*)gr->dc0 + i * sB : nullptr;
     }
     a.dgx = dgx;
@@ -859,7 +878,7 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
     a.status = (int*)(ws + L.status);
     if ((rc = hip_status(launch_scan_bwd(a, st))) != RNN_OK) return rc;
 
-    const int in_l = l == 0 ? d->input_size : m.D * H;
+    const int in_l = l == 0 ? d->input_size : m.D * K;
     const float* x_l = l == 0 ? (const float*)io->x : (const float*)(rsv + RL.y[l - 1]);
     float* dx_l = l == 0 ? (float*)gr->dx : (float*)(ws + (((l - 1) % 2 == 0) ? L.dx0 : L.dx1));
     for (int di = 0; di < m.D; ++di) {
@@ -873,18 +892,28 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
       if ((rc = hip_status(launch_gemm_gen(g, st))) != RNN_OK) return rc;
       // dW_hh = dG_h^T H_prev
       HprevArgs hp{};
-      hp.y = y_l; hp.ldy = m.D * H; hp.col0 = di * H;
+      hp.y = y_l; hp.ldy = m.D * K; hp.col0 = di * K;
       hp.h0 = a.h0[di];
       hp.out = hprev;
-      hp.T = t_max; hp.B = d->B; hp.H = H; hp.packed = a.packed; hp.rev = di == 1;
+      hp.T = t_max; hp.B = d->B; hp.H = K; hp.packed = a.packed; hp.rev = di == 1;
       hp.lengths = dev_len; hp.offsets = dev_off;
       if ((rc = hip_status(launch_hprev(hp, st))) != RNN_OK) return rc;
       GemmGenArgs gh{};
       gh.A = dgh + di * G; gh.sam = 1; gh.sak = (long long)m.D * G;
-      gh.B = hprev; gh.sbk = H; gh.sbn = 1;
-      gh.C = (float*)gr->dw_hh[i]; gh.ldc = H;
-      gh.M = G; gh.N = H; gh.K = rows; gh.accumulate = 0;
+      gh.B = hprev; gh.sbk = K; gh.sbn = 1;
+      gh.C = (float*)gr->dw_hh[i]; gh.ldc = K;
+      gh.M = G; gh.N = K; gh.K = rows; gh.accumulate = 0;
       if ((rc = hip_status(launch_gemm_gen(gh, st))) != RNN_OK) return rc;
+      if (proj) {  // dW_hr = dh^T m, m = o tanh(c) from the reserve
+        float* mbuf = (float*)(ws + L.mbuf);
+        if ((rc = hip_status(launch_mgather(a.rsv, m.D, di, H, m.rows, mbuf, st))) != RNN_OK) return rc;
+        GemmGenArgs gr2{};
+        gr2.A = (const float*)(ws + L.dh) + di * K; gr2.sam = 1; gr2.sak = (long long)m.D * K;
+        gr2.B = mbuf; gr2.sbk = H; gr2.sbn = 1;
+        gr2.C = (float*)gr->dw_hr[i]; gr2.ldc = H;
+        gr2.M = K; gr2.N = H; gr2.K = rows; gr2.accumulate = 0;
+        if ((rc = hip_status(launch_gemm_gen(gr2, st))) != RNN_OK) return rc;
+      }
       if (d->has_bias) {
         if ((rc = hip_status(launch_colsum(dgx + di * G, (long long)m.D * G, rows, G, part, kColsumChunks,
                                            (float*)gr->db_ih[i], st))) != RNN_OK)

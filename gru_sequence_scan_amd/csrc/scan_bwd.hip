@@ -253,17 +253,267 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// LSTMP: the recurrent input is the projection h = W_hr m (width P). Per
+// step, two exchanges as in the forward:
+//   1. each member sums, for its own ps projection outputs, every member's
+//      partial W_hh^T dG of the previous step, adds dy, and publishes dh_t;
+//   2. after the first barrier every member reads the whole dh_t, forms
+//      dm = W_hr^T dh_t for its own units, runs the cell backward with dm
+//      in place of dh, and publishes its partial W_hh^T dG over P.
+// ---------------------------------------------------------------------------
+struct BwdPLds {
+  int wht, wht_ld, wrt, wrt_ld, as, as_ld, dht, dht_ld, acc1, acc1_ld, acc2, acc2_ld, lens, flag, total;
+};
+
+__host__ __device__ inline BwdPLds bwdp_lds(const ScanBwdArgs& a) {
+  BwdPLds L;
+  const int rows = rup_b(a.bb, 16), hsp = rup_b(a.hs, 16);
+  L.wht_ld = a.kp + 4;
+  L.wrt_ld = a.Pp + 4;
+  L.as_ld = a.kp + 4;
+  L.dht_ld = a.Pp + 4;
+  L.acc1_ld = a.Pp + 4;
+  L.acc2_ld = hsp + 4;
+  int o = 0;
+  L.wht = o;
+  o += a.Pp * L.wht_ld * 4;  // wht[p][q * hs + u] = W_hh[q * H + j0 + u][p]
+  L.wrt = o;
+  o += hsp * L.wrt_ld * 4;   // wrt[u][p] = W_hr[p][j0 + u]
+  L.as = o;
+  o += rows * L.as_ld * 4;   // own gate gradients
+  L.dht = o;
+  o += rows * L.dht_ld * 4;  // the whole dh_t of the block
+  L.acc1 = o;
+  o += rows * L.acc1_ld * 4;  // partial W_hh^T dG over P
+  L.acc2 = o;
+  o += rows * L.acc2_ld * 4;  // dm of the own units
+  L.lens = o;
+  o += rup_b(a.bb, 4) * 4;
+  L.flag = o;
+  o += 16;
+  L.total = o;
+  return L;
+}
+
+__global__ void __launch_bounds__(kBT) scan_bwd_proj_kernel(ScanBwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const BwdPLds L = bwdp_lds(a);
+  const int tid = threadIdx.x;
+  const int H = a.H, P = a.P, G = a.G, D = a.D, R = 5 * H;
+  int grp, s;
+  if (a.gpx > 0) {
+    const int xcd = blockIdx.x % a.nxcd, slot = blockIdx.x / a.nxcd;
+    grp = xcd * a.gpx + slot / a.ns;
+    s = slot % a.ns;
+  } else {
+    grp = blockIdx.x / a.ns;
+    s = blockIdx.x % a.ns;
+  }
+  if (grp >= D * a.nbb) return;
+  const int d = grp / a.nbb, blk = grp - d * a.nbb;
+  const bool rev = d == 1;
+  const int b0 = blk * a.bb;
+  const int j0 = s * a.hs, hs_act = max(0, min(a.hs, H - j0));
+  const int p0 = s * a.ps, ps_act = max(0, min(a.ps, P - p0));
+  const int hsp = rup_b(a.hs, 16);
+  unsigned* counter = a.counters + (size_t)grp * 16;
+  int* abort_flag = reinterpret_cast<int*>(lds + L.flag);
+  int* lens = reinterpret_cast<int*>(lds + L.lens);
+  float* wht = reinterpret_cast<float*>(lds + L.wht);
+  float* wrt = reinterpret_cast<float*>(lds + L.wrt);
+  float* As = reinterpret_cast<float*>(lds + L.as);
+  float* acc1 = reinterpret_cast<float*>(lds + L.acc1);
+  float* acc2 = reinterpret_cast<float*>(lds + L.acc2);
+  const int tile_rows = rup_b(a.bb, 16);
+  const bool use_mfma = a.bb % 16 == 0;
+
+  if (tid == 0) *abort_flag = 0;
+  for (int r = tid; r < a.bb; r += kBT) lens[r] = b0 + r < a.B ? (a.lengths ? a.lengths[b0 + r] : a.T) : 0;
+  const float* Whh = a.w_hh[d];
+  const float* Whr = a.w_hr[d];
+  for (int e = tid; e < a.Pp * a.kp; e += kBT) {
+    const int p = e / a.kp, kk = e - p * a.kp;
+    const int q = kk / a.hs, u = kk - q * a.hs;
+    wht[p * L.wht_ld + kk] = (p < P && q < 4 && u < hs_act) ? Whh[(size_t)(q * H + j0 + u) * P + p] : 0.f;
+  }
+  for (int e = tid; e < hsp * a.Pp; e += kBT) {
+    const int u = e / a.Pp, p = e - u * a.Pp;
+    wrt[u * L.wrt_ld + p] = (u < hs_act && p < P) ? Whr[(size_t)p * H + j0 + u] : 0.f;
+  }
+  for (int e = tid; e < tile_rows * L.as_ld; e += kBT) As[e] = 0.f;
+  const __amdgpu_buffer_rsrc_t ex2_rs = make_rsrc(a.ex2, (uint32_t)(D * a.B * a.Pp) * 4u);
+  if (s == 0) {  // the padding columns of this block's dh_t rows read as zero
+    for (int e = tid; e < a.bb * (a.Pp - P); e += kBT) {
+      const int r = e / (a.Pp - P), p = P + (e - r * (a.Pp - P));
+      if (b0 + r < a.B) coh_store4(ex2_rs, (uint32_t)((d * a.B + b0 + r) * a.Pp + p) * 4u, 0u);
+    }
+  }
+  __syncthreads();
+  int maxlen = 0;
+  for (int r = 0; r < a.bb; ++r) maxlen = max(maxlen, lens[r]);
+  maxlen = __builtin_amdgcn_readfirstlane(maxlen);
+  const int nsteps = maxlen;
+  auto t_of = [&](int k) { return rev ? k : maxlen - 1 - k; };
+  const __attribute__((address_space(4))) int* offs = (const __attribute__((address_space(4))) int*)a.offsets;
+  auto row_of = [&](int t) -> int { return a.packed ? offs[t] : t * a.B; };
+  const __amdgpu_buffer_rsrc_t ex_rs = make_rsrc(a.ex, (uint32_t)(2 * D * a.ns * a.B * a.Pp) * 4u);
+  auto ex_el = [&](int par, int m, int b, int c) -> uint32_t {
+    return (uint32_t)((((par * D + d) * a.ns + m) * a.B + b) * a.Pp + c);
+  };
+
+  float dcr[kMaxEptB];
+#pragma unroll
+  for (int i = 0; i < kMaxEptB; ++i) dcr[i] = 0.f;
+
+  unsigned nbar = 0;
+  for (int k = 0; k <= nsteps; ++k) {
+    const int t = k < nsteps ? t_of(k) : -1;
+    const int tpk = k > 0 ? t_of(k - 1) : -1;
+    const int rowbase = t >= 0 ? row_of(t) : 0;
+    // stage 1: own projection outputs of dh_t
+#pragma unroll
+    for (int i = 0; i < kMaxEptB; ++i) {
+      const int e = tid + i * kBT;
+      const int r = e / a.ps, pp = e - r * a.ps;
+      const int b = b0 + r, p = p0 + pp;
+      const int len = (e < a.bb * a.ps && pp < ps_act && b < a.B) ? lens[r] : 0;
+      const bool act = t >= 0 && t < len;
+      const bool was = tpk >= 0 && tpk < len;
+      const size_t row = (size_t)rowbase + b;
+      const float dyv = act ? a.dy[row * (D * P) + d * P + p] : 0.f;
+      const float dhn = (act && !was && a.dh_n[d]) ? a.dh_n[d][(size_t)b * P + p] : 0.f;
+      float dh_rec = 0.f;
+      if (was) {
+        float pv[kBwdMaxMembersDev];
+#pragma unroll
+        for (int m = 0; m < kBwdMaxMembersDev; ++m)
+          if (m < a.ns) pv[m] = __builtin_bit_cast(float, coh_load4(ex_rs, ex_el((k - 1) & 1, m, b, p) * 4u));
+#pragma unroll
+        for (int m = 0; m < kBwdMaxMembersDev; ++m)
+          if (m < a.ns) dh_rec += pv[m];
+      }
+      if (was && !act && a.dh0[d]) a.dh0[d][(size_t)b * P + p] = dh_rec;
+      if (act) {
+        const float dh = (was ? dh_rec : dhn) + dyv;
+        a.dh[(row * D + d) * P + p] = dh;
+        coh_store4(ex2_rs, (uint32_t)((d * a.B + b) * a.Pp + p) * 4u, __builtin_bit_cast(uint32_t, dh));
+      }
+    }
+    // rows whose walk ended: the cell-state gradient of the initial state
+#pragma unroll
+    for (int i = 0; i < kMaxEptB; ++i) {
+      const int e = tid + i * kBT;
+      const int r = e / a.hs, u = e - r * a.hs;
+      const int len = (e < a.bb * a.hs && u < hs_act && b0 + r < a.B) ? lens[r] : 0;
+      const bool act = t >= 0 && t < len, was = tpk >= 0 && tpk < len;
+      if (was && !act && a.dc0[d]) a.dc0[d][(size_t)(b0 + r) * H + j0 + u] = dcr[i];
+    }
+    if (k == nsteps) break;
+    ++nbar;
+    if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+    // stage 2: the whole dh_t, dm = W_hr^T dh_t for the own units
+    load_tile_coherent<float>(ex2_rs, (uint32_t)((d * a.B + b0) * a.Pp), a.Pp, b0, a.B, use_mfma ? tile_rows : a.bb,
+                              a.Pp, lds, L.dht, L.dht_ld);
+    __syncthreads();
+    if (use_mfma)
+      mm_mfma<float>(lds, L.dht, L.dht_ld, L.wrt, L.wrt_ld, acc2, L.acc2_ld, tile_rows / 16, hsp / 16, a.Pp);
+    else
+      mm_valu<float>(lds, L.dht, L.dht_ld, L.wrt, L.wrt_ld, acc2, L.acc2_ld, a.bb, hsp, a.Pp);
+    __syncthreads();
+    // stage 3: the cell backward of the own units with dm
+#pragma unroll
+    for (int i = 0; i < kMaxEptB; ++i) {
+      const int e = tid + i * kBT;
+      const int r = e / a.hs, u = e - r * a.hs;
+      const int b = b0 + r, j = j0 + u;
+      const int len = (e < a.bb * a.hs && u < hs_act && b < a.B) ? lens[r] : 0;
+      if (len == 0) continue;
+      const bool act = t < len, was = tpk >= 0 && tpk < len;
+      if (!act) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) As[r * L.as_ld + q * a.hs + u] = 0.f;
+        continue;
+      }
+      const size_t row = (size_t)rowbase + b;
+      const bool has_prev = rev ? (t + 1 < len) : (t >= 1);
+      const int tp = rev ? t + 1 : t - 1;
+      const float* rv = a.rsv + (row * D + d) * R + j;
+      const float ig = rv[0], fg = rv[H], gg = rv[2 * H], og = rv[3 * H], c = rv[4 * H];
+      const float cp = has_prev ? a.rsv[(((size_t)row_of(tp) + b) * D + d) * R + 4 * H + j]
+                                : (a.c0[d] ? a.c0[d][(size_t)b * H + j] : 0.f);
+      const float dc_in = was ? dcr[i] : (a.dc_n[d] ? a.dc_n[d][(size_t)b * H + j] : 0.f);
+      const float dm = acc2[r * L.acc2_ld + u];
+      const float tc = ftanh(c);
+      const float dct = dc_in + dm * og * (1.f - tc * tc);
+      const float dai = dct * gg * ig * (1.f - ig);
+      const float daf = dct * cp * fg * (1.f - fg);
+      const float dag = dct * ig * (1.f - gg * gg);
+      const float dao = dm * tc * og * (1.f - og);
+      dcr[i] = dct * fg;
+      float* gx = a.dgx + (row * D + d) * G + j;
+      gx[0] = dai;
+      gx[H] = daf;
+      gx[2 * H] = dag;
+      gx[3 * H] = dao;
+      As[r * L.as_ld + u] = dai;
+      As[r * L.as_ld + a.hs + u] = daf;
+      As[r * L.as_ld + 2 * a.hs + u] = dag;
+      As[r * L.as_ld + 3 * a.hs + u] = dao;
+    }
+    __syncthreads();
+    // stage 4: this member's partial W_hh^T dG over the P columns
+    if (use_mfma)
+      mm_mfma<float>(lds, L.as, L.as_ld, L.wht, L.wht_ld, acc1, L.acc1_ld, tile_rows / 16, a.Pp / 16, a.kp);
+    else
+      mm_valu<float>(lds, L.as, L.as_ld, L.wht, L.wht_ld, acc1, L.acc1_ld, a.bb, a.Pp, a.kp);
+    __syncthreads();
+    const int cpr = a.Pp / 4;
+    for (int e = tid; e < a.bb * cpr; e += kBT) {
+      const int r = e / cpr, cc = e - r * cpr;
+      if (b0 + r < a.B)
+        coh_store16(ex_rs, ex_el(k & 1, s, b0 + r, 4 * cc) * 4u,
+                    *reinterpret_cast<const u32x4*>(acc1 + r * L.acc1_ld + 4 * cc));
+    }
+    ++nbar;
+    if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+  }
+}
+
+__global__ void __launch_bounds__(256) mgather_kernel(const float* rsv, int D, int d, int H, long long rows,
+                                                      float* out) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= rows * H) return;
+  const long long row = e / H;
+  const int j = (int)(e - row * H);
+  const float* rv = rsv + (row * D + d) * (5 * H) + j;
+  out[e] = rv[3 * H] * tanhf(rv[4 * H]);
+}
+
 }  // namespace
 
-int scan_bwd_lds_bytes(const ScanBwdArgs& a) { return bwd_lds(a).total; }
+int scan_bwd_lds_bytes(const ScanBwdArgs& a) { return a.mode == kLSTMP ? bwdp_lds(a).total : bwd_lds(a).total; }
+
+hipError_t launch_mgather(const float* rsv, int D, int d, int H, long long rows, float* out, hipStream_t stream) {
+  const long long n = rows * H;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mgather_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, rsv, D, d, H, rows, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t stream) {
-  const int lds = bwd_lds(a).total;
-  hipError_t e = hipFuncSetAttribute((const void*)scan_bwd_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const bool proj = a.mode == kLSTMP;
+  const int lds = scan_bwd_lds_bytes(a);
+  const void* fn = proj ? (const void*)scan_bwd_proj_kernel : (const void*)scan_bwd_kernel;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int groups = a.D * a.nbb;
   const int grid = a.gpx > 0 ? a.nxcd * a.gpx * a.ns : groups * a.ns;
-  hipLaunchKernelGGL(scan_bwd_kernel, dim3(grid), dim3(kBT), lds, stream, a);
+  if (proj)
+    hipLaunchKernelGGL(scan_bwd_proj_kernel, dim3(grid), dim3(kBT), lds, stream, a);
+  else
+    hipLaunchKernelGGL(scan_bwd_kernel, dim3(grid), dim3(kBT), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -238,14 +238,14 @@ typedef struct RnnIO {
 
 /* Gradients for rnn_backward (device pointers, fp32, C-dense, canonical
  * shapes; the shapes of the tensors they are gradients of):
- *   dy    like y (PADDED [T, B, D*H] | PACKED [N_tok, D*H]), required;
+ *   dy    like y (PADDED [T, B, D*K] | PACKED [N_tok, D*K]), required;
  *         positions t >= L_b are never read
- *   dh_n  [L*D, B, H], dc_n [L*D, B, H] (LSTM) or NULL (= zero)
+ *   dh_n  [L*D, B, K], dc_n [L*D, B, H] (LSTM, LSTMP) or NULL (= zero)
  *   dx    like x, required; written whole (zero at t >= L_b in PADDED)
- *   dh0, dc0 [L*D, B, H] or NULL (= skip)
- *   dw_ih[i] [G, in_l], dw_hh[i] [G, H], db_ih[i], db_hh[i] [G] for
- *   i = l*D + d (bias gradients required when has_bias); written, not
- *   accumulated. */
+ *   dh0 [L*D, B, K], dc0 [L*D, B, H] or NULL (= skip)
+ *   dw_ih[i] [G, in_l], dw_hh[i] [G, K], db_ih[i], db_hh[i] [G] and, for
+ *   LSTMP, dw_hr[i] [P, H], for i = l*D + d (bias gradients required when
+ *   has_bias); written, not accumulated. K = P for LSTMP, else H. */
 typedef struct RnnGrads {
   const void* dy;
   const void* dh_n;
@@ -257,6 +257,7 @@ typedef struct RnnGrads {
   void* dw_hh[RNN_MAX_LD];
   void* db_ih[RNN_MAX_LD];
   void* db_hh[RNN_MAX_LD];
+  void* dw_hr[RNN_MAX_LD];
 } RnnGrads;
 
 /* Version of this ABI (RNN_ABI_VERSION). */
@@ -316,7 +317,7 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
 
 /* Training (backward through time; pytorch/pytorch issue "Integrating CuDNN
  * API for LSTMs with projections", thread: the backward of these cells).
- * Built for fp32 LSTM and GRU stacks without clipping, every layout,
+ * Built for fp32 LSTM, LSTMP and GRU stacks without clipping, every layout,
  * length mix, layer count and direction the forward takes; other
  * combinations return RNN_E_UNSUPPORTED.
  *

@@ -265,3 +265,33 @@ def test_binding_rematerialises_non_canonical_strides():
     assert _c_dense(r) and torch.equal(r, t)
     tt = torch.arange(12.0).reshape(3, 4).t()          # transposed
     assert not _c_dense(tt) and torch.equal(_dense(tt), tt)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({}, OK),
+    ({"mode": 1}, OK),
+    ({"mode": 2, "proj_size": 8}, OK),
+    ({"mode": 0, "bidirectional": 1, "num_layers": 3}, OK),
+    ({"dtype": 1}, E_UNSUPPORTED),                                            # training is fp32
+    ({"clip": 1, "cell_clip_lo": -1.0, "cell_clip_hi": 1.0}, E_UNSUPPORTED),  # no clipped backward
+    ({"mode": 3, "layout": 2, "state_dim": 20, "action_dim": 6, "embed_dim": 200, "belief_dim": 200},
+     E_UNSUPPORTED),
+])
+def test_training_sizes_validation(lib, kw, expect):
+    d = _desc(**kw)
+    for fn in ("rnn_reserve_bytes", "rnn_backward_workspace_bytes"):
+        n = ctypes.c_size_t(0)
+        st = getattr(lib, fn)(ctypes.byref(d), None, ctypes.byref(n))
+        assert st == expect, (fn, gss.rnn_strerror(st))
+        if st == OK:
+            assert n.value > 0
+
+
+def test_reserve_holds_gates_and_inner_layer_outputs(lib):
+    # LSTM T=8 B=4 H=32 one layer: 5H fp32 gate values per token
+    n1 = ctypes.c_size_t(0)
+    assert lib.rnn_reserve_bytes(ctypes.byref(_desc()), None, ctypes.byref(n1)) == OK
+    assert n1.value >= 8 * 4 * 5 * 32 * 4
+    n2 = ctypes.c_size_t(0)
+    assert lib.rnn_reserve_bytes(ctypes.byref(_desc(num_layers=2)), None, ctypes.byref(n2)) == OK
+    assert n2.value >= 2 * n1.value + 8 * 4 * 32 * 4   # the lower layer's output is kept too

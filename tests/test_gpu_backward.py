@@ -27,60 +27,71 @@ BWD_GPU_CASES = [
     ("gru_bidir_padded_varlen_2l", "gru", 11, 7, 6, 24, 2, True, "padded", "unsorted", True, 0),
     ("lstm_3layers_mfma", "lstm", 6, 16, 16, 48, 3, False, "padded", None, True, 16),
     ("gru_b33_rows", "gru", 5, 33, 12, 40, 1, True, "packed", (2, 5), True, 0),
+    ("lstmp_mfma", "lstmp", 8, 16, 12, 32, 1, False, "padded", None, True, 16, 16),
+    ("lstmp_bidir_packed_2l", "lstmp", 10, 9, 8, 24, 2, True, "packed", (1, 10), True, 0, 12),
+    ("lstmp_padded_varlen_nobias", "lstmp", 9, 5, 6, 20, 1, False, "padded", "unsorted", False, 0, 8),
 ]
 
 
+def _unpack(case):
+    """name, mode, T, B, F, H, L, bidir, layout, varlen, bias, tile_batch, P."""
+    return case if len(case) == 13 else case + (0,)
+
+
 def _inputs(case):
-    name, mode, T, B, F, H, L, bidir, layout, varlen, bias, tb = case
+    name, mode, T, B, F, H, L, bidir, layout, varlen, bias, tb, P = _unpack(case)
     lengths, vl = None, None
     if varlen == "unsorted":
         lengths = np.random.default_rng(9).integers(1, T + 1, size=B).astype(np.int32)
     elif varlen is not None:
         vl = varlen
-    d = synth.make_rnn_inputs(mode, T, B, F, H, num_layers=L, bidirectional=bidir, layout=layout,
+    d = synth.make_rnn_inputs(mode, T, B, F, H, proj_size=P, num_layers=L, bidirectional=bidir, layout=layout,
                               lengths=lengths, varlen=vl, w_scale=1.0 / np.sqrt(H), bias=bias,
                               seed=zlib.crc32(name.encode()) % 1000, h0_std=0.3, c0_std=0.3)
     if layout == "padded":
         d["x"] = np.nan_to_num(d["x"])  # padded positions must be finite for training
     rng = np.random.default_rng(zlib.crc32(name.encode()) % 977)
     D = 2 if bidir else 1
+    K = P if mode == "lstmp" else H
     rows = d["x"].shape[0] if layout == "packed" else None
-    yshape = (rows, D * H) if layout == "packed" else (T, B, D * H)
+    yshape = (rows, D * K) if layout == "packed" else (T, B, D * K)
     dy = rng.normal(size=yshape).astype(np.float32)
-    dh_n = rng.normal(size=(L * D, B, H)).astype(np.float32)
-    dc_n = rng.normal(size=(L * D, B, H)).astype(np.float32) if mode == "lstm" else None
+    dh_n = rng.normal(size=(L * D, B, K)).astype(np.float32)
+    dc_n = rng.normal(size=(L * D, B, H)).astype(np.float32) if mode != "gru" else None
     return d, dy, dh_n, dc_n
 
 
 @pytest.mark.parametrize("case", BWD_GPU_CASES, ids=[c[0] for c in BWD_GPU_CASES])
 def test_backward_matches_oracle(case):
-    name, mode, T, B, F, H, L, bidir, layout, varlen, bias, tb = case
+    name, mode, T, B, F, H, L, bidir, layout, varlen, bias, tb, P = _unpack(case)
     log(f"[gpu] backward case {name}")
     d, dy, dh_n, dc_n = _inputs(case)
     f = lambda a: to_dev(a, torch.float32)
     params = [{k: f(v) for k, v in p.items() if v is not None} for p in d["params"]]
     (y, hn, cn), ctx = gss.rnn_forward_train(mode, f(d["x"]), params, h0=f(d["h0"]), c0=f(d.get("c0")),
                                              lengths=d["lengths"], layout=layout, num_layers=L,
-                                             bidirectional=bidir, tile_batch=tb)
+                                             bidirectional=bidir, proj_size=P, tile_batch=tb)
     dx, dh0, dc0, grads = gss.rnn_backward(ctx, f(dy), f(dh_n), f(dc_n))
     torch.cuda.synchronize()
     # the training forward's outputs are the forward's
     yr, hnr, cnr = oracle.rnn_forward(mode, d["x"], d["params"], lengths=d["lengths"], h0=d["h0"],
-                                      c0=d.get("c0"), num_layers=L, bidirectional=bidir, layout=layout)
+                                      c0=d.get("c0"), num_layers=L, bidirectional=bidir, proj_size=P,
+                                      layout=layout)
     yg = y.cpu().numpy().astype(np.float64)
     if layout == "padded" and d["lengths"] is not None:
         yg = np.where(np.isnan(yr), np.nan, yg)
     assert_close(yg, yr, "f32", name + " y")
     assert_close(hn.cpu().numpy(), hnr, "f32", name + " h_n")
     ref = oracle.rnn_backward(mode, d["x"], d["params"], dy, dh_n=dh_n, dc_n=dc_n, lengths=d["lengths"],
-                              h0=d["h0"], c0=d.get("c0"), num_layers=L, bidirectional=bidir, layout=layout)
+                              h0=d["h0"], c0=d.get("c0"), num_layers=L, bidirectional=bidir, proj_size=P,
+                              layout=layout)
     g = lambda t: t.cpu().numpy().astype(np.float64)
     assert_grad_close(g(dx), ref[0], name + " dx")
     assert_grad_close(g(dh0), ref[1], name + " dh0")
-    if mode == "lstm":
+    if mode != "gru":
         assert_grad_close(g(dc0), ref[2], name + " dc0")
     for i, (gg, rr) in enumerate(zip(grads, ref[3])):
-        for k in ("w_ih", "w_hh", "b_ih", "b_hh"):
+        for k in ("w_ih", "w_hh", "b_ih", "b_hh", "w_hr"):
             if "d" + k in gg:
                 assert_grad_close(g(gg["d" + k]), rr[k], f"{name} [{i}] d{k}")
 
