@@ -124,6 +124,7 @@ struct ScanBwdArgs {
   float* ex2;            // [D][B][Pp] the whole dh_t of the step, coherent
 };
 int scan_bwd_lds_bytes(const ScanBwdArgs& a);
+constexpr int kScanBwdMaxMembers = 64;  // members per group of the backward scan
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t stream);
 
 // C[m, n] (+)= sum_k A(m, k) B(k, n), fp32, with A(m, k) = A[m * sam + k * sak]

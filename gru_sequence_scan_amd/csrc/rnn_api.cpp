@@ -688,7 +688,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
 // ---------------------------------------------------------------------------
 // Backward through time (training)
 // ---------------------------------------------------------------------------
-constexpr int kBwdMaxMembers = 64;
+constexpr int kBwdMaxMembers = kScanBwdMaxMembers;
 
 struct BwdPlan {
   int bb, hs, ns, nbb, kp, lds, ps;

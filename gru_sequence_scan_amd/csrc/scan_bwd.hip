@@ -29,7 +29,7 @@ namespace {
 
 constexpr int kBT = kScanThreads;
 constexpr int kMaxEptB = 4;  // owned elements per thread: bb * hs <= 1024
-constexpr int kBwdMaxMembersDev = 64;  // members per group (the planner's bound)
+constexpr int kBwdMaxMembersDev = kScanBwdMaxMembers;
 
 __host__ __device__ inline int rup_b(int x, int m) { return (x + m - 1) / m * m; }
 
