@@ -78,6 +78,8 @@ __device__ __forceinline__ f32x4 dot_chain(const float* xr, const float* wr, int
   return acc;
 }
 
+constexpr int kWholePassK4 = 16;  // K up to 64: one wave per 64-column pass
+
 struct Plain {
   __device__ float operator()(int, int, float x) const { return x; }
 };
@@ -97,9 +99,11 @@ __device__ __forceinline__ float red_sum(const float* red, int v, int c) {
 // 4x4 per instruction, lane l of a pass owning output column 64 * pass + l.
 // X and W rows are 16-byte aligned and zero-padded to a multiple of 4.
 // Narrow products (N <= 64) split K over all waves; wider ones give each
-// 64-column pass two waves that split K in halves (or whole passes per wave
-// when there are more passes than wave pairs); partials meet in `red`
-// (kWaves x 4 x 64 floats) and are summed in a fixed order.
+// 64-column pass two waves that split K in halves, or whole passes per wave
+// when there are more passes than wave pairs or K is short (a reduction
+// through LDS and a barrier would cost more than the chain it shortens);
+// partials meet in `red` (kWaves x 4 x 64 floats) and are summed in a fixed
+// order.
 template <typename Epi = Plain>
 __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out, int ldo, int N, int K,
                     float* red, Epi epi = Epi()) {
@@ -109,7 +113,7 @@ __device__ void mv4(const float* X, int ldx, const float* W, int ldw, float* out
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   if (N > 64) {
     const int npass = (N + 63) >> 6;
-    if (2 * npass > kWaves) {
+    if (2 * npass > kWaves || K4 <= kWholePassK4) {
       for (int cg = __builtin_amdgcn_readfirstlane(wave); cg < npass; cg += kWaves) {
         const int c = cg * 64 + lane;
         const f32x4 acc = dot_chain(xr, W + (c < N ? c : N - 1) * ldw, 0, K4, zero4);
