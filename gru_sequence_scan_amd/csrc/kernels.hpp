@@ -98,6 +98,7 @@ struct ScanBwdArgs {
   int bb, hs, ns, nbb, nxcd, gpx;
   int Hp;              // exchange row width (H rounded up to 32)
   int kp;              // product depth: gates * hs rounded up to 16
+  int acc_cols;        // columns of the partial product per pass (divides Hp, multiple of 16)
   const float* w_hh[2];  // [G, H]
   const float* rsv;      // [rows, D, R] this layer (see ScanArgs::rsv)
   const float* y;        // [rows, D * H] this layer's forward output

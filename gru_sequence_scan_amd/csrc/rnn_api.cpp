@@ -691,7 +691,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
 constexpr int kBwdMaxMembers = kScanBwdMaxMembers;
 
 struct BwdPlan {
-  int bb, hs, ns, nbb, kp, lds, ps;
+  int bb, hs, ns, nbb, kp, lds, ps, acc_cols;
 };
 
 // Same shape of search as plan_scan: every group co-resident, LDS within a
@@ -726,14 +726,25 @@ int plan_scan_bwd(const RnnDesc* d, const Dims& m, int cus, BwdPlan* out) {
       a.mode = d->mode == RNN_MODE_GRU ? kGRU : (proj ? kLSTMP : kLSTM);
       a.bb = bb; a.hs = hs; a.Hp = Hp; a.kp = rup(m.gates * hs, 16);
       a.P = m.K; a.Pp = Hp; a.ps = ps;
-      const int lds = scan_bwd_lds_bytes(a);
+      // the partial product passes through LDS in as few column passes as fit
+      int passes = 1, lds = 0;
+      for (; passes <= 8; passes *= 2) {
+        a.acc_cols = Hp / passes;
+        if (proj || a.acc_cols % 16 != 0) a.acc_cols = Hp;
+        lds = scan_bwd_lds_bytes(a);
+        if (lds <= kMaxLds || proj || a.acc_cols % 32 != 0) break;
+      }
       if (lds > kMaxLds) continue;
       const double xbytes = (double)ns * std::min(bb, B) * (proj ? ps : hs) * 4 + (double)bb * Hp * 4;
       double t = barrier_us(ns) + xbytes / 100e3 + mm_us(bb % 16 == 0, 4, bb, Hp, a.kp);
       if (proj) t += barrier_us(ns) + (double)bb * Hp * 4 / 100e3 + mm_us(bb % 16 == 0, 4, bb, rup(hs, 16), Hp);
+      t += 0.1 * (Hp / a.acc_cols - 1);  // a barrier per extra pass
+      // every member writes its partial sums of all columns each step: the
+      // device-wide exchange grows with the member count
+      t += (double)m.D * B * ns * Hp * 4 * 2 / 5e6;
       if (t < best) {
         best = t;
-        *out = BwdPlan{bb, hs, ns, nbb, a.kp, lds, ps};
+        *out = BwdPlan{bb, hs, ns, nbb, a.kp, lds, ps, a.acc_cols};
         found = true;
       }
     }
@@ -851,7 +862,7 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
     a.T = t_max; a.B = d->B; a.H = H; a.D = m.D; a.G = G;
     a.packed = d->layout == RNN_LAYOUT_PACKED;
     a.bb = p.bb; a.hs = p.hs; a.ns = p.ns; a.nbb = p.nbb; a.nxcd = 1; a.gpx = 0;
-    a.Hp = m.Kp; a.kp = p.kp;
+    a.Hp = m.Kp; a.kp = p.kp; a.acc_cols = p.acc_cols;
     a.P = K; a.Pp = m.Kp; a.ps = p.ps;
     a.dh = proj ? (float*)(ws + L.dh) : nullptr;
     a.ex2 = proj ? (float*)(ws + L.ex2) : nullptr;

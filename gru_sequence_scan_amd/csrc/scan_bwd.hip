@@ -44,14 +44,14 @@ __host__ __device__ inline BwdLds bwd_lds(const ScanBwdArgs& a) {
   // distinct banks
   L.wt_ld = a.kp + 4;
   L.as_ld = a.kp + 4;
-  L.acc_ld = a.Hp + 4;
+  L.acc_ld = a.acc_cols + 4;
   int o = 0;
   L.wt = o;
   o += a.Hp * L.wt_ld * 4;  // wt[c][q * hs + u] = W_hh[q * H + j0 + u][c]
   L.as = o;
   o += rows * L.as_ld * 4;  // own hidden-side gate gradients [rows][gates * hs]
   L.acc = o;
-  o += rows * L.acc_ld * 4;  // this member's partial sums [rows][Hp]
+  o += rows * L.acc_ld * 4;  // one pass of this member's partial sums [rows][acc_cols]
   L.lens = o;
   o += rup_b(a.bb, 4) * 4;
   L.flag = o;
@@ -235,18 +235,23 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
     }
     if (k == nsteps) break;
     lds_barrier();
-    // this member's share of W_hh^T (hidden-side gradients), all H columns
-    if (use_mfma)
-      mm_mfma<float>(lds, L.as, L.as_ld, L.wt, L.wt_ld, acc, L.acc_ld, tile_rows / 16, a.Hp / 16, a.kp);
-    else
-      mm_valu<float>(lds, L.as, L.as_ld, L.wt, L.wt_ld, acc, L.acc_ld, a.bb, a.Hp, a.kp);
-    lds_barrier();
-    const int cpr = a.Hp / 4;
-    for (int e = tid; e < a.bb * cpr; e += kBT) {
-      const int r = e / cpr, cc = e - r * cpr;
-      if (b0 + r < a.B)
-        coh_store16(ex_rs, ex_el(k & 1, s, b0 + r, 4 * cc) * 4u,
-                    *reinterpret_cast<const u32x4*>(acc + r * L.acc_ld + 4 * cc));
+    // this member's share of W_hh^T (hidden-side gradients), all H columns,
+    // in passes of acc_cols columns through the LDS accumulator
+    const int cpr = a.acc_cols / 4;
+    for (int c0 = 0; c0 < a.Hp; c0 += a.acc_cols) {
+      const int wt_off = L.wt + c0 * L.wt_ld * 4;
+      if (use_mfma)
+        mm_mfma<float>(lds, L.as, L.as_ld, wt_off, L.wt_ld, acc, L.acc_ld, tile_rows / 16, a.acc_cols / 16, a.kp);
+      else
+        mm_valu<float>(lds, L.as, L.as_ld, wt_off, L.wt_ld, acc, L.acc_ld, a.bb, a.acc_cols, a.kp);
+      lds_barrier();
+      for (int e = tid; e < a.bb * cpr; e += kBT) {
+        const int r = e / cpr, cc = e - r * cpr;
+        if (b0 + r < a.B)
+          coh_store16(ex_rs, ex_el(k & 1, s, b0 + r, c0 + 4 * cc) * 4u,
+                      *reinterpret_cast<const u32x4*>(acc + r * L.acc_ld + 4 * cc));
+      }
+      if (c0 + a.acc_cols < a.Hp) lds_barrier();  // the accumulator is reused
     }
     ++nbar;
     if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
