@@ -51,7 +51,9 @@ __host__ __device__ inline BwdLds bwd_lds(const ScanBwdArgs& a) {
   L.as = o;
   o += rows * L.as_ld * 4;  // own hidden-side gate gradients [rows][gates * hs]
   L.acc = o;
-  o += rows * L.acc_ld * 4;  // one pass of this member's partial sums [rows][acc_cols]
+  // one pass of this member's partial sums [rows][acc_cols] (the vector-ALU
+  // product only: the MFMA product stores from its accumulators)
+  if (a.bb % 16 != 0) o += rows * L.acc_ld * 4;
   L.lens = o;
   o += rup_b(a.bb, 4) * 4;
   L.flag = o;
@@ -235,23 +237,35 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
     }
     if (k == nsteps) break;
     lds_barrier();
-    // this member's share of W_hh^T (hidden-side gradients), all H columns,
-    // in passes of acc_cols columns through the LDS accumulator
-    const int cpr = a.acc_cols / 4;
-    for (int c0 = 0; c0 < a.Hp; c0 += a.acc_cols) {
-      const int wt_off = L.wt + c0 * L.wt_ld * 4;
-      if (use_mfma)
-        mm_mfma<float>(lds, L.as, L.as_ld, wt_off, L.wt_ld, acc, L.acc_ld, tile_rows / 16, a.acc_cols / 16, a.kp);
-      else
-        mm_valu<float>(lds, L.as, L.as_ld, wt_off, L.wt_ld, acc, L.acc_ld, a.bb, a.acc_cols, a.kp);
-      lds_barrier();
-      for (int e = tid; e < a.bb * cpr; e += kBT) {
-        const int r = e / cpr, cc = e - r * cpr;
-        if (b0 + r < a.B)
-          coh_store16(ex_rs, ex_el(k & 1, s, b0 + r, c0 + 4 * cc) * 4u,
-                      *reinterpret_cast<const u32x4*>(acc + r * L.acc_ld + 4 * cc));
+    // this member's share of W_hh^T (hidden-side gradients), all H columns
+    if (use_mfma) {
+      // Columns of the recurrent width as the MFMA rows, batch rows as its
+      // columns: every lane finishes with four consecutive columns of one
+      // batch row and stores them from its accumulator in one 16-byte store
+      // (rows past the block or the batch go out of range and are dropped).
+      const int lr = tid & 15, lq = (tid & 63) >> 4;
+      mm_mfma_epi<float>(lds, L.wt, L.wt_ld, L.as, L.as_ld, a.Hp / 16, tile_rows / 16, a.kp,
+                         [&](int m, int n, const f32x4& c) {
+                           const int r = n * 16 + lr;
+                           const uint32_t off = (r < a.bb && b0 + r < a.B)
+                                                    ? ex_el(k & 1, s, b0 + r, m * 16 + 4 * lq) * 4u
+                                                    : 0x80000000u;
+                           coh_store16(ex_rs, off, __builtin_bit_cast(u32x4, c));
+                         });
+    } else {
+      // in passes of acc_cols columns through the LDS accumulator
+      const int cpr = a.acc_cols / 4;
+      for (int c0 = 0; c0 < a.Hp; c0 += a.acc_cols) {
+        mm_valu<float>(lds, L.as, L.as_ld, L.wt + c0 * L.wt_ld * 4, L.wt_ld, acc, L.acc_ld, a.bb, a.acc_cols, a.kp);
+        lds_barrier();
+        for (int e = tid; e < a.bb * cpr; e += kBT) {
+          const int r = e / cpr, cc = e - r * cpr;
+          if (b0 + r < a.B)
+            coh_store16(ex_rs, ex_el(k & 1, s, b0 + r, c0 + 4 * cc) * 4u,
+                        *reinterpret_cast<const u32x4*>(acc + r * L.acc_ld + 4 * cc));
+        }
+        if (c0 + a.acc_cols < a.Hp) lds_barrier();  // the accumulator is reused
       }
-      if (c0 + a.acc_cols < a.Hp) lds_barrier();  // the accumulator is reused
     }
     ++nbar;
     if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;

@@ -49,10 +49,12 @@ struct Chunk<float> {
   }
 };
 
-// NT output tiles of one wave over the whole K, two chunks of loads in flight.
-template <typename DT, int NT>
-__device__ __forceinline__ void mm_tiles(const DT* As, int as_ld, const DT* Ws, int w_ld, float* acc, int acc_ld,
-                                         const int* tm, const int* tn, int kp) {
+// NT output tiles of one wave over the whole K, two chunks of loads in flight;
+// each finished 16x16 accumulator goes to epi(tm, tn, c), where lane l holds
+// column tn * 16 + l % 16, rows tm * 16 + 4 * (l / 16) + v.
+template <typename DT, int NT, typename Epi>
+__device__ __forceinline__ void mm_tiles_epi(const DT* As, int as_ld, const DT* Ws, int w_ld, const int* tm,
+                                             const int* tn, int kp, Epi&& epi) {
   typedef typename Chunk<DT>::T V;
   constexpr int kEpc = 16 / sizeof(DT);
   constexpr int kK = Chunk<DT>::kK;
@@ -92,11 +94,18 @@ __device__ __forceinline__ void mm_tiles(const DT* As, int as_ld, const DT* Ws, 
 #pragma unroll
     for (int j = 0; j < NT; ++j) c[j] = Chunk<DT>::mfma(a0[j], b0[j], c[j]);
   }
-  // 16x16 accumulator layout: lane holds column l % 16, rows 4 * (l / 16) + v.
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
+  for (int j = 0; j < NT; ++j) epi(tm[j], tn[j], c[j]);
+}
+
+template <typename DT, int NT>
+__device__ __forceinline__ void mm_tiles(const DT* As, int as_ld, const DT* Ws, int w_ld, float* acc, int acc_ld,
+                                         const int* tm, const int* tn, int kp) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  mm_tiles_epi<DT, NT>(As, as_ld, Ws, w_ld, tm, tn, kp, [&](int m, int n, const f32x4& c) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[(tm[j] * 16 + 4 * lq + v) * acc_ld + tn[j] * 16 + lr] = c[j][v];
+    for (int v = 0; v < 4; ++v) acc[(m * 16 + 4 * lq + v) * acc_ld + n * 16 + lr] = c[v];
+  });
 }
 
 // acc[r][c] = sum_k A[r][k] * W[c][k] on 16x16 MFMA tiles (rows a multiple
@@ -126,6 +135,37 @@ __device__ void mm_mfma(const char* lds, int as_off, int as_ld, int w_off, int w
       case 2: mm_tiles<DT, 2>(As, as_ld, Ws, w_ld, acc, acc_ld, tm, tn, kp); break;
       case 3: mm_tiles<DT, 3>(As, as_ld, Ws, w_ld, acc, acc_ld, tm, tn, kp); break;
       default: mm_tiles<DT, 4>(As, as_ld, Ws, w_ld, acc, acc_ld, tm, tn, kp); break;
+    }
+    t0 += n;
+  }
+}
+
+// The same tiling with each finished accumulator handed to epi (mm_tiles_epi's
+// layout) instead of written to LDS.
+template <typename DT, typename Epi>
+__device__ void mm_mfma_epi(const char* lds, int as_off, int as_ld, int w_off, int w_ld, int mtiles, int ntiles,
+                            int kp, Epi&& epi) {
+  const DT* As = reinterpret_cast<const DT*>(lds + as_off);
+  const DT* Ws = reinterpret_cast<const DT*>(lds + w_off);
+  const int wave = threadIdx.x >> 6;
+  const int total = mtiles * ntiles;
+  const int per = (total + 3) / 4;
+  int t0 = wave * per;
+  const int t1 = min(total, t0 + per);
+  while (t0 < t1) {
+    const int n = min(4, t1 - t0);
+    int tm[4], tn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tt = t0 + min(j, n - 1);
+      tm[j] = tt / ntiles;
+      tn[j] = tt - tm[j] * ntiles;
+    }
+    switch (n) {
+      case 1: mm_tiles_epi<DT, 1>(As, as_ld, Ws, w_ld, tm, tn, kp, epi); break;
+      case 2: mm_tiles_epi<DT, 2>(As, as_ld, Ws, w_ld, tm, tn, kp, epi); break;
+      case 3: mm_tiles_epi<DT, 3>(As, as_ld, Ws, w_ld, tm, tn, kp, epi); break;
+      default: mm_tiles_epi<DT, 4>(As, as_ld, Ws, w_ld, tm, tn, kp, epi); break;
     }
     t0 += n;
   }

@@ -30,9 +30,12 @@ BWD_GPU_CASES = [
     ("lstmp_mfma", "lstmp", 8, 16, 12, 32, 1, False, "padded", None, True, 16, 16),
     ("lstmp_bidir_packed_2l", "lstmp", 10, 9, 8, 24, 2, True, "packed", (1, 10), True, 0, 12),
     ("lstmp_padded_varlen_nobias", "lstmp", 9, 5, 6, 20, 1, False, "padded", "unsorted", False, 0, 8),
-    # wide batch tiles whose partial products pass through LDS in column passes
-    ("gru_b256_h512_colpass", "gru", 3, 256, 32, 512, 1, False, "padded", None, True, 0),
-    ("lstm_bidir_b128_h512_colpass", "lstm", 4, 128, 16, 512, 1, True, "packed", (1, 4), True, 0),
+    # wide batch tiles (MFMA partial products stored from the accumulators)
+    ("gru_b256_h512_wide", "gru", 3, 256, 32, 512, 1, False, "padded", None, True, 0),
+    ("lstm_bidir_b128_h512_wide", "lstm", 4, 128, 16, 512, 1, True, "packed", (1, 4), True, 0),
+    # a vector-ALU block of 40 rows: its partial products pass through LDS in
+    # two column passes
+    ("lstm_b40_valu_colpass", "lstm", 3, 40, 8, 512, 1, False, "padded", None, True, 40),
 ]
 
 
