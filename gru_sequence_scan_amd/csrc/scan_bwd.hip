@@ -134,6 +134,48 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
     dhd[i] = 0.f;
   }
 
+  // The loads of a step that do not depend on the exchange (reserved gate
+  // values, dy, the previous state, the final-state gradients) are issued one
+  // step early, between this workgroup's arrival at the group barrier and its
+  // wait, so that their latency overlaps the wait.
+  float pre_rv[kMaxEptB][5], pre_dy[kMaxEptB], pre_prev[kMaxEptB], pre_dhn[kMaxEptB], pre_dcn[kMaxEptB];
+  auto prefetch = [&](int k) {
+    const int t = k < nsteps ? t_of(k) : -1;
+    const int tpk = k > 0 ? t_of(k - 1) : -1;
+    const int rowbase = t >= 0 ? row_of(t) : 0;
+#pragma unroll
+    for (int i = 0; i < kMaxEptB; ++i) {
+      const int b = b0 + er[i], j = j0 + eu[i];
+      const int len = elen[i];
+      const bool act = t >= 0 && t < len;
+      const bool was = tpk >= 0 && tpk < len;
+      const size_t row = (size_t)rowbase + b;
+      const bool has_prev = act && (rev ? (t + 1 < len) : (t >= 1));
+      const int tp = rev ? t + 1 : t - 1;
+      const size_t prow = has_prev ? (size_t)row_of(tp) + b : 0;
+#pragma unroll
+      for (int q = 0; q < 5; ++q) pre_rv[i][q] = 0.f;
+      pre_dy[i] = pre_prev[i] = pre_dhn[i] = pre_dcn[i] = 0.f;
+      if (act) {
+        const float* rv = a.rsv + (row * D + d) * R + j;
+#pragma unroll
+        for (int q = 0; q < 5; ++q)
+          if (q < (gru ? 4 : 5)) pre_rv[i][q] = rv[q * H];
+        pre_dy[i] = a.dy[row * (D * H) + d * H + j];
+        if (gru)
+          pre_prev[i] = has_prev ? a.y[prow * (D * H) + d * H + j] : (a.h0[d] ? a.h0[d][(size_t)b * H + j] : 0.f);
+        else
+          pre_prev[i] =
+              has_prev ? a.rsv[(prow * D + d) * R + 4 * H + j] : (a.c0[d] ? a.c0[d][(size_t)b * H + j] : 0.f);
+        if (!was) {
+          pre_dhn[i] = a.dh_n[d] ? a.dh_n[d][(size_t)b * H + j] : 0.f;
+          pre_dcn[i] = (!gru && a.dc_n[d]) ? a.dc_n[d][(size_t)b * H + j] : 0.f;
+        }
+      }
+    }
+  };
+
+  prefetch(0);
   unsigned nbar = 0;
   for (int k = 0; k <= nsteps; ++k) {
     const int t = k < nsteps ? t_of(k) : -1;
@@ -145,30 +187,11 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
       const int len = elen[i];
       const bool act = t >= 0 && t < len;
       const bool was = tpk >= 0 && tpk < len;
-      // Every load this element needs is issued before the first is used, so
-      // their latencies overlap: this step's dy and reserved gate values, the
-      // previous state, then the previous step's partial sums of all members.
       const size_t row = (size_t)rowbase + b;
-      const bool has_prev = act && (rev ? (t + 1 < len) : (t >= 1));
-      const int tp = rev ? t + 1 : t - 1;
-      const size_t prow = has_prev ? (size_t)row_of(tp) + b : 0;
-      float rvv[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-      float dyv = 0.f, prevv = 0.f, dhn = 0.f, dcn = 0.f;
-      if (act) {
-        const float* rv = a.rsv + (row * D + d) * R + j;
+      float rvv[5];
 #pragma unroll
-        for (int q = 0; q < 5; ++q)
-          if (q < (gru ? 4 : 5)) rvv[q] = rv[q * H];
-        dyv = a.dy[row * (D * H) + d * H + j];
-        if (gru)
-          prevv = has_prev ? a.y[prow * (D * H) + d * H + j] : (a.h0[d] ? a.h0[d][(size_t)b * H + j] : 0.f);
-        else
-          prevv = has_prev ? a.rsv[(prow * D + d) * R + 4 * H + j] : (a.c0[d] ? a.c0[d][(size_t)b * H + j] : 0.f);
-        if (!was) {
-          dhn = a.dh_n[d] ? a.dh_n[d][(size_t)b * H + j] : 0.f;
-          dcn = (!gru && a.dc_n[d]) ? a.dc_n[d][(size_t)b * H + j] : 0.f;
-        }
-      }
+      for (int q = 0; q < 5; ++q) rvv[q] = pre_rv[i][q];
+      const float dyv = pre_dy[i], prevv = pre_prev[i], dhn = pre_dhn[i], dcn = pre_dcn[i];
       // recurrent gradient from the previous step's partial sums, summed
       // over the members in order (up to 64 loads in flight)
       float dh_rec = 0.f;
@@ -268,7 +291,9 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
       }
     }
     ++nbar;
-    if (!group_barrier(counter, nbar * a.ns, a.status, abort_flag)) return;
+    group_arrive(counter);
+    prefetch(k + 1);
+    if (!group_wait(counter, nbar * a.ns, a.status, abort_flag)) return;
   }
 }
 
