@@ -136,7 +136,12 @@ struct GemmGenArgs {
   float* C; long long ldc;
   int M, N, K;
   int accumulate;      // 1: C += product, 0: C = product
+  float* part;         // split-K partial products, gemm_gen_part_floats(M, N, K) floats (may be null when 0)
+  int vec_a, vec_b;    // set by launch_gemm_gen
 };
+// The split of K for an M x N x K product (independent of the device).
+void gemm_gen_split(int M, int N, int K, int* splits, int* kchunk);
+size_t gemm_gen_part_floats(int M, int N, int K);
 hipError_t launch_gemm_gen(const GemmGenArgs& a, hipStream_t stream);
 // out[n] = sum over m of A[m * lda + n] for n < N (fixed order), using
 // `partial` (nchunk * N floats) for a two-pass deterministic reduction.

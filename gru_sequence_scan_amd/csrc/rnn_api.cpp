@@ -753,7 +753,7 @@ int plan_scan_bwd(const RnnDesc* d, const Dims& m, int cus, BwdPlan* out) {
 }
 
 struct BwdLayout {
-  size_t status, counters, ints, dgx, dgh, hprev, dx0, dx1, ex, part, ex2, dh, mbuf, total;
+  size_t status, counters, ints, dgx, dgh, hprev, dx0, dx1, ex, part, gpart, ex2, dh, mbuf, total;
   size_t counters_bytes;
   int n_ints;
 };
@@ -780,6 +780,16 @@ BwdLayout bwd_layout_of(const RnnDesc* d, const Dims& m, bool has_lengths) {
   w.dx1 = d->num_layers > 2 ? take(dxb) : 0;
   w.ex = take((size_t)2 * m.D * kBwdMaxMembers * d->B * m.Kp * 4);
   w.part = take((size_t)kColsumChunks * std::max(m.G, m.K) * 4);
+  // split-K partial products of the largest weight-gradient or dX product
+  size_t gp = 0;
+  const int rows_i = (int)rows;
+  for (int l = 0; l < d->num_layers; ++l) {
+    const int in_l = l == 0 ? d->input_size : m.D * m.K;
+    gp = std::max({gp, gemm_gen_part_floats(m.G, in_l, rows_i), gemm_gen_part_floats(m.G, m.K, rows_i),
+                   gemm_gen_part_floats(rows_i, in_l, m.G)});
+    if (d->mode == RNN_MODE_LSTMP) gp = std::max(gp, gemm_gen_part_floats(m.K, d->hidden_size, rows_i));
+  }
+  w.gpart = take(std::max<size_t>(gp, 1) * 4);
   if (d->mode == RNN_MODE_LSTMP) {
     w.ex2 = take((size_t)m.D * d->B * m.Kp * 4);
     w.dh = take(rows * m.D * m.K * 4);
@@ -850,6 +860,7 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
       return rc;
   }
   float* hprev = (float*)(ws + L.hprev);
+  float* gpart = (float*)(ws + L.gpart);
   float* part = (float*)(ws + L.part);
   const size_t sB = (size_t)d->B * H, sK = (size_t)d->B * K;
   const int rows = (int)m.rows;
@@ -900,6 +911,7 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
       g.B = x_l; g.sbk = in_l; g.sbn = 1;
       g.C = (float*)gr->dw_ih[i]; g.ldc = in_l;
       g.M = G; g.N = in_l; g.K = rows; g.accumulate = 0;
+      g.part = gpart;
       if ((rc = hip_status(launch_gemm_gen(g, st))) != RNN_OK) return rc;
       // dW_hh = dG_h^T H_prev
       HprevArgs hp{};
@@ -914,6 +926,7 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
       gh.B = hprev; gh.sbk = K; gh.sbn = 1;
       gh.C = (float*)gr->dw_hh[i]; gh.ldc = K;
       gh.M = G; gh.N = K; gh.K = rows; gh.accumulate = 0;
+      gh.part = gpart;
       if ((rc = hip_status(launch_gemm_gen(gh, st))) != RNN_OK) return rc;
       if (proj) {  // dW_hr = dh^T m, m = o tanh(c) from the reserve
         float* mbuf = (float*)(ws + L.mbuf);
@@ -923,7 +936,8 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
         gr2.B = mbuf; gr2.sbk = H; gr2.sbn = 1;
         gr2.C = (float*)gr->dw_hr[i]; gr2.ldc = H;
         gr2.M = K; gr2.N = H; gr2.K = rows; gr2.accumulate = 0;
-        if ((rc = hip_status(launch_gemm_gen(gr2, st))) != RNN_OK) return rc;
+        gr2.part = gpart;
+      if ((rc = hip_status(launch_gemm_gen(gr2, st))) != RNN_OK) return rc;
       }
       if (d->has_bias) {
         if ((rc = hip_status(launch_colsum(dgx + di * G, (long long)m.D * G, rows, G, part, kColsumChunks,
@@ -939,6 +953,7 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
       gx.B = (const float*)w->w_ih[i]; gx.sbk = in_l; gx.sbn = 1;
       gx.C = dx_l; gx.ldc = in_l;
       gx.M = rows; gx.N = in_l; gx.K = G; gx.accumulate = di > 0;
+      gx.part = gpart;
       if ((rc = hip_status(launch_gemm_gen(gx, st))) != RNN_OK) return rc;
     }
   }
