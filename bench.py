@@ -383,15 +383,19 @@ def train_flops(spec, d):
     D = 2 if spec.bidirectional else 1
     G = (3 if spec.mode == "gru" else 4) * spec.hidden_size
     H = spec.hidden_size
+    P = spec.proj_size if spec.mode == "lstmp" else 0
+    K = P or H  # recurrent width
     L = d["lengths"]
     tokens = int(L.sum()) if L is not None else spec.T * spec.B
     rows = tokens if spec.layout == "packed" else spec.T * spec.B
     fl = 0
     for layer in range(spec.num_layers):
-        in_l = spec.input_size if layer == 0 else D * H
-        fl += 2 * rows * D * G * in_l + 2 * tokens * D * G * H            # forward
-        fl += 2 * tokens * D * G * H                                      # backward recurrent product
-        fl += 2 * rows * D * G * in_l * 2 + 2 * rows * D * G * H          # dW_ih, dX, dW_hh
+        in_l = spec.input_size if layer == 0 else D * K
+        fl += 2 * rows * D * G * in_l + 2 * tokens * D * G * K            # forward
+        fl += 2 * tokens * D * G * K                                      # backward recurrent product
+        fl += 2 * rows * D * G * in_l * 2 + 2 * rows * D * G * K          # dW_ih, dX, dW_hh
+        if P:
+            fl += 2 * tokens * D * P * H * 2 + 2 * rows * D * P * H       # projection forward and back, dW_hr
     return fl, tokens
 
 
@@ -405,9 +409,8 @@ def train_main(args):
 
     name = synth.ORDER[int(args.workload) - 1] if args.workload.isdigit() else args.workload
     spec = synth.spec(name)
-    if spec.mode not in ("lstm", "gru") or spec.dtype != "f32":
-        print(f"training is built for fp32 LSTM / GRU stacks; {name} is {spec.dtype} {spec.mode}",
-              file=sys.stderr)
+    if spec.mode not in ("lstm", "gru", "lstmp"):
+        print(f"training is built for LSTM / GRU / LSTMP stacks; {name} is {spec.mode}", file=sys.stderr)
         sys.exit(2)
     d = synth.make_inputs(name)
     dev = torch.device("cuda:0")
@@ -420,11 +423,14 @@ def train_main(args):
     x = T(np.nan_to_num(d["x"]))
     D = 2 if spec.bidirectional else 1
     H = spec.hidden_size
+    P = spec.proj_size if spec.mode == "lstmp" else 0
+    K = P or H
     rng = np.random.default_rng(spec.seed + 1)
-    yshape = (x.shape[0], D * H) if spec.layout == "packed" else (spec.T, spec.B, D * H)
+    yshape = (x.shape[0], D * K) if spec.layout == "packed" else (spec.T, spec.B, D * K)
     dy = T(rng.normal(size=yshape))
     kw = dict(lengths=d["lengths"], layout=spec.layout, num_layers=spec.num_layers,
-              bidirectional=spec.bidirectional, tile_batch=args.tile_batch, tile_hidden=args.tile_hidden)
+              bidirectional=spec.bidirectional, proj_size=P, tile_batch=args.tile_batch,
+              tile_hidden=args.tile_hidden)
 
     def step():
         _, ctx = gss.rnn_forward_train(spec.mode, x, params, **kw)
@@ -452,7 +458,11 @@ def train_main(args):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": name, "pass": "forward+backward", "mode": spec.mode, "T": spec.T, "B": spec.B,
                    "input": spec.input_size, "hidden": H, "layers": spec.num_layers,
-                   "bidirectional": spec.bidirectional, "layout": spec.layout, "tokens": tokens},
+                   "bidirectional": spec.bidirectional, "layout": spec.layout, "tokens": tokens,
+                   **({"proj": P} if P else {}),
+                   # training computes in fp32; a bf16 forward workload's
+                   # (bf16-representable) inputs are taken as fp32
+                   **({"operands": "fp32 (the bf16 workload's values, widened)"} if spec.dtype == "bf16" else {})},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": None, "kernel": "training step (all kernels)",
                      "avg_us": ev_ms * 1e3, "algorithmic_flops": flops},
@@ -474,18 +484,20 @@ def cpu_baseline_train(spec, d, seconds):
     L = d["lengths"]
     order = np.random.default_rng(0).permutation(spec.B)
     D = 2 if spec.bidirectional else 1
+    P = spec.proj_size if spec.mode == "lstmp" else 0
+    K = P or spec.hidden_size
 
     def run(rows):
         sub = np.sort(order[:rows])
         lengths = None if L is None else L[sub]
         if spec.layout == "packed":
             x = oracle.pack_sequence(np.nan_to_num(d["x_padded"][:, sub]), lengths)
-            dy = np.ones((x.shape[0], D * spec.hidden_size))
+            dy = np.ones((x.shape[0], D * K))
         else:
             x = d["x"][:, sub]
-            dy = np.ones((spec.T, rows, D * spec.hidden_size))
+            dy = np.ones((spec.T, rows, D * K))
         kw = dict(lengths=lengths, num_layers=spec.num_layers, bidirectional=spec.bidirectional,
-                  layout=spec.layout)
+                  layout=spec.layout, proj_size=P)
         t0 = time.perf_counter()
         oracle.rnn_forward(spec.mode, x, d["params"], **kw)
         oracle.rnn_backward(spec.mode, x, d["params"], dy, **kw)
