@@ -79,6 +79,68 @@ __device__ __forceinline__ u32x4 load_chunk(const DT* base, int rows, int K, int
   return v;
 }
 
+// Epilogue: bias fold and fp32 store of the 128x128 tile. The accumulators
+// pass through LDS 64 rows at a time (one pass per wave row), so that each
+// lane then stores whole 16-byte chunks of a C row: a wave writes two full
+// 512-byte row segments per instruction instead of 2 x 128 bytes of single
+// dwords. The stores are non-temporal: G_x is read back only by the
+// recurrence, after the whole product. 32x32 accumulator layout: lane holds
+// column l32 and rows 8 (v / 4) + 4 half + v % 4. The LDS row stride of 136
+// floats puts the two lane halves (rows 4 apart) on disjoint banks.
+constexpr int kEpiStride = 136;
+constexpr int kEpiBytes = 64 * kEpiStride * 4;  // 34816
+static_assert(kEpiBytes <= 2 * 2 * kTileBytes, "epilogue staging exceeds the operand buffers");
+
+template <typename DT>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[2][2], float* lds, int m0, int n0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, half = lane >> 5, l32 = lane & 31;
+  const int c4 = tid & 31, rbase = tid >> 5;  // this thread's 16-byte column chunk and first row
+  const int n = n0 + 4 * c4;
+  float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (a.has_bias) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (n + e >= a.N) continue;
+      const int dir = (n + e) / a.G, nr = n + e - dir * a.G;
+      bias[e] = to_f32<DT>(reinterpret_cast<const DT*>(a.b_ih[dir])[nr]);
+      if (nr < a.hh_fold_rows) bias[e] += to_f32<DT>(reinterpret_cast<const DT*>(a.b_hh[dir])[nr]);
+    }
+  }
+  const bool vec = (a.N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.C) & 15) == 0 && n + 4 <= a.N;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if (p) __syncthreads();  // the first pass's reads are done
+    if (wm == p) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            lds[(i * 32 + 8 * (v >> 2) + 4 * half + (v & 3)) * kEpiStride + wn * 64 + j * 32 + l32] = acc[i][j][v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = rbase + 8 * i;
+      const int m = m0 + p * 64 + r;
+      if (m >= a.M) break;
+      f32x4 v = *reinterpret_cast<const f32x4*>(lds + r * kEpiStride + 4 * c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += bias[e];
+      float* dst = a.C + (size_t)m * a.N + n;
+      if (vec) {
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) dst[e] = v[e];
+      }
+    }
+  }
+}
+
 template <typename DT>
 __global__ void __launch_bounds__(256) gemm_xw_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2][2][kTileBytes];
@@ -160,27 +222,7 @@ __global__ void __launch_bounds__(256) gemm_xw_kernel(GemmArgs a) {
     __syncthreads();
   }
 
-  // Epilogue: bias fold and fp32 store. 32x32 accumulator layout: lane holds
-  // column l32 and rows 8*(v/4) + 4*half + (v%4).
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + l32;
-    if (n >= a.N) continue;
-    float bias = 0.0f;
-    if (a.has_bias) {
-      const int dir = n / a.G, nr = n - dir * a.G;
-      bias = to_f32<DT>(reinterpret_cast<const DT*>(a.b_ih[dir])[nr]);
-      if (nr < a.hh_fold_rows) bias += to_f32<DT>(reinterpret_cast<const DT*>(a.b_hh[dir])[nr]);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (m < a.M) a.C[(size_t)m * a.N + n] = acc[i][j][v] + bias;
-      }
-    }
-  }
+  store_tile<DT>(a, acc, reinterpret_cast<float*>(&smem[0][0][0]), m0, n0);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,6 +238,7 @@ __global__ void __launch_bounds__(256) gemm_xw_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kStages = 4;
 constexpr int kStageBytes = (kBM + kBN) * kRowBytes;  // 16 KiB
+static_assert(kEpiBytes <= kStages * kStageBytes, "epilogue staging exceeds the LDS ring");
 
 __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 2) & 3); }
 
@@ -325,26 +368,9 @@ __global__ void __launch_bounds__(256) gemm_xw_pipe_kernel(GemmArgs a) {
         MfmaSwz<DT>::run(As, wm * 64 + i * 32 + l32, Bs, wn * 64 + j * 32 + l32, half, acc[i][j]);
   }
 
-  // Epilogue as in gemm_xw_kernel.
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + l32;
-    if (n >= a.N) continue;
-    float bias = 0.0f;
-    if (a.has_bias) {
-      const int dir = n / a.G, nr = n - dir * a.G;
-      bias = to_f32<DT>(reinterpret_cast<const DT*>(a.b_ih[dir])[nr]);
-      if (nr < a.hh_fold_rows) bias += to_f32<DT>(reinterpret_cast<const DT*>(a.b_hh[dir])[nr]);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (m < a.M) a.C[(size_t)m * a.N + n] = acc[i][j][v] + bias;
-      }
-    }
-  }
+  // Every wave is done reading the ring before the epilogue reuses it.
+  __syncthreads();
+  store_tile<DT>(a, acc, reinterpret_cast<float*>(&smem[0][0]), m0, n0);
 }
 
 }  // namespace
@@ -354,8 +380,8 @@ hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream)
   const int ntm = (a.M + kBM - 1) / kBM;
   const dim3 grid(ntn * ntm), block(256);
   // fp32 operands: the streamed form (measured 10% faster at K = 1024). bf16
-  // operands: the fp32 output write bounds both forms and the register-staged
-  // one, at three workgroups per CU, overlaps it slightly better.
+  // operands: the register-staged form, at three workgroups per CU, measured
+  // 10-30% faster than the streamed one at two.
   const bool pipe = !dtype_bf16 && a.vec_ok && a.zero16 && a.K % (kRowBytes / 4) == 0;
   if (dtype_bf16) {
     if (pipe)

@@ -497,55 +497,61 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     }
     __syncthreads();
 
-    // Gate math on the owned elements; only the exchanged state is stored
-    // before the barrier arrival.
+    // Gate math on the owned elements: every element first, then every
+    // store. The G_x values were loaded a step ahead, but the vector-memory
+    // counter retires in order, so a wait for them placed after a store of
+    // this step would also wait for that store to reach the coherence point.
+    // Only the exchanged state is stored before the barrier arrival.
+    float gsv[kMaxEpt][5];
 #pragma unroll
     for (int i = 0; i < kMaxEpt; ++i) {
       const int r = er[i], u = eu[i];
-      const int b = b0 + r;
       if (t >= lenreg[i]) continue;
-      const int j = j0 + u;
       const float* ar = acc + r * L.acc_ld;
       if (a.mode == kGRU) {
         const float rg = fsigmoid(gxv[i][0] + ar[u]);
         const float zg = fsigmoid(gxv[i][1] + ar[a.hs + u]);
-        const float ng = ftanh(gxv[i][2] + rg * (ar[2 * a.hs + u] + bhn[i]));
-        const float h = (1.f - zg) * ng + zg * hreg[i];
-        if (a.rsv) {
-          float* rv = a.rsv + ((size_t)(rowbase + b) * a.D + d) * (4 * a.H) + j;
-          rv[0] = rg;
-          rv[a.H] = zg;
-          rv[2 * a.H] = ng;
-          rv[3 * a.H] = ar[2 * a.hs + u] + bhn[i];
-        }
-        hreg[i] = h;
-        if (solo)
-          tile[r * L.as_ld + j] = from_f32<DT>(h);
-        else
-          coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), h);
+        const float hn_pre = ar[2 * a.hs + u] + bhn[i];
+        const float ng = ftanh(gxv[i][2] + rg * hn_pre);
+        gsv[i][0] = rg;
+        gsv[i][1] = zg;
+        gsv[i][2] = ng;
+        gsv[i][3] = hn_pre;
+        hreg[i] = (1.f - zg) * ng + zg * hreg[i];
       } else {
         const float ig = fsigmoid(gxv[i][0] + ar[u]);
         const float fg = fsigmoid(gxv[i][1] + ar[a.hs + u]);
         const float gg = ftanh(gxv[i][2] + ar[2 * a.hs + u]);
         const float og = fsigmoid(gxv[i][3] + ar[3 * a.hs + u]);
         const float c = clampf(fg * creg[i] + ig * gg, a.c_lo, a.c_hi);
-        const float m = og * ftanh(c);
-        if (a.rsv) {
-          float* rv = a.rsv + ((size_t)(rowbase + b) * a.D + d) * (5 * a.H) + j;
-          rv[0] = ig;
-          rv[a.H] = fg;
-          rv[2 * a.H] = gg;
-          rv[3 * a.H] = og;
-          rv[4 * a.H] = c;
-        }
+        gsv[i][0] = ig;
+        gsv[i][1] = fg;
+        gsv[i][2] = gg;
+        gsv[i][3] = og;
+        gsv[i][4] = c;
         creg[i] = c;
-        hreg[i] = m;
-        if (solo)
-          tile[r * L.as_ld + j] = from_f32<DT>(m);
-        else if (a.mode == kLSTM)
-          coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), m);
-        else
-          coh_store_elem<DT>(mx_rs, mx_el(b, j), m);
+        hreg[i] = og * ftanh(c);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxEpt; ++i) {
+      const int r = er[i], u = eu[i];
+      const int b = b0 + r;
+      if (t >= lenreg[i]) continue;
+      const int j = j0 + u;
+      const float h = hreg[i];
+      if (solo)
+        tile[r * L.as_ld + j] = from_f32<DT>(h);
+      else if (a.mode != kLSTMP)
+        coh_store_elem<DT>(hx_rs, hx_el(par ^ 1, b, j), h);
+      else
+        coh_store_elem<DT>(mx_rs, mx_el(b, j), h);
+      if (a.rsv) {
+        const int nsv = a.mode == kGRU ? 4 : 5;
+        float* rv = a.rsv + ((size_t)(rowbase + b) * a.D + d) * (nsv * a.H) + j;
+#pragma unroll
+        for (int q = 0; q < 5; ++q)
+          if (q < nsv) rv[q * a.H] = gsv[i][q];
       }
     }
     ++nbar;
