@@ -48,20 +48,20 @@ KERNEL_SOURCES = {
 # the ratio the same counter reads for a plain copy of known size
 # (--calibrate-copy). Valid only for the kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1578755, "write_bytes": 209408,
-                  "sources": "e7b0e248aab102ee"},
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186349358, "write_bytes": 25801350,
-                   "sources": "f697425d4261139a"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484741994, "write_bytes": 137109504,
-                    "sources": "e7b0e248aab102ee"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": 1, "fetch_bytes": 612226732, "write_bytes": 100467712,
-                      "sources": "e7b0e248aab102ee"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430798996, "write_bytes": 162342912,
-                        "sources": "e7b0e248aab102ee"},
-    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 89031, "write_bytes": 16512,
-                         "sources": "8fa5d4c56ef316cf"},
-    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 348819337, "write_bytes": 47403520,
-                         "sources": "f697425d4261139a"},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186338970, "write_bytes": 25801344,
+                  "sources": "d100d75e8eede01d"},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1605092, "write_bytes": 209408,
+                  "sources": "b1686d3f3fede4da"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484451342, "write_bytes": 137109504,
+                  "sources": "b1686d3f3fede4da"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": 0, "fetch_bytes": 612221646, "write_bytes": 100467712,
+                  "sources": "b1686d3f3fede4da"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430865187, "write_bytes": 162342912,
+                  "sources": "b1686d3f3fede4da"},
+    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 89032, "write_bytes": 16512,
+                  "sources": "fb89612b950ff62c"},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347734128, "write_bytes": 47402835,
+                  "sources": "d100d75e8eede01d"},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
