@@ -133,16 +133,23 @@ __device__ __forceinline__ void mm_wreg(const typename Chunk<DT>::T (&wr)[kScanR
 #pragma unroll
     for (int j = 0; j < NTC; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const DT* ap = As + (rt * 16 + lr) * as_ld + lq * kEpc + ks * a.rcpt * kK;
+    // Groups of four A chunks, each loaded before the previous group's
+    // MFMAs so that its LDS latency overlaps them.
+    V x[2][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[0][q] = *reinterpret_cast<const V*>(ap + q * kK);
 #pragma unroll
     for (int g = 0; g < CPT; g += 4) {
       if (g < a.rcpt) {  // rcpt is a multiple of 4
-        V x[4];
+        const int cur = (g / 4) & 1;
+        if (g + 4 < a.rcpt) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = *reinterpret_cast<const V*>(ap + (g + q) * kK);
+          for (int q = 0; q < 4; ++q) x[cur ^ 1][q] = *reinterpret_cast<const V*>(ap + (g + 4 + q) * kK);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int j = 0; j < NTC; ++j) c[j] = Chunk<DT>::mfma(x[q], wr[j * CPT + g + q], c[j]);
+          for (int j = 0; j < NTC; ++j) c[j] = Chunk<DT>::mfma(x[cur][q], wr[j * CPT + g + q], c[j]);
       }
     }
 #pragma unroll
