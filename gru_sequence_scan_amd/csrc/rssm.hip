@@ -535,12 +535,15 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
         if (has_h) hv = coh_load16(hx_rs, hx_el(par, b0 + rh, 4 * ch) * 4u);
         f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
         if (has_p) {
-          // all members' partials in a fixed order, sixteen loads in flight
+          // all members' partials in a fixed order, up to sixteen loads in
+          // flight (no load past the last member: traffic at the coherence
+          // point delays the other members' exchange)
           for (int m0 = 0; m0 < a.nw; m0 += 16) {
             u32x4 pv[16];
 #pragma unroll
             for (int m = 0; m < 16; ++m)
-              pv[m] = coh_load16(px_rs, px_el(par, b0 + rp, min(m0 + m, a.nw - 1), 4 * cp) * 4u);
+              pv[m] = m0 + m < a.nw ? coh_load16(px_rs, px_el(par, b0 + rp, m0 + m, 4 * cp) * 4u)
+                                    : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
               const f32x4 v = __builtin_bit_cast(f32x4, pv[m]);
@@ -573,7 +576,8 @@ __global__ void __launch_bounds__(kThreads) rssm_kernel(RssmArgs a) {
             u32x4 pv[16];
 #pragma unroll
             for (int m = 0; m < 16; ++m)
-              pv[m] = coh_load16(px_rs, px_el(par, b0 + rq, min(m0 + m, a.nw - 1), ea0 + 4 * cq) * 4u);
+              pv[m] = m0 + m < a.nw ? coh_load16(px_rs, px_el(par, b0 + rq, m0 + m, ea0 + 4 * cq) * 4u)
+                                    : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
               const f32x4 v = __builtin_bit_cast(f32x4, pv[m]);
