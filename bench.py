@@ -48,20 +48,20 @@ KERNEL_SOURCES = {
 # the ratio the same counter reads for a plain copy of known size
 # (--calibrate-copy). Valid only for the kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186338970, "write_bytes": 25801344,
-                  "sources": "d100d75e8eede01d"},
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1605092, "write_bytes": 209408,
-                  "sources": "b1686d3f3fede4da"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484451342, "write_bytes": 137109504,
-                  "sources": "b1686d3f3fede4da"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": 0, "fetch_bytes": 612221646, "write_bytes": 100467712,
-                  "sources": "b1686d3f3fede4da"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430865187, "write_bytes": 162342912,
-                  "sources": "b1686d3f3fede4da"},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186278276, "write_bytes": 25801517,
+                  "sources": "f3f12ae4c2a7ef3b"},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1607677, "write_bytes": 209408,
+                  "sources": "97ca7187a943543d"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484441768, "write_bytes": 137109504,
+                  "sources": "97ca7187a943543d"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": 1, "fetch_bytes": 612174902, "write_bytes": 100467712,
+                  "sources": "97ca7187a943543d"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430866825, "write_bytes": 162342912,
+                  "sources": "97ca7187a943543d"},
     "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 89032, "write_bytes": 16512,
                   "sources": "fb89612b950ff62c"},
-    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347734128, "write_bytes": 47402835,
-                  "sources": "d100d75e8eede01d"},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347890972, "write_bytes": 59181267,
+                  "sources": "f3f12ae4c2a7ef3b"},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
