@@ -215,10 +215,15 @@ WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
 // Launch planning
 // ---------------------------------------------------------------------------
 // Per-step time model (microseconds) from measurements on MI355X: a group
-// barrier with device-coherent exchange costs ~0.65 us plus ~9 ns per member;
+// barrier with device-coherent exchange costs ~0.65 us plus 6-9 ns per member;
 // the exchange read streams at roughly 100 GB/s per workgroup; MFMA and LDS
 // rates are those of one compute unit at 2.4 GHz.
 double barrier_us(int members) { return 0.65 + 0.009 * members; }
+// The forward scan's step pays less per member: a sweep of its launch shapes
+// measured LSTMP (B=32, H=1024, P=256) at 7.15 ms per layer with 32 members
+// of 32 units against 7.80 ms with 16 of 64, while the best GRU, var-len and
+// B=1 shapes stay where they were with 6 ns per member.
+double scan_barrier_us(int members) { return 0.65 + 0.006 * members; }
 
 double mm_us(bool mfma, int esize, int rows, int cols, int kp) {
   // (LDS-resident weights; the VALU form is bound by LDS latency, measured
@@ -345,7 +350,7 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wre
         const double xf = xcd_aligned && ns > 1 ? 0.85 : 1.0;
         // a one-member group keeps h in LDS: no exchange and no barrier
         const double ex =
-            ns == 1 && !lstmp ? 0.1 : (barrier_us(ns) + 0.3 + (double)bb * m.Kp * m.esize / 100e3) * xf;
+            ns == 1 && !lstmp ? 0.1 : (scan_barrier_us(ns) + 0.3 + (double)bb * m.Kp * m.esize / 100e3) * xf;
         double mm;
         if (wreg && mfma) {
           // per wave: rtiles * rcpt chunks, rnt MFMA tiles each; the h tile
@@ -362,7 +367,7 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wre
           double mp = mm_us(mfma, m.esize, bb, ps, mfma ? m.Hp : H);
           if (a.pnt > 0)  // K split over the waves
             mp = mp * a.pnt * a.pks / 4.0 + (a.pks > 1 ? 0.125 : 0.0);
-          t += (barrier_us(ns) + 0.3 + (double)bb * m.Hp * m.esize / 100e3) * xf + mp;
+          t += (scan_barrier_us(ns) + 0.3 + (double)bb * m.Hp * m.esize / 100e3) * xf + mp;
         }
         if (d->placement == 2 && !xcd_aligned) t += 1e3;  // requested: aligned plans first
         if (d->weights == 2 && !wreg) t += 1e3;            // requested: registers first
