@@ -48,20 +48,20 @@ KERNEL_SOURCES = {
 # the ratio the same counter reads for a plain copy of known size
 # (--calibrate-copy). Valid only for the kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186278276, "write_bytes": 25801517,
-                  "sources": "f3f12ae4c2a7ef3b"},
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1607677, "write_bytes": 209408,
-                  "sources": "97ca7187a943543d"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484441768, "write_bytes": 137109504,
-                  "sources": "97ca7187a943543d"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": 1, "fetch_bytes": 612174902, "write_bytes": 100467712,
-                  "sources": "97ca7187a943543d"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430866825, "write_bytes": 162342912,
-                  "sources": "97ca7187a943543d"},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186357888, "write_bytes": 25801350,
+                  "sources": "a6733cd17529444a"},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1608650, "write_bytes": 209408,
+                  "sources": "e63469f7e8bb78a7"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484502258, "write_bytes": 137109504,
+                  "sources": "e63469f7e8bb78a7"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": 0, "fetch_bytes": 612232320, "write_bytes": 118933504,
+                  "sources": "e63469f7e8bb78a7"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430878472, "write_bytes": 162342912,
+                  "sources": "e63469f7e8bb78a7"},
     "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 89032, "write_bytes": 16512,
-                  "sources": "fb89612b950ff62c"},
-    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347890972, "write_bytes": 59181267,
-                  "sources": "f3f12ae4c2a7ef3b"},
+                  "sources": "a6a0a461dadf8b05"},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347908225, "write_bytes": 59181325,
+                  "sources": "a6733cd17529444a"},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
