@@ -12,7 +12,7 @@
 // 2x2 arrangement, each wave a 64x64 block of 32x32 MFMA tiles
 // (v_mfma_f32_32x32x16_bf16 for bf16 operands, v_mfma_f32_32x32x2_f32 for
 // fp32). K advances 64 bytes per stage. The main form streams stages
-// straight from global memory into a four-deep LDS ring (below); a simpler
+// straight from global memory into a three-deep LDS ring (below); a simpler
 // register-staged double buffer handles ragged K and unaligned rows.
 // Every lane reads whole 16-byte chunks from LDS: the k index a lane supplies
 // to each MFMA step is permuted identically for both operands, which leaves
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256) gemm_xw_kernel(GemmArgs a) {
 // bank groups. Needs K to be a whole number of stages and 16-byte aligned
 // rows; rows past M or N read a zero chunk.
 // ---------------------------------------------------------------------------
-constexpr int kStages = 4;
+constexpr int kStages = 3;  // 48 KiB: three workgroups per CU (measured 6% faster than four stages at two)
 constexpr int kStageBytes = (kBM + kBN) * kRowBytes;  // 16 KiB
 static_assert(kEpiBytes <= kStages * kStageBytes, "epilogue staging exceeds the LDS ring");
 
