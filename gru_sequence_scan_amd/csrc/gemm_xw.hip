@@ -18,6 +18,8 @@
 // to each MFMA step is permuted identically for both operands, which leaves
 // each dot product unchanged. Output tiles are dealt to XCDs in contiguous
 // runs so that tiles sharing X rows share an L2.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -87,27 +89,49 @@ __device__ __forceinline__ u32x4 load_chunk(const DT* base, int rows, int K, int
 // recurrence, after the whole product. 32x32 accumulator layout: lane holds
 // column l32 and rows 8 (v / 4) + 4 half + v % 4. The LDS row stride of 136
 // floats puts the two lane halves (rows 4 apart) on disjoint banks.
+// b_ih(n) plus, except for the GRU candidate rows, b_hh(n) (zero without biases).
+template <typename DT>
+__device__ __forceinline__ float fold_bias(const GemmArgs& a, int n) {
+  if (!a.has_bias) return 0.0f;
+  const int dir = n / a.G, nr = n - dir * a.G;
+  float b = to_f32<DT>(reinterpret_cast<const DT*>(a.b_ih[dir])[nr]);
+  if (nr < a.hh_fold_rows) b += to_f32<DT>(reinterpret_cast<const DT*>(a.b_hh[dir])[nr]);
+  return b;
+}
+
+// K stages [kt0, kt1) of this workgroup's split (blockIdx.y), and where its
+// tile goes: the output with the bias fold, or its partial buffer.
+struct KRange {
+  int kt0, kt1;
+  float* C;
+  bool with_bias;
+};
+__device__ __forceinline__ KRange k_range(const GemmArgs& a, int nk) {
+  if (a.splits <= 1) return KRange{0, nk, a.C, true};
+  const int s = blockIdx.y, per = (nk + a.splits - 1) / a.splits;
+  const int kt0 = min(nk, s * per), kt1 = min(nk, kt0 + per);
+  return KRange{kt0, kt1, a.part + (size_t)s * a.M * a.N, false};
+}
+
 constexpr int kEpiStride = 136;
 constexpr int kEpiBytes = 64 * kEpiStride * 4;  // 34816
 static_assert(kEpiBytes <= 2 * 2 * kTileBytes, "epilogue staging exceeds the operand buffers");
 
 template <typename DT>
-__device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[2][2], float* lds, int m0, int n0) {
+__device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[2][2], float* lds, int m0, int n0,
+                                           float* C, bool with_bias) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, half = lane >> 5, l32 = lane & 31;
   const int c4 = tid & 31, rbase = tid >> 5;  // this thread's 16-byte column chunk and first row
   const int n = n0 + 4 * c4;
   float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (a.has_bias) {
+  if (with_bias) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (n + e >= a.N) continue;
-      const int dir = (n + e) / a.G, nr = n + e - dir * a.G;
-      bias[e] = to_f32<DT>(reinterpret_cast<const DT*>(a.b_ih[dir])[nr]);
-      if (nr < a.hh_fold_rows) bias[e] += to_f32<DT>(reinterpret_cast<const DT*>(a.b_hh[dir])[nr]);
+      if (n + e < a.N) bias[e] = fold_bias<DT>(a, n + e);
     }
   }
-  const bool vec = (a.N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.C) & 15) == 0 && n + 4 <= a.N;
+  const bool vec = (a.N & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0 && n + 4 <= a.N;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     if (p) __syncthreads();  // the first pass's reads are done
@@ -129,7 +153,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[2][2
       f32x4 v = *reinterpret_cast<const f32x4*>(lds + r * kEpiStride + 4 * c4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += bias[e];
-      float* dst = a.C + (size_t)m * a.N + n;
+      float* dst = C + (size_t)m * a.N + n;
       if (vec) {
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
       } else {
@@ -201,12 +225,13 @@ __global__ void __launch_bounds__(256) gemm_xw_kernel(GemmArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int half = lane >> 5, l32 = lane & 31;
 
-  gload(0);
+  const KRange kr = k_range(a, nk);
+  gload(kr.kt0 * kBK);
   lstore(0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+  for (int kt = kr.kt0; kt < kr.kt1; ++kt) {
+    const int buf = (kt - kr.kt0) & 1;
+    if (kt + 1 < kr.kt1) gload((kt + 1) * kBK);
     const char* As = smem[buf][0];
     const char* Bs = smem[buf][1];
 #pragma unroll
@@ -218,11 +243,11 @@ __global__ void __launch_bounds__(256) gemm_xw_kernel(GemmArgs a) {
         Mfma<DT>::run(arow, brow, half, acc[i][j]);
       }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    if (kt + 1 < kr.kt1) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  store_tile<DT>(a, acc, reinterpret_cast<float*>(&smem[0][0][0]), m0, n0);
+  store_tile<DT>(a, acc, reinterpret_cast<float*>(&smem[0][0][0]), m0, n0, kr.C, kr.with_bias);
 }
 
 // ---------------------------------------------------------------------------
@@ -326,8 +351,9 @@ __global__ void __launch_bounds__(256) gemm_xw_pipe_kernel(GemmArgs a) {
     kofs[j] = p ? c * kEpc * (int)sizeof(DT) : 0;  // byte offset of the chunk within a stage
   }
   const int nk = a.K / kBK;
+  const KRange kr = k_range(a, nk);
   auto issue = [&](int kt) {
-    char* dst = smem[kt % kStages];
+    char* dst = smem[(kt - kr.kt0) % kStages];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const char* g = src[j] == a.zero16 ? src[j] : src[j] + (size_t)kt * kRowBytes + kofs[j];
@@ -347,19 +373,19 @@ __global__ void __launch_bounds__(256) gemm_xw_pipe_kernel(GemmArgs a) {
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
+    if (kr.kt0 + s < kr.kt1) issue(kr.kt0 + s);
+  for (int kt = kr.kt0; kt < kr.kt1; ++kt) {
     // Stage kt landed once at most the later stages' loads are pending. A
     // bare barrier then makes every wave's part of it visible (and every
     // wave is done reading the buffer that the next issue refills, since its
     // MFMAs consumed those reads); __syncthreads would also drain the
     // younger stages' loads.
-    wait_vm(4 * min(kStages - 2, nk - 1 - kt));
+    wait_vm(4 * min(kStages - 2, kr.kt1 - 1 - kt));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-    const char* As = smem[kt % kStages];
+    if (kt + kStages - 1 < kr.kt1) issue(kt + kStages - 1);
+    const char* As = smem[(kt - kr.kt0) % kStages];
     const char* Bs = As + kBM * kRowBytes;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -370,15 +396,53 @@ __global__ void __launch_bounds__(256) gemm_xw_pipe_kernel(GemmArgs a) {
 
   // Every wave is done reading the ring before the epilogue reuses it.
   __syncthreads();
-  store_tile<DT>(a, acc, reinterpret_cast<float*>(&smem[0][0]), m0, n0);
+  store_tile<DT>(a, acc, reinterpret_cast<float*>(&smem[0][0]), m0, n0, kr.C, kr.with_bias);
+}
+
+// C = sum over the splits, in split order, of the partial products, plus the
+// bias fold: four consecutive outputs per thread (N % 4 == 0) or one. Plain
+// stores: a split product is small, and the recurrence reads it next.
+template <typename DT>
+__global__ void __launch_bounds__(256) gemm_xw_reduce_kernel(GemmArgs a) {
+  const size_t total = (size_t)a.M * a.N;
+  const size_t plane = total;
+  if ((a.N & 3) == 0) {
+    for (size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x; i4 * 4 < total; i4 += (size_t)gridDim.x * 256) {
+      const size_t i = i4 * 4;
+      f32x4 v = *reinterpret_cast<const f32x4*>(a.part + i);
+      for (int s = 1; s < a.splits; ++s) v += *reinterpret_cast<const f32x4*>(a.part + s * plane + i);
+      const int n = (int)(i % a.N);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += fold_bias<DT>(a, n + e);
+      *reinterpret_cast<f32x4*>(a.C + i) = v;
+    }
+  } else {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+      float v = a.part[i];
+      for (int s = 1; s < a.splits; ++s) v += a.part[s * plane + i];
+      a.C[i] = v + fold_bias<DT>(a, (int)(i % a.N));
+    }
+  }
 }
 
 }  // namespace
 
+// Products with fewer than 64 output tiles leave most of the 256 CUs idle
+// (the TVM benchmark's T = 80, B = 1 LSTM has 8): split K so that the launch
+// has about 128 workgroups, each keeping at least four K stages.
+int gemm_xw_splits(long long M, int N, int K, int dtype_bf16) {
+  const long long tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  if (tiles >= 64) return 1;
+  const int nk = (K + kRowBytes / (dtype_bf16 ? 2 : 4) - 1) / (kRowBytes / (dtype_bf16 ? 2 : 4));
+  int s = (int)std::min<long long>(8, std::max<long long>(1, 128 / tiles));
+  s = std::min(s, std::max(1, nk / 4));
+  return s;
+}
+
 hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream) {
   const int ntn = (a.N + kBN - 1) / kBN;
   const int ntm = (a.M + kBM - 1) / kBM;
-  const dim3 grid(ntn * ntm), block(256);
+  const dim3 grid(ntn * ntm, a.splits > 1 ? a.splits : 1), block(256);
   // fp32 operands: the streamed form (measured 10% faster at K = 1024). bf16
   // operands: the register-staged form, at three workgroups per CU, measured
   // 10-30% faster than the streamed one at two.
@@ -393,6 +457,16 @@ hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream)
       hipLaunchKernelGGL(gemm_xw_pipe_kernel<float>, grid, block, 0, stream, a);
     else
       hipLaunchKernelGGL(gemm_xw_kernel<float>, grid, block, 0, stream, a);
+  }
+  if (a.splits > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t work = ((size_t)a.M * a.N + 3) / 4;
+    const int blocks = (int)std::min<size_t>(1024, (work + 255) / 256);
+    if (dtype_bf16)
+      hipLaunchKernelGGL(gemm_xw_reduce_kernel<bf16>, dim3(blocks), block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(gemm_xw_reduce_kernel<float>, dim3(blocks), block, 0, stream, a);
   }
   return hipGetLastError();
 }

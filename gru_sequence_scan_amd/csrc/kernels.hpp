@@ -18,7 +18,12 @@ struct GemmArgs {
   int has_bias;
   int vec_ok;           // A and W rows 16-byte aligned (K * esize % 16 == 0)
   const void* zero16;   // 16 zero bytes in device memory (stand-in for rows past M or N)
+  int splits;           // > 1: K split over blockIdx.y, partial tiles summed by a second kernel
+  float* part;          // [splits][M][N] partial products (splits > 1)
 };
+// Split of K for a product with few output tiles (1 = none); the same figure
+// sizes the workspace and drives the launch.
+int gemm_xw_splits(long long M, int N, int K, int dtype_bf16);
 hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream);
 
 // Kernel 2: persistent scan over time for one layer, all directions.

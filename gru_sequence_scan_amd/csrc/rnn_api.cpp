@@ -151,7 +151,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // needs no device)
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t status, counters, ints, gx, inter0, inter1, hx, mx, ex_h, ex_p, total;
+  size_t status, counters, ints, gx, inter0, inter1, hx, mx, ex_h, ex_p, gpart, total;
   size_t counters_bytes;
   int n_ints;
 };
@@ -207,6 +207,14 @@ WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
   w.inter1 = d->num_layers > 2 ? take(inter) : 0;
   w.hx = take((size_t)2 * m.D * d->B * m.Kp * m.esize);
   w.mx = d->mode == RNN_MODE_LSTMP ? take((size_t)m.D * d->B * m.Hp * m.esize) : 0;
+  // split-K partial products of the input GEMMs with few output tiles
+  size_t gpart = 0;
+  for (int l = 0; l < d->num_layers; ++l) {
+    const int in_l = l == 0 ? d->input_size : m.D * m.K;
+    const int sp = gemm_xw_splits(m.rows, m.D * m.G, in_l, d->dtype == RNN_DTYPE_BF16);
+    if (sp > 1) gpart = std::max(gpart, (size_t)sp * (size_t)m.rows * m.D * m.G * 4);
+  }
+  w.gpart = gpart ? take(gpart) : 0;
   w.total = o;
   return w;
 }
@@ -642,6 +650,8 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     }
     g.vec_ok = vec;
     g.zero16 = ws + L.status + kZeroChunk;
+    g.splits = gemm_xw_splits(g.M, g.N, g.K, bf16);
+    g.part = g.splits > 1 ? (float*)(ws + L.gpart) : nullptr;
     if ((rc = prof.begin(1)) != RNN_OK) return rc;
     if ((rc = hip_status(launch_gemm_xw(g, bf16, st))) != RNN_OK) return rc;
     if ((rc = prof.end()) != RNN_OK) return rc;

@@ -61,6 +61,13 @@ SMALL = [
     ("bigru_packed_bf16", "gru", "bf16", 13, 34, 32, 64, 0, 2, True, "packed", (2, 13), True, False),
     ("bilstmp_packed", "lstmp", "f32", 12, 17, 16, 48, 16, 2, True, "packed", (1, 12), True, True),
     ("lstm_padded_varlen", "lstm", "f32", 14, 19, 12, 36, 0, 1, True, "padded", "unsorted", True, True),
+    # input products with few output tiles split K over workgroups (ragged
+    # split ranges; register-staged fp32, unaligned bf16 rows, streamed fp32,
+    # and both layers of a packed bidirectional stack)
+    ("lstm_splitk_f32", "lstm", "f32", 5, 7, 200, 48, 0, 1, False, "padded", None, True, True),
+    ("gru_splitk_bf16", "gru", "bf16", 6, 5, 300, 40, 0, 1, False, "padded", None, True, True),
+    ("lstm_splitk_pipe", "lstm", "f32", 4, 9, 256, 72, 0, 1, False, "padded", None, True, False),
+    ("bilstm_splitk_packed", "lstm", "f32", 7, 6, 160, 96, 0, 2, True, "packed", (1, 7), True, True),
 ]
 
 
