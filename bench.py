@@ -48,20 +48,20 @@ KERNEL_SOURCES = {
 # the ratio the same counter reads for a plain copy of known size
 # (--calibrate-copy). Valid only for the kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186357888, "write_bytes": 25801350,
-                  "sources": "a6733cd17529444a"},
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1608650, "write_bytes": 209408,
-                  "sources": "e63469f7e8bb78a7"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484502258, "write_bytes": 137109504,
-                  "sources": "e63469f7e8bb78a7"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": 0, "fetch_bytes": 612232320, "write_bytes": 118933504,
-                  "sources": "e63469f7e8bb78a7"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430878831, "write_bytes": 162342912,
-                  "sources": "e63469f7e8bb78a7"},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186313269, "write_bytes": 25801344,
+                  "sources": "0e4a066d23eb9b61"},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1604093, "write_bytes": 209408,
+                  "sources": "3f354d56f448965b"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484489305, "write_bytes": 137109504,
+                  "sources": "3f354d56f448965b"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": 1, "fetch_bytes": 612697552, "write_bytes": 118933504,
+                  "sources": "3f354d56f448965b"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430868463, "write_bytes": 162342912,
+                  "sources": "3f354d56f448965b"},
     "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 89032, "write_bytes": 16512,
-                  "sources": "a6a0a461dadf8b05"},
-    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347908225, "write_bytes": 59181325,
-                  "sources": "a6733cd17529444a"},
+                  "sources": "b8254d84c30cf6bc"},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347863479, "write_bytes": 59181414,
+                  "sources": "0e4a066d23eb9b61"},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
