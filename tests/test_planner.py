@@ -146,3 +146,22 @@ def test_wave_scan_choice(mode, H, expect):
         # a tiling hint asks for the tiled scan
         d.tile_batch = 1
         assert gss.rnn_plan_info(d)["kernel"] == 2
+
+
+# Launch shapes that a sweep of the tiling hints measured fastest on MI355X
+# (rows per group, hidden units per member): the cost model must keep
+# choosing them.
+MEASURED_BEST = {
+    "lstm_t80_b1": (1, 16),
+    "gru_t256_b256": (16, 32),
+    "lstmp_t1000_b32": (16, 32),
+    "bilstm_varlen_b64": (16, 16),
+    "rssm_b50_t50": (2, 20),
+}
+
+
+@pytest.mark.parametrize("name", list(MEASURED_BEST))
+def test_plans_match_measured_best_shapes(name):
+    _, d, lengths = desc_for(name)
+    p = gss.rnn_plan_info(d, lengths)
+    assert (p["rows"], p["hidden_per_wg"]) == MEASURED_BEST[name]
