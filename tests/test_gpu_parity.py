@@ -91,6 +91,30 @@ def test_small_cases(case):
     _compare(d, got, ref, name)
 
 
+# The largest hidden sizes the planner accepts on one MI355X: groups of 128 to
+# 256 members (every CU in one group for the B = 1 fp32 and the bf16 H = 2048
+# cases), weights resident in LDS or registers. One size beyond is rejected
+# before launch (checked on the CPU in the planner tests).
+MAX_CASES = [
+    # name, mode, dtype, T, B, F, H
+    ("lstm_f32_h1024_b1", "lstm", "f32", 3, 1, 64, 1024),
+    ("lstm_f32_h1024_b16", "lstm", "f32", 3, 16, 64, 1024),
+    ("gru_f32_h1024_b16", "gru", "f32", 3, 16, 64, 1024),
+    ("lstm_bf16_h2048_b16", "lstm", "bf16", 3, 16, 64, 2048),
+]
+
+
+@pytest.mark.parametrize("case", MAX_CASES, ids=[c[0] for c in MAX_CASES])
+def test_max_size_cases(case):
+    name, mode, dt, T, B, F, H = case
+    log(f"[gpu] maximum size case {name}")
+    d = synth.make_rnn_inputs(mode, T, B, F, H, dtype=dt, w_scale=1.0 / np.sqrt(H),
+                              seed=zlib.crc32(name.encode()) % 1000, h0_std=0.3, c0_std=0.3)
+    got = run_rnn(d, y_fill=float("nan"))
+    ref = _oracle(d)
+    _compare(d, got, ref, name)
+
+
 @pytest.mark.parametrize("case", __import__("layout_cases").REG_CASES, ids=lambda c: c[0])
 def test_register_layouts(case):
     """Each register-resident W_hh layout (and the LDS fallback) against the

@@ -165,3 +165,23 @@ def test_plans_match_measured_best_shapes(name):
     _, d, lengths = desc_for(name)
     p = gss.rnn_plan_info(d, lengths)
     assert (p["rows"], p["hidden_per_wg"]) == MEASURED_BEST[name]
+
+
+@pytest.mark.parametrize("mode,dtype,H,B,ok", [
+    (0, 0, 1024, 1, True), (0, 0, 1024, 16, True), (1, 0, 1024, 16, True), (0, 1, 2048, 16, True),
+    (0, 0, 1280, 1, False), (0, 0, 1280, 16, False), (1, 0, 1280, 16, False), (0, 1, 2560, 16, False),
+])
+def test_largest_hidden_sizes(mode, dtype, H, B, ok):
+    """The largest recurrences that fit the persistent kernels on one device
+    plan; one step beyond is RNN_E_PLAN before anything is launched."""
+    d = gss.RnnDesc()
+    d.mode, d.dtype, d.layout, d.T, d.B = mode, dtype, 0, 3, B
+    d.input_size, d.hidden_size, d.proj_size = 64, H, 0
+    d.num_layers, d.bidirectional, d.has_bias = 1, 0, 1
+    if ok:
+        p = gss.rnn_plan_info(d)
+        assert p["hidden_per_wg"] * p["members"] >= H and p["workgroups"] <= 256
+    else:
+        with pytest.raises(gss.RnnError) as e:
+            gss.rnn_plan_info(d)
+        assert e.value.status == CODE["RNN_E_PLAN"]
