@@ -358,6 +358,24 @@ def main():
         roofline["traffic_fetch"] = meas["fetch_bytes"]
         roofline["traffic_write"] = meas["write_bytes"]
 
+    # The dominant kernel per recurrence step: its step count, time per step
+    # and group barriers per step (0 for one-member groups and the one-wave
+    # scan), for comparison with the device-coherent round trip that bounds a
+    # barrier.
+    if spec.mode in ("rssm", "rssm_actor"):
+        n_rec, layer_dirs, bars = d["T"], 1, 1
+    else:
+        n_rec = int(lengths.max()) if lengths is not None else spec.T
+        layer_dirs = spec.num_layers * (2 if spec.bidirectional else 1)
+        if dom["kernel"] == "scan_wave":
+            bars = 0
+        else:
+            members = gss.rnn_plan_info(desc, lengths)["members"]
+            bars = 0 if (members == 1 and spec.mode != "lstmp") else (2 if spec.mode == "lstmp" else 1)
+    roofline["recurrence_steps"] = n_rec
+    roofline["us_per_step"] = dom["avg_us"] / n_rec
+    roofline["barriers_per_step"] = bars
+
     ms_per_step = elapsed / K * 1e3
     value = tokens / (elapsed / K)
     ctx = PAGES_CONTEXT.get(name)
@@ -368,6 +386,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": vs,
         "dtype": spec.dtype, "data": "synthetic", "config": config,
         "roofline": roofline, "kernels": kernels,
+        "cell_steps_per_s": value * layer_dirs,
     }
     if ctx:
         rec["pages_context"] = {k: v for k, v in ctx.items()}
