@@ -491,6 +491,27 @@ def train_main(args):
     print(json.dumps(line), flush=True)
 
 
+def host_info():
+    """The host CPU model and the BLAS library numpy uses (the oracle's
+    products run on it)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name')} {b.get('version')}"
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
 def cpu_baseline_train(spec, d, seconds):
     """The float64 oracle's forward + BPTT on a sample of batch rows (all
     timesteps), sized from a one-row probe."""
@@ -527,7 +548,8 @@ def cpu_baseline_train(spec, d, seconds):
     rows = int(min(spec.B, max(1, seconds / max(t1, 1e-6))))
     tokens, el = run(rows)
     return {"value": tokens / el, "unit": UNIT, "cores": int(threads), "kind": "oracle",
-            "sample": f"forward + backward of {rows} of {spec.B} batch rows over all timesteps, {el:.1f} s"}
+            "sample": f"forward + backward of {rows} of {spec.B} batch rows over all timesteps, {el:.1f} s",
+            **host_info()}
 
 
 def cpu_baseline_any(spec, d, seconds):
@@ -578,7 +600,7 @@ def cpu_baseline_any(spec, d, seconds):
         tokens, el = run(rows)
         sample = f"{rows} of {spec.B} batch rows over all timesteps, {el:.1f} s"
     return {"value": tokens / el, "unit": UNIT, "cores": int(threads), "kind": "oracle",
-            "sample": sample}
+            "sample": sample, **host_info()}
 
 
 if __name__ == "__main__":
