@@ -406,7 +406,8 @@ template <typename DT>
 __global__ void __launch_bounds__(256) gemm_xw_reduce_kernel(GemmArgs a) {
   const size_t total = (size_t)a.M * a.N;
   const size_t plane = total;
-  if ((a.N & 3) == 0) {
+  if ((a.N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.C) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(a.part) & 15) == 0) {
     for (size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x; i4 * 4 < total; i4 += (size_t)gridDim.x * 256) {
       const size_t i = i4 * 4;
       f32x4 v = *reinterpret_cast<const f32x4*>(a.part + i);
@@ -444,8 +445,8 @@ hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream)
   const int ntm = (a.M + kBM - 1) / kBM;
   const dim3 grid(ntn * ntm, a.splits > 1 ? a.splits : 1), block(256);
   // fp32 operands: the streamed form (measured 10% faster at K = 1024). bf16
-  // operands: the register-staged form, at three workgroups per CU, measured
-  // 10-30% faster than the streamed one at two.
+  // operands: the register-staged form (up to four workgroups per CU),
+  // measured 0-30% faster than the streamed one.
   const bool pipe = !dtype_bf16 && a.vec_ok && a.zero16 && a.K % (kRowBytes / 4) == 0;
   if (dtype_bf16) {
     if (pipe)
