@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the recurrence forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|1..5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|NAME|1..5]
 
 A step is one rnn_forward of the whole hot path for the workload (every
 kernel it enqueues: input-projection GEMMs, scans, or the RSSM kernel) on
@@ -10,8 +10,11 @@ the throughput in timestep*batch/s, the roofline of the dominant kernel
 (timed with HIP events around its launches inside the timed region) and the
 float64 CPU oracle timed on the host on a bounded sample of the same work.
 
-Default workload: the RSSM-prior unroll, B=50, T=50 (state 20, action 6,
-hidden 200, GRU hidden 200, fp32).
+Default (--workload all): the headline is the RSSM-prior unroll, B=50, T=50
+(state 20, action 6, hidden 200, GRU hidden 200, fp32), at the top level of
+the line; "configs" then holds the same record (value, ms per step, median
+and minimum, dominant-kernel roofline, CPU baseline) for each of the five
+configurations, each timed for the same K steps after W warm-ups.
 """
 
 import argparse
@@ -28,11 +31,14 @@ sys.path.insert(0, ROOT)
 
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
+# LDS: 128 bytes per clock per CU, 256 CUs at 2.4 GHz
+PEAK_LDS_GBS = 128 * 256 * 2.4
 PEAK_TFLOPS = {"bf16": 2500.0, "f32_mfma": 157.3, "f32_vector": 157.3}
 
 KIND_NAMES = {1: "gemm_xw", 2: "scan", 3: "rssm", 4: "scan_wave"}
 METRIC = "timestep\u00b7batch/s per RNN config; % of MFMA / on-chip BW roofline"
 UNIT = "timestep\u00b7batch/s"
+HEADLINE = "rssm_b50_t50"
 
 # Sources whose change invalidates a kernel's measured traffic.
 CSRC = os.path.join(ROOT, "gru_sequence_scan_amd", "csrc")
@@ -78,8 +84,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="rssm_b50_t50")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--workload", default="all",
+                    help="'all' (default): the RSSM unroll as the headline plus a block per config; "
+                         "or one workload name / 1-based index")
+    ap.add_argument("--cpu-seconds", type=float, default=5.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--tile-batch", type=int, default=0)
     ap.add_argument("--tile-hidden", type=int, default=0)
@@ -167,42 +175,30 @@ def algorithmic(spec, d):
     return out
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the recurrence shards by batch with no exchange; see the design notes)", file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.train:
-        train_main(args)
-        return
+def prepare(name, args):
+    """Inputs of a workload resident on the GPU and the C structs of one
+    rnn_forward over them (built once, outside any timed region)."""
     import torch
 
     import gru_sequence_scan_amd as gss
     import synth
 
-    name = synth.ORDER[int(args.workload) - 1] if args.workload.isdigit() else args.workload
     spec = synth.spec(name)
     d = synth.make_inputs(name)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
 
     def T(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(dt)
 
-    # Build the C structs once (inputs resident in HBM before timing).
     keep = []
+    hints = dict(tile_batch=args.tile_batch, tile_hidden=args.tile_hidden, placement=args.placement,
+                 return_workspace=True, check_status=False)
     if spec.mode in ("rssm", "rssm_actor"):
         actor = spec.mode == "rssm_actor"
         w = {k: T(v) for k, v in d["weights"].items()}
         aw = {k: T(v) for k, v in d["actor"].items()} if actor else None
         acts, eps = T(d["actions"]), T(d["eps"])
-        hints = dict(tile_batch=args.tile_batch, tile_hidden=args.tile_hidden, placement=args.placement,
-                     return_workspace=True)
         if actor:
             (out, ws) = gss.rssm_actor_unroll(eps, w, aw, **hints)
         else:
@@ -238,11 +234,8 @@ def main():
         x = T(d["x"])
         (out, ws) = gss.rnn_forward(spec.mode, x, params, lengths=d["lengths"], layout=spec.layout,
                                     num_layers=spec.num_layers, bidirectional=spec.bidirectional,
-                                    proj_size=spec.proj_size, tile_batch=args.tile_batch,
-                                    tile_hidden=args.tile_hidden, placement=args.placement,
-                                    return_workspace=True)
+                                    proj_size=spec.proj_size, **hints)
         y, hn, cn = out
-        D = 2 if spec.bidirectional else 1
         desc = gss.RnnDesc()
         desc.mode = gss.MODES[spec.mode]
         desc.dtype = 1 if spec.dtype == "bf16" else 0
@@ -259,13 +252,49 @@ def main():
         io.x, io.y, io.h_n = x.data_ptr(), y.data_ptr(), hn.data_ptr()
         io.c_n = cn.data_ptr() if cn is not None else None
         lengths = d["lengths"]
-        keep_len, io.lengths_host = gss.binding._len_ptr(lengths)
+        keep_len, io.lengths_host = gss.binding._len_ptr(lengths, spec.B)
         keep += [params, x, out, keep_len]
         tokens = int(lengths.sum()) if lengths is not None else spec.T * spec.B
         config = {"workload": name, "mode": spec.mode, "T": spec.T, "B": spec.B, "input": spec.input_size,
                   "hidden": spec.hidden_size, "proj": spec.proj_size, "layers": spec.num_layers,
                   "bidirectional": spec.bidirectional, "layout": spec.layout, "tokens": tokens}
     torch.cuda.synchronize()
+    return {"name": name, "spec": spec, "d": d, "desc": desc, "wt": wt, "io": io, "ws": ws, "keep": keep,
+            "tokens": tokens, "config": config, "lengths": lengths}
+
+
+def onchip_bytes(spec, d, plan):
+    """Bytes of resident weights one launch of the recurrence kernel reads
+    from on-chip storage: every member reads its slice once per step (the
+    RSSM's replicated small matrices once per member)."""
+    if spec.mode in ("rssm", "rssm_actor"):
+        S, A, E, Hb, Ea = d["state_dim"], d["action_dim"], d["embed_dim"], d["belief_dim"], d.get("actor_dim", 0)
+        split = 3 * Hb * (E + Hb) + E * Hb + Ea * Hb                 # sliced over the members
+        repl = E * (S + A) + 2 * S * E + Ea * S + A * Ea              # whole in every member
+        per_step = plan["groups"] * (split + plan["members"] * repl) * 4
+        return per_step * d["T"]
+    D = 2 if spec.bidirectional else 1
+    G = (3 if spec.mode == "gru" else 4) * spec.hidden_size
+    K = spec.proj_size if spec.mode == "lstmp" else spec.hidden_size
+    es = 2 if spec.dtype == "bf16" else 4
+    P = spec.proj_size if spec.mode == "lstmp" else 0
+    L = d["lengths"]
+    steps = int(L.max()) if L is not None else spec.T
+    blocks = max(1, plan.get("groups", 1))  # batch blocks per direction
+    return steps * D * blocks * (G * K + P * spec.hidden_size) * es
+
+
+def measure(name, args, rt_us, with_cpu):
+    """Time K forwards of one workload after W warm-ups; per-kernel times from
+    HIP events recorded on the launch stream by rnn_forward_profiled."""
+    import torch
+
+    import gru_sequence_scan_amd as gss
+
+    pr = prepare(name, args)
+    spec, d, desc, wt, io, ws = pr["spec"], pr["d"], pr["desc"], pr["wt"], pr["io"], pr["ws"]
+    lengths, tokens = pr["lengths"], pr["tokens"]
+    dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev).cuda_stream
     hip = _hip()
     lib = gss.lib()
@@ -290,7 +319,7 @@ def main():
         step()
     torch.cuda.synchronize()
     if gss.rnn_read_status(ws_ptr, stream) != 0:
-        raise RuntimeError("device status error after warmup")
+        raise RuntimeError(f"{name}: device status error after warmup")
 
     K = args.steps
     ev_arrays = []
@@ -312,15 +341,19 @@ def main():
     elapsed = time.perf_counter() - t0
     status = gss.rnn_read_status(ws_ptr, stream)
     if status != 0:
-        raise RuntimeError(f"device status {status} after timed steps")
+        raise RuntimeError(f"{name}: device status {status} after timed steps")
 
     n_k = nk.value
     per_kernel = [[] for _ in range(n_k)]
+    step_ms = []
     for arr in ev_arrays:
         for j in range(min(n_k, max_k)):
             ms = ctypes.c_float(0)
             hip.hipEventElapsedTime(ctypes.byref(ms), arr[2 * j], arr[2 * j + 1])
             per_kernel[j].append(ms.value)
+        ms = ctypes.c_float(0)
+        hip.hipEventElapsedTime(ctypes.byref(ms), arr[0], arr[2 * (min(n_k, max_k) - 1) + 1])
+        step_ms.append(ms.value)
     for arr in ev_arrays:
         for j in range(2 * max_k):
             hip.hipEventDestroy(arr[j])
@@ -332,12 +365,12 @@ def main():
         idx = seen.get(kd, 0)
         seen[kd] = idx + 1
         a = algo[kd][idx]
-        avg_ms = float(np.mean(per_kernel[j]))
-        kernels.append({"kernel": KIND_NAMES[kd], "index": idx, "avg_us": avg_ms * 1e3,
-                        "min_us": float(np.min(per_kernel[j])) * 1e3, "flops": a["flops"], "bytes": a["bytes"]})
+        v = np.asarray(per_kernel[j]) * 1e3
+        kernels.append({"kernel": KIND_NAMES[kd], "index": idx, "avg_us": float(v.mean()),
+                        "median_us": float(np.median(v)), "min_us": float(v.min()),
+                        "flops": a["flops"], "bytes": a["bytes"]})
     dom = max(kernels, key=lambda k: k["avg_us"])
     achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
-    unit = "TFLOP/s"
     if dom["kernel"] == "scan_wave" or (dom["kernel"] == "scan" and spec.B < 16):
         # the small-batch scans run their products on the vector ALUs
         bound, peak = "alu", PEAK_TFLOPS["f32_vector"]
@@ -349,8 +382,9 @@ def main():
     digest = sources_digest(dom["kernel"])
     if meas and (meas["kernel"], meas["index"]) == (dom["kernel"], dom["index"]) and meas["sources"] == digest:
         traffic = meas["fetch_bytes"] + meas["write_bytes"]
-    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                 "traffic": traffic, "kernel": f"{dom['kernel']}[{dom['index']}]", "avg_us": dom["avg_us"],
+                "median_us": dom["median_us"], "min_us": dom["min_us"],
                 "algorithmic_flops": dom["flops"], "algorithmic_hbm_bytes": dom["bytes"],
                 "hbm_frac": dom["bytes"] / (dom["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
                 "sources": digest}
@@ -358,40 +392,100 @@ def main():
         roofline["traffic_fetch"] = meas["fetch_bytes"]
         roofline["traffic_write"] = meas["write_bytes"]
 
-    # The dominant kernel per recurrence step: its step count, time per step
-    # and group barriers per step (0 for one-member groups and the one-wave
-    # scan), for comparison with the device-coherent round trip that bounds a
-    # barrier.
+    # The recurrence kernel's steps, time per step and cross-CU exchanges per
+    # step; its on-chip term; the fraction against the compute units the
+    # launch occupies; and the floor that the measured device-coherent round
+    # trip puts under its steps.
     if spec.mode in ("rssm", "rssm_actor"):
-        n_rec, layer_dirs, bars = d["T"], 1, 1
+        n_rec, layer_dirs = d["T"], 1
     else:
         n_rec = int(lengths.max()) if lengths is not None else spec.T
         layer_dirs = spec.num_layers * (2 if spec.bidirectional else 1)
-        if dom["kernel"] == "scan_wave":
-            bars = 0
-        else:
-            members = gss.rnn_plan_info(desc, lengths)["members"]
-            bars = 0 if (members == 1 and spec.mode != "lstmp") else (2 if spec.mode == "lstmp" else 1)
-    roofline["recurrence_steps"] = n_rec
-    roofline["us_per_step"] = dom["avg_us"] / n_rec
-    roofline["barriers_per_step"] = bars
-
+    plan = gss.rnn_plan_info(desc, lengths)
+    if plan["kernel"] == 4:
+        bars, occ = 0, min(256, plan["workgroups"])
+    else:
+        members = plan["members"]
+        lstmp = spec.mode == "lstmp"
+        bars = 0 if (members == 1 and not lstmp) else (2 if lstmp else 1)
+        occ = min(256, plan["workgroups"])
+    if dom["kernel"] == "gemm_xw":
+        occ = 256
+    ob = onchip_bytes(spec, d, plan) if dom["kernel"] in ("scan", "rssm", "scan_wave") else 0
+    t_roof = max(dom["flops"] / (peak * 1e12), ob / (PEAK_LDS_GBS * 1e9), dom["bytes"] / (PEAK_HBM_GBS * 1e9))
+    roofline.update({
+        "recurrence_steps": n_rec, "us_per_step": dom["avg_us"] / n_rec, "barriers_per_step": bars,
+        "onchip_bytes": ob, "t_roof_us": t_roof * 1e6, "roof_frac": t_roof * 1e6 / dom["avg_us"],
+        "occupied_cus": occ, "frac_occupied_cus": achieved / (peak * occ / 256.0),
+        "exchange_roundtrip_us": rt_us,
+        "barrier_floor_us": n_rec * bars * rt_us if rt_us is not None else None,
+    })
     ms_per_step = elapsed / K * 1e3
     value = tokens / (elapsed / K)
     ctx = PAGES_CONTEXT.get(name)
     vs = (value / max(ctx.values())) if ctx else None
-    rec = {
-        "metric": METRIC, "value": value, "unit": UNIT,
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": vs,
-        "dtype": spec.dtype, "data": "synthetic", "config": config,
-        "roofline": roofline, "kernels": kernels,
-        "cell_steps_per_s": value * layer_dirs,
-    }
+    rec = {"config": pr["config"], "value": value, "ms_per_step": ms_per_step,
+           "median_kernel_span_ms": float(np.median(step_ms)), "min_kernel_span_ms": float(np.min(step_ms)),
+           "dtype": spec.dtype, "vs_baseline": vs, "roofline": roofline, "kernels": kernels,
+           "cell_steps_per_s": value * layer_dirs}
     if ctx:
         rec["pages_context"] = {k: v for k, v in ctx.items()}
-    if not args.no_cpu:
+    if with_cpu:
         rec["cpu_baseline"] = cpu_baseline_any(spec, d, args.cpu_seconds)
+    del pr
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the recurrence shards by batch with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.train:
+        train_main(args)
+        return
+    import torch
+
+    import gru_sequence_scan_amd as gss
+    import synth
+
+    torch.cuda.set_device(torch.device("cuda:0"))
+    try:
+        rt_us = gss.rnn_exchange_roundtrip_ns(2000) / 1e3
+    except gss.RnnError:
+        rt_us = None
+    wl = args.workload
+    head = synth.ORDER[int(wl) - 1] if wl.isdigit() else (HEADLINE if wl == "all" else wl)
+    others = [n for n in synth.ORDER if n != head] if wl == "all" else []
+    print(f"bench: {head}", file=sys.stderr, flush=True)
+    h = measure(head, args, rt_us, not args.no_cpu)
+    rec = {
+        "metric": METRIC, "value": h["value"], "unit": UNIT,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": h["vs_baseline"],
+        "dtype": h["dtype"], "data": "synthetic", "config": h["config"],
+        "roofline": h["roofline"], "kernels": h["kernels"],
+        "median_kernel_span_ms": h["median_kernel_span_ms"], "min_kernel_span_ms": h["min_kernel_span_ms"],
+        "cell_steps_per_s": h["cell_steps_per_s"],
+    }
+    if "pages_context" in h:
+        rec["pages_context"] = h["pages_context"]
+    if "cpu_baseline" in h:
+        rec["cpu_baseline"] = h["cpu_baseline"]
+    if others:
+        per = {}
+        for n in synth.ORDER:
+            if n == head:
+                per[n] = {k: v for k, v in h.items()}
+                continue
+            print(f"bench: {n}", file=sys.stderr, flush=True)
+            per[n] = measure(n, args, rt_us, not args.no_cpu)
+            torch.cuda.empty_cache()
+        rec["configs"] = per
     print(json.dumps(rec), flush=True)
 
 

@@ -130,6 +130,9 @@ def lib():
         L.rnn_backward.argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(RnnWeights), ctypes.POINTER(RnnIO),
                                    ctypes.POINTER(RnnGrads), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]
+        L.rnn_exchange_roundtrip_ns.restype = ctypes.c_int
+        L.rnn_exchange_roundtrip_ns.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                                ctypes.POINTER(ctypes.c_double)]
         if L.rnn_abi_version() != RNN_ABI_VERSION:
             raise RuntimeError("native library ABI version mismatch")
         _lib = L
@@ -148,15 +151,21 @@ def rnn_strerror(status):
     return lib().rnn_strerror(int(status)).decode()
 
 
-def _len_ptr(lengths):
+def _len_ptr(lengths, B):
+    """A C int32 array of the B sequence lengths (None stays None). The C
+    side reads exactly B ints, so a list of any other length is refused here
+    instead of being read past its end."""
     if lengths is None:
         return None, None
-    arr = (ctypes.c_int32 * len(lengths))(*[int(v) for v in lengths])
+    vals = [int(v) for v in lengths]
+    if len(vals) != int(B):
+        raise ValueError(f"lengths: {len(vals)} values for a batch of {int(B)} rows")
+    arr = (ctypes.c_int32 * len(vals))(*vals)
     return arr, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
 
 
 def rnn_workspace_bytes(desc, lengths=None):
-    keep, lp = _len_ptr(lengths)
+    keep, lp = _len_ptr(lengths, desc.B)
     n = ctypes.c_size_t(0)
     st = lib().rnn_workspace_bytes(ctypes.byref(desc), lp, ctypes.byref(n))
     if st != 0:
@@ -178,7 +187,7 @@ PLAN_FIELDS = ("kernel", "workgroups", "lds_bytes", "rows", "hidden_per_wg", "me
 def rnn_plan_info(desc, lengths=None, cus=256, xcds=8):
     """The launch shape the library would choose on a device with `cus`
     compute units in `xcds` XCDs (host only), as a dict of PLAN_FIELDS."""
-    keep, lp = _len_ptr(lengths)
+    keep, lp = _len_ptr(lengths, desc.B)
     info = (ctypes.c_int * len(PLAN_FIELDS))()
     st = lib().rnn_plan_info(ctypes.byref(desc), lp, int(cus), int(xcds), info, len(PLAN_FIELDS))
     if st != 0:
@@ -187,6 +196,8 @@ def rnn_plan_info(desc, lengths=None, cus=256, xcds=8):
 
 
 def rnn_read_status(workspace_ptr, stream_ptr):
+    """Synchronise the stream and return the device status word of the last
+    call that used this workspace (0, or RNN_E_TIMEOUT = -9)."""
     v = ctypes.c_int(0)
     st = lib().rnn_read_status(ctypes.c_void_p(workspace_ptr), ctypes.c_void_p(stream_ptr), ctypes.byref(v))
     if st != 0:
@@ -196,6 +207,18 @@ def rnn_read_status(workspace_ptr, stream_ptr):
 
 def rnn_device_check():
     return lib().rnn_device_check()
+
+
+def rnn_exchange_roundtrip_ns(iters=2000, device="cuda:0"):
+    """Mean nanoseconds of one device-coherent round trip between two
+    workgroups on different XCDs (C rnn_exchange_roundtrip_ns)."""
+    buf = torch.empty(1024, dtype=torch.uint8, device=device)
+    v = ctypes.c_double(0.0)
+    st = lib().rnn_exchange_roundtrip_ns(buf.data_ptr(), buf.numel(), int(iters), _stream_ptr(torch.device(device)),
+                                         ctypes.byref(v))
+    if st != 0:
+        raise RnnError(st, "rnn_exchange_roundtrip_ns")
+    return v.value
 
 
 # ---------------------------------------------------------------------------
@@ -243,20 +266,31 @@ def _check(t, name, shape, dtype, device):
     return _dense(t)
 
 
-def _call(desc, w, io, lengths, device, keep):
+def check_device_status(ws, device, where):
+    """Wait for the stream and raise RnnError when the kernels that used
+    workspace `ws` reported a device-side failure (a step barrier's watchdog:
+    RNN_E_TIMEOUT), whose outputs are invalid."""
+    st = rnn_read_status(ws.data_ptr(), _stream_ptr(device))
+    if st != 0:
+        raise RnnError(st, where + " (device status)")
+
+
+def _call(desc, w, io, lengths, device, keep, check_status):
     ws_bytes = rnn_workspace_bytes(desc, lengths)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device)
     keep.append(ws)
     st = rnn_forward_raw(desc, w, io, ws.data_ptr(), ws.numel(), _stream_ptr(device))
     if st != 0:
         raise RnnError(st, "rnn_forward")
+    if check_status:
+        check_device_status(ws, device, "rnn_forward")
     return ws
 
 
 def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padded",
                 num_layers=1, bidirectional=False, proj_size=0, hidden_size=None, y_out=None,
                 tile_batch=0, tile_hidden=0, placement=0, weights=0, cell_clip=None, proj_clip=None,
-                return_workspace=False, _train=False):
+                return_workspace=False, check_status=True, _train=False):
     """Forward of an LSTM / GRU / LSTMP stack on the current HIP stream.
 
     x: padded [T, B, F] or packed [N_tok, F] (float32 or bfloat16, on a GPU).
@@ -266,11 +300,20 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     masks rows, which are then never written past their length).
     cell_clip: c (clamp to [-c, c]) or (lo, hi), clamps the updated LSTM cell
     state; proj_clip: p, clamps the LSTMP projected output to [-p, p].
+    check_status (default True): wait for the stream after the call and
+    raise RnnError if the device reported a failure (a persistent group whose
+    workgroups were not all resident ends with RNN_E_TIMEOUT and leaves the
+    outputs invalid). With False the call stays asynchronous and the caller
+    checks rnn_read_status on the returned workspace (return_workspace=True).
     Returns (y, h_n, c_n) with c_n None for GRU.
     """
     mode = mode.lower()
     if mode not in ("lstm", "gru", "lstmp"):
         raise ValueError(f"mode {mode!r}")
+    if lengths is not None:
+        lengths = [int(v) for v in (lengths.tolist() if hasattr(lengths, "tolist") else lengths)]
+        if layout == "padded" and x.dim() == 3 and len(lengths) != x.shape[1]:
+            raise ValueError(f"lengths: {len(lengths)} values for a batch of {x.shape[1]} rows")
     dtype, device = x.dtype, x.device
     if dtype not in DTYPES:
         raise ValueError(f"dtype {dtype} not supported (float32, bfloat16)")
@@ -284,8 +327,8 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     H = params[0]["w_hh"].shape[0] // gates if hidden_size is None else hidden_size
     K = proj_size if mode == "lstmp" else H
     F = x.shape[-1]
-    if lengths is not None:
-        lengths = [int(v) for v in (lengths.tolist() if hasattr(lengths, "tolist") else lengths)]
+    if layout not in ("padded", "packed"):
+        raise ValueError(f"layout {layout!r}")
     if layout == "packed":
         if lengths is None:
             raise ValueError("packed layout needs lengths")
@@ -295,7 +338,11 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
         x = _check(x, "x", (n_tok, F), dtype, device)
         y_shape = (n_tok, D * K)
     else:
+        if x.dim() != 3:
+            raise ValueError(f"x: padded layout needs [T, B, F], got shape {tuple(x.shape)}")
         T, B = x.shape[0], x.shape[1]
+        if lengths is not None and len(lengths) != B:
+            raise ValueError(f"lengths: {len(lengths)} values for a batch of {B} rows")
         x = _check(x, "x", (T, B, F), dtype, device)
         y_shape = (T, B, D * K)
     has_bias = params[0].get("b_ih") is not None
@@ -342,7 +389,7 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
         desc.proj_clip = float(proj_clip)
     io = RnnIO()
     io.x = _ptr(x)
-    keep_len, io.lengths_host = _len_ptr(lengths)
+    keep_len, io.lengths_host = _len_ptr(lengths, B)
     io.h0, io.c0 = _ptr(h0), _ptr(c0)
     io.y, io.h_n, io.c_n = _ptr(y), _ptr(h_n), _ptr(c_n)
     out = (y, h_n, c_n)
@@ -358,9 +405,11 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
                                      reserve.numel(), ws.data_ptr(), ws.numel(), _stream_ptr(device))
         if st != 0:
             raise RnnError(st, "rnn_forward_train")
+        if check_status:
+            check_device_status(ws, device, "rnn_forward_train")
         ctx = TrainContext(desc, w, io, keep + [keep_len, y, h_n, c_n], reserve, lengths, mode, params, D, H, K)
         return out, ctx
-    ws = _call(desc, w, io, lengths, device, keep)
+    ws = _call(desc, w, io, lengths, device, keep, check_status)
     return (out, ws) if return_workspace else out
 
 
@@ -379,12 +428,12 @@ def rnn_forward_train(mode, x, params, **kw):
     return rnn_forward(mode, x, params, _train=True, **kw)
 
 
-def rnn_backward(ctx, dy, dh_n=None, dc_n=None):
+def rnn_backward(ctx, dy, dh_n=None, dc_n=None, check_status=True):
     """Gradients through the forward recorded in ctx, given dy (shape of y)
     and optionally dh_n, dc_n (shape of h_n, c_n). Returns (dx, dh0, dc0,
     grads) with grads a list over layer * D + direction of dicts dw_ih,
     dw_hh, db_ih, db_hh (bias entries only with biases) and dw_hr (LSTMP);
-    dc0 None for GRU."""
+    dc0 None for GRU. check_status as for rnn_forward."""
     y = ctx.keep[-3]
     device, dtype = y.device, y.dtype
     desc, io = ctx.desc, ctx.io
@@ -421,12 +470,14 @@ def rnn_backward(ctx, dy, dh_n=None, dc_n=None):
                             _stream_ptr(device))
     if st != 0:
         raise RnnError(st, "rnn_backward")
+    if check_status:
+        check_device_status(ws, device, "rnn_backward")
     ctx.bwd_workspace = ws
     return dx, dh0, dc0, grads
 
 
 def _rssm(mode, actions, eps, weights, actor, A, state0, belief0, scale_lb, tile_batch, tile_hidden,
-          placement):
+          placement, check_status):
     """Marshal one RSSM unroll (given actions, or an actor) into the C ABI."""
     dtype, device = eps.dtype, eps.device
     if dtype != torch.float32:
@@ -474,33 +525,35 @@ def _rssm(mode, actions, eps, weights, actor, A, state0, belief0, scale_lb, tile
     io.x, io.noise, io.s0, io.h0 = _ptr(actions), _ptr(eps), _ptr(state0), _ptr(belief0)
     io.means, io.stds, io.states, io.beliefs = _ptr(means), _ptr(stds), _ptr(states), _ptr(beliefs)
     io.actions = _ptr(acts)
-    ws = _call(desc, w, io, None, device, keep)
+    ws = _call(desc, w, io, None, device, keep, check_status)
     out = (means, stds, states, beliefs) + ((acts,) if actor is not None else ())
     return out, ws
 
 
 def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale_lb=0.1,
-                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False):
+                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False, check_status=True):
     """RSSM prior unrolled over actions [B, T, A] with injected eps [B, T, S].
 
     weights: dict with w_as [E, S + A], b_as, w_ih [3Hb, E], w_hh [3Hb, Hb],
     b_ih, b_hh, w_1 [E, Hb], b_1, w_2 [2S, E], b_2 (float32, on the GPU).
+    check_status as for rnn_forward.
     Returns (means, stds, states, beliefs) stacked on dim 1.
     """
     out, ws = _rssm("rssm", actions, eps, weights, None, actions.shape[2], state0, belief0, scale_lb,
-                    tile_batch, tile_hidden, placement)
+                    tile_batch, tile_hidden, placement, check_status)
     return (out, ws) if return_workspace else out
 
 
 def rssm_actor_unroll(eps, weights, actor, state0=None, belief0=None, *, scale_lb=0.1,
-                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False):
+                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False, check_status=True):
     """RSSM prior unrolled for H = eps.shape[1] steps with the actor choosing
     each action from the previous state and belief.
 
     weights as for rssm_prior_unroll; actor: dict with w_a1 [Ea, S + Hb],
     b_a1 [Ea], w_a2 [A, Ea], b_a2 [A] (float32, on the GPU).
+    check_status as for rnn_forward.
     Returns (means, stds, states, beliefs, actions) stacked on dim 1.
     """
     out, ws = _rssm("rssm_actor", None, eps, weights, actor, actor["w_a2"].shape[0], state0, belief0,
-                    scale_lb, tile_batch, tile_hidden, placement)
+                    scale_lb, tile_batch, tile_hidden, placement, check_status)
     return (out, ws) if return_workspace else out

@@ -211,5 +211,9 @@ hipError_t launch_write_ints(int* dst, const int* src, int n, hipStream_t stream
 
 // Zero-fill of small workspace regions (counters, status word).
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+// Device-coherent round trip between two workgroups on different XCDs:
+// buf >= 512 bytes zeroed, out[0] = 100 MHz ticks for `iters` round trips,
+// out[1], out[2] nonzero when a bounded wait ran out.
+hipError_t launch_exchange_probe(void* buf, int iters, unsigned long long* out, hipStream_t stream);
 
 }  // namespace rnnk

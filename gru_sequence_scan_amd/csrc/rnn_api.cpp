@@ -1102,6 +1102,26 @@ int rnn_device_check(void) {
   return current_device_info(&info);
 }
 
+int rnn_exchange_roundtrip_ns(void* buffer, size_t bytes, int iters, void* stream, double* ns_per_round_trip) {
+  if (!buffer || !ns_per_round_trip) return RNN_E_NULL;
+  if (bytes < 1024 || iters < 1 || iters > 100000) return RNN_E_SHAPE;
+  if (!aligned(buffer, 256)) return RNN_E_ALIGN;
+  DeviceInfo info;
+  int rc = current_device_info(&info);
+  if (rc != RNN_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* b = static_cast<char*>(buffer);
+  unsigned long long* out = reinterpret_cast<unsigned long long*>(b + 512);
+  if ((rc = hip_status(launch_fill_zero(b, 1024, st))) != RNN_OK) return rc;
+  if ((rc = hip_status(launch_exchange_probe(b, iters, out, st))) != RNN_OK) return rc;
+  if (hipStreamSynchronize(st) != hipSuccess) return RNN_E_HIP;
+  unsigned long long h[3] = {0, 0, 0};
+  if (hipMemcpy(h, out, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return RNN_E_HIP;
+  if (h[1] || h[2]) return RNN_E_TIMEOUT;
+  *ns_per_round_trip = (double)h[0] * 10.0 / iters;  // 100 MHz real-time clock
+  return RNN_OK;
+}
+
 int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* workspace,
                          size_t ws_bytes, void* stream, void* const* events, int n_events, int* kinds,
                          int* n_kernels) {

@@ -1,6 +1,9 @@
 // Small stream-ordered helpers: zero-fill of workspace words and copies of
 // host int arrays (lengths, packed offsets) into the workspace through
-// kernel arguments, so nothing has to stay alive on the host after a call.
+// kernel arguments, so nothing has to stay alive on the host after a call;
+// and a probe of the device-coherent round trip that bounds every step of
+// the persistent kernels.
+#include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace rnnk {
@@ -20,7 +23,47 @@ __global__ void write_ints_kernel(int* dst, IntChunk c, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = c.v[i];
 }
 
+// Two workgroups (ids 0 and 1, which the dispatcher places on different
+// XCDs) pass a counter back and forth through two words 256 bytes apart,
+// with the same device-scope stores and loads the persistent kernels use
+// for their exchange. Word 0 carries A's value, word 64 B's echo. Every
+// wait is bounded by `spin` polls; a wait that runs out sets out[1].
+__global__ void exchange_probe_kernel(unsigned* buf, int iters, unsigned spin, unsigned long long* out) {
+  if (threadIdx.x != 0 || blockIdx.x > 1) return;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(buf, 512);
+  const bool a_side = blockIdx.x == 0;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  unsigned failed = 0;
+  for (int i = 1; i <= iters && !failed; ++i) {
+    if (a_side) {
+      coh_store4(rs, 0, (unsigned)i);
+      unsigned n = 0;
+      while (coh_load4(rs, 256) != (unsigned)i)
+        if (++n > spin) { failed = 1; break; }
+    } else {
+      unsigned n = 0;
+      while (coh_load4(rs, 0) != (unsigned)i)
+        if (++n > spin) { failed = 1; break; }
+      if (!failed) coh_store4(rs, 256, (unsigned)i);
+    }
+  }
+  wait_all_mem();
+  const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+  if (a_side) {
+    out[0] = t1 - t0;
+    out[1] = failed;
+  } else {
+    out[2] = failed;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_exchange_probe(void* buf, int iters, unsigned long long* out, hipStream_t stream) {
+  hipLaunchKernelGGL(exchange_probe_kernel, dim3(2), dim3(64), 0, stream, reinterpret_cast<unsigned*>(buf), iters,
+                     2000000u, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
   const size_t n = bytes / 4;

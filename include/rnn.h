@@ -41,9 +41,20 @@
  *     review: do the layout work before the loop). Nothing is enqueued when
  *     a call returns an error.
  *   - The library keeps no mutable global state and reads no environment
- *     variables (same PR: a module-global mode flag leaked across threads);
- *     concurrent calls on different streams with different workspaces are
- *     safe. Two calls that share a workspace must be stream-ordered.
+ *     variables (same PR: a module-global mode flag leaked across threads),
+ *     so calls may be made from several host threads. Two calls that share
+ *     a workspace must be stream-ordered.
+ *   - Device residency. The recurrence kernels (the scan, the backward scan
+ *     and the RSSM kernel) are persistent: the workgroups of one group wait
+ *     for each other every step, so all of them must be resident at once.
+ *     The launch is sized to the device's compute units assuming nothing
+ *     else runs on it. If other kernels (another call on another stream,
+ *     or any other work) occupy compute units during such a launch, a group
+ *     can be left partly resident; its members then give up after a bounded
+ *     wait (about 2 s) and the call reports RNN_E_TIMEOUT through
+ *     rnn_read_status, with invalid outputs. Calls never hang, but they
+ *     succeed only when these kernels have the device to themselves:
+ *     serialise calls (one stream, or events) rather than overlapping them.
  *   - Floating-point results are deterministic: the same inputs give the
  *     same bits (no floating-point atomics).
  */
@@ -349,6 +360,19 @@ int rnn_backward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io
 
 /* RNN_OK when the current device is a gfx950 GPU; RNN_E_DEVICE otherwise. */
 int rnn_device_check(void);
+
+/* Measurement helper: the time one device-coherent round trip takes between
+ * two workgroups on different XCDs of the current device, using the same
+ * device-scope stores and loads the persistent kernels exchange their state
+ * with every step (a step that waits on another compute unit's result pays
+ * at least one such one-way trip; a counter barrier pays about a round
+ * trip). `buffer` is caller-owned device memory of at least 1024 bytes,
+ * 256-byte aligned, whose contents are overwritten; iters in [1, 100000].
+ * Enqueues on `stream`, synchronises it and writes the mean nanoseconds per
+ * round trip. Returns RNN_OK, RNN_E_NULL, RNN_E_SHAPE, RNN_E_ALIGN,
+ * RNN_E_DEVICE, RNN_E_HIP, or RNN_E_TIMEOUT when a bounded wait ran out
+ * (the two workgroups were not resident together). */
+int rnn_exchange_roundtrip_ns(void* buffer, size_t bytes, int iters, void* stream, double* ns_per_round_trip);
 
 #ifdef __cplusplus
 }

@@ -63,25 +63,3 @@ def run_rssm_actor(d, **kw):
                                 to_dev(d["h0"], torch.float32), **kw)
     torch.cuda.synchronize()
     return [t.cpu().numpy().astype(np.float64) for t in out]
-
-
-def subset_rows(d, rows):
-    """The same problem restricted to batch rows `rows` (rows are independent)."""
-    rows = np.asarray(rows)
-    e = dict(d)
-    e["B"] = len(rows)
-    L = d["lengths"]
-    e["lengths"] = None if L is None else np.ascontiguousarray(L[rows])
-    if d["layout"] == "packed":
-        import synth
-        xp = d["x_padded"][:, rows]
-        e["x_padded"] = xp
-        T = int(np.max(e["lengths"]))
-        bs, off = synth.packed_layout(e["lengths"])
-        e["x"] = np.concatenate([xp[t, :bs[t]] for t in range(T)], axis=0)
-    else:
-        e["x"] = d["x"][:, rows]
-        e["x_padded"] = e["x"]
-    e["h0"] = None if d["h0"] is None else d["h0"][:, rows]
-    e["c0"] = None if d.get("c0") is None else d["c0"][:, rows]
-    return e

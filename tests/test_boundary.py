@@ -98,7 +98,7 @@ def _desc(**kw):
 
 
 def _ws(desc, lengths=None):
-    keep, lp = gss.binding._len_ptr(lengths)
+    keep, lp = gss.binding._len_ptr(lengths, desc.B if desc is not None else 0)
     n = ctypes.c_size_t(0)
     return gss.lib().rnn_workspace_bytes(ctypes.byref(desc) if desc is not None else None, lp, ctypes.byref(n)), n.value
 
@@ -295,3 +295,26 @@ def test_reserve_holds_gates_and_inner_layer_outputs(lib):
     n2 = ctypes.c_size_t(0)
     assert lib.rnn_reserve_bytes(ctypes.byref(_desc(num_layers=2)), None, ctypes.byref(n2)) == OK
     assert n2.value >= 2 * n1.value + 8 * 4 * 32 * 4   # the lower layer's output is kept too
+
+
+@pytest.mark.parametrize("n", [3, 5])
+def test_lengths_count_must_match_batch(lib, n):
+    """The C side reads exactly B lengths; a shorter or longer host list is
+    refused before any call (a short list would be read past its end)."""
+    d = _desc(B=4)
+    with pytest.raises(ValueError, match="lengths"):
+        gss.rnn_workspace_bytes(d, [2] * n)
+    with pytest.raises(ValueError, match="lengths"):
+        gss.rnn_plan_info(d, [2] * n)
+    assert gss.rnn_workspace_bytes(d, [2] * 4) > 0
+
+
+@pytest.mark.parametrize("n", [3, 5])
+def test_lengths_count_checked_by_forward(lib, n):
+    """rnn_forward refuses a length list whose size is not the batch size,
+    for the padded layout too, before touching a device."""
+    import torch
+    x = torch.zeros(6, 4, 8)
+    params = [{"w_ih": torch.zeros(64, 8), "w_hh": torch.zeros(64, 16)}]
+    with pytest.raises(ValueError, match="lengths"):
+        gss.rnn_forward("lstm", x, params, lengths=[2] * n)

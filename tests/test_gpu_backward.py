@@ -115,3 +115,39 @@ def test_backward_deterministic():
         outs.append([dx.cpu(), dh0.cpu(), grads[0]["dw_hh"].cpu(), grads[3]["db_ih"].cpu()])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(600)
+def test_backward_full_bilstm_varlen_b64():
+    """The var-len stack's training step at full size (B = 64, packed,
+    N_tok = 19,334, 498 steps, two bidirectional layers of 512) in the launch
+    plan the training benchmark runs: dx and dh0 / dc0 on every row and every
+    weight and bias gradient whole, against the oracle's BPTT."""
+    name = "bilstm_varlen_b64"
+    d = synth.make_inputs(name)
+    log(f"[gpu] backward full-size {name}")
+    rng = np.random.default_rng(2024)
+    L, B, H = d["lengths"], d["B"], d["hidden_size"]
+    dy = rng.normal(size=(d["x"].shape[0], 2 * H)).astype(np.float32)
+    dh_n = rng.normal(size=(4, B, H)).astype(np.float32)
+    dc_n = rng.normal(size=(4, B, H)).astype(np.float32)
+    f = lambda a: to_dev(a, torch.float32)
+    params = [{k: f(v) for k, v in p.items() if v is not None} for p in d["params"]]
+    (y, hn, cn), ctx = gss.rnn_forward_train("lstm", f(d["x"]), params, lengths=L, layout="packed",
+                                             num_layers=2, bidirectional=True)
+    dx, dh0, dc0, grads = gss.rnn_backward(ctx, f(dy), f(dh_n), f(dc_n))
+    torch.cuda.synchronize()
+    g = lambda t: t.cpu().numpy().astype(np.float64)
+    yr, hnr, cnr = oracle.rnn_forward("lstm", d["x"], d["params"], lengths=L, num_layers=2, bidirectional=True,
+                                      layout="packed")
+    assert_close(g(y), yr, "f32", name + " y")
+    assert_close(g(hn), hnr, "f32", name + " h_n")
+    assert_close(g(cn), cnr, "f32", name + " c_n")
+    ref = oracle.rnn_backward("lstm", d["x"], d["params"], dy, dh_n=dh_n, dc_n=dc_n, lengths=L, num_layers=2,
+                              bidirectional=True, layout="packed")
+    assert_grad_close(g(dx), ref[0], name + " dx")
+    assert_grad_close(g(dh0), ref[1], name + " dh0")
+    assert_grad_close(g(dc0), ref[2], name + " dc0")
+    for i, (gg, rr) in enumerate(zip(grads, ref[3])):
+        for k in ("w_ih", "w_hh", "b_ih", "b_hh"):
+            assert_grad_close(g(gg["d" + k]), rr[k], f"{name} [{i}] d{k}")
