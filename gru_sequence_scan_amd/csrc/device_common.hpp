@@ -39,6 +39,18 @@ __device__ __forceinline__ u32x4 coh_load16(__amdgpu_buffer_rsrc_t rs, uint32_t 
 __device__ __forceinline__ uint32_t coh_load4(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)byte_off, 0, kCohPolicy);
 }
+// Polling reads: the same device-scope loads behind a compiler memory
+// barrier, so a load repeated in a spin loop is issued every iteration
+// (without the barrier the compiler treats the buffer load as a pure read
+// and hoists it out of the loop as an invariant).
+__device__ __forceinline__ u32x4 coh_poll16(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+  asm volatile("" ::: "memory");
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)byte_off, 0, kCohPolicy);
+}
+__device__ __forceinline__ uint32_t coh_poll4(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+  asm volatile("" ::: "memory");
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)byte_off, 0, kCohPolicy);
+}
 __device__ __forceinline__ void coh_store16(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)byte_off, 0, kCohPolicy);
 }

@@ -38,11 +38,11 @@ __global__ void exchange_probe_kernel(unsigned* buf, int iters, unsigned spin, u
     if (a_side) {
       coh_store4(rs, 0, (unsigned)i);
       unsigned n = 0;
-      while (coh_load4(rs, 256) != (unsigned)i)
+      while (coh_poll4(rs, 256) != (unsigned)i)
         if (++n > spin) { failed = 1; break; }
     } else {
       unsigned n = 0;
-      while (coh_load4(rs, 0) != (unsigned)i)
+      while (coh_poll4(rs, 0) != (unsigned)i)
         if (++n > spin) { failed = 1; break; }
       if (!failed) coh_store4(rs, 256, (unsigned)i);
     }
