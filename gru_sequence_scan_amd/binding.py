@@ -130,6 +130,9 @@ def lib():
         L.rnn_backward.argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(RnnWeights), ctypes.POINTER(RnnIO),
                                    ctypes.POINTER(RnnGrads), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]
+        L.rnn_forward_noalloc.restype = ctypes.c_int
+        L.rnn_forward_noalloc.argtypes = [ctypes.POINTER(RnnDesc), ctypes.POINTER(RnnWeights),
+                                          ctypes.POINTER(RnnIO), ctypes.c_void_p, ctypes.c_void_p]
         L.rnn_exchange_roundtrip_ns.restype = ctypes.c_int
         L.rnn_exchange_roundtrip_ns.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                                 ctypes.POINTER(ctypes.c_double)]
@@ -275,7 +278,27 @@ def check_device_status(ws, device, where):
         raise RnnError(st, where + " (device status)")
 
 
-def _call(desc, w, io, lengths, device, keep, check_status):
+RNN_NOALLOC_MAX_WORKSPACE = 32 << 20
+
+
+def _call_noalloc(desc, w, io, device, check_status):
+    """C rnn_forward_noalloc: the library's own workspace, the device status
+    copied into a one-int tensor."""
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    st = lib().rnn_forward_noalloc(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(io), _stream_ptr(device),
+                                   ctypes.c_void_p(status.data_ptr()))
+    if st != 0:
+        raise RnnError(st, "rnn_forward_noalloc")
+    if check_status:
+        v = int(status.item())
+        if v != 0:
+            raise RnnError(v, "rnn_forward_noalloc (device status)")
+    return status
+
+
+def _call(desc, w, io, lengths, device, keep, check_status, noalloc=False):
+    if noalloc:
+        return _call_noalloc(desc, w, io, device, check_status)
     ws_bytes = rnn_workspace_bytes(desc, lengths)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device)
     keep.append(ws)
@@ -290,7 +313,7 @@ def _call(desc, w, io, lengths, device, keep, check_status):
 def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padded",
                 num_layers=1, bidirectional=False, proj_size=0, hidden_size=None, y_out=None,
                 tile_batch=0, tile_hidden=0, placement=0, weights=0, cell_clip=None, proj_clip=None,
-                return_workspace=False, check_status=True, _train=False):
+                return_workspace=False, check_status=True, noalloc=False, _train=False):
     """Forward of an LSTM / GRU / LSTMP stack on the current HIP stream.
 
     x: padded [T, B, F] or packed [N_tok, F] (float32 or bfloat16, on a GPU).
@@ -305,6 +328,9 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     workgroups were not all resident ends with RNN_E_TIMEOUT and leaves the
     outputs invalid). With False the call stays asynchronous and the caller
     checks rnn_read_status on the returned workspace (return_workspace=True).
+    noalloc: call rnn_forward_noalloc (the library's own workspace, for
+    problems up to RNN_NOALLOC_MAX_WORKSPACE bytes); the returned
+    "workspace" is then the one-int device status tensor.
     Returns (y, h_n, c_n) with c_n None for GRU.
     """
     mode = mode.lower()
@@ -409,7 +435,7 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
             check_device_status(ws, device, "rnn_forward_train")
         ctx = TrainContext(desc, w, io, keep + [keep_len, y, h_n, c_n], reserve, lengths, mode, params, D, H, K)
         return out, ctx
-    ws = _call(desc, w, io, lengths, device, keep, check_status)
+    ws = _call(desc, w, io, lengths, device, keep, check_status, noalloc)
     return (out, ws) if return_workspace else out
 
 
@@ -477,7 +503,7 @@ def rnn_backward(ctx, dy, dh_n=None, dc_n=None, check_status=True):
 
 
 def _rssm(mode, actions, eps, weights, actor, A, state0, belief0, scale_lb, tile_batch, tile_hidden,
-          placement, check_status):
+          placement, check_status, noalloc=False):
     """Marshal one RSSM unroll (given actions, or an actor) into the C ABI."""
     dtype, device = eps.dtype, eps.device
     if dtype != torch.float32:
@@ -525,22 +551,23 @@ def _rssm(mode, actions, eps, weights, actor, A, state0, belief0, scale_lb, tile
     io.x, io.noise, io.s0, io.h0 = _ptr(actions), _ptr(eps), _ptr(state0), _ptr(belief0)
     io.means, io.stds, io.states, io.beliefs = _ptr(means), _ptr(stds), _ptr(states), _ptr(beliefs)
     io.actions = _ptr(acts)
-    ws = _call(desc, w, io, None, device, keep, check_status)
+    ws = _call(desc, w, io, None, device, keep, check_status, noalloc)
     out = (means, stds, states, beliefs) + ((acts,) if actor is not None else ())
     return out, ws
 
 
 def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale_lb=0.1,
-                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False, check_status=True):
+                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False, check_status=True,
+                      noalloc=False):
     """RSSM prior unrolled over actions [B, T, A] with injected eps [B, T, S].
 
     weights: dict with w_as [E, S + A], b_as, w_ih [3Hb, E], w_hh [3Hb, Hb],
     b_ih, b_hh, w_1 [E, Hb], b_1, w_2 [2S, E], b_2 (float32, on the GPU).
-    check_status as for rnn_forward.
+    check_status and noalloc as for rnn_forward.
     Returns (means, stds, states, beliefs) stacked on dim 1.
     """
     out, ws = _rssm("rssm", actions, eps, weights, None, actions.shape[2], state0, belief0, scale_lb,
-                    tile_batch, tile_hidden, placement, check_status)
+                    tile_batch, tile_hidden, placement, check_status, noalloc)
     return (out, ws) if return_workspace else out
 
 

@@ -211,6 +211,8 @@ hipError_t launch_write_ints(int* dst, const int* src, int n, hipStream_t stream
 
 // Zero-fill of small workspace regions (counters, status word).
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+// *dst = *src (one int, stream-ordered).
+hipError_t launch_copy_int(int* dst, const int* src, hipStream_t stream);
 // Device-coherent round trip between two workgroups on different XCDs:
 // buf >= 512 bytes zeroed, out[0] = 100 MHz ticks for `iters` round trips,
 // out[1], out[2] nonzero when a bounded wait ran out.

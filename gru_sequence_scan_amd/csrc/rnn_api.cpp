@@ -975,6 +975,37 @@ int backward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, const R
   return RNN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Library-owned workspace of rnn_forward_noalloc. Each device the library
+// runs on holds its own copy of the array from the code object's load until
+// the process ends. In host code `scratch` names a host-side stand-in, not
+// device memory: only the address hipGetSymbolAddress returns for the
+// current device may be handed to kernels.
+// ---------------------------------------------------------------------------
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[RNN_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RNN_E_DEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RNN_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RNN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1153,6 +1184,32 @@ int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const R
 int rnn_forward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* workspace,
                 size_t ws_bytes, void* stream) {
   return rnn_forward_profiled(desc, weights, io, workspace, ws_bytes, stream, nullptr, 0, nullptr, nullptr);
+}
+
+int rnn_forward_noalloc(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* stream,
+                        int32_t* device_status) {
+  int rc = validate_desc(desc);
+  if (rc != RNN_OK) return rc;
+  if (!weights || !io) return RNN_E_NULL;
+  long long n_tok = 0;
+  int t_max = 0;
+  const int32_t* lens = is_rssm(desc->mode) ? nullptr : io->lengths_host;
+  if ((rc = validate_lengths(desc, lens, &n_tok, &t_max)) != RNN_OK) return rc;
+  if (layout_of(desc, n_tok, lens != nullptr).total > (size_t)RNN_NOALLOC_MAX_WORKSPACE) return RNN_E_WORKSPACE;
+  if (device_status && !aligned(device_status, 4)) return RNN_E_ALIGN;
+  DeviceInfo info;
+  if ((rc = current_device_info(&info)) != RNN_OK) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_on_current_device(&ws)) != RNN_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Prof prof;
+  char* w = static_cast<char*>(ws);
+  rc = is_rssm(desc->mode)
+           ? forward_rssm(desc, weights, io, w, RNN_NOALLOC_MAX_WORKSPACE, st, info.cus, info.xcds, prof)
+           : forward_rnn(desc, weights, io, w, RNN_NOALLOC_MAX_WORKSPACE, st, info.cus, info.xcds, prof);
+  if (rc == RNN_OK && device_status)
+    rc = hip_status(launch_copy_int(device_status, reinterpret_cast<const int*>(w), st));
+  return rc;
 }
 
 int rnn_read_status(const void* workspace, void* stream, int* device_status) {

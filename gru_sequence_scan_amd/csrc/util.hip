@@ -57,7 +57,16 @@ __global__ void exchange_probe_kernel(unsigned* buf, int iters, unsigned spin, u
   }
 }
 
+__global__ void copy_int_kernel(int* dst, const int* src) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
 }  // namespace
+
+hipError_t launch_copy_int(int* dst, const int* src, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_int_kernel, dim3(1), dim3(64), 0, stream, dst, src);
+  return hipGetLastError();
+}
 
 hipError_t launch_exchange_probe(void* buf, int iters, unsigned long long* out, hipStream_t stream) {
   hipLaunchKernelGGL(exchange_probe_kernel, dim3(2), dim3(64), 0, stream, reinterpret_cast<unsigned*>(buf), iters,

@@ -292,6 +292,30 @@ int rnn_workspace_bytes(const RnnDesc* desc, const int32_t* lengths_host, size_t
 int rnn_forward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io,
                 void* workspace, size_t ws_bytes, void* stream);
 
+/* Size of the device array rnn_forward_noalloc uses as its workspace. */
+#define RNN_NOALLOC_MAX_WORKSPACE (32u << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. The same
+ * forward as rnn_forward (same kernels, launch plan, results and errors),
+ * with the workspace taken from a device array the library owns instead of
+ * from the caller: RNN_NOALLOC_MAX_WORKSPACE bytes per device, held from the
+ * library's first use of that device until the process ends. The caller
+ * still passes (and owns) every input and output. The call allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library routine.
+ *   - Problems whose rnn_workspace_bytes exceeds RNN_NOALLOC_MAX_WORKSPACE
+ *     return RNN_E_WORKSPACE before anything is enqueued.
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's contents (what must start at zero is cleared by each
+ *     call): calls on one device must be ordered (one stream, or events);
+ *     calls that overlap in time race and give undefined results.
+ *   - device_status: NULL, or a 4-byte aligned device int that receives the
+ *     call's device status word (RNN_OK or RNN_E_TIMEOUT), in stream order
+ *     after the forward's kernels.
+ * Errors as rnn_forward. */
+int rnn_forward_noalloc(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* stream,
+                        int32_t* device_status);
+
 /* Same as rnn_forward, and additionally brackets each compute kernel it
  * enqueues with caller-created hipEvent_t handles: events[2i] is recorded on
  * `stream` right before the i-th kernel and events[2i + 1] right after it,
