@@ -92,6 +92,8 @@ def parse():
     ap.add_argument("--tile-batch", type=int, default=0)
     ap.add_argument("--tile-hidden", type=int, default=0)
     ap.add_argument("--placement", type=int, default=0, help="0 auto, 1 flat, 2 XCD-aligned groups")
+    ap.add_argument("--weights", type=int, default=0,
+                    help="RnnDesc.weights hint: 0 auto, 1 LDS-resident, 2 register-resident")
     ap.add_argument("--train", action="store_true",
                     help="time a training step (rnn_forward_train + rnn_backward) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -202,7 +204,7 @@ def prepare(name, args):
         if actor:
             (out, ws) = gss.rssm_actor_unroll(eps, w, aw, **hints)
         else:
-            (out, ws) = gss.rssm_prior_unroll(acts, eps, w, **hints)
+            (out, ws) = gss.rssm_prior_unroll(acts, eps, w, weights_hint=args.weights, **hints)
         B, Tn = d["B"], d["T"]
         desc = gss.RnnDesc()
         desc.mode, desc.dtype, desc.layout = gss.MODES[spec.mode], 0, 2
@@ -211,6 +213,7 @@ def prepare(name, args):
         desc.state_dim, desc.action_dim = d["state_dim"], d["action_dim"]
         desc.embed_dim, desc.belief_dim, desc.scale_lb = d["embed_dim"], d["belief_dim"], 0.1
         desc.tile_batch, desc.tile_hidden, desc.placement = args.tile_batch, args.tile_hidden, args.placement
+        desc.weights = args.weights
         wt = gss.RnnWeights()
         wt.w_as, wt.b_as, wt.w_1, wt.b_1, wt.w_2, wt.b_2 = (w[k].data_ptr() for k in
                                                             ("w_as", "b_as", "w_1", "b_1", "w_2", "b_2"))
@@ -234,7 +237,7 @@ def prepare(name, args):
         x = T(d["x"])
         (out, ws) = gss.rnn_forward(spec.mode, x, params, lengths=d["lengths"], layout=spec.layout,
                                     num_layers=spec.num_layers, bidirectional=spec.bidirectional,
-                                    proj_size=spec.proj_size, **hints)
+                                    proj_size=spec.proj_size, weights=args.weights, **hints)
         y, hn, cn = out
         desc = gss.RnnDesc()
         desc.mode = gss.MODES[spec.mode]
@@ -244,6 +247,7 @@ def prepare(name, args):
         desc.input_size, desc.hidden_size, desc.proj_size = spec.input_size, spec.hidden_size, spec.proj_size
         desc.num_layers, desc.bidirectional, desc.has_bias = spec.num_layers, int(spec.bidirectional), 1
         desc.tile_batch, desc.tile_hidden, desc.placement = args.tile_batch, args.tile_hidden, args.placement
+        desc.weights = args.weights
         wt = gss.RnnWeights()
         for i, p in enumerate(params):
             for k, v in p.items():

@@ -503,7 +503,7 @@ def rnn_backward(ctx, dy, dh_n=None, dc_n=None, check_status=True):
 
 
 def _rssm(mode, actions, eps, weights, actor, A, state0, belief0, scale_lb, tile_batch, tile_hidden,
-          placement, check_status, noalloc=False):
+          placement, check_status, noalloc=False, weights_hint=0):
     """Marshal one RSSM unroll (given actions, or an actor) into the C ABI."""
     dtype, device = eps.dtype, eps.device
     if dtype != torch.float32:
@@ -547,6 +547,7 @@ def _rssm(mode, actions, eps, weights, actor, A, state0, belief0, scale_lb, tile
     desc.actor_dim = Ea
     desc.scale_lb = scale_lb
     desc.tile_batch, desc.tile_hidden, desc.placement = tile_batch, tile_hidden, placement
+    desc.weights = weights_hint
     io = RnnIO()
     io.x, io.noise, io.s0, io.h0 = _ptr(actions), _ptr(eps), _ptr(state0), _ptr(belief0)
     io.means, io.stds, io.states, io.beliefs = _ptr(means), _ptr(stds), _ptr(states), _ptr(beliefs)
@@ -558,16 +559,20 @@ def _rssm(mode, actions, eps, weights, actor, A, state0, belief0, scale_lb, tile
 
 def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale_lb=0.1,
                       tile_batch=0, tile_hidden=0, placement=0, return_workspace=False, check_status=True,
-                      noalloc=False):
+                      noalloc=False, weights_hint=0):
     """RSSM prior unrolled over actions [B, T, A] with injected eps [B, T, S].
 
     weights: dict with w_as [E, S + A], b_as, w_ih [3Hb, E], w_hh [3Hb, Hb],
     b_ih, b_hh, w_1 [E, Hb], b_1, w_2 [2S, E], b_2 (float32, on the GPU).
-    check_status and noalloc as for rnn_forward.
+    check_status and noalloc as for rnn_forward. weights_hint (the
+    RnnDesc.weights field): 0 chooses the kernel, 1 the kernel with the GRU
+    input weights in LDS and ten-odd members per group, 2 the kernel with
+    every GRU weight slice in registers and wide members (RNN_E_PLAN when
+    the shape does not fit it).
     Returns (means, stds, states, beliefs) stacked on dim 1.
     """
     out, ws = _rssm("rssm", actions, eps, weights, None, actions.shape[2], state0, belief0, scale_lb,
-                    tile_batch, tile_hidden, placement, check_status, noalloc)
+                    tile_batch, tile_hidden, placement, check_status, noalloc, weights_hint)
     return (out, ws) if return_workspace else out
 
 

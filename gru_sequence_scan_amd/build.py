@@ -16,8 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB_NAME = "librnn_gfx950.so"
-SOURCES = ["gemm_xw.hip", "scan.hip", "scan_wave.hip", "scan_bwd.hip", "gemm_gen.hip", "rssm.hip", "util.hip",
-           "rnn_api.cpp"]
+SOURCES = ["gemm_xw.hip", "scan.hip", "scan_wave.hip", "scan_bwd.hip", "gemm_gen.hip", "rssm.hip", "rssm2.hip",
+           "util.hip", "rnn_api.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

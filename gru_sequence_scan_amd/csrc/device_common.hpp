@@ -168,7 +168,15 @@ __device__ __forceinline__ float fexpm1(float x) {
   return fexp(x) - 1.0f;
 }
 
-__device__ __forceinline__ float felu(float x) { return x > 0.0f ? x : fexpm1(x); }
+// ELU with alpha = 1 without branches: both branches of expm1 are formed and
+// selected (the exp branch overflows harmlessly for large positive x, which
+// takes x itself), so a wave never runs them one after the other.
+__device__ __forceinline__ float felu(float x) {
+  const float p = x * (1.0f + x * (0.5f + x * (0.166666666667f + x * (0.041666666667f + x * 0.008333333333f))));
+  const float q = fexp(x) - 1.0f;
+  const float m = __builtin_fabsf(x) < 0.0625f ? p : q;
+  return x > 0.0f ? x : m;
+}
 
 __device__ __forceinline__ float flog1p_small(float y) {  // 0 <= y <= 1
   if (y < 0.0625f) {

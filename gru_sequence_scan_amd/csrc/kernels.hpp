@@ -191,15 +191,26 @@ struct RssmArgs {
   const float* w_a1; const float* b_a1; const float* w_a2; const float* b_a2;
   float* act_out;
   // exchange (workspace)
-  float* ex_h;   // [2][B][Hbp]   whole h_t, ping-pong on t
-  float* ex_p;   // [2][B][nw][Ep] per-member partial sums of W_1 h_t (columns
-                 // 0..E-1) and, with an actor, of W_a1[:, S:] h_t (from r4(E))
+  float* ex_h;   // kernel 3: [2][B][Hbp] whole h_t, ping-pong on t;
+                 // kernel 3b: [4][B][Hbp] ring of write-once slots
+  float* ex_p;   // kernel 3: [2][B][nw][Ep] per-member partial sums of W_1 h_t
+                 // (columns 0..E-1) and, with an actor, of W_a1[:, S:] h_t
+                 // (from r4(E)); kernel 3b: [4][B][nw][Ep] ring
+  unsigned* xid; // kernel 3b: [ngroups][nw] members' XCC ids (sentinel-filled)
   int Ep, Hbp;
   unsigned* counters;  // [ngroups], 64 bytes apart
   int* status;
 };
 hipError_t launch_rssm(const RssmArgs& a, hipStream_t stream);
 int rssm_lds_bytes(const RssmArgs& a);
+// Kernel 3b: the RSSM prior (no actor) with wide members holding their GRU
+// slices in registers and a ring exchange inside one XCD (gpx > 0 groups per
+// XCD). The rings and xid hold the sentinel 0xFFFFFFFF before the launch.
+bool rssm_reg_fits(const RssmArgs& a);
+int rssm_reg_lds_bytes(const RssmArgs& a);
+int rssm_ring_slots();
+int rssm_reg_max_members();
+hipError_t launch_rssm_reg(const RssmArgs& a, hipStream_t stream);
 int rssm_max_rows();
 constexpr int kRssmMaxMembers = 64;
 int scan_lds_bytes(const ScanArgs& a, int esize);
@@ -211,6 +222,8 @@ hipError_t launch_write_ints(int* dst, const int* src, int n, hipStream_t stream
 
 // Zero-fill of small workspace regions (counters, status word).
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+// Fill with a 32-bit pattern (bytes a multiple of 4).
+hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t value, hipStream_t stream);
 // *dst = *src (one int, stream-ordered).
 hipError_t launch_copy_int(int* dst, const int* src, hipStream_t stream);
 // Device-coherent round trip between two workgroups on different XCDs:

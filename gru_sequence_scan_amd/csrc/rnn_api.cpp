@@ -151,7 +151,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // needs no device)
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t status, counters, ints, gx, inter0, inter1, hx, mx, ex_h, ex_p, gpart, total;
+  size_t status, counters, ints, gx, inter0, inter1, hx, mx, ex_h, ex_p, xid, gpart, total;
   size_t counters_bytes;
   int n_ints;
 };
@@ -190,9 +190,13 @@ WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
   if (is_rssm(d->mode)) {
     w.counters_bytes = (size_t)d->B * kCounterBytes;
     w.counters = take(w.counters_bytes);
+    // exchange buffers sized for either RSSM kernel: ping-pong (kernel 3)
+    // or a ring of write-once slots (kernel 3b), and the members' XCC ids
     const int Hbp = rup(d->belief_dim, 4), Ep = rssm_ex_cols(d);
-    w.ex_h = take((size_t)2 * d->B * Hbp * 4);
-    w.ex_p = take((size_t)2 * d->B * kRssmMaxMembers * Ep * 4);
+    const int slots = std::max(2, rssm_ring_slots());
+    w.xid = take((size_t)d->B * kRssmMaxMembers * 4);
+    w.ex_h = take((size_t)slots * d->B * Hbp * 4);
+    w.ex_p = take((size_t)slots * d->B * kRssmMaxMembers * Ep * 4);
     w.total = o;
     return w;
   }
@@ -393,13 +397,61 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wre
 
 struct RssmPlan {
   int rows, ngroups, nw, h_per, gpx, lds;
+  int reg;  // 1: kernel 3b (GRU slices in registers, ring exchange inside an XCD)
 };
 
 // Grid of an RSSM plan: with XCD-aligned groups every XCD gets gpx whole
 // groups (the last XCDs may hold padding slots).
 int rssm_grid(const RssmPlan& p, int xcds) { return p.gpx > 0 ? xcds * p.gpx * p.nw : p.ngroups * p.nw; }
 
+// Kernel 3b (no actor): groups of at most rssm_reg_max_members() wide
+// members whose GRU slices fit the register layout, every group on one XCD.
+// The step model: the exchange costs ~1.1 us plus the bytes one member reads
+// (every member's partial sums and the whole h_t of the group's rows) at
+// ~13 GB/s per member, from a sweep of ring exchanges inside one XCD; the
+// products are the per-wave MFMA chains (the slice products take a fixed
+// number of chunks per wave whatever the slice width) at ~12 cycles each,
+// plus six workgroup barriers and the gate math.
+bool plan_rssm_reg(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
+  // flat placement (consecutive ids form a group) rules it out: its
+  // exchange is only valid when a group's members share an XCD
+  if (d->mode != RNN_MODE_RSSM_PRIOR || d->weights == 1 || d->placement == 1) return false;
+  const int B = d->B, S = d->state_dim, A = d->action_dim, E = d->embed_dim, Hb = d->belief_dim;
+  const int per_xcd = cus / xcds;
+  double best = 1e30;
+  bool found = false;
+  for (int rows = 1; rows <= rssm_max_rows(); ++rows) {
+    if (d->tile_batch > 0 && rows != d->tile_batch) continue;
+    const int ngroups = cdiv(B, rows);
+    const int gpx = cdiv(ngroups, xcds);
+    for (int nw = 1; nw <= rssm_reg_max_members(); ++nw) {
+      const int h_per = cdiv(Hb, nw);
+      if (d->tile_hidden > 0 && h_per != d->tile_hidden) continue;
+      if (nw > 1 && cdiv(Hb, nw - 1) == h_per) continue;
+      if (gpx * nw > per_xcd) continue;
+      RssmArgs a{};
+      a.S = S; a.A = A; a.E = E; a.Hb = Hb; a.rows = rows; a.nw = nw; a.h_per = h_per; a.Ea = 0;
+      a.Ep = rup(E, 4); a.Hbp = rup(Hb, 4);
+      if (!rssm_reg_fits(a)) continue;
+      const int lds = rssm_reg_lds_bytes(a);
+      if (lds > kMaxLds) continue;
+      const double bytes = (double)rows * ((double)nw * a.Ep + a.Hbp) * 4.0;
+      const int nq = cdiv(cdiv(std::max(E, Hb), 4), 4), n2 = cdiv(cdiv(E, 4), 8);
+      const double mfma = 4.0 * (2 * nq + std::max(nq, n2) + cdiv(h_per, 4) + cdiv(S + A, 4));
+      const double t = 1.1 + bytes / 13.3e3 + (mfma * 12.0 + 6 * 150.0 + 400.0) / 2400.0;
+      if (t < best) {
+        best = t;
+        *out = RssmPlan{rows, ngroups, nw, h_per, gpx, lds, 1};
+        found = true;
+      }
+    }
+  }
+  return found;
+}
+
 int plan_rssm(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
+  if (plan_rssm_reg(d, cus, xcds, out)) return RNN_OK;
+  if (d->weights == 2) return RNN_E_PLAN;  // registers requested, no such plan
   const int B = d->B, S = d->state_dim, A = d->action_dim, E = d->embed_dim, Hb = d->belief_dim;
   const int Ea = d->actor_dim;
   const int per_xcd = xcds > 1 ? cus / xcds : 0;
@@ -433,7 +485,7 @@ int plan_rssm(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
       if (d->placement == 2 && !xcd_aligned) t += 1e3;  // requested: aligned plans first
       if (t < best) {
         best = t;
-        *out = RssmPlan{rows, ngroups, nw, h_per, xcd_aligned ? gpx : 0, lds};
+        *out = RssmPlan{rows, ngroups, nw, h_per, xcd_aligned ? gpx : 0, lds, 0};
         found = true;
       }
     }
@@ -518,12 +570,20 @@ int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* w
   a.beliefs = (float*)io->beliefs;
   a.ex_h = (float*)(ws + L.ex_h); a.ex_p = (float*)(ws + L.ex_p);
   a.Ep = rssm_ex_cols(d); a.Hbp = rup(d->belief_dim, 4);
+  a.xid = (unsigned*)(ws + L.xid);
   a.counters = (unsigned*)(ws + L.counters);
   a.status = (int*)(ws + L.status);
   // status word and counters are contiguous at the start of the workspace
   if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
+  if (p.reg) {
+    // the XCC ids and both rings start as the sentinel: ids, h ring and the
+    // used front of the partial ring are consecutive (the fill covers the
+    // alignment gaps between them too)
+    const size_t end = L.ex_p + (size_t)rssm_ring_slots() * d->B * p.nw * a.Ep * 4;
+    if ((rc = hip_status(launch_fill_u32(ws + L.xid, end - L.xid, 0xFFFFFFFFu, st))) != RNN_OK) return rc;
+  }
   if ((rc = prof.begin(3)) != RNN_OK) return rc;
-  if ((rc = hip_status(launch_rssm(a, st))) != RNN_OK) return rc;
+  if ((rc = hip_status(p.reg ? launch_rssm_reg(a, st) : launch_rssm(a, st))) != RNN_OK) return rc;
   return prof.end();
 }
 
@@ -1051,6 +1111,7 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
     if ((rc = plan_rssm(desc, cus, xcds, &p)) != RNN_OK) return rc;
     info[0] = 3; info[1] = rssm_grid(p, xcds); info[2] = p.lds; info[3] = p.rows; info[4] = p.h_per;
     info[5] = p.nw; info[6] = 0; info[7] = p.ngroups; info[8] = p.gpx;
+    if (n_info >= 13) info[9] = p.reg;
     return RNN_OK;
   }
   long long n_tok = 0;

@@ -10,9 +10,9 @@ namespace rnnk {
 
 namespace {
 
-__global__ void fill_zero_kernel(uint32_t* p, size_t n) {
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
+    p[i] = value;
 }
 
 struct IntChunk {
@@ -74,14 +74,16 @@ hipError_t launch_exchange_probe(void* buf, int iters, unsigned long long* out, 
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t value, hipStream_t stream) {
   const size_t n = bytes / 4;
   if (n == 0) return hipSuccess;
   const size_t want = (n + 255) / 256;
   const int blocks = (int)(want < 256 ? want : 256);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(p), n);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(p), n, value);
   return hipGetLastError();
 }
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) { return launch_fill_u32(p, bytes, 0u, stream); }
 
 hipError_t launch_write_ints(int* dst, const int* src, int n, hipStream_t stream) {
   for (int base = 0; base < n; base += kIntsPerLaunch) {

@@ -257,11 +257,17 @@ def test_packed_equals_padded_on_gpu():
 # RSSM prior
 # ---------------------------------------------------------------------------
 
-def test_rssm_small():
-    log("[gpu] rssm small")
+# weights hint: 0 lets the planner choose (the register kernel where the
+# shape fits it), 1 the kernel with LDS-resident input weights
+RSSM_KERNELS = [0, 1]
+
+
+@pytest.mark.parametrize("wh", RSSM_KERNELS)
+def test_rssm_small(wh):
+    log(f"[gpu] rssm small (weights hint {wh})")
     d = synth.make_rssm_inputs(7, 9, state_dim=5, action_dim=3, embed_dim=24, belief_dim=20, seed=9,
                                s0_std=0.5, h0_std=0.5)
-    got = run_rssm(d)
+    got = run_rssm(d, weights_hint=wh)
     ref = oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"], d["s0"], d["h0"])
     for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs")):
         assert_close(g, r, "f32", "rssm " + nm)
@@ -276,22 +282,24 @@ RSSM_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("wh", RSSM_KERNELS)
 @pytest.mark.parametrize("case", RSSM_SHAPES, ids=[c[0] for c in RSSM_SHAPES])
-def test_rssm_shapes(case):
+def test_rssm_shapes(case, wh):
     name, B, T, S, A, E, Hb, tb, th = case
-    log(f"[gpu] rssm shape {name}")
+    log(f"[gpu] rssm shape {name} (weights hint {wh})")
     d = synth.make_rssm_inputs(B, T, state_dim=S, action_dim=A, embed_dim=E, belief_dim=Hb,
                                seed=zlib.crc32(name.encode()) % 1000, s0_std=0.5, h0_std=0.5)
-    got = run_rssm(d, tile_batch=tb, tile_hidden=th)
+    got = run_rssm(d, tile_batch=tb, tile_hidden=th, weights_hint=wh)
     ref = oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"], d["s0"], d["h0"])
     for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs")):
         assert_close(g, r, "f32", f"{name} {nm}")
 
 
-def test_rssm_zero_weights_closed_form():
-    log("[gpu] rssm closed form")
+@pytest.mark.parametrize("wh", RSSM_KERNELS)
+def test_rssm_zero_weights_closed_form(wh):
+    log(f"[gpu] rssm closed form (weights hint {wh})")
     d = synth.make_rssm_inputs(6, 4, seed=10, zero_weights=True)
-    means, stds, states, beliefs = run_rssm(d)
+    means, stds, states, beliefs = run_rssm(d, weights_hint=wh)
     assert np.all(beliefs == 0) and np.all(means == 0)
     k = np.log(2.0) + 0.1
     assert_close(stds, np.full_like(stds, k), "f32", "stds")
@@ -351,13 +359,29 @@ def test_full_lstm_t80_b1():
     _compare(d, run_rnn(d), _oracle(d), "lstm_t80_b1")
 
 
-def test_full_rssm_b50_t50():
+@pytest.mark.parametrize("wh", RSSM_KERNELS)
+def test_full_rssm_b50_t50(wh):
     d = synth.make_inputs("rssm_b50_t50")
-    log("[gpu] full-size rssm_b50_t50")
-    got = run_rssm(d)
+    log(f"[gpu] full-size rssm_b50_t50 (weights hint {wh})")
+    got = run_rssm(d, weights_hint=wh)
     ref = oracle.rssm_prior_unroll(d["actions"], d["eps"], d["weights"])
     for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs")):
         assert_close(g, r, "f32", "rssm_b50_t50 " + nm)
+
+
+def test_rssm_register_kernel_chosen_for_the_headline_shape():
+    """The planner takes the register kernel (wide members, ring exchange
+    inside an XCD) for the B=50, T=50 unroll; hint 1 keeps the other one."""
+    import gru_sequence_scan_amd as gss
+    d = gss.RnnDesc()
+    for k, v in dict(mode=3, dtype=0, layout=2, T=50, B=50, num_layers=1, has_bias=1, state_dim=20,
+                     action_dim=6, embed_dim=200, belief_dim=200).items():
+        setattr(d, k, v)
+    d.scale_lb = 0.1
+    p = gss.rnn_plan_info(d)
+    assert p["wreg"] == 1 and p["members"] <= 8 and p["groups_per_xcd"] > 0
+    d.weights = 1
+    assert gss.rnn_plan_info(d)["wreg"] == 0
 
 
 def test_full_gru_t256_b256():

@@ -156,7 +156,6 @@ MEASURED_BEST = {
     "gru_t256_b256": (16, 32),
     "lstmp_t1000_b32": (16, 32),
     "bilstm_varlen_b64": (16, 16),
-    "rssm_b50_t50": (2, 20),
 }
 
 
@@ -165,6 +164,21 @@ def test_plans_match_measured_best_shapes(name):
     _, d, lengths = desc_for(name)
     p = gss.rnn_plan_info(d, lengths)
     assert (p["rows"], p["hidden_per_wg"]) == MEASURED_BEST[name]
+
+
+# The RSSM unroll's launch shapes on the register kernel, measured on MI355X
+# (microseconds per unroll, one box): the shapes lie within a few percent of
+# each other, so the planner's choice must be within 3% of the fastest.
+RSSM_MEASURED_US = {(2, 40): 325.6, (3, 40): 329.1, (4, 40): 334.9, (2, 34): 321.6, (2, 29): 316.4,
+                    (2, 25): 320.4, (4, 25): 328.7}
+
+
+def test_rssm_plan_within_measured_best():
+    _, d, lengths = desc_for("rssm_b50_t50")
+    p = gss.rnn_plan_info(d, lengths)
+    assert p["wreg"] == 1
+    t = RSSM_MEASURED_US[(p["rows"], p["hidden_per_wg"])]
+    assert t <= 1.03 * min(RSSM_MEASURED_US.values())
 
 
 @pytest.mark.parametrize("mode,dtype,H,B,ok", [
