@@ -478,6 +478,12 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   for (int k = 0; k < nsteps; ++k) {
     const int t = t_of(k);
     const int rowbase = a.packed ? a.offsets[t] : t * a.B;
+    // The previous step's output stores and this step's G_x prefetch were
+    // issued before the group barrier, which took longer than they do: an
+    // explicit wait here is free, and it leaves no load pending on any
+    // register, so the compiler need not wait for every outstanding memory
+    // operation before each LDS read and MFMA of the product below.
+    if (!solo) wait_all_mem();
 
     // h_{t-1} of the block -> LDS, then the hidden-hidden product.
     if (!solo) {
@@ -582,6 +588,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
       return;
 
     if (a.mode == kLSTMP) {
+      wait_all_mem();  // as at the top of the step
       // hidden-projection dense: h_t = m_t W_hr^T for this slice of P
       load_tile_coherent<DT>(mx_rs, mx_el(b0, 0), a.Hp, b0, a.B, use_mfma ? rup(a.bb, 16) : a.bb,
                              a.Hp, lds, L.as, L.as_ld);
