@@ -411,18 +411,18 @@ def measure(name, args, rt_us, with_cpu):
     else:
         members = plan["members"]
         lstmp = spec.mode == "lstmp"
-        bars = 0 if (members == 1 and not lstmp) else (2 if lstmp else 1)
+        bars = 0 if (members == 1 and not lstmp) else (2 if lstmp else 1)  # exchanges per step
         occ = min(256, plan["workgroups"])
     if dom["kernel"] == "gemm_xw":
         occ = 256
     ob = onchip_bytes(spec, d, plan) if dom["kernel"] in ("scan", "rssm", "scan_wave") else 0
     t_roof = max(dom["flops"] / (peak * 1e12), ob / (PEAK_LDS_GBS * 1e9), dom["bytes"] / (PEAK_HBM_GBS * 1e9))
     roofline.update({
-        "recurrence_steps": n_rec, "us_per_step": dom["avg_us"] / n_rec, "barriers_per_step": bars,
+        "recurrence_steps": n_rec, "us_per_step": dom["avg_us"] / n_rec, "exchanges_per_step": bars,
         "onchip_bytes": ob, "t_roof_us": t_roof * 1e6, "roof_frac": t_roof * 1e6 / dom["avg_us"],
         "occupied_cus": occ, "frac_occupied_cus": achieved / (peak * occ / 256.0),
         "exchange_roundtrip_us": rt_us,
-        "barrier_floor_us": n_rec * bars * rt_us if rt_us is not None else None,
+        "exchange_floor_us": n_rec * bars * rt_us if rt_us is not None else None,
     })
     ms_per_step = elapsed / K * 1e3
     value = tokens / (elapsed / K)

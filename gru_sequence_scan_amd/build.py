@@ -6,6 +6,7 @@ produces gru_sequence_scan_amd/_lib/librnn_gfx950.so. The library is plain
 C ABI (include/rnn.h); the Python binding loads it with ctypes.
 """
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -16,11 +17,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB_NAME = "librnn_gfx950.so"
-SOURCES = ["gemm_xw.hip", "scan.hip", "scan_wave.hip", "scan_bwd.hip", "gemm_gen.hip", "rssm.hip", "rssm2.hip",
-           "util.hip", "rnn_api.cpp"]
+SOURCES = ["gemm_xw.hip", "scan.hip", "scan_bf16_reg.hip", "scan_bf16_lds.hip", "scan_f32_reg.hip", "scan_f32_lds.hip",
+           "scan_wave.hip", "scan_bwd.hip", "gemm_gen.hip", "rssm.hip", "rssm2.hip", "util.hip", "rnn_api.cpp"]
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # Keep the compiler from forming packed-fp32 VALU instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -38,24 +39,40 @@ def lib_path():
     return os.path.join(OUT_DIR, LIB_NAME)
 
 
-def build(verbose=False):
-    os.makedirs(OUT_DIR, exist_ok=True)
-    out = lib_path()
-    tmp = out + ".tmp"
-    cmd = [hipcc_path()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    srcs = []
-    for s in SOURCES:
-        path = os.path.join(CSRC, s)
-        srcs += (["-x", "hip", path] if s.endswith(".cpp") else [path])
-    cmd += srcs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
+    return res.returncode, errs
+
+
+def build(verbose=False, jobs=None):
+    """Compile every source to an object (in parallel), then link the library."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    obj_dir = os.path.join(OUT_DIR, "obj")
+    os.makedirs(obj_dir, exist_ok=True)
+    out = lib_path()
+    tmp = out + ".tmp"
+    hipcc = hipcc_path()
+    base = [hipcc] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    cmds, objs = [], []
+    for s in SOURCES:
+        path = os.path.join(CSRC, s)
+        obj = os.path.join(obj_dir, os.path.splitext(s)[0] + ".o")
+        objs.append(obj)
+        cmds.append(base + ["-c"] + (["-x", "hip", path] if s.endswith(".cpp") else [path]) + ["-o", obj])
+    jobs = jobs or max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    for cmd, (rc, errs) in zip(cmds, results):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed ({rc}) for {cmd[-3]}:\n{errs}")
+        if verbose and errs.strip():
+            print(errs, file=sys.stderr)
+    rc, errs = _run([hipcc, "-shared", "-fPIC", "--offload-arch=gfx950"] + objs + ["-o", tmp])
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{errs}")
     os.replace(tmp, out)
     return out
 

@@ -76,12 +76,16 @@ struct ScanArgs {
   void* y;             // [rows, D * K]
   const int* lengths;  // device [B] or null (all T)
   const int* offsets;  // device [T + 1] (packed)
-  // exchange and synchronisation (workspace)
-  void* hx;            // [2][D][B][Kp]
-  void* mx;            // [D][B][Hp] (LSTMP)
-  unsigned* counters;  // [D * nbb] counters, 64 bytes apart
+  // exchange (workspace): rings of write-once slots, all-ones before the
+  // launch (kRingSlots slots in scan_common.hpp)
+  void* hx;            // [4][D][B][Kp] h_t (LSTMP: the projected h_t)
+  void* mx;            // [4][D][B][Hp] m_t (LSTMP)
+  unsigned* xid;       // [D * nbb * ns] members' XCD ids
+  unsigned* counters;  // unused by the forward scan
   int* status;
 };
+constexpr int kScanRingSlots = 4;
+constexpr int kScanMaxWorkgroups = 4096;  // xid entries per layer
 hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
 constexpr int kScanRegChunks = 32;
 

@@ -151,7 +151,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // needs no device)
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t status, counters, ints, gx, inter0, inter1, hx, mx, ex_h, ex_p, xid, gpart, total;
+  size_t status, counters, ints, gx, inter0, inter1, hx, mx, ex_h, ex_p, xid, ring_end, gpart, total;
   size_t counters_bytes;
   int n_ints;
 };
@@ -177,6 +177,16 @@ Dims dims_of(const RnnDesc* d, long long n_tok) {
 // Columns of one member's partial-sum row in the RSSM exchange: W_1 h
 // (E, padded to 4), then the actor's W_a1[:, S:] h (Ea, padded to 4).
 int rssm_ex_cols(const RnnDesc* d) { return rup(d->embed_dim, 4) + rup(d->actor_dim, 4); }
+
+// Per-layer exchange regions of the forward scan (aligned sizes, so the
+// layers' regions stay aligned).
+size_t xid_layer_bytes() { return align_up((size_t)kScanMaxWorkgroups * 4, kAlign); }
+size_t hx_ring_bytes(const RnnDesc* d, const Dims& m) {
+  return align_up((size_t)kScanRingSlots * m.D * d->B * m.Kp * m.esize, kAlign);
+}
+size_t mx_ring_bytes(const RnnDesc* d, const Dims& m) {
+  return align_up((size_t)kScanRingSlots * m.D * d->B * m.Hp * m.esize, kAlign);
+}
 
 WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
   WsLayout w{};
@@ -209,8 +219,13 @@ WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
   const size_t inter = (size_t)m.rows * m.D * m.K * m.esize;
   w.inter0 = d->num_layers > 1 ? take(inter) : 0;
   w.inter1 = d->num_layers > 2 ? take(inter) : 0;
-  w.hx = take((size_t)2 * m.D * d->B * m.Kp * m.esize);
-  w.mx = d->mode == RNN_MODE_LSTMP ? take((size_t)m.D * d->B * m.Hp * m.esize) : 0;
+  // the forward scan's exchange, one region per layer and all sentinel-filled
+  // by one fill before the first layer: the members' XCD ids, the h ring and
+  // (LSTMP) the m ring
+  w.xid = take(xid_layer_bytes() * d->num_layers);
+  w.hx = take(hx_ring_bytes(d, m) * d->num_layers);
+  w.mx = d->mode == RNN_MODE_LSTMP ? take(mx_ring_bytes(d, m) * d->num_layers) : w.hx;
+  w.ring_end = o;
   // split-K partial products of the input GEMMs with few output tiles
   size_t gpart = 0;
   for (int l = 0; l < d->num_layers; ++l) {
@@ -336,14 +351,15 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wre
   double best = 1e30;
   bool found = false;
   for (int bb : bbs) {
-    if (bb < 1) continue;
+    if (bb < 1 || bb > 64) continue;  // the scan tracks a block's rows in 64-bit masks
     const bool mfma = bb % 16 == 0;
     for (int hs : hss) {
       if (hs < 1 || bb * hs > 1024) continue;
       const int ns = cdiv(H, hs);
       const int nbb = cdiv(B, bb);
-      if ((long long)m.D * nbb * ns > cus) continue;
+      if ((long long)m.D * nbb * ns > std::min(cus, kScanMaxWorkgroups)) continue;
       const int ps = lstmp ? cdiv(P, ns) : 0;
+      if (bb * ps > 1024) continue;  // projection outputs: at most 4 per thread
       const int ncw = rup(m.gates * hs, 16);
       for (int wreg = allow_wreg && d->weights != 1 ? 1 : 0; wreg >= 0; --wreg) {
         ScanArgs a{};
@@ -656,10 +672,19 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   const bool wave = !rsv && use_wave_scan(d, m);
   ScanPlan p{};
   if (!wave && (rc = plan_scan(d, m, cus, xcds, wreg_ok, &p)) != RNN_OK) return rc;
+  // the scan addresses one layer's rings, and one step's rows of G_x and y,
+  // with 32-bit byte offsets
+  if (!wave && (std::max(hx_ring_bytes(d, m), mx_ring_bytes(d, m)) >= ((size_t)1 << 31) ||
+                (size_t)d->B * m.D * m.G * 4 >= ((size_t)1 << 31) ||
+                (size_t)d->B * m.D * m.K * es >= ((size_t)1 << 31)))
+    return RNN_E_PLAN;
   const ReserveLayout RL = reserve_of(d, m);
 
   // ---- enqueue ----
   if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
+  if (!wave &&
+      (rc = hip_status(launch_fill_u32(ws + L.xid, L.ring_end - L.xid, 0xFFFFFFFFu, st))) != RNN_OK)
+    return rc;
   int* dev_len = nullptr;
   int* dev_off = nullptr;
   if (has_len) {
@@ -747,8 +772,9 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     a.rsv = rsv ? (float*)(rsv + RL.gates[l]) : nullptr;
     a.lengths = dev_len;
     a.offsets = dev_off;
-    a.hx = ws + L.hx;
-    a.mx = d->mode == RNN_MODE_LSTMP ? ws + L.mx : nullptr;
+    a.hx = ws + L.hx + l * hx_ring_bytes(d, m);
+    a.mx = d->mode == RNN_MODE_LSTMP ? ws + L.mx + l * mx_ring_bytes(d, m) : nullptr;
+    a.xid = (unsigned*)(ws + L.xid + l * xid_layer_bytes());
     a.counters = (unsigned*)(ws + L.counters + (size_t)l * m.D * d->B * kCounterBytes);
     a.status = (int*)(ws + L.status);
     if ((rc = prof.begin(wave ? 4 : 2)) != RNN_OK) return rc;

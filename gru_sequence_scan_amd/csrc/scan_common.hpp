@@ -4,6 +4,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "kernels.hpp"
 
 namespace rnnk {
 namespace {
@@ -112,7 +113,7 @@ __device__ __forceinline__ void mm_tiles(const DT* As, int as_ld, const DT* Ws, 
 // of 16), A and W in LDS. Each wave takes a contiguous run of tiles and
 // computes up to four of them together.
 template <typename DT>
-__device__ void mm_mfma(const char* lds, int as_off, int as_ld, int w_off, int w_ld, float* acc,
+__device__ __forceinline__ void mm_mfma(const char* lds, int as_off, int as_ld, int w_off, int w_ld, float* acc,
                         int acc_ld, int mtiles, int ntiles, int kp) {
   const DT* As = reinterpret_cast<const DT*>(lds + as_off);
   const DT* Ws = reinterpret_cast<const DT*>(lds + w_off);
@@ -215,7 +216,7 @@ __device__ void load_tile_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t src_base_
 // Load `nrows` weight rows into LDS as [nrows][ld], zero-padding k >= klen
 // and rows for which row_of() returns -1.
 template <typename DT, typename RowFn>
-__device__ void load_weights(const DT* w, int klen, int kpad, int nrows, RowFn row_of, char* lds,
+__device__ __forceinline__ void load_weights(const DT* w, int klen, int kpad, int nrows, RowFn row_of, char* lds,
                              int off, int ld) {
   DT* dst = reinterpret_cast<DT*>(lds + off);
   const int total = nrows * kpad;
@@ -227,5 +228,310 @@ __device__ void load_weights(const DT* w, int klen, int kpad, int nrows, RowFn r
 }
 
 
+// ---------------------------------------------------------------------------
+// Ring exchange of the forward scan. Step k's exchanged state goes to slot
+// k mod kRingSlots of a ring that holds the all-ones sentinel (0xFFFF per
+// bf16 element, 0xFFFFFFFF per fp32 element) until the element's owner
+// stores its value; readers poll their 16-byte chunks with device-scope
+// loads until no sentinel is left in them (padding columns hold zeros). A NaN
+// result is stored as the canonical quiet NaN, so no value equals the
+// sentinel. The store is plain when every member of the group runs on one
+// XCD (it lands in that XCD's L2, where the others' device-scope loads find
+// it) and device-scope otherwise.
+// ---------------------------------------------------------------------------
+constexpr int kRingSlots = kScanRingSlots;
+
+template <typename DT>
+__device__ __forceinline__ void ring_store(__amdgpu_buffer_rsrc_t rs, uint32_t elem, float v, bool local);
+template <>
+__device__ __forceinline__ void ring_store<float>(__amdgpu_buffer_rsrc_t rs, uint32_t elem, float v, bool local) {
+  const uint32_t bits = v == v ? __builtin_bit_cast(uint32_t, v) : 0x7FC00000u;
+  if (local)
+    __builtin_amdgcn_raw_buffer_store_b32(bits, rs, (int)(elem * 4u), 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(bits, rs, (int)(elem * 4u), 0, kCohPolicy);
+}
+template <>
+__device__ __forceinline__ void ring_store<bf16>(__amdgpu_buffer_rsrc_t rs, uint32_t elem, float v, bool local) {
+  const uint16_t bits = v == v ? __builtin_bit_cast(uint16_t, (bf16)v) : (uint16_t)0x7FC0u;
+  if (local)
+    __builtin_amdgcn_raw_buffer_store_b16(bits, rs, (int)(elem * 2u), 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b16(bits, rs, (int)(elem * 2u), 0, kCohPolicy);
+}
+// Plain store of one element at a byte offset; dropped when the offset lies
+// past the end of the buffer.
+template <typename DT>
+__device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, float v) {
+  if constexpr (sizeof(DT) == 4)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, (int)byte_off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)v), rs, (int)byte_off, 0, 0);
+}
+
+// Put an element back to the sentinel.
+template <typename DT>
+__device__ __forceinline__ void ring_reset(__amdgpu_buffer_rsrc_t rs, uint32_t elem, bool local) {
+  if (sizeof(DT) == 4) {
+    if (local)
+      __builtin_amdgcn_raw_buffer_store_b32(0xFFFFFFFFu, rs, (int)(elem * 4u), 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(0xFFFFFFFFu, rs, (int)(elem * 4u), 0, kCohPolicy);
+  } else {
+    if (local)
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0xFFFFu, rs, (int)(elem * 2u), 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0xFFFFu, rs, (int)(elem * 2u), 0, kCohPolicy);
+  }
+}
+
+// True when any element of a 16-byte chunk holds the sentinel.
+template <typename DT>
+__device__ __forceinline__ bool chunk_pending(const u32x4& v) {
+  if (sizeof(DT) == 4) return v[0] == 0xFFFFFFFFu || v[1] == 0xFFFFFFFFu || v[2] == 0xFFFFFFFFu || v[3] == 0xFFFFFFFFu;
+  bool s = false;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s = s || (v[e] & 0xFFFFu) == 0xFFFFu || v[e] >= 0xFFFF0000u;
+  return s;
+}
+
+// True when any element of eight chunks holds the sentinel: the sentinel is
+// the largest value of the element's unsigned integer type, so one running
+// maximum (packed per 16-bit half for bf16) answers for all of them.
+template <typename DT>
+__device__ __forceinline__ bool batch_pending(const u32x4 (&v)[8]) {
+  if (sizeof(DT) == 4) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, max(max(v[i][0], v[i][1]), max(v[i][2], v[i][3])));
+    return m == 0xFFFFFFFFu;
+  }
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // through a scalar: hipcc's __builtin_bit_cast of an ext-vector element
+      // expression reads element 0 whatever the index
+      const uint32_t x = v[i][e];
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, x));
+    }
+  return m[0] == 0xFFFFu || m[1] == 0xFFFFu;
+}
+
+// Polling a tile of `rows` rows (at most 64) of width `width` elements (a
+// multiple of a chunk) into LDS (row stride dst_ld elements). Row r comes
+// from the ring at element ring_el + r * ring_ld when bit r of `ring` is
+// set (polled until complete), from the first h0_valid elements of
+// h0 + r * h0_ld when bit r of `init` is set (a row's first step; the rest
+// of the row is zero), and is zero otherwise. The ring's padding columns
+// hold zeros, so whole chunks are checked and copied.
+//
+// Thread t handles chunks t, t + 256, ... of the tile (row-major), eight at
+// a time (a batch): poll_issue loads a batch, poll_finish loads its pending
+// chunks again until their values arrive and writes the batch to LDS. A
+// chunk's (row, column) comes from a cursor advanced by 256 chunks with
+// adds and one compare, and the cursor enters each call through an opaque
+// copy: the per-chunk index math is redone every step instead of being
+// hoisted out of the step loop into registers.
+//
+// When the watchdog fires (no progress for ~2 s, or another member's error
+// in *status) the status word gets kStatusTimeout, *abort_lds is set and
+// poll_finish returns false; the caller checks the flag after its next
+// workgroup barrier.
+struct PollGeom {
+  int cpr;       // chunks per row
+  int q, rem;    // 256 chunks = q rows + rem chunks
+  int total;     // chunks in the tile
+};
+
+__device__ __forceinline__ PollGeom poll_geom(int rows, int width, int epc) {
+  PollGeom g;
+  g.cpr = width / epc;
+  g.q = kScanThreads / g.cpr;
+  g.rem = kScanThreads - g.q * g.cpr;
+  g.total = rows * g.cpr;
+  return g;
+}
+
+// Cursor (row, chunk column) of chunk threadIdx.x, packed as row << 16 | col.
+__device__ __forceinline__ uint32_t poll_cursor0(const PollGeom& g) {
+  const int t = threadIdx.x;
+  return (uint32_t)(t / g.cpr) << 16 | (uint32_t)(t % g.cpr);
+}
+
+__device__ __forceinline__ void cursor_step(int& r, int& cc, const PollGeom& g) {
+  cc += g.rem;
+  r += g.q;
+  if (cc >= g.cpr) {
+    cc -= g.cpr;
+    ++r;
+  }
+}
+
+struct PollBatch {
+  u32x4 v[8];
+  unsigned pend;
+  uint32_t cur;  // cursor of the batch's first chunk
+};
+
+// A byte offset past the end of every ring (each under 2 GiB).
+constexpr uint32_t kPollOob = 0x7FFFFFF0u;
+
+template <typename DT>
+__device__ __forceinline__ void poll_issue(PollBatch& pb, uint32_t cur, int base, const PollGeom& g,
+                                           __amdgpu_buffer_rsrc_t rs, uint32_t ring_el, int ring_ld, uint64_t ring) {
+  constexpr int kEpc = 16 / sizeof(DT);
+  asm volatile("" : "+v"(cur));
+  pb.cur = cur;
+  pb.pend = 0;
+  int r = (int)(cur >> 16), cc = (int)(cur & 0xFFFFu);
+  // Eight loads, unconditionally: a chunk that is not polled reads past the
+  // end of the buffer (zero). Straight-line code lets the compiler wait for
+  // exactly these loads, not for what the caller issues after them.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool in = base + i * kScanThreads + (int)threadIdx.x < g.total;
+    const bool from_ring = in && ((ring >> r) & 1ull);
+    const uint32_t off = (ring_el + (uint32_t)(r * ring_ld + cc * kEpc)) * (uint32_t)sizeof(DT);
+    pb.v[i] = coh_poll16(rs, from_ring ? off : kPollOob);
+    cursor_step(r, cc, g);
+  }
+}
+
+template <typename DT>
+__device__ __forceinline__ bool poll_finish(PollBatch& pb, int base, const PollGeom& g, __amdgpu_buffer_rsrc_t rs,
+                                            uint32_t ring_el, int ring_ld, uint64_t init, const DT* h0, int h0_ld,
+                                            int h0_valid, char* lds, int dst_off, int dst_ld, int* status,
+                                            int* abort_lds) {
+  constexpr int kEpc = 16 / sizeof(DT);
+  DT* dst = reinterpret_cast<DT*>(lds + dst_off);
+  bool ok = true;
+  uint64_t t0 = 0;
+  unsigned polls = 0;
+  // First check, branch-free (chunks not polled read zero: never pending);
+  // chunk by chunk only when some sentinel is left.
+  pb.pend = 0;
+  if (batch_pending<DT>(pb.v)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb.pend |= chunk_pending<DT>(pb.v[i]) ? 1u << i : 0u;
+  }
+  while (pb.pend) {
+    if ((++polls & 63u) == 0) {
+      const uint64_t now = __builtin_amdgcn_s_memrealtime();
+      if (t0 == 0) t0 = now;
+      const int st = __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (st != kStatusOk || now - t0 > kWatchdogTicks) {
+        __hip_atomic_store(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *abort_lds = 1;
+        ok = false;
+        break;
+      }
+    }
+    {
+      int r = (int)(pb.cur >> 16), cc = (int)(pb.cur & 0xFFFFu);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if ((pb.pend >> i) & 1u)
+          pb.v[i] = coh_poll16(rs, (ring_el + (uint32_t)(r * ring_ld + cc * kEpc)) * (uint32_t)sizeof(DT));
+        cursor_step(r, cc, g);
+      }
+    }
+    // Check every chunk, branch-free: a completed chunk stays complete, and
+    // no load result is left unread on any path (a register with a load in
+    // flight on some path makes the compiler wait for all memory operations
+    // before the register is next written).
+    pb.pend = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb.pend |= chunk_pending<DT>(pb.v[i]) ? 1u << i : 0u;
+  }
+  {
+    int r = (int)(pb.cur >> 16), cc = (int)(pb.cur & 0xFFFFu);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (base + i * kScanThreads + (int)threadIdx.x < g.total)
+        *reinterpret_cast<u32x4*>(dst + r * dst_ld + cc * kEpc) = pb.v[i];
+      cursor_step(r, cc, g);
+    }
+  }
+  // Rows at their first step take h0 (rare: kept out of the unrolled code).
+  // The same thread wrote the chunk's zeros just above.
+  if (init && h0) {
+    int r = (int)(pb.cur >> 16), cc = (int)(pb.cur & 0xFFFFu);
+#pragma nounroll
+    for (int i = 0; i < 8; ++i) {
+      if (base + i * kScanThreads + (int)threadIdx.x < g.total && ((init >> r) & 1ull)) {
+#pragma nounroll
+        for (int e = 0; e < kEpc && cc * kEpc + e < h0_valid; ++e)
+          dst[r * dst_ld + cc * kEpc + e] = h0[(size_t)r * h0_ld + cc * kEpc + e];
+      }
+      cursor_step(r, cc, g);
+    }
+  }
+  return ok;
+}
+
+// The whole tile. cur0 = poll_cursor0(g). between() runs after the first
+// batch's loads are issued and before they are waited for (work whose
+// memory operations should not delay the poll: the vector-memory counter
+// retires in issue order).
+template <typename DT, typename BetweenFn>
+__device__ __forceinline__ void poll_tile(const PollGeom& g, uint32_t cur0, __amdgpu_buffer_rsrc_t rs,
+                                          uint32_t ring_el, int ring_ld, uint64_t ring, uint64_t init, const DT* h0,
+                                          int h0_ld, int h0_valid, char* lds, int dst_off, int dst_ld, int* status,
+                                          int* abort_lds, BetweenFn between) {
+  PollBatch pb;
+  poll_issue<DT>(pb, cur0, 0, g, rs, ring_el, ring_ld, ring);
+  between();
+  bool ok = poll_finish<DT>(pb, 0, g, rs, ring_el, ring_ld, init, h0, h0_ld, h0_valid, lds, dst_off, dst_ld, status,
+                            abort_lds);
+  if (g.total <= 8 * kScanThreads) return;
+  int r = (int)(pb.cur >> 16), cc = (int)(pb.cur & 0xFFFFu);
+  for (int base = kScanThreads * 8; ok && base < g.total; base += kScanThreads * 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cursor_step(r, cc, g);
+    poll_issue<DT>(pb, (uint32_t)r << 16 | (uint32_t)cc, base, g, rs, ring_el, ring_ld, ring);
+    ok = poll_finish<DT>(pb, base, g, rs, ring_el, ring_ld, init, h0, h0_ld, h0_valid, lds, dst_off, dst_ld, status,
+                         abort_lds);
+  }
+}
+
+// Whether every member of a group runs on one XCD: each member publishes its
+// hardware XCC id (device-scope store into ids[member], which holds the
+// sentinel before the launch) and reads the others' (bounded wait). Called
+// by every thread; the answer is the same in every member. *ok turns false
+// when the wait ran out (the members were not all resident).
+__device__ bool group_on_one_xcd(unsigned* ids, int members, int me, int* ok_lds, int* flag_lds) {
+  if (threadIdx.x == 0) {
+    unsigned hw;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(hw));
+    hw &= 0xFu;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(ids, (uint32_t)members * 4u);
+    coh_store4(xr, (uint32_t)me * 4u, hw);
+    bool same = true, ok = true;
+    uint64_t t0 = 0;
+    for (int m = 0; m < members && ok; ++m) {
+      unsigned polls = 0, id;
+      while ((id = coh_poll4(xr, (uint32_t)m * 4u)) == 0xFFFFFFFFu) {
+        if ((++polls & 63u) == 0) {
+          const uint64_t now = __builtin_amdgcn_s_memrealtime();
+          if (t0 == 0) t0 = now;
+          if (now - t0 > kWatchdogTicks) {
+            ok = false;
+            break;
+          }
+        }
+      }
+      same = same && id == hw;
+    }
+    *flag_lds = same ? 1 : 0;
+    *ok_lds = ok ? 1 : 0;
+  }
+  __syncthreads();
+  return *flag_lds != 0;
+}
+
 }  // namespace
+
 }  // namespace rnnk

@@ -1,0 +1,10 @@
+// Kernel 2 instances: f32 elements, W_hh slices in LDS.
+#include "scan_kernel.hpp"
+
+namespace rnnk {
+
+hipError_t launch_scan_f32_lds(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
+  return launch_scan_proj<float, false>(a, lds, grid, stream);
+}
+
+}  // namespace rnnk
