@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--placement", type=int, default=0, help="0 auto, 1 flat, 2 XCD-aligned groups")
     ap.add_argument("--weights", type=int, default=0,
                     help="RnnDesc.weights hint: 0 auto, 1 LDS-resident, 2 register-resident")
+    ap.add_argument("--gx-f32", action="store_true",
+                    help="store the hoisted G_x in fp32 also for bf16 workloads (default: the storage dtype)")
     ap.add_argument("--train", action="store_true",
                     help="time a training step (rnn_forward_train + rnn_backward) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -140,7 +142,7 @@ def _hip():
     return h
 
 
-def algorithmic(spec, d):
+def algorithmic(spec, d, gx_f32=False):
     """Algorithmic flops and HBM bytes per launch, by kernel kind and layer."""
     import synth  # noqa: F401
     out = {}
@@ -159,6 +161,7 @@ def algorithmic(spec, d):
     G = gates * H
     K = spec.proj_size if spec.mode == "lstmp" else H
     es = 2 if spec.dtype == "bf16" else 4
+    gs = 4 if gx_f32 else es  # bytes per element of the hoisted G_x
     L = d["lengths"]
     tokens = int(L.sum()) if L is not None else spec.T * spec.B
     rows = tokens if spec.layout == "packed" else spec.T * spec.B
@@ -166,11 +169,11 @@ def algorithmic(spec, d):
     for layer in range(spec.num_layers):
         in_l = spec.input_size if layer == 0 else D * K
         gemms.append({"flops": 2 * rows * D * G * in_l,
-                      "bytes": rows * in_l * es + D * G * in_l * es + rows * D * G * 4, "tokens": tokens})
+                      "bytes": rows * in_l * es + D * G * in_l * es + rows * D * G * gs, "tokens": tokens})
         fl = 2 * tokens * D * G * K
         if spec.mode == "lstmp":
             fl += 2 * tokens * D * spec.proj_size * H
-        scans.append({"flops": fl, "bytes": tokens * D * (G * 4 + K * es), "tokens": tokens})
+        scans.append({"flops": fl, "bytes": tokens * D * (G * gs + K * es), "tokens": tokens})
     out[1] = gemms
     out[2] = scans
     out[4] = scans  # the one-wave-per-row scan does the same work
@@ -214,6 +217,7 @@ def prepare(name, args):
         desc.embed_dim, desc.belief_dim, desc.scale_lb = d["embed_dim"], d["belief_dim"], 0.1
         desc.tile_batch, desc.tile_hidden, desc.placement = args.tile_batch, args.tile_hidden, args.placement
         desc.weights = args.weights
+        desc.gx_dtype = 1 if args.gx_f32 else 0
         wt = gss.RnnWeights()
         wt.w_as, wt.b_as, wt.w_1, wt.b_1, wt.w_2, wt.b_2 = (w[k].data_ptr() for k in
                                                             ("w_as", "b_as", "w_1", "b_1", "w_2", "b_2"))
@@ -237,7 +241,8 @@ def prepare(name, args):
         x = T(d["x"])
         (out, ws) = gss.rnn_forward(spec.mode, x, params, lengths=d["lengths"], layout=spec.layout,
                                     num_layers=spec.num_layers, bidirectional=spec.bidirectional,
-                                    proj_size=spec.proj_size, weights=args.weights, **hints)
+                                    proj_size=spec.proj_size, weights=args.weights,
+                                    gx_dtype="f32" if args.gx_f32 else "auto", **hints)
         y, hn, cn = out
         desc = gss.RnnDesc()
         desc.mode = gss.MODES[spec.mode]
@@ -248,6 +253,7 @@ def prepare(name, args):
         desc.num_layers, desc.bidirectional, desc.has_bias = spec.num_layers, int(spec.bidirectional), 1
         desc.tile_batch, desc.tile_hidden, desc.placement = args.tile_batch, args.tile_hidden, args.placement
         desc.weights = args.weights
+        desc.gx_dtype = 1 if args.gx_f32 else 0
         wt = gss.RnnWeights()
         for i, p in enumerate(params):
             for k, v in p.items():
@@ -261,7 +267,8 @@ def prepare(name, args):
         tokens = int(lengths.sum()) if lengths is not None else spec.T * spec.B
         config = {"workload": name, "mode": spec.mode, "T": spec.T, "B": spec.B, "input": spec.input_size,
                   "hidden": spec.hidden_size, "proj": spec.proj_size, "layers": spec.num_layers,
-                  "bidirectional": spec.bidirectional, "layout": spec.layout, "tokens": tokens}
+                  "bidirectional": spec.bidirectional, "layout": spec.layout, "tokens": tokens,
+                  "gx_dtype": "f32" if (args.gx_f32 or spec.dtype == "f32") else spec.dtype}
     torch.cuda.synchronize()
     return {"name": name, "spec": spec, "d": d, "desc": desc, "wt": wt, "io": io, "ws": ws, "keep": keep,
             "tokens": tokens, "config": config, "lengths": lengths}
@@ -362,7 +369,7 @@ def measure(name, args, rt_us, with_cpu):
         for j in range(2 * max_k):
             hip.hipEventDestroy(arr[j])
     kind_list = [kinds[j] for j in range(min(n_k, max_k))]
-    algo = algorithmic(spec, d)
+    algo = algorithmic(spec, d, getattr(args, "gx_f32", False))
     kernels = []
     seen = {}
     for j, kd in enumerate(kind_list):

@@ -46,7 +46,7 @@ class RnnDesc(ctypes.Structure):
         ("tile_batch", ctypes.c_int32), ("tile_hidden", ctypes.c_int32),
         ("placement", ctypes.c_int32), ("weights", ctypes.c_int32),
         ("clip", ctypes.c_int32), ("cell_clip_lo", ctypes.c_float), ("cell_clip_hi", ctypes.c_float),
-        ("proj_clip", ctypes.c_float), ("actor_dim", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+        ("proj_clip", ctypes.c_float), ("actor_dim", ctypes.c_int32), ("gx_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -313,7 +313,7 @@ def _call(desc, w, io, lengths, device, keep, check_status, noalloc=False):
 def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padded",
                 num_layers=1, bidirectional=False, proj_size=0, hidden_size=None, y_out=None,
                 tile_batch=0, tile_hidden=0, placement=0, weights=0, cell_clip=None, proj_clip=None,
-                return_workspace=False, check_status=True, noalloc=False, _train=False):
+                gx_dtype="auto", return_workspace=False, check_status=True, noalloc=False, _train=False):
     """Forward of an LSTM / GRU / LSTMP stack on the current HIP stream.
 
     x: padded [T, B, F] or packed [N_tok, F] (float32 or bfloat16, on a GPU).
@@ -323,6 +323,8 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     masks rows, which are then never written past their length).
     cell_clip: c (clamp to [-c, c]) or (lo, hi), clamps the updated LSTM cell
     state; proj_clip: p, clamps the LSTMP projected output to [-p, p].
+    gx_dtype: "auto" stores the hoisted input projection in x's dtype, "f32"
+    always in fp32.
     check_status (default True): wait for the stream after the call and
     raise RnnError if the device reported a failure (a persistent group whose
     workgroups were not all resident ends with RNN_E_TIMEOUT and leaves the
@@ -406,6 +408,9 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     desc.num_layers, desc.bidirectional, desc.has_bias = num_layers, int(bidirectional), int(has_bias)
     desc.tile_batch, desc.tile_hidden, desc.placement = tile_batch, tile_hidden, placement
     desc.weights = weights
+    if gx_dtype not in ("auto", "f32"):
+        raise ValueError("gx_dtype must be 'auto' or 'f32'")
+    desc.gx_dtype = 1 if gx_dtype == "f32" else 0
     if cell_clip is not None:
         lo, hi = (-cell_clip, cell_clip) if isinstance(cell_clip, (int, float)) else cell_clip
         desc.clip |= CLIP_CELL

@@ -103,7 +103,7 @@ __device__ __forceinline__ float fold_bias(const GemmArgs& a, int n) {
 // tile goes: the output with the bias fold, or its partial buffer.
 struct KRange {
   int kt0, kt1;
-  float* C;
+  void* C;
   bool with_bias;
 };
 __device__ __forceinline__ KRange k_range(const GemmArgs& a, int nk) {
@@ -117,9 +117,27 @@ constexpr int kEpiStride = 136;
 constexpr int kEpiBytes = 64 * kEpiStride * 4;  // 34816
 static_assert(kEpiBytes <= 2 * 2 * kTileBytes, "epilogue staging exceeds the operand buffers");
 
+// Four outputs as bf16 (round to nearest even), one 8-byte store.
+__device__ __forceinline__ void store4_bf16(bf16* dst, const f32x4& v, bool vec, int valid) {
+  if (vec) {
+    uint32_t w[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      w[e] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[2 * e]) |
+             (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[2 * e + 1]) << 16;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(dst));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < valid) dst[e] = (bf16)v[e];
+  }
+}
+
 template <typename DT>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[2][2], float* lds, int m0, int n0,
-                                           float* C, bool with_bias) {
+                                           void* Cv, bool with_bias) {
+  const bool out_bf16 = with_bias && a.c_bf16;  // partial tiles stay fp32
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, half = lane >> 5, l32 = lane & 31;
   const int c4 = tid & 31, rbase = tid >> 5;  // this thread's 16-byte column chunk and first row
@@ -131,7 +149,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[2][2
       if (n + e < a.N) bias[e] = fold_bias<DT>(a, n + e);
     }
   }
-  const bool vec = (a.N & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0 && n + 4 <= a.N;
+  const bool vec = (a.N & 3) == 0 && (reinterpret_cast<uintptr_t>(Cv) & 15) == 0 && n + 4 <= a.N;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     if (p) __syncthreads();  // the first pass's reads are done
@@ -153,7 +171,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, f32x16 (&acc)[2][2
       f32x4 v = *reinterpret_cast<const f32x4*>(lds + r * kEpiStride + 4 * c4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += bias[e];
-      float* dst = C + (size_t)m * a.N + n;
+      if (out_bf16) {
+        store4_bf16(reinterpret_cast<bf16*>(Cv) + (size_t)m * a.N + n, v, vec, a.N - n);
+        continue;
+      }
+      float* dst = reinterpret_cast<float*>(Cv) + (size_t)m * a.N + n;
       if (vec) {
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
       } else {
@@ -415,13 +437,20 @@ __global__ void __launch_bounds__(256) gemm_xw_reduce_kernel(GemmArgs a) {
       const int n = (int)(i % a.N);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += fold_bias<DT>(a, n + e);
-      *reinterpret_cast<f32x4*>(a.C + i) = v;
+      if (a.c_bf16)
+        store4_bf16(reinterpret_cast<bf16*>(a.C) + i, v, true, 4);
+      else
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.C) + i) = v;
     }
   } else {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
       float v = a.part[i];
       for (int s = 1; s < a.splits; ++s) v += a.part[s * plane + i];
-      a.C[i] = v + fold_bias<DT>(a, (int)(i % a.N));
+      v += fold_bias<DT>(a, (int)(i % a.N));
+      if (a.c_bf16)
+        reinterpret_cast<bf16*>(a.C)[i] = (bf16)v;
+      else
+        reinterpret_cast<float*>(a.C)[i] = v;
     }
   }
 }

@@ -12,7 +12,8 @@ struct GemmArgs {
   const void* W[2];     // per direction [G, K]
   const void* b_ih[2];  // per direction [G] (has_bias)
   const void* b_hh[2];  // per direction [G] (has_bias)
-  float* C;             // [M, N] fp32, N = D * G
+  void* C;              // [M, N], N = D * G: fp32, or bf16 when c_bf16
+  int c_bf16;           // store C (with the bias fold) as bf16
   int M, N, K, G;
   int hh_fold_rows;     // b_hh folded for gate rows < this (G, or 2H for GRU)
   int has_bias;
@@ -72,7 +73,8 @@ struct ScanArgs {
   const void* c0[2];   // [B, H] or null
   void* h_n[2];        // [B, K] or null
   void* c_n[2];        // [B, H] or null
-  const float* gx;     // [rows, D * G]
+  const void* gx;      // [rows, D * G] fp32, or bf16 when gx_bf16
+  int gx_bf16;
   void* y;             // [rows, D * K]
   const int* lengths;  // device [B] or null (all T)
   const int* offsets;  // device [T + 1] (packed)

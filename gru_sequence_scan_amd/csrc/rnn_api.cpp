@@ -76,6 +76,7 @@ int validate_desc(const RnnDesc* d) {
   if (!d) return RNN_E_NULL;
   for (int r : d->reserved)
     if (r != 0) return RNN_E_SHAPE;
+  if (d->gx_dtype != RNN_GX_AS_DTYPE && d->gx_dtype != RNN_GX_F32) return RNN_E_SHAPE;
   if (d->placement < 0 || d->placement > 2) return RNN_E_SHAPE;
   if (d->weights < 0 || d->weights > 2) return RNN_E_SHAPE;
   if (d->dtype != RNN_DTYPE_F32 && d->dtype != RNN_DTYPE_BF16) return RNN_E_UNSUPPORTED;
@@ -90,6 +91,7 @@ int validate_desc(const RnnDesc* d) {
     if (d->state_dim < 1 || d->action_dim < 1 || d->embed_dim < 1 || d->belief_dim < 1) return RNN_E_SHAPE;
     if (!std::isfinite(d->scale_lb)) return RNN_E_SHAPE;
     if (d->clip != 0) return RNN_E_UNSUPPORTED;
+    if (d->gx_dtype != RNN_GX_AS_DTYPE) return RNN_E_UNSUPPORTED;  // no hoisted G_x
     const double big = (double)d->B * d->T * std::max({d->state_dim, d->belief_dim, d->action_dim});
     if (big > 2e9) return RNN_E_SHAPE;
     const double wa1 = (double)d->actor_dim * (d->state_dim + d->belief_dim);
@@ -178,6 +180,15 @@ Dims dims_of(const RnnDesc* d, long long n_tok) {
 // (E, padded to 4), then the actor's W_a1[:, S:] h (Ea, padded to 4).
 int rssm_ex_cols(const RnnDesc* d) { return rup(d->embed_dim, 4) + rup(d->actor_dim, 4); }
 
+bool use_wave_scan(const RnnDesc* d, const Dims& m);
+
+// Bytes per element of the hoisted G_x: the storage dtype's unless fp32 is
+// requested, or the one-wave scan runs the layer (its G_x reads are one
+// word per lane per step, where bf16 saves nothing and costs the widening).
+int gx_esize(const RnnDesc* d, const Dims& m) {
+  return d->dtype == RNN_DTYPE_BF16 && d->gx_dtype == RNN_GX_AS_DTYPE && !use_wave_scan(d, m) ? 2 : 4;
+}
+
 // Per-layer exchange regions of the forward scan (aligned sizes, so the
 // layers' regions stay aligned).
 size_t xid_layer_bytes() { return align_up((size_t)kScanMaxWorkgroups * 4, kAlign); }
@@ -215,7 +226,8 @@ WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
   w.counters = take(w.counters_bytes);
   w.n_ints = has_lengths ? d->B + d->T + 1 : 0;
   w.ints = take((size_t)std::max(w.n_ints, 1) * 4);
-  w.gx = take((size_t)m.rows * m.D * m.G * 4);
+  // (16 bytes of slack: a bf16 element is read with the aligned word that holds it)
+  w.gx = take((size_t)m.rows * m.D * m.G * gx_esize(d, m) + 16);
   const size_t inter = (size_t)m.rows * m.D * m.K * m.esize;
   w.inter0 = d->num_layers > 1 ? take(inter) : 0;
   w.inter1 = d->num_layers > 2 ? take(inter) : 0;
@@ -711,7 +723,8 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     for (int l = 0; l + 1 < d->num_layers; ++l)
       if ((rc = hip_status(launch_fill_zero(rsv + RL.y[l], (size_t)m.rows * m.D * m.K * 4, st))) != RNN_OK)
         return rc;
-  float* gx = (float*)(ws + L.gx);
+  void* gx = ws + L.gx;
+  const int gx_bf16 = !wave && gx_esize(d, m) == 2;
   const void* layer_in = io->x;
   for (int l = 0; l < d->num_layers; ++l) {
     const int in_l = l == 0 ? d->input_size : m.D * m.K;
@@ -725,6 +738,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     g.hh_fold_rows = d->mode == RNN_MODE_GRU ? 2 * d->hidden_size : m.G;
     g.has_bias = d->has_bias;
     g.C = gx;
+    g.c_bf16 = gx_bf16;
     bool vec = (size_t)in_l * es % 16 == 0 && aligned(layer_in, 16);
     for (int di = 0; di < m.D; ++di) {
       const int i = l * m.D + di;
@@ -768,6 +782,7 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
       a.c_n[di] = (d->mode != RNN_MODE_GRU && io->c_n) ? (char*)io->c_n + (size_t)i * d->B * d->hidden_size * es : nullptr;
     }
     a.gx = gx;
+    a.gx_bf16 = gx_bf16;
     a.y = layer_out;
     a.rsv = rsv ? (float*)(rsv + RL.gates[l]) : nullptr;
     a.lengths = dev_len;

@@ -1,10 +1,10 @@
-// Kernel 2 instances: bf16 elements, W_hh slices in registers.
+// Kernel 2 instances: bf16 elements and fp32 G_x, W_hh slices in registers.
 #include "scan_kernel.hpp"
 
 namespace rnnk {
 
 hipError_t launch_scan_bf16_reg(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
-  return launch_scan_proj<bf16, true>(a, lds, grid, stream);
+  return launch_scan_proj<bf16, true, false>(a, lds, grid, stream);
 }
 
 }  // namespace rnnk

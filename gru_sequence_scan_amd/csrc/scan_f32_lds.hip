@@ -4,7 +4,7 @@
 namespace rnnk {
 
 hipError_t launch_scan_f32_lds(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
-  return launch_scan_proj<float, false>(a, lds, grid, stream);
+  return launch_scan_proj<float, false, false>(a, lds, grid, stream);
 }
 
 }  // namespace rnnk

@@ -27,6 +27,8 @@
 // t = L_b - 1 from h0. A group stops once none of its rows is active.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "scan_common.hpp"
@@ -291,7 +293,8 @@ __device__ __forceinline__ void reduce_ksplit(const float* red, int rks, int row
 
 // EPT: gate elements (and, for LSTMP, projection outputs) owned per thread,
 // 1, 2 or 4 (bb * hs <= 256 * EPT). PROJ: LSTMP (the hidden projection).
-template <typename DT, bool WREG, int EPT, bool PROJ>
+// GXB: G_x stored as bf16 (bf16 storage only).
+template <typename DT, bool WREG, int EPT, bool PROJ, bool GXB>
 __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const ScanLds L = scan_lds(a, (int)sizeof(DT));
@@ -489,23 +492,37 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   constexpr uint32_t kOob = 0x7FFFFFF0u;
   const uint32_t es = sizeof(DT);
 
-  // G_x of the owned elements for loop step k1 (zero for inactive ones).
-  auto prefetch = [&](int k1, float (&g)[EPT][4]) __attribute__((always_inline)) {
+  // G_x of the owned elements for loop step k1 (zero for inactive ones), as
+  // raw words (GXB: 16-bit loads of bf16 G_x, else 32-bit), widened by gxf
+  // where the gate math uses them: widening here would make every load
+  // wait at once. For the 16-bit loads the offsets pass through an opaque
+  // copy: the select with a constant arm is otherwise split into two loads
+  // on divergent branches, which both issue when lanes differ and leave the
+  // compiler's count of younger loads short, so the poll check would wait
+  // for some G_x loads (for the 32-bit loads the split measured faster).
+  typedef typename std::conditional<GXB, uint16_t, uint32_t>::type GxW;
+  constexpr uint32_t gsz = sizeof(GxW);
+  auto prefetch = [&](int k1, uint32_t (&g)[EPT][4]) __attribute__((always_inline)) {
     const bool in = k1 < nsteps;
     const int t1 = in ? t_of(k1) : 0;
-    const __amdgpu_buffer_rsrc_t g_rs =
-        make_rsrc(a.gx + (size_t)rowbase_of(t1) * DG, (uint32_t)(a.B * DG) * 4u);
+    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(
+        reinterpret_cast<const char*>(a.gx) + (size_t)rowbase_of(t1) * DG * gsz, (uint32_t)(a.B * DG) * gsz);
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const bool act = in && t1 < lenreg[i];
       const uint32_t e0 = (uint32_t)((b0 + er[i]) * DG + d * a.G + j0 + eu[i]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t off = act && q < gates ? (e0 + (uint32_t)(q * a.H)) * 4u : kOob;
-        g[i][q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(g_rs, (int)off, 0, 0));
+        uint32_t off = act && q < gates ? (e0 + (uint32_t)(q * a.H)) * gsz : kOob;
+        if constexpr (GXB) asm volatile("" : "+v"(off));
+        if constexpr (GXB)
+          g[i][q] = __builtin_amdgcn_raw_buffer_load_b16(g_rs, (int)off, 0, 0);
+        else
+          g[i][q] = __builtin_amdgcn_raw_buffer_load_b32(g_rs, (int)off, 0, 0);
       }
     }
   };
+  auto gxf = [&](uint32_t w) __attribute__((always_inline)) { return __builtin_bit_cast(float, GXB ? w << 16 : w); };
   // Output y of loop step kp, whose h is still in hreg (for LSTMP: whose
   // projected h is still in acc). h_n and c_n are written after the loop.
   auto outputs = [&](int kp) __attribute__((always_inline)) {
@@ -537,7 +554,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   // One loop step. gc holds this step's G_x; the next step's goes to gn and
   // is moved to gc once the gate math is done (before the ring stores, so
   // the move waits for nothing issued after the loads).
-  float gc[EPT][4], gn[EPT][4];
+  uint32_t gc[EPT][4], gn[EPT][4];
   float hlast[EPT];  // LSTMP: last projected h of each owned output (for h_n)
 #pragma unroll
   for (int i = 0; i < EPT; ++i) hlast[i] = 0.f;
@@ -595,20 +612,20 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
       if (t >= lenreg[i]) continue;
       const float* ar = acc + r * L.acc_ld;
       if (a.mode == kGRU) {
-        const float rg = fsigmoid(gc[i][0] + ar[u]);
-        const float zg = fsigmoid(gc[i][1] + ar[a.hs + u]);
+        const float rg = fsigmoid(gxf(gc[i][0]) + ar[u]);
+        const float zg = fsigmoid(gxf(gc[i][1]) + ar[a.hs + u]);
         const float hn_pre = ar[2 * a.hs + u] + bhn[i];
-        const float ng = ftanh(gc[i][2] + rg * hn_pre);
+        const float ng = ftanh(gxf(gc[i][2]) + rg * hn_pre);
         gsv[i][0] = rg;
         gsv[i][1] = zg;
         gsv[i][2] = ng;
         gsv[i][3] = hn_pre;
         hreg[i] = (1.f - zg) * ng + zg * hreg[i];
       } else {
-        const float ig = fsigmoid(gc[i][0] + ar[u]);
-        const float fg = fsigmoid(gc[i][1] + ar[a.hs + u]);
-        const float gg = ftanh(gc[i][2] + ar[2 * a.hs + u]);
-        const float og = fsigmoid(gc[i][3] + ar[3 * a.hs + u]);
+        const float ig = fsigmoid(gxf(gc[i][0]) + ar[u]);
+        const float fg = fsigmoid(gxf(gc[i][1]) + ar[a.hs + u]);
+        const float gg = ftanh(gxf(gc[i][2]) + ar[2 * a.hs + u]);
+        const float og = fsigmoid(gxf(gc[i][3]) + ar[3 * a.hs + u]);
         const float c = clampf(fg * creg[i] + ig * gg, a.c_lo, a.c_hi);
         gsv[i][0] = ig;
         gsv[i][1] = fg;
@@ -731,28 +748,29 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
 
 
 // Launch of one instance: EPT from the owned elements, PROJ from the mode.
-template <typename DT, bool WREG, int EPT, bool PROJ>
+template <typename DT, bool WREG, int EPT, bool PROJ, bool GXB>
 hipError_t launch_scan_as(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<DT, WREG, EPT, PROJ>,
+  hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<DT, WREG, EPT, PROJ, GXB>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((scan_kernel<DT, WREG, EPT, PROJ>), grid, dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((scan_kernel<DT, WREG, EPT, PROJ, GXB>), grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
-template <typename DT, bool WREG, bool PROJ>
+template <typename DT, bool WREG, bool PROJ, bool GXB>
 hipError_t launch_scan_ept(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
   const int own = max(a.bb * a.hs, PROJ ? a.bb * a.ps : 0);
-  if (own <= kThreads) return launch_scan_as<DT, WREG, 1, PROJ>(a, lds, grid, stream);
-  if (own <= 2 * kThreads) return launch_scan_as<DT, WREG, 2, PROJ>(a, lds, grid, stream);
-  if (own <= kMaxEpt * kThreads) return launch_scan_as<DT, WREG, kMaxEpt, PROJ>(a, lds, grid, stream);
+  if (own <= kThreads) return launch_scan_as<DT, WREG, 1, PROJ, GXB>(a, lds, grid, stream);
+  if (own <= 2 * kThreads) return launch_scan_as<DT, WREG, 2, PROJ, GXB>(a, lds, grid, stream);
+  if (own <= kMaxEpt * kThreads) return launch_scan_as<DT, WREG, kMaxEpt, PROJ, GXB>(a, lds, grid, stream);
   return hipErrorInvalidValue;
 }
 
-template <typename DT, bool WREG>
+// bf16 G_x only with bf16 storage.
+template <typename DT, bool WREG, bool GXB>
 hipError_t launch_scan_proj(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
-  return a.mode == kLSTMP ? launch_scan_ept<DT, WREG, true>(a, lds, grid, stream)
-                          : launch_scan_ept<DT, WREG, false>(a, lds, grid, stream);
+  return a.mode == kLSTMP ? launch_scan_ept<DT, WREG, true, GXB>(a, lds, grid, stream)
+                          : launch_scan_ept<DT, WREG, false, GXB>(a, lds, grid, stream);
 }
 
 }  // namespace

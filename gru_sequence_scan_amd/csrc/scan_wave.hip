@@ -83,7 +83,9 @@ __global__ void __launch_bounds__(kWaveThreads) scan_wave_kernel(ScanArgs a) {
   auto t_of = [&](int k) { return rev ? n - 1 - k : k; };
   auto gx_at = [&](int k) -> float {  // Gx of step k (clamped into the sequence)
     const int t = t_of(k < n ? k : n - 1);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.gx + ((size_t)(row_of(t) + b) * DG + d * G), (uint32_t)G * 4u);
+    // (fp32 G_x: the host keeps G_x in fp32 for layers this kernel runs)
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const float*>(a.gx) + ((size_t)(row_of(t) + b) * DG + d * G), (uint32_t)G * 4u);
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0));
   };
   DT* y = reinterpret_cast<DT*>(a.y);

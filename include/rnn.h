@@ -175,8 +175,16 @@ typedef struct RnnDesc {
   float proj_clip;
   int32_t actor_dim;     /* RSSM_ACTOR: hidden width Ea of the actor MLP (>= 1);
                             must be 0 in every other mode                     */
-  int32_t reserved[3];   /* must be zero                                       */
+  int32_t gx_dtype;      /* storage of the hoisted input projection G_x (LSTM,
+                            GRU, LSTMP): RNN_GX_AS_DTYPE (0) in the storage
+                            dtype (bf16 for bf16 storage: the product is
+                            accumulated in fp32 and rounded once), RNN_GX_F32
+                            (1) in fp32; must be 0 in the RSSM modes          */
+  int32_t reserved[2];   /* must be zero                                       */
 } RnnDesc;
+
+#define RNN_GX_AS_DTYPE 0
+#define RNN_GX_F32 1
 
 #define RNN_CLIP_CELL 1
 #define RNN_CLIP_PROJ 2

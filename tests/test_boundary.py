@@ -193,9 +193,35 @@ def test_actor_exchange_is_larger(lib):
 
 
 def test_reserved_fields_must_be_zero(lib):
+    for i in range(2):
+        d = _desc()
+        d.reserved[i] = 1
+        assert _ws(d)[0] == E_SHAPE
+
+
+def test_gx_dtype_values(lib):
+    """G_x storage: 0 follows the storage dtype, 1 forces fp32; anything else
+    is a shape error, and the RSSM modes (no hoisted product) reject it."""
     d = _desc()
-    d.reserved[2] = 1
+    d.gx_dtype = 2
     assert _ws(d)[0] == E_SHAPE
+    d = _desc(mode=3, **RSSM_KW)
+    d.gx_dtype = 1
+    assert _ws(d)[0] == E_UNSUPPORTED
+
+
+def test_bf16_gx_halves_the_gate_buffer(lib):
+    """bf16 storage keeps G_x in bf16 unless fp32 is requested: the workspace
+    shrinks by half the G_x buffer (rows * D * G * 2 bytes, give or take the
+    256-byte section alignment)."""
+    kw = dict(mode=1, dtype=1, T=20, B=8, input_size=16, hidden_size=32)
+    st0, n_bf = _ws(_desc(**kw))
+    d = _desc(**kw)
+    d.gx_dtype = 1
+    st1, n_f32 = _ws(d)
+    assert st0 == st1 == OK
+    half = 20 * 8 * 3 * 32 * 2
+    assert abs((n_f32 - n_bf) - half) <= 256
 
 
 def test_null_desc(lib):

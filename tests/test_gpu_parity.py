@@ -67,7 +67,39 @@ SMALL = [
     ("gru_splitk_bf16", "gru", "bf16", 6, 5, 300, 40, 0, 1, False, "padded", None, True, True),
     ("lstm_splitk_pipe", "lstm", "f32", 4, 9, 256, 72, 0, 1, False, "padded", None, True, False),
     ("bilstm_splitk_packed", "lstm", "f32", 7, 6, 160, 96, 0, 2, True, "packed", (1, 7), True, True),
+    # bf16 G_x rows of odd width (3H with H odd): a step's rows start at a
+    # 2-byte offset; and the one-wave kernel on bf16 storage (G = 63)
+    ("gru_odd_bf16", "gru", "bf16", 9, 18, 24, 33, 0, 1, False, "padded", None, True, True),
+    ("gru_wave_bf16", "gru", "bf16", 11, 3, 8, 21, 0, 1, False, "padded", None, True, True),
 ]
+
+
+def _small_inputs(case):
+    name, mode, dt, T, B, F, H, P, L, bidir, layout, varlen, bias, state = case
+    lengths = None
+    vl = None
+    if varlen == "unsorted":
+        lengths = np.random.default_rng(7).integers(1, T + 1, size=B).astype(np.int32)
+        lengths[3] = T
+    elif varlen is not None:
+        vl = varlen
+    return synth.make_rnn_inputs(mode, T, B, F, H, proj_size=P, num_layers=L, bidirectional=bidir,
+                                 dtype=dt, layout=layout, lengths=lengths, varlen=vl,
+                                 w_scale=1.0 / np.sqrt(H), bias=bias, seed=zlib.crc32(name.encode()) % 1000,
+                                 h0_std=0.3 if state else 0.0, c0_std=0.3 if state else 0.0)
+
+
+GX_F32 = ["gru_bf16", "lstmp_bf16", "bigru_packed_bf16", "gru_odd_bf16"]
+
+
+@pytest.mark.parametrize("name", GX_F32)
+def test_bf16_storage_with_fp32_gx(name):
+    """bf16 storage with the hoisted product kept in fp32 (gx_dtype="f32")."""
+    case = next(c for c in SMALL if c[0] == name)
+    log(f"[gpu] small case {name}, fp32 G_x")
+    d = _small_inputs(case)
+    got = run_rnn(d, y_fill=float("nan"), gx_dtype="f32")
+    _compare(d, got, _oracle(d), name + " (fp32 G_x)")
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
