@@ -44,30 +44,29 @@ HEADLINE = "rssm_b50_t50"
 CSRC = os.path.join(ROOT, "gru_sequence_scan_amd", "csrc")
 KERNEL_SOURCES = {
     "gemm_xw": ["gemm_xw.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
-    "scan": ["scan.hip", "scan_common.hpp", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
-    "rssm": ["rssm.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
+    "scan": ["scan.hip", "scan_kernel.hpp", "scan_common.hpp", "scan_bf16_reg.hip", "scan_bf16_lds.hip",
+             "scan_bf16gx_reg.hip", "scan_bf16gx_lds.hip", "scan_f32_reg.hip", "scan_f32_lds.hip",
+             "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
+    "rssm": ["rssm.hip", "rssm2.hip", "rssm_common.hpp", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
     "scan_wave": ["scan_wave.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
 }
 
 # HBM bytes per launch of a workload's dominant kernel, from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE), each divided by
 # the ratio the same counter reads for a plain copy of known size
-# (--calibrate-copy). Valid only for the kernel sources they were taken on.
+# (--calibrate-copy), and the same kernel's MFMA and LDS counters
+# ("counters": MFMA FLOP executed, MFMA busy share of the 1024 SIMDs, LDS
+# active share of the 256 CUs, bank-conflict cycles per LDS-active cycle)
+# with those of the first input GEMM ("gemm_counters"). Valid only for the
+# kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 186313269, "write_bytes": 25801344,
-                  "sources": "0e4a066d23eb9b61"},
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1604093, "write_bytes": 209408,
-                  "sources": "3f354d56f448965b"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 484489305, "write_bytes": 137109504,
-                  "sources": "3f354d56f448965b"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": 1, "fetch_bytes": 612697552, "write_bytes": 118933504,
-                  "sources": "3f354d56f448965b"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 430868463, "write_bytes": 162342912,
-                  "sources": "3f354d56f448965b"},
-    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 89032, "write_bytes": 16512,
-                  "sources": "b8254d84c30cf6bc"},
-    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347863479, "write_bytes": 59181414,
-                  "sources": "0e4a066d23eb9b61"},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 9898338, "write_bytes": 3564000, "sources": "52f6c92e145ab8a3", "counters": {"mfma_flops": 4199424000, "mfma_busy": 0.07796, "lds_active": 0.07389, "lds_bank_conflict": 0.07161}},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1476791, "write_bytes": 88576, "sources": "d624821b153aaffe", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 0.00422, "lds_bank_conflict": 0.0}, "gemm_counters": {"mfma_flops": 134217728, "mfma_busy": 0.0465, "lds_active": 0.00668, "lds_bank_conflict": 0.0}, "gemm_sources": "ec46422efff7389b"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 215440119, "write_bytes": 68427776, "sources": "d624821b153aaffe", "counters": {"mfma_flops": 137438953472, "mfma_busy": 0.05473, "lds_active": 0.10173, "lds_bank_conflict": 0.33589}, "gemm_counters": {"mfma_flops": 103079215104, "mfma_busy": 0.25933, "lds_active": 0.43716, "lds_bank_conflict": 0.2963}, "gemm_sources": "ec46422efff7389b"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": 0, "fetch_bytes": 267927065, "write_bytes": 16795648, "sources": "d624821b153aaffe", "counters": {"mfma_flops": 100663296000, "mfma_busy": 0.00562, "lds_active": 0.02485, "lds_bank_conflict": 0.31987}, "gemm_counters": {"mfma_flops": 83886080000, "mfma_busy": 0.21039, "lds_active": 0.37412, "lds_bank_conflict": 0.27778}, "gemm_sources": "ec46422efff7389b"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 351826879, "write_bytes": 80773120, "sources": "d624821b153aaffe", "counters": {"mfma_flops": 95093260288, "mfma_busy": 0.2607, "lds_active": 0.08959, "lds_bank_conflict": 0.40563}, "gemm_counters": {"mfma_flops": 40802189312, "mfma_busy": 0.72956, "lds_active": 0.06262, "lds_bank_conflict": 0.0}, "gemm_sources": "ec46422efff7389b"},
+    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 89032, "write_bytes": 16512, "sources": "58978e0d28e6f30c", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 5e-05, "lds_bank_conflict": 0.0}, "gemm_counters": {"mfma_flops": 1048576, "mfma_busy": 0.00036, "lds_active": 0.00016, "lds_bank_conflict": 0.0}, "gemm_sources": "ec46422efff7389b"},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347691609, "write_bytes": 56108557, "sources": "52f6c92e145ab8a3", "counters": {"mfma_flops": 7234560000, "mfma_busy": 0.08346, "lds_active": 0.11099, "lds_bank_conflict": 0.1031}},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
@@ -402,6 +401,11 @@ def measure(name, args, rt_us, with_cpu):
     if meas and traffic is not None:
         roofline["traffic_fetch"] = meas["fetch_bytes"]
         roofline["traffic_write"] = meas["write_bytes"]
+        # MFMA and LDS counters of the same kernel (rocprofv3 --pmc, same rule)
+        if "counters" in meas:
+            roofline["counters"] = meas["counters"]
+    if meas and "gemm_counters" in meas and meas.get("gemm_sources") == sources_digest("gemm_xw"):
+        roofline["gemm_counters"] = meas["gemm_counters"]
 
     # The recurrence kernel's steps, time per step and cross-CU exchanges per
     # step; its on-chip term; the fraction against the compute units the
