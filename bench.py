@@ -35,7 +35,10 @@ PEAK_HBM_GBS = 8000.0
 PEAK_LDS_GBS = 128 * 256 * 2.4
 PEAK_TFLOPS = {"bf16": 2500.0, "f32_mfma": 157.3, "f32_vector": 157.3}
 
-KIND_NAMES = {1: "gemm_xw", 2: "scan", 3: "rssm", 4: "scan_wave"}
+# kernel kinds reported by rnn_forward_profiled (kind | layer << 8; kind 5, a
+# launch scanning a time chunk of several stacked layers: first layer | last
+# layer << 4)
+KIND_NAMES = {1: "gemm_xw", 2: "scan", 3: "rssm", 4: "scan_wave", 5: "scan"}
 METRIC = "timestep\u00b7batch/s per RNN config; % of MFMA / on-chip BW roofline"
 UNIT = "timestep\u00b7batch/s"
 HEADLINE = "rssm_b50_t50"
@@ -93,6 +96,8 @@ def parse():
     ap.add_argument("--placement", type=int, default=0, help="0 auto, 1 flat, 2 XCD-aligned groups")
     ap.add_argument("--weights", type=int, default=0,
                     help="RnnDesc.weights hint: 0 auto, 1 LDS-resident, 2 register-resident")
+    ap.add_argument("--layer-pipeline", default="auto", choices=["auto", "off", "on"],
+                    help="multi-layer stacks: scan the layers' time chunks together (auto: where modelled faster)")
     ap.add_argument("--gx-f32", action="store_true",
                     help="store the hoisted G_x in fp32 also for bf16 workloads (default: the storage dtype)")
     ap.add_argument("--train", action="store_true",
@@ -241,7 +246,8 @@ def prepare(name, args):
         (out, ws) = gss.rnn_forward(spec.mode, x, params, lengths=d["lengths"], layout=spec.layout,
                                     num_layers=spec.num_layers, bidirectional=spec.bidirectional,
                                     proj_size=spec.proj_size, weights=args.weights,
-                                    gx_dtype="f32" if args.gx_f32 else "auto", **hints)
+                                    gx_dtype="f32" if args.gx_f32 else "auto",
+                                    layer_pipeline=args.layer_pipeline, **hints)
         y, hn, cn = out
         desc = gss.RnnDesc()
         desc.mode = gss.MODES[spec.mode]
@@ -253,6 +259,7 @@ def prepare(name, args):
         desc.tile_batch, desc.tile_hidden, desc.placement = args.tile_batch, args.tile_hidden, args.placement
         desc.weights = args.weights
         desc.gx_dtype = 1 if args.gx_f32 else 0
+        desc.layer_pipeline = gss.PIPE_MODES[args.layer_pipeline]
         wt = gss.RnnWeights()
         for i, p in enumerate(params):
             for k, v in p.items():
@@ -267,7 +274,8 @@ def prepare(name, args):
         config = {"workload": name, "mode": spec.mode, "T": spec.T, "B": spec.B, "input": spec.input_size,
                   "hidden": spec.hidden_size, "proj": spec.proj_size, "layers": spec.num_layers,
                   "bidirectional": spec.bidirectional, "layout": spec.layout, "tokens": tokens,
-                  "gx_dtype": "f32" if (args.gx_f32 or spec.dtype == "f32") else spec.dtype}
+                  "gx_dtype": "f32" if (args.gx_f32 or spec.dtype == "f32") else spec.dtype,
+                  "layer_pipeline": args.layer_pipeline}
     torch.cuda.synchronize()
     return {"name": name, "spec": spec, "d": d, "desc": desc, "wt": wt, "io": io, "ws": ws, "keep": keep,
             "tokens": tokens, "config": config, "lengths": lengths}
@@ -313,7 +321,7 @@ def measure(name, args, rt_us, with_cpu):
                                          ctypes.POINTER(gss.RnnIO), ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
-    max_k = 8
+    max_k = 256
     ws_ptr, ws_n = ws.data_ptr(), ws.numel()
 
     def step(evs=None, kinds=None, nk=None):
@@ -367,19 +375,33 @@ def measure(name, args, rt_us, with_cpu):
     for arr in ev_arrays:
         for j in range(2 * max_k):
             hip.hipEventDestroy(arr[j])
-    kind_list = [kinds[j] for j in range(min(n_k, max_k))]
+    if n_k > max_k:
+        raise RuntimeError(f"{name}: {n_k} kernels per forward, more than the {max_k} timed")
+    kind_list = [kinds[j] for j in range(n_k)]
     algo = algorithmic(spec, d, getattr(args, "gx_f32", False))
+    # One entry per (kernel kind, layer): a pipelined stack launches a G_x
+    # product per layer and time chunk and one scan per wave over several
+    # layers (kind 5, taken together as one entry); an entry's figures are
+    # per launch (its algorithmic work and time over its launch count).
+    groups = {}
+    for j, kw in enumerate(kind_list):
+        kd, lay = kw & 0xFF, kw >> 8
+        groups.setdefault((2, -1) if kd == 5 else (kd, lay), []).append(j)
     kernels = []
-    seen = {}
-    for j, kd in enumerate(kind_list):
-        idx = seen.get(kd, 0)
-        seen[kd] = idx + 1
-        a = algo[kd][idx]
-        v = np.asarray(per_kernel[j]) * 1e3
-        kernels.append({"kernel": KIND_NAMES[kd], "index": idx, "avg_us": float(v.mean()),
+    for (kd, lay), js in groups.items():
+        if lay < 0:
+            a = {"flops": sum(x["flops"] for x in algo[2]), "bytes": sum(x["bytes"] for x in algo[2])}
+            index = f"0-{spec.num_layers - 1}"
+        else:
+            a = algo[kd][lay]
+            index = lay
+        tot = np.sum([np.asarray(per_kernel[j]) for j in js], axis=0) * 1e3  # us per forward
+        v = tot / len(js)
+        kernels.append({"kernel": KIND_NAMES[kd], "index": index, "launches": len(js),
+                        "total_us": float(tot.mean()), "avg_us": float(v.mean()),
                         "median_us": float(np.median(v)), "min_us": float(v.min()),
-                        "flops": a["flops"], "bytes": a["bytes"]})
-    dom = max(kernels, key=lambda k: k["avg_us"])
+                        "flops": a["flops"] / len(js), "bytes": a["bytes"] / len(js)})
+    dom = max(kernels, key=lambda k: k["total_us"])
     achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
     if dom["kernel"] == "scan_wave" or (dom["kernel"] == "scan" and spec.B < 16):
         # the small-batch scans run their products on the vector ALUs
@@ -417,24 +439,38 @@ def measure(name, args, rt_us, with_cpu):
         n_rec = int(lengths.max()) if lengths is not None else spec.T
         layer_dirs = spec.num_layers * (2 if spec.bidirectional else 1)
     plan = gss.rnn_plan_info(desc, lengths)
+    piped = isinstance(dom["index"], str)  # one scan launch per wave of chunks
+    slots = spec.num_layers if plan.get("pipe_chunk", 0) else 1
     if plan["kernel"] == 4:
         bars, occ = 0, min(256, plan["workgroups"])
     else:
         members = plan["members"]
         lstmp = spec.mode == "lstmp"
         bars = 0 if (members == 1 and not lstmp) else (2 if lstmp else 1)  # exchanges per step
-        occ = min(256, plan["workgroups"])
+        dirs = 1 if plan["kernel"] == 3 else (2 if spec.bidirectional else 1)
+        occ = min(256, plan["groups"] * dirs * members * slots)  # workgroups that do work
     if dom["kernel"] == "gemm_xw":
         occ = 256
     ob = onchip_bytes(spec, d, plan) if dom["kernel"] in ("scan", "rssm", "scan_wave") else 0
+    rec_us = dom["avg_us"]
+    if piped:
+        # the waves walk chunk-length steps in sequence, the layers side by side
+        ch, L = plan["pipe_chunk"], spec.num_layers
+        n = -(-spec.T // ch)
+        n_rec = sum(max(min(ch, spec.T - c * ch) for c in range(max(0, w - L + 1), min(n - 1, w) + 1))
+                    for w in range(n + L - 1))
+        ob = ob * L / dom["launches"]
+        rec_us = dom["total_us"]
     t_roof = max(dom["flops"] / (peak * 1e12), ob / (PEAK_LDS_GBS * 1e9), dom["bytes"] / (PEAK_HBM_GBS * 1e9))
     roofline.update({
-        "recurrence_steps": n_rec, "us_per_step": dom["avg_us"] / n_rec, "exchanges_per_step": bars,
+        "recurrence_steps": n_rec, "us_per_step": rec_us / n_rec, "exchanges_per_step": bars,
         "onchip_bytes": ob, "t_roof_us": t_roof * 1e6, "roof_frac": t_roof * 1e6 / dom["avg_us"],
         "occupied_cus": occ, "frac_occupied_cus": achieved / (peak * occ / 256.0),
         "exchange_roundtrip_us": rt_us,
         "exchange_floor_us": n_rec * bars * rt_us if rt_us is not None else None,
     })
+    if piped:
+        roofline.update({"pipeline_chunk": plan["pipe_chunk"], "launches": dom["launches"]})
     ms_per_step = elapsed / K * 1e3
     value = tokens / (elapsed / K)
     ctx = PAGES_CONTEXT.get(name)

@@ -16,6 +16,6 @@ rnn_forward_train and rnn_backward (fp32 LSTM / LSTMP / GRU).
 from .binding import (  # noqa: F401
     RNN_ABI_VERSION, RnnDesc, RnnWeights, RnnIO, RnnError, lib, lib_path,
     rnn_abi_version, rnn_strerror, rnn_workspace_bytes, rnn_forward_raw, rnn_read_status,
-    rnn_device_check, rnn_exchange_roundtrip_ns, rnn_forward, rssm_prior_unroll, rssm_actor_unroll, rnn_plan_info, MODES, STATUS,
-    CLIP_CELL, CLIP_PROJ, RnnGrads, rnn_forward_train, rnn_backward, TrainContext,
+    rnn_device_check, rnn_exchange_roundtrip_ns, rnn_forward, rssm_prior_unroll, rssm_actor_unroll, rnn_plan_info,
+    MODES, PIPE_MODES, STATUS, CLIP_CELL, CLIP_PROJ, RnnGrads, rnn_forward_train, rnn_backward, TrainContext,
 )

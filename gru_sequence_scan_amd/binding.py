@@ -17,6 +17,7 @@ RNN_MAX_LAYERS = 8
 RNN_MAX_LD = 2 * RNN_MAX_LAYERS
 
 MODES = {"lstm": 0, "gru": 1, "lstmp": 2, "rssm": 3, "rssm_actor": 4}
+PIPE_MODES = {"auto": 0, "off": 1, "on": 2}  # RnnDesc.layer_pipeline
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 LAYOUTS = {"padded": 0, "packed": 1, "batch_major": 2}
 STATUS = {
@@ -46,7 +47,8 @@ class RnnDesc(ctypes.Structure):
         ("tile_batch", ctypes.c_int32), ("tile_hidden", ctypes.c_int32),
         ("placement", ctypes.c_int32), ("weights", ctypes.c_int32),
         ("clip", ctypes.c_int32), ("cell_clip_lo", ctypes.c_float), ("cell_clip_hi", ctypes.c_float),
-        ("proj_clip", ctypes.c_float), ("actor_dim", ctypes.c_int32), ("gx_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
+        ("proj_clip", ctypes.c_float), ("actor_dim", ctypes.c_int32), ("gx_dtype", ctypes.c_int32),
+        ("layer_pipeline", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
     ]
 
 
@@ -184,7 +186,7 @@ def rnn_forward_raw(desc, weights, io, workspace_ptr, ws_bytes, stream_ptr):
 
 
 PLAN_FIELDS = ("kernel", "workgroups", "lds_bytes", "rows", "hidden_per_wg", "members", "proj_per_wg",
-               "groups", "groups_per_xcd", "wreg", "reg_tiles", "reg_ksplit", "reg_chunks")
+               "groups", "groups_per_xcd", "wreg", "reg_tiles", "reg_ksplit", "reg_chunks", "pipe_chunk")
 
 
 def rnn_plan_info(desc, lengths=None, cus=256, xcds=8):
@@ -313,7 +315,8 @@ def _call(desc, w, io, lengths, device, keep, check_status, noalloc=False):
 def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padded",
                 num_layers=1, bidirectional=False, proj_size=0, hidden_size=None, y_out=None,
                 tile_batch=0, tile_hidden=0, placement=0, weights=0, cell_clip=None, proj_clip=None,
-                gx_dtype="auto", return_workspace=False, check_status=True, noalloc=False, _train=False):
+                gx_dtype="auto", layer_pipeline="auto", return_workspace=False, check_status=True,
+                noalloc=False, _train=False):
     """Forward of an LSTM / GRU / LSTMP stack on the current HIP stream.
 
     x: padded [T, B, F] or packed [N_tok, F] (float32 or bfloat16, on a GPU).
@@ -324,7 +327,10 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     cell_clip: c (clamp to [-c, c]) or (lo, hi), clamps the updated LSTM cell
     state; proj_clip: p, clamps the LSTMP projected output to [-p, p].
     gx_dtype: "auto" stores the hoisted input projection in x's dtype, "f32"
-    always in fp32.
+    always in fp32. layer_pipeline: "auto" scans a unidirectional padded
+    stack's layers concurrently, one time chunk apart, where the launch-shape
+    model expects a gain; "off" runs it layer by layer; "on" pipelines it
+    whenever it fits (the results are the same bit for bit).
     check_status (default True): wait for the stream after the call and
     raise RnnError if the device reported a failure (a persistent group whose
     workgroups were not all resident ends with RNN_E_TIMEOUT and leaves the
@@ -411,6 +417,9 @@ def rnn_forward(mode, x, params, *, h0=None, c0=None, lengths=None, layout="padd
     if gx_dtype not in ("auto", "f32"):
         raise ValueError("gx_dtype must be 'auto' or 'f32'")
     desc.gx_dtype = 1 if gx_dtype == "f32" else 0
+    if layer_pipeline not in PIPE_MODES:
+        raise ValueError("layer_pipeline must be 'auto', 'off' or 'on'")
+    desc.layer_pipeline = PIPE_MODES[layer_pipeline]
     if cell_clip is not None:
         lo, hi = (-cell_clip, cell_clip) if isinstance(cell_clip, (int, float)) else cell_clip
         desc.clip |= CLIP_CELL

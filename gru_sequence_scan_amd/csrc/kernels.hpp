@@ -30,9 +30,15 @@ hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream)
 // Kernel 2: persistent scan over time for one layer, all directions.
 enum ScanMode { kLSTM = 0, kGRU = 1, kLSTMP = 2 };
 
+// Layer slots of one scan launch: stacked layers whose time chunks are
+// scanned together (layer pipelining, one direction).
+constexpr int kScanMaxSlots = 8;
+
 struct ScanArgs {
   int mode;          // ScanMode
-  int T;             // number of time steps looped over (T_max)
+  int nslot;         // layer slots (1, or up to kScanMaxSlots with D = 1);
+                     // groups are numbered slot-major
+  int T[kScanMaxSlots];  // time steps looped over per slot (T_max); 0: idle
   int B, H, K, P;    // K = recurrent width (H, or P for LSTMP)
   int D;             // directions
   int G;             // gate rows per direction
@@ -65,24 +71,33 @@ struct ScanArgs {
   // [rows, D, R] fp32 with R = 5H for LSTM (i, f, g, o, c_t) and 4H for GRU
   // (r, z, n, W_hn h_{t-1} + b_hn); null when not training.
   float* rsv;
-  // per direction tensors (already offset to this layer)
-  const void* w_hh[2];
-  const void* w_hr[2];
-  const void* b_hh[2];
-  const void* h0[2];   // [B, K] or null
-  const void* c0[2];   // [B, H] or null
-  void* h_n[2];        // [B, K] or null
-  void* c_n[2];        // [B, H] or null
-  const void* gx;      // [rows, D * G] fp32, or bf16 when gx_bf16
-  int gx_bf16;
-  void* y;             // [rows, D * K]
-  const int* lengths;  // device [B] or null (all T)
-  const int* offsets;  // device [T + 1] (packed)
+  // per (slot, direction) tensors, index slot * D + d, already offset to
+  // the slot's layer
+  const void* w_hh[kScanMaxSlots];
+  const void* w_hr[kScanMaxSlots];
+  const void* b_hh[kScanMaxSlots];
+  const void* h0[kScanMaxSlots];   // [B, K] or null
+  const void* c0[kScanMaxSlots];   // [B, H] or null
+  void* h_n[kScanMaxSlots];        // [B, K] or null
+  void* c_n[kScanMaxSlots];        // [B, H] or null
+  // fp32 copies of the carried state (time-chunked runs: bit-identical to an
+  // unchunked one): initial h (GRU's update reads it; [B, H]) and c ([B, H])
+  // and the final ones; each null when unused
+  const float* h0f[kScanMaxSlots];
+  const float* c0f[kScanMaxSlots];
+  float* h_nf[kScanMaxSlots];
+  float* c_nf[kScanMaxSlots];
+  // per slot
+  const void* gx[kScanMaxSlots];  // [rows, D * G] fp32, or bf16 when gx_bf16
+  void* y[kScanMaxSlots];         // [rows, D * K]
   // exchange (workspace): rings of write-once slots, all-ones before the
   // launch (kRingSlots slots in scan_common.hpp)
-  void* hx;            // [4][D][B][Kp] h_t (LSTMP: the projected h_t)
-  void* mx;            // [4][D][B][Hp] m_t (LSTMP)
-  unsigned* xid;       // [D * nbb * ns] members' XCD ids
+  void* hx[kScanMaxSlots];        // [4][D][B][Kp] h_t (LSTMP: the projected h_t)
+  void* mx[kScanMaxSlots];        // [4][D][B][Hp] m_t (LSTMP)
+  unsigned* xid[kScanMaxSlots];   // [D * nbb * ns] members' XCD ids
+  int gx_bf16;
+  const int* lengths;  // device [B] or null (all T)
+  const int* offsets;  // device [T + 1] (packed)
   unsigned* counters;  // unused by the forward scan
   int* status;
 };
@@ -93,8 +108,8 @@ constexpr int kScanRegChunks = 32;
 
 // Kernel 2b: one wavefront per (direction, batch row) when all gate rows of
 // a unit set fit one wave (LSTM H <= 16, GRU H <= 21; not LSTMP). Uses the
-// ScanArgs problem fields, the per-direction tensors, gx, y, lengths,
-// offsets and the clip bounds; no tiling, exchange or counters.
+// ScanArgs problem fields, slot 0's tensors, lengths, offsets and the clip
+// bounds; no tiling, exchange or counters.
 bool scan_wave_fits(int mode, int H, int K);
 int scan_wave_grid(int D, int B);
 hipError_t launch_scan_wave(const ScanArgs& a, int dtype_bf16, hipStream_t stream);

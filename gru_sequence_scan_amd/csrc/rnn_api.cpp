@@ -77,6 +77,7 @@ int validate_desc(const RnnDesc* d) {
   for (int r : d->reserved)
     if (r != 0) return RNN_E_SHAPE;
   if (d->gx_dtype != RNN_GX_AS_DTYPE && d->gx_dtype != RNN_GX_F32) return RNN_E_SHAPE;
+  if (d->layer_pipeline < RNN_PIPE_AUTO || d->layer_pipeline > RNN_PIPE_ON) return RNN_E_SHAPE;
   if (d->placement < 0 || d->placement > 2) return RNN_E_SHAPE;
   if (d->weights < 0 || d->weights > 2) return RNN_E_SHAPE;
   if (d->dtype != RNN_DTYPE_F32 && d->dtype != RNN_DTYPE_BF16) return RNN_E_UNSUPPORTED;
@@ -92,6 +93,7 @@ int validate_desc(const RnnDesc* d) {
     if (!std::isfinite(d->scale_lb)) return RNN_E_SHAPE;
     if (d->clip != 0) return RNN_E_UNSUPPORTED;
     if (d->gx_dtype != RNN_GX_AS_DTYPE) return RNN_E_UNSUPPORTED;  // no hoisted G_x
+    if (d->layer_pipeline != 0) return RNN_E_UNSUPPORTED;          // one layer
     const double big = (double)d->B * d->T * std::max({d->state_dim, d->belief_dim, d->action_dim});
     if (big > 2e9) return RNN_E_SHAPE;
     const double wa1 = (double)d->actor_dim * (d->state_dim + d->belief_dim);
@@ -112,12 +114,14 @@ int validate_desc(const RnnDesc* d) {
   if (d->num_layers < 1 || d->num_layers > RNN_MAX_LAYERS) return RNN_E_SHAPE;
   if (d->bidirectional != 0 && d->bidirectional != 1) return RNN_E_SHAPE;
   if (d->input_size < 1 || d->hidden_size < 1) return RNN_E_SHAPE;
-  const int D = d->bidirectional ? 2 : 1;
-  const int G = (d->mode == RNN_MODE_GRU ? 3 : 4) * d->hidden_size;
-  const int K = d->mode == RNN_MODE_LSTMP ? d->proj_size : d->hidden_size;
+  // sizes in double: the products of valid int fields can overflow int
+  const double D = d->bidirectional ? 2 : 1;
+  const double G = (d->mode == RNN_MODE_GRU ? 3.0 : 4.0) * d->hidden_size;
+  const double K = d->mode == RNN_MODE_LSTMP ? d->proj_size : d->hidden_size;
   const double rows = (double)d->T * d->B;
-  if (rows * D * G > 2e9 || rows * std::max(d->input_size, D * K) > 2e9) return RNN_E_SHAPE;
-  if ((double)d->hidden_size * std::max(d->input_size, D * K) > 2e9) return RNN_E_SHAPE;
+  const double in_max = std::max((double)d->input_size, D * K);
+  if (rows * D * G > 2e9 || rows * in_max > 2e9) return RNN_E_SHAPE;
+  if ((double)d->hidden_size * in_max > 2e9) return RNN_E_SHAPE;
   return RNN_OK;
 }
 
@@ -153,9 +157,15 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // needs no device)
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t status, counters, ints, gx, inter0, inter1, hx, mx, ex_h, ex_p, xid, ring_end, gpart, total;
+  size_t status, counters, ints, gx, inter0, inter1, ex_h, ex_p, xid, ring_end, gpart, total;
   size_t counters_bytes;
   int n_ints;
+  // forward scan exchange, one block per layer: XCD ids, h ring, m ring
+  size_t ex, ex_layer, ex_hx, ex_mx;  // first block, block size, ring offsets in a block
+  // layer pipelining (when the descriptor allows it): per-layer G_x of one
+  // time chunk, and the state carried between chunks (h in the storage
+  // dtype [B, K]; fp32 h and c [B, H]), two sets [2][num_layers] by parity
+  size_t gxp, gxp_layer, sth, sth_layer, sthf, stcf, stf_layer;
 };
 
 struct Dims {
@@ -199,6 +209,27 @@ size_t mx_ring_bytes(const RnnDesc* d, const Dims& m) {
   return align_up((size_t)kScanRingSlots * m.D * d->B * m.Hp * m.esize, kAlign);
 }
 
+// Layer pipelining: a unidirectional, padded, fixed-length stack of >= 2
+// LSTM / GRU / LSTMP layers (not the one-wave scan) runs its layers on
+// separate streams, one time chunk apart. The shape depends only on the
+// descriptor, so the workspace size does too.
+constexpr int kPipeChunks = 16;    // time chunks aimed at
+constexpr int kPipeMinChunk = 32;  // steps per chunk at least
+struct PipeShape {
+  bool on;
+  int chunk, nchunks;
+};
+PipeShape pipe_shape(const RnnDesc* d, bool has_lengths, const Dims& m) {
+  PipeShape ps{false, 0, 0};
+  if (d->layer_pipeline == RNN_PIPE_OFF || d->num_layers < 2 || d->bidirectional || d->layout != RNN_LAYOUT_PADDED ||
+      has_lengths || !is_rnn_mode(d->mode) || use_wave_scan(d, m))
+    return ps;
+  const int chunk = std::max(kPipeMinChunk, cdiv(d->T, kPipeChunks));
+  const int n = cdiv(d->T, chunk);
+  if (n < 2) return ps;
+  return PipeShape{true, chunk, n};
+}
+
 WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
   WsLayout w{};
   size_t o = 0;
@@ -231,13 +262,25 @@ WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
   const size_t inter = (size_t)m.rows * m.D * m.K * m.esize;
   w.inter0 = d->num_layers > 1 ? take(inter) : 0;
   w.inter1 = d->num_layers > 2 ? take(inter) : 0;
-  // the forward scan's exchange, one region per layer and all sentinel-filled
-  // by one fill before the first layer: the members' XCD ids, the h ring and
-  // (LSTMP) the m ring
-  w.xid = take(xid_layer_bytes() * d->num_layers);
-  w.hx = take(hx_ring_bytes(d, m) * d->num_layers);
-  w.mx = d->mode == RNN_MODE_LSTMP ? take(mx_ring_bytes(d, m) * d->num_layers) : w.hx;
+  // the forward scan's exchange, one block per layer (the members' XCD ids,
+  // the h ring and, LSTMP, the m ring), all sentinel-filled by one fill
+  // before the first layer (per layer and chunk when pipelined)
+  w.ex_hx = xid_layer_bytes();
+  w.ex_mx = w.ex_hx + hx_ring_bytes(d, m);
+  w.ex_layer = w.ex_mx + (d->mode == RNN_MODE_LSTMP ? mx_ring_bytes(d, m) : 0);
+  w.ex = take(w.ex_layer * d->num_layers);
   w.ring_end = o;
+  const PipeShape ps = pipe_shape(d, has_lengths, m);
+  if (ps.on) {
+    w.gxp_layer = align_up((size_t)ps.chunk * d->B * m.G * gx_esize(d, m) + 16, kAlign);
+    w.gxp = take(w.gxp_layer * d->num_layers);
+    // two sets, by chunk parity: a chunk reads one and writes the other
+    w.sth_layer = align_up((size_t)d->B * m.K * m.esize, kAlign);
+    w.sth = take(w.sth_layer * d->num_layers * 2);
+    w.stf_layer = align_up((size_t)d->B * d->hidden_size * 4, kAlign);
+    w.sthf = take(w.stf_layer * d->num_layers * 2);
+    w.stcf = take(w.stf_layer * d->num_layers * 2);
+  }
   // split-K partial products of the input GEMMs with few output tiles
   size_t gpart = 0;
   for (int l = 0; l < d->num_layers; ++l) {
@@ -289,7 +332,10 @@ struct ScanPlan {
   int pnt, pks, pcpt;        // LSTMP projection product layout (ScanArgs)
 };
 
-int scan_grid(const ScanPlan& p, int D, int xcds) { return p.gpx > 0 ? xcds * p.gpx * p.ns : D * p.nbb * p.ns; }
+// Grid of a plan over `groups_per_nbb` = layer slots x directions.
+int scan_grid(const ScanPlan& p, int slots_x_dirs, int xcds) {
+  return p.gpx > 0 ? xcds * p.gpx * p.ns : slots_x_dirs * p.nbb * p.ns;
+}
 
 // Register layout of a slice of ncw W_hh rows (padded to 16) for a batch
 // block of bb rows, or false when none fits kScanRegChunks 16-byte chunks
@@ -341,7 +387,11 @@ bool reg_layout(int bb, int ncw, int Kp, int esize, int* rnt, int* rks, int* rcp
   return ok;
 }
 
-int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wreg, ScanPlan* out) {
+// The tiled scan's launch shape for `nslot` layer slots (stacked layers
+// scanned in one launch) of D directions each, with its modelled time per
+// step in *cost_us when non-null.
+int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wreg, ScanPlan* out, int nslot = 1,
+              double* cost_us = nullptr) {
   const int B = d->B, H = d->hidden_size, P = d->proj_size;
   const bool lstmp = d->mode == RNN_MODE_LSTMP;
   std::vector<int> bbs;
@@ -369,7 +419,7 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wre
       if (hs < 1 || bb * hs > 1024) continue;
       const int ns = cdiv(H, hs);
       const int nbb = cdiv(B, bb);
-      if ((long long)m.D * nbb * ns > std::min(cus, kScanMaxWorkgroups)) continue;
+      if ((long long)m.D * nbb * ns > kScanMaxWorkgroups || (long long)nslot * m.D * nbb * ns > cus) continue;
       const int ps = lstmp ? cdiv(P, ns) : 0;
       if (bb * ps > 1024) continue;  // projection outputs: at most 4 per thread
       const int ncw = rup(m.gates * hs, 16);
@@ -383,7 +433,7 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wre
           a.pnt = a.pks = a.pcpt = 0;
         const int lds = scan_lds_bytes(a, m.esize);
         if (lds > kMaxLds) continue;
-        const int groups = m.D * nbb;
+        const int groups = nslot * m.D * nbb;
         const int gpx = per_xcd > 0 && d->placement != 1 ? cdiv(groups, xcds) : 0;
         const bool xcd_aligned = gpx > 0 && gpx * ns <= per_xcd;
         // a group whose members share one XCD exchanges ~15% faster (measured)
@@ -420,6 +470,7 @@ int plan_scan(const RnnDesc* d, const Dims& m, int cus, int xcds, bool allow_wre
       }
     }
   }
+  if (found && cost_us) *cost_us = best;
   return found ? RNN_OK : RNN_E_PLAN;
 }
 
@@ -527,14 +578,16 @@ int plan_rssm(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
 int hip_status(hipError_t e) { return e == hipSuccess ? RNN_OK : RNN_E_HIP; }
 
 // Optional per-kernel event brackets (rnn_forward_profiled).
+// kinds[n] = kernel kind | layer << 8 (kind 5, a pipelined scan: first
+// layer | last layer << 4).
 struct Prof {
   void* const* events = nullptr;
   int n_events = 0;
   int* kinds = nullptr;
   int n = 0;
   hipStream_t st = nullptr;
-  int begin(int kind) {
-    if (kinds && n < n_events / 2) kinds[n] = kind;
+  int begin(int kind, int layer) {
+    if (kinds && n < n_events / 2) kinds[n] = kind | layer << 8;
     if (events && n < n_events / 2)
       return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[2 * n]), st));
     return RNN_OK;
@@ -610,7 +663,7 @@ int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* w
     const size_t end = L.ex_p + (size_t)rssm_ring_slots() * d->B * p.nw * a.Ep * 4;
     if ((rc = hip_status(launch_fill_u32(ws + L.xid, end - L.xid, 0xFFFFFFFFu, st))) != RNN_OK) return rc;
   }
-  if ((rc = prof.begin(3)) != RNN_OK) return rc;
+  if ((rc = prof.begin(3, 0)) != RNN_OK) return rc;
   if ((rc = hip_status(p.reg ? launch_rssm_reg(a, st) : launch_rssm(a, st))) != RNN_OK) return rc;
   return prof.end();
 }
@@ -653,6 +706,181 @@ int validate_train(const RnnDesc* d) {
   return RNN_OK;
 }
 
+// The G_x product of layer l (both directions) over `rows` rows of its
+// input starting at row r0, into C.
+GemmArgs layer_gemm(const RnnDesc* d, const RnnWeights* w, const Dims& m, int l, const void* in, long long r0,
+                    int rows, void* C, int c_bf16, char* ws, const WsLayout& L, bool allow_split) {
+  const size_t es = m.esize;
+  const int in_l = l == 0 ? d->input_size : m.D * m.K;
+  GemmArgs g{};
+  g.A = (const char*)in + (size_t)r0 * in_l * es;
+  g.M = rows; g.N = m.D * m.G; g.K = in_l; g.G = m.G;
+  g.hh_fold_rows = d->mode == RNN_MODE_GRU ? 2 * d->hidden_size : m.G;
+  g.has_bias = d->has_bias;
+  g.C = C;
+  g.c_bf16 = c_bf16;
+  bool vec = (size_t)in_l * es % 16 == 0 && aligned(g.A, 16);
+  for (int di = 0; di < m.D; ++di) {
+    const int i = l * m.D + di;
+    g.W[di] = w->w_ih[i];
+    g.b_ih[di] = w->b_ih[i];
+    g.b_hh[di] = w->b_hh[i];
+    vec = vec && aligned(w->w_ih[i], 16);
+  }
+  g.vec_ok = vec;
+  g.zero16 = ws + L.status + kZeroChunk;
+  g.splits = allow_split ? gemm_xw_splits(g.M, g.N, g.K, d->dtype == RNN_DTYPE_BF16) : 1;
+  g.part = g.splits > 1 ? (float*)(ws + L.gpart) : nullptr;
+  return g;
+}
+
+// The scan arguments of layer l that do not depend on the time range: the
+// problem, the plan, the weights, the clamps and the layer's exchange block.
+ScanArgs layer_scan(const RnnDesc* d, const RnnWeights* w, const Dims& m, const ScanPlan& p, int xcds, int l,
+                    char* ws, const WsLayout& L) {
+  ScanArgs a{};
+  a.mode = d->mode == RNN_MODE_GRU ? kGRU : (d->mode == RNN_MODE_LSTMP ? kLSTMP : kLSTM);
+  a.B = d->B; a.H = d->hidden_size; a.K = m.K; a.P = d->proj_size; a.D = m.D; a.G = m.G;
+  a.packed = d->layout == RNN_LAYOUT_PACKED;
+  a.has_bias = d->has_bias;
+  a.bb = p.bb; a.hs = p.hs; a.ns = p.ns; a.ps = p.ps; a.nbb = p.nbb; a.Kp = m.Kp; a.Hp = m.Hp;
+  a.nxcd = xcds; a.gpx = p.gpx;
+  a.wreg = p.wreg; a.rnt = p.rnt; a.rks = p.rks; a.rcpt = p.rcpt;
+  a.pnt = p.pnt; a.pks = p.pks; a.pcpt = p.pcpt;
+  const float inf = std::numeric_limits<float>::infinity();
+  const bool cclip = d->clip & RNN_CLIP_CELL, pclip = d->clip & RNN_CLIP_PROJ;
+  a.c_lo = cclip ? d->cell_clip_lo : -inf;
+  a.c_hi = cclip ? d->cell_clip_hi : inf;
+  a.p_lo = pclip ? -d->proj_clip : -inf;
+  a.p_hi = pclip ? d->proj_clip : inf;
+  for (int di = 0; di < m.D; ++di) {
+    const int i = l * m.D + di;
+    a.w_hh[di] = w->w_hh[i];
+    a.w_hr[di] = d->mode == RNN_MODE_LSTMP ? w->w_hr[i] : nullptr;
+    a.b_hh[di] = d->has_bias ? w->b_hh[i] : nullptr;
+  }
+  char* ex = ws + L.ex + l * L.ex_layer;
+  a.nslot = 1;
+  a.xid[0] = (unsigned*)ex;
+  a.hx[0] = ex + L.ex_hx;
+  a.mx[0] = d->mode == RNN_MODE_LSTMP ? ex + L.ex_mx : nullptr;
+  a.counters = (unsigned*)(ws + L.counters + (size_t)l * m.D * d->B * kCounterBytes);
+  a.status = (int*)(ws + L.status);
+  return a;
+}
+
+// The launch plan of the forward: the one-wave scan, or the tiled scan's
+// plan and whether the layers run pipelined: one launch then scans a time
+// chunk of every stacked layer at once (layer l on chunk w - l at wave w),
+// so it needs num_layers x the workgroups of a single layer's scan, and the
+// stack takes nchunks + num_layers - 1 chunk scans instead of num_layers x
+// nchunks. It is taken when the cost model expects it to be faster.
+constexpr double kPipeWaveUs = 20.0, kLayerUs = 10.0;  // launch overheads (measured, MI355X)
+struct ForwardPlan {
+  bool wave, pipe;
+  PipeShape ps;
+  ScanPlan p;
+};
+int plan_forward(const RnnDesc* d, const Dims& m, bool has_len, int cus, int xcds, bool wreg_ok, bool training,
+                 ForwardPlan* out) {
+  ForwardPlan f{};
+  f.wave = !training && use_wave_scan(d, m);
+  if (f.wave) {
+    *out = f;
+    return RNN_OK;
+  }
+  f.ps = pipe_shape(d, has_len, m);
+  double one = 0.0;
+  const int rc = plan_scan(d, m, cus, xcds, wreg_ok, &f.p, 1, &one);
+  ScanPlan pp{};
+  double piped = 0.0;
+  if (f.ps.on && !training && plan_scan(d, m, cus, xcds, wreg_ok, &pp, d->num_layers, &piped) == RNN_OK) {
+    // per-step costs times the steps each schedule walks in sequence, plus
+    // the launches around each scan (a wave: exchange reset, one G_x
+    // product per active layer, the scan; a layer: its product and scan)
+    const int L = d->num_layers, waves = f.ps.nchunks + L - 1;
+    const double tp = piped * (double)f.ps.chunk * waves + kPipeWaveUs * waves;
+    const double tl = one * (double)d->T * L + kLayerUs * L;
+    if (rc != RNN_OK || tp < tl || d->layer_pipeline == RNN_PIPE_ON) {
+      f.pipe = true;
+      f.p = pp;
+    }
+  }
+  if (!f.pipe && rc != RNN_OK) return rc;
+  *out = f;
+  return RNN_OK;
+}
+
+// Layer pipelining on the caller's stream, in waves: wave w resets the
+// exchange blocks of the active layers, computes layer l's G_x for its time
+// chunk c = w - l (from x, or from layer l - 1's output of chunk c, written
+// by the previous wave), and scans every active layer's chunk in one launch.
+// The state crosses chunk boundaries through the workspace: h in the
+// storage dtype (the first step's operand, what the ring would hold) and
+// fp32 h and c (the registers), so the results are those of the
+// layer-by-layer run, bit for bit. Chunk c reads state set c % 2 and writes
+// set (c + 1) % 2.
+int forward_rnn_pipe(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws, const WsLayout& L,
+                     const Dims& m, const ForwardPlan& f, hipStream_t st, int xcds, Prof& prof) {
+  int rc;
+  const int nl = d->num_layers, n = f.ps.nchunks, chunk = f.ps.chunk;
+  const size_t es = m.esize;
+  const bool bf16 = d->dtype == RNN_DTYPE_BF16;
+  const int gx_bf16 = gx_esize(d, m) == 2;
+  const int B = d->B, H = d->hidden_size, K = m.K;
+  const bool cell = d->mode != RNN_MODE_GRU;
+  auto layer_out = [&](int l) -> char* {
+    return l == nl - 1 ? (char*)io->y : ws + ((l % 2 == 0) ? L.inter0 : L.inter1);
+  };
+  auto sth = [&](int set, int l) { return ws + L.sth + ((size_t)set * nl + l) * L.sth_layer; };
+  auto sthf = [&](int set, int l) { return (float*)(ws + L.sthf + ((size_t)set * nl + l) * L.stf_layer); };
+  auto stcf = [&](int set, int l) { return (float*)(ws + L.stcf + ((size_t)set * nl + l) * L.stf_layer); };
+  for (int wv = 0; wv < n + nl - 1; ++wv) {
+    const int l0 = std::max(0, wv - n + 1), l1 = std::min(nl - 1, wv);
+    if ((rc = hip_status(launch_fill_u32(ws + L.ex + l0 * L.ex_layer, (size_t)(l1 - l0 + 1) * L.ex_layer,
+                                         0xFFFFFFFFu, st))) != RNN_OK)
+      return rc;
+    ScanArgs a = layer_scan(d, w, m, f.p, xcds, 0, ws, L);
+    a.nslot = nl;
+    a.gx_bf16 = gx_bf16;
+    for (int l = 0; l < nl; ++l) a.T[l] = 0;
+    for (int l = l0; l <= l1; ++l) {
+      const int c = wv - l, t0 = c * chunk, tc = std::min(d->T, t0 + chunk) - t0;
+      const bool first = c == 0, last = c == n - 1;
+      char* gxc = ws + L.gxp + l * L.gxp_layer;
+      const void* in = l == 0 ? io->x : (const void*)layer_out(l - 1);
+      const GemmArgs g = layer_gemm(d, w, m, l, in, (long long)t0 * B, tc * B, gxc, gx_bf16, ws, L, false);
+      if ((rc = prof.begin(1, l)) != RNN_OK) return rc;
+      if ((rc = hip_status(launch_gemm_xw(g, bf16, st))) != RNN_OK) return rc;
+      if ((rc = prof.end()) != RNN_OK) return rc;
+      const ScanArgs al = layer_scan(d, w, m, f.p, xcds, l, ws, L);
+      a.T[l] = tc;
+      a.gx[l] = gxc;
+      a.y[l] = layer_out(l) + (size_t)t0 * B * K * es;
+      a.hx[l] = al.hx[0];
+      a.mx[l] = al.mx[0];
+      a.xid[l] = al.xid[0];
+      a.w_hh[l] = al.w_hh[0];
+      a.w_hr[l] = al.w_hr[0];
+      a.b_hh[l] = al.b_hh[0];
+      const int rs = c % 2, wset = (c + 1) % 2;
+      a.h0[l] = first ? (io->h0 ? (const char*)io->h0 + (size_t)l * B * K * es : nullptr) : sth(rs, l);
+      a.c0[l] = first && cell && io->c0 ? (const char*)io->c0 + (size_t)l * B * H * es : nullptr;
+      a.h0f[l] = first ? nullptr : sthf(rs, l);
+      a.c0f[l] = first || !cell ? nullptr : stcf(rs, l);
+      a.h_n[l] = last ? (io->h_n ? (char*)io->h_n + (size_t)l * B * K * es : nullptr) : sth(wset, l);
+      a.c_n[l] = last && cell && io->c_n ? (char*)io->c_n + (size_t)l * B * H * es : nullptr;
+      a.h_nf[l] = last ? nullptr : sthf(wset, l);
+      a.c_nf[l] = last || !cell ? nullptr : stcf(wset, l);
+    }
+    // kind 5: one launch scanning layers l0 .. l1
+    if ((rc = prof.begin(5, l0 | l1 << 4)) != RNN_OK) return rc;
+    if ((rc = hip_status(launch_scan(a, bf16, st))) != RNN_OK) return rc;
+    if ((rc = prof.end()) != RNN_OK) return rc;
+  }
+  return RNN_OK;
+}
+
 int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws, size_t ws_bytes,
                 hipStream_t st, int cus, int xcds, Prof& prof, char* rsv = nullptr) {
   int rc;
@@ -681,9 +909,10 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   // W_hh slices go to registers only as whole aligned 16-byte chunks
   bool wreg_ok = (size_t)m.K * es % 16 == 0;
   for (int i = 0; i < LD; ++i) wreg_ok = wreg_ok && aligned(w->w_hh[i], 16);
-  const bool wave = !rsv && use_wave_scan(d, m);
-  ScanPlan p{};
-  if (!wave && (rc = plan_scan(d, m, cus, xcds, wreg_ok, &p)) != RNN_OK) return rc;
+  ForwardPlan f{};
+  if ((rc = plan_forward(d, m, has_len, cus, xcds, wreg_ok, rsv != nullptr, &f)) != RNN_OK) return rc;
+  const bool wave = f.wave;
+  const ScanPlan& p = f.p;
   // the scan addresses one layer's rings, and one step's rows of G_x and y,
   // with 32-bit byte offsets
   if (!wave && (std::max(hx_ring_bytes(d, m), mx_ring_bytes(d, m)) >= ((size_t)1 << 31) ||
@@ -694,8 +923,9 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
 
   // ---- enqueue ----
   if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
+  if (f.pipe) return forward_rnn_pipe(d, w, io, ws, L, m, f, st, xcds, prof);
   if (!wave &&
-      (rc = hip_status(launch_fill_u32(ws + L.xid, L.ring_end - L.xid, 0xFFFFFFFFu, st))) != RNN_OK)
+      (rc = hip_status(launch_fill_u32(ws + L.ex, L.ring_end - L.ex, 0xFFFFFFFFu, st))) != RNN_OK)
     return rc;
   int* dev_len = nullptr;
   int* dev_off = nullptr;
@@ -727,72 +957,51 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   const int gx_bf16 = !wave && gx_esize(d, m) == 2;
   const void* layer_in = io->x;
   for (int l = 0; l < d->num_layers; ++l) {
-    const int in_l = l == 0 ? d->input_size : m.D * m.K;
     void* layer_out = l == d->num_layers - 1 ? io->y
                       : rsv ? (void*)(rsv + RL.y[l])
                             : (void*)(ws + ((l % 2 == 0) ? L.inter0 : L.inter1));
     // Kernel 1: Gx for every row of this layer, both directions.
-    GemmArgs g{};
-    g.A = layer_in;
-    g.M = (int)m.rows; g.N = m.D * m.G; g.K = in_l; g.G = m.G;
-    g.hh_fold_rows = d->mode == RNN_MODE_GRU ? 2 * d->hidden_size : m.G;
-    g.has_bias = d->has_bias;
-    g.C = gx;
-    g.c_bf16 = gx_bf16;
-    bool vec = (size_t)in_l * es % 16 == 0 && aligned(layer_in, 16);
-    for (int di = 0; di < m.D; ++di) {
-      const int i = l * m.D + di;
-      g.W[di] = w->w_ih[i];
-      g.b_ih[di] = w->b_ih[i];
-      g.b_hh[di] = w->b_hh[i];
-      vec = vec && aligned(w->w_ih[i], 16);
-    }
-    g.vec_ok = vec;
-    g.zero16 = ws + L.status + kZeroChunk;
-    g.splits = gemm_xw_splits(g.M, g.N, g.K, bf16);
-    g.part = g.splits > 1 ? (float*)(ws + L.gpart) : nullptr;
-    if ((rc = prof.begin(1)) != RNN_OK) return rc;
+    const GemmArgs g = layer_gemm(d, w, m, l, layer_in, 0, (int)m.rows, gx, gx_bf16, ws, L, true);
+    if ((rc = prof.begin(1, l)) != RNN_OK) return rc;
     if ((rc = hip_status(launch_gemm_xw(g, bf16, st))) != RNN_OK) return rc;
     if ((rc = prof.end()) != RNN_OK) return rc;
 
     // Kernel 2: the scan.
-    ScanArgs a{};
-    a.mode = d->mode == RNN_MODE_GRU ? kGRU : (d->mode == RNN_MODE_LSTMP ? kLSTMP : kLSTM);
-    a.T = t_max; a.B = d->B; a.H = d->hidden_size; a.K = m.K; a.P = d->proj_size; a.D = m.D; a.G = m.G;
-    a.packed = d->layout == RNN_LAYOUT_PACKED;
-    a.has_bias = d->has_bias;
-    a.bb = p.bb; a.hs = p.hs; a.ns = p.ns; a.ps = p.ps; a.nbb = p.nbb; a.Kp = m.Kp; a.Hp = m.Hp;
-    a.nxcd = xcds; a.gpx = p.gpx;
-    a.wreg = p.wreg; a.rnt = p.rnt; a.rks = p.rks; a.rcpt = p.rcpt;
-    a.pnt = p.pnt; a.pks = p.pks; a.pcpt = p.pcpt;
-    const float inf = std::numeric_limits<float>::infinity();
-    const bool cclip = d->clip & RNN_CLIP_CELL, pclip = d->clip & RNN_CLIP_PROJ;
-    a.c_lo = cclip ? d->cell_clip_lo : -inf;
-    a.c_hi = cclip ? d->cell_clip_hi : inf;
-    a.p_lo = pclip ? -d->proj_clip : -inf;
-    a.p_hi = pclip ? d->proj_clip : inf;
+    ScanArgs a = wave ? ScanArgs{} : layer_scan(d, w, m, p, xcds, l, ws, L);
+    if (wave) {
+      a.mode = d->mode == RNN_MODE_GRU ? kGRU : (d->mode == RNN_MODE_LSTMP ? kLSTMP : kLSTM);
+      a.B = d->B; a.H = d->hidden_size; a.K = m.K; a.P = d->proj_size; a.D = m.D; a.G = m.G;
+      a.packed = d->layout == RNN_LAYOUT_PACKED;
+      a.has_bias = d->has_bias;
+      const float inf = std::numeric_limits<float>::infinity();
+      const bool cclip = d->clip & RNN_CLIP_CELL;
+      a.c_lo = cclip ? d->cell_clip_lo : -inf;
+      a.c_hi = cclip ? d->cell_clip_hi : inf;
+      a.p_lo = -inf;
+      a.p_hi = inf;
+      for (int di = 0; di < m.D; ++di) {
+        const int i = l * m.D + di;
+        a.w_hh[di] = w->w_hh[i];
+        a.b_hh[di] = d->has_bias ? w->b_hh[i] : nullptr;
+      }
+      a.status = (int*)(ws + L.status);
+    }
+    a.nslot = 1;
+    a.T[0] = t_max;
     for (int di = 0; di < m.D; ++di) {
       const int i = l * m.D + di;
-      a.w_hh[di] = w->w_hh[i];
-      a.w_hr[di] = d->mode == RNN_MODE_LSTMP ? w->w_hr[i] : nullptr;
-      a.b_hh[di] = d->has_bias ? w->b_hh[i] : nullptr;
       a.h0[di] = io->h0 ? (const char*)io->h0 + (size_t)i * d->B * m.K * es : nullptr;
       a.c0[di] = (d->mode != RNN_MODE_GRU && io->c0) ? (const char*)io->c0 + (size_t)i * d->B * d->hidden_size * es : nullptr;
       a.h_n[di] = io->h_n ? (char*)io->h_n + (size_t)i * d->B * m.K * es : nullptr;
       a.c_n[di] = (d->mode != RNN_MODE_GRU && io->c_n) ? (char*)io->c_n + (size_t)i * d->B * d->hidden_size * es : nullptr;
     }
-    a.gx = gx;
+    a.gx[0] = gx;
     a.gx_bf16 = gx_bf16;
-    a.y = layer_out;
+    a.y[0] = layer_out;
     a.rsv = rsv ? (float*)(rsv + RL.gates[l]) : nullptr;
     a.lengths = dev_len;
     a.offsets = dev_off;
-    a.hx = ws + L.hx + l * hx_ring_bytes(d, m);
-    a.mx = d->mode == RNN_MODE_LSTMP ? ws + L.mx + l * mx_ring_bytes(d, m) : nullptr;
-    a.xid = (unsigned*)(ws + L.xid + l * xid_layer_bytes());
-    a.counters = (unsigned*)(ws + L.counters + (size_t)l * m.D * d->B * kCounterBytes);
-    a.status = (int*)(ws + L.status);
-    if ((rc = prof.begin(wave ? 4 : 2)) != RNN_OK) return rc;
+    if ((rc = prof.begin(wave ? 4 : 2, l)) != RNN_OK) return rc;
     if ((rc = hip_status(wave ? launch_scan_wave(a, bf16, st) : launch_scan(a, bf16, st))) != RNN_OK) return rc;
     if ((rc = prof.end()) != RNN_OK) return rc;
     layer_in = layer_out;
@@ -1165,13 +1374,16 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
     info[5] = 1; info[6] = 0; info[7] = desc->B; info[8] = 0;
     return RNN_OK;
   }
-  ScanPlan p;
-  if ((rc = plan_scan(desc, m, cus, xcds, (size_t)m.K * m.esize % 16 == 0, &p)) != RNN_OK) return rc;
-  info[0] = 2; info[1] = scan_grid(p, m.D, xcds); info[2] = p.lds; info[3] = p.bb; info[4] = p.hs;
-  info[5] = p.ns; info[6] = p.ps; info[7] = p.nbb; info[8] = p.gpx;
+  ForwardPlan f;
+  rc = plan_forward(desc, m, lengths_host != nullptr, cus, xcds, (size_t)m.K * m.esize % 16 == 0, false, &f);
+  if (rc != RNN_OK) return rc;
+  const ScanPlan& p = f.p;
+  info[0] = 2; info[1] = scan_grid(p, (f.pipe ? desc->num_layers : 1) * m.D, xcds); info[2] = p.lds;
+  info[3] = p.bb; info[4] = p.hs; info[5] = p.ns; info[6] = p.ps; info[7] = p.nbb; info[8] = p.gpx;
   if (n_info >= 13) {
     info[9] = p.wreg; info[10] = p.rnt; info[11] = p.rks; info[12] = p.rcpt;
   }
+  if (n_info >= 14) info[13] = f.pipe ? f.ps.chunk : 0;
   return RNN_OK;
 }
 

@@ -17,7 +17,7 @@ hipError_t launch_scan_f32_lds(const ScanArgs& a, int lds, dim3 grid, hipStream_
 hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream) {
   const int esize = dtype_bf16 ? 2 : 4;
   const int lds = scan_lds(a, esize).total;
-  const dim3 grid(a.gpx > 0 ? a.nxcd * a.gpx * a.ns : a.D * a.nbb * a.ns);
+  const dim3 grid(a.gpx > 0 ? a.nxcd * a.gpx * a.ns : a.nslot * a.D * a.nbb * a.ns);
   if (dtype_bf16 && a.gx_bf16)
     return a.wreg ? launch_scan_bf16gx_reg(a, lds, grid, stream) : launch_scan_bf16gx_lds(a, lds, grid, stream);
   if (dtype_bf16)

@@ -301,22 +301,28 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   const int tid = threadIdx.x;
   const int gates = a.mode == kGRU ? 3 : 4;
 
-  // Workgroup -> (direction, batch block, hidden slice). Workgroups are dealt
-  // to the XCDs round-robin by id, so with gpx > 0 the ids xcd, xcd + nxcd,
-  // ... form the groups of one XCD and a group's exchange stays between the
-  // CUs of one chiplet (placement only; correctness never depends on it).
+  // Workgroup -> (layer slot, direction, batch block, hidden slice).
+  // Workgroups are dealt to the XCDs round-robin by id, so with gpx > 0 the
+  // ids xcd, xcd + nxcd, ... form the groups of one XCD and a group's
+  // exchange stays between the CUs of one chiplet (placement only;
+  // correctness never depends on it).
   int s, grp;
   if (a.gpx > 0) {
-    const int xcd = blockIdx.x % a.nxcd, slot = blockIdx.x / a.nxcd;
-    grp = xcd * a.gpx + slot / a.ns;
-    s = slot % a.ns;
+    const int xcd = blockIdx.x % a.nxcd, pos = blockIdx.x / a.nxcd;
+    grp = xcd * a.gpx + pos / a.ns;
+    s = pos % a.ns;
   } else {
     s = blockIdx.x % a.ns;
     grp = blockIdx.x / a.ns;
   }
-  if (grp >= a.D * a.nbb) return;  // padding slots of the XCD-aligned layout
+  const int gpl = a.D * a.nbb;  // groups per layer slot
+  if (grp >= a.nslot * gpl) return;  // padding slots of the XCD-aligned layout
+  const int ls = grp / gpl;
+  if (a.T[ls] <= 0) return;  // idle slot
+  grp -= ls * gpl;
   const int nb = grp % a.nbb;
   const int d = grp / a.nbb;
+  const int q = ls * a.D + d;  // index of the per-(slot, direction) tensors
   const int b0 = nb * a.bb;
   const int j0 = s * a.hs;
   const int hs_act = min(a.hs, a.H - j0);  // may be <= 0 for a trailing slice
@@ -333,9 +339,9 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   // Ring slots: step k's exchanged state (h_t, for LSTMP the projected h_t)
   // goes to hx slot k mod kRingSlots; LSTMP's m_t to mx slot k mod kRingSlots.
   const uint32_t hx_bytes = (uint32_t)(kRingSlots * a.D * a.B * a.Kp) * sizeof(DT);
-  const __amdgpu_buffer_rsrc_t hx_rs = make_rsrc(a.hx, hx_bytes);
+  const __amdgpu_buffer_rsrc_t hx_rs = make_rsrc(a.hx[ls], hx_bytes);
   const uint32_t mx_bytes = PROJ ? (uint32_t)(kRingSlots * a.D * a.B * a.Hp) * sizeof(DT) : 16u;
-  const __amdgpu_buffer_rsrc_t mx_rs = make_rsrc(PROJ ? a.mx : a.hx, mx_bytes);
+  const __amdgpu_buffer_rsrc_t mx_rs = make_rsrc(PROJ ? a.mx[ls] : a.hx[ls], mx_bytes);
   auto hx_el = [&](int k, int b, int c) -> uint32_t {
     return (uint32_t)((((k & (kRingSlots - 1)) * a.D + d) * a.B + b) * a.Kp + c);
   };
@@ -347,7 +353,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   // wave's outstanding memory operations.
   int* lens = reinterpret_cast<int*>(lds + L.lens);
   for (int r = tid; r < a.bb; r += kThreads)
-    lens[r] = b0 + r < a.B ? (a.lengths ? a.lengths[b0 + r] : a.T) : 0;
+    lens[r] = b0 + r < a.B ? (a.lengths ? a.lengths[b0 + r] : a.T[ls]) : 0;
   if (tid == 0) {
     flags[0] = 0;
     flags[1] = 1;
@@ -357,7 +363,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   auto len_of = [&](int b) -> int { return lens[b - b0]; };
 
   // --- resident weights -----------------------------------------------------
-  const DT* whh = reinterpret_cast<const DT*>(a.w_hh[d]);
+  const DT* whh = reinterpret_cast<const DT*>(a.w_hh[q]);
   typename Chunk<DT>::T wreg[WREG ? kScanRegChunks : 1];
   if constexpr (WREG) {
     switch (a.rnt) {
@@ -372,7 +378,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     }, lds, L.ws, L.ws_ld);
   }
   if (PROJ) {
-    const DT* whr = reinterpret_cast<const DT*>(a.w_hr[d]);
+    const DT* whr = reinterpret_cast<const DT*>(a.w_hr[q]);
     load_weights<DT>(whr, a.H, a.Hp, L.ncp_wr, [&](int r) -> int {
       return r < ps_act ? p0 + r : -1;
     }, lds, L.wr, L.wr_ld);
@@ -388,7 +394,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   // Plain stores suffice for the ring when the whole group runs on one XCD.
   bool local = true;
   if (!solo && a.ns > 1) {
-    local = group_on_one_xcd(a.xid + (size_t)grp * a.ns, a.ns, s, flags + 2, flags + 1);
+    local = group_on_one_xcd(a.xid[ls] + (size_t)grp * a.ns, a.ns, s, flags + 2, flags + 1);
     if (!flags[2]) {
       if (tid == 0) __hip_atomic_store(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
@@ -410,7 +416,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     }
   }
   if (solo) {
-    const DT* h0s = reinterpret_cast<const DT*>(a.h0[d]);
+    const DT* h0s = reinterpret_cast<const DT*>(a.h0[q]);
     for (int e = tid; e < tile_rows * a.Kp; e += kThreads) {
       const int r = e / a.Kp, k = e - r * a.Kp;
       const int b = b0 + r;
@@ -422,9 +428,9 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   const int n_el = a.bb * a.hs;
   float hreg[EPT], creg[EPT];
   float bhn[EPT];
-  const DT* h0 = reinterpret_cast<const DT*>(a.h0[d]);
-  const DT* c0 = reinterpret_cast<const DT*>(a.c0[d]);
-  const DT* bhh = reinterpret_cast<const DT*>(a.b_hh[d]);
+  const DT* h0 = reinterpret_cast<const DT*>(a.h0[q]);
+  const DT* c0 = reinterpret_cast<const DT*>(a.c0[q]);
+  const DT* bhh = reinterpret_cast<const DT*>(a.b_hh[q]);
   // Owned element i: row er[i] of the block, unit eu[i] of the slice, and the
   // row's length (0 when the element is not owned), computed once.
   int lenreg[EPT], er[EPT], eu[EPT];
@@ -439,8 +445,14 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     lenreg[i] = (e < n_el && u < hs_act && b < a.B) ? len_of(b) : 0;
     if (e < n_el && u < hs_act && b < a.B) {
       const int j = j0 + u;
-      if (!PROJ && h0) hreg[i] = to_f32<DT>(h0[(size_t)b * a.K + j]);
-      if (a.mode != kGRU && c0) creg[i] = to_f32<DT>(c0[(size_t)b * a.H + j]);
+      if (!PROJ && a.h0f[q])
+        hreg[i] = a.h0f[q][(size_t)b * a.H + j];
+      else if (!PROJ && h0)
+        hreg[i] = to_f32<DT>(h0[(size_t)b * a.K + j]);
+      if (a.mode != kGRU && a.c0f[q])
+        creg[i] = a.c0f[q][(size_t)b * a.H + j];
+      else if (a.mode != kGRU && c0)
+        creg[i] = to_f32<DT>(c0[(size_t)b * a.H + j]);
       if (a.mode == kGRU && a.has_bias) bhn[i] = to_f32<DT>(bhh[2 * a.H + j]);
     }
   }
@@ -453,9 +465,9 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
 
   float* acc = reinterpret_cast<float*>(lds + L.acc);
   const int mtiles = rup(a.bb, 16) / 16;
-  DT* yout = reinterpret_cast<DT*>(a.y);
-  DT* hn = reinterpret_cast<DT*>(a.h_n[d]);
-  DT* cn = reinterpret_cast<DT*>(a.c_n[d]);
+  DT* yout = reinterpret_cast<DT*>(a.y[ls]);
+  DT* hn = reinterpret_cast<DT*>(a.h_n[q]);
+  DT* cn = reinterpret_cast<DT*>(a.c_n[q]);
   // The block takes part in steps t < maxlen: forward t = 0 .. maxlen-1,
   // reverse t = maxlen-1 .. 0 (earlier reverse steps have no active row).
   const int nsteps = maxlen;
@@ -506,7 +518,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     const bool in = k1 < nsteps;
     const int t1 = in ? t_of(k1) : 0;
     const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(
-        reinterpret_cast<const char*>(a.gx) + (size_t)rowbase_of(t1) * DG * gsz, (uint32_t)(a.B * DG) * gsz);
+        reinterpret_cast<const char*>(a.gx[ls]) + (size_t)rowbase_of(t1) * DG * gsz, (uint32_t)(a.B * DG) * gsz);
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const bool act = in && t1 < lenreg[i];
@@ -734,6 +746,8 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
     const int b = b0 + er[i], j = j0 + eu[i];
     if (!PROJ && hn) hn[(size_t)b * a.K + j] = from_f32<DT>(hreg[i]);
     if (a.mode != kGRU && cn) cn[(size_t)b * a.H + j] = from_f32<DT>(creg[i]);
+    if (!PROJ && a.h_nf[q]) a.h_nf[q][(size_t)b * a.H + j] = hreg[i];
+    if (a.mode != kGRU && a.c_nf[q]) a.c_nf[q][(size_t)b * a.H + j] = creg[i];
   }
   if (PROJ && hn) {
 #pragma unroll

@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(kWaveThreads) scan_wave_kernel(ScanArgs a) {
   const int H = a.H, K = a.K, G = a.G;
   const int DG = a.D * G, DK = a.D * K;
   const bool rev = d == 1;
-  const int n = a.lengths ? __builtin_amdgcn_readfirstlane(a.lengths[b]) : a.T;
+  const int n = a.lengths ? __builtin_amdgcn_readfirstlane(a.lengths[b]) : a.T[0];
 
   // this lane's gate row: gate q, unit u
   const int q = lane / H, u = lane - q * H;
@@ -85,10 +85,10 @@ __global__ void __launch_bounds__(kWaveThreads) scan_wave_kernel(ScanArgs a) {
     const int t = t_of(k < n ? k : n - 1);
     // (fp32 G_x: the host keeps G_x in fp32 for layers this kernel runs)
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(reinterpret_cast<const float*>(a.gx) + ((size_t)(row_of(t) + b) * DG + d * G), (uint32_t)G * 4u);
+        make_rsrc(reinterpret_cast<const float*>(a.gx[0]) + ((size_t)(row_of(t) + b) * DG + d * G), (uint32_t)G * 4u);
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0));
   };
-  DT* y = reinterpret_cast<DT*>(a.y);
+  DT* y = reinterpret_cast<DT*>(a.y[0]);
 
   // One step. Steps past the sequence (the tail of the last group of four)
   // run the same instructions with the state kept and the store sent out of

@@ -180,11 +180,24 @@ typedef struct RnnDesc {
                             dtype (bf16 for bf16 storage: the product is
                             accumulated in fp32 and rounded once), RNN_GX_F32
                             (1) in fp32; must be 0 in the RSSM modes          */
-  int32_t reserved[2];   /* must be zero                                       */
+  int32_t layer_pipeline; /* launch-shape hint for unidirectional, padded,
+                            fixed-length stacks of >= 2 LSTM / GRU / LSTMP
+                            layers and T > 32: RNN_PIPE_AUTO (0) one launch
+                            scans a time chunk of every layer, layer l one
+                            chunk behind layer l - 1, when every layer's
+                            groups fit on the device at once and the
+                            launch-shape model expects a gain; RNN_PIPE_OFF
+                            (1) layer by layer; RNN_PIPE_ON (2) pipelined
+                            whenever it fits. Results are identical in all
+                            three. Must be 0 for RSSM                       */
+  int32_t reserved[1];   /* must be zero                                       */
 } RnnDesc;
 
 #define RNN_GX_AS_DTYPE 0
 #define RNN_GX_F32 1
+#define RNN_PIPE_AUTO 0
+#define RNN_PIPE_OFF 1
+#define RNN_PIPE_ON 2
 
 #define RNN_CLIP_CELL 1
 #define RNN_CLIP_PROJ 2
@@ -355,7 +368,10 @@ int rnn_read_status(const void* workspace, void* stream, int* device_status);
  * n_info >= 13, info[9..12] = {scan W_hh slice in registers (1) or LDS (0),
  * MFMA column tiles per wave (0: VALU), waves splitting K (VALU: K slices),
  * 16-byte chunks per tile per lane}; the plan assumes 16-byte aligned
- * weights. For inspection and tests; touches no device. */
+ * weights. With n_info >= 14, info[13] = the time chunk of a pipelined
+ * layer stack (0: layer by layer; when pipelined, "workgroups launched" is
+ * that of one launch scanning every layer's chunk). For inspection and
+ * tests; touches no device. */
 int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int xcds, int* info, int n_info);
 
 /* Training (backward through time; pytorch/pytorch issue "Integrating CuDNN

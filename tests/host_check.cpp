@@ -60,7 +60,8 @@ RnnDesc random_desc() {
   d.proj_clip = next_u32() % 7 == 0 ? -1.0f : 0.5f;
   d.actor_dim = d.mode == 4 ? (tame ? range(1, 64) : pick(kSizes)) : (next_u32() % 9 == 0 ? 3 : 0);
   d.gx_dtype = next_u32() % 6 == 0 ? pick({-1, 0, 1, 2}) : 0;
-  if (next_u32() % 25 == 0) d.reserved[next_u32() % 2] = 1;
+  d.layer_pipeline = next_u32() % 6 == 0 ? pick({-1, 0, 1, 2, 3}) : 0;
+  if (next_u32() % 25 == 0) d.reserved[0] = 1;
   return d;
 }
 

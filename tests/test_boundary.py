@@ -193,7 +193,7 @@ def test_actor_exchange_is_larger(lib):
 
 
 def test_reserved_fields_must_be_zero(lib):
-    for i in range(2):
+    for i in range(1):
         d = _desc()
         d.reserved[i] = 1
         assert _ws(d)[0] == E_SHAPE
@@ -207,6 +207,33 @@ def test_gx_dtype_values(lib):
     assert _ws(d)[0] == E_SHAPE
     d = _desc(mode=3, **RSSM_KW)
     d.gx_dtype = 1
+    assert _ws(d)[0] == E_UNSUPPORTED
+
+
+def test_layer_pipeline_values(lib):
+    """The layer-pipelining hint takes 0 (auto), 1 (off) and 2 (on); other
+    values are a shape error and the RSSM modes take only 0. Pipelining adds
+    per-layer chunk buffers to the workspace of a qualifying stack (two
+    layers, padded, unidirectional, T > 32) and nothing to one that does not
+    qualify (bidirectional)."""
+    kw = dict(mode=2, dtype=1, T=100, B=8, input_size=16, hidden_size=32, num_layers=2, proj_size=8)
+    sizes = {}
+    for v in (0, 1, 2):
+        d = _desc(**kw)
+        d.layer_pipeline = v
+        st, sizes[v] = _ws(d)
+        assert st == OK
+    assert sizes[0] == sizes[2] > sizes[1]
+    for v in (-1, 3):
+        d = _desc(**kw)
+        d.layer_pipeline = v
+        assert _ws(d)[0] == E_SHAPE
+    d = _desc(**dict(kw, bidirectional=1))
+    n_auto = _ws(d)[1]
+    d.layer_pipeline = 1
+    assert _ws(d)[1] == n_auto
+    d = _desc(mode=3, **RSSM_KW)
+    d.layer_pipeline = 2
     assert _ws(d)[0] == E_UNSUPPORTED
 
 

@@ -248,6 +248,55 @@ def test_determinism_bitwise():
             assert np.array_equal(x, y)
 
 
+# Layer-pipelined stacks (one launch scans a time chunk of every layer, layer
+# l one chunk behind layer l - 1; the state crosses chunk boundaries through
+# the workspace). Chunks of 32 steps, so each case has several chunks and a
+# ragged last one (1 step where T = 32 k + 1).
+PIPE_CASES = [
+    # name, mode, dtype, T, B, F, H, P, L, cell_clip, proj_clip
+    ("pipe_lstm_f32", "lstm", "f32", 130, 20, 24, 64, 0, 2, None, None),
+    ("pipe_gru_bf16_3l", "gru", "bf16", 129, 33, 40, 96, 0, 3, None, None),
+    ("pipe_lstmp_bf16", "lstmp", "bf16", 100, 32, 40, 128, 40, 2, None, None),
+    ("pipe_lstmp_f32_4l", "lstmp", "f32", 97, 17, 16, 48, 16, 4, None, None),
+    ("pipe_lstm_b2", "lstm", "f32", 100, 2, 8, 24, 0, 2, None, None),
+    ("pipe_lstmp_clip_bf16", "lstmp", "bf16", 100, 33, 40, 128, 40, 2, 0.4, 0.1),
+]
+
+
+def _desc_of(d):
+    import gru_sequence_scan_amd as gss
+    desc = gss.RnnDesc()
+    desc.mode, desc.dtype = gss.MODES[d["mode"]], 1 if d["dtype"] == "bf16" else 0
+    desc.T, desc.B, desc.input_size, desc.hidden_size = d["T"], d["B"], d["x"].shape[-1], d["hidden_size"]
+    desc.proj_size, desc.num_layers, desc.has_bias = d["proj_size"], d["num_layers"], 1
+    return desc
+
+
+@pytest.mark.parametrize("case", PIPE_CASES, ids=[c[0] for c in PIPE_CASES])
+def test_layer_pipeline(case):
+    """The pipelined stack gives the layer-by-layer run's results bit for
+    bit, and both match the oracle."""
+    import gru_sequence_scan_amd as gss
+    name, mode, dt, T, B, F, H, P, L, cc, pc = case
+    log(f"[gpu] layer pipeline case {name}")
+    d = synth.make_rnn_inputs(mode, T, B, F, H, proj_size=P, num_layers=L, dtype=dt,
+                              w_scale=(2.0 if cc else 1.0) / np.sqrt(H),
+                              seed=zlib.crc32(name.encode()) % 1000, h0_std=0.3, c0_std=0.3)
+    desc = _desc_of(d)
+    desc.layer_pipeline = gss.PIPE_MODES["on"]
+    assert gss.rnn_plan_info(desc)["pipe_chunk"] == 32
+    piped = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc, layer_pipeline="on")
+    layered = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc, layer_pipeline="off")
+    for a, b, what in zip(piped, layered, ("y", "h_n", "c_n")):
+        if b is not None:
+            assert np.array_equal(a, b), f"{name}: pipelined {what} differs from the layer-by-layer run"
+    lohi = None if cc is None else (-cc, cc)
+    _compare(d, piped, _oracle(d, cell_clip=lohi, proj_clip=pc), name)
+    if dt == "bf16":
+        got = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc, gx_dtype="f32", layer_pipeline="on")
+        _compare(d, got, _oracle(d, cell_clip=lohi, proj_clip=pc), name + " (fp32 G_x)")
+
+
 @pytest.mark.parametrize("mode,P", [("lstm", 0), ("gru", 0), ("lstmp", 16)])
 def test_time_chunking_matches_one_call(mode, P):
     log(f"[gpu] chunking {mode}")

@@ -68,7 +68,10 @@ def test_plan_is_coresident_and_covers(name, cus, xcds):
         assert p["rows"] * p["hidden_per_wg"] <= 1024
         if s.mode == "lstmp":
             assert p["proj_per_wg"] * p["members"] >= s.proj_size
-        groups = D * p["groups"]
+        # a pipelined stack scans a chunk of every layer in one launch
+        groups = D * p["groups"] * (s.num_layers if p["pipe_chunk"] else 1)
+        if p["pipe_chunk"]:
+            assert D == 1 and s.num_layers >= 2 and 1 <= p["pipe_chunk"] < s.T
         if p["groups_per_xcd"]:
             assert p["groups_per_xcd"] * xcds >= groups
             assert p["groups_per_xcd"] * p["members"] <= cus // xcds
@@ -199,3 +202,27 @@ def test_largest_hidden_sizes(mode, dtype, H, B, ok):
         with pytest.raises(gss.RnnError) as e:
             gss.rnn_plan_info(d)
         assert e.value.status == CODE["RNN_E_PLAN"]
+
+
+def test_layer_pipeline_plans():
+    """Which stacks the planner pipelines: the LSTMP stack (two layers of
+    7 ms scans) by default; a short or one-layer stack never (one chunk);
+    a bidirectional or packed stack never; "off" never; "on" whenever the
+    stack qualifies and its launch fits."""
+    _, d, _ = desc_for("lstmp_t1000_b32")
+    p = gss.rnn_plan_info(d)
+    assert p["pipe_chunk"] == 63 and p["workgroups"] == 256
+    d.layer_pipeline = gss.PIPE_MODES["off"]
+    assert gss.rnn_plan_info(d)["pipe_chunk"] == 0
+    _, d, lengths = desc_for("bilstm_varlen_b64")
+    d.layer_pipeline = gss.PIPE_MODES["on"]
+    assert gss.rnn_plan_info(d, lengths)["pipe_chunk"] == 0
+    _, d, _ = desc_for("gru_t256_b256")
+    d.layer_pipeline = gss.PIPE_MODES["on"]
+    assert gss.rnn_plan_info(d)["pipe_chunk"] == 0  # one layer
+    d.num_layers = 2
+    p = gss.rnn_plan_info(d)
+    assert p["pipe_chunk"] == 32
+    assert p["workgroups"] == 2 * p["groups"] * p["members"] or p["groups_per_xcd"] > 0
+    d.T = 32  # one chunk: nothing to overlap
+    assert gss.rnn_plan_info(d)["pipe_chunk"] == 0
