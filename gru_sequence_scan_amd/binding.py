@@ -186,7 +186,8 @@ def rnn_forward_raw(desc, weights, io, workspace_ptr, ws_bytes, stream_ptr):
 
 
 PLAN_FIELDS = ("kernel", "workgroups", "lds_bytes", "rows", "hidden_per_wg", "members", "proj_per_wg",
-               "groups", "groups_per_xcd", "wreg", "reg_tiles", "reg_ksplit", "reg_chunks", "pipe_chunk")
+               "groups", "groups_per_xcd", "wreg", "reg_tiles", "reg_ksplit", "reg_chunks", "pipe_chunk",
+               "model_step_ns")
 
 
 def rnn_plan_info(desc, lengths=None, cus=256, xcds=8):

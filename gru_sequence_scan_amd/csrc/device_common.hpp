@@ -73,6 +73,28 @@ __device__ __forceinline__ void coh_store_elem<bf16>(__amdgpu_buffer_rsrc_t rs, 
   coh_store2(rs, elem * 2u, __builtin_bit_cast(uint16_t, (bf16)v));
 }
 
+// Fill LDS from global memory for i = 0 .. n-1: value(i) loads element i
+// (or gives a constant), put(i, v) stores it. Each thread issues eight loads
+// before any of their stores waits; a plain loop waits for every load in
+// turn (the forward scan's W_hr slice, 32 such iterations per thread, took
+// 20 us to load that way).
+template <int kT, typename LoadFn, typename PutFn>
+__device__ __forceinline__ void lds_fill(int n, LoadFn value, PutFn put) {
+  for (int base = 0; base < n; base += 8 * kT) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kT + (int)threadIdx.x;
+      v[u] = i < n ? value(i) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * kT + (int)threadIdx.x;
+      if (i < n) put(i, v[u]);
+    }
+  }
+}
+
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() {
   __builtin_amdgcn_s_waitcnt(0);

@@ -162,9 +162,10 @@ struct WsLayout {
   int n_ints;
   // forward scan exchange, one block per layer: XCD ids, h ring, m ring
   size_t ex, ex_layer, ex_hx, ex_mx;  // first block, block size, ring offsets in a block
-  // layer pipelining (when the descriptor allows it): per-layer G_x of one
-  // time chunk, and the state carried between chunks (h in the storage
-  // dtype [B, K]; fp32 h and c [B, H]), two sets [2][num_layers] by parity
+  // layer pipelining (when the descriptor allows it): G_x of one time chunk
+  // for each layer above the first (layer 0's is all in gx), and the state
+  // carried between chunks (h in the storage dtype [B, K]; fp32 h and c
+  // [B, H]), two sets [2][num_layers] by parity
   size_t gxp, gxp_layer, sth, sth_layer, sthf, stcf, stf_layer;
 };
 
@@ -210,10 +211,13 @@ size_t mx_ring_bytes(const RnnDesc* d, const Dims& m) {
 }
 
 // Layer pipelining: a unidirectional, padded, fixed-length stack of >= 2
-// LSTM / GRU / LSTMP layers (not the one-wave scan) runs its layers on
-// separate streams, one time chunk apart. The shape depends only on the
-// descriptor, so the workspace size does too.
-constexpr int kPipeChunks = 16;    // time chunks aimed at
+// LSTM / GRU / LSTMP layers (not the one-wave scan) can be scanned in time
+// chunks, one launch per wave covering a chunk of every layer. The chunk
+// count balances the fixed cost of a wave (~40 us measured: exchange reset,
+// chunk product, scan launch) against the pipeline's fill and drain (L - 1
+// chunks): (n + L - 1) (F + s T / n) is least at n = sqrt((L - 1) s T / F),
+// i.e. sqrt((L - 1) T / 8) for steps of s ~ 5 us. The shape depends only on
+// the descriptor, so the workspace size does too.
 constexpr int kPipeMinChunk = 32;  // steps per chunk at least
 struct PipeShape {
   bool on;
@@ -221,10 +225,11 @@ struct PipeShape {
 };
 PipeShape pipe_shape(const RnnDesc* d, bool has_lengths, const Dims& m) {
   PipeShape ps{false, 0, 0};
-  if (d->layer_pipeline == RNN_PIPE_OFF || d->num_layers < 2 || d->bidirectional || d->layout != RNN_LAYOUT_PADDED ||
-      has_lengths || !is_rnn_mode(d->mode) || use_wave_scan(d, m))
+  if (d->layer_pipeline == RNN_PIPE_OFF || d->num_layers < 2 || d->bidirectional ||
+      d->layout != RNN_LAYOUT_PADDED || has_lengths || !is_rnn_mode(d->mode) || use_wave_scan(d, m))
     return ps;
-  const int chunk = std::max(kPipeMinChunk, cdiv(d->T, kPipeChunks));
+  const long n0 = std::lround(std::sqrt((d->num_layers - 1) * (double)d->T / 8.0));
+  const int chunk = std::max(kPipeMinChunk, cdiv(d->T, (int)std::max(2L, n0)));
   const int n = cdiv(d->T, chunk);
   if (n < 2) return ps;
   return PipeShape{true, chunk, n};
@@ -273,7 +278,7 @@ WsLayout layout_of(const RnnDesc* d, long long n_tok, bool has_lengths) {
   const PipeShape ps = pipe_shape(d, has_lengths, m);
   if (ps.on) {
     w.gxp_layer = align_up((size_t)ps.chunk * d->B * m.G * gx_esize(d, m) + 16, kAlign);
-    w.gxp = take(w.gxp_layer * d->num_layers);
+    w.gxp = take(w.gxp_layer * (d->num_layers - 1));  // layers 1 .. L-1 (layer 0 uses gx)
     // two sets, by chunk parity: a chunk reads one and writes the other
     w.sth_layer = align_up((size_t)d->B * m.K * m.esize, kAlign);
     w.sth = take(w.sth_layer * d->num_layers * 2);
@@ -775,15 +780,21 @@ ScanArgs layer_scan(const RnnDesc* d, const RnnWeights* w, const Dims& m, const 
 // so it needs num_layers x the workgroups of a single layer's scan, and the
 // stack takes nchunks + num_layers - 1 chunk scans instead of num_layers x
 // nchunks. It is taken when the cost model expects it to be faster.
-constexpr double kPipeWaveUs = 20.0, kLayerUs = 10.0;  // launch overheads (measured, MI355X)
+// Measured on MI355X: a scan step takes 2.3-2.9x the model's time (LSTMP
+// B=32 6.97 us vs 3.05, GRU B=256 3.86 vs 1.34, var-len BiLSTM 4.67 vs 1.73,
+// LSTM B=1 3.28 vs 1.21; the model ranks launch shapes, this scale makes it
+// absolute); fixed costs per pipelined wave and per layer.
+constexpr double kModelScale = 2.6, kPipeWaveUs = 40.0, kLayerUs = 35.0;
 struct ForwardPlan {
   bool wave, pipe;
   PipeShape ps;
   ScanPlan p;
+  double step_us;  // modelled time of one scan step of the chosen plan
 };
 int plan_forward(const RnnDesc* d, const Dims& m, bool has_len, int cus, int xcds, bool wreg_ok, bool training,
                  ForwardPlan* out) {
   ForwardPlan f{};
+  f.step_us = 0.0;
   f.wave = !training && use_wave_scan(d, m);
   if (f.wave) {
     *out = f;
@@ -799,22 +810,24 @@ int plan_forward(const RnnDesc* d, const Dims& m, bool has_len, int cus, int xcd
     // the launches around each scan (a wave: exchange reset, one G_x
     // product per active layer, the scan; a layer: its product and scan)
     const int L = d->num_layers, waves = f.ps.nchunks + L - 1;
-    const double tp = piped * (double)f.ps.chunk * waves + kPipeWaveUs * waves;
-    const double tl = one * (double)d->T * L + kLayerUs * L;
+    const double tp = kModelScale * piped * (double)f.ps.chunk * waves + kPipeWaveUs * waves;
+    const double tl = kModelScale * one * (double)d->T * L + kLayerUs * L;
     if (rc != RNN_OK || tp < tl || d->layer_pipeline == RNN_PIPE_ON) {
       f.pipe = true;
       f.p = pp;
     }
   }
+  f.step_us = f.pipe ? piped : one;
   if (!f.pipe && rc != RNN_OK) return rc;
   *out = f;
   return RNN_OK;
 }
 
-// Layer pipelining on the caller's stream, in waves: wave w resets the
-// exchange blocks of the active layers, computes layer l's G_x for its time
-// chunk c = w - l (from x, or from layer l - 1's output of chunk c, written
-// by the previous wave), and scans every active layer's chunk in one launch.
+// Layer pipelining on the caller's stream, in waves, after layer 0's G_x for
+// all steps: wave w resets the exchange blocks of the active layers,
+// computes layer l's (l > 0) G_x for its time chunk c = w - l from layer
+// l - 1's output of chunk c (written by the previous wave), and scans every
+// active layer's chunk in one launch.
 // The state crosses chunk boundaries through the workspace: h in the
 // storage dtype (the first step's operand, what the ring would hold) and
 // fp32 h and c (the registers), so the results are those of the
@@ -832,6 +845,12 @@ int forward_rnn_pipe(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, cha
   auto layer_out = [&](int l) -> char* {
     return l == nl - 1 ? (char*)io->y : ws + ((l % 2 == 0) ? L.inter0 : L.inter1);
   };
+  // layer 0's G_x for every step in one product (its input x is all there)
+  const size_t gxs = gx_esize(d, m);
+  const GemmArgs g0 = layer_gemm(d, w, m, 0, io->x, 0, (int)m.rows, ws + L.gx, gx_bf16, ws, L, true);
+  if ((rc = prof.begin(1, 0)) != RNN_OK) return rc;
+  if ((rc = hip_status(launch_gemm_xw(g0, bf16, st))) != RNN_OK) return rc;
+  if ((rc = prof.end()) != RNN_OK) return rc;
   auto sth = [&](int set, int l) { return ws + L.sth + ((size_t)set * nl + l) * L.sth_layer; };
   auto sthf = [&](int set, int l) { return (float*)(ws + L.sthf + ((size_t)set * nl + l) * L.stf_layer); };
   auto stcf = [&](int set, int l) { return (float*)(ws + L.stcf + ((size_t)set * nl + l) * L.stf_layer); };
@@ -847,12 +866,17 @@ int forward_rnn_pipe(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, cha
     for (int l = l0; l <= l1; ++l) {
       const int c = wv - l, t0 = c * chunk, tc = std::min(d->T, t0 + chunk) - t0;
       const bool first = c == 0, last = c == n - 1;
-      char* gxc = ws + L.gxp + l * L.gxp_layer;
-      const void* in = l == 0 ? io->x : (const void*)layer_out(l - 1);
-      const GemmArgs g = layer_gemm(d, w, m, l, in, (long long)t0 * B, tc * B, gxc, gx_bf16, ws, L, false);
-      if ((rc = prof.begin(1, l)) != RNN_OK) return rc;
-      if ((rc = hip_status(launch_gemm_xw(g, bf16, st))) != RNN_OK) return rc;
-      if ((rc = prof.end()) != RNN_OK) return rc;
+      char* gxc;
+      if (l == 0) {
+        gxc = ws + L.gx + (size_t)t0 * B * m.G * gxs;
+      } else {
+        gxc = ws + L.gxp + (size_t)(l - 1) * L.gxp_layer;
+        const GemmArgs g = layer_gemm(d, w, m, l, layer_out(l - 1), (long long)t0 * B, tc * B, gxc, gx_bf16, ws,
+                                      L, false);
+        if ((rc = prof.begin(1, l)) != RNN_OK) return rc;
+        if ((rc = hip_status(launch_gemm_xw(g, bf16, st))) != RNN_OK) return rc;
+        if ((rc = prof.end()) != RNN_OK) return rc;
+      }
       const ScanArgs al = layer_scan(d, w, m, f.p, xcds, l, ws, L);
       a.T[l] = tc;
       a.gx[l] = gxc;
@@ -1384,6 +1408,7 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
     info[9] = p.wreg; info[10] = p.rnt; info[11] = p.rks; info[12] = p.rcpt;
   }
   if (n_info >= 14) info[13] = f.pipe ? f.ps.chunk : 0;
+  if (n_info >= 15) info[14] = (int)std::lround(f.step_us * 1000.0);
   return RNN_OK;
 }
 

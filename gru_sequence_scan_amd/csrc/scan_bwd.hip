@@ -96,13 +96,14 @@ __global__ void __launch_bounds__(kBT) scan_bwd_kernel(ScanBwdArgs a) {
   if (tid == 0) *abort_flag = 0;
   for (int r = tid; r < a.bb; r += kBT) lens[r] = b0 + r < a.B ? (a.lengths ? a.lengths[b0 + r] : a.T) : 0;
   const float* W = a.w_hh[d];
-  for (int e = tid; e < a.Hp * a.kp; e += kBT) {
+  lds_fill<kBT>(a.Hp * a.kp, [&](int e) {
     const int c = e / a.kp, kk = e - c * a.kp;
     const int q = kk / a.hs, u = kk - q * a.hs;
-    float v = 0.f;
-    if (c < H && q < gates && u < hs_act) v = W[(size_t)(q * H + j0 + u) * H + c];
+    return (c < H && q < gates && u < hs_act) ? W[(size_t)(q * H + j0 + u) * H + c] : 0.f;
+  }, [&](int e, float v) {
+    const int c = e / a.kp, kk = e - c * a.kp;
     wt[c * L.wt_ld + kk] = v;
-  }
+  });
   for (int e = tid; e < tile_rows * L.as_ld; e += kBT) As[e] = 0.f;
   __syncthreads();
   int maxlen = 0;
@@ -377,15 +378,21 @@ __global__ void __launch_bounds__(kBT) scan_bwd_proj_kernel(ScanBwdArgs a) {
   for (int r = tid; r < a.bb; r += kBT) lens[r] = b0 + r < a.B ? (a.lengths ? a.lengths[b0 + r] : a.T) : 0;
   const float* Whh = a.w_hh[d];
   const float* Whr = a.w_hr[d];
-  for (int e = tid; e < a.Pp * a.kp; e += kBT) {
+  lds_fill<kBT>(a.Pp * a.kp, [&](int e) {
     const int p = e / a.kp, kk = e - p * a.kp;
     const int q = kk / a.hs, u = kk - q * a.hs;
-    wht[p * L.wht_ld + kk] = (p < P && q < 4 && u < hs_act) ? Whh[(size_t)(q * H + j0 + u) * P + p] : 0.f;
-  }
-  for (int e = tid; e < hsp * a.Pp; e += kBT) {
+    return (p < P && q < 4 && u < hs_act) ? Whh[(size_t)(q * H + j0 + u) * P + p] : 0.f;
+  }, [&](int e, float v) {
+    const int p = e / a.kp, kk = e - p * a.kp;
+    wht[p * L.wht_ld + kk] = v;
+  });
+  lds_fill<kBT>(hsp * a.Pp, [&](int e) {
     const int u = e / a.Pp, p = e - u * a.Pp;
-    wrt[u * L.wrt_ld + p] = (u < hs_act && p < P) ? Whr[(size_t)p * H + j0 + u] : 0.f;
-  }
+    return (u < hs_act && p < P) ? Whr[(size_t)p * H + j0 + u] : 0.f;
+  }, [&](int e, float v) {
+    const int u = e / a.Pp, p = e - u * a.Pp;
+    wrt[u * L.wrt_ld + p] = v;
+  });
   for (int e = tid; e < tile_rows * L.as_ld; e += kBT) As[e] = 0.f;
   const __amdgpu_buffer_rsrc_t ex2_rs = make_rsrc(a.ex2, (uint32_t)(D * a.B * a.Pp) * 4u);
   if (s == 0) {  // the padding columns of this block's dh_t rows read as zero

@@ -214,11 +214,38 @@ __device__ void load_tile_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t src_base_
 }
 
 // Load `nrows` weight rows into LDS as [nrows][ld], zero-padding k >= klen
-// and rows for which row_of() returns -1.
+// and rows for which row_of() returns -1. Rows of whole 16-byte chunks (the
+// usual case) move as 16-byte loads, eight in flight per thread before any
+// LDS store waits for them; otherwise element by element.
 template <typename DT, typename RowFn>
 __device__ __forceinline__ void load_weights(const DT* w, int klen, int kpad, int nrows, RowFn row_of, char* lds,
                              int off, int ld) {
   DT* dst = reinterpret_cast<DT*>(lds + off);
+  constexpr int kEpc = 16 / sizeof(DT);
+  if (klen % kEpc == 0 && ld % kEpc == 0 && (reinterpret_cast<uintptr_t>(w) & 15u) == 0) {
+    const int cpr = kpad / kEpc, total = nrows * cpr;
+    for (int base = 0; base < total; base += kScanThreads * 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = base + i * kScanThreads + threadIdx.x;
+        const int r = idx / cpr, cc = idx - r * cpr;
+        const int gr = idx < total ? row_of(r) : -1;
+        v[i] = gr >= 0 && cc * kEpc < klen
+                   ? *reinterpret_cast<const u32x4*>(w + (size_t)gr * klen + cc * kEpc)
+                   : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = base + i * kScanThreads + threadIdx.x;
+        if (idx < total) {
+          const int r = idx / cpr, cc = idx - r * cpr;
+          *reinterpret_cast<u32x4*>(dst + r * ld + cc * kEpc) = v[i];
+        }
+      }
+    }
+    return;
+  }
   const int total = nrows * kpad;
   for (int idx = threadIdx.x; idx < total; idx += kScanThreads) {
     const int r = idx / kpad, k = idx - r * kpad;
@@ -497,36 +524,43 @@ __device__ __forceinline__ void poll_tile(const PollGeom& g, uint32_t cur0, __am
   }
 }
 
-// Whether every member of a group runs on one XCD: each member publishes its
-// hardware XCC id (device-scope store into ids[member], which holds the
-// sentinel before the launch) and reads the others' (bounded wait). Called
-// by every thread; the answer is the same in every member. *ok turns false
-// when the wait ran out (the members were not all resident).
-__device__ bool group_on_one_xcd(unsigned* ids, int members, int me, int* ok_lds, int* flag_lds) {
+// Whether every member of a group runs on one XCD. publish_xcd: each member
+// stores its hardware XCC id (device-scope) into ids[member], which holds
+// the sentinel before the launch. group_on_one_xcd, called by every thread:
+// reads all members' ids at once, one thread each (bounded wait; one thread
+// reading them in turn took ~7 us for 32 members); the answer is the same in
+// every member. *ok turns false when the wait ran out (the members were not
+// all resident).
+__device__ __forceinline__ void publish_xcd(unsigned* ids, int members, int me) {
   if (threadIdx.x == 0) {
     unsigned hw;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(hw));
-    hw &= 0xFu;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(ids, (uint32_t)members * 4u);
-    coh_store4(xr, (uint32_t)me * 4u, hw);
-    bool same = true, ok = true;
+    coh_store4(make_rsrc(ids, (uint32_t)members * 4u), (uint32_t)me * 4u, hw & 0xFu);
+  }
+}
+__device__ bool group_on_one_xcd(unsigned* ids, int members, int* ok_lds, int* flag_lds) {
+  unsigned hw;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(hw));
+  hw &= 0xFu;
+  if (threadIdx.x == 0) {
+    *flag_lds = 1;
+    *ok_lds = 1;
+  }
+  __syncthreads();
+  // thread m reads member m's id (all in flight at once)
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(ids, (uint32_t)members * 4u);
+  for (int m = threadIdx.x; m < members; m += kScanThreads) {
+    unsigned polls = 0, id;
     uint64_t t0 = 0;
-    for (int m = 0; m < members && ok; ++m) {
-      unsigned polls = 0, id;
-      while ((id = coh_poll4(xr, (uint32_t)m * 4u)) == 0xFFFFFFFFu) {
-        if ((++polls & 63u) == 0) {
-          const uint64_t now = __builtin_amdgcn_s_memrealtime();
-          if (t0 == 0) t0 = now;
-          if (now - t0 > kWatchdogTicks) {
-            ok = false;
-            break;
-          }
-        }
+    while ((id = coh_poll4(xr, (uint32_t)m * 4u)) == 0xFFFFFFFFu) {
+      if ((++polls & 63u) == 0) {
+        const uint64_t now = __builtin_amdgcn_s_memrealtime();
+        if (t0 == 0) t0 = now;
+        if (now - t0 > kWatchdogTicks) break;
       }
-      same = same && id == hw;
     }
-    *flag_lds = same ? 1 : 0;
-    *ok_lds = ok ? 1 : 0;
+    if (id == 0xFFFFFFFFu) *ok_lds = 0;
+    else if (id != hw) *flag_lds = 0;
   }
   __syncthreads();
   return *flag_lds != 0;

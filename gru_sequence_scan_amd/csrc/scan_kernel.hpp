@@ -393,8 +393,11 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   DT* tile = reinterpret_cast<DT*>(lds + L.as);
   // Plain stores suffice for the ring when the whole group runs on one XCD.
   bool local = true;
-  if (!solo && a.ns > 1) {
-    local = group_on_one_xcd(a.xid[ls] + (size_t)grp * a.ns, a.ns, s, flags + 2, flags + 1);
+  if (a.ns > 1) {
+    // (publishing at kernel entry instead, to overlap the members' arrival
+    // with the weight loads, measured 12-16% slower steps on every shape)
+    publish_xcd(a.xid[ls] + (size_t)grp * a.ns, a.ns, s);
+    local = group_on_one_xcd(a.xid[ls] + (size_t)grp * a.ns, a.ns, flags + 2, flags + 1);
     if (!flags[2]) {
       if (tid == 0) __hip_atomic_store(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;

@@ -370,8 +370,9 @@ int rnn_read_status(const void* workspace, void* stream, int* device_status);
  * 16-byte chunks per tile per lane}; the plan assumes 16-byte aligned
  * weights. With n_info >= 14, info[13] = the time chunk of a pipelined
  * layer stack (0: layer by layer; when pipelined, "workgroups launched" is
- * that of one launch scanning every layer's chunk). For inspection and
- * tests; touches no device. */
+ * that of one launch scanning every layer's chunk). With n_info >= 15,
+ * info[14] = the launch-shape model's time per scan step in ns (0 for the
+ * one-wave and RSSM kernels). For inspection and tests; touches no device. */
 int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int xcds, int* info, int n_info);
 
 /* Training (backward through time; pytorch/pytorch issue "Integrating CuDNN

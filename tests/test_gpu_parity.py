@@ -250,16 +250,16 @@ def test_determinism_bitwise():
 
 # Layer-pipelined stacks (one launch scans a time chunk of every layer, layer
 # l one chunk behind layer l - 1; the state crosses chunk boundaries through
-# the workspace). Chunks of 32 steps, so each case has several chunks and a
-# ragged last one (1 step where T = 32 k + 1).
+# the workspace): several chunks each, with a ragged last one (1 step for
+# the T = 65, 97 and 129 cases, whose chunks are 32 steps).
 PIPE_CASES = [
-    # name, mode, dtype, T, B, F, H, P, L, cell_clip, proj_clip
-    ("pipe_lstm_f32", "lstm", "f32", 130, 20, 24, 64, 0, 2, None, None),
-    ("pipe_gru_bf16_3l", "gru", "bf16", 129, 33, 40, 96, 0, 3, None, None),
-    ("pipe_lstmp_bf16", "lstmp", "bf16", 100, 32, 40, 128, 40, 2, None, None),
-    ("pipe_lstmp_f32_4l", "lstmp", "f32", 97, 17, 16, 48, 16, 4, None, None),
-    ("pipe_lstm_b2", "lstm", "f32", 100, 2, 8, 24, 0, 2, None, None),
-    ("pipe_lstmp_clip_bf16", "lstmp", "bf16", 100, 33, 40, 128, 40, 2, 0.4, 0.1),
+    # name, mode, dtype, T, B, F, H, P, L, cell_clip, proj_clip, last chunk's steps
+    ("pipe_lstm_f32", "lstm", "f32", 130, 20, 24, 64, 0, 2, None, None, 31),
+    ("pipe_gru_bf16_3l", "gru", "bf16", 129, 33, 40, 96, 0, 3, None, None, 1),
+    ("pipe_lstmp_bf16", "lstmp", "bf16", 100, 32, 40, 128, 40, 2, None, None, 4),
+    ("pipe_lstmp_f32_4l", "lstmp", "f32", 97, 17, 16, 48, 16, 4, None, None, 1),
+    ("pipe_lstm_b2", "lstm", "f32", 100, 2, 8, 24, 0, 2, None, None, 4),
+    ("pipe_lstmp_clip_bf16", "lstmp", "bf16", 65, 33, 40, 128, 40, 2, 0.4, 0.1, 1),
 ]
 
 
@@ -277,14 +277,15 @@ def test_layer_pipeline(case):
     """The pipelined stack gives the layer-by-layer run's results bit for
     bit, and both match the oracle."""
     import gru_sequence_scan_amd as gss
-    name, mode, dt, T, B, F, H, P, L, cc, pc = case
+    name, mode, dt, T, B, F, H, P, L, cc, pc, tail = case
     log(f"[gpu] layer pipeline case {name}")
     d = synth.make_rnn_inputs(mode, T, B, F, H, proj_size=P, num_layers=L, dtype=dt,
                               w_scale=(2.0 if cc else 1.0) / np.sqrt(H),
                               seed=zlib.crc32(name.encode()) % 1000, h0_std=0.3, c0_std=0.3)
     desc = _desc_of(d)
     desc.layer_pipeline = gss.PIPE_MODES["on"]
-    assert gss.rnn_plan_info(desc)["pipe_chunk"] == 32
+    chunk = gss.rnn_plan_info(desc)["pipe_chunk"]
+    assert chunk >= 32 and T > chunk and T - (T - 1) // chunk * chunk == tail
     piped = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc, layer_pipeline="on")
     layered = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc, layer_pipeline="off")
     for a, b, what in zip(piped, layered, ("y", "h_n", "c_n")):
