@@ -98,6 +98,13 @@ struct ScanArgs {
   int gx_bf16;
   const int* lengths;  // device [B] or null (all T)
   const int* offsets;  // device [T + 1] (packed)
+  // One-wave scan with the input projection inside: x [rows, in_w] and the
+  // per-direction W_ih [G, in_w] and b_ih [G] (x null: G_x comes from gx)
+  const void* x;
+  int in_w;
+  const void* w_ih[kScanMaxSlots];
+  const void* b_ih[kScanMaxSlots];
+  int zero_status;     // the launch first clears *status (it is the forward's first)
   unsigned* counters;  // unused by the forward scan
   int* status;
 };
@@ -106,11 +113,15 @@ constexpr int kScanMaxWorkgroups = 4096;  // xid entries per layer
 hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
 constexpr int kScanRegChunks = 32;
 
-// Kernel 2b: one wavefront per (direction, batch row) when all gate rows of
-// a unit set fit one wave (LSTM H <= 16, GRU H <= 21; not LSTMP). Uses the
-// ScanArgs problem fields, slot 0's tensors, lengths, offsets and the clip
-// bounds; no tiling, exchange or counters.
+// Kernel 2b: one wave per (direction, batch row) when the gate rows of all
+// units fit one wave (LSTM and GRU with H <= 16; not LSTMP). Uses the
+// ScanArgs problem fields, slot 0's tensors, lengths, offsets, the clip
+// bounds, and x / in_w / w_ih / b_ih when it forms G_x itself
+// (scan_wave_fuses: x rows of at most 128 bytes in whole 16-byte chunks,
+// the longest sequence's x within 16 KB); no tiling, exchange or counters.
 bool scan_wave_fits(int mode, int H, int K);
+bool scan_wave_fuses(int in_w, int esize, long long max_steps);
+int scan_wave_lds_bytes(int in_w, int esize, long long max_steps);  // per workgroup (0 unless fused)
 int scan_wave_grid(int D, int B);
 hipError_t launch_scan_wave(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
 

@@ -674,9 +674,11 @@ int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* w
 }
 
 // The one-wave-per-row scan runs when every gate row of the layer fits one
-// wavefront and no tiling hint asks for the tiled scan.
+// wavefront and no tiling hint asks for the tiled scan (and y is addressed
+// with 32-bit byte offsets).
 bool use_wave_scan(const RnnDesc* d, const Dims& m) {
   if (d->tile_batch || d->tile_hidden || d->weights) return false;
+  if ((double)m.rows * m.D * m.K * m.esize >= 2147483647.0) return false;
   const int mk = d->mode == RNN_MODE_GRU ? kGRU : (d->mode == RNN_MODE_LSTMP ? kLSTMP : kLSTM);
   return scan_wave_fits(mk, d->hidden_size, m.K);
 }
@@ -945,8 +947,20 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     return RNN_E_PLAN;
   const ReserveLayout RL = reserve_of(d, m);
 
+  // The one-wave scan forms a narrow layer's G_x itself from x in LDS; when
+  // it does so for every layer, the forward is its launches alone (the
+  // first clears the status word, which nothing else here uses).
+  auto wave_fuses = [&](int l, const void* in) {
+    const int in_l = l == 0 ? d->input_size : m.D * m.K;
+    return wave && scan_wave_fuses(in_l, (int)es, t_max) && aligned(in, 16);
+  };
+  bool all_fused = wave && aligned(io->x, 16);
+  for (int l = 0; l < d->num_layers && all_fused; ++l) all_fused = wave_fuses(l, l == 0 ? io->x : ws);
+
   // ---- enqueue ----
-  if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
+  if (!all_fused &&
+      (rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK)
+    return rc;
   if (f.pipe) return forward_rnn_pipe(d, w, io, ws, L, m, f, st, xcds, prof);
   if (!wave &&
       (rc = hip_status(launch_fill_u32(ws + L.ex, L.ring_end - L.ex, 0xFFFFFFFFu, st))) != RNN_OK)
@@ -984,11 +998,15 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     void* layer_out = l == d->num_layers - 1 ? io->y
                       : rsv ? (void*)(rsv + RL.y[l])
                             : (void*)(ws + ((l % 2 == 0) ? L.inter0 : L.inter1));
-    // Kernel 1: Gx for every row of this layer, both directions.
-    const GemmArgs g = layer_gemm(d, w, m, l, layer_in, 0, (int)m.rows, gx, gx_bf16, ws, L, true);
-    if ((rc = prof.begin(1, l)) != RNN_OK) return rc;
-    if ((rc = hip_status(launch_gemm_xw(g, bf16, st))) != RNN_OK) return rc;
-    if ((rc = prof.end()) != RNN_OK) return rc;
+    // Kernel 1: Gx for every row of this layer, both directions (unless the
+    // one-wave scan forms it).
+    const bool fused = wave_fuses(l, layer_in);
+    if (!fused) {
+      const GemmArgs g = layer_gemm(d, w, m, l, layer_in, 0, (int)m.rows, gx, gx_bf16, ws, L, true);
+      if ((rc = prof.begin(1, l)) != RNN_OK) return rc;
+      if ((rc = hip_status(launch_gemm_xw(g, bf16, st))) != RNN_OK) return rc;
+      if ((rc = prof.end()) != RNN_OK) return rc;
+    }
 
     // Kernel 2: the scan.
     ScanArgs a = wave ? ScanArgs{} : layer_scan(d, w, m, p, xcds, l, ws, L);
@@ -1007,8 +1025,13 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
         const int i = l * m.D + di;
         a.w_hh[di] = w->w_hh[i];
         a.b_hh[di] = d->has_bias ? w->b_hh[i] : nullptr;
+        a.w_ih[di] = w->w_ih[i];
+        a.b_ih[di] = d->has_bias ? w->b_ih[i] : nullptr;
       }
       a.status = (int*)(ws + L.status);
+      a.x = fused ? layer_in : nullptr;
+      a.in_w = l == 0 ? d->input_size : m.D * m.K;
+      a.zero_status = all_fused && l == 0;
     }
     a.nslot = 1;
     a.T[0] = t_max;
@@ -1394,7 +1417,9 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
   const Dims m = dims_of(desc, n_tok);
   if (use_wave_scan(desc, m)) {
     // one wave per (direction, row): no co-residency needed, no LDS
-    info[0] = 4; info[1] = scan_wave_grid(m.D, desc->B); info[2] = 0; info[3] = 1; info[4] = desc->hidden_size;
+    info[0] = 4; info[1] = scan_wave_grid(m.D, desc->B);
+    info[2] = scan_wave_lds_bytes(desc->input_size, m.esize, t_max);  // x staged for layer 0
+    info[3] = 1; info[4] = desc->hidden_size;
     info[5] = 1; info[6] = 0; info[7] = desc->B; info[8] = 0;
     return RNN_OK;
   }

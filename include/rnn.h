@@ -358,10 +358,11 @@ int rnn_read_status(const void* workspace, void* stream, int* device_status);
 /* Host-only: the launch shape rnn_forward would use for this problem on a
  * device with `cus` compute units in `xcds` chiplets (XCDs; workgroups are
  * dealt to them round-robin). info[0..8] = {kernel (2 tiled scan, 3 RSSM,
- * 4 one-wave-per-row scan: LSTM with H <= 16 or GRU with H <= 21 when no
+ * 4 one-wave-per-row scan: LSTM or GRU with H <= 16 when no
  * tiling hint is set; its waves are independent, so it needs no
  * co-residency),
- * workgroups launched, LDS bytes per workgroup, batch rows per workgroup,
+ * workgroups launched, LDS bytes per workgroup (kernel 4: the x rows it
+ * stages when it forms layer 0's input projection itself), batch rows per workgroup,
  * hidden units per workgroup, workgroups per group, projection outputs per
  * workgroup (LSTMP), number of groups (per direction for the scan), groups
  * per XCD when every group sits on one XCD (else 0)}; n_info >= 9. With

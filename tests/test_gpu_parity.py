@@ -68,9 +68,12 @@ SMALL = [
     ("lstm_splitk_pipe", "lstm", "f32", 4, 9, 256, 72, 0, 1, False, "padded", None, True, False),
     ("bilstm_splitk_packed", "lstm", "f32", 7, 6, 160, 96, 0, 2, True, "packed", (1, 7), True, True),
     # bf16 G_x rows of odd width (3H with H odd): a step's rows start at a
-    # 2-byte offset; and the one-wave kernel on bf16 storage (G = 63)
+    # 2-byte offset; and the one-wave kernel on bf16 storage (G = 45), its
+    # input (8 bf16) narrow enough for the projection inside the kernel
     ("gru_odd_bf16", "gru", "bf16", 9, 18, 24, 33, 0, 1, False, "padded", None, True, True),
-    ("gru_wave_bf16", "gru", "bf16", 11, 3, 8, 21, 0, 1, False, "padded", None, True, True),
+    ("gru_wave_bf16", "gru", "bf16", 11, 3, 8, 15, 0, 1, False, "padded", None, True, True),
+    # GRU just past the one-wave kernel's width (H = 17): the tiled scan
+    ("gru_h17_tiled", "gru", "f32", 9, 3, 8, 17, 0, 1, False, "padded", None, True, True),
 ]
 
 
@@ -196,7 +199,13 @@ WAVE_CASES = [
     # name, mode, dtype, T, B, F, H, L, bidir, layout, varlen, bias, cell_clip
     ("wave_lstm_h16_b1", "lstm", "f32", 40, 1, 16, 16, 1, False, "padded", None, True, None),
     ("wave_bilstm_packed", "lstm", "f32", 17, 9, 12, 16, 2, True, "packed", (1, 17), True, None),
-    ("wave_gru_h21_bf16", "gru", "bf16", 23, 6, 20, 21, 2, False, "padded", None, True, None),
+    ("wave_gru_h16_bf16", "gru", "bf16", 23, 6, 20, 16, 2, False, "padded", None, True, None),
+    # input projection inside the kernel (x staged in LDS) and from kernel 1:
+    # fp32 rows of 8 (fused), a sequence whose x passes 16 KB (kernel 1),
+    # bf16 rows of 16 (fused) in both directions of a two-layer stack
+    ("wave_gru_fused_f32", "gru", "f32", 30, 5, 8, 12, 1, False, "padded", None, True, None),
+    ("wave_lstm_long_unfused", "lstm", "f32", 200, 2, 32, 16, 1, False, "padded", None, True, None),
+    ("wave_bilstm_fused_bf16", "lstm", "bf16", 40, 7, 16, 8, 2, True, "padded", "unsorted", True, (-0.4, 0.3)),
     ("wave_gru_h1", "gru", "f32", 9, 3, 4, 1, 1, False, "padded", None, True, None),
     ("wave_lstm_h5_varlen", "lstm", "f32", 15, 7, 6, 5, 1, True, "padded", "unsorted", True, None),
     ("wave_lstm_clip", "lstm", "f32", 12, 4, 8, 12, 1, False, "padded", None, True, (-0.3, 0.25)),

@@ -52,7 +52,8 @@ def test_plan_is_coresident_and_covers(name, cus, xcds):
         # one independent wave per (direction, row): any grid size works
         D = 2 if s.bidirectional else 1
         assert s.mode in ("lstm", "gru") and (3 if s.mode == "gru" else 4) * s.hidden_size <= 64
-        assert p["workgroups"] * 4 >= D * s.B and p["lds_bytes"] == 0
+        # (LDS only for x staged by the kernel's own input projection)
+        assert p["workgroups"] * 4 >= D * s.B and p["lds_bytes"] in (0, 4 * 16384)
         return
     assert p["workgroups"] <= cus
     assert 0 < p["lds_bytes"] <= LDS_MAX
@@ -137,7 +138,7 @@ def test_forced_register_layouts(case):
     assert (p["wreg"], p["reg_tiles"], p["reg_ksplit"], p["reg_chunks"]) == expect
 
 
-@pytest.mark.parametrize("mode,H,expect", [("lstm", 16, 4), ("lstm", 17, 2), ("gru", 21, 4), ("gru", 22, 2),
+@pytest.mark.parametrize("mode,H,expect", [("lstm", 16, 4), ("lstm", 17, 2), ("gru", 16, 4), ("gru", 17, 2),
                                            ("lstm", 1, 4), ("lstmp", 8, 2)])
 def test_wave_scan_choice(mode, H, expect):
     d = gss.RnnDesc()
