@@ -95,6 +95,18 @@ __device__ __forceinline__ void lds_fill(int n, LoadFn value, PutFn put) {
   }
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations (the s_waitcnt immediate keeps vmcnt and expcnt at their
+// maximum, lgkmcnt 0) and meets the other waves. __syncthreads also drains
+// every outstanding global store, which a barrier that only orders LDS
+// accesses does not need.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() {
   __builtin_amdgcn_s_waitcnt(0);

@@ -11,17 +11,6 @@ namespace {
 
 constexpr int kScanThreads = 256;
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS
-// operations (the s_waitcnt immediate keeps vmcnt and expcnt at their
-// maximum, lgkmcnt 0) and meets the other waves. __syncthreads also drains
-// every outstanding global store, which a barrier that only orders LDS
-// accesses does not need.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // One 16-byte chunk per lane of each operand feeds one 16x16 MFMA step:
 // bf16 16x16x32 takes 8 values of k per lane directly; fp32 16x16x4 takes

@@ -293,8 +293,10 @@ __device__ __forceinline__ void reduce_ksplit(const float* red, int rks, int row
 
 // EPT: gate elements (and, for LSTMP, projection outputs) owned per thread,
 // 1, 2 or 4 (bb * hs <= 256 * EPT). PROJ: LSTMP (the hidden projection).
-// GXB: G_x stored as bf16 (bf16 storage only).
-template <typename DT, bool WREG, int EPT, bool PROJ, bool GXB>
+// GXB: G_x stored as bf16 (bf16 storage only). RSV: training, the gate
+// values go to the reserve (fp32 only; the forward instances carry none of
+// that code or its scalar state).
+template <typename DT, bool WREG, int EPT, bool PROJ, bool GXB, bool RSV>
 __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const ScanLds L = scan_lds(a, (int)sizeof(DT));
@@ -668,7 +670,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
         ring_store<DT>(hx_rs, hx_el(k, b, j), h, local);
       else
         ring_store<DT>(mx_rs, mx_el(k, b, j), h, local);
-      if (a.rsv) {
+      if (RSV) {
         const int nsv = a.mode == kGRU ? 4 : 5;
         float* rv = a.rsv + ((size_t)(rowbase + b) * a.D + d) * (nsv * a.H) + j;
 #pragma unroll
@@ -765,29 +767,30 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(ScanArgs a) {
 
 
 // Launch of one instance: EPT from the owned elements, PROJ from the mode.
-template <typename DT, bool WREG, int EPT, bool PROJ, bool GXB>
+template <typename DT, bool WREG, int EPT, bool PROJ, bool GXB, bool RSV>
 hipError_t launch_scan_as(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<DT, WREG, EPT, PROJ, GXB>,
+  hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<DT, WREG, EPT, PROJ, GXB, RSV>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((scan_kernel<DT, WREG, EPT, PROJ, GXB>), grid, dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((scan_kernel<DT, WREG, EPT, PROJ, GXB, RSV>), grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
-template <typename DT, bool WREG, bool PROJ, bool GXB>
+template <typename DT, bool WREG, bool PROJ, bool GXB, bool RSV>
 hipError_t launch_scan_ept(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
   const int own = max(a.bb * a.hs, PROJ ? a.bb * a.ps : 0);
-  if (own <= kThreads) return launch_scan_as<DT, WREG, 1, PROJ, GXB>(a, lds, grid, stream);
-  if (own <= 2 * kThreads) return launch_scan_as<DT, WREG, 2, PROJ, GXB>(a, lds, grid, stream);
-  if (own <= kMaxEpt * kThreads) return launch_scan_as<DT, WREG, kMaxEpt, PROJ, GXB>(a, lds, grid, stream);
+  if (own <= kThreads) return launch_scan_as<DT, WREG, 1, PROJ, GXB, RSV>(a, lds, grid, stream);
+  if (own <= 2 * kThreads) return launch_scan_as<DT, WREG, 2, PROJ, GXB, RSV>(a, lds, grid, stream);
+  if (own <= kMaxEpt * kThreads) return launch_scan_as<DT, WREG, kMaxEpt, PROJ, GXB, RSV>(a, lds, grid, stream);
   return hipErrorInvalidValue;
 }
 
-// bf16 G_x only with bf16 storage.
-template <typename DT, bool WREG, bool GXB>
+// bf16 G_x only with bf16 storage; RSV: the training instances (a.rsv set).
+template <typename DT, bool WREG, bool GXB, bool RSV = false>
 hipError_t launch_scan_proj(const ScanArgs& a, int lds, dim3 grid, hipStream_t stream) {
-  return a.mode == kLSTMP ? launch_scan_ept<DT, WREG, true, GXB>(a, lds, grid, stream)
-                          : launch_scan_ept<DT, WREG, false, GXB>(a, lds, grid, stream);
+  if ((a.rsv != nullptr) != RSV) return hipErrorInvalidValue;
+  return a.mode == kLSTMP ? launch_scan_ept<DT, WREG, true, GXB, RSV>(a, lds, grid, stream)
+                          : launch_scan_ept<DT, WREG, false, GXB, RSV>(a, lds, grid, stream);
 }
 
 }  // namespace
