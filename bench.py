@@ -63,13 +63,13 @@ KERNEL_SOURCES = {
 # with those of the first input GEMM ("gemm_counters"). Valid only for the
 # kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 9898338, "write_bytes": 3564000, "sources": "52f6c92e145ab8a3", "counters": {"mfma_flops": 4199424000, "mfma_busy": 0.07796, "lds_active": 0.07389, "lds_bank_conflict": 0.07161}},
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1476791, "write_bytes": 88576, "sources": "d624821b153aaffe", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 0.00422, "lds_bank_conflict": 0.0}, "gemm_counters": {"mfma_flops": 134217728, "mfma_busy": 0.0465, "lds_active": 0.00668, "lds_bank_conflict": 0.0}, "gemm_sources": "ec46422efff7389b"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 215440119, "write_bytes": 68427776, "sources": "d624821b153aaffe", "counters": {"mfma_flops": 137438953472, "mfma_busy": 0.05473, "lds_active": 0.10173, "lds_bank_conflict": 0.33589}, "gemm_counters": {"mfma_flops": 103079215104, "mfma_busy": 0.25933, "lds_active": 0.43716, "lds_bank_conflict": 0.2963}, "gemm_sources": "ec46422efff7389b"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": 0, "fetch_bytes": 267927065, "write_bytes": 16795648, "sources": "d624821b153aaffe", "counters": {"mfma_flops": 100663296000, "mfma_busy": 0.00562, "lds_active": 0.02485, "lds_bank_conflict": 0.31987}, "gemm_counters": {"mfma_flops": 83886080000, "mfma_busy": 0.21039, "lds_active": 0.37412, "lds_bank_conflict": 0.27778}, "gemm_sources": "ec46422efff7389b"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 351826879, "write_bytes": 80773120, "sources": "d624821b153aaffe", "counters": {"mfma_flops": 95093260288, "mfma_busy": 0.2607, "lds_active": 0.08959, "lds_bank_conflict": 0.40563}, "gemm_counters": {"mfma_flops": 40802189312, "mfma_busy": 0.72956, "lds_active": 0.06262, "lds_bank_conflict": 0.0}, "gemm_sources": "ec46422efff7389b"},
-    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 89032, "write_bytes": 16512, "sources": "58978e0d28e6f30c", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 5e-05, "lds_bank_conflict": 0.0}, "gemm_counters": {"mfma_flops": 1048576, "mfma_busy": 0.00036, "lds_active": 0.00016, "lds_bank_conflict": 0.0}, "gemm_sources": "ec46422efff7389b"},
-    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347691609, "write_bytes": 56108557, "sources": "52f6c92e145ab8a3", "counters": {"mfma_flops": 7234560000, "mfma_busy": 0.08346, "lds_active": 0.11099, "lds_bank_conflict": 0.1031}},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 9898568, "write_bytes": 3564000, "sources": "1fa3a10ef8bc7db5", "counters": {"mfma_flops": 4199424000, "mfma_busy": 0.0778, "lds_active": 0.07373, "lds_bank_conflict": 0.07161}},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1477917, "write_bytes": 88576, "sources": "b1ed972d277a206b", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 0.00459, "lds_bank_conflict": 0.0}, "gemm_counters": {"mfma_flops": 134217728, "mfma_busy": 0.0463, "lds_active": 0.00673, "lds_bank_conflict": 0.0}, "gemm_sources": "1332b5e0f7b74dcc"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 215456733, "write_bytes": 68427776, "sources": "b1ed972d277a206b", "counters": {"mfma_flops": 137438953472, "mfma_busy": 0.0538, "lds_active": 0.09999, "lds_bank_conflict": 0.33587}, "gemm_counters": {"mfma_flops": 103079215104, "mfma_busy": 0.2609, "lds_active": 0.43678, "lds_bank_conflict": 0.2963}, "gemm_sources": "1332b5e0f7b74dcc"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": "0-1", "fetch_bytes": 54539386, "write_bytes": 3594581, "sources": "b1ed972d277a206b", "counters": {"mfma_flops": 16777216000, "mfma_busy": 0.01005, "lds_active": 0.04481, "lds_bank_conflict": 0.32038}, "gemm_counters": {"mfma_flops": 83886080000, "mfma_busy": 0.21982, "lds_active": 0.4018, "lds_bank_conflict": 0.27778}, "gemm_sources": "1332b5e0f7b74dcc"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 351878460, "write_bytes": 80773120, "sources": "b1ed972d277a206b", "counters": {"mfma_flops": 95093260288, "mfma_busy": 0.26371, "lds_active": 0.091, "lds_bank_conflict": 0.40562}, "gemm_counters": {"mfma_flops": 40802189312, "mfma_busy": 0.72909, "lds_active": 0.06201, "lds_bank_conflict": 0.0}, "gemm_sources": "1332b5e0f7b74dcc"},
+    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 44363, "write_bytes": 16544, "sources": "3942465c319d76a2", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 0.00012, "lds_bank_conflict": 0.0}},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347652417, "write_bytes": 56108947, "sources": "1fa3a10ef8bc7db5", "counters": {"mfma_flops": 7234560000, "mfma_busy": 0.08451, "lds_active": 0.10773, "lds_bank_conflict": 0.1031}},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
