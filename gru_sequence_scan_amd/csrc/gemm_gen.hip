@@ -272,13 +272,13 @@ hipError_t launch_gemm_gen(const GemmGenArgs& in, hipStream_t stream) {
   if (e != hipSuccess) return e;
   dim3 grid((a.N + kBN - 1) / kBN, (a.M + kBM - 1) / kBM, splits);
   if (a_kfast)
-    hipLaunchKernelGGL(gemm_gen_kernel<true>, grid, dim3(kGemmThreads), kGemmLds, stream, a, kchunk);
+    launch_kernel(gemm_gen_kernel<true>, grid, dim3(kGemmThreads), kGemmLds, stream, a, kchunk);
   else
-    hipLaunchKernelGGL(gemm_gen_kernel<false>, grid, dim3(kGemmThreads), kGemmLds, stream, a, kchunk);
+    launch_kernel(gemm_gen_kernel<false>, grid, dim3(kGemmThreads), kGemmLds, stream, a, kchunk);
   if ((e = hipGetLastError()) != hipSuccess || splits == 1) return e;
   const long long mn = (long long)a.M * a.N;
   const int blocks = (int)std::min<long long>((mn + 255) / 256, 4096);
-  hipLaunchKernelGGL(gemm_split_reduce_kernel, dim3(blocks), dim3(256), 0, stream, a.part, splits, a.M, a.N, a.C,
+  launch_kernel(gemm_split_reduce_kernel, dim3(blocks), dim3(256), 0, stream, a.part, splits, a.M, a.N, a.C,
                      a.ldc, a.accumulate);
   return hipGetLastError();
 }
@@ -287,15 +287,15 @@ hipError_t launch_colsum(const float* A, long long lda, int M, int N, float* par
                          hipStream_t stream) {
   if (N <= 0) return hipSuccess;
   dim3 g1((N + 255) / 256, nchunk);
-  hipLaunchKernelGGL(colsum_partial_kernel, g1, dim3(256), 0, stream, A, lda, M, N, partial, nchunk);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, (const float*)partial, N,
+  launch_kernel(colsum_partial_kernel, g1, dim3(256), 0, stream, A, lda, M, N, partial, nchunk);
+  launch_kernel(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, (const float*)partial, N,
                      nchunk, out);
   return hipGetLastError();
 }
 
 hipError_t launch_hprev(const HprevArgs& a, hipStream_t stream) {
   dim3 grid((a.B * a.H + 255) / 256, a.T);
-  hipLaunchKernelGGL(hprev_kernel, grid, dim3(256), 0, stream, a);
+  launch_kernel(hprev_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

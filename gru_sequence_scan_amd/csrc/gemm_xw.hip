@@ -479,14 +479,14 @@ hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream)
   const bool pipe = !dtype_bf16 && a.vec_ok && a.zero16 && a.K % (kRowBytes / 4) == 0;
   if (dtype_bf16) {
     if (pipe)
-      hipLaunchKernelGGL(gemm_xw_pipe_kernel<bf16>, grid, block, 0, stream, a);
+      launch_kernel(gemm_xw_pipe_kernel<bf16>, grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL(gemm_xw_kernel<bf16>, grid, block, 0, stream, a);
+      launch_kernel(gemm_xw_kernel<bf16>, grid, block, 0, stream, a);
   } else {
     if (pipe)
-      hipLaunchKernelGGL(gemm_xw_pipe_kernel<float>, grid, block, 0, stream, a);
+      launch_kernel(gemm_xw_pipe_kernel<float>, grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL(gemm_xw_kernel<float>, grid, block, 0, stream, a);
+      launch_kernel(gemm_xw_kernel<float>, grid, block, 0, stream, a);
   }
   if (a.splits > 1) {
     hipError_t e = hipGetLastError();
@@ -494,9 +494,9 @@ hipError_t launch_gemm_xw(const GemmArgs& a, int dtype_bf16, hipStream_t stream)
     const size_t work = ((size_t)a.M * a.N + 3) / 4;
     const int blocks = (int)std::min<size_t>(1024, (work + 255) / 256);
     if (dtype_bf16)
-      hipLaunchKernelGGL(gemm_xw_reduce_kernel<bf16>, dim3(blocks), block, 0, stream, a);
+      launch_kernel(gemm_xw_reduce_kernel<bf16>, dim3(blocks), block, 0, stream, a);
     else
-      hipLaunchKernelGGL(gemm_xw_reduce_kernel<float>, dim3(blocks), block, 0, stream, a);
+      launch_kernel(gemm_xw_reduce_kernel<float>, dim3(blocks), block, 0, stream, a);
   }
   return hipGetLastError();
 }

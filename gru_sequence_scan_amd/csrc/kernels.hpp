@@ -1,10 +1,29 @@
 // Launch interface between the host library and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace rnnk {
+
+// Timing events for the launches of one bracket (host side, per thread; set
+// only by the profiled entry point). The first launch after they are set
+// records `start` when its dispatch begins; every launch records `stop` when
+// it completes. The events travel with the dispatch packets, so timing adds
+// no packets (and no gaps) between kernels.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream, Args... args) {
+  LaunchEvents& ev = launch_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev.start, ev.stop, 0u, args...);
+  ev.start = nullptr;
+}
 
 // Kernel 1: Gx = X W^T + folded bias, both directions in one launch.
 struct GemmArgs {
@@ -256,6 +275,9 @@ hipError_t launch_write_ints(int* dst, const int* src, int n, hipStream_t stream
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 // Fill with a 32-bit pattern (bytes a multiple of 4).
 hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t value, hipStream_t stream);
+// Two fills in one launch: bytes1 at p1 with value1, bytes2 at p2 with value2.
+hipError_t launch_fill2_u32(void* p1, size_t bytes1, uint32_t value1, void* p2, size_t bytes2, uint32_t value2,
+                            hipStream_t stream);
 // *dst = *src (one int, stream-ordered).
 hipError_t launch_copy_int(int* dst, const int* src, hipStream_t stream);
 // Device-coherent round trip between two workgroups on different XCDs:

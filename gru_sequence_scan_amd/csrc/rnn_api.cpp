@@ -18,6 +18,11 @@
 
 using namespace rnnk;
 
+rnnk::LaunchEvents& rnnk::launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -584,7 +589,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? RNN_OK : RNN_E_HIP; }
 
 // Optional per-kernel event brackets (rnn_forward_profiled).
 // kinds[n] = kernel kind | layer << 8 (kind 5, a pipelined scan: first
-// layer | last layer << 4).
+// layer | last layer << 4). The bracket's events ride on its launches
+// (start with the first dispatch, stop with the last completion); a bracket
+// that launched nothing records both directly.
 struct Prof {
   void* const* events = nullptr;
   int n_events = 0;
@@ -593,17 +600,27 @@ struct Prof {
   hipStream_t st = nullptr;
   int begin(int kind, int layer) {
     if (kinds && n < n_events / 2) kinds[n] = kind | layer << 8;
-    if (events && n < n_events / 2)
-      return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[2 * n]), st));
+    if (events && n < n_events / 2) {
+      rnnk::LaunchEvents& ev = rnnk::launch_events();
+      ev.start = reinterpret_cast<hipEvent_t>(events[2 * n]);
+      ev.stop = reinterpret_cast<hipEvent_t>(events[2 * n + 1]);
+    }
     return RNN_OK;
   }
   int end() {
     int rc = RNN_OK;
-    if (events && n < n_events / 2)
-      rc = hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(events[2 * n + 1]), st));
+    rnnk::LaunchEvents& ev = rnnk::launch_events();
+    if (events && n < n_events / 2 && ev.start) {
+      rc = hip_status(hipEventRecord(ev.start, st));
+      if (rc == RNN_OK) rc = hip_status(hipEventRecord(ev.stop, st));
+    }
+    ev = rnnk::LaunchEvents{};
     ++n;
     return rc;
   }
+  // an early return inside a bracket must not leave events armed for a
+  // later call on this thread
+  ~Prof() { rnnk::launch_events() = rnnk::LaunchEvents{}; }
 };
 
 int check_ptr(const void* p, size_t elem) {
@@ -659,15 +676,15 @@ int forward_rssm(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* w
   a.xid = (unsigned*)(ws + L.xid);
   a.counters = (unsigned*)(ws + L.counters);
   a.status = (int*)(ws + L.status);
-  // status word and counters are contiguous at the start of the workspace
-  if ((rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK) return rc;
-  if (p.reg) {
-    // the XCC ids and both rings start as the sentinel: ids, h ring and the
-    // used front of the partial ring are consecutive (the fill covers the
-    // alignment gaps between them too)
-    const size_t end = L.ex_p + (size_t)rssm_ring_slots() * d->B * p.nw * a.Ep * 4;
-    if ((rc = hip_status(launch_fill_u32(ws + L.xid, end - L.xid, 0xFFFFFFFFu, st))) != RNN_OK) return rc;
-  }
+  // status word and counters are contiguous at the start of the workspace;
+  // for kernel 3b the XCC ids and both rings start as the sentinel: ids, h
+  // ring and the used front of the partial ring are consecutive (the fill
+  // covers the alignment gaps between them too). One launch does both.
+  const size_t zero_bytes = L.counters + L.counters_bytes;
+  const size_t ring_end = L.ex_p + (size_t)rssm_ring_slots() * d->B * p.nw * a.Ep * 4;
+  if ((rc = hip_status(launch_fill2_u32(ws, zero_bytes, 0u, ws + L.xid, p.reg ? ring_end - L.xid : 0, 0xFFFFFFFFu,
+                                        st))) != RNN_OK)
+    return rc;
   if ((rc = prof.begin(3, 0)) != RNN_OK) return rc;
   if ((rc = hip_status(p.reg ? launch_rssm_reg(a, st) : launch_rssm(a, st))) != RNN_OK) return rc;
   return prof.end();
@@ -850,6 +867,11 @@ int forward_rnn_pipe(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, cha
   // layer 0's G_x for every step in one product (its input x is all there)
   const size_t gxs = gx_esize(d, m);
   const GemmArgs g0 = layer_gemm(d, w, m, 0, io->x, 0, (int)m.rows, ws + L.gx, gx_bf16, ws, L, true);
+  // status word, counters (and the GEMM's zero chunk beside them) and the
+  // first wave's exchange (layer 0 only), before anything reads them
+  if ((rc = hip_status(launch_fill2_u32(ws, L.counters + L.counters_bytes, 0u, ws + L.ex, L.ex_layer, 0xFFFFFFFFu,
+                                        st))) != RNN_OK)
+    return rc;
   if ((rc = prof.begin(1, 0)) != RNN_OK) return rc;
   if ((rc = hip_status(launch_gemm_xw(g0, bf16, st))) != RNN_OK) return rc;
   if ((rc = prof.end()) != RNN_OK) return rc;
@@ -858,8 +880,8 @@ int forward_rnn_pipe(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, cha
   auto stcf = [&](int set, int l) { return (float*)(ws + L.stcf + ((size_t)set * nl + l) * L.stf_layer); };
   for (int wv = 0; wv < n + nl - 1; ++wv) {
     const int l0 = std::max(0, wv - n + 1), l1 = std::min(nl - 1, wv);
-    if ((rc = hip_status(launch_fill_u32(ws + L.ex + l0 * L.ex_layer, (size_t)(l1 - l0 + 1) * L.ex_layer,
-                                         0xFFFFFFFFu, st))) != RNN_OK)
+    if (wv > 0 && (rc = hip_status(launch_fill_u32(ws + L.ex + l0 * L.ex_layer, (size_t)(l1 - l0 + 1) * L.ex_layer,
+                                                   0xFFFFFFFFu, st))) != RNN_OK)
       return rc;
     ScanArgs a = layer_scan(d, w, m, f.p, xcds, 0, ws, L);
     a.nslot = nl;
@@ -958,12 +980,13 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
   for (int l = 0; l < d->num_layers && all_fused; ++l) all_fused = wave_fuses(l, l == 0 ? io->x : ws);
 
   // ---- enqueue ----
-  if (!all_fused &&
-      (rc = hip_status(launch_fill_zero(ws, L.counters + L.counters_bytes, st))) != RNN_OK)
-    return rc;
+  // the pipelined path zeroes the status word and counters with its first
+  // ring fill
   if (f.pipe) return forward_rnn_pipe(d, w, io, ws, L, m, f, st, xcds, prof);
-  if (!wave &&
-      (rc = hip_status(launch_fill_u32(ws + L.ex, L.ring_end - L.ex, 0xFFFFFFFFu, st))) != RNN_OK)
+  // status word and counters (unless the one-wave scan clears the status
+  // itself) and the exchange rings of the tiled scan, in one launch
+  if ((rc = hip_status(launch_fill2_u32(ws, all_fused ? 0 : L.counters + L.counters_bytes, 0u, ws + L.ex,
+                                        wave ? 0 : L.ring_end - L.ex, 0xFFFFFFFFu, st))) != RNN_OK)
     return rc;
   int* dev_len = nullptr;
   int* dev_off = nullptr;

@@ -515,7 +515,7 @@ hipError_t launch_rssm_reg_as(const RssmArgs& a, int lds, hipStream_t stream) {
                                      lds);
   if (e != hipSuccess) return e;
   const int grid = a.nxcd * a.gpx * a.nw;
-  hipLaunchKernelGGL((rssm_reg_kernel<NQ>), dim3(grid), dim3(kThreads), lds, stream, a);
+  launch_kernel((rssm_reg_kernel<NQ>), dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 

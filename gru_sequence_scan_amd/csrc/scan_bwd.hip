@@ -549,7 +549,7 @@ int scan_bwd_lds_bytes(const ScanBwdArgs& a) { return a.mode == kLSTMP ? bwdp_ld
 hipError_t launch_mgather(const float* rsv, int D, int d, int H, long long rows, float* out, hipStream_t stream) {
   const long long n = rows * H;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mgather_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, rsv, D, d, H, rows, out);
+  launch_kernel(mgather_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, rsv, D, d, H, rows, out);
   return hipGetLastError();
 }
 
@@ -562,9 +562,9 @@ hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t stream) {
   const int groups = a.D * a.nbb;
   const int grid = a.gpx > 0 ? a.nxcd * a.gpx * a.ns : groups * a.ns;
   if (proj)
-    hipLaunchKernelGGL(scan_bwd_proj_kernel, dim3(grid), dim3(kBT), lds, stream, a);
+    launch_kernel(scan_bwd_proj_kernel, dim3(grid), dim3(kBT), lds, stream, a);
   else
-    hipLaunchKernelGGL(scan_bwd_kernel, dim3(grid), dim3(kBT), lds, stream, a);
+    launch_kernel(scan_bwd_kernel, dim3(grid), dim3(kBT), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -772,7 +772,7 @@ hipError_t launch_scan_as(const ScanArgs& a, int lds, dim3 grid, hipStream_t str
   hipError_t e = hipFuncSetAttribute((const void*)scan_kernel<DT, WREG, EPT, PROJ, GXB, RSV>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((scan_kernel<DT, WREG, EPT, PROJ, GXB, RSV>), grid, dim3(kThreads), lds, stream, a);
+  launch_kernel((scan_kernel<DT, WREG, EPT, PROJ, GXB, RSV>), grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 

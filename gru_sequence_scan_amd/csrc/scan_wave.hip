@@ -303,7 +303,7 @@ hipError_t launch_as(const ScanArgs& a, hipStream_t stream) {
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((scan_wave_kernel<DT, GRU, CPR>), dim3(grid), dim3(kWaveThreads), lds, stream, a);
+  launch_kernel((scan_wave_kernel<DT, GRU, CPR>), dim3(grid), dim3(kWaveThreads), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -15,6 +15,16 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
     p[i] = value;
 }
 
+// Element i < n1 of the joint range goes to p1, the rest to p2.
+__global__ void fill2_u32_kernel(uint32_t* p1, size_t n1, uint32_t v1, uint32_t* p2, size_t n2, uint32_t v2) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n1 + n2; i += (size_t)gridDim.x * blockDim.x) {
+    if (i < n1)
+      p1[i] = v1;
+    else
+      p2[i - n1] = v2;
+  }
+}
+
 struct IntChunk {
   int v[kIntsPerLaunch];
 };
@@ -64,12 +74,12 @@ __global__ void copy_int_kernel(int* dst, const int* src) {
 }  // namespace
 
 hipError_t launch_copy_int(int* dst, const int* src, hipStream_t stream) {
-  hipLaunchKernelGGL(copy_int_kernel, dim3(1), dim3(64), 0, stream, dst, src);
+  launch_kernel(copy_int_kernel, dim3(1), dim3(64), 0, stream, dst, src);
   return hipGetLastError();
 }
 
 hipError_t launch_exchange_probe(void* buf, int iters, unsigned long long* out, hipStream_t stream) {
-  hipLaunchKernelGGL(exchange_probe_kernel, dim3(2), dim3(64), 0, stream, reinterpret_cast<unsigned*>(buf), iters,
+  launch_kernel(exchange_probe_kernel, dim3(2), dim3(64), 0, stream, reinterpret_cast<unsigned*>(buf), iters,
                      2000000u, out);
   return hipGetLastError();
 }
@@ -79,7 +89,18 @@ hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t value, hipStream_t st
   if (n == 0) return hipSuccess;
   const size_t want = (n + 255) / 256;
   const int blocks = (int)(want < 256 ? want : 256);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(p), n, value);
+  launch_kernel(fill_u32_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(p), n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill2_u32(void* p1, size_t bytes1, uint32_t value1, void* p2, size_t bytes2, uint32_t value2,
+                            hipStream_t stream) {
+  const size_t n1 = bytes1 / 4, n2 = bytes2 / 4;
+  if (n1 + n2 == 0) return hipSuccess;
+  const size_t want = (n1 + n2 + 255) / 256;
+  const int blocks = (int)(want < 256 ? want : 256);
+  launch_kernel(fill2_u32_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(p1), n1, value1,
+                reinterpret_cast<uint32_t*>(p2), n2, value2);
   return hipGetLastError();
 }
 
@@ -90,7 +111,7 @@ hipError_t launch_write_ints(int* dst, const int* src, int n, hipStream_t stream
     const int m = n - base < kIntsPerLaunch ? n - base : kIntsPerLaunch;
     IntChunk c;
     for (int i = 0; i < m; ++i) c.v[i] = src[base + i];
-    hipLaunchKernelGGL(write_ints_kernel, dim3(1), dim3(256), 0, stream, dst + base, c, m);
+    launch_kernel(write_ints_kernel, dim3(1), dim3(256), 0, stream, dst + base, c, m);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
