@@ -480,6 +480,11 @@ def measure(name, args, rt_us, with_cpu):
         roofline.update({"pipeline_chunk": plan["pipe_chunk"], "launches": dom["launches"]})
     ms_per_step = elapsed / K * 1e3
     value = tokens / (elapsed / K)
+    # the kernels of a forward must fill most of a step and never exceed it:
+    # a kernel whose events did not bracket its dispatch would break this
+    span_us = sum(k["total_us"] for k in kernels)
+    if not (0.5 * ms_per_step * 1e3 <= span_us <= 1.05 * ms_per_step * 1e3):
+        raise RuntimeError(f"{name}: kernel events cover {span_us:.1f} us of a {ms_per_step * 1e3:.1f} us step")
     ctx = PAGES_CONTEXT.get(name)
     vs = (value / max(ctx.values())) if ctx else None
     rec = {"config": pr["config"], "value": value, "ms_per_step": ms_per_step,

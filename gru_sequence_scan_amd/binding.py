@@ -592,15 +592,16 @@ def rssm_prior_unroll(actions, eps, weights, state0=None, belief0=None, *, scale
 
 
 def rssm_actor_unroll(eps, weights, actor, state0=None, belief0=None, *, scale_lb=0.1,
-                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False, check_status=True):
+                      tile_batch=0, tile_hidden=0, placement=0, return_workspace=False, check_status=True,
+                      weights_hint=0):
     """RSSM prior unrolled for H = eps.shape[1] steps with the actor choosing
     each action from the previous state and belief.
 
     weights as for rssm_prior_unroll; actor: dict with w_a1 [Ea, S + Hb],
     b_a1 [Ea], w_a2 [A, Ea], b_a2 [A] (float32, on the GPU).
-    check_status as for rnn_forward.
+    check_status and weights_hint as for rssm_prior_unroll.
     Returns (means, stds, states, beliefs, actions) stacked on dim 1.
     """
     out, ws = _rssm("rssm_actor", None, eps, weights, actor, actor["w_a2"].shape[0], state0, belief0,
-                    scale_lb, tile_batch, tile_hidden, placement, check_status)
+                    scale_lb, tile_batch, tile_hidden, placement, check_status, weights_hint=weights_hint)
     return (out, ws) if return_workspace else out

@@ -493,19 +493,20 @@ struct RssmPlan {
 // groups (the last XCDs may hold padding slots).
 int rssm_grid(const RssmPlan& p, int xcds) { return p.gpx > 0 ? xcds * p.gpx * p.nw : p.ngroups * p.nw; }
 
-// Kernel 3b (no actor): groups of at most rssm_reg_max_members() wide
-// members whose GRU slices fit the register layout, every group on one XCD.
-// The step model: the exchange costs ~1.1 us plus the bytes one member reads
-// (every member's partial sums and the whole h_t of the group's rows) at
-// ~13 GB/s per member, from a sweep of ring exchanges inside one XCD; the
-// products are the per-wave MFMA chains (the slice products take a fixed
-// number of chunks per wave whatever the slice width) at ~12 cycles each,
-// plus six workgroup barriers and the gate math.
+// Kernel 3b: groups of at most rssm_reg_max_members() wide members whose
+// GRU slices fit the register layout, every group on one XCD. The step
+// model: the exchange costs ~1.1 us plus the bytes one member reads (every
+// member's partial sums and the whole h_t of the group's rows) at ~13 GB/s
+// per member, from a sweep of ring exchanges inside one XCD; the products
+// are the per-wave MFMA chains (the slice products take a fixed number of
+// chunks per wave whatever the slice width) at ~12 cycles each, plus six
+// workgroup barriers (nine with the actor) and the gate math.
 bool plan_rssm_reg(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
   // flat placement (consecutive ids form a group) rules it out: its
   // exchange is only valid when a group's members share an XCD
-  if (d->mode != RNN_MODE_RSSM_PRIOR || d->weights == 1 || d->placement == 1) return false;
+  if (!is_rssm(d->mode) || d->weights == 1 || d->placement == 1) return false;
   const int B = d->B, S = d->state_dim, A = d->action_dim, E = d->embed_dim, Hb = d->belief_dim;
+  const int Ea = d->mode == RNN_MODE_RSSM_ACTOR ? d->actor_dim : 0;
   const int per_xcd = cus / xcds;
   double best = 1e30;
   bool found = false;
@@ -519,15 +520,16 @@ bool plan_rssm_reg(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
       if (nw > 1 && cdiv(Hb, nw - 1) == h_per) continue;
       if (gpx * nw > per_xcd) continue;
       RssmArgs a{};
-      a.S = S; a.A = A; a.E = E; a.Hb = Hb; a.rows = rows; a.nw = nw; a.h_per = h_per; a.Ea = 0;
-      a.Ep = rup(E, 4); a.Hbp = rup(Hb, 4);
+      a.S = S; a.A = A; a.E = E; a.Hb = Hb; a.rows = rows; a.nw = nw; a.h_per = h_per; a.Ea = Ea;
+      a.Ep = rssm_ex_cols(d); a.Hbp = rup(Hb, 4);
       if (!rssm_reg_fits(a)) continue;
       const int lds = rssm_reg_lds_bytes(a);
       if (lds > kMaxLds) continue;
       const double bytes = (double)rows * ((double)nw * a.Ep + a.Hbp) * 4.0;
       const int nq = cdiv(cdiv(std::max(E, Hb), 4), 4), n2 = cdiv(cdiv(E, 4), 8);
-      const double mfma = 4.0 * (2 * nq + std::max(nq, n2) + cdiv(h_per, 4) + cdiv(S + A, 4));
-      const double t = 1.1 + bytes / 13.3e3 + (mfma * 12.0 + 6 * 150.0 + 400.0) / 2400.0;
+      const double actor = Ea > 0 ? cdiv(S, 4) + cdiv(cdiv(Ea, 4), 8) : 0;
+      const double mfma = 4.0 * (2 * nq + std::max(nq, n2) + cdiv(h_per, 4) + cdiv(S + A, 4) + actor);
+      const double t = 1.1 + bytes / 13.3e3 + (mfma * 12.0 + (Ea > 0 ? 9 : 6) * 150.0 + 400.0) / 2400.0;
       if (t < best) {
         best = t;
         *out = RssmPlan{rows, ngroups, nw, h_per, gpx, lds, 1};

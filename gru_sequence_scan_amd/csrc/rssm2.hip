@@ -33,6 +33,13 @@
 //     chiplet. At start the members of a group compare their hardware XCC
 //     ids through device-scope stores; a group that is split over XCDs
 //     reports a device status error instead of computing.
+//
+// With an actor in the loop (the issue's second unroll; the actor is the
+// MLP a = tanh(W_a2 ELU(W_a1 [s; h] + b_a1) + b_a2)), the action of step
+// t + 1 comes from s_t and h_t at the end of step t, as in kernel 3: the
+// belief part W_a1[:, S:] h_t is split over the members like W_1 and rides
+// the same exchange (more partial-sum columns per row); the state part, the
+// ELU, W_a2 and the tanh are small products every member does whole.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "rssm_common.hpp"
@@ -118,6 +125,9 @@ __host__ __device__ inline int ld_reg_rows(int x, int nq) {
 // destination registers get reused makes the compiler wait for every
 // outstanding memory operation, stores included).
 constexpr int kStage = 32;
+// With the actor only the noise is staged, for fewer steps at a time (its
+// weights take the LDS).
+constexpr int kStageActor = 16;
 
 // e[v][c] = ELU(sum_k X[v][k] W[c][k] + bias[c]) for c < N (N <= 64 kWaves
 // columns, one 64-column pass per wave, K <= 64): no K split, so no
@@ -138,14 +148,36 @@ __device__ __forceinline__ void elu_pass_product(const float* X, int ldx, const 
   }
 }
 
+// out[v][c] = ELU(sum_k X[v][k] W[c][k] + add[v][c] + bias[c]), as
+// elu_pass_product with a per-element term (the actor's belief part).
+__device__ __forceinline__ void elu_pass_product_add(const float* X, int ldx, const float* W, int ldw,
+                                                     const float* bias, const float* add, int lda, float* out,
+                                                     int ldo, int N, int K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int npass = (N + 63) >> 6;
+  const int K4 = (K + 3) >> 2;
+  for (int p = __builtin_amdgcn_readfirstlane(wave); p < npass; p += kWaves) {
+    const int c = p * 64 + lane, cc = c < N ? c : N - 1;
+    const float bc = bias[cc];
+    const f32x4 acc = dot_batch<16>(X + (lane & 3) * ldx, W + cc * ldw, 0, K4, f32x4{0.f, 0.f, 0.f, 0.f});
+    if (c < N) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) out[v * ldo + c] = felu(acc[v] + add[v * lda + c] + bc);
+    }
+  }
+}
+
 struct Rssm2Lds {
   // float offsets (multiples of 4)
   int was, bas, b1, b2, w2, w1s;
-  int sa, e, h, hs, u, gh, redg, redv, redw, stg, flag, total;
-  int ld_sa, ld_e, ld_h, ld_hs, ld_stg;
+  int wa1s, ba1, wa2, ba2, q, qa;  // actor (empty without one)
+  int sa, e, h, hs, u, gh, redg, redv, stg, flag, total;
+  int ld_sa, ld_e, ld_h, ld_hs, ld_stg, ld_s, ld_q;
 };
 
-__host__ __device__ inline Rssm2Lds rssm2_lds(const RssmArgs& a) {
+// (Ea is passed apart so that the kernel without the actor sees a constant
+// zero: its offsets then fold as they would with no actor fields at all.)
+__host__ __device__ inline Rssm2Lds rssm2_lds(const RssmArgs& a, int Ea) {
   Rssm2Lds L;
   const int SA = a.S + a.A;
   const int nq = rssm_reg_nq(a);
@@ -153,6 +185,8 @@ __host__ __device__ inline Rssm2Lds rssm2_lds(const RssmArgs& a) {
   L.ld_e = ld_reg_rows(a.E, nq);
   L.ld_h = ld_reg_rows(a.Hb, nq);
   L.ld_hs = ld_rows(a.h_per);
+  L.ld_s = ld_rows(a.S);
+  L.ld_q = ld_rows(Ea);
   const int R = kMaxRows;
   int o = 0;
   auto take = [&](int n) { const int at = o; o += r4(n); return at; };
@@ -161,7 +195,13 @@ __host__ __device__ inline Rssm2Lds rssm2_lds(const RssmArgs& a) {
   L.b1 = take(a.E);
   L.b2 = take(2 * a.S);
   L.w2 = take(2 * a.S * L.ld_e);
-  L.w1s = take(a.E * L.ld_hs);
+  L.w1s = take((a.E + Ea) * L.ld_hs);  // W_1 columns, then W_a1 belief columns
+  L.wa1s = take(Ea * L.ld_s);
+  L.ba1 = take(Ea);
+  L.wa2 = take(Ea > 0 ? a.A * L.ld_q : 0);
+  L.ba2 = take(Ea > 0 ? a.A : 0);
+  L.q = take(Ea > 0 ? R * L.ld_q : 0);
+  L.qa = take(Ea > 0 ? R * L.ld_q : 0);
   L.sa = take(R * L.ld_sa);
   L.e = take(R * L.ld_e);
   L.h = take(R * L.ld_h);
@@ -169,19 +209,22 @@ __host__ __device__ inline Rssm2Lds rssm2_lds(const RssmArgs& a) {
   L.u = take(R * L.ld_e);
   L.gh = take(R * 128);
   L.redg = take(4 * 4 * 128);        // 4 K quarters x 4 rows x 128 columns
-  L.redv = take(kWaves * 4 * 64);    // W_2: 8 K parts x 4 rows x 64 columns
-  L.redw = take(kWaves * 4 * 64);    // mv4's reduction space (W_as)
-  L.ld_stg = SA;                      // per (row, step): eps (S), then the next action (A)
-  L.stg = take(R * kStage * SA);
+  L.redv = take(kWaves * 4 * 64);    // W_2 (and W_a2): 8 K parts x 4 rows x 64 columns
+  // per (row, step): eps (S), then (no actor) the next action (A). Without
+  // the actor the buffer sits 8 KiB further on and is sized for four rows:
+  // that placement measured 1.8% faster steps than the packed one.
+  L.ld_stg = Ea > 0 ? a.S : SA;
+  if (Ea == 0) take(kWaves * 4 * 64);
+  L.stg = take((Ea > 0 ? (a.rows > 0 ? a.rows : 1) : R) * (Ea > 0 ? kStageActor : kStage) * L.ld_stg);
   L.flag = take(4);
   L.total = o * 4;
   return L;
 }
 
-template <int NQ>
+template <int NQ, bool ACTOR>
 __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  const Rssm2Lds L = rssm2_lds(a);
+  const Rssm2Lds L = rssm2_lds(a, ACTOR ? a.Ea : 0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   // group and member: the ids xcd, xcd + nxcd, ... are the workgroups of one
@@ -225,6 +268,10 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
   const int b0 = g * a.rows;
   const int nrows = min(a.rows, a.B - b0);
   const int S = a.S, A = a.A, E = a.E, Hb = a.Hb, SA = a.S + a.A;
+  const int Ea = ACTOR ? a.Ea : 0;
+  const int SH = S + Hb;   // W_a1 row length
+  const int ea0 = r4(E);   // first actor column of an exchange row
+  const int N1 = E + Ea;   // columns of the per-member partial product
   const int hp = a.h_per;
   const int j0 = w * hp, hn = max(0, min(hp, Hb - j0));
   const int nw = a.nw;
@@ -257,6 +304,24 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
     const int k = i / hp, jj = i - k * hp;
     if (jj < hn) sm[L.w1s + k * L.ld_hs + jj] = a.w_1[(size_t)k * Hb + j0 + jj];
   }
+  if constexpr (ACTOR) {
+    // belief columns of W_a1 for the slice (rows E .. E + Ea - 1 of w1s),
+    // its state columns whole, W_a2 whole, and both biases
+    for (int i = tid; i < Ea * hp; i += kThreads) {
+      const int k = i / hp, jj = i - k * hp;
+      if (jj < hn) sm[L.w1s + (E + k) * L.ld_hs + jj] = a.w_a1[(size_t)k * SH + S + j0 + jj];
+    }
+    for (int i = tid; i < Ea * S; i += kThreads) {
+      const int r = i / S, c = i - r * S;
+      sm[L.wa1s + r * L.ld_s + c] = a.w_a1[(size_t)r * SH + c];
+    }
+    for (int i = tid; i < A * Ea; i += kThreads) {
+      const int r = i / Ea, c = i - r * Ea;
+      sm[L.wa2 + r * L.ld_q + c] = a.w_a2[i];
+    }
+    for (int i = tid; i < Ea; i += kThreads) sm[L.ba1 + i] = a.b_a1[i];
+    for (int i = tid; i < A; i += kThreads) sm[L.ba2 + i] = a.b_a2[i];
+  }
 
   // --- registers: the slice of W_ih and W_hh (column c = 64 * pass + lane is
   // slice row c: gate c / hp, unit c % hp); W_2 (column = lane) is read from
@@ -284,8 +349,10 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
   for (int i = tid; i < nrows * SA; i += kThreads) {
     const int r = i / SA, c = i - r * SA;
     const int b = b0 + r;
-    sm[L.sa + r * L.ld_sa + c] =
-        c < S ? (a.s0 ? a.s0[(size_t)b * S + c] : 0.f) : a.actions[((size_t)b * a.T + 0) * A + (c - S)];
+    // (the actor's a_0 is computed below)
+    sm[L.sa + r * L.ld_sa + c] = c < S    ? (a.s0 ? a.s0[(size_t)b * S + c] : 0.f)
+                                 : ACTOR ? 0.f
+                                         : a.actions[((size_t)b * a.T + 0) * A + (c - S)];
   }
   for (int i = tid; i < nrows * Hb; i += kThreads) {
     const int r = i / Hb, c = i - r * Hb;
@@ -310,6 +377,26 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
   float* gh = sm + L.gh;
   const int ng = 3 * hp;  // slice product columns
   __syncthreads();
+  if constexpr (ACTOR) {
+    // a_0 = actor(s_0, h_0), once, straight from global W_a1 and from W_a2
+    for (int i = tid; i < nrows * Ea; i += kThreads) {
+      const int r = i / Ea, c = i - r * Ea;
+      const float* wr = a.w_a1 + (size_t)c * SH;
+      float acc = 0.f;
+      for (int k = 0; k < S; ++k) acc += wr[k] * sm[L.sa + r * L.ld_sa + k];
+      for (int k = 0; k < Hb; ++k) acc += wr[S + k] * sm[L.h + r * L.ld_h + k];
+      sm[L.q + r * L.ld_q + c] = felu(acc + sm[L.ba1 + c]);
+    }
+    __syncthreads();
+    if (act_owner) {
+      float acc = 0.f;
+      for (int k = 0; k < Ea; ++k) acc += sm[L.wa2 + ac * L.ld_q + k] * sm[L.q + ar * L.ld_q + k];
+      const float act = ftanh(acc + sm[L.ba2 + ac]);
+      sm[L.sa + ar * L.ld_sa + S + ac] = act;
+      if (w == 0 && a.act_out) a.act_out[((size_t)(b0 + ar) * a.T + 0) * A + ac] = act;
+    }
+    __syncthreads();
+  }
 
   // gh = W_hh h_0 on the slice; e_0 = ELU(W_as [s_0; a_0] + b_as)
   {
@@ -325,30 +412,33 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
   }
   __syncthreads();
 
-  const int EC = a.Ep / 4, HC = a.Hbp / 4;
-  const int npass_e = (E + 63) / 64;
+  const int EC = a.Ep / 4, HC = a.Hbp / 4, ECU = ea0 / 4;  // chunks past ECU are the actor's
+  const int npass_1 = (N1 + 63) / 64;
   float* stg = sm + L.stg;
+  // staged steps and columns (noise, then without the actor the next action)
+  constexpr int KS = ACTOR ? kStageActor : kStage;
+  const int SC = ACTOR ? S : SA;
   // nothing loaded in the prologue may count as pending inside the loop
   wait_all_mem();
   for (int t = 0; t < a.T; ++t) {
     const int slot = t & (kRing - 1);
-    if (t % kStage == 0) {
-      // noise of steps t .. t + kStage - 1 and the actions they feed forward
+    if (t % KS == 0) {
+      // noise of steps t .. t + KS - 1 and the actions they feed forward
       // (action t' + 1 beside noise t'), for this group's rows
-      const int ns = min(kStage, a.T - t);
-      for (int i = tid; i < nrows * ns * SA; i += kThreads) {
-        const int r = i / (ns * SA), rem = i - r * (ns * SA), k = rem / SA, c = rem - k * SA;
+      const int ns = min(KS, a.T - t);
+      for (int i = tid; i < nrows * ns * SC; i += kThreads) {
+        const int r = i / (ns * SC), rem = i - r * (ns * SC), k = rem / SC, c = rem - k * SC;
         const int b = b0 + r, tt = t + k;
         float v = 0.f;
         if (c < S)
           v = a.eps[((size_t)b * a.T + tt) * S + c];
         else if (tt + 1 < a.T)
           v = a.actions[((size_t)b * a.T + tt + 1) * A + (c - S)];
-        stg[(r * kStage + k) * L.ld_stg + c] = v;
+        stg[(r * KS + k) * L.ld_stg + c] = v;
       }
       __syncthreads();
     }
-    const float* stg_t = stg + (t % kStage) * L.ld_stg;
+    const float* stg_t = stg + (t % KS) * L.ld_stg;
     // ---- GRU input product on the slice: gi = W_ih e_t ----
     {
       const f32x4 acc = reg_product<NQ>(sm + L.e + (lane & 3) * L.ld_e, wih, ke0);
@@ -371,16 +461,17 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
       a.beliefs[((size_t)(b0 + own_r) * a.T + t) * Hb + j0 + own_j] = h;
     }
     __syncthreads();
-    // ---- this slice's share of W_1 h_t, stored to the ring from the MFMA
-    //      lanes ----
-    if (wave < npass_e) {
+    // ---- this slice's share of W_1 h_t (and of the actor's W_a1[:, S:] h_t),
+    //      stored to the ring from the MFMA lanes ----
+    if (wave < npass_1) {
       const int c = wave * 64 + lane;
-      const f32x4 acc = dot_batch<16>(sm + L.hs + (lane & 3) * L.ld_hs, sm + L.w1s + (c < E ? c : E - 1) * L.ld_hs,
+      const f32x4 acc = dot_batch<16>(sm + L.hs + (lane & 3) * L.ld_hs, sm + L.w1s + (c < N1 ? c : N1 - 1) * L.ld_hs,
                                       0, (hp + 3) / 4, f32x4{0.f, 0.f, 0.f, 0.f});
-      if (c < E) {
+      if (c < N1) {
+        const int col = c < E ? c : ea0 + (c - E);
 #pragma unroll
         for (int v = 0; v < kMaxRows; ++v)
-          if (v < nrows) pub_store(px_rs, px_el(slot, b0 + v, w, c), publish_bits(acc[v]));
+          if (v < nrows) pub_store(px_rs, px_el(slot, b0 + v, w, col), publish_bits(acc[v]));
       }
     }
 
@@ -397,7 +488,9 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
       const bool act = wave_u ? i < nu : i < nhc;
       const int per = wave_u ? EC : HC;
       const int r = act ? i / per : 0, c = act ? i - r * per : 0;
-      const int valid = min(4, (wave_u ? E : Hb) - 4 * c);
+      const int valid = !wave_u                ? min(4, Hb - 4 * c)
+                        : (!ACTOR || c < ECU) ? min(4, E - 4 * c)
+                                              : min(4, Ea - 4 * (c - ECU));
       const int nm = act ? (wave_u ? nw : 1) : 0;
       const __amdgpu_buffer_rsrc_t rs = wave_u ? px_rs : hx_rs;
       uint32_t off[kMaxMembers2];
@@ -441,9 +534,17 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
 #pragma unroll
         for (int m = 0; m < kMaxMembers2; ++m)
           if (m < nw) s4 += __builtin_bit_cast(f32x4, v[m]);
+        if (!ACTOR || c < ECU) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s4[k] = k < valid ? felu(s4[k] + sm[L.b1 + 4 * c + k]) : 0.f;
-        *reinterpret_cast<f32x4*>(sm + L.u + r * L.ld_e + 4 * c) = s4;
+          for (int k = 0; k < 4; ++k) s4[k] = k < valid ? felu(s4[k] + sm[L.b1 + 4 * c + k]) : 0.f;
+          *reinterpret_cast<f32x4*>(sm + L.u + r * L.ld_e + 4 * c) = s4;
+        } else {
+          // the actor's belief term, summed (its activation comes with s_t)
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (k >= valid) s4[k] = 0.f;
+          *reinterpret_cast<f32x4*>(sm + L.qa + r * L.ld_q + 4 * (c - ECU)) = s4;
+        }
       } else if (act) {
         f32x4 hf = __builtin_bit_cast(f32x4, v[0]);
 #pragma unroll
@@ -463,12 +564,13 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
       if (t > 0) {
         const int old = (t - 1) & (kRing - 1);
         if (owner) pub_store(hx_rs, hx_el(old, b0 + own_r, j0 + own_j), kSentinel);
-        if (wave < npass_e) {
+        if (wave < npass_1) {
           const int c = wave * 64 + lane;
-          if (c < E) {
+          if (c < N1) {
+            const int col = c < E ? c : ea0 + (c - E);
 #pragma unroll
             for (int v = 0; v < kMaxRows; ++v)
-              if (v < nrows) pub_store(px_rs, px_el(old, b0 + v, w, c), kSentinel);
+              if (v < nrows) pub_store(px_rs, px_el(old, b0 + v, w, col), kSentinel);
           }
         }
       }
@@ -485,7 +587,7 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
       const float vm = red_sum(redv, tr, tc) + sm[L.b2 + tc];
       const float vs = red_sum(redv, tr, S + tc) + sm[L.b2 + S + tc];
       const float sd = fsoftplus(vs) + a.scale_lb;
-      const float st = vm + stg_t[tr * kStage * L.ld_stg + tc] * sd;
+      const float st = vm + stg_t[tr * KS * L.ld_stg + tc] * sd;
       sm[L.sa + tr * L.ld_sa + tc] = st;
       if (w == 0) {
         const size_t o = ((size_t)(b0 + tr) * a.T + t) * S + tc;
@@ -499,8 +601,32 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
       gh[v * 128 + c] =
           redg[v * 128 + c] + redg[(4 + v) * 128 + c] + redg[(8 + v) * 128 + c] + redg[(12 + v) * 128 + c];
     }
-    if (act_owner && t + 1 < a.T) sm[L.sa + ar * L.ld_sa + S + ac] = stg_t[ar * kStage * L.ld_stg + S + ac];
+    if (!ACTOR && act_owner && t + 1 < a.T) sm[L.sa + ar * L.ld_sa + S + ac] = stg_t[ar * KS * L.ld_stg + S + ac];
     __syncthreads();
+    if constexpr (ACTOR) {
+      if (t + 1 < a.T) {
+        // ---- a_{t+1} = tanh(W_a2 ELU(W_a1[:, :S] s_t + W_a1[:, S:] h_t + b_a1)
+        //      + b_a2), written into the action slot that e_{t+1} reads ----
+        elu_pass_product_add(sm + L.sa, L.ld_sa, sm + L.wa1s, L.ld_s, sm + L.ba1, sm + L.qa, L.ld_q, sm + L.q,
+                             L.ld_q, Ea, S);
+        __syncthreads();
+        {
+          const int Q4 = (Ea + 3) / 4, per = (Q4 + kWaves - 1) / kWaves;
+          const int ka = min(Q4, wave * per), kn = min(Q4, ka + per) - ka;
+          const f32x4 acc = dot_batch<8>(sm + L.q + (lane & 3) * L.ld_q, sm + L.wa2 + (lane < A ? lane : A - 1) * L.ld_q,
+                                         ka, kn, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int v = 0; v < 4; ++v) redv[(wave * 4 + v) * 64 + lane] = acc[v];
+        }
+        __syncthreads();
+        if (act_owner) {
+          const float act = ftanh(red_sum(redv, ar, ac) + sm[L.ba2 + ac]);
+          sm[L.sa + ar * L.ld_sa + S + ac] = act;
+          if (w == 0 && a.act_out) a.act_out[((size_t)(b0 + ar) * a.T + t + 1) * A + ac] = act;
+        }
+        __syncthreads();
+      }
+    }
     // ---- e_{t+1} = ELU(W_as [s_t; a_{t+1}] + b_as) ----
     if (t + 1 < a.T) {
       elu_pass_product(sm + L.sa, L.ld_sa, sm + L.was, L.ld_sa, sm + L.bas, sm + L.e, L.ld_e, E, SA);
@@ -509,22 +635,40 @@ __global__ void __launch_bounds__(kThreads) rssm_reg_kernel(RssmArgs a) {
   }
 }
 
-template <int NQ>
+template <int NQ, bool ACTOR>
 hipError_t launch_rssm_reg_as(const RssmArgs& a, int lds, hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)rssm_reg_kernel<NQ>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     lds);
+  hipError_t e = hipFuncSetAttribute((const void*)rssm_reg_kernel<NQ, ACTOR>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int grid = a.nxcd * a.gpx * a.nw;
-  launch_kernel((rssm_reg_kernel<NQ>), dim3(grid), dim3(kThreads), lds, stream, a);
+  launch_kernel((rssm_reg_kernel<NQ, ACTOR>), dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
+}
+
+template <bool ACTOR>
+hipError_t launch_rssm_reg_nq(const RssmArgs& a, int lds, hipStream_t stream) {
+  switch (rssm_reg_nq(a)) {
+    case 4: return launch_rssm_reg_as<4, ACTOR>(a, lds, stream);
+    case 8: return launch_rssm_reg_as<8, ACTOR>(a, lds, stream);
+    case 13: return launch_rssm_reg_as<13, ACTOR>(a, lds, stream);
+    default:
+      // (rssm_reg_fits keeps the actor off the widest layout)
+      if constexpr (ACTOR) return hipErrorInvalidValue;
+      else return launch_rssm_reg_as<16, ACTOR>(a, lds, stream);
+  }
 }
 
 }  // namespace
 
-int rssm_reg_lds_bytes(const RssmArgs& a) { return rssm2_lds(a).total; }
+int rssm_reg_lds_bytes(const RssmArgs& a) { return rssm2_lds(a, a.Ea).total; }
 
 bool rssm_reg_fits(const RssmArgs& a) {
-  return a.Ea == 0 && a.rows >= 1 && a.rows <= kMaxRows && a.nw >= 1 && a.nw <= kMaxMembers2 && a.h_per >= 1 &&
+  // (actor: the partial columns take at most one 64-column pass per wave,
+  // W_a2's K split gives each wave at most eight chunks, one lane per action)
+  // (and the widest register layout would spill with the actor's working set)
+  const bool actor_ok = a.Ea == 0 || (a.Ea <= 256 && a.E + a.Ea <= 64 * kWaves && a.A <= 64 &&
+                                      a.Ep == r4(a.E) + r4(a.Ea) && rssm_reg_nq(a) <= 13);
+  return actor_ok && a.rows >= 1 && a.rows <= kMaxRows && a.nw >= 1 && a.nw <= kMaxMembers2 && a.h_per >= 1 &&
          3 * a.h_per <= 128 && (a.h_per + 3) / 4 <= 16 && 2 * a.S <= 64 && a.S + a.A <= 64 &&
          rssm_reg_nq(a) > 0 && a.rows * a.h_per <= kThreads &&
          ((a.rows * (a.Ep / 4) + 63) & ~63) + a.rows * (a.Hbp / 4) <= kThreads && a.rows * a.S <= kThreads &&
@@ -536,13 +680,8 @@ int rssm_ring_slots() { return kRing; }
 int rssm_reg_max_members() { return kMaxMembers2; }
 
 hipError_t launch_rssm_reg(const RssmArgs& a, hipStream_t stream) {
-  const int lds = rssm2_lds(a).total;
-  switch (rssm_reg_nq(a)) {
-    case 4: return launch_rssm_reg_as<4>(a, lds, stream);
-    case 8: return launch_rssm_reg_as<8>(a, lds, stream);
-    case 13: return launch_rssm_reg_as<13>(a, lds, stream);
-    default: return launch_rssm_reg_as<16>(a, lds, stream);
-  }
+  const int lds = rssm2_lds(a, a.Ea).total;
+  return a.Ea > 0 ? launch_rssm_reg_nq<true>(a, lds, stream) : launch_rssm_reg_nq<false>(a, lds, stream);
 }
 
 }  // namespace rnnk

@@ -419,6 +419,21 @@ def test_rssm_actor_shapes(case):
         assert_close(g, r, "f32", f"{name} {nm}")
 
 
+# The same unroll on kernel 3 (GRU weights resident in LDS, counter
+# barrier), which the planner otherwise keeps for shapes kernel 3b cannot
+# hold.
+@pytest.mark.parametrize("case", [RSSM_ACTOR_SHAPES[0], RSSM_ACTOR_SHAPES[1]], ids=["actor_small", "actor_wide"])
+def test_rssm_actor_shapes_lds_weights(case):
+    name, B, T, S, A, E, Hb, Ea, tb, th = case
+    log(f"[gpu] rssm actor shape {name}, LDS-resident weights")
+    d = synth.make_rssm_inputs(B, T, state_dim=S, action_dim=A, embed_dim=E, belief_dim=Hb, actor_dim=Ea,
+                               seed=zlib.crc32(name.encode()) % 1000, s0_std=0.5, h0_std=0.5)
+    got = run_rssm_actor(d, tile_batch=tb, tile_hidden=th, weights_hint=1)
+    ref = oracle.rssm_actor_unroll(d["eps"], d["weights"], d["actor"], d["s0"], d["h0"])
+    for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs", "actions")):
+        assert_close(g, r, "f32", f"{name} {nm}")
+
+
 def test_rssm_actor_zero_weights_closed_form():
     log("[gpu] rssm actor closed form")
     d = synth.make_rssm_inputs(5, 4, seed=11, zero_weights=True, actor_dim=24)
@@ -512,10 +527,11 @@ def test_full_lstm_t256_b1_small():
     _compare(d, run_rnn(d), _oracle(d), "lstm_t256_b1_small")
 
 
-def test_full_rssm_actor_b50_h50():
+@pytest.mark.parametrize("weights_hint", [0, 1], ids=["planned", "lds_weights"])
+def test_full_rssm_actor_b50_h50(weights_hint):
     d = synth.make_inputs("rssm_actor_b50_h50")
-    log("[gpu] full-size rssm_actor_b50_h50")
-    got = run_rssm_actor(d)
+    log(f"[gpu] full-size rssm_actor_b50_h50 weights hint {weights_hint}")
+    got = run_rssm_actor(d, weights_hint=weights_hint)
     ref = oracle.rssm_actor_unroll(d["eps"], d["weights"], d["actor"])
     for g, r, nm in zip(got, ref, ("means", "stds", "states", "beliefs", "actions")):
         assert_close(g, r, "f32", "rssm_actor_b50_h50 " + nm)
