@@ -496,11 +496,12 @@ int rssm_grid(const RssmPlan& p, int xcds) { return p.gpx > 0 ? xcds * p.gpx * p
 // Kernel 3b: groups of at most rssm_reg_max_members() wide members whose
 // GRU slices fit the register layout, every group on one XCD. The step
 // model: the exchange costs ~1.1 us plus the bytes one member reads (every
-// member's partial sums and the whole h_t of the group's rows) at ~13 GB/s
-// per member, from a sweep of ring exchanges inside one XCD; the products
-// are the per-wave MFMA chains (the slice products take a fixed number of
-// chunks per wave whatever the slice width) at ~12 cycles each, plus six
-// workgroup barriers (nine with the actor) and the gate math.
+// member's partial sums and the whole h_t of the group's rows) at ~43 GB/s
+// per member, plus ~15 ns per unit of the slice (gates, partial products,
+// publishing), both fitted to unrolls at B=50, T=50 over 2-4 rows and 5-8
+// members; the products are the per-wave MFMA chains (the slice products
+// take a fixed number of chunks per wave whatever the slice width) at ~12
+// cycles each, plus six workgroup barriers (nine with the actor).
 bool plan_rssm_reg(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
   // flat placement (consecutive ids form a group) rules it out: its
   // exchange is only valid when a group's members share an XCD
@@ -529,7 +530,7 @@ bool plan_rssm_reg(const RnnDesc* d, int cus, int xcds, RssmPlan* out) {
       const int nq = cdiv(cdiv(std::max(E, Hb), 4), 4), n2 = cdiv(cdiv(E, 4), 8);
       const double actor = Ea > 0 ? cdiv(S, 4) + cdiv(cdiv(Ea, 4), 8) : 0;
       const double mfma = 4.0 * (2 * nq + std::max(nq, n2) + cdiv(h_per, 4) + cdiv(S + A, 4) + actor);
-      const double t = 1.1 + bytes / 13.3e3 + (mfma * 12.0 + (Ea > 0 ? 9 : 6) * 150.0 + 400.0) / 2400.0;
+      const double t = 1.1 + bytes / 43e3 + 0.015 * h_per + (mfma * 12.0 + (Ea > 0 ? 9 : 6) * 150.0 + 400.0) / 2400.0;
       if (t < best) {
         best = t;
         *out = RssmPlan{rows, ngroups, nw, h_per, gpx, lds, 1};
