@@ -77,6 +77,28 @@ __device__ __forceinline__ f32x4 dot_batch(const float* xr, const float* wr, int
   return acc;
 }
 
+// dst[r * ldd + c] = src[r * ldsrc + c] for r < rows, c < cols: a global
+// matrix staged into LDS by the whole workgroup, wave w taking rows w * RB
+// onwards RB at a time (their loads in flight together), lanes taking
+// columns. A loop of single load-store pairs waits out one memory latency
+// per element.
+template <int RB = 8>
+__device__ __forceinline__ void stage_rows(float* dst, int ldd, const float* src, size_t ldsrc, int rows, int cols) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int c0 = 0; c0 < cols; c0 += 64) {
+    const int c = c0 + lane;
+    for (int r0 = wave * RB; r0 < rows; r0 += kWaves * RB) {
+      float v[RB];
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+        if (r0 + j < rows && c < cols) v[j] = src[(size_t)(r0 + j) * ldsrc + c];
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+        if (r0 + j < rows && c < cols) dst[(r0 + j) * ldd + c] = v[j];
+    }
+  }
+}
+
 constexpr int kWholePassK4 = 16;  // K up to 64: one wave per 64-column pass
 
 struct Plain {
