@@ -47,7 +47,7 @@ HEADLINE = "rssm_b50_t50"
 CSRC = os.path.join(ROOT, "gru_sequence_scan_amd", "csrc")
 KERNEL_SOURCES = {
     "gemm_xw": ["gemm_xw.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
-    "scan": ["scan.hip", "scan_kernel.hpp", "scan_common.hpp", "scan_bf16_reg.hip", "scan_bf16_lds.hip",
+    "scan": ["scan.hip", "scan_kernel.hpp", "scan_common.hpp", "scan_small.hip", "scan_bf16_reg.hip", "scan_bf16_lds.hip",
              "scan_bf16gx_reg.hip", "scan_bf16gx_lds.hip", "scan_f32_reg.hip", "scan_f32_lds.hip",
              "scan_f32t_reg.hip", "scan_f32t_lds.hip", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],
     "rssm": ["rssm.hip", "rssm2.hip", "rssm_common.hpp", "device_common.hpp", "kernels.hpp", "rnn_api.cpp"],

@@ -19,7 +19,7 @@ OUT_DIR = os.path.join(PKG, "_lib")
 LIB_NAME = "librnn_gfx950.so"
 SOURCES = ["gemm_xw.hip", "scan.hip", "scan_bf16_reg.hip", "scan_bf16_lds.hip", "scan_bf16gx_reg.hip",
            "scan_bf16gx_lds.hip", "scan_f32_reg.hip", "scan_f32_lds.hip", "scan_f32t_reg.hip", "scan_f32t_lds.hip",
-           "scan_wave.hip", "scan_bwd.hip", "gemm_gen.hip", "rssm.hip", "rssm2.hip", "util.hip", "rnn_api.cpp"]
+           "scan_wave.hip", "scan_small.hip", "scan_bwd.hip", "gemm_gen.hip", "rssm.hip", "rssm2.hip", "util.hip", "rnn_api.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

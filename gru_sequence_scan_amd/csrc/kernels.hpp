@@ -132,6 +132,16 @@ constexpr int kScanMaxWorkgroups = 4096;  // xid entries per layer
 hipError_t launch_scan(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
 constexpr int kScanRegChunks = 32;
 
+// Kernel 2c: a few independent sequences (direction x batch row groups of
+// at most kScanSmallMaxGroups), each a group of `ns` workgroups of eight
+// waves owning `hs` hidden units per workgroup (hs / 8 per wave), W_hh rows
+// in registers, h exchanged through an fp32 ring of row stride Kp >= 64 x
+// scan_small_chunks(K). LSTM and GRU, K <= 512.
+constexpr int kScanSmallMaxGroups = 8;
+int scan_small_chunks(int K);               // K chunks per lane: 1, 2, 4 or 8 (0: K > 512)
+int scan_small_units_per_wg(int mode, int K);
+hipError_t launch_scan_small(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
+
 // Kernel 2b: one wave per (direction, batch row) when the gate rows of all
 // units fit one wave (LSTM and GRU with H <= 16; not LSTMP). Uses the
 // ScanArgs problem fields, slot 0's tensors, lengths, offsets, the clip

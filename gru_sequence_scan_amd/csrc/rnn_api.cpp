@@ -201,15 +201,24 @@ bool use_wave_scan(const RnnDesc* d, const Dims& m);
 // Bytes per element of the hoisted G_x: the storage dtype's unless fp32 is
 // requested, or the one-wave scan runs the layer (its G_x reads are one
 // word per lane per step, where bf16 saves nothing and costs the widening).
+bool small_scan_shape(const RnnDesc* d, const Dims& m);
+
 int gx_esize(const RnnDesc* d, const Dims& m) {
-  return d->dtype == RNN_DTYPE_BF16 && d->gx_dtype == RNN_GX_AS_DTYPE && !use_wave_scan(d, m) ? 2 : 4;
+  return d->dtype == RNN_DTYPE_BF16 && d->gx_dtype == RNN_GX_AS_DTYPE && !use_wave_scan(d, m) &&
+                 !small_scan_shape(d, m)
+             ? 2
+             : 4;
 }
 
 // Per-layer exchange regions of the forward scan (aligned sizes, so the
 // layers' regions stay aligned).
 size_t xid_layer_bytes() { return align_up((size_t)kScanMaxWorkgroups * 4, kAlign); }
 size_t hx_ring_bytes(const RnnDesc* d, const Dims& m) {
-  return align_up((size_t)kScanRingSlots * m.D * d->B * m.Kp * m.esize, kAlign);
+  size_t b = (size_t)kScanRingSlots * m.D * d->B * m.Kp * m.esize;
+  // kernel 2c's ring: fp32, rows of 64 x its K chunks per lane
+  if (small_scan_shape(d, m))
+    b = std::max(b, (size_t)kScanRingSlots * m.D * d->B * 64 * scan_small_chunks(m.K) * 4);
+  return align_up(b, kAlign);
 }
 size_t mx_ring_bytes(const RnnDesc* d, const Dims& m) {
   return align_up((size_t)kScanRingSlots * m.D * d->B * m.Hp * m.esize, kAlign);
@@ -807,8 +816,47 @@ ScanArgs layer_scan(const RnnDesc* d, const RnnWeights* w, const Dims& m, const 
 // LSTM B=1 3.28 vs 1.21; the model ranks launch shapes, this scale makes it
 // absolute); fixed costs per pipelined wave and per layer.
 constexpr double kModelScale = 2.6, kPipeWaveUs = 40.0, kLayerUs = 35.0;
+
+// Kernel 2c for a few independent sequences: LSTM or GRU of width up to 512,
+// at most kScanSmallMaxGroups (direction, row) groups, no tiling or weight
+// hint (those ask for the tiled scan), y rows addressed with 32-bit byte
+// offsets. A descriptor-only test (it sizes the workspace and the G_x
+// dtype); whether the launch fits the device is plan_small's.
+bool small_scan_shape(const RnnDesc* d, const Dims& m) {
+  if (d->mode != RNN_MODE_LSTM && d->mode != RNN_MODE_GRU) return false;
+  if (d->tile_batch || d->tile_hidden || d->weights) return false;
+  // (a stack asked to run pipelined runs the tiled scan's layer slots)
+  if (d->layer_pipeline == RNN_PIPE_ON && d->num_layers > 1) return false;
+  if (m.D * d->B > kScanSmallMaxGroups || scan_small_chunks(m.K) == 0) return false;
+  if ((double)m.rows * m.D * m.K * m.esize >= 2147483647.0) return false;
+  return !use_wave_scan(d, m);
+}
+struct SmallPlan {
+  bool on;
+  int hs, ns, gpx;  // units per workgroup, members per group, groups per XCD (0: flat)
+};
+SmallPlan plan_small(const RnnDesc* d, const Dims& m, int cus, int xcds) {
+  SmallPlan s{};
+  if (!small_scan_shape(d, m)) return s;
+  const int mk = d->mode == RNN_MODE_GRU ? kGRU : kLSTM;
+  s.hs = scan_small_units_per_wg(mk, m.K);
+  s.ns = cdiv(d->hidden_size, s.hs);
+  const int groups = m.D * d->B;
+  if (groups * s.ns > cus || groups * s.ns > kScanMaxWorkgroups) return s;
+  // members of a group on one XCD when a whole number of groups fits each
+  // (placement 1 asks for consecutive ids, 2 for aligned groups)
+  const int gpx = cdiv(groups, xcds);
+  const bool aligned_ok = xcds > 1 && gpx * s.ns <= cus / xcds;
+  if (d->placement == 2 && !aligned_ok) return s;
+  s.gpx = aligned_ok && d->placement != 1 ? gpx : 0;
+  s.on = true;
+  return s;
+}
+int small_grid(const SmallPlan& s, int groups, int xcds) { return s.gpx > 0 ? xcds * s.gpx * s.ns : groups * s.ns; }
+
 struct ForwardPlan {
   bool wave, pipe;
+  SmallPlan sp;
   PipeShape ps;
   ScanPlan p;
   double step_us;  // modelled time of one scan step of the chosen plan
@@ -821,6 +869,13 @@ int plan_forward(const RnnDesc* d, const Dims& m, bool has_len, int cus, int xcd
   if (f.wave) {
     *out = f;
     return RNN_OK;
+  }
+  if (!training) {
+    f.sp = plan_small(d, m, cus, xcds);
+    if (f.sp.on) {
+      *out = f;
+      return RNN_OK;
+    }
   }
   f.ps = pipe_shape(d, has_len, m);
   double one = 0.0;
@@ -1036,6 +1091,10 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
 
     // Kernel 2: the scan.
     ScanArgs a = wave ? ScanArgs{} : layer_scan(d, w, m, p, xcds, l, ws, L);
+    if (f.sp.on) {
+      a.hs = f.sp.hs; a.ns = f.sp.ns; a.gpx = f.sp.gpx; a.nxcd = xcds;
+      a.Kp = 64 * scan_small_chunks(m.K);
+    }
     if (wave) {
       a.mode = d->mode == RNN_MODE_GRU ? kGRU : (d->mode == RNN_MODE_LSTMP ? kLSTMP : kLSTM);
       a.B = d->B; a.H = d->hidden_size; a.K = m.K; a.P = d->proj_size; a.D = m.D; a.G = m.G;
@@ -1075,7 +1134,10 @@ int forward_rnn(const RnnDesc* d, const RnnWeights* w, const RnnIO* io, char* ws
     a.lengths = dev_len;
     a.offsets = dev_off;
     if ((rc = prof.begin(wave ? 4 : 2, l)) != RNN_OK) return rc;
-    if ((rc = hip_status(wave ? launch_scan_wave(a, bf16, st) : launch_scan(a, bf16, st))) != RNN_OK) return rc;
+    if ((rc = hip_status(wave        ? launch_scan_wave(a, bf16, st)
+                         : f.sp.on ? launch_scan_small(a, bf16, st)
+                                   : launch_scan(a, bf16, st))) != RNN_OK)
+      return rc;
     if ((rc = prof.end()) != RNN_OK) return rc;
     layer_in = layer_out;
   }
@@ -1452,6 +1514,12 @@ int rnn_plan_info(const RnnDesc* desc, const int32_t* lengths_host, int cus, int
   ForwardPlan f;
   rc = plan_forward(desc, m, lengths_host != nullptr, cus, xcds, (size_t)m.K * m.esize % 16 == 0, false, &f);
   if (rc != RNN_OK) return rc;
+  if (f.sp.on) {
+    // kernel 2c: groups of ns workgroups, one per (direction, row)
+    info[0] = 5; info[1] = small_grid(f.sp, m.D * desc->B, xcds); info[2] = 0;
+    info[3] = 1; info[4] = f.sp.hs; info[5] = f.sp.ns; info[6] = 0; info[7] = m.D * desc->B; info[8] = f.sp.gpx;
+    return RNN_OK;
+  }
   const ScanPlan& p = f.p;
   info[0] = 2; info[1] = scan_grid(p, (f.pipe ? desc->num_layers : 1) * m.D, xcds); info[2] = p.lds;
   info[3] = p.bb; info[4] = p.hs; info[5] = p.ns; info[6] = p.ps; info[7] = p.nbb; info[8] = p.gpx;

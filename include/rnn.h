@@ -360,7 +360,9 @@ int rnn_read_status(const void* workspace, void* stream, int* device_status);
  * dealt to them round-robin). info[0..8] = {kernel (2 tiled scan, 3 RSSM,
  * 4 one-wave-per-row scan: LSTM or GRU with H <= 16 when no
  * tiling hint is set; its waves are independent, so it needs no
- * co-residency),
+ * co-residency; 5 few-row scan: LSTM or GRU with H <= 512 and at most 8
+ * direction x batch rows, no tiling or weight hint, not asked to pipeline
+ * a stack: one group of workgroups per direction and row, no LDS),
  * workgroups launched, LDS bytes per workgroup (kernel 4: the x rows it
  * stages when it forms layer 0's input projection itself), batch rows per workgroup,
  * hidden units per workgroup, workgroups per group, projection outputs per

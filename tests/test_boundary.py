@@ -240,14 +240,15 @@ def test_layer_pipeline_values(lib):
 def test_bf16_gx_halves_the_gate_buffer(lib):
     """bf16 storage keeps G_x in bf16 unless fp32 is requested: the workspace
     shrinks by half the G_x buffer (rows * D * G * 2 bytes, give or take the
-    256-byte section alignment)."""
-    kw = dict(mode=1, dtype=1, T=20, B=8, input_size=16, hidden_size=32)
+    256-byte section alignment). (B = 16 runs the tiled scan; the few-row
+    scan reads fp32 G_x whatever the storage dtype.)"""
+    kw = dict(mode=1, dtype=1, T=20, B=16, input_size=16, hidden_size=32)
     st0, n_bf = _ws(_desc(**kw))
     d = _desc(**kw)
     d.gx_dtype = 1
     st1, n_f32 = _ws(d)
     assert st0 == st1 == OK
-    half = 20 * 8 * 3 * 32 * 2
+    half = 20 * 16 * 3 * 32 * 2
     assert abs((n_f32 - n_bf) - half) <= 256
 
 

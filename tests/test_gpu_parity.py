@@ -293,10 +293,14 @@ def test_layer_pipeline(case):
                               seed=zlib.crc32(name.encode()) % 1000, h0_std=0.3, c0_std=0.3)
     desc = _desc_of(d)
     desc.layer_pipeline = gss.PIPE_MODES["on"]
-    chunk = gss.rnn_plan_info(desc)["pipe_chunk"]
+    plan = gss.rnn_plan_info(desc)
+    chunk = plan["pipe_chunk"]
     assert chunk >= 32 and T > chunk and T - (T - 1) // chunk * chunk == tail
-    piped = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc, layer_pipeline="on")
-    layered = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc, layer_pipeline="off")
+    # the layer-by-layer run in the same tiled launch shape (a small batch
+    # would otherwise take the few-row scan, whose sums run in another order)
+    tiles = dict(tile_batch=plan["rows"], tile_hidden=plan["hidden_per_wg"])
+    piped = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc, layer_pipeline="on", **tiles)
+    layered = run_rnn(d, y_fill=float("nan"), cell_clip=cc, proj_clip=pc, layer_pipeline="off", **tiles)
     for a, b, what in zip(piped, layered, ("y", "h_n", "c_n")):
         if b is not None:
             assert np.array_equal(a, b), f"{name}: pipelined {what} differs from the layer-by-layer run"

@@ -56,6 +56,21 @@ def test_plan_is_coresident_and_covers(name, cus, xcds):
         assert p["workgroups"] * 4 >= D * s.B and p["lds_bytes"] in (0, 4 * (16384 + 4096))
         return
     assert p["workgroups"] <= cus
+    if p["kernel"] == 5:
+        # the few-row scan: one group of `members` workgroups per
+        # (direction, row), every group co-resident, no LDS
+        D = 2 if s.bidirectional else 1
+        assert s.mode in ("lstm", "gru") and D * s.B <= 8 and s.hidden_size <= 512
+        assert p["groups"] == D * s.B and p["rows"] == 1 and p["lds_bytes"] == 0
+        assert p["hidden_per_wg"] * p["members"] >= s.hidden_size
+        assert p["hidden_per_wg"] * (p["members"] - 1) < s.hidden_size
+        if p["groups_per_xcd"]:
+            assert p["groups_per_xcd"] * xcds >= p["groups"]
+            assert p["groups_per_xcd"] * p["members"] <= cus // xcds
+            assert p["workgroups"] == xcds * p["groups_per_xcd"] * p["members"]
+        else:
+            assert p["workgroups"] == p["groups"] * p["members"]
+        return
     assert 0 < p["lds_bytes"] <= LDS_MAX
     if p["kernel"] == 3:
         assert p["groups"] == math.ceil(s.B / p["rows"])
@@ -138,11 +153,14 @@ def test_forced_register_layouts(case):
     assert (p["wreg"], p["reg_tiles"], p["reg_ksplit"], p["reg_chunks"]) == expect
 
 
-@pytest.mark.parametrize("mode,H,expect", [("lstm", 16, 4), ("lstm", 17, 2), ("gru", 16, 4), ("gru", 17, 2),
-                                           ("lstm", 1, 4), ("lstmp", 8, 2)])
-def test_wave_scan_choice(mode, H, expect):
+# one-wave scan (4) up to 16 units; above, the few-row scan (5) for up to 8
+# (direction, row) groups and the tiled scan (2) for more rows or LSTMP
+@pytest.mark.parametrize("mode,H,B,expect", [("lstm", 16, 5, 4), ("lstm", 17, 5, 5), ("gru", 16, 5, 4),
+                                             ("gru", 17, 5, 5), ("lstm", 1, 5, 4), ("lstmp", 8, 5, 2),
+                                             ("lstm", 17, 9, 2), ("gru", 512, 8, 5), ("gru", 513, 8, 2)])
+def test_wave_scan_choice(mode, H, B, expect):
     d = gss.RnnDesc()
-    d.mode, d.T, d.B, d.input_size, d.hidden_size, d.num_layers, d.has_bias = gss.MODES[mode], 8, 5, 7, H, 1, 1
+    d.mode, d.T, d.B, d.input_size, d.hidden_size, d.num_layers, d.has_bias = gss.MODES[mode], 8, B, 7, H, 1, 1
     if mode == "lstmp":
         d.proj_size = 4
     assert gss.rnn_plan_info(d)["kernel"] == expect
