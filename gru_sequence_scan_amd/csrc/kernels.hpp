@@ -139,7 +139,7 @@ constexpr int kScanRegChunks = 32;
 // scan_small_chunks(K). LSTM and GRU, K <= 512.
 constexpr int kScanSmallMaxGroups = 8;
 int scan_small_chunks(int K);               // K chunks per lane: 1, 2, 4 or 8 (0: K > 512)
-int scan_small_units_per_wg(int mode, int K);
+int scan_small_units_per_wg(int units_per_wave);  // units_per_wave: 1, 2 or 4
 hipError_t launch_scan_small(const ScanArgs& a, int dtype_bf16, hipStream_t stream);
 
 // Kernel 2b: one wave per (direction, batch row) when the gate rows of all

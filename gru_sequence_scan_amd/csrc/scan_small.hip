@@ -283,12 +283,7 @@ int scan_small_chunks(int K) {
   return j <= 1 ? 1 : j <= 2 ? 2 : j <= 4 ? 4 : j <= 8 ? 8 : 0;
 }
 
-int scan_small_units_per_wg(int mode, int K) {
-  // two units per wave (a wave's R gate rows over its four DPP rows: 2 rows
-  // per DPP row for LSTM), four when K is short
-  (void)mode;
-  return (K <= 128 ? 4 : 2) * kSmWaves;
-}
+int scan_small_units_per_wg(int units_per_wave) { return units_per_wave * kSmWaves; }
 
 hipError_t launch_scan_small(const ScanArgs& a, int dtype_bf16, hipStream_t stream) {
   if (a.mode != kLSTM && a.mode != kGRU) return hipErrorInvalidValue;

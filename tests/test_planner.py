@@ -174,7 +174,9 @@ def test_wave_scan_choice(mode, H, B, expect):
 # (rows per group, hidden units per member): the cost model must keep
 # choosing them.
 MEASURED_BEST = {
-    "lstm_t80_b1": (1, 16),
+    # (the few-row scan: one row per group; 8 units per member measured
+    # 125 us per scan against 135 and 185 for 16 and 32)
+    "lstm_t80_b1": (1, 8),
     "gru_t256_b256": (16, 32),
     "lstmp_t1000_b32": (16, 32),
     "bilstm_varlen_b64": (16, 16),
