@@ -125,6 +125,44 @@ def test_small_cases(case):
     _compare(d, got, ref, name)
 
 
+# The few-row scan (kernel 5 in the plan: at most 8 direction x batch rows,
+# H <= 512): LSTM and GRU, fp32 and bf16, padded and packed variable
+# lengths, both directions, stacked layers, one and two units per wave.
+SMALL_SCAN = [
+    # name, mode, dtype, T, B, F, H, L, bidir, layout, varlen, state
+    ("few_bilstm_packed_2l", "lstm", "f32", 13, 4, 24, 72, 2, True, "packed", (1, 13), True),
+    ("few_gru_bf16_varlen", "gru", "bf16", 11, 3, 40, 300, 1, False, "padded", "unsorted", True),
+    ("few_lstm_h512_b8_two_units", "lstm", "f32", 5, 8, 512, 512, 1, False, "padded", None, False),
+    ("few_gru_b1_wide_in", "gru", "f32", 7, 1, 512, 256, 1, False, "padded", None, True),
+    ("few_lstm_bf16_in_600", "lstm", "bf16", 6, 2, 600, 64, 1, False, "padded", None, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_SCAN, ids=[c[0] for c in SMALL_SCAN])
+def test_small_scan_cases(case):
+    import gru_sequence_scan_amd as gss
+    name, mode, dt, T, B, F, H, L, bidir, layout, varlen, state = case
+    log(f"[gpu] few-row scan case {name}")
+    lengths = None
+    vl = None
+    if varlen == "unsorted":
+        lengths = np.random.default_rng(11).integers(1, T + 1, size=B).astype(np.int32)
+        lengths[1] = T
+    elif varlen is not None:
+        vl = varlen
+    d = synth.make_rnn_inputs(mode, T, B, F, H, num_layers=L, bidirectional=bidir, dtype=dt, layout=layout,
+                              lengths=lengths, varlen=vl, w_scale=1.0 / np.sqrt(H),
+                              seed=zlib.crc32(name.encode()) % 1000, h0_std=0.3 if state else 0.0,
+                              c0_std=0.3 if state else 0.0)
+    desc = _desc_of(d)
+    desc.bidirectional = int(bidir)
+    desc.layout = 1 if layout == "packed" else 0
+    assert gss.rnn_plan_info(desc, d["lengths"])["kernel"] == 5
+    got = run_rnn(d, y_fill=float("nan"))
+    ref = _oracle(d)
+    _compare(d, got, ref, name)
+
+
 # The largest hidden sizes the planner accepts on one MI355X: groups of 128 to
 # 256 members (every CU in one group for the B = 1 fp32 and the bf16 H = 2048
 # cases), weights resident in LDS or registers. One size beyond is rejected
