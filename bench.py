@@ -63,13 +63,13 @@ KERNEL_SOURCES = {
 # with those of the first input GEMM ("gemm_counters"). Valid only for the
 # kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 9898568, "write_bytes": 3564000, "sources": "1fa3a10ef8bc7db5", "counters": {"mfma_flops": 4199424000, "mfma_busy": 0.0778, "lds_active": 0.07373, "lds_bank_conflict": 0.07161}},
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1477917, "write_bytes": 88576, "sources": "b1ed972d277a206b", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 0.00459, "lds_bank_conflict": 0.0}, "gemm_counters": {"mfma_flops": 134217728, "mfma_busy": 0.0463, "lds_active": 0.00673, "lds_bank_conflict": 0.0}, "gemm_sources": "1332b5e0f7b74dcc"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 215456733, "write_bytes": 68427776, "sources": "b1ed972d277a206b", "counters": {"mfma_flops": 137438953472, "mfma_busy": 0.0538, "lds_active": 0.09999, "lds_bank_conflict": 0.33587}, "gemm_counters": {"mfma_flops": 103079215104, "mfma_busy": 0.2609, "lds_active": 0.43678, "lds_bank_conflict": 0.2963}, "gemm_sources": "1332b5e0f7b74dcc"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": "0-1", "fetch_bytes": 54539386, "write_bytes": 3594581, "sources": "b1ed972d277a206b", "counters": {"mfma_flops": 16777216000, "mfma_busy": 0.01005, "lds_active": 0.04481, "lds_bank_conflict": 0.32038}, "gemm_counters": {"mfma_flops": 83886080000, "mfma_busy": 0.21982, "lds_active": 0.4018, "lds_bank_conflict": 0.27778}, "gemm_sources": "1332b5e0f7b74dcc"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 351878460, "write_bytes": 80773120, "sources": "b1ed972d277a206b", "counters": {"mfma_flops": 95093260288, "mfma_busy": 0.26371, "lds_active": 0.091, "lds_bank_conflict": 0.40562}, "gemm_counters": {"mfma_flops": 40802189312, "mfma_busy": 0.72909, "lds_active": 0.06201, "lds_bank_conflict": 0.0}, "gemm_sources": "1332b5e0f7b74dcc"},
-    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 44363, "write_bytes": 16544, "sources": "3942465c319d76a2", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 0.00012, "lds_bank_conflict": 0.0}},
-    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 347652417, "write_bytes": 56108947, "sources": "1fa3a10ef8bc7db5", "counters": {"mfma_flops": 7234560000, "mfma_busy": 0.08451, "lds_active": 0.10773, "lds_bank_conflict": 0.1031}},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 10394544, "write_bytes": 4046400, "sources": "9aa000e3df75e19e", "counters": {"mfma_flops": 6473318400, "mfma_busy": 0.12691, "lds_active": 0.11624, "lds_bank_conflict": 0.07353}},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1435372, "write_bytes": 89088, "sources": "0ad437ce7a0904cd", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 3e-05, "lds_bank_conflict": 0.0}, "gemm_counters": {"mfma_flops": 134217728, "mfma_busy": 0.04301, "lds_active": 0.00609, "lds_bank_conflict": 0.0}, "gemm_sources": "6f2709bfd2327e56"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 215456707, "write_bytes": 68427776, "sources": "0ad437ce7a0904cd", "counters": {"mfma_flops": 137438953472, "mfma_busy": 0.05369, "lds_active": 0.09996, "lds_bank_conflict": 0.33587}, "gemm_counters": {"mfma_flops": 103079215104, "mfma_busy": 0.25699, "lds_active": 0.43613, "lds_bank_conflict": 0.2963}, "gemm_sources": "6f2709bfd2327e56"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": "0-1", "fetch_bytes": 54539397, "write_bytes": 3594581, "sources": "0ad437ce7a0904cd", "counters": {"mfma_flops": 16777216000, "mfma_busy": 0.01006, "lds_active": 0.04482, "lds_bank_conflict": 0.32038}, "gemm_counters": {"mfma_flops": 83886080000, "mfma_busy": 0.21285, "lds_active": 0.38128, "lds_bank_conflict": 0.27778}, "gemm_sources": "6f2709bfd2327e56"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 351877283, "write_bytes": 80773120, "sources": "0ad437ce7a0904cd", "counters": {"mfma_flops": 95093260288, "mfma_busy": 0.26483, "lds_active": 0.09087, "lds_bank_conflict": 0.40562}, "gemm_counters": {"mfma_flops": 40802189312, "mfma_busy": 0.71647, "lds_active": 0.0615, "lds_bank_conflict": 0.0}, "gemm_sources": "6f2709bfd2327e56"},
+    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 44363, "write_bytes": 16544, "sources": "20d2a80487ce80d5", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 0.00012, "lds_bank_conflict": 0.0}},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 12972182, "write_bytes": 5386400, "sources": "9aa000e3df75e19e", "counters": {"mfma_flops": 8308326400, "mfma_busy": 0.12219, "lds_active": 0.12736, "lds_bank_conflict": 0.06538}},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
