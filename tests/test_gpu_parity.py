@@ -67,6 +67,10 @@ SMALL = [
     ("gru_splitk_bf16", "gru", "bf16", 6, 5, 300, 40, 0, 1, False, "padded", None, True, True),
     ("lstm_splitk_pipe", "lstm", "f32", 4, 9, 256, 72, 0, 1, False, "padded", None, True, False),
     ("bilstm_splitk_packed", "lstm", "f32", 7, 6, 160, 96, 0, 2, True, "packed", (1, 7), True, True),
+    # bf16 rows that are whole K stages (the two-stage prefetch form): split
+    # ranges of five and four stages, and an odd stage count without a split
+    ("gru_splitk_pf_bf16", "gru", "bf16", 4, 4, 448, 64, 0, 1, False, "padded", None, True, True),
+    ("gru_pf_odd_stages_bf16", "gru", "bf16", 9, 40, 96, 96, 0, 1, False, "padded", None, True, True),
     # bf16 G_x rows of odd width (3H with H odd): a step's rows start at a
     # 2-byte offset; and the one-wave kernel on bf16 storage (G = 45), its
     # input (8 bf16) narrow enough for the projection inside the kernel
