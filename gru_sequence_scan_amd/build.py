@@ -36,6 +36,12 @@ def hipcc_path():
     return p
 
 
+def link_flags(hipcc):
+    """roctx (host ranges for timeline tools) from the ROCm tree hipcc belongs to."""
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc))), "lib")
+    return ["-L", rocm_lib, "-lrocprofiler-sdk-roctx", "-Wl,-rpath," + rocm_lib]
+
+
 def lib_path():
     return os.path.join(OUT_DIR, LIB_NAME)
 
@@ -71,7 +77,7 @@ def build(verbose=False, jobs=None):
             raise RuntimeError(f"hipcc failed ({rc}) for {cmd[-3]}:\n{errs}")
         if verbose and errs.strip():
             print(errs, file=sys.stderr)
-    rc, errs = _run([hipcc, "-shared", "-fPIC", "--offload-arch=gfx950"] + objs + ["-o", tmp])
+    rc, errs = _run([hipcc, "-shared", "-fPIC", "--offload-arch=gfx950"] + objs + link_flags(hipcc) + ["-o", tmp])
     if rc != 0:
         raise RuntimeError(f"link failed ({rc}):\n{errs}")
     os.replace(tmp, out)

@@ -5,10 +5,12 @@
 // between calls is a per-device cache of immutable facts (architecture name,
 // compute-unit count), filled once under a lock.
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <limits>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -604,13 +606,36 @@ int hip_status(hipError_t e) { return e == hipSuccess ? RNN_OK : RNN_E_HIP; }
 // layer | last layer << 4). The bracket's events ride on its launches
 // (start with the first dispatch, stop with the last completion); a bracket
 // that launched nothing records both directly.
+// A named host range (roctx) around one public call, for timeline tools
+// such as rocprofv3 --marker-trace; a no-op when no tool is attached.
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
+
+// Per-launch brackets: the kind and layer of every kernel the call enqueues
+// (kind 1 input projection, 2 tiled scan, 3 RSSM unroll, 4 one-wave scan,
+// 5 pipelined scans of two layers), HIP events on the launch when the caller
+// asked for timing, and a roctx range named after the launch.
 struct Prof {
   void* const* events = nullptr;
   int n_events = 0;
   int* kinds = nullptr;
   int n = 0;
+  int open = 0;  // roctx ranges pushed and not yet popped
   hipStream_t st = nullptr;
   int begin(int kind, int layer) {
+    static const char* const names[] = {"?", "input_projection", "scan", "rssm_unroll", "scan_wave", "scan"};
+    char label[48];
+    const char* nm = kind >= 1 && kind <= 5 ? names[kind] : names[0];
+    if (kind == 5)
+      snprintf(label, sizeof label, "%s L%d+L%d", nm, layer & 15, layer >> 4);
+    else
+      snprintf(label, sizeof label, "%s L%d", nm, layer);
+    roctxRangePushA(label);
+    ++open;
     if (kinds && n < n_events / 2) kinds[n] = kind | layer << 8;
     if (events && n < n_events / 2) {
       rnnk::LaunchEvents& ev = rnnk::launch_events();
@@ -628,11 +653,18 @@ struct Prof {
     }
     ev = rnnk::LaunchEvents{};
     ++n;
+    if (open > 0) {
+      roctxRangePop();
+      --open;
+    }
     return rc;
   }
   // an early return inside a bracket must not leave events armed for a
-  // later call on this thread
-  ~Prof() { rnnk::launch_events() = rnnk::LaunchEvents{}; }
+  // later call on this thread, nor a range open
+  ~Prof() {
+    rnnk::launch_events() = rnnk::LaunchEvents{};
+    for (; open > 0; --open) roctxRangePop();
+  }
 };
 
 int check_ptr(const void* p, size_t elem) {
@@ -1568,6 +1600,7 @@ int rnn_backward_workspace_bytes(const RnnDesc* desc, const int32_t* lengths_hos
 
 int rnn_forward_train(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* reserve,
                       size_t reserve_bytes, void* workspace, size_t ws_bytes, void* stream) {
+  Range range("rnn_forward_train");
   int rc = validate_desc(desc);
   if (rc != RNN_OK) return rc;
   if ((rc = validate_train(desc)) != RNN_OK) return rc;
@@ -1586,6 +1619,7 @@ int rnn_forward_train(const RnnDesc* desc, const RnnWeights* weights, const RnnI
 
 int rnn_backward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, const RnnGrads* grads,
                  const void* reserve, size_t reserve_bytes, void* workspace, size_t ws_bytes, void* stream) {
+  Range range("rnn_backward");
   int rc = validate_desc(desc);
   if (rc != RNN_OK) return rc;
   if ((rc = validate_train(desc)) != RNN_OK) return rc;
@@ -1624,6 +1658,7 @@ int rnn_exchange_roundtrip_ns(void* buffer, size_t bytes, int iters, void* strea
 int rnn_forward_profiled(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* workspace,
                          size_t ws_bytes, void* stream, void* const* events, int n_events, int* kinds,
                          int* n_kernels) {
+  Range range("rnn_forward");
   int rc = validate_desc(desc);
   if (rc != RNN_OK) return rc;
   if (!weights || !io) return RNN_E_NULL;
@@ -1656,6 +1691,7 @@ int rnn_forward(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io,
 
 int rnn_forward_noalloc(const RnnDesc* desc, const RnnWeights* weights, const RnnIO* io, void* stream,
                         int32_t* device_status) {
+  Range range("rnn_forward_noalloc");
   int rc = validate_desc(desc);
   if (rc != RNN_OK) return rc;
   if (!weights || !io) return RNN_E_NULL;

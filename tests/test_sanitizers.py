@@ -51,7 +51,7 @@ def test_host_library_under_asan_ubsan(tmp_path):
         for (rc, err), cmd in zip(ex.map(_run, cmds), cmds):
             assert rc == 0, f"compile failed: {cmd[-3]}\n{err[-2000:]}"
     exe = str(tmp_path / "host_check")
-    rc, err = _run([hipcc, "--offload-arch=gfx950"] + SAN + objs + ["-o", exe])
+    rc, err = _run([hipcc, "--offload-arch=gfx950"] + SAN + objs + bld.link_flags(hipcc) + ["-o", exe])
     assert rc == 0, err[-2000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
