@@ -63,13 +63,13 @@ KERNEL_SOURCES = {
 # with those of the first input GEMM ("gemm_counters"). Valid only for the
 # kernel sources they were taken on.
 MEASURED_TRAFFIC = {
-    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 10394544, "write_bytes": 4046400, "sources": "9aa000e3df75e19e", "counters": {"mfma_flops": 6473318400, "mfma_busy": 0.12691, "lds_active": 0.11624, "lds_bank_conflict": 0.07353}},
-    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1435372, "write_bytes": 89088, "sources": "0ad437ce7a0904cd", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 3e-05, "lds_bank_conflict": 0.0}, "gemm_counters": {"mfma_flops": 134217728, "mfma_busy": 0.04301, "lds_active": 0.00609, "lds_bank_conflict": 0.0}, "gemm_sources": "6f2709bfd2327e56"},
-    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 215456707, "write_bytes": 68427776, "sources": "0ad437ce7a0904cd", "counters": {"mfma_flops": 137438953472, "mfma_busy": 0.05369, "lds_active": 0.09996, "lds_bank_conflict": 0.33587}, "gemm_counters": {"mfma_flops": 103079215104, "mfma_busy": 0.25699, "lds_active": 0.43613, "lds_bank_conflict": 0.2963}, "gemm_sources": "6f2709bfd2327e56"},
-    "lstmp_t1000_b32": {"kernel": "scan", "index": "0-1", "fetch_bytes": 54539397, "write_bytes": 3594581, "sources": "0ad437ce7a0904cd", "counters": {"mfma_flops": 16777216000, "mfma_busy": 0.01006, "lds_active": 0.04482, "lds_bank_conflict": 0.32038}, "gemm_counters": {"mfma_flops": 83886080000, "mfma_busy": 0.21285, "lds_active": 0.38128, "lds_bank_conflict": 0.27778}, "gemm_sources": "6f2709bfd2327e56"},
-    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 351877283, "write_bytes": 80773120, "sources": "0ad437ce7a0904cd", "counters": {"mfma_flops": 95093260288, "mfma_busy": 0.26483, "lds_active": 0.09087, "lds_bank_conflict": 0.40562}, "gemm_counters": {"mfma_flops": 40802189312, "mfma_busy": 0.71647, "lds_active": 0.0615, "lds_bank_conflict": 0.0}, "gemm_sources": "6f2709bfd2327e56"},
-    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 44363, "write_bytes": 16544, "sources": "20d2a80487ce80d5", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 0.00012, "lds_bank_conflict": 0.0}},
-    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 12972182, "write_bytes": 5386400, "sources": "9aa000e3df75e19e", "counters": {"mfma_flops": 8308326400, "mfma_busy": 0.12219, "lds_active": 0.12736, "lds_bank_conflict": 0.06538}},
+    "rssm_b50_t50": {"kernel": "rssm", "index": 0, "fetch_bytes": 10394800, "write_bytes": 4046400, "sources": "95d745d87b07bc55", "counters": {"mfma_flops": 6473318400, "mfma_busy": 0.12671, "lds_active": 0.11652, "lds_bank_conflict": 0.07353}},
+    "lstm_t80_b1": {"kernel": "scan", "index": 0, "fetch_bytes": 1435372, "write_bytes": 89088, "sources": "4fee0762a840a6ce", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 3e-05, "lds_bank_conflict": 0.0}, "gemm_counters": {"mfma_flops": 134217728, "mfma_busy": 0.04447, "lds_active": 0.00636, "lds_bank_conflict": 0.0}, "gemm_sources": "e4088e4395184de3"},
+    "gru_t256_b256": {"kernel": "scan", "index": 0, "fetch_bytes": 215456758, "write_bytes": 68427776, "sources": "4fee0762a840a6ce", "counters": {"mfma_flops": 137438953472, "mfma_busy": 0.05366, "lds_active": 0.10002, "lds_bank_conflict": 0.33587}, "gemm_counters": {"mfma_flops": 103079215104, "mfma_busy": 0.25616, "lds_active": 0.43209, "lds_bank_conflict": 0.2963}, "gemm_sources": "e4088e4395184de3"},
+    "lstmp_t1000_b32": {"kernel": "scan", "index": "0-1", "fetch_bytes": 54539399, "write_bytes": 3594581, "sources": "4fee0762a840a6ce", "counters": {"mfma_flops": 16777216000, "mfma_busy": 0.01007, "lds_active": 0.04482, "lds_bank_conflict": 0.32038}, "gemm_counters": {"mfma_flops": 83886080000, "mfma_busy": 0.21653, "lds_active": 0.39409, "lds_bank_conflict": 0.27778}, "gemm_sources": "e4088e4395184de3"},
+    "bilstm_varlen_b64": {"kernel": "scan", "index": 1, "fetch_bytes": 351878435, "write_bytes": 80773120, "sources": "4fee0762a840a6ce", "counters": {"mfma_flops": 95093260288, "mfma_busy": 0.26271, "lds_active": 0.09065, "lds_bank_conflict": 0.40562}, "gemm_counters": {"mfma_flops": 40802189312, "mfma_busy": 0.71499, "lds_active": 0.06179, "lds_bank_conflict": 0.0}, "gemm_sources": "e4088e4395184de3"},
+    "lstm_t256_b1_small": {"kernel": "scan_wave", "index": 0, "fetch_bytes": 44363, "write_bytes": 16544, "sources": "bc88e60b733c51bf", "counters": {"mfma_flops": 0, "mfma_busy": 0.0, "lds_active": 0.00012, "lds_bank_conflict": 0.0}},
+    "rssm_actor_b50_h50": {"kernel": "rssm", "index": 0, "fetch_bytes": 12972182, "write_bytes": 5386400, "sources": "95d745d87b07bc55", "counters": {"mfma_flops": 8308326400, "mfma_busy": 0.12246, "lds_active": 0.12681, "lds_bank_conflict": 0.06538}},
 }
 
 # The pages' own numbers for the same metric and workload (CPU, Ryzen 5900X,
